@@ -1,0 +1,254 @@
+"""Thin Python binding of libbc (include/bc.h): argument marshalling only.
+
+Every function here has the name of the C entry point it calls and does no
+arithmetic of the decode step; all of it runs in the HIP kernels.  torch
+tensors provide device memory and the current stream.  If libbc.so is not
+built, importing this module raises -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbc.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libbc.so is not built ({LIB_PATH}); run __graft_entry__.build() first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+c_int, c_double, c_float, c_size_t, c_void_p = ctypes.c_int, ctypes.c_double, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+BC_OK, BC_ERR_INVALID, BC_ERR_UNSUPPORTED, BC_ERR_WORKSPACE, BC_ERR_HIP = 0, -1, -2, -3, -4
+
+
+class BcError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        msg = _lib.bc_last_error().decode(errors="replace")
+        super().__init__(f"{where} failed with code {code}: {msg}")
+        self.code = code
+
+
+class bc_model_dims(ctypes.Structure):
+    _fields_ = [("n_layers", c_int), ("d", c_int), ("d_ff", c_int), ("vocab", c_int),
+                ("n_heads", c_int), ("n_kv_heads", c_int), ("head_dim", c_int)]
+
+
+class bc_kv_policy(ctypes.Structure):
+    _fields_ = [("r_kv", c_double), ("sinks", c_int), ("window", c_int), ("block", c_int)]
+
+
+class bc_kv_budget_info(ctypes.Structure):
+    _fields_ = [("t_sel", c_int), ("k_blk", c_int), ("n_cand", c_int), ("b_lo", c_int),
+                ("sinks", c_int), ("window", c_int)]
+
+
+class bc_layer(ctypes.Structure):
+    _fields_ = [("w_qkv", c_void_p), ("w_o", c_void_p), ("w_gu", c_void_p), ("w_down", c_void_p),
+                ("g_attn", c_void_p), ("g_mlp", c_void_p), ("k_cache", c_void_p), ("v_cache", c_void_p),
+                ("kv_summary", c_void_p), ("n_cap", c_int)]
+
+
+class bc_layer_taps(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("x1", "idx_qkv", "q", "k", "v", "idx_kv", "a", "idx_o", "h_mid", "x2",
+                                        "idx_gu", "hff", "idx_down")]
+
+
+class bc_step(ctypes.Structure):
+    _fields_ = [("n_ctx", c_int), ("r_p", c_double), ("kv", bc_kv_policy), ("n_splits", c_int),
+                ("rope_theta", c_double), ("rms_eps", c_double), ("taps", ctypes.POINTER(bc_layer_taps))]
+
+
+P = c_void_p
+_SIG = {
+    "bc_abi_version": (c_int, []),
+    "bc_last_error": (ctypes.c_char_p, []),
+    "bc_channel_keep": (c_int, [c_double, c_int]),
+    "bc_kv_budget": (c_int, [c_int, ctypes.POINTER(bc_kv_policy), ctypes.POINTER(bc_kv_budget_info)]),
+    "bc_workspace_init": (c_int, [P, c_size_t, P]),
+    "bc_select_channels": (c_int, [P, c_int, c_int, P, P]),
+    "bc_sparse_gemv_workspace_bytes": (c_size_t, [c_int, c_int]),
+    "bc_sparse_gemv": (c_int, [P, c_int, c_int, P, P, c_int, P, P, c_size_t, P]),
+    "bc_kv_score_select_workspace_bytes": (c_size_t, [c_int, c_int, ctypes.POINTER(bc_kv_policy)]),
+    "bc_kv_score_select": (c_int, [P, P, c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(bc_kv_policy), P, P,
+                                   P, c_size_t, P]),
+    "bc_build_kv_summary": (c_int, [P, c_int, c_int, c_int, c_int, P, P]),
+    "bc_splitk_attn_partial": (c_int, [P, P, P, c_int, P, c_int, c_int, c_int, c_int, c_int, c_float, P, P, P, P]),
+    "bc_splitk_reduce": (c_int, [P, P, P, c_int, c_int, c_int, P, P]),
+    "bc_attn_default_splits": (c_int, [c_int, c_int]),
+    "bc_layer_workspace_bytes": (c_size_t, [ctypes.POINTER(bc_model_dims), c_int, c_int]),
+    "bc_decode_layer": (c_int, [ctypes.POINTER(bc_model_dims), ctypes.POINTER(bc_layer), ctypes.POINTER(bc_step),
+                                P, P, c_size_t, P]),
+    "bc_pack_gate_up": (c_int, [P, P, c_int, c_int, P, P]),
+    "bc_lm_head_workspace_bytes": (c_size_t, [ctypes.POINTER(bc_model_dims)]),
+    "bc_lm_head": (c_int, [ctypes.POINTER(bc_model_dims), P, P, P, P, P, c_double, P, c_size_t, P]),
+}
+for _name, (_res, _args) in _SIG.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_SIG)
+
+
+def library():
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous CUDA/HIP tensors"
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str):
+    if rc != BC_OK:
+        raise BcError(rc, where)
+    return rc
+
+
+def _ws(t):
+    return (_ptr(t), 0 if t is None else t.numel() * t.element_size())
+
+
+def dims(d: dict) -> bc_model_dims:
+    return bc_model_dims(d.get("n_layers", 1), d["d"], d["d_ff"], d.get("vocab", 8), d["n_heads"],
+                         d["n_kv_heads"], d["head_dim"])
+
+
+def policy(r_kv: float, sinks: int = 4, window: int = 1024, block: int = 16) -> bc_kv_policy:
+    return bc_kv_policy(float(r_kv), int(sinks), int(window), int(block))
+
+
+# ----------------------------------------------------------- host queries
+def bc_abi_version() -> int:
+    return _lib.bc_abi_version()
+
+
+def bc_channel_keep(r_p: float, d_in: int) -> int:
+    k = _lib.bc_channel_keep(float(r_p), int(d_in))
+    if k < 0:
+        raise BcError(k, "bc_channel_keep")
+    return k
+
+
+def bc_kv_budget(n_ctx: int, pol: bc_kv_policy) -> dict:
+    out = bc_kv_budget_info()
+    _check(_lib.bc_kv_budget(int(n_ctx), ctypes.byref(pol), ctypes.byref(out)), "bc_kv_budget")
+    return {f: getattr(out, f) for f, _ in bc_kv_budget_info._fields_}
+
+
+def bc_attn_default_splits(n_sel: int, n_kv_heads: int) -> int:
+    return _lib.bc_attn_default_splits(int(n_sel), int(n_kv_heads))
+
+
+def bc_sparse_gemv_workspace_bytes(d_out: int, k: int) -> int:
+    return _lib.bc_sparse_gemv_workspace_bytes(int(d_out), int(k))
+
+
+def bc_kv_score_select_workspace_bytes(n_ctx: int, n_kv_heads: int, pol: bc_kv_policy) -> int:
+    return _lib.bc_kv_score_select_workspace_bytes(int(n_ctx), int(n_kv_heads), ctypes.byref(pol))
+
+
+def bc_layer_workspace_bytes(md: bc_model_dims, max_ctx: int, max_splits: int) -> int:
+    return _lib.bc_layer_workspace_bytes(ctypes.byref(md), int(max_ctx), int(max_splits))
+
+
+def bc_lm_head_workspace_bytes(md: bc_model_dims) -> int:
+    return _lib.bc_lm_head_workspace_bytes(ctypes.byref(md))
+
+
+# ------------------------------------------------------------ device calls
+def bc_workspace_init(ws, stream=None):
+    p, n = _ws(ws)
+    return _check(_lib.bc_workspace_init(p, n, _stream(stream)), "bc_workspace_init")
+
+
+def bc_select_channels(x, k: int, idx_out, stream=None):
+    return _check(_lib.bc_select_channels(_ptr(x), x.numel(), int(k), _ptr(idx_out), _stream(stream)),
+                  "bc_select_channels")
+
+
+def bc_sparse_gemv(wt, x, idx, k: int, y, ws, stream=None):
+    d_in, d_out = wt.shape
+    p, n = _ws(ws)
+    return _check(_lib.bc_sparse_gemv(_ptr(wt), d_in, d_out, _ptr(x), _ptr(idx), int(k), _ptr(y), p, n,
+                                      _stream(stream)), "bc_sparse_gemv")
+
+
+def bc_kv_score_select(q, summary, n_ctx: int, n_heads: int, n_kv_heads: int, head_dim: int,
+                       pol: bc_kv_policy, idx_out, scores_out=None, ws=None, stream=None):
+    nb_cap = summary.shape[1]
+    p, n = _ws(ws)
+    return _check(_lib.bc_kv_score_select(_ptr(q), _ptr(summary), nb_cap, int(n_ctx), int(n_heads), int(n_kv_heads),
+                                          int(head_dim), ctypes.byref(pol), _ptr(idx_out), _ptr(scores_out), p, n,
+                                          _stream(stream)), "bc_kv_score_select")
+
+
+def bc_build_kv_summary(k_cache, n_ctx: int, summary, stream=None):
+    n_kv, n_cap, hd = k_cache.shape
+    return _check(_lib.bc_build_kv_summary(_ptr(k_cache), n_kv, n_cap, hd, int(n_ctx), _ptr(summary),
+                                           _stream(stream)), "bc_build_kv_summary")
+
+
+def bc_splitk_attn_partial(q, k_cache, v_cache, idx, n_sel: int, n_heads: int, n_kv_heads: int, n_splits: int,
+                           scale: float, m, l, o, stream=None):
+    _, n_cap, hd = k_cache.shape
+    return _check(_lib.bc_splitk_attn_partial(_ptr(q), _ptr(k_cache), _ptr(v_cache), n_cap, _ptr(idx), int(n_sel),
+                                              int(n_heads), int(n_kv_heads), hd, int(n_splits), float(scale),
+                                              _ptr(m), _ptr(l), _ptr(o), _stream(stream)), "bc_splitk_attn_partial")
+
+
+def bc_splitk_reduce(m, l, o, out, stream=None):
+    n_heads, n_splits, hd = o.shape
+    return _check(_lib.bc_splitk_reduce(_ptr(m), _ptr(l), _ptr(o), n_heads, n_splits, hd, _ptr(out),
+                                        _stream(stream)), "bc_splitk_reduce")
+
+
+def bc_pack_gate_up(w_gate_t, w_up_t, w_gu, stream=None):
+    d, d_ff = w_gate_t.shape
+    return _check(_lib.bc_pack_gate_up(_ptr(w_gate_t), _ptr(w_up_t), d, d_ff, _ptr(w_gu), _stream(stream)),
+                  "bc_pack_gate_up")
+
+
+def make_layer(w_qkv, w_o, w_gu, w_down, g_attn, g_mlp, k_cache, v_cache, kv_summary=None) -> bc_layer:
+    return bc_layer(_ptr(w_qkv), _ptr(w_o), _ptr(w_gu), _ptr(w_down), _ptr(g_attn), _ptr(g_mlp), _ptr(k_cache),
+                    _ptr(v_cache), _ptr(kv_summary), int(k_cache.shape[1]))
+
+
+def make_taps(**bufs) -> bc_layer_taps:
+    return bc_layer_taps(**{k: _ptr(v) for k, v in bufs.items()})
+
+
+def make_step(n_ctx: int, r_p: float, pol: bc_kv_policy, n_splits: int = 0, rope_theta: float = 500000.0,
+              rms_eps: float = 1e-5, taps: bc_layer_taps | None = None) -> bc_step:
+    st = bc_step(int(n_ctx), float(r_p), pol, int(n_splits), float(rope_theta), float(rms_eps), None)
+    if taps is not None:
+        st.taps = ctypes.pointer(taps)
+    return st
+
+
+def bc_decode_layer(md: bc_model_dims, layer: bc_layer, step: bc_step, hidden, ws, stream=None):
+    p, n = _ws(ws)
+    return _check(_lib.bc_decode_layer(ctypes.byref(md), ctypes.byref(layer), ctypes.byref(step), _ptr(hidden), p,
+                                       n, _stream(stream)), "bc_decode_layer")
+
+
+def bc_lm_head(md: bc_model_dims, hidden, g_final, w_head_t, logits, token, rms_eps: float, ws, stream=None):
+    p, n = _ws(ws)
+    return _check(_lib.bc_lm_head(ctypes.byref(md), _ptr(hidden), _ptr(g_final), _ptr(w_head_t), _ptr(logits),
+                                  _ptr(token), float(rms_eps), p, n, _stream(stream)), "bc_lm_head")

@@ -1,0 +1,227 @@
+// bc_kv.hip -- attention-scored KV selection for gfx950.
+//
+// README "What it does in one picture": an attention-scored selection keeps
+// sinks, part of the history and the recent KV entries.  History is scored
+// per 16-token block with an upper bound of the query-key product built from
+// the block's per-dimension key minima and maxima (the query-aware block
+// bound of Quest, one of the paper's listed ancestors), summed over the
+// query heads that share the KV head.
+//
+// Summary layout: [n_kv_heads][n_cap/16][head_dim][2] bf16, (min, max) per
+// dim, so one 16-byte load gives 4 dims of a block.
+// Scoring: 32 lanes per block at head_dim 128 (16 at 64), lane p holds dims
+// 4p..4p+3 of every query head of the group; the fixed fp32 order is
+//   a_{j,p} = (t_{j,4p} + t_{j,4p+1}) + (t_{j,4p+2} + t_{j,4p+3}),
+//   c_p = adjacent-pair tree over j, s = adjacent-pair tree over p,
+// the last one being the xor-1,2,4,8,16 butterfly over the lanes.
+// Selection: one 1024-thread work-group per KV head, exact radix top-k on
+// order-preserving keys of the scores (equal scores: lower block), then the
+// list sinks | kept blocks' tokens | window is written in ascending order.
+#include <math.h>
+
+#include "bc_device.hpp"
+#include "bc_internal.hpp"
+
+namespace bc {
+
+namespace {
+
+constexpr int kScoreThreads = 256;
+constexpr int kScoreBlocksPerGroup = 64;
+constexpr int kSelThreads = 1024;
+
+template <int D, int G>
+__global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams p) {
+  constexpr int P = D / 4;            // lanes per candidate block
+  constexpr int CPW = kWave / P;      // candidate blocks per wave load
+  const int g = blockIdx.y;
+  const int lane = wave_lane(), w = wave_id();
+  const int cs = lane / P, pp = lane % P;
+  const int n_cand = p.bud.n_cand;
+
+  float qf[G][4];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    uint2 t = *reinterpret_cast<const uint2*>(p.q + size_t(g * G + j) * D + 4 * pp);
+    qf[j][0] = bf16_lo(t.x); qf[j][1] = bf16_hi(t.x);
+    qf[j][2] = bf16_lo(t.y); qf[j][3] = bf16_hi(t.y);
+  }
+  const int cbeg = blockIdx.x * kScoreBlocksPerGroup;
+  const int cend = min(n_cand, cbeg + kScoreBlocksPerGroup);
+  const uint16_t* sg = p.summary + size_t(g) * p.nb_cap * D * 2;
+  for (int cb = cbeg + w * CPW; cb < cend; cb += (kScoreThreads / kWave) * CPW) {
+    const int c = cb + cs;
+    const bool valid = c < cend;
+    const int b = p.bud.b_lo + (valid ? c : cbeg);
+    const uint4 mm = *reinterpret_cast<const uint4*>(sg + (size_t(b) * D + 4 * pp) * 2);
+    const float mn[4] = {bf16_lo(mm.x), bf16_lo(mm.y), bf16_lo(mm.z), bf16_lo(mm.w)};
+    const float mx[4] = {bf16_hi(mm.x), bf16_hi(mm.y), bf16_hi(mm.z), bf16_hi(mm.w)};
+    float a[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float t[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float x1 = qf[j][u] * mx[u];
+        const float x2 = qf[j][u] * mn[u];
+        t[u] = x1 > x2 ? x1 : x2;
+      }
+      a[j] = (t[0] + t[1]) + (t[2] + t[3]);
+    }
+#pragma unroll
+    for (int len = G; len > 1; len >>= 1)
+#pragma unroll
+      for (int i = 0; i < len / 2; ++i) a[i] = a[2 * i] + a[2 * i + 1];
+    float v = a[0];
+    v = v + dpp_f<kDppXor1>(v);
+    v = v + dpp_f<kDppXor2>(v);
+    v = v + dpp_f<kDppHalfMirror>(v);
+    v = v + dpp_f<kDppMirror>(v);
+    if constexpr (P == 32) v = v + __shfl_xor(v, 16, kWave);
+    if (valid && pp == 0) p.scores[size_t(g) * n_cand + c] = v;
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_kv_block_select(const KvSelectParams p) {
+  __shared__ TopkSmem<kSelThreads> sm;
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x;
+  const bc_kv_budget_info bd = p.bud;
+  int32_t* out = p.idx_out + size_t(g) * bd.t_sel;
+  const float* sc = p.scores + size_t(g) * bd.n_cand;
+  for (int t = tid; t < bd.sinks; t += kSelThreads) out[t] = t;
+  for (int t = tid; t < bd.window; t += kSelThreads) out[bd.t_sel - bd.window + t] = p.n_ctx - bd.window + t;
+  auto key = [sc](int i) -> uint32_t { return float_order_key(sc[i]); };
+  const int b_lo = bd.b_lo, sinks = bd.sinks;
+  auto emit = [out, b_lo, sinks](int rk, int i) {
+    int32_t* o = out + sinks + 16 * rk;
+    const int t0 = 16 * (b_lo + i);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) o[u] = t0 + u;
+  };
+  block_topk<kSelThreads, 32>(bd.n_cand, bd.k_blk, key, emit, sm);
+}
+
+// One wave per (block, KV head): per dim the min and max over the block's
+// tokens below n_ctx.
+__global__ __launch_bounds__(256) void k_build_summary(const uint16_t* k_cache, int n_cap, int head_dim, int n_ctx,
+                                                      uint16_t* summary) {
+  const int g = blockIdx.y;
+  const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nb = (n_ctx + 15) / 16;
+  if (blk >= nb) return;
+  const int lane = threadIdx.x & 63;
+  const int t0 = blk * 16, t1 = min(n_ctx, t0 + 16);
+  for (int d = lane; d < head_dim; d += kWave) {
+    const uint16_t* kc = k_cache + (size_t(g) * n_cap + t0) * head_dim + d;
+    uint16_t bmn = kc[0], bmx = kc[0];
+    float mn = bf16_to_f32(bmn), mx = mn;
+    for (int t = t0 + 1; t < t1; ++t) {
+      const uint16_t u = kc[size_t(t - t0) * head_dim];
+      const float f = bf16_to_f32(u);
+      if (f < mn) { mn = f; bmn = u; }
+      if (f > mx) { mx = f; bmx = u; }
+    }
+    uint16_t* sp = summary + ((size_t(g) * (n_cap / 16) + blk) * head_dim + d) * 2;
+    sp[0] = bmn;
+    sp[1] = bmx;
+  }
+}
+
+template <int D>
+int launch_score_d(const KvSelectParams& p, hipStream_t s) {
+  dim3 grid(ceil_div(p.bud.n_cand, kScoreBlocksPerGroup), p.n_kv_heads), block(kScoreThreads);
+  switch (p.n_heads / p.n_kv_heads) {
+    case 1: k_kv_score<D, 1><<<grid, block, 0, s>>>(p); break;
+    case 2: k_kv_score<D, 2><<<grid, block, 0, s>>>(p); break;
+    case 4: k_kv_score<D, 4><<<grid, block, 0, s>>>(p); break;
+    case 8: k_kv_score<D, 8><<<grid, block, 0, s>>>(p); break;
+    default: return set_error(BC_ERR_UNSUPPORTED, "kv score: group %d", p.n_heads / p.n_kv_heads);
+  }
+  return check_launch("k_kv_score");
+}
+
+}  // namespace
+
+int launch_kv_score_select(const KvSelectParams& p, hipStream_t s) {
+  if (p.bud.n_cand > 0 && p.bud.k_blk > 0) {
+    int rc = p.head_dim == 128 ? launch_score_d<128>(p, s)
+             : p.head_dim == 64 ? launch_score_d<64>(p, s)
+                                : set_error(BC_ERR_UNSUPPORTED, "kv score: head_dim %d", p.head_dim);
+    if (rc != BC_OK) return rc;
+  }
+  k_kv_block_select<<<dim3(p.n_kv_heads), dim3(kSelThreads), 0, s>>>(p);
+  return check_launch("k_kv_block_select");
+}
+
+}  // namespace bc
+
+using namespace bc;
+
+extern "C" int bc_kv_budget(int n_ctx, const bc_kv_policy* pol, bc_kv_budget_info* out) {
+  if (!pol || !out || n_ctx < 0) return set_error(BC_ERR_INVALID, "bc_kv_budget: bad arguments");
+  if (pol->block != 16) return set_error(BC_ERR_UNSUPPORTED, "bc_kv_budget: block must be 16");
+  if (pol->sinks < 0 || pol->window < 0 || !(pol->r_kv >= 0.0))
+    return set_error(BC_ERR_INVALID, "bc_kv_budget: sinks/window/r_kv out of range");
+  if (pol->r_kv >= 1.0) {
+    *out = bc_kv_budget_info{n_ctx, 0, 0, 0, 0, 0};
+    return BC_OK;
+  }
+  long long T = static_cast<long long>(floor(pol->r_kv * double(n_ctx) + 0.5));
+  if (T > n_ctx) T = n_ctx;
+  if (T < 0) T = 0;
+  const int t = static_cast<int>(T);
+  const int sp = pol->sinks < t ? pol->sinks : t;
+  const int wp = pol->window < t - sp ? pol->window : t - sp;
+  int kb = (t - sp - wp) / 16;
+  const int b_lo = (sp + 15) / 16;
+  const int b_hi = (n_ctx - wp) / 16;
+  const int nc = b_hi > b_lo ? b_hi - b_lo : 0;
+  if (kb > nc) kb = nc;
+  *out = bc_kv_budget_info{sp + wp + 16 * kb, kb, nc, b_lo, sp, wp};
+  return BC_OK;
+}
+
+extern "C" size_t bc_kv_score_select_workspace_bytes(int n_ctx, int n_kv_heads, const bc_kv_policy* pol) {
+  bc_kv_budget_info b;
+  if (n_kv_heads <= 0 || bc_kv_budget(n_ctx, pol, &b) != BC_OK) return 0;
+  return align_up(size_t(n_kv_heads) * (b.n_cand > 0 ? b.n_cand : 1) * 4, 256);
+}
+
+extern "C" int bc_kv_score_select(const uint16_t* q, const uint16_t* summary, int nb_cap, int n_ctx, int n_heads,
+                                  int n_kv_heads, int head_dim, const bc_kv_policy* pol, int32_t* idx_out,
+                                  float* scores_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !summary || !pol || !idx_out) return set_error(BC_ERR_INVALID, "bc_kv_score_select: NULL pointer");
+  if (n_heads <= 0 || n_kv_heads <= 0 || n_heads % n_kv_heads != 0)
+    return set_error(BC_ERR_INVALID, "bc_kv_score_select: heads %d / %d", n_heads, n_kv_heads);
+  if (!valid_head_dim(head_dim)) return set_error(BC_ERR_UNSUPPORTED, "head_dim %d", head_dim);
+  if (!valid_group(n_heads / n_kv_heads)) return set_error(BC_ERR_UNSUPPORTED, "group %d", n_heads / n_kv_heads);
+  if (n_ctx < 1 || nb_cap * 16 < n_ctx) return set_error(BC_ERR_INVALID, "bc_kv_score_select: n_ctx=%d nb_cap=%d", n_ctx, nb_cap);
+  if (pol->r_kv >= 1.0) return set_error(BC_ERR_INVALID, "bc_kv_score_select: r_kv >= 1 needs no selection");
+  bc_kv_budget_info b;
+  int rc = bc_kv_budget(n_ctx, pol, &b);
+  if (rc != BC_OK) return rc;
+  float* scores = scores_out;
+  if (scores == nullptr) {
+    size_t need = bc_kv_score_select_workspace_bytes(n_ctx, n_kv_heads, pol);
+    if (!ws || ws_bytes < need) return set_error(BC_ERR_WORKSPACE, "bc_kv_score_select: workspace %zu < %zu", ws_bytes, need);
+    scores = static_cast<float*>(ws);
+  }
+  KvSelectParams p{};
+  p.q = q; p.summary = summary; p.nb_cap = nb_cap; p.n_ctx = n_ctx; p.n_heads = n_heads;
+  p.n_kv_heads = n_kv_heads; p.head_dim = head_dim; p.bud = b; p.scores = scores; p.idx_out = idx_out;
+  return launch_kv_score_select(p, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int bc_build_kv_summary(const uint16_t* k_cache, int n_kv_heads, int n_cap, int head_dim, int n_ctx,
+                                   uint16_t* summary, void* stream) {
+  if (!k_cache || !summary) return set_error(BC_ERR_INVALID, "bc_build_kv_summary: NULL pointer");
+  if (n_kv_heads <= 0 || n_cap <= 0 || n_cap % 16 != 0 || n_ctx < 0 || n_ctx > n_cap)
+    return set_error(BC_ERR_INVALID, "bc_build_kv_summary: n_kv_heads=%d n_cap=%d n_ctx=%d", n_kv_heads, n_cap, n_ctx);
+  if (!valid_head_dim(head_dim)) return set_error(BC_ERR_UNSUPPORTED, "head_dim %d", head_dim);
+  const int nb = (n_ctx + 15) / 16;
+  if (nb == 0) return BC_OK;
+  k_build_summary<<<dim3(ceil_div(nb, 4), n_kv_heads), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      k_cache, n_cap, head_dim, n_ctx, summary);
+  return check_launch("k_build_summary");
+}

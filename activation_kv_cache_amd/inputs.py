@@ -94,3 +94,14 @@ def kv_cache(base_seed: int, dims: dict, n_cap: int, std: float, layer: int = 0)
 TINY = dict(d=512, n_heads=8, n_kv_heads=2, head_dim=64, d_ff=1408, vocab=1024, n_layers=1)
 LLAMA8B = dict(d=4096, n_heads=32, n_kv_heads=8, head_dim=128, d_ff=14336, vocab=128256,
                n_layers=32)
+
+
+def device_normal_bf16(base_seed: int, name: str, shape, std: float = 1.0, device="cuda"):
+    """Large seeded tensors drawn on the device (torch Philox generator seeded
+    from the same per-name child seed); returned as int16-viewed bf16."""
+    seed = int(_child_seed(base_seed, name).generate_state(1, dtype=np.uint64)[0] & 0x7FFFFFFFFFFFFFFF)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    t.normal_(0.0, std, generator=g)
+    return t.view(torch.int16)

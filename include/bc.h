@@ -1,0 +1,245 @@
+/*
+ * bc.h -- C ABI of libbc: one decode step of one sequence on an MI355X
+ * (gfx950): activation-sparse projection GEMV and split-K grouped-query
+ * decode attention over a KV cache that is read densely or through an
+ * attention-scored selection of sinks, history blocks and a recent window.
+ *
+ * Source of the method: "Where Activation Sparsity and KV-Cache Sparsity
+ * Cross in LLM Decoding" (ByteCross), GitHub README page.  Each entry point
+ * names the README section that defines what it computes.
+ *
+ * Conventions (all entry points)
+ *   - bf16 values are uint16_t bit patterns.  Every data pointer is a DEVICE
+ *     pointer owned by the caller, 16-byte aligned, contiguous in the layout
+ *     stated; the library never keeps a pointer after the call returns.
+ *   - No entry point allocates, frees or synchronises.  All work is enqueued
+ *     on `stream` (a hipStream_t passed as void*; NULL = the null stream).
+ *   - Return BC_OK (0) or a negative error code.  Arguments are checked on the
+ *     host before anything is enqueued; on error nothing is enqueued and
+ *     bc_last_error() returns a message (thread-local).  No exception crosses
+ *     the ABI.
+ *   - Index contents are not checked on the device: out-of-range channel or
+ *     token ids are undefined behaviour.
+ *   - Every count (k, T_sel, split sizes) is a function of host-known
+ *     scalars, so no call reads anything back from the device.
+ *   - Workspaces: a workspace is caller-owned device memory whose size comes
+ *     from the matching *_workspace_bytes query.  It must be cleared once with
+ *     bc_workspace_init after allocation; every call leaves it ready for the
+ *     next one.  Calls that share one workspace must not overlap in time.
+ */
+#ifndef BC_H
+#define BC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BC_ABI_VERSION 1
+
+enum {
+  BC_OK = 0,
+  BC_ERR_INVALID = -1,     /* NULL pointer, bad size, k out of range       */
+  BC_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, group size... */
+  BC_ERR_WORKSPACE = -3,   /* workspace smaller than the query returned    */
+  BC_ERR_HIP = -4          /* a HIP launch or runtime call failed          */
+};
+
+/* Decoder dimensions (README "Quick start": the config fields the byte
+ * account reads).  head_dim * n_heads must equal d (README FAQ).
+ * Supported here: head_dim in {64, 128}; n_heads / n_kv_heads in {1,2,4,8}. */
+typedef struct {
+  int n_layers, d, d_ff, vocab, n_heads, n_kv_heads, head_dim;
+} bc_model_dims;
+
+/* KV policy (README "What it does in one picture": the selection keeps
+ * sinks, part of the history and the recent entries).  r_kv >= 1 reads the
+ * whole cache.  block must be 16 (the summary granularity). */
+typedef struct {
+  double r_kv;
+  int sinks;
+  int window;
+  int block;
+} bc_kv_policy;
+
+/* Sizes of one KV selection, all host-computable:
+ *   T = min(n, floor(r_kv*n + 1/2)); sinks' = min(sinks, T);
+ *   window' = min(window, T - sinks'); candidates = the 16-aligned blocks that
+ *   lie wholly in [sinks', n - window'); k_blk = min(floor((T - sinks' -
+ *   window')/16), candidates); T_sel = sinks' + window' + 16*k_blk.
+ *   For r_kv >= 1: T_sel = n and nothing is scored. */
+typedef struct {
+  int t_sel, k_blk, n_cand, b_lo, sinks, window;
+} bc_kv_budget_info;
+
+int bc_abi_version(void);
+const char* bc_last_error(void);
+
+/* Number of kept channels: floor(r_p*d_in + 1/2) clamped to [1, d_in];
+ * r_p >= 1 keeps all d_in.  Returns the count (>0) or BC_ERR_INVALID. */
+int bc_channel_keep(double r_p, int d_in);
+
+/* Fills *out (see bc_kv_budget_info).  Returns BC_OK or BC_ERR_INVALID. */
+int bc_kv_budget(int n_ctx, const bc_kv_policy* pol, bc_kv_budget_info* out);
+
+/* Clears `bytes` bytes of a workspace with a fill kernel (no memset node,
+ * so it may be captured in a graph). */
+int bc_workspace_init(void* ws, size_t bytes, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* a1. Channel selection (README "What it does in one picture"; "Timing and
+ * quality on a GPU": activation sparsity on all seven projections).
+ * Exact top-k of |x| over x[0..d_in): the key of channel i is bits(x_i) &
+ * 0x7FFF; larger key first, equal keys by lower index; -0 and +0 tie.
+ * idx_out[0..k) receives the kept channels in ascending order.
+ * 1 <= k <= d_in <= 65536.  x: bf16 [d_in]; idx_out: int32 [k]. */
+int bc_select_channels(const uint16_t* x, int d_in, int k, int32_t* idx_out, void* stream);
+
+/* a2. Sparse projection GEMV (README "What it does": the activations select
+ * the weight columns that are read).  y[o] = sum_{j<k} W^T[idx_j][o] * x[idx_j]
+ * with fp32 accumulation, rounded to bf16 (nearest even).
+ *   wt  bf16 [d_in][d_out]  W transposed: row i is input channel i's weights
+ *   x   bf16 [d_in]
+ *   idx int32 [k] ascending channel ids, or NULL for the dense GEMV (k = d_in)
+ *   y   bf16 [d_out]
+ * d_out % 8 == 0.  ws/ws_bytes from bc_sparse_gemv_workspace_bytes(d_out, k).
+ * The sum over channels is split into fixed chunks and added in a fixed
+ * order, so results are deterministic run to run. */
+size_t bc_sparse_gemv_workspace_bytes(int d_out, int k);
+int bc_sparse_gemv(const uint16_t* wt, int d_in, int d_out, const uint16_t* x, const int32_t* idx,
+                   int k, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/* a4. Attention-scored KV selection (README "What it does": sinks, part of
+ * the history and the recent entries), scored per 16-token block by an upper
+ * bound of the query-key product built from per-block key minima and maxima.
+ * For KV head g and candidate block b (see bc_kv_budget_info):
+ *   t_{j,d} = max(q_{j,d}*kmax_{b,d}, q_{j,d}*kmin_{b,d})         (fp32, exact)
+ *   a_{j,p} = (t_{j,4p} + t_{j,4p+1}) + (t_{j,4p+2} + t_{j,4p+3})
+ *   c_p     = adjacent-pair tree over the group's heads j of a_{j,p}
+ *   s_{g,b} = adjacent-pair tree over p = 0..head_dim/4-1 of c_p
+ * (adjacent-pair tree: v_i <- v_{2i} + v_{2i+1} until one value remains;
+ * fp32 in exactly this order).  The k_blk highest scores are kept (equal
+ * scores: lower block); idx_out[g] = sinks, kept blocks' tokens and the
+ * window, ascending.
+ *   q        bf16 [n_heads][head_dim] post-rotary query; query head j reads
+ *            KV head j / (n_heads/n_kv_heads)
+ *   summary  bf16 [n_kv_heads][nb_cap][head_dim][2]  (min, max) per dim
+ *   idx_out  int32 [n_kv_heads][T_sel]
+ *   scores_out  optional fp32 [n_kv_heads][n_cand] (candidate order)
+ * Requires r_kv < 1 (the dense case needs no list).  ws from
+ * bc_kv_score_select_workspace_bytes. */
+size_t bc_kv_score_select_workspace_bytes(int n_ctx, int n_kv_heads, const bc_kv_policy* pol);
+int bc_kv_score_select(const uint16_t* q, const uint16_t* summary, int nb_cap, int n_ctx,
+                       int n_heads, int n_kv_heads, int head_dim, const bc_kv_policy* pol,
+                       int32_t* idx_out, float* scores_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Per-block key summaries of a pre-filled cache (setup, not timed):
+ * for every 16-token block holding tokens below n_ctx, per dim the min and
+ * max over those tokens.  k_cache bf16 [n_kv_heads][n_cap][head_dim];
+ * summary bf16 [n_kv_heads][n_cap/16][head_dim][2].  n_cap % 16 == 0. */
+int bc_build_kv_summary(const uint16_t* k_cache, int n_kv_heads, int n_cap, int head_dim, int n_ctx,
+                        uint16_t* summary, void* stream);
+
+/* a5. Split-K decode attention, partial pass (README "Overview": dense and
+ * sparse modes read their caches through the same split-K kernel).  For
+ * query head j (KV head g = j / (n_heads/n_kv_heads)) and split s covering
+ * list positions [s*c, min(n_sel, (s+1)*c)), c = ceil(n_sel/n_splits):
+ *   z_t = scale * (q_j . k_t); m = max z; l = sum e^(z-m); o = sum e^(z-m) v_t
+ * (m in natural-log units, o unnormalised; an empty split gives (-inf,0,0)).
+ *   q       bf16 [n_heads][head_dim]
+ *   k_cache, v_cache  bf16 [n_kv_heads][n_cap][head_dim]
+ *   idx     int32 [n_kv_heads][n_sel] token ids, or NULL for tokens 0..n_sel-1
+ *   m, l    fp32 [n_heads][n_splits];  o  fp32 [n_heads][n_splits][head_dim]
+ * 1 <= n_splits <= 4096. */
+int bc_splitk_attn_partial(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, int n_cap,
+                           const int32_t* idx, int n_sel, int n_heads, int n_kv_heads, int head_dim,
+                           int n_splits, float scale, float* m, float* l, float* o, void* stream);
+
+/* a6. Merge of the split partials (README "Overview", split-K attention):
+ * M = max_s m_s; out = sum_s o_s e^(m_s-M) / sum_s l_s e^(m_s-M), rounded to
+ * bf16; all splits empty gives 0.  out bf16 [n_heads][head_dim]. */
+int bc_splitk_reduce(const float* m, const float* l, const float* o, int n_heads, int n_splits,
+                     int head_dim, uint16_t* out, void* stream);
+
+/* Split count the library picks for n_sel listed tokens (used when a step
+ * passes n_splits = 0). */
+int bc_attn_default_splits(int n_sel, int n_kv_heads);
+
+/* ---------------------------------------------------------------------- */
+/* a7. One decoder layer of the decode step (README "Timing and quality on a
+ * GPU": TEAL on all seven projections, the cache read through split-K
+ * attention; the layer glue is the plain Llama reading):
+ *   x1 = RMSNorm(h)*g_attn; S1 = top-k(x1); [q k v] = W_qkv[:,S1] x1[S1];
+ *   rotary (rotate-half, theta) on q and k at position n_ctx-1; k, v written
+ *   to slot n_ctx-1 and that block's (min, max) summary recomputed;
+ *   L = KV selection (r_kv < 1) or tokens 0..n_ctx-1; a = attention(q, L);
+ *   S2 = top-k(a); h1 = h + W_o[:,S2] a[S2]; x2 = RMSNorm(h1)*g_mlp;
+ *   S3 = top-k(x2); f = SiLU(W_gate x2) * (W_up x2) over S3;
+ *   S4 = top-k(f); h = h1 + W_down[:,S4] f[S4].
+ * k = bc_channel_keep(r_p, d_in) per GEMV input; r_p >= 1 is dense. */
+typedef struct {
+  const uint16_t* w_qkv;   /* bf16 [d][n_heads*hd + 2*n_kv_heads*hd]  (q | k | v) */
+  const uint16_t* w_o;     /* bf16 [n_heads*hd][d] */
+  const uint16_t* w_gu;    /* bf16 [d][2*d_ff] from bc_pack_gate_up */
+  const uint16_t* w_down;  /* bf16 [d_ff][d] */
+  const uint16_t* g_attn;  /* bf16 [d] */
+  const uint16_t* g_mlp;   /* bf16 [d] */
+  uint16_t* k_cache;       /* bf16 [n_kv_heads][n_cap][hd] */
+  uint16_t* v_cache;       /* bf16 [n_kv_heads][n_cap][hd] */
+  uint16_t* kv_summary;    /* bf16 [n_kv_heads][n_cap/16][hd][2]; may be NULL when r_kv >= 1 */
+  int n_cap;               /* multiple of 16 */
+} bc_layer;
+
+/* Optional copies of every stage (device buffers, any may be NULL). */
+typedef struct {
+  uint16_t* x1;       /* [d] */
+  int32_t* idx_qkv;   /* [k_d] */
+  uint16_t* q;        /* [n_heads][hd] post-rotary */
+  uint16_t* k;        /* [n_kv_heads][hd] post-rotary */
+  uint16_t* v;        /* [n_kv_heads][hd] */
+  int32_t* idx_kv;    /* [n_kv_heads][T_sel] */
+  uint16_t* a;        /* [n_heads*hd] */
+  int32_t* idx_o;     /* [k_d] */
+  uint16_t* h_mid;    /* [d] */
+  uint16_t* x2;       /* [d] */
+  int32_t* idx_gu;    /* [k_d] */
+  uint16_t* hff;      /* [d_ff] */
+  int32_t* idx_down;  /* [k_ff] */
+} bc_layer_taps;
+
+typedef struct {
+  int n_ctx;           /* tokens attended, the current one included (1..n_cap) */
+  double r_p;          /* projection keep; >= 1 dense */
+  bc_kv_policy kv;     /* r_kv >= 1 dense */
+  int n_splits;        /* attention splits; 0 = bc_attn_default_splits */
+  double rope_theta;   /* e.g. 500000 */
+  double rms_eps;      /* e.g. 1e-5 */
+  const bc_layer_taps* taps;  /* optional */
+} bc_step;
+
+size_t bc_layer_workspace_bytes(const bc_model_dims* dims, int max_ctx, int max_splits);
+int bc_decode_layer(const bc_model_dims* dims, const bc_layer* layer, const bc_step* step,
+                    uint16_t* hidden, void* ws, size_t ws_bytes, void* stream);
+
+/* Packs W_gate^T and W_up^T (each bf16 [d][d_ff]) into the layout
+ * bc_decode_layer reads: per row, groups of up to 256 gate columns followed
+ * by the same up columns.  w_gu bf16 [d][2*d_ff].  (setup, not timed) */
+int bc_pack_gate_up(const uint16_t* w_gate_t, const uint16_t* w_up_t, int d, int d_ff, uint16_t* w_gu,
+                    void* stream);
+
+/* a8 tail. Final RMSNorm and the dense LM head of the step (the LM head is
+ * in the step's bytes: README "Quick start", the 1.60x bound):
+ * logits = W_head (RMSNorm(h)*g), token = argmax (lowest index on ties).
+ *   w_head_t bf16 [d][vocab]; logits fp32 [vocab]; token int32 [1]. */
+size_t bc_lm_head_workspace_bytes(const bc_model_dims* dims);
+int bc_lm_head(const bc_model_dims* dims, const uint16_t* hidden, const uint16_t* g_final,
+               const uint16_t* w_head_t, float* logits, int32_t* token, double rms_eps,
+               void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BC_H */

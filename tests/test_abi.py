@@ -1,0 +1,96 @@
+"""The C ABI library loads and exports every entry point include/bc.h declares;
+host-only queries agree with the oracle; argument errors are caught on the
+host before anything is enqueued.  No device compute here (CPU suite)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bc.h")
+LIB = os.path.join(ROOT, "activation_kv_cache_amd", "libbc.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bc_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def bc():
+    if not os.path.exists(LIB):
+        pytest.fail("libbc.so is not built: run __graft_entry__.build()")
+    from activation_kv_cache_amd import binding
+    return binding
+
+
+def test_header_declares_the_six_calls():
+    names = _declared()
+    for n in ("bc_select_channels", "bc_sparse_gemv", "bc_kv_score_select", "bc_splitk_attn_partial",
+              "bc_splitk_reduce", "bc_decode_layer"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(bc):
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(_declared()) == set(bc.EXPORTED)
+
+
+def test_abi_version(bc):
+    assert bc.bc_abi_version() == 1
+
+
+@pytest.mark.parametrize("r_p,d", [(0.5, 4096), (0.7, 4096), (0.7, 14336), (0.5, 1408), (1.0, 77), (0.0001, 77),
+                                   (0.25, 6), (0.3333, 1000)])
+def test_channel_keep_matches_oracle(bc, r_p, d):
+    assert bc.bc_channel_keep(r_p, d) == oracle.channel_keep(r_p, d)
+
+
+@pytest.mark.parametrize("n,r_kv,sinks,window", [(2048, 0.3, 4, 128), (131072, 0.3, 4, 1024),
+                                                 (131072, 0.5, 4, 1024), (2048, 0.3, 4, 1024),
+                                                 (1999, 0.4, 4, 100), (5, 0.5, 4, 16), (1, 0.1, 4, 1024),
+                                                 (4000, 1.0, 4, 1024), (3000, 0.0, 4, 16)])
+def test_kv_budget_matches_oracle(bc, n, r_kv, sinks, window):
+    got = bc.bc_kv_budget(n, bc.policy(r_kv, sinks, window))
+    ref = oracle.kv_budget(n, r_kv, sinks, window)
+    assert (got["t_sel"], got["k_blk"], got["n_cand"], got["b_lo"], got["sinks"], got["window"]) == (
+        ref["T_sel"], ref["k_blk"], ref["n_cand"], ref["b_lo"], ref["sinks"], ref["window"])
+
+
+def test_host_side_errors(bc):
+    lib = bc.library()
+    P = None
+    # NULL pointers, bad sizes, unsupported head_dim, small workspace: all rejected before any launch
+    assert lib.bc_select_channels(P, 10, 3, P, P) == bc.BC_ERR_INVALID
+    assert lib.bc_select_channels(1 << 20, 10, 11, 1 << 20, P) == bc.BC_ERR_INVALID
+    assert lib.bc_sparse_gemv(P, 10, 16, P, P, 10, P, P, 0, P) == bc.BC_ERR_INVALID
+    assert lib.bc_sparse_gemv(1 << 20, 10, 12, 1 << 20, P, 10, 1 << 20, 1 << 20, 1 << 20, P) == bc.BC_ERR_UNSUPPORTED
+    assert lib.bc_sparse_gemv(1 << 20, 64, 16, 1 << 20, P, 64, 1 << 20, 1 << 20, 1, P) == bc.BC_ERR_WORKSPACE
+    assert lib.bc_splitk_attn_partial(1 << 20, 1 << 20, 1 << 20, 64, P, 64, 8, 2, 96, 1, 0.1, 1 << 20, 1 << 20,
+                                      1 << 20, P) == bc.BC_ERR_UNSUPPORTED
+    assert lib.bc_splitk_attn_partial(1 << 20, 1 << 20, 1 << 20, 64, P, 65, 8, 2, 64, 1, 0.1, 1 << 20, 1 << 20,
+                                      1 << 20, P) == bc.BC_ERR_INVALID
+    assert lib.bc_splitk_reduce(1 << 20, 1 << 20, 1 << 20, 8, 0, 64, 1 << 20, P) == bc.BC_ERR_INVALID
+    pol = bc.policy(0.3, 4, 128, block=32)
+    out = bc.bc_kv_budget_info()
+    assert lib.bc_kv_budget(100, ctypes.byref(pol), ctypes.byref(out)) == bc.BC_ERR_UNSUPPORTED
+    assert "block" in lib.bc_last_error().decode()
+    md = bc.dims(dict(d=512, d_ff=1408, n_heads=8, n_kv_heads=2, head_dim=64))
+    assert bc.bc_layer_workspace_bytes(md, 2048, 8) > 0
+    bad = bc.dims(dict(d=500, d_ff=1408, n_heads=8, n_kv_heads=2, head_dim=64))
+    assert bc.bc_layer_workspace_bytes(bad, 2048, 8) == 0
+
+
+def test_workspace_queries_monotone(bc):
+    md = bc.dims(dict(d=4096, d_ff=14336, n_heads=32, n_kv_heads=8, head_dim=128, vocab=128256))
+    a = bc.bc_layer_workspace_bytes(md, 2048, 32)
+    b = bc.bc_layer_workspace_bytes(md, 131072, 128)
+    assert 0 < a < b < 64 << 20
+    assert bc.bc_sparse_gemv_workspace_bytes(28672, 4096) >= bc.bc_sparse_gemv_workspace_bytes(28672, 2048) > 0
+    assert bc.bc_lm_head_workspace_bytes(md) > 0

@@ -1,0 +1,202 @@
+"""GPU parity of the KV summaries and the attention-scored KV selection
+(bit-exact scores and index lists) and of split-K attention (partials and
+merged output within 2e-3 + 1e-2|ref|) against the CPU oracle, through the
+C ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from activation_kv_cache_amd import inputs as gen
+
+from gpu_util import assert_close, assert_close_bf16, dev, host, host_u16, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+def _bc():
+    from activation_kv_cache_amd import binding as bc
+    return bc
+
+
+def _summary_host(K, n, n_cap):
+    Hkv, _, D = K.shape
+    s = np.zeros((Hkv, n_cap // 16, D, 2), np.uint16)
+    for g in range(Hkv):
+        t = oracle.kv_summary(K[g], n)
+        s[g, :t.shape[0]] = t
+    return s
+
+
+@pytest.mark.parametrize("Hkv,n_cap,n,D", [(2, 2048, 2048, 64), (2, 2048, 1999, 64), (8, 8192, 8192, 128),
+                                            (8, 4096, 17, 128)])
+def test_build_summary_bit_exact(Hkv, n_cap, n, D):
+    bc = _bc()
+    K = gen.normal_bf16(1, f"sumk{n}", (Hkv, n_cap, D), 1.0)
+    s = torch.zeros((Hkv, n_cap // 16, D, 2), dtype=torch.int16, device="cuda")
+    bc.bc_build_kv_summary(dev(K), n, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(s), _summary_host(K, n, n_cap))
+
+
+KV_CASES = [
+    # (name, dims, n_cap, n, r_kv, sinks, window)
+    ("tiny-0.3", gen.TINY, 2048, 2048, 0.3, 4, 128),
+    ("tiny-ragged", gen.TINY, 2048, 1999, 0.4, 4, 100),
+    ("tiny-streaming", gen.TINY, 2048, 2048, 0.3, 4, 1024),
+    ("8b-2k-0.3", gen.LLAMA8B, 2048, 2048, 0.3, 4, 1024),
+    ("8b-8k-0.5", gen.LLAMA8B, 8192, 8192, 0.5, 4, 1024),
+    ("8b-32k-0.3", gen.LLAMA8B, 32768, 32768, 0.3, 4, 1024),
+    ("8b-128k-0.3", gen.LLAMA8B, 131072, 131072, 0.3, 4, 1024),
+    ("8b-128k-0.5", gen.LLAMA8B, 131072, 131072, 0.5, 4, 1024),
+]
+
+
+@pytest.mark.parametrize("name,dims,n_cap,n,r_kv,sinks,window", KV_CASES, ids=[c[0] for c in KV_CASES])
+def test_kv_score_select_bit_exact(name, dims, n_cap, n, r_kv, sinks, window):
+    bc = _bc()
+    H, Hkv, D = dims["n_heads"], dims["n_kv_heads"], dims["head_dim"]
+    q = gen.normal_bf16(2, f"kq{name}", (H, D))
+    nb = (n + 15) // 16
+    # summaries straight from the seeded generator: min <= max per dim
+    a = gen.normal_bf16(2, f"ka{name}", (Hkv, nb, D), 1.0)
+    b = gen.normal_bf16(2, f"kb{name}", (Hkv, nb, D), 1.0)
+    av, bv = oracle.bf16_to_f64(a), oracle.bf16_to_f64(b)
+    summ = np.zeros((Hkv, n_cap // 16, D, 2), np.uint16)
+    summ[:, :nb, :, 0] = np.where(av <= bv, a, b)
+    summ[:, :nb, :, 1] = np.where(av <= bv, b, a)
+    pol = bc.policy(r_kv, sinks, window)
+    bud = bc.bc_kv_budget(n, pol)
+    ref_bud = oracle.kv_budget(n, r_kv, sinks, window)
+    assert (bud["t_sel"], bud["k_blk"], bud["n_cand"]) == (ref_bud["T_sel"], ref_bud["k_blk"], ref_bud["n_cand"])
+    idx = torch.full((Hkv, bud["t_sel"]), -1, dtype=torch.int32, device="cuda")
+    scores = torch.empty((Hkv, max(bud["n_cand"], 1)), dtype=torch.float32, device="cuda")
+    bc.bc_kv_score_select(dev(q), dev(summ), n, H, Hkv, D, pol, idx, scores)
+    torch.cuda.synchronize()
+    ref_idx, ref_scores = oracle.kv_select(q, summ, n, H, Hkv, r_kv, sinks, window, want_scores=True)
+    if bud["n_cand"] > 0 and bud["k_blk"] > 0:
+        assert np.array_equal(host(scores)[:, :bud["n_cand"]].view(np.uint32), ref_scores.view(np.uint32)), \
+            "scores differ in bits"
+    assert np.array_equal(host(idx), ref_idx)
+
+
+def test_kv_select_ties_and_planted_block():
+    """Equal scores (identical summaries) are taken lowest block first; a
+    planted block aligned with the queries is always kept."""
+    bc = _bc()
+    dims = gen.LLAMA8B
+    H, Hkv, D, n, n_cap = 32, 8, 128, 8192, 8192
+    q = gen.normal_bf16(3, "tieq", (H, D))
+    row = gen.normal_bf16(3, "tierow", (D,))
+    summ = np.zeros((Hkv, n_cap // 16, D, 2), np.uint16)
+    summ[:, :, :, 0] = row
+    summ[:, :, :, 1] = row
+    planted = 300
+    qv = oracle.bf16_to_f64(q)
+    for g in range(Hkv):
+        direction = np.sign(qv[4 * g:4 * g + 4].sum(0))
+        summ[g, planted, :, 0] = oracle.f64_to_bf16(direction * 4.0)
+        summ[g, planted, :, 1] = oracle.f64_to_bf16(direction * 4.0)
+    pol = bc.policy(0.2, 4, 1024)
+    bud = bc.bc_kv_budget(n, pol)
+    idx = torch.full((Hkv, bud["t_sel"]), -1, dtype=torch.int32, device="cuda")
+    ws = workspace(bc.bc_kv_score_select_workspace_bytes(n, Hkv, pol))
+    bc.bc_kv_score_select(dev(q), dev(summ), n, H, Hkv, D, pol, idx, None, ws)
+    torch.cuda.synchronize()
+    got = host(idx)
+    assert np.array_equal(got, oracle.kv_select(q, summ, n, H, Hkv, 0.2, 4, 1024))
+    for g in range(Hkv):
+        assert set(range(16 * planted, 16 * planted + 16)) <= set(got[g].tolist())
+
+
+def _attn_inputs(name, dims, n_cap, std_k=1.0, std_v=1.0, planted=False):
+    H, Hkv, D = dims["n_heads"], dims["n_kv_heads"], dims["head_dim"]
+    q = gen.normal_bf16(4, f"aq{name}", (H, D))
+    K = gen.normal_bf16(4, f"ak{name}", (Hkv, n_cap, D), std_k)
+    V = gen.normal_bf16(4, f"av{name}", (Hkv, n_cap, D), std_v)
+    if planted:
+        # a few keys aligned with the query group give O(1) attention outputs
+        qv = oracle.bf16_to_f64(q)
+        rng = gen.rng(4, f"plant{name}")
+        for g in range(Hkv):
+            dirn = qv[g * (H // Hkv):(g + 1) * (H // Hkv)].sum(0)
+            dirn = dirn / np.linalg.norm(dirn) * 3.0 * math.sqrt(D) / 4
+            for t in rng.choice(n_cap, 8, replace=False):
+                K[g, t] = oracle.f64_to_bf16(dirn)
+    return q, K, V
+
+
+ATTN_CASES = [
+    # (name, dims, n_cap, n_sel, r_kv, n_splits, planted)
+    ("tiny-dense", gen.TINY, 2048, 2048, 1.0, 8, False),
+    ("tiny-dense-planted", gen.TINY, 2048, 2048, 1.0, 8, True),
+    ("tiny-sel", gen.TINY, 2048, 2048, 0.3, 8, True),
+    ("tiny-ragged-splits", gen.TINY, 2048, 1001, 1.0, 7, True),
+    ("tiny-one-split", gen.TINY, 2048, 333, 1.0, 1, True),
+    ("tiny-more-splits-than-rows", gen.TINY, 64, 5, 1.0, 16, False),
+    ("8b-2k-dense", gen.LLAMA8B, 2048, 2048, 1.0, 32, True),
+    ("8b-8k-sel", gen.LLAMA8B, 8192, 8192, 0.5, 0, True),
+    ("8b-32k-dense", gen.LLAMA8B, 32768, 32768, 1.0, 0, True),
+    ("8b-128k-dense", gen.LLAMA8B, 131072, 131072, 1.0, 0, True),
+    ("8b-128k-sel", gen.LLAMA8B, 131072, 131072, 0.3, 0, True),
+]
+
+
+@pytest.mark.parametrize("name,dims,n_cap,n,r_kv,S,planted", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_splitk_attention_vs_oracle(name, dims, n_cap, n, r_kv, S, planted):
+    bc = _bc()
+    H, Hkv, D = dims["n_heads"], dims["n_kv_heads"], dims["head_dim"]
+    q, K, V = _attn_inputs(name, dims, n_cap, planted=planted)
+    if r_kv < 1:
+        summ = _summary_host(K, n, n_cap)
+        lst = oracle.kv_select(q, summ, n, H, Hkv, r_kv, 4, 1024 if D == 128 else 128)
+        n_sel = lst.shape[1]
+    else:
+        lst, n_sel = None, n
+    if S == 0:
+        S = bc.bc_attn_default_splits(n_sel, Hkv)
+    m = torch.empty((H, S), dtype=torch.float32, device="cuda")
+    l = torch.empty((H, S), dtype=torch.float32, device="cuda")
+    o = torch.empty((H, S, D), dtype=torch.float32, device="cuda")
+    out = torch.empty((H, D), dtype=torch.int16, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    bc.bc_splitk_attn_partial(dev(q), dev(K), dev(V), None if lst is None else dev(lst), n_sel, H, Hkv, S, scale,
+                              m, l, o)
+    bc.bc_splitk_reduce(m, l, o, out)
+    torch.cuda.synchronize()
+    rm, rl, ro = oracle.attn_partial(q, K, V, lst, n_sel, H, Hkv, S, scale)
+    ref64, _ = oracle.attn_reduce(rm, rl, ro)
+    gm, gl, go = host(m), host(l), host(o)
+    empty = np.isneginf(rm)
+    assert np.array_equal(np.isneginf(gm), empty)
+    assert np.all(gl[empty] == 0) and np.all(go[empty] == 0)
+    ne = ~empty
+    assert_close(gm[ne], rm[ne], "m", atol=1e-4, rtol=1e-5)
+    assert_close(gl[ne], rl[ne], "l", atol=1e-5, rtol=1e-4)
+    assert_close((go / np.where(gl > 0, gl, 1)[..., None])[ne], (ro / np.where(rl > 0, rl, 1)[..., None])[ne], "o/l")
+    rel = assert_close_bf16(host_u16(out), ref64, name)
+    assert rel < 1e-2, f"rel-L2 {rel}"
+
+
+def test_dense_attention_equals_identity_list():
+    """idx = NULL and idx = 0..n-1 read the same rows through the same kernel: bit-identical."""
+    bc = _bc()
+    dims = gen.LLAMA8B
+    H, Hkv, D, n = 32, 8, 128, 4096
+    q, K, V = _attn_inputs("ident", dims, n)
+    S = bc.bc_attn_default_splits(n, Hkv)
+    outs = []
+    for lst in (None, np.tile(np.arange(n, dtype=np.int32), (Hkv, 1))):
+        m = torch.empty((H, S), dtype=torch.float32, device="cuda")
+        l = torch.empty_like(m)
+        o = torch.empty((H, S, D), dtype=torch.float32, device="cuda")
+        out = torch.empty((H, D), dtype=torch.int16, device="cuda")
+        bc.bc_splitk_attn_partial(dev(q), dev(K), dev(V), None if lst is None else dev(lst), n, H, Hkv, S,
+                                  1 / math.sqrt(D), m, l, o)
+        bc.bc_splitk_reduce(m, l, o, out)
+        outs.append((m, l, o, out))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

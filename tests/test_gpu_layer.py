@@ -1,0 +1,160 @@
+"""GPU parity of the whole decoder layer (bc_decode_layer) and the LM head
+against the CPU oracle.
+
+Stage by stage with teacher forcing: the oracle recomputes every stage from
+the GPU's own inputs to that stage (taps), so selections are compared bit for
+bit and floating-point stages within 2e-3 + 1e-2|ref|.  With both keeps at 1
+the layer is also compared end to end without forcing."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from activation_kv_cache_amd import inputs as gen
+
+from gpu_util import assert_close, assert_close_bf16, dev, host, host_u16, workspace
+
+pytestmark = pytest.mark.gpu
+
+FP_STAGES = ("x1", "q", "k", "v", "a", "h_mid", "x2", "hff", "h_out")
+IDX_STAGES = ("idx_qkv", "idx_kv", "idx_o", "idx_gu", "idx_down")
+
+
+def _bc():
+    from activation_kv_cache_amd import binding as bc
+    return bc
+
+
+def _run_layer(dims, n_cap, n, r_p, r_kv, sinks, window, n_splits, seed, k_std=0.02, plant=False):
+    bc = _bc()
+    H, Hkv, D, d, dff = dims["n_heads"], dims["n_kv_heads"], dims["head_dim"], dims["d"], dims["d_ff"]
+    W = gen.layer_weights(seed, dims)
+    K, V = gen.kv_cache(seed, dims, n_cap, k_std)
+    h = gen.activation_bf16(seed, "h0", d)
+    summ = np.zeros((Hkv, n_cap // 16, D, 2), np.uint16)
+    for g in range(Hkv):
+        s = oracle.kv_summary(K[g], n - 1)
+        summ[g, :s.shape[0]] = s
+    w = {k: dev(v) for k, v in W.items()}
+    w_gu = torch.empty((d, 2 * dff), dtype=torch.int16, device="cuda")
+    bc.bc_pack_gate_up(w["gate"], w["up"], w_gu)
+    kc, vc, sm, hh = dev(K), dev(V), dev(summ), dev(h)
+    md = bc.dims(dims)
+    pol = bc.policy(r_kv, sinks, window)
+    bud = bc.bc_kv_budget(n, pol)
+    n_sel = bud["t_sel"]
+    S = n_splits or bc.bc_attn_default_splits(n_sel, Hkv)
+    ws = workspace(bc.bc_layer_workspace_bytes(md, n_cap, S))
+    k_d, k_ff = oracle.channel_keep(r_p, d), oracle.channel_keep(r_p, dff)
+    i16, i32 = torch.int16, torch.int32
+    sizes = {"x1": (d, i16), "idx_qkv": (k_d, i32), "q": (H * D, i16), "k": (Hkv * D, i16), "v": (Hkv * D, i16),
+             "idx_kv": (Hkv * n_sel, i32), "a": (H * D, i16), "idx_o": (k_d, i32), "h_mid": (d, i16),
+             "x2": (d, i16), "idx_gu": (k_d, i32), "hff": (dff, i16), "idx_down": (k_ff, i32)}
+    taps = {k: torch.full((n,), -1, dtype=t, device="cuda") for k, (n, t) in sizes.items()}
+    layer = bc.make_layer(w["qkv"], w["o"], w_gu, w["down"], w["g1"], w["g2"], kc, vc, sm)
+    step = bc.make_step(n, r_p, pol, S, taps=bc.make_taps(**taps))
+    bc.bc_decode_layer(md, layer, step, hh, ws)
+    torch.cuda.synchronize()
+    got = {}
+    for k, t in taps.items():
+        got[k] = host(t) if t.dtype == torch.int32 else host_u16(t)
+    got["h_out"] = host_u16(hh)
+    got["K"], got["V"], got["summ"] = host_u16(kc), host_u16(vc), host_u16(sm)
+    return W, K, V, h, summ, got, S
+
+
+def _shape_forced(got, dims, r_p, r_kv):
+    H, Hkv, D = dims["n_heads"], dims["n_kv_heads"], dims["head_dim"]
+    f = {k: got[k] for k in ("x1", "a", "h_mid", "x2", "hff")}
+    f["q"] = got["q"].reshape(H, D)
+    f["k"] = got["k"].reshape(Hkv, D)
+    f["v"] = got["v"].reshape(Hkv, D)
+    if r_p < 1:
+        for k in ("idx_qkv", "idx_o", "idx_gu", "idx_down"):
+            f[k] = got[k]
+    if r_kv < 1:
+        f["idx_kv"] = got["idx_kv"].reshape(Hkv, -1)
+    return f
+
+
+LAYER_CASES = [
+    # (name, dims, n_cap, n, r_p, r_kv, sinks, window, n_splits)
+    ("tiny-dense", gen.TINY, 2048, 2048, 1.0, 1.0, 4, 128, 8),
+    ("tiny-proj", gen.TINY, 2048, 2048, 0.5, 1.0, 4, 128, 8),
+    ("tiny-kv", gen.TINY, 2048, 2048, 1.0, 0.3, 4, 128, 8),
+    ("tiny-both", gen.TINY, 2048, 2048, 0.5, 0.3, 4, 128, 8),
+    ("tiny-ragged-ctx", gen.TINY, 2064, 2051, 0.7, 0.3, 4, 128, 5),
+    ("tiny-first-token", gen.TINY, 64, 1, 0.5, 1.0, 4, 128, 1),
+    ("8b-2k-dense", gen.LLAMA8B, 2048, 2048, 1.0, 1.0, 4, 1024, 0),
+    ("8b-2k-both-0.5-0.3", gen.LLAMA8B, 2048, 2048, 0.5, 0.3, 4, 1024, 0),
+    ("8b-8k-both-0.7-0.3", gen.LLAMA8B, 8192, 8192, 0.7, 0.3, 4, 1024, 0),
+]
+
+
+@pytest.mark.parametrize("name,dims,n_cap,n,r_p,r_kv,sinks,window,S", LAYER_CASES, ids=[c[0] for c in LAYER_CASES])
+def test_decode_layer_teacher_forced(name, dims, n_cap, n, r_p, r_kv, sinks, window, S):
+    W, K, V, h, summ, got, S = _run_layer(dims, n_cap, n, r_p, r_kv, sinks, window, S, seed=9)
+    forced = _shape_forced(got, dims, r_p, r_kv)
+    Ko, Vo, so = K.copy(), V.copy(), summ.copy()
+    ref = oracle.decode_layer(h, W, Ko, Vo, so, n, dims, r_p, r_kv, sinks, window, S, forced=forced)
+    for st in IDX_STAGES:
+        if ref.get(st) is None:
+            continue
+        assert np.array_equal(got[st].reshape(ref[st].shape), ref[st]), f"{name}: {st} differs"
+    for st in FP_STAGES:
+        r = ref[st]
+        assert_close_bf16(got[st], oracle.bf16_to_f64(r), f"{name}: {st}")
+    # the cache holds the GPU's new row and the refreshed summary matches the oracle's
+    assert np.array_equal(got["K"][:, n - 1], forced["k"]) and np.array_equal(got["V"][:, n - 1], forced["v"])
+    assert np.array_equal(got["summ"], so)
+
+
+@pytest.mark.parametrize("dims,n_cap,n", [(gen.TINY, 2048, 2048), (gen.LLAMA8B, 2048, 2048)], ids=["tiny", "8b-2k"])
+def test_dense_layer_end_to_end(dims, n_cap, n):
+    W, K, V, h, summ, got, S = _run_layer(dims, n_cap, n, 1.0, 1.0, 4, 1024, 0, seed=10)
+    ref = oracle.decode_layer(h, W, K.copy(), V.copy(), summ.copy(), n, dims, 1.0, 1.0, 4, 1024, S)
+    rel = assert_close_bf16(got["h_out"], oracle.bf16_to_f64(ref["h_out"]), "h_out")
+    assert rel < 1e-2
+
+
+def test_lm_head_tiny():
+    bc = _bc()
+    dims = dict(gen.TINY, vocab=1000)
+    d, V = dims["d"], dims["vocab"]
+    h = gen.activation_bf16(12, "lmh", d)
+    g = gen.to_bf16_bits(np.ones(d, np.float32))
+    wt = gen.normal_bf16(12, "lmw", (d, V), 0.02)
+    md = bc.dims(dims)
+    ws = workspace(bc.bc_lm_head_workspace_bytes(md))
+    logits = torch.empty(V, dtype=torch.float32, device="cuda")
+    tok = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    bc.bc_lm_head(md, dev(h), dev(g), dev(wt), logits, tok, 1e-5, ws)
+    torch.cuda.synchronize()
+    _, y64, arg = oracle.lm_head(h, g, wt)
+    lg = host(logits)
+    assert_close(lg, y64, "logits")
+    assert int(host(tok)[0]) == int(np.argmax(lg))
+    assert y64[int(host(tok)[0])] >= y64[arg] - 1e-2
+
+
+def test_lm_head_8b_sampled():
+    """Full 8B head (4096 x 128256, 1.05 GB): logits checked at sampled columns."""
+    bc = _bc()
+    dims = gen.LLAMA8B
+    d, V = dims["d"], dims["vocab"]
+    h = gen.activation_bf16(13, "lmh8", d)
+    g = gen.to_bf16_bits(np.ones(d, np.float32))
+    wt = gen.device_normal_bf16(13, "lmw8", (d, V), 0.02)
+    md = bc.dims(dims)
+    ws = workspace(bc.bc_lm_head_workspace_bytes(md))
+    logits = torch.empty(V, dtype=torch.float32, device="cuda")
+    tok = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    bc.bc_lm_head(md, dev(h), dev(g), wt, logits, tok, 1e-5, ws)
+    torch.cuda.synchronize()
+    cols = np.sort(gen.rng(13, "lmcols").choice(V, 2048, replace=False))
+    sub = host_u16(wt[:, torch.from_numpy(cols).cuda()].contiguous())
+    x = oracle.rmsnorm(h, g)
+    y64, _ = oracle.sparse_gemv(sub, x)
+    lg = host(logits)
+    assert_close(lg[cols], y64, "sampled logits")
+    assert int(host(tok)[0]) == int(np.argmax(lg))
