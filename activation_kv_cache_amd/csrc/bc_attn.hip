@@ -14,9 +14,8 @@
 // work-group are merged through LDS at the end.  In index mode the split's
 // slice of the index list is staged in LDS.
 //
-// Merge pass: M = max m_s, out = sum o_s e^(m_s-M) / sum l_s e^(m_s-M);
-// optionally the last work-group selects the top-k channels of the output
-// for the next GEMV.
+// Merge pass: M = max m_s, out = sum o_s e^(m_s-M) / sum l_s e^(m_s-M),
+// one thread per (head, dim).
 #include <math.h>
 
 #include "bc_device.hpp"
@@ -176,52 +175,29 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
   }
 }
 
-struct ReduceSmem {
-  union {
-    TopkSmem<kAttnThreads> topk;
-  } u;
-  int flag;
-};
-
 __global__ __launch_bounds__(kAttnThreads) void k_attn_reduce(const ReduceParams p) {
-  __shared__ ReduceSmem sm;
   const int tid = threadIdx.x;
   const int D = p.head_dim;
   const int heads_per_block = kAttnThreads / D;
   const int j = blockIdx.x * heads_per_block + tid / D;
   const int d = tid % D;
-  if (j < p.n_heads) {
-    const float* mj = p.m + size_t(j) * p.n_splits;
-    const float* lj = p.l + size_t(j) * p.n_splits;
-    const float* oj = p.o + size_t(j) * p.n_splits * D + d;
-    float M = -INFINITY;
-    for (int s = 0; s < p.n_splits; ++s) M = fmaxf(M, mj[s]);
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < p.n_splits; ++s) {
-        const float ms = mj[s];
-        if (ms == -INFINITY) continue;
-        const float wgt = expf(ms - M);
-        num += oj[size_t(s) * D] * wgt;
-        den += lj[s] * wgt;
-      }
+  if (j >= p.n_heads) return;
+  const float* mj = p.m + size_t(j) * p.n_splits;
+  const float* lj = p.l + size_t(j) * p.n_splits;
+  const float* oj = p.o + size_t(j) * p.n_splits * D + d;
+  float M = -INFINITY;
+  for (int s = 0; s < p.n_splits; ++s) M = fmaxf(M, mj[s]);
+  float num = 0.f, den = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < p.n_splits; ++s) {
+      const float ms = mj[s];
+      if (ms == -INFINITY) continue;
+      const float wgt = expf(ms - M);
+      num += oj[size_t(s) * D] * wgt;
+      den += lj[s] * wgt;
     }
-    p.out[size_t(j) * D + d] = f32_to_bf16(den > 0.f ? num / den : 0.f);
   }
-  if (p.counters == nullptr) return;
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) sm.flag = atomicAdd(p.counters, 1u) == gridDim.x - 1;
-  __syncthreads();
-  if (!sm.flag) return;
-  __threadfence();
-  if (tid == 0) *p.counters = 0u;
-  const int n = p.n_heads * D;
-  const uint16_t* x = p.out;
-  int32_t* idx_out = p.tail_idx_out;
-  auto key = [x](int i) -> uint32_t { return uint32_t(x[i]) & 0x7FFFu; };
-  auto emit = [idx_out](int rk, int i) { idx_out[rk] = i; };
-  block_topk<kAttnThreads, 15>(n, p.tail_k, key, emit, sm.u.topk);
+  p.out[size_t(j) * D + d] = f32_to_bf16(den > 0.f ? num / den : 0.f);
 }
 
 template <int D>
@@ -299,6 +275,6 @@ extern "C" int bc_splitk_reduce(const float* m, const float* l, const float* o, 
   if (!valid_head_dim(head_dim)) return set_error(BC_ERR_UNSUPPORTED, "head_dim %d", head_dim);
   ReduceParams p{};
   p.m = m; p.l = l; p.o = o; p.n_heads = n_heads; p.n_splits = n_splits; p.head_dim = head_dim;
-  p.out = out; p.counters = nullptr;
+  p.out = out;
   return launch_attn_reduce(p, static_cast<hipStream_t>(stream));
 }

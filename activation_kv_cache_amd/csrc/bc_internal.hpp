@@ -17,18 +17,17 @@ int check_launch(const char* what);
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-constexpr int kGemvTile = 512;   // output columns per work-group (64 lanes x 8)
+constexpr int kGemvTile = 128;   // output columns per work-group (16 lanes x 8)
 constexpr int kGemvThreads = 256;
 
-enum Epi : int { EPI_BF16 = 0, EPI_F32_ARGMAX = 1, EPI_RESID = 2, EPI_QKV = 3, EPI_SWIGLU = 4 };
-enum Tail : int { TAIL_NONE = 0, TAIL_SELECT = 1, TAIL_NORM_SELECT = 2, TAIL_ARGMAX = 3 };
+enum GemvMode : int { MAIN_PARTIAL = 0, MAIN_BF16 = 1, MAIN_F32_ARGMAX = 2 };
+enum FinishKind : int { FIN_BF16 = 0, FIN_QKV = 1, FIN_RESID = 2, FIN_SWIGLU = 3 };
 
 struct GemvPlan {
   int n_tiles;
   int n_splits;
   int rows_per_split;
-  size_t counter_bytes;   // (n_tiles + 1) uint32, 256-aligned
-  size_t partial_bytes;   // n_splits * d_out fp32 when n_splits > 1
+  size_t partial_bytes;   // n_splits * d_out fp32
 };
 GemvPlan plan_gemv(int d_out, int k);
 
@@ -39,34 +38,36 @@ struct GemvParams {
   const int32_t* idx;
   int k;
   int rows_per_split, n_splits, n_tiles;
-  float* partial;
-  uint32_t* counters;     // n_tiles + 1, zero on entry, zero on exit
-  // epilogues
-  uint16_t* y;
-  float* yf;
-  const uint16_t* resid;
+  float* partial;         // MAIN_PARTIAL: [n_splits][d_out]
+  uint16_t* y;            // MAIN_BF16
+  float* yf;              // MAIN_F32_ARGMAX
+  float* tile_max;
+  int32_t* tile_arg;
+};
+int launch_gemv_main(int mode, const GemvParams& p, hipStream_t s);
+
+struct FinishParams {
+  const float* partial;
+  int n_splits, d_out;
+  uint16_t* y;                  // bf16 output (d_out, or d_ff for SwiGLU)
+  const uint16_t* resid;        // FIN_RESID: optional residual
+  const uint16_t* norm_gain;    // FIN_RESID: RMSNorm gain of the next input (optional)
+  float eps;
+  uint16_t* x_next;             // FIN_RESID: RMSNorm output
+  int sel_k;                    // top-k of the next input when 0 < sel_k < n
+  int32_t* idx_next;
+  // FIN_QKV
   uint16_t* q_out;
   uint16_t* k_cache;
   uint16_t* v_cache;
   uint16_t* summary;
   int n_heads, n_kv_heads, head_dim, n_cap, pos;
-  float pad0;
   double theta;
+  // FIN_SWIGLU
   int d_ff;
-  float* tile_max;
-  int32_t* tile_arg;
-  int32_t* token_out;
-  // tail (run once by the last work-group to finish)
-  int tail;
-  const uint16_t* tail_in;
-  int tail_n;
-  const uint16_t* tail_gain;
-  float tail_eps;
-  uint16_t* tail_x_out;
-  int tail_k;
-  int32_t* tail_idx_out;
 };
-int launch_gemv(int epi, const GemvParams& p, hipStream_t s);
+int launch_finish(int kind, const FinishParams& p, hipStream_t s);
+int launch_argmax_finish(const float* tile_max, const int32_t* tile_arg, int n_tiles, int32_t* token, hipStream_t s);
 
 struct AttnParams {
   const uint16_t* q;
@@ -88,9 +89,6 @@ struct ReduceParams {
   const float* o;
   int n_heads, n_splits, head_dim;
   uint16_t* out;
-  uint32_t* counters;     // 1 word; only with a select tail
-  int tail_k;             // select top-k of out (n_heads*head_dim) when 0 < tail_k < n
-  int32_t* tail_idx_out;
 };
 int launch_attn_reduce(const ReduceParams& p, hipStream_t s);
 

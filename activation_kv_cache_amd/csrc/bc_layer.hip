@@ -1,15 +1,18 @@
 // bc_layer.hip -- one decoder layer of the decode step, the LM head, and the
 // small entry points of libbc (errors, budgets, workspace, packing).
 //
-// bc_decode_layer enqueues, on one stream and with no host synchronisation:
-//   1. k_norm_select     x1 = RMSNorm(h); S1 = top-k(x1)           (1 work-group)
-//   2. k_gemv<QKV>       q,k,v over S1; rotary; append k,v; refresh the block summary
-//   3. k_kv_score, k_kv_block_select  (r_kv < 1 only)
-//   4. k_attn_partial    split-K partials over the list (or 0..n-1)
-//   5. k_attn_reduce     merge; its last work-group selects S2 = top-k(a)
-//   6. k_gemv<RESID>     h1 = h + W_o a over S2; tail: x2 = RMSNorm(h1), S3
-//   7. k_gemv<SWIGLU>    f = SiLU(gate) * up over S3; tail: S4 = top-k(f)
-//   8. k_gemv<RESID>     h = h1 + W_down f over S4
+// bc_decode_layer enqueues, on one stream and with no host synchronisation
+// (kernel boundaries are the only cross-work-group synchronisation):
+//   k_norm_select          x1 = RMSNorm(h) * g_attn; S1 = top-k(x1)      (1 work-group)
+//   k_gemv_main, k_finish_qkv   q, k, v over S1; rotary; append k, v at slot
+//                          n-1; refresh that block's (min, max) summary
+//   k_kv_score, k_kv_block_select   KV list (r_kv < 1 only)
+//   k_attn_partial, k_attn_reduce   split-K attention -> a
+//   k_select               S2 = top-k(a)                                 (sparse only)
+//   k_gemv_main, k_finish_resid     h1 = h + W_o a over S2; x2 = RMSNorm(h1) * g_mlp;
+//                          S3 = top-k(x2)                                (finish: 1 work-group)
+//   k_gemv_main, k_finish_swiglu    f = SiLU(gate) * up over S3; S4 = top-k(f)
+//   k_gemv_main, k_finish_resid     h = h1 + W_down f over S4
 // Every launch size depends only on host-known scalars.
 #include <math.h>
 #include <stdarg.h>
@@ -22,7 +25,6 @@ namespace bc {
 
 namespace {
 thread_local char g_err[512] = "";
-constexpr int kOneGroupThreads = 1024;
 }  // namespace
 
 int set_error(int code, const char* fmt, ...) {
@@ -43,41 +45,6 @@ bool valid_head_dim(int hd) { return hd == 64 || hd == 128; }
 bool valid_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
 namespace {
-
-__global__ __launch_bounds__(kOneGroupThreads) void k_norm_select(const uint16_t* h, const uint16_t* g, int d,
-                                                                 float eps, uint16_t* x_out, int k,
-                                                                 int32_t* idx_out) {
-  __shared__ TopkSmem<kOneGroupThreads> sm;
-  __shared__ float part[kOneGroupThreads / kWave];
-  const int tid = threadIdx.x;
-  float s = 0.f;
-  for (int i = tid; i < d; i += kOneGroupThreads) {
-    const float v = bf16_to_f32(h[i]);
-    s += v * v;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, kWave);
-  if (wave_lane() == 0) part[tid >> 6] = s;
-  __syncthreads();
-  float ss = 0.f;
-#pragma unroll
-  for (int w = 0; w < kOneGroupThreads / kWave; ++w) ss += part[w];
-  const float inv = 1.0f / sqrtf(ss / float(d) + eps);
-  for (int i = tid; i < d; i += kOneGroupThreads)
-    x_out[i] = f32_to_bf16(bf16_to_f32(h[i]) * inv * bf16_to_f32(g[i]));
-  __syncthreads();
-  if (idx_out == nullptr || k >= d) return;
-  auto key = [x_out](int i) -> uint32_t { return uint32_t(x_out[i]) & 0x7FFFu; };
-  auto emit = [idx_out](int r, int i) { idx_out[r] = i; };
-  block_topk<kOneGroupThreads, 15>(d, k, key, emit, sm);
-}
-
-__global__ __launch_bounds__(kOneGroupThreads) void k_select(const uint16_t* x, int n, int k, int32_t* idx_out) {
-  __shared__ TopkSmem<kOneGroupThreads> sm;
-  auto key = [x](int i) -> uint32_t { return uint32_t(x[i]) & 0x7FFFu; };
-  auto emit = [idx_out](int r, int i) { idx_out[r] = i; };
-  block_topk<kOneGroupThreads, 15>(n, k, key, emit, sm);
-}
 
 __global__ void k_fill_zero(uint4* p, size_t n16, uint8_t* tail, size_t ntail) {
   const size_t stride = size_t(gridDim.x) * blockDim.x;
@@ -101,11 +68,9 @@ __global__ __launch_bounds__(256) void k_pack_gate_up(const uint16_t* gate, cons
 
 // ------------------------------------------------------------ layer layout
 struct LayerLayout {
-  size_t counters, partial, x1, idx_qkv, q, scores, idx_kv, m, l, o, a, idx_o, h_mid, x2, idx_gu, hff, idx_down;
+  size_t partial, x1, idx_qkv, q, scores, idx_kv, m, l, o, a, idx_o, h_mid, x2, idx_gu, hff, idx_down;
   size_t total;
 };
-constexpr int kCounterSlots = 5;      // qkv, o, gate|up, down, attention merge
-constexpr int kCounterWords = 1024;
 
 size_t gemv_partial_max(const bc_model_dims& m) {
   const int qkv = m.n_heads * m.head_dim + 2 * m.n_kv_heads * m.head_dim;
@@ -125,7 +90,6 @@ LayerLayout layer_layout(const bc_model_dims& m, int n_ctx, int n_splits) {
   auto take = [&off](size_t bytes) { size_t o = off; off += align_up(bytes > 0 ? bytes : 1, 256); return o; };
   const int hd = m.head_dim, H = m.n_heads, Hkv = m.n_kv_heads;
   const int nb = (n_ctx + 15) / 16;
-  L.counters = take(size_t(kCounterSlots) * kCounterWords * 4);
   L.partial = take(gemv_partial_max(m));
   L.x1 = take(size_t(m.d) * 2);
   L.idx_qkv = take(size_t(m.d) * 4);
@@ -169,17 +133,6 @@ int copy_tap(void* dst, const void* src, size_t bytes, hipStream_t s) {
 }
 
 }  // namespace
-
-int launch_norm_select(const uint16_t* h, const uint16_t* g, int d, float eps, uint16_t* x_out, int k,
-                       int32_t* idx_out, hipStream_t s) {
-  k_norm_select<<<1, kOneGroupThreads, 0, s>>>(h, g, d, eps, x_out, k, idx_out);
-  return check_launch("k_norm_select");
-}
-
-int launch_select(const uint16_t* x, int n, int k, int32_t* idx_out, hipStream_t s) {
-  k_select<<<1, kOneGroupThreads, 0, s>>>(x, n, k, idx_out);
-  return check_launch("k_select");
-}
 
 int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s) {
   const size_t n16 = bytes / 16;
@@ -235,6 +188,26 @@ extern "C" size_t bc_layer_workspace_bytes(const bc_model_dims* dims, int max_ct
   return layer_layout(*dims, max_ctx, max_splits).total;
 }
 
+namespace {
+
+// One projection: main kernel (chunk partials) and its finish.
+int run_gemv(const uint16_t* wt, int d_in, int d_out, const uint16_t* x, const int32_t* idx, int k, float* partial,
+             int fin_kind, FinishParams f, hipStream_t s) {
+  const GemvPlan pl = plan_gemv(d_out, k);
+  GemvParams p{};
+  p.wt = wt; p.d_in = d_in; p.d_out = d_out; p.x = x; p.idx = idx; p.k = k;
+  p.rows_per_split = pl.rows_per_split; p.n_splits = pl.n_splits; p.n_tiles = pl.n_tiles;
+  p.partial = partial;
+  int rc = launch_gemv_main(MAIN_PARTIAL, p, s);
+  if (rc != BC_OK) return rc;
+  f.partial = partial;
+  f.n_splits = pl.n_splits;
+  f.d_out = d_out;
+  return launch_finish(fin_kind, f, s);
+}
+
+}  // namespace
+
 extern "C" int bc_decode_layer(const bc_model_dims* dims, const bc_layer* ly, const bc_step* st, uint16_t* hidden,
                                void* ws, size_t ws_bytes, void* stream) {
   int rc = check_dims(dims);
@@ -256,7 +229,7 @@ extern "C" int bc_decode_layer(const bc_model_dims* dims, const bc_layer* ly, co
   const bc_model_dims& m = *dims;
   const int hd = m.head_dim, H = m.n_heads, Hkv = m.n_kv_heads;
   const int n_sel = kv_sparse ? bud.t_sel : st->n_ctx;
-  int n_splits = st->n_splits > 0 ? st->n_splits : bc_attn_default_splits(n_sel, Hkv);
+  const int n_splits = st->n_splits > 0 ? st->n_splits : bc_attn_default_splits(n_sel, Hkv);
   if (n_splits > 4096) return set_error(BC_ERR_INVALID, "bc_decode_layer: n_splits=%d", n_splits);
   const LayerLayout L = layer_layout(m, st->n_ctx, n_splits);
   if (ws_bytes < L.total) return set_error(BC_ERR_WORKSPACE, "bc_decode_layer: workspace %zu < %zu", ws_bytes, L.total);
@@ -268,32 +241,27 @@ extern "C" int bc_decode_layer(const bc_model_dims* dims, const bc_layer* ly, co
   const int k_ff = bc_channel_keep(st->r_p, m.d_ff);
   const int qkv_out = H * hd + 2 * Hkv * hd;
   const int pos = st->n_ctx - 1;
-  uint32_t* counters = at<uint32_t>(ws, L.counters);
   float* partial = at<float>(ws, L.partial);
   const float eps = float(st->rms_eps);
+  int32_t* idx_qkv = sparse ? at<int32_t>(ws, L.idx_qkv) : nullptr;
+  int32_t* idx_o = sparse ? at<int32_t>(ws, L.idx_o) : nullptr;
+  int32_t* idx_gu = sparse ? at<int32_t>(ws, L.idx_gu) : nullptr;
+  int32_t* idx_down = sparse ? at<int32_t>(ws, L.idx_down) : nullptr;
 
-  // 1. x1 = RMSNorm(h), S1
-  rc = launch_norm_select(hidden, ly->g_attn, m.d, eps, at<uint16_t>(ws, L.x1), k_d,
-                          sparse ? at<int32_t>(ws, L.idx_qkv) : nullptr, s);
+  // x1 = RMSNorm(h), S1
+  rc = launch_norm_select(hidden, ly->g_attn, m.d, eps, at<uint16_t>(ws, L.x1), k_d, idx_qkv, s);
   if (rc != BC_OK) return rc;
 
-  // 2. q, k, v; rotary; append; summary
+  // q, k, v; rotary; append; summary
   {
-    GemvPlan pl = plan_gemv(qkv_out, k_d);
-    GemvParams p{};
-    p.wt = ly->w_qkv; p.d_in = m.d; p.d_out = qkv_out; p.x = at<uint16_t>(ws, L.x1);
-    p.idx = sparse ? at<int32_t>(ws, L.idx_qkv) : nullptr; p.k = k_d;
-    p.rows_per_split = pl.rows_per_split; p.n_splits = pl.n_splits; p.n_tiles = pl.n_tiles;
-    p.partial = partial; p.counters = counters + 0 * kCounterWords;
-    p.q_out = at<uint16_t>(ws, L.q); p.k_cache = ly->k_cache; p.v_cache = ly->v_cache;
-    p.summary = ly->kv_summary;
-    p.n_heads = H; p.n_kv_heads = Hkv; p.head_dim = hd; p.n_cap = ly->n_cap; p.pos = pos;
-    p.theta = st->rope_theta;
-    p.tail = TAIL_NONE;
-    if ((rc = launch_gemv(EPI_QKV, p, s)) != BC_OK) return rc;
+    FinishParams f{};
+    f.q_out = at<uint16_t>(ws, L.q); f.k_cache = ly->k_cache; f.v_cache = ly->v_cache; f.summary = ly->kv_summary;
+    f.n_heads = H; f.n_kv_heads = Hkv; f.head_dim = hd; f.n_cap = ly->n_cap; f.pos = pos; f.theta = st->rope_theta;
+    rc = run_gemv(ly->w_qkv, m.d, qkv_out, at<uint16_t>(ws, L.x1), idx_qkv, k_d, partial, FIN_QKV, f, s);
+    if (rc != BC_OK) return rc;
   }
 
-  // 3. KV selection
+  // KV selection
   if (kv_sparse) {
     KvSelectParams p{};
     p.q = at<uint16_t>(ws, L.q); p.summary = ly->kv_summary; p.nb_cap = ly->n_cap / 16; p.n_ctx = st->n_ctx;
@@ -302,7 +270,7 @@ extern "C" int bc_decode_layer(const bc_model_dims* dims, const bc_layer* ly, co
     if ((rc = launch_kv_score_select(p, s)) != BC_OK) return rc;
   }
 
-  // 4-5. attention; S2 = top-k(a)
+  // attention; S2 = top-k(a)
   {
     AttnParams p{};
     p.q = at<uint16_t>(ws, L.q); p.k_cache = ly->k_cache; p.v_cache = ly->v_cache; p.n_cap = ly->n_cap;
@@ -314,93 +282,69 @@ extern "C" int bc_decode_layer(const bc_model_dims* dims, const bc_layer* ly, co
     ReduceParams r{};
     r.m = p.m; r.l = p.l; r.o = p.o; r.n_heads = H; r.n_splits = n_splits; r.head_dim = hd;
     r.out = at<uint16_t>(ws, L.a);
-    r.counters = sparse ? counters + 4 * kCounterWords : nullptr;
-    r.tail_k = k_d; r.tail_idx_out = at<int32_t>(ws, L.idx_o);
     if ((rc = launch_attn_reduce(r, s)) != BC_OK) return rc;
+    if (sparse && k_d < H * hd && (rc = launch_select(at<uint16_t>(ws, L.a), H * hd, k_d, idx_o, s)) != BC_OK)
+      return rc;
   }
 
-  // 6. h1 = h + W_o a; tail: x2 = RMSNorm(h1), S3
+  // h1 = h + W_o a; x2 = RMSNorm(h1); S3
   {
-    GemvPlan pl = plan_gemv(m.d, k_d);
-    GemvParams p{};
-    p.wt = ly->w_o; p.d_in = H * hd; p.d_out = m.d; p.x = at<uint16_t>(ws, L.a);
-    p.idx = sparse ? at<int32_t>(ws, L.idx_o) : nullptr; p.k = k_d;
-    p.rows_per_split = pl.rows_per_split; p.n_splits = pl.n_splits; p.n_tiles = pl.n_tiles;
-    p.partial = partial; p.counters = counters + 1 * kCounterWords;
-    p.y = at<uint16_t>(ws, L.h_mid); p.resid = hidden;
-    p.tail = TAIL_NORM_SELECT; p.tail_in = at<uint16_t>(ws, L.h_mid); p.tail_n = m.d; p.tail_gain = ly->g_mlp;
-    p.tail_eps = eps; p.tail_x_out = at<uint16_t>(ws, L.x2); p.tail_k = sparse ? k_d : m.d;
-    p.tail_idx_out = at<int32_t>(ws, L.idx_gu);
-    if ((rc = launch_gemv(EPI_RESID, p, s)) != BC_OK) return rc;
+    FinishParams f{};
+    f.y = at<uint16_t>(ws, L.h_mid); f.resid = hidden; f.norm_gain = ly->g_mlp; f.eps = eps;
+    f.x_next = at<uint16_t>(ws, L.x2); f.sel_k = sparse ? k_d : 0; f.idx_next = idx_gu;
+    rc = run_gemv(ly->w_o, H * hd, m.d, at<uint16_t>(ws, L.a), idx_o, k_d, partial, FIN_RESID, f, s);
+    if (rc != BC_OK) return rc;
   }
 
-  // 7. f = SiLU(gate) * up; tail: S4
+  // f = SiLU(gate) * up; S4
   {
-    GemvPlan pl = plan_gemv(2 * m.d_ff, k_d);
-    GemvParams p{};
-    p.wt = ly->w_gu; p.d_in = m.d; p.d_out = 2 * m.d_ff; p.x = at<uint16_t>(ws, L.x2);
-    p.idx = sparse ? at<int32_t>(ws, L.idx_gu) : nullptr; p.k = k_d;
-    p.rows_per_split = pl.rows_per_split; p.n_splits = pl.n_splits; p.n_tiles = pl.n_tiles;
-    p.partial = partial; p.counters = counters + 2 * kCounterWords;
-    p.y = at<uint16_t>(ws, L.hff); p.d_ff = m.d_ff;
-    if (sparse) {
-      p.tail = TAIL_SELECT; p.tail_in = at<uint16_t>(ws, L.hff); p.tail_n = m.d_ff; p.tail_k = k_ff;
-      p.tail_idx_out = at<int32_t>(ws, L.idx_down);
-    } else {
-      p.tail = TAIL_NONE;
-    }
-    if ((rc = launch_gemv(EPI_SWIGLU, p, s)) != BC_OK) return rc;
+    FinishParams f{};
+    f.y = at<uint16_t>(ws, L.hff); f.d_ff = m.d_ff; f.sel_k = sparse ? k_ff : 0; f.idx_next = idx_down;
+    rc = run_gemv(ly->w_gu, m.d, 2 * m.d_ff, at<uint16_t>(ws, L.x2), idx_gu, k_d, partial, FIN_SWIGLU, f, s);
+    if (rc != BC_OK) return rc;
   }
 
-  // 8. h = h1 + W_down f
+  // h = h1 + W_down f
   {
-    GemvPlan pl = plan_gemv(m.d, k_ff);
-    GemvParams p{};
-    p.wt = ly->w_down; p.d_in = m.d_ff; p.d_out = m.d; p.x = at<uint16_t>(ws, L.hff);
-    p.idx = sparse ? at<int32_t>(ws, L.idx_down) : nullptr; p.k = k_ff;
-    p.rows_per_split = pl.rows_per_split; p.n_splits = pl.n_splits; p.n_tiles = pl.n_tiles;
-    p.partial = partial; p.counters = counters + 3 * kCounterWords;
-    p.y = hidden; p.resid = at<uint16_t>(ws, L.h_mid);
-    p.tail = TAIL_NONE;
-    if ((rc = launch_gemv(EPI_RESID, p, s)) != BC_OK) return rc;
+    FinishParams f{};
+    f.y = hidden; f.resid = at<uint16_t>(ws, L.h_mid);
+    rc = run_gemv(ly->w_down, m.d_ff, m.d, at<uint16_t>(ws, L.hff), idx_down, k_ff, partial, FIN_RESID, f, s);
+    if (rc != BC_OK) return rc;
   }
 
   if (const bc_layer_taps* t = st->taps) {
-    const size_t qb = size_t(H) * hd * 2, kvb = size_t(Hkv) * hd * 2;
+    const size_t qb = size_t(H) * hd * 2;
     if ((rc = copy_tap(t->x1, at<void>(ws, L.x1), size_t(m.d) * 2, s)) != BC_OK) return rc;
-    if (sparse && (rc = copy_tap(t->idx_qkv, at<void>(ws, L.idx_qkv), size_t(k_d) * 4, s)) != BC_OK) return rc;
+    if (sparse && (rc = copy_tap(t->idx_qkv, idx_qkv, size_t(k_d) * 4, s)) != BC_OK) return rc;
     if ((rc = copy_tap(t->q, at<void>(ws, L.q), qb, s)) != BC_OK) return rc;
     for (int g = 0; g < Hkv && (t->k || t->v); ++g) {
       const size_t src = (size_t(g) * ly->n_cap + pos) * hd;
       if (t->k && (rc = copy_tap(t->k + size_t(g) * hd, ly->k_cache + src, size_t(hd) * 2, s)) != BC_OK) return rc;
       if (t->v && (rc = copy_tap(t->v + size_t(g) * hd, ly->v_cache + src, size_t(hd) * 2, s)) != BC_OK) return rc;
     }
-    (void)kvb;
     if (kv_sparse && (rc = copy_tap(t->idx_kv, at<void>(ws, L.idx_kv), size_t(Hkv) * n_sel * 4, s)) != BC_OK) return rc;
     if ((rc = copy_tap(t->a, at<void>(ws, L.a), qb, s)) != BC_OK) return rc;
-    if (sparse && (rc = copy_tap(t->idx_o, at<void>(ws, L.idx_o), size_t(k_d) * 4, s)) != BC_OK) return rc;
+    if (sparse && (rc = copy_tap(t->idx_o, idx_o, size_t(k_d) * 4, s)) != BC_OK) return rc;
     if ((rc = copy_tap(t->h_mid, at<void>(ws, L.h_mid), size_t(m.d) * 2, s)) != BC_OK) return rc;
     if ((rc = copy_tap(t->x2, at<void>(ws, L.x2), size_t(m.d) * 2, s)) != BC_OK) return rc;
-    if (sparse && (rc = copy_tap(t->idx_gu, at<void>(ws, L.idx_gu), size_t(k_d) * 4, s)) != BC_OK) return rc;
+    if (sparse && (rc = copy_tap(t->idx_gu, idx_gu, size_t(k_d) * 4, s)) != BC_OK) return rc;
     if ((rc = copy_tap(t->hff, at<void>(ws, L.hff), size_t(m.d_ff) * 2, s)) != BC_OK) return rc;
-    if (sparse && (rc = copy_tap(t->idx_down, at<void>(ws, L.idx_down), size_t(k_ff) * 4, s)) != BC_OK) return rc;
+    if (sparse && (rc = copy_tap(t->idx_down, idx_down, size_t(k_ff) * 4, s)) != BC_OK) return rc;
   }
   return BC_OK;
 }
 
 // ------------------------------------------------------------------ LM head
 namespace {
-struct HeadLayout { size_t counters, partial, x, tile_max, tile_arg, total; };
+struct HeadLayout { size_t x, logits_tile_max, tile_arg, total; };
 HeadLayout head_layout(const bc_model_dims& m) {
-  GemvPlan pl = plan_gemv(m.vocab, m.d);
+  const int n_tiles = ceil_div(m.vocab, kGemvTile);
   HeadLayout L;
   size_t off = 0;
   auto take = [&off](size_t bytes) { size_t o = off; off += align_up(bytes > 0 ? bytes : 1, 256); return o; };
-  L.counters = take(pl.counter_bytes);
-  L.partial = take(pl.partial_bytes);
   L.x = take(size_t(m.d) * 2);
-  L.tile_max = take(size_t(pl.n_tiles) * 4);
-  L.tile_arg = take(size_t(pl.n_tiles) * 4);
+  L.logits_tile_max = take(size_t(n_tiles) * 4);
+  L.tile_arg = take(size_t(n_tiles) * 4);
   L.total = off;
   return L;
 }
@@ -424,12 +368,10 @@ extern "C" int bc_lm_head(const bc_model_dims* dims, const uint16_t* hidden, con
   hipStream_t s = static_cast<hipStream_t>(stream);
   rc = launch_norm_select(hidden, g_final, dims->d, float(rms_eps), at<uint16_t>(ws, L.x), dims->d, nullptr, s);
   if (rc != BC_OK) return rc;
-  GemvPlan pl = plan_gemv(dims->vocab, dims->d);
   GemvParams p{};
   p.wt = w_head_t; p.d_in = dims->d; p.d_out = dims->vocab; p.x = at<uint16_t>(ws, L.x); p.idx = nullptr;
-  p.k = dims->d; p.rows_per_split = pl.rows_per_split; p.n_splits = pl.n_splits; p.n_tiles = pl.n_tiles;
-  p.partial = at<float>(ws, L.partial); p.counters = at<uint32_t>(ws, L.counters);
-  p.yf = logits; p.tile_max = at<float>(ws, L.tile_max); p.tile_arg = at<int32_t>(ws, L.tile_arg);
-  p.token_out = token; p.tail = TAIL_ARGMAX;
-  return launch_gemv(EPI_F32_ARGMAX, p, s);
+  p.k = dims->d; p.rows_per_split = dims->d; p.n_splits = 1; p.n_tiles = ceil_div(dims->vocab, kGemvTile);
+  p.yf = logits; p.tile_max = at<float>(ws, L.logits_tile_max); p.tile_arg = at<int32_t>(ws, L.tile_arg);
+  if ((rc = launch_gemv_main(MAIN_F32_ARGMAX, p, s)) != BC_OK) return rc;
+  return launch_argmax_finish(p.tile_max, p.tile_arg, p.n_tiles, token, s);
 }

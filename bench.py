@@ -1,0 +1,400 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark at Llama-3.1-8B dimensions on one MI355X.
+
+A step is one full decode step of one sequence: 32 x bc_decode_layer
+(activation-sparse projection GEMVs and split-K attention over the KV cache,
+read densely or through the scored selection) + final RMSNorm + dense LM
+head + argmax, captured once as a HIP graph and replayed.  Weights are random
+N(0, 0.02), the KV cache N(0, 1) pre-filled to 131072 tokens, the hidden
+input N(0, 1) with 1% outlier channels x10; all drawn on the device from
+seeded generators.  The context is held fixed: every step writes the new
+token at slot n-1 again.
+
+The headline line is the dense step at 131072 tokens (r_p = r_kv = 1):
+value = algorithmic bytes of the step / step time.  The other cells (modes
+and contexts) are reported under "cells".  Algorithmic bytes per step:
+  r_p-weighted projection weights + LM head + 4096 B x L x T_sel (K and V)
+  + [KV selection] 256 B x L x n (block summaries) + index lists, partials.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-step µs and achieved HBM GB/s vs context 2K–128K, Llama-3.1-8B dims"
+HBM_PEAK_GBS = 8000.0
+DIMS = dict(n_layers=32, d=4096, d_ff=14336, vocab=128256, n_heads=32, n_kv_heads=8, head_dim=128)
+SINKS, WINDOW = 4, 1024
+KERNEL_SOURCES = ["activation_kv_cache_amd/csrc/bc_attn.hip", "activation_kv_cache_amd/csrc/bc_device.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ byte account
+def channel_keep(r_p, n):
+    return n if r_p >= 1 else max(1, min(n, int(math.floor(r_p * n + 0.5))))
+
+
+def gemv_bytes(d_in, d_out, k, sparse):
+    b = 2 * k * d_out + 2 * d_out + 2 * (k if sparse else d_in)
+    return b + (4 * k if sparse else 0)
+
+
+def attn_bytes(n_sel, S, sparse):
+    D = DIMS
+    kv = 2 * D["n_kv_heads"] * D["head_dim"] * 2 * n_sel
+    part = D["n_heads"] * S * (D["head_dim"] + 2) * 4
+    return kv + part + (4 * D["n_kv_heads"] * n_sel if sparse else 0)
+
+
+def layer_bytes(n, r_p, r_kv, t_sel, S):
+    D = DIMS
+    d, dff, H, Hkv, hd = D["d"], D["d_ff"], D["n_heads"], D["n_kv_heads"], D["head_dim"]
+    sp = r_p < 1
+    kd, kf = channel_keep(r_p, d), channel_keep(r_p, dff)
+    b = gemv_bytes(d, H * hd + 2 * Hkv * hd, kd, sp)
+    b += gemv_bytes(H * hd, d, kd, sp)
+    b += gemv_bytes(d, 2 * dff, kd, sp)
+    b += gemv_bytes(dff, d, kf, sp)
+    b += attn_bytes(t_sel, S, r_kv < 1)
+    if r_kv < 1:
+        b += 2 * Hkv * hd * 2 * ((n + 15) // 16) + 4 * Hkv * t_sel
+    return b
+
+
+def step_bytes(n, r_p, r_kv, t_sel, S):
+    D = DIMS
+    return D["n_layers"] * layer_bytes(n, r_p, r_kv, t_sel, S) + 2 * D["d"] * D["vocab"] + 4 * D["vocab"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------- model
+class Model:
+    def __init__(self, max_ctx, seed=0):
+        from activation_kv_cache_amd import binding as bc
+        from activation_kv_cache_amd import inputs as gen
+
+        self.bc = bc
+        D = DIMS
+        d, dff, H, Hkv, hd, L = D["d"], D["d_ff"], D["n_heads"], D["n_kv_heads"], D["head_dim"], D["n_layers"]
+        self.max_ctx = max_ctx
+        self.md = bc.dims(D)
+        t0 = time.time()
+        one = torch.full((d,), 1.0, dtype=torch.bfloat16, device="cuda").view(torch.int16)
+        self.g_attn, self.g_mlp, self.g_final = one, one.clone(), one.clone()
+        self.layers = []
+        for li in range(L):
+            p = f"layer{li}/"
+            w_qkv = gen.device_normal_bf16(seed, p + "wqkv", (d, H * hd + 2 * Hkv * hd), 0.02)
+            w_o = gen.device_normal_bf16(seed, p + "wo", (H * hd, d), 0.02)
+            gate = gen.device_normal_bf16(seed, p + "wgate", (d, dff), 0.02)
+            up = gen.device_normal_bf16(seed, p + "wup", (d, dff), 0.02)
+            w_gu = torch.empty((d, 2 * dff), dtype=torch.int16, device="cuda")
+            bc.bc_pack_gate_up(gate, up, w_gu)
+            del gate, up
+            w_down = gen.device_normal_bf16(seed, p + "wdown", (dff, d), 0.02)
+            k = gen.device_normal_bf16(seed, p + "kcache", (Hkv, max_ctx, hd), 1.0)
+            v = gen.device_normal_bf16(seed, p + "vcache", (Hkv, max_ctx, hd), 1.0)
+            summ = torch.empty((Hkv, max_ctx // 16, hd, 2), dtype=torch.int16, device="cuda")
+            bc.bc_build_kv_summary(k, max_ctx, summ)
+            self.layers.append(dict(w_qkv=w_qkv, w_o=w_o, w_gu=w_gu, w_down=w_down, k=k, v=v, summ=summ))
+        self.w_head = gen.device_normal_bf16(seed, "lm_head", (d, D["vocab"]), 0.02)
+        h0 = gen.activation_bf16(seed, "h0", d)
+        self.h0 = torch.from_numpy(h0.view(np.int16)).cuda()
+        self.h = torch.empty_like(self.h0)
+        self.logits = torch.empty(D["vocab"], dtype=torch.float32, device="cuda")
+        self.token = torch.empty(1, dtype=torch.int32, device="cuda")
+        self.ws = torch.empty(bc.bc_layer_workspace_bytes(self.md, max_ctx, 1024) // 4 + 64, dtype=torch.int32,
+                              device="cuda")
+        self.ws_head = torch.empty(bc.bc_lm_head_workspace_bytes(self.md) // 4 + 64, dtype=torch.int32,
+                                   device="cuda")
+        bc.bc_workspace_init(self.ws)
+        bc.bc_workspace_init(self.ws_head)
+        self.c_layers = [bc.make_layer(l["w_qkv"], l["w_o"], l["w_gu"], l["w_down"], self.g_attn, self.g_mlp,
+                                       l["k"], l["v"], l["summ"]) for l in self.layers]
+        torch.cuda.synchronize()
+        log(f"[bench] model ready in {time.time() - t0:.1f}s; "
+            f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
+
+    def plan(self, n, r_p, r_kv):
+        bc = self.bc
+        pol = bc.policy(r_kv, SINKS, WINDOW)
+        t_sel = bc.bc_kv_budget(n, pol)["t_sel"]
+        S = bc.bc_attn_default_splits(t_sel, DIMS["n_kv_heads"])
+        return pol, t_sel, S
+
+    def step(self, n, r_p, r_kv):
+        bc = self.bc
+        pol, _, S = self.plan(n, r_p, r_kv)
+        st = bc.make_step(n, r_p, pol, S)
+        self.h.copy_(self.h0)
+        for cl in self.c_layers:
+            bc.bc_decode_layer(self.md, cl, st, self.h, self.ws)
+        bc.bc_lm_head(self.md, self.h, self.g_final, self.w_head, self.logits, self.token, 1e-5, self.ws_head)
+
+    def graph(self, n, r_p, r_kv):
+        self.step(n, r_p, r_kv)          # eager once: validates arguments outside capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(n, r_p, r_kv)
+        torch.cuda.synchronize()
+        return g
+
+
+def time_graph(g, steps, warmup):
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        g.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def time_attention_kernel(model, n, reps=3):
+    """Average duration of bc_splitk_attn_partial over the 32 layers' caches
+    (one launch per layer, as in the step), timed with events on the stream
+    the kernels are launched on."""
+    bc = model.bc
+    D = DIMS
+    H, Hkv, hd = D["n_heads"], D["n_kv_heads"], D["head_dim"]
+    S = bc.bc_attn_default_splits(n, Hkv)
+    q = torch.randn((H, hd), dtype=torch.bfloat16, device="cuda").view(torch.int16)
+    m = torch.empty((H, S), dtype=torch.float32, device="cuda")
+    l = torch.empty_like(m)
+    o = torch.empty((H, S, hd), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(hd)
+    for ly in model.layers[:4]:
+        bc.bc_splitk_attn_partial(q, ly["k"], ly["v"], None, n, H, Hkv, S, scale, m, l, o)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        for ly in model.layers:
+            bc.bc_splitk_attn_partial(q, ly["k"], ly["v"], None, n, H, Hkv, S, scale, m, l, o)
+    e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / (reps * len(model.layers))
+    return us, attn_bytes(n, S, False), S
+
+
+def time_gemv_kernel(model, which="w_gu", r_p=1.0, reps=3):
+    """Average duration of one bc_sparse_gemv launch over the 32 layers'
+    matrices (dense or top-k channels of a fixed input)."""
+    bc = model.bc
+    from activation_kv_cache_amd import inputs as gen
+    w0 = model.layers[0][which]
+    d_in, d_out = w0.shape
+    k = channel_keep(r_p, d_in)
+    x = torch.from_numpy(gen.activation_bf16(1, "gemvx", d_in).view(np.int16)).cuda()
+    idx = None
+    if r_p < 1:
+        idx = torch.empty(k, dtype=torch.int32, device="cuda")
+        bc.bc_select_channels(x, k, idx)
+    y = torch.empty(d_out, dtype=torch.int16, device="cuda")
+    ws = torch.empty(bc.bc_sparse_gemv_workspace_bytes(d_out, k) // 4 + 64, dtype=torch.int32, device="cuda")
+    bc.bc_workspace_init(ws)
+    for ly in model.layers[:4]:
+        bc.bc_sparse_gemv(ly[which], x, idx, k, y, ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        for ly in model.layers:
+            bc.bc_sparse_gemv(ly[which], x, idx, k, y, ws)
+    e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / (reps * len(model.layers))
+    return us, gemv_bytes(d_in, d_out, k, r_p < 1), k
+
+
+def load_traffic(n):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 counter summary, or None when the kernel sources changed since
+    the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "attn_partial_dense_131072_pmc.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_hash") != kernel_source_hash() or rec.get("context") != n:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(model, n):
+    """The CPU oracle, as it stands, on one decoder layer of the dense step at
+    context n (layer 0's weights and cache copied to the host)."""
+    import oracle
+
+    D = DIMS
+    ly = model.layers[0]
+    t0 = time.time()
+
+    def h16(t):
+        return t.cpu().numpy().view(np.uint16)
+
+    d, dff = D["d"], D["d_ff"]
+    w_gu = h16(ly["w_gu"])
+    # undo the gate|up packing for the oracle's separate matrices
+    gate = np.empty((d, dff), np.uint16)
+    up = np.empty((d, dff), np.uint16)
+    for t in range((dff + 255) // 256):
+        w = min(256, dff - 256 * t)
+        gate[:, 256 * t:256 * t + w] = w_gu[:, 512 * t:512 * t + w]
+        up[:, 256 * t:256 * t + w] = w_gu[:, 512 * t + w:512 * t + 2 * w]
+    W = dict(qkv=h16(ly["w_qkv"]), o=h16(ly["w_o"]), gate=gate, up=up, down=h16(ly["w_down"]),
+             g1=h16(model.g_attn), g2=h16(model.g_mlp))
+    K = h16(ly["k"][:, :n])
+    V = h16(ly["v"][:, :n])
+    summ = h16(ly["summ"])
+    h = h16(model.h0)
+    dims = dict(d=d, d_ff=dff, n_heads=D["n_heads"], n_kv_heads=D["n_kv_heads"], head_dim=D["head_dim"])
+    log(f"[bench] cpu baseline inputs on host in {time.time() - t0:.1f}s")
+    S = 1
+    reps, elapsed = 0, 0.0
+    while reps < 3 and elapsed < 10.0:
+        t1 = time.perf_counter()
+        oracle.decode_layer(h, W, K.copy(), V.copy(), summ.copy(), n, dims, 1.0, 1.0, SINKS, WINDOW, S)
+        elapsed += time.perf_counter() - t1
+        reps += 1
+    sample_bytes = layer_bytes(n, 1.0, 1.0, n, S)
+    return {"value": round(sample_bytes * reps / elapsed / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"one of the 32 decoder layers of the dense {n}-token step (weights "
+                      f"{layer_bytes(0, 1.0, 1.0, 0, 1) / 1e6:.0f} MB + KV {4096 * n / 1e6:.0f} MB), fp64 oracle, "
+                      f"{reps} run(s) in {elapsed:.1f}s; GB/s = that layer's algorithmic bytes / oracle time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--contexts", default="2048,8192,32768,131072")
+    ap.add_argument("--cells", default="default", help="default | dense | none")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attn-only", type=int, default=0,
+                    help="only launch the dense attention kernel this many times per layer (for counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (no sharding or collectives); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    contexts = [int(c) for c in args.contexts.split(",")]
+    head_n = max(contexts)
+    model = Model(max_ctx=max(contexts))
+
+    if args.attn_only:
+        us, b, S = time_attention_kernel(model, head_n, reps=args.attn_only)
+        log(f"[bench] attention kernel at n={head_n}: {us:.1f} us, {b / us / 1e3:.0f} GB/s, S={S}")
+        print(json.dumps({"attn_us": us, "attn_bytes": b, "splits": S}))
+        return
+
+    cells = [(1.0, 1.0, n) for n in contexts]
+    if args.cells == "default":
+        small = [n for n in contexts if n <= 8192]
+        cells += [(1.0, rkv, n) for rkv in (0.3, 0.5) for n in contexts]
+        cells += [(rp, 1.0, n) for rp in (0.7, 0.5) for n in small]
+        cells += [(rp, rkv, n) for rp, rkv in ((0.7, 0.3), (0.5, 0.3), (0.5, 0.5)) for n in contexts]
+    elif args.cells == "none":
+        cells = [(1.0, 1.0, head_n)]
+
+    results = []
+    headline = None
+    for (r_p, r_kv, n) in cells:
+        _, t_sel, S = model.plan(n, r_p, r_kv)
+        g = model.graph(n, r_p, r_kv)
+        is_head = (r_p, r_kv, n) == (1.0, 1.0, head_n)
+        ms = time_graph(g, args.steps if is_head else min(args.steps, 20), args.warmup)
+        del g
+        b = step_bytes(n, r_p, r_kv, t_sel, S)
+        cell = {"r_p": r_p, "r_kv": r_kv, "context": n, "step_us": round(ms * 1000, 1),
+                "gbs": round(b / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "bytes": b, "t_sel": t_sel, "splits": S}
+        results.append(cell)
+        log(f"[bench] r_p={r_p} r_kv={r_kv} n={n}: {cell['step_us']} us/step, {cell['gbs']} GB/s "
+            f"({100 * cell['frac_hbm']:.1f}% of 8 TB/s)")
+        if is_head:
+            headline = (ms, b)
+    for c in results:
+        dense = next((x for x in results if x["context"] == c["context"] and x["r_p"] == 1 and x["r_kv"] == 1), None)
+        if dense:
+            c["speedup_vs_dense"] = round(dense["step_us"] / c["step_us"], 3)
+
+    ms, b = headline
+    attn_us, attn_b, attn_S = time_attention_kernel(model, head_n)
+    gemv_us, gemv_b, _ = time_gemv_kernel(model, "w_gu", 1.0)
+    gemv_sp_us, gemv_sp_b, _ = time_gemv_kernel(model, "w_gu", 0.5)
+    log(f"[bench] attention kernel {attn_us:.1f} us ({attn_b / attn_us / 1e3:.0f} GB/s); gate|up GEMV dense "
+        f"{gemv_us:.1f} us ({gemv_b / gemv_us / 1e3:.0f} GB/s), r_p 0.5 {gemv_sp_us:.1f} us "
+        f"({gemv_sp_b / gemv_sp_us / 1e3:.0f} GB/s)")
+    achieved = attn_b / (attn_us * 1e-6) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(b / (ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: random-init N(0,0.02) weights of Llama-3.1-8B shape, N(0,1) pre-filled KV cache",
+        "config": {"workload": f"dense decode step of one sequence at Llama-3.1-8B dims: 32 layers + LM head, "
+                               f"context {head_n}, r_p=1, r_kv=1", "context": head_n, "r_p": 1.0, "r_kv": 1.0,
+                   "layers": 32, "batch": 1},
+        "roofline": {"bound": "hbm", "kernel": "k_attn_partial (bc_splitk_attn_partial), dense, one layer",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(head_n),
+                     "launch_us": round(attn_us, 2), "bytes_per_launch": attn_b, "splits": attn_S},
+        "gemv_roofline": {"kernel": "k_gemv (bc_sparse_gemv), gate|up 4096x28672",
+                          "dense": {"us": round(gemv_us, 2), "gbs": round(gemv_b / gemv_us / 1e3, 1),
+                                    "frac": round(gemv_b / gemv_us / 1e3 / HBM_PEAK_GBS, 4)},
+                          "r_p_0.5": {"us": round(gemv_sp_us, 2), "gbs": round(gemv_sp_b / gemv_sp_us / 1e3, 1),
+                                      "frac": round(gemv_sp_b / gemv_sp_us / 1e3 / HBM_PEAK_GBS, 4)}},
+        "cells": results,
+    }
+    if not args.no_cpu_baseline:
+        try:
+            out["cpu_baseline"] = cpu_baseline(model, head_n)
+        except Exception as e:  # the GPU figure stands on its own
+            log(f"[bench] cpu baseline failed: {e!r}")
+            out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

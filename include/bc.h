@@ -224,7 +224,7 @@ int bc_decode_layer(const bc_model_dims* dims, const bc_layer* layer, const bc_s
                     uint16_t* hidden, void* ws, size_t ws_bytes, void* stream);
 
 /* Packs W_gate^T and W_up^T (each bf16 [d][d_ff]) into the layout
- * bc_decode_layer reads: per row, groups of up to 256 gate columns followed
+ * bc_decode_layer reads: per row, groups of up to 64 gate columns followed
  * by the same up columns.  w_gu bf16 [d][2*d_ff].  (setup, not timed) */
 int bc_pack_gate_up(const uint16_t* w_gate_t, const uint16_t* w_up_t, int d, int d_ff, uint16_t* w_gu,
                     void* stream);
