@@ -15,7 +15,7 @@
 // slice of the index list is staged in LDS.
 //
 // Merge pass: M = max m_s, out = sum o_s e^(m_s-M) / sum l_s e^(m_s-M),
-// one thread per (head, dim).
+// one work-group per query head.
 #include <math.h>
 
 #include "bc_device.hpp"
@@ -175,29 +175,67 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
   }
 }
 
+// One work-group per query head.  M and the weights w_s = e^(m_s - M) are
+// computed once into LDS; the weighted sums over splits are split between
+// thread groups (fixed halves) and combined in a fixed order.
+constexpr int kReduceMaxSplits = 4096;
+
 __global__ __launch_bounds__(kAttnThreads) void k_attn_reduce(const ReduceParams p) {
-  const int tid = threadIdx.x;
-  const int D = p.head_dim;
-  const int heads_per_block = kAttnThreads / D;
-  const int j = blockIdx.x * heads_per_block + tid / D;
-  const int d = tid % D;
-  if (j >= p.n_heads) return;
-  const float* mj = p.m + size_t(j) * p.n_splits;
-  const float* lj = p.l + size_t(j) * p.n_splits;
-  const float* oj = p.o + size_t(j) * p.n_splits * D + d;
-  float M = -INFINITY;
-  for (int s = 0; s < p.n_splits; ++s) M = fmaxf(M, mj[s]);
-  float num = 0.f, den = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < p.n_splits; ++s) {
-      const float ms = mj[s];
-      if (ms == -INFINITY) continue;
-      const float wgt = expf(ms - M);
-      num += oj[size_t(s) * D] * wgt;
-      den += lj[s] * wgt;
-    }
+  __shared__ float wts[kReduceMaxSplits];
+  __shared__ float part[kAttnThreads];
+  __shared__ float red[kAttnThreads / kWave];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int j = blockIdx.x;
+  const int D = p.head_dim, S = p.n_splits;
+  const float* mj = p.m + size_t(j) * S;
+  const float* lj = p.l + size_t(j) * S;
+  float mx = -INFINITY;
+  for (int s = tid; s < S; s += kAttnThreads) mx = fmaxf(mx, mj[s]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+  if (lane == 0) red[w] = mx;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int i = 1; i < kAttnThreads / kWave; ++i) M = fmaxf(M, red[i]);
+  __syncthreads();
+  float den = 0.f;
+  for (int s = tid; s < S; s += kAttnThreads) {
+    const float ms = mj[s];
+    const float wt = (ms == -INFINITY || M == -INFINITY) ? 0.f : expf(ms - M);
+    wts[s] = wt;
+    den += wt * lj[s];
   }
-  p.out[size_t(j) * D + d] = f32_to_bf16(den > 0.f ? num / den : 0.f);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, kWave);
+  if (lane == 0) red[w] = den;
+  __syncthreads();
+  den = 0.f;
+#pragma unroll
+  for (int i = 0; i < kAttnThreads / kWave; ++i) den += red[i];
+  const int groups = kAttnThreads / D;          // 2 at head_dim 128, 4 at 64
+  const int grp = tid / D, d = tid % D;
+  const int per = (S + groups - 1) / groups;
+  const int s0 = min(S, grp * per), s1 = min(S, s0 + per);
+  const float* oj = p.o + size_t(j) * S * D + d;
+  float num = 0.f;
+  int s = s0;
+  for (; s + 4 <= s1; s += 4) {
+    const float o0 = oj[size_t(s) * D], o1 = oj[size_t(s + 1) * D];
+    const float o2 = oj[size_t(s + 2) * D], o3 = oj[size_t(s + 3) * D];
+    num += o0 * wts[s];
+    num += o1 * wts[s + 1];
+    num += o2 * wts[s + 2];
+    num += o3 * wts[s + 3];
+  }
+  for (; s < s1; ++s) num += oj[size_t(s) * D] * wts[s];
+  part[tid] = num;
+  __syncthreads();
+  if (tid < D) {
+    float t = 0.f;
+    for (int g = 0; g < groups; ++g) t += part[g * D + tid];
+    p.out[size_t(j) * D + tid] = f32_to_bf16(den > 0.f ? t / den : 0.f);
+  }
 }
 
 template <int D>
@@ -222,9 +260,7 @@ int launch_attn_partial(const AttnParams& p, hipStream_t s) {
 }
 
 int launch_attn_reduce(const ReduceParams& p, hipStream_t s) {
-  const int hpb = kAttnThreads / p.head_dim;
-  dim3 grid(ceil_div(p.n_heads, hpb)), block(kAttnThreads);
-  k_attn_reduce<<<grid, block, 0, s>>>(p);
+  k_attn_reduce<<<dim3(p.n_heads), dim3(kAttnThreads), 0, s>>>(p);
   return check_launch("k_attn_reduce");
 }
 

@@ -90,68 +90,79 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 }
 
 // ------------------------------------------------------ block top-k select
-// LDS needed by block_topk: NW*256 histogram words + 256 merged + small.
-template <int NT>
+// Keys are staged in LDS when they fit (kTopkLdsBytes); larger inputs read
+// key_fn directly.
+constexpr int kTopkLdsBytes = 65536;
+
+template <int NT, typename KeyT>
 struct TopkSmem {
+  static constexpr int CAP = kTopkLdsBytes / int(sizeof(KeyT));
+  KeyT keys[CAP];
   uint32_t hist[NT / kWave][256];
-  uint32_t merged[256];
-  uint32_t scan[NT / kWave + 1];
+  uint32_t wave_gt[NT / kWave];
+  uint32_t wave_eq[NT / kWave];
   uint32_t sel_bin, sel_above;
 };
 
-// Exact top-k over n integer keys given by key_fn(i) (only the low `bits`
-// bits are used; bits in {15, 32}).  Keeps the k largest keys, equal keys
-// by lower position, and calls emit(rank, i) for every kept position, rank
-// being its place in ascending position order.  Every thread of the block
-// must call it.  Passes of 8 bits from the top; per-wave histograms in LDS.
-template <int NT, int BITS, typename KeyFn, typename EmitFn>
-__device__ void block_topk(int n, int k, KeyFn key_fn, EmitFn emit, TopkSmem<NT>& sm) {
+// Exact top-k over n integer keys given by key_fn(i) (the low BITS bits are
+// used; BITS in {15, 32}).  Keeps the k largest keys, equal keys by lower
+// position, and calls emit(rank, i) for every kept position, rank being its
+// place in ascending position order.  Every thread of the block must call it.
+//   1. keys staged in LDS (if they fit);
+//   2. radix passes of 8 bits from the top, per-wave histograms, wave 0 finds
+//      the bin holding the k-th largest key -> threshold key thr and the
+//      number need_eq of keys equal to thr that are kept;
+//   3. each wave owns a contiguous slice of positions; per-wave counts of
+//      keys > thr and == thr give every wave its tie allowance and output
+//      offset; a ballot pass then emits the kept positions in order.
+template <int NT, int BITS, typename KeyT, typename KeyFn, typename EmitFn>
+__device__ void block_topk(int n, int k, KeyFn key_fn, EmitFn emit, TopkSmem<NT, KeyT>& sm) {
   constexpr int NW = NT / kWave;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = tid >> 6, lane = tid & 63;
   if (k >= n) {
     for (int i = tid; i < n; i += NT) emit(i, i);
     return;
   }
   if (k <= 0) return;
-
-  uint32_t prefix = 0;     // decided high bits of the threshold key
-  int decided = 0;         // number of decided high bits
-  uint32_t k_rem = uint32_t(k);
-  int pass_bits[4];
-  int npass = 0;
-  {
-    int left = BITS;
-    while (left > 0) { int b = left >= 8 ? 8 : left; pass_bits[npass++] = b; left -= b; }
+  const bool staged = n <= TopkSmem<NT, KeyT>::CAP;
+  if (staged) {
+    for (int i = tid; i < n; i += NT) sm.keys[i] = KeyT(key_fn(i));
   }
-  for (int p = 0; p < npass; ++p) {
-    const int width = pass_bits[p];
+  auto key = [&](int i) -> uint32_t { return staged ? uint32_t(sm.keys[i]) : uint32_t(key_fn(i)); };
+
+  uint32_t prefix = 0;
+  int decided = 0;
+  uint32_t k_rem = uint32_t(k);
+  constexpr int NPASS = (BITS + 7) / 8;
+#pragma unroll
+  for (int pass = 0; pass < NPASS; ++pass) {
+    const int width = (BITS - decided) >= 8 ? 8 : (BITS - decided);
     const int shift = BITS - decided - width;
-    const uint32_t hi_mask = decided == 0 ? 0u : (~0u << (BITS - decided)) & (BITS == 32 ? ~0u : ((1u << BITS) - 1u));
-    for (int i = tid; i < NW * 256; i += NT) (&sm.hist[0][0])[i] = 0;
+    const uint32_t keymask = BITS == 32 ? ~0u : ((1u << BITS) - 1u);
+    const uint32_t hi_mask = decided == 0 ? 0u : ((~0u << (BITS - decided)) & keymask);
+    for (int i = lane; i < 256; i += kWave) sm.hist[w][i] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += NT) {
-      uint32_t key = key_fn(i);
-      if (((key ^ prefix) & hi_mask) == 0)
-        atomicAdd(&sm.hist[w][(key >> shift) & ((1u << width) - 1u)], 1u);
-    }
-    __syncthreads();
-    for (int b = tid; b < 256; b += NT) {
-      uint32_t s = 0;
-      for (int ww = 0; ww < NW; ++ww) s += sm.hist[ww][b];
-      sm.merged[b] = s;
+      const uint32_t kk = key(i);
+      if (((kk ^ prefix) & hi_mask) == 0) atomicAdd(&sm.hist[w][(kk >> shift) & ((1u << width) - 1u)], 1u);
     }
     __syncthreads();
     if (w == 0) {
-      // lane l owns bins 255-4l .. 252-4l (descending); find where the running
-      // count from the top reaches k_rem.
-      const int lane = wave_lane();
+      // lane owns bins 255-4*lane .. 252-4*lane (descending)
       uint32_t c[4];
-      uint32_t s = 0;
+      uint32_t sum = 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) { c[u] = sm.merged[255 - 4 * lane - u]; s += c[u]; }
-      uint32_t inc = wave_inclusive_scan(s);
-      uint32_t ex = inc - s;
+      for (int u = 0; u < 4; ++u) {
+        const int b = 255 - 4 * lane - u;
+        uint32_t t = 0;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) t += sm.hist[ww][b];
+        c[u] = t;
+        sum += t;
+      }
+      const uint32_t inc = wave_inclusive_scan(sum);
+      const uint32_t ex = inc - sum;
       if (ex < k_rem && k_rem <= inc) {
         uint32_t run = ex;
 #pragma unroll
@@ -165,37 +176,41 @@ __device__ void block_topk(int n, int k, KeyFn key_fn, EmitFn emit, TopkSmem<NT>
     prefix |= sm.sel_bin << shift;
     k_rem -= sm.sel_above;
     decided += width;
-    __syncthreads();
   }
-  // threshold key = prefix; keep every key above it and the first k_rem equal ones.
-  const uint32_t thr = prefix;
-  const uint32_t need_eq = k_rem;
-  const int per = (n + NT - 1) / NT;
-  const int i0 = tid * per;
-  const int i1 = min(n, i0 + per);
-  uint32_t eq = 0;
-  for (int i = i0; i < i1; ++i) eq += key_fn(i) == thr;
-  uint32_t tot;
-  uint32_t eq_before = block_exclusive_scan<NT>(eq, sm.scan, &tot);
-  uint32_t sel = 0;
-  {
-    uint32_t e = eq_before;
-    for (int i = i0; i < i1; ++i) {
-      uint32_t key = key_fn(i);
-      if (key > thr) ++sel;
-      else if (key == thr) { if (e < need_eq) ++sel; ++e; }
-    }
+  const uint32_t thr = prefix, need_eq = k_rem;
+
+  // per-wave counts over its contiguous slice
+  const int per = (n + NW - 1) / NW;
+  const int w0 = min(n, w * per), w1 = min(n, w0 + per);
+  uint32_t gt = 0, eq = 0;
+  for (int b = w0; b < w1; b += kWave) {
+    const int i = b + lane;
+    const uint32_t kk = i < w1 ? key(i) : 0u;
+    const bool in = i < w1;
+    gt += __popcll(__ballot(in && kk > thr));
+    eq += __popcll(__ballot(in && kk == thr));
   }
-  uint32_t rank = block_exclusive_scan<NT>(sel, sm.scan, &tot);
-  {
-    uint32_t e = eq_before;
-    for (int i = i0; i < i1; ++i) {
-      uint32_t key = key_fn(i);
-      bool take = false;
-      if (key > thr) take = true;
-      else if (key == thr) { take = e < need_eq; ++e; }
-      if (take) emit(int(rank++), i);
-    }
+  if (lane == 0) { sm.wave_gt[w] = gt; sm.wave_eq[w] = eq; }
+  __syncthreads();
+  uint32_t eq_before = 0, out = 0;
+  for (int ww = 0; ww < w; ++ww) {
+    const uint32_t e = sm.wave_eq[ww];
+    const uint32_t allow = eq_before >= need_eq ? 0u : min(e, need_eq - eq_before);
+    out += sm.wave_gt[ww] + allow;
+    eq_before += e;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int b = w0; b < w1; b += kWave) {
+    const int i = b + lane;
+    const bool in = i < w1;
+    const uint32_t kk = in ? key(i) : 0u;
+    const uint64_t eqm = __ballot(in && kk == thr);
+    const uint32_t my_tie = eq_before + uint32_t(__popcll(eqm & below));
+    const bool take = in && (kk > thr || (kk == thr && my_tie < need_eq));
+    const uint64_t tm = __ballot(take);
+    if (take) emit(int(out + uint32_t(__popcll(tm & below))), i);
+    out += uint32_t(__popcll(tm));
+    eq_before += uint32_t(__popcll(eqm));
   }
   __syncthreads();
 }

@@ -154,16 +154,44 @@ __device__ __forceinline__ float chunk_sum(const float* partial, int n_splits, i
   return v;
 }
 
+// Same for 4 consecutive columns (c % 4 == 0, d_out % 8 == 0).
+__device__ __forceinline__ float4 chunk_sum4(const float* partial, int n_splits, int d_out, int c) {
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* pp = partial + c;
+  int s = 0;
+  for (; s + 4 <= n_splits; s += 4) {
+    const float4 a0 = *reinterpret_cast<const float4*>(pp + size_t(s) * d_out);
+    const float4 a1 = *reinterpret_cast<const float4*>(pp + size_t(s + 1) * d_out);
+    const float4 a2 = *reinterpret_cast<const float4*>(pp + size_t(s + 2) * d_out);
+    const float4 a3 = *reinterpret_cast<const float4*>(pp + size_t(s + 3) * d_out);
+    v.x += a0.x; v.y += a0.y; v.z += a0.z; v.w += a0.w;
+    v.x += a1.x; v.y += a1.y; v.z += a1.z; v.w += a1.w;
+    v.x += a2.x; v.y += a2.y; v.z += a2.z; v.w += a2.w;
+    v.x += a3.x; v.y += a3.y; v.z += a3.z; v.w += a3.w;
+  }
+  for (; s < n_splits; ++s) {
+    const float4 a0 = *reinterpret_cast<const float4*>(pp + size_t(s) * d_out);
+    v.x += a0.x; v.y += a0.y; v.z += a0.z; v.w += a0.w;
+  }
+  return v;
+}
+
 __global__ __launch_bounds__(256) void k_finish_bf16(const FinishParams p) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c < p.d_out) p.y[c] = f32_to_bf16(chunk_sum(p.partial, p.n_splits, p.d_out, c));
 }
 
-// Rotary (rotate-half) cos/sin of pair i at position pos, angle in double.
-__device__ __forceinline__ void rope_cs(int pos, double theta, int i, int D, float* cs, float* sn) {
-  const double ang = double(pos) * pow(theta, -2.0 * double(i) / double(D));
-  *cs = float(cos(ang));
-  *sn = float(sin(ang));
+// Rotary (rotate-half) cos/sin of pair i at position pos.  The angle
+// pos * theta^(-2i/D) is formed in double and reduced by 2*pi in double
+// (two-part constant), so single-precision sincos of the reduced angle is
+// accurate to float rounding at any position.
+__device__ __forceinline__ void rope_cs(int pos, double log2_theta, int i, int D, float* cs, float* sn) {
+  const double inv_freq = exp2(-2.0 * double(i) / double(D) * log2_theta);
+  const double ang = double(pos) * inv_freq;
+  const double kq = rint(ang * 0.15915494309189533577);
+  double r = fma(-kq, 6.28318530717958623200, ang);
+  r = fma(-kq, 2.44929359829470635445e-16, r);
+  sincosf(float(r), sn, cs);
 }
 
 // One work-group per head of the q | k | v output: thread i owns the pair
@@ -179,7 +207,7 @@ __global__ __launch_bounds__(64) void k_finish_qkv(const FinishParams p) {
     float b = chunk_sum(p.partial, p.n_splits, p.d_out, base + i + half);
     if (head < qh + kvh) {
       float cs, sn;
-      rope_cs(p.pos, p.theta, i, D, &cs, &sn);
+      rope_cs(p.pos, p.log2_theta, i, D, &cs, &sn);
       const float ra = a * cs - b * sn;
       const float rb = b * cs + a * sn;
       a = ra;
@@ -202,13 +230,16 @@ __global__ __launch_bounds__(64) void k_finish_qkv(const FinishParams p) {
         for (int e = 0; e < 2; ++e) {
           const int dd = e ? i + half : i;
           const uint16_t nb = e ? bb : ba;
+          uint16_t rows[16];
+#pragma unroll
+          for (int t = 0; t < 16; ++t) rows[t] = blk * 16 + t < p.pos ? kc[size_t(blk * 16 + t) * D + dd] : nb;
           uint16_t bmn = nb, bmx = nb;
           float mn = bf16_to_f32(nb), mx = mn;
-          for (int t = blk * 16; t < p.pos; ++t) {
-            const uint16_t u = kc[size_t(t) * D + dd];
-            const float f = bf16_to_f32(u);
-            if (f < mn) { mn = f; bmn = u; }
-            if (f > mx) { mx = f; bmx = u; }
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const float f = bf16_to_f32(rows[t]);
+            if (f < mn) { mn = f; bmn = rows[t]; }
+            if (f > mx) { mx = f; bmx = rows[t]; }
           }
           sp[dd * 2 + 0] = bmn;
           sp[dd * 2 + 1] = bmx;
@@ -226,7 +257,7 @@ __global__ __launch_bounds__(64) void k_finish_qkv(const FinishParams p) {
 constexpr int kOneGroup = 1024;
 
 struct OneGroupSmem {
-  TopkSmem<kOneGroup> topk;
+  TopkSmem<kOneGroup, uint16_t> topk;
   float part[kOneGroup / kWave];
 };
 
@@ -249,20 +280,28 @@ __device__ float one_group_sum_squares(const uint16_t* x, int n, float* part) {
   return t;
 }
 
-__device__ void one_group_select(const uint16_t* x, int n, int k, int32_t* idx_out, TopkSmem<kOneGroup>& sm) {
+__device__ void one_group_select(const uint16_t* x, int n, int k, int32_t* idx_out,
+                                 TopkSmem<kOneGroup, uint16_t>& sm) {
   auto key = [x](int i) -> uint32_t { return uint32_t(x[i]) & 0x7FFFu; };
   auto emit = [idx_out](int r, int i) { idx_out[r] = i; };
-  block_topk<kOneGroup, 15>(n, k, key, emit, sm);
+  block_topk<kOneGroup, 15, uint16_t>(n, k, key, emit, sm);
 }
 
 // One work-group: y = bf16(resid + sum of chunks); then optionally
 // x_next = RMSNorm(y) * gain and the top-k of x_next.
 __global__ __launch_bounds__(kOneGroup) void k_finish_resid(const FinishParams p) {
   __shared__ OneGroupSmem sm;
-  for (int c = threadIdx.x; c < p.d_out; c += kOneGroup) {
-    float v = chunk_sum(p.partial, p.n_splits, p.d_out, c);
-    if (p.resid) v += bf16_to_f32(p.resid[c]);
-    p.y[c] = f32_to_bf16(v);
+  for (int c = threadIdx.x * 4; c < p.d_out; c += kOneGroup * 4) {
+    const float4 v = chunk_sum4(p.partial, p.n_splits, p.d_out, c);
+    float r[4] = {v.x, v.y, v.z, v.w};
+    if (p.resid) {
+      const uint2 rr = *reinterpret_cast<const uint2*>(p.resid + c);
+      r[0] += bf16_lo(rr.x); r[1] += bf16_hi(rr.x); r[2] += bf16_lo(rr.y); r[3] += bf16_hi(rr.y);
+    }
+    uint2 o;
+    o.x = uint32_t(f32_to_bf16(r[0])) | (uint32_t(f32_to_bf16(r[1])) << 16);
+    o.y = uint32_t(f32_to_bf16(r[2])) | (uint32_t(f32_to_bf16(r[3])) << 16);
+    *reinterpret_cast<uint2*>(p.y + c) = o;
   }
   __syncthreads();
   if (p.norm_gain == nullptr) return;
@@ -281,14 +320,21 @@ __global__ __launch_bounds__(kOneGroup) void k_finish_resid(const FinishParams p
 __global__ __launch_bounds__(kOneGroup) void k_finish_swiglu(const FinishParams p) {
   __shared__ OneGroupSmem sm;
   const int half = kGemvTile / 2;
-  const int stride = gridDim.x * kOneGroup;
-  for (int u = blockIdx.x * kOneGroup + threadIdx.x; u < p.d_ff; u += stride) {
+  const int stride = gridDim.x * kOneGroup * 4;
+  for (int u = (blockIdx.x * kOneGroup + threadIdx.x) * 4; u < p.d_ff; u += stride) {
     const int t = u / half, off = u % half;
     const int w = min(half, p.d_ff - t * half);
-    const float gt = chunk_sum(p.partial, p.n_splits, p.d_out, t * kGemvTile + off);
-    const float up = chunk_sum(p.partial, p.n_splits, p.d_out, t * kGemvTile + w + off);
-    const float silu = gt / (1.0f + expf(-gt));
-    p.y[u] = f32_to_bf16(silu * up);
+    const float4 gt = chunk_sum4(p.partial, p.n_splits, p.d_out, t * kGemvTile + off);
+    const float4 up = chunk_sum4(p.partial, p.n_splits, p.d_out, t * kGemvTile + w + off);
+    const float g[4] = {gt.x, gt.y, gt.z, gt.w};
+    const float v[4] = {up.x, up.y, up.z, up.w};
+    uint16_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(g[e] / (1.0f + expf(-g[e])) * v[e]);
+    uint2 ov;
+    ov.x = uint32_t(o[0]) | (uint32_t(o[1]) << 16);
+    ov.y = uint32_t(o[2]) | (uint32_t(o[3]) << 16);
+    *reinterpret_cast<uint2*>(p.y + u) = ov;
   }
   if (p.sel_k <= 0 || p.sel_k >= p.d_ff) return;
   __syncthreads();
@@ -322,7 +368,7 @@ __global__ __launch_bounds__(256) void k_argmax_finish(const float* tile_max, co
 }
 
 __global__ __launch_bounds__(kOneGroup) void k_select(const uint16_t* x, int n, int k, int32_t* idx_out) {
-  __shared__ TopkSmem<kOneGroup> sm;
+  __shared__ TopkSmem<kOneGroup, uint16_t> sm;
   one_group_select(x, n, k, idx_out, sm);
 }
 
@@ -374,7 +420,7 @@ int launch_finish(int kind, const FinishParams& p, hipStream_t s) {
     case FIN_RESID: k_finish_resid<<<1, kOneGroup, 0, s>>>(p); break;
     case FIN_SWIGLU: {
       const bool sel = p.sel_k > 0 && p.sel_k < p.d_ff;
-      k_finish_swiglu<<<sel ? 1 : ceil_div(p.d_ff, kOneGroup), kOneGroup, 0, s>>>(p);
+      k_finish_swiglu<<<sel ? 1 : ceil_div(p.d_ff, kOneGroup * 4), kOneGroup, 0, s>>>(p);
       break;
     }
     default: return set_error(BC_ERR_INVALID, "unknown finish kind %d", kind);

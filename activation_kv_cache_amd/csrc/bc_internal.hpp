@@ -62,7 +62,7 @@ struct FinishParams {
   uint16_t* v_cache;
   uint16_t* summary;
   int n_heads, n_kv_heads, head_dim, n_cap, pos;
-  double theta;
+  double log2_theta;
   // FIN_SWIGLU
   int d_ff;
 };

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
 }
 
 __global__ __launch_bounds__(kSelThreads) void k_kv_block_select(const KvSelectParams p) {
-  __shared__ TopkSmem<kSelThreads> sm;
+  __shared__ TopkSmem<kSelThreads, uint32_t> sm;
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   const bc_kv_budget_info bd = p.bud;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kSelThreads) void k_kv_block_select(const KvSelectP
 #pragma unroll
     for (int u = 0; u < 16; ++u) o[u] = t0 + u;
   };
-  block_topk<kSelThreads, 32>(bd.n_cand, bd.k_blk, key, emit, sm);
+  block_topk<kSelThreads, 32, uint32_t>(bd.n_cand, bd.k_blk, key, emit, sm);
 }
 
 // One wave per (block, KV head): per dim the min and max over the block's

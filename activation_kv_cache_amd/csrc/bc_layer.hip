@@ -256,7 +256,7 @@ extern "C" int bc_decode_layer(const bc_model_dims* dims, const bc_layer* ly, co
   {
     FinishParams f{};
     f.q_out = at<uint16_t>(ws, L.q); f.k_cache = ly->k_cache; f.v_cache = ly->v_cache; f.summary = ly->kv_summary;
-    f.n_heads = H; f.n_kv_heads = Hkv; f.head_dim = hd; f.n_cap = ly->n_cap; f.pos = pos; f.theta = st->rope_theta;
+    f.n_heads = H; f.n_kv_heads = Hkv; f.head_dim = hd; f.n_cap = ly->n_cap; f.pos = pos; f.log2_theta = log2(st->rope_theta);
     rc = run_gemv(ly->w_qkv, m.d, qkv_out, at<uint16_t>(ws, L.x1), idx_qkv, k_d, partial, FIN_QKV, f, s);
     if (rc != BC_OK) return rc;
   }
