@@ -72,6 +72,7 @@ _SIG = {
     "bc_select_channels": (c_int, [P, c_int, c_int, P, P]),
     "bc_sparse_gemv_workspace_bytes": (c_size_t, [c_int, c_int]),
     "bc_sparse_gemv": (c_int, [P, c_int, c_int, P, P, c_int, P, P, c_size_t, P]),
+    "bc_sparse_gemv_tiled": (c_int, [P, c_int, c_int, P, P, c_int, P, P, c_size_t, P]),
     "bc_kv_score_select_workspace_bytes": (c_size_t, [c_int, c_int, ctypes.POINTER(bc_kv_policy)]),
     "bc_kv_score_select": (c_int, [P, P, c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(bc_kv_policy), P, P,
                                    P, c_size_t, P]),
@@ -83,6 +84,7 @@ _SIG = {
     "bc_decode_layer": (c_int, [ctypes.POINTER(bc_model_dims), ctypes.POINTER(bc_layer), ctypes.POINTER(bc_step),
                                 P, P, c_size_t, P]),
     "bc_pack_gate_up": (c_int, [P, P, c_int, c_int, P, P]),
+    "bc_pack_weight_tiles": (c_int, [P, c_int, c_int, P, P]),
     "bc_lm_head_workspace_bytes": (c_size_t, [ctypes.POINTER(bc_model_dims)]),
     "bc_lm_head": (c_int, [ctypes.POINTER(bc_model_dims), P, P, P, P, P, c_double, P, c_size_t, P]),
 }
@@ -190,6 +192,12 @@ def bc_sparse_gemv(wt, x, idx, k: int, y, ws, stream=None):
                                       _stream(stream)), "bc_sparse_gemv")
 
 
+def bc_sparse_gemv_tiled(wt_packed, d_in: int, d_out: int, x, idx, k: int, y, ws, stream=None):
+    p, n = _ws(ws)
+    return _check(_lib.bc_sparse_gemv_tiled(_ptr(wt_packed), int(d_in), int(d_out), _ptr(x), _ptr(idx), int(k),
+                                            _ptr(y), p, n, _stream(stream)), "bc_sparse_gemv_tiled")
+
+
 def bc_kv_score_select(q, summary, n_ctx: int, n_heads: int, n_kv_heads: int, head_dim: int,
                        pol: bc_kv_policy, idx_out, scores_out=None, ws=None, stream=None):
     nb_cap = summary.shape[1]
@@ -221,8 +229,22 @@ def bc_splitk_reduce(m, l, o, out, stream=None):
 
 def bc_pack_gate_up(w_gate_t, w_up_t, w_gu, stream=None):
     d, d_ff = w_gate_t.shape
+    assert w_gu.numel() == 2 * d * d_ff
     return _check(_lib.bc_pack_gate_up(_ptr(w_gate_t), _ptr(w_up_t), d, d_ff, _ptr(w_gu), _stream(stream)),
                   "bc_pack_gate_up")
+
+
+def bc_pack_weight_tiles(wt, packed, stream=None):
+    d_in, d_out = wt.shape
+    return _check(_lib.bc_pack_weight_tiles(_ptr(wt), d_in, d_out, _ptr(packed), _stream(stream)),
+                  "bc_pack_weight_tiles")
+
+
+def packed_tiles(wt, stream=None):
+    """A new device tensor holding wt in the tile-major layout."""
+    out = torch.empty(wt.numel(), dtype=wt.dtype, device=wt.device)
+    bc_pack_weight_tiles(wt, out, stream)
+    return out
 
 
 def make_layer(w_qkv, w_o, w_gu, w_down, g_attn, g_mlp, k_cache, v_cache, kv_summary=None) -> bc_layer:

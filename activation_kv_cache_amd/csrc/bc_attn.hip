@@ -5,14 +5,19 @@
 // dense mode is the same kernel with idx == NULL.
 //
 // Partial pass: one work-group per (split, KV head).  A key (value) row is
-// head_dim bf16 = 256 B at head_dim 128; 16 lanes hold one row (16 B each),
-// so one wave load covers 4 consecutive list positions (1 KB contiguous in
-// dense mode and inside a selected 16-token block).  The G query heads of the
-// KV head live in registers as bf16 pairs; q.k uses v_dot2 (bf16 pairs into
-// fp32) and a DPP sum over the 16 lanes.  Each group of 16 lanes keeps its
-// own online-softmax state (m, l, o) in log2 units; the 16 states of a
-// work-group are merged through LDS at the end.  In index mode the split's
-// slice of the index list is staged in LDS.
+// head_dim bf16 = 256 B at head_dim 128; a group of 8 lanes holds one row,
+// lane r the dims [8r, 8r+8) and [64+8r, 64+8r+8) (two 16-byte loads, each
+// covering 128 contiguous bytes of the row across the group), so one wave
+// load instruction reads 8 rows.  A wave iteration takes 2 rows per group.
+// The G query heads of the KV head live in registers as bf16 pairs; q.k uses
+// v_dot2 (bf16 pairs into fp32) and a 3-step DPP sum over the group.  The
+// softmax weights are rounded to bf16 and paired over the two rows, so p.v is
+// again v_dot2 with fp32 accumulation (the pairs of value rows are formed
+// with v_perm); the weight sum l adds the same rounded weights.  Each lane
+// group keeps its own online-softmax state and only rescales when the
+// running max grows by more than 8 in log2 units.  States are merged across
+// the wave with shuffles and across the 4 waves through LDS.  In index mode
+// the split's slice of the index list is staged in LDS.
 //
 // Merge pass: M = max m_s, out = sum o_s e^(m_s-M) / sum l_s e^(m_s-M),
 // one work-group per query head.
@@ -33,135 +38,253 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 constexpr int kAttnThreads = 256;
+constexpr int kAttnWaves = kAttnThreads / kWave;
 constexpr int kIdxChunk = 1024;
 constexpr float kLn2 = 0.693147180559945309f;
 
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32, nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 template <int D, int G>
 struct AttnSmem {
-  static constexpr int LPT = D / 8;
-  static constexpr int SLOTS = (kAttnThreads / kWave) * (kWave / LPT);
-  float o[SLOTS][G][D];
-  float m[SLOTS][G];
-  float l[SLOTS][G];
+  uint16_t q[G][D];
+  float o[kAttnWaves][G][D];
+  float m[kAttnWaves][G];
+  float l[kAttnWaves][G];
   int32_t idx[kIdxChunk];
 };
 
+// Online-softmax state of one lane group: running max m (raw q.k units),
+// sum l of the (bf16-rounded) weights, and o over the lane's 16 dims.
+template <int G>
+struct AttnState {
+  float m[G], l[G], o[G][16];
+  float mx[G];   // true max of the logits seen (m may lag it by up to tau)
+};
+
+// K and V of the two rows a lane group takes in one wave iteration.
+struct AttnRows {
+  uint4 ka[2], kb[2], va[2], vb[2];
+};
+
+// Rows base + u*TPL + sub (u = 0, 1) of the chunk [c0, c1); positions past
+// c1 read row c1-1 again (their weight is masked to zero).  Lane r of a row
+// group loads dims [8r, 8r+8) and [D/2 + 8r, D/2 + 8r + 8).
+template <int D>
+__device__ __forceinline__ void attn_load(const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
+                                          const int32_t* sidx, int base, int c0, int c1, int sub, AttnRows& rw) {
+  constexpr int LPT = D / 16;
+  constexpr int TPL = kWave / LPT;
+  constexpr int HALF = D / 2;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int pos = base + u * TPL + sub;
+    const int pc = pos < c1 ? pos : c1 - 1;
+    const int t = sidx ? sidx[pc - c0] : pc;
+    const size_t off = size_t(t) * D;
+    rw.ka[u] = *reinterpret_cast<const uint4*>(Kg + off);
+    rw.kb[u] = *reinterpret_cast<const uint4*>(Kg + off + HALF);
+    rw.va[u] = *reinterpret_cast<const uint4*>(Vg + off);
+    rw.vb[u] = *reinterpret_cast<const uint4*>(Vg + off + HALF);
+  }
+}
+
+// Online-softmax update of one lane group with its two rows.  q comes from
+// LDS ([G][D] bf16; lane r reads its 16 dims of every head).
+template <int D, int G, bool MASKED>
+__device__ __forceinline__ void attn_compute(const AttnRows& rw, const uint16_t* sq, int base, int c1, int sub, int r,
+                                             float c, float tau, AttnState<G>& st) {
+  constexpr int LPT = D / 16;
+  constexpr int TPL = kWave / LPT;
+  constexpr int HALF = D / 2;
+  bool valid[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) valid[u] = !MASKED || base + u * TPL + sub < c1;
+  float a[G][2];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const uint4 q0 = *reinterpret_cast<const uint4*>(sq + j * D + 8 * r);
+    const uint4 q1 = *reinterpret_cast<const uint4*>(sq + j * D + HALF + 8 * r);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float acc = dot2(q0.x, rw.ka[u].x, 0.f);
+      acc = dot2(q0.y, rw.ka[u].y, acc);
+      acc = dot2(q0.z, rw.ka[u].z, acc);
+      acc = dot2(q0.w, rw.ka[u].w, acc);
+      acc = dot2(q1.x, rw.kb[u].x, acc);
+      acc = dot2(q1.y, rw.kb[u].y, acc);
+      acc = dot2(q1.z, rw.kb[u].z, acc);
+      acc = dot2(q1.w, rw.kb[u].w, acc);
+      acc = group_sum<LPT>(acc);
+      a[j][u] = (MASKED && !valid[u]) ? -INFINITY : acc;
+    }
+  }
+  // lazy rescaling: the running max only moves when a new logit exceeds it
+  // by more than tau (weights stay below 2^8 in between)
+  bool need[G];
+  bool any_need = false;
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float mt = fmaxf(a[j][0], a[j][1]);
+    need[j] = mt > st.m[j] + tau;
+    any_need |= need[j];
+    st.mx[j] = fmaxf(st.mx[j], mt);
+  }
+  if (__any(any_need)) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float mt = fmaxf(a[j][0], a[j][1]);
+      const float mn = need[j] ? mt : st.m[j];
+      const float alpha = need[j] ? (st.m[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m[j] - mn) * c)) : 1.f;
+      st.l[j] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.o[j][e] *= alpha;
+      st.m[j] = mn;
+    }
+  }
+  // value pairs (row 0, row 1) per dim, shared by every head of the group
+  uint32_t vp[16];
+  {
+    const uint32_t w0[8] = {rw.va[0].x, rw.va[0].y, rw.va[0].z, rw.va[0].w,
+                            rw.vb[0].x, rw.vb[0].y, rw.vb[0].z, rw.vb[0].w};
+    const uint32_t w1[8] = {rw.va[1].x, rw.va[1].y, rw.va[1].z, rw.va[1].w,
+                            rw.vb[1].x, rw.vb[1].y, rw.vb[1].z, rw.vb[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      vp[2 * i] = __builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u);
+      vp[2 * i + 1] = __builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float mc = st.m[j] == -INFINITY ? 0.f : st.m[j] * c;
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(a[j][0], c, -mc));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(a[j][1], c, -mc));
+    const uint32_t pk = pack_bf16x2(p0, p1);
+    st.l[j] += bf16_lo(pk) + bf16_hi(pk);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st.o[j][e] = dot2(pk, vp[e], st.o[j][e]);
+  }
+}
+
+// Merge state b into a (same lane dims).
+template <int G>
+__device__ __forceinline__ void attn_merge(AttnState<G>& a, const AttnState<G>& b, float c) {
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const float M = fmaxf(a.m[j], b.m[j]);
+    const float wa = a.m[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((a.m[j] - M) * c);
+    const float wb = b.m[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((b.m[j] - M) * c);
+    a.l[j] = a.l[j] * wa + b.l[j] * wb;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) a.o[j][e] = a.o[j][e] * wa + b.o[j][e] * wb;
+    a.m[j] = M;
+  }
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams p) {
-  constexpr int LPT = D / 8;          // lanes per row
-  constexpr int TPL = kWave / LPT;    // rows per wave load
-  constexpr int U = 16 / TPL;         // loads per iteration: 16 positions per wave iteration
-  constexpr int TPI = TPL * U;
+  constexpr int LPT = D / 16;          // lanes per row
+  constexpr int TPL = kWave / LPT;     // rows per wave load
+  constexpr int TPI = 2 * TPL;         // rows per wave iteration
+  constexpr int HALF = D / 2;
   __shared__ AttnSmem<D, G> sm;
 
   const int s = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, lane = wave_lane(), w = wave_id();
   const int sub = lane / LPT, r = lane % LPT;
-  const int c = (p.n_sel + p.n_splits - 1) / p.n_splits;
-  const int lo = s * c;
-  const int hi = min(p.n_sel, lo + c);
+  const int cn = (p.n_sel + p.n_splits - 1) / p.n_splits;
+  const int lo = s * cn;
+  const int hi = min(p.n_sel, lo + cn);
+  const float c = p.scale_log2;
+  const float tau = 8.0f / c;
 
-  uint32_t qv[G][4];
+  for (int i = tid; i < G * D / 8; i += kAttnThreads)
+    reinterpret_cast<uint4*>(&sm.q[0][0])[i] = reinterpret_cast<const uint4*>(p.q + size_t(g) * G * D)[i];
+  AttnState<G> st;
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    uint4 t = *reinterpret_cast<const uint4*>(p.q + size_t(g * G + j) * D + r * 8);
-    qv[j][0] = t.x; qv[j][1] = t.y; qv[j][2] = t.z; qv[j][3] = t.w;
-  }
-  float m_run[G], l_run[G], o_acc[G][8];
+    st.m[j] = -INFINITY;
+    st.mx[j] = -INFINITY;
+    st.l[j] = 0.f;
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    m_run[j] = -INFINITY;
-    l_run[j] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o_acc[j][e] = 0.f;
+    for (int e = 0; e < 16; ++e) st.o[j][e] = 0.f;
   }
-
-  const uint16_t* Kg = p.k_cache + size_t(g) * p.n_cap * D + r * 8;
-  const uint16_t* Vg = p.v_cache + size_t(g) * p.n_cap * D + r * 8;
+  const uint16_t* Kg = p.k_cache + size_t(g) * p.n_cap * D + 8 * r;
+  const uint16_t* Vg = p.v_cache + size_t(g) * p.n_cap * D + 8 * r;
   const int32_t* idxg = p.idx ? p.idx + size_t(g) * p.n_sel : nullptr;
 
+  __syncthreads();
   for (int c0 = lo; c0 < hi; c0 += kIdxChunk) {
     const int c1 = min(hi, c0 + kIdxChunk);
+    const int32_t* sidx = nullptr;
     if (idxg) {
       for (int i = tid; i < c1 - c0; i += kAttnThreads) sm.idx[i] = idxg[c0 + i];
       __syncthreads();
+      sidx = sm.idx;
     }
-    for (int base = c0 + w * TPI; base < c1; base += (kAttnThreads / kWave) * TPI) {
-      uint4 kr[U], vr[U];
-      bool valid[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        int pos = base + u * TPL + sub;
-        valid[u] = pos < c1;
-        int pc = valid[u] ? pos : c1 - 1;
-        int t = idxg ? sm.idx[pc - c0] : pc;
-        kr[u] = *reinterpret_cast<const uint4*>(Kg + size_t(t) * D);
-        vr[u] = *reinterpret_cast<const uint4*>(Vg + size_t(t) * D);
-      }
-      float z[G][U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          float a = dot2(qv[j][0], kr[u].x, 0.f);
-          a = dot2(qv[j][1], kr[u].y, a);
-          a = dot2(qv[j][2], kr[u].z, a);
-          a = dot2(qv[j][3], kr[u].w, a);
-          a = group_sum<LPT>(a);
-          z[j][u] = valid[u] ? a * p.scale_log2 : -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        float mt = z[j][0];
-#pragma unroll
-        for (int u = 1; u < U; ++u) mt = fmaxf(mt, z[j][u]);
-        const float mn = fmaxf(m_run[j], mt);
-        const float alpha = m_run[j] == -INFINITY ? 0.f : exp2f(m_run[j] - mn);
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o_acc[j][e] *= alpha;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const float pu = valid[u] ? exp2f(z[j][u] - mn) : 0.f;
-          psum += pu;
-          o_acc[j][0] += pu * bf16_lo(vr[u].x);
-          o_acc[j][1] += pu * bf16_hi(vr[u].x);
-          o_acc[j][2] += pu * bf16_lo(vr[u].y);
-          o_acc[j][3] += pu * bf16_hi(vr[u].y);
-          o_acc[j][4] += pu * bf16_lo(vr[u].z);
-          o_acc[j][5] += pu * bf16_hi(vr[u].z);
-          o_acc[j][6] += pu * bf16_lo(vr[u].w);
-          o_acc[j][7] += pu * bf16_hi(vr[u].w);
-        }
-        l_run[j] = l_run[j] * alpha + psum;
-        m_run[j] = mn;
-      }
+    int base = c0 + w * TPI;
+    for (; base + TPI <= c1; base += kAttnWaves * TPI) {
+      AttnRows rw;
+      attn_load<D>(Kg, Vg, sidx, base, c0, c1, sub, rw);
+      attn_compute<D, G, false>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
+    }
+    if (base < c1) {
+      AttnRows rw;
+      attn_load<D>(Kg, Vg, sidx, base, c0, c1, sub, rw);
+      attn_compute<D, G, true>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
     }
     if (idxg) __syncthreads();
   }
 
-  // merge the work-group's lane-group states
-  const int slot = w * TPL + sub;
+  // express every lane state at its true max, then merge the row groups of
+  // the wave (lanes with the same r), then the waves
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    float4* dst = reinterpret_cast<float4*>(&sm.o[slot][j][r * 8]);
-    dst[0] = make_float4(o_acc[j][0], o_acc[j][1], o_acc[j][2], o_acc[j][3]);
-    dst[1] = make_float4(o_acc[j][4], o_acc[j][5], o_acc[j][6], o_acc[j][7]);
-    if (r == 0) { sm.m[slot][j] = m_run[j]; sm.l[slot][j] = l_run[j]; }
+    const float alpha = st.m[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m[j] - st.mx[j]) * c);
+    st.l[j] *= alpha;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st.o[j][e] *= alpha;
+    st.m[j] = st.mx[j];
+  }
+#pragma unroll
+  for (int off = LPT; off < kWave; off <<= 1) {
+    AttnState<G> o;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      o.m[j] = __shfl_xor(st.m[j], off, kWave);
+      o.l[j] = __shfl_xor(st.l[j], off, kWave);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o.o[j][e] = __shfl_xor(st.o[j][e], off, kWave);
+    }
+    attn_merge<G>(st, o, c);
+  }
+  if (sub == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sm.o[w][j][8 * r + e] = st.o[j][e];
+        sm.o[w][j][HALF + 8 * r + e] = st.o[j][8 + e];
+      }
+      if (r == 0) { sm.m[w][j] = st.m[j]; sm.l[w][j] = st.l[j]; }
+    }
   }
   __syncthreads();
-  constexpr int SLOTS = AttnSmem<D, G>::SLOTS;
   for (int e = tid; e < G * D; e += kAttnThreads) {
     const int j = e / D, d = e % D;
     float M = -INFINITY;
-    for (int q = 0; q < SLOTS; ++q) M = fmaxf(M, sm.m[q][j]);
+#pragma unroll
+    for (int q = 0; q < kAttnWaves; ++q) M = fmaxf(M, sm.m[q][j]);
     float acc = 0.f, lsum = 0.f;
     if (M != -INFINITY) {
-      for (int q = 0; q < SLOTS; ++q) {
+#pragma unroll
+      for (int q = 0; q < kAttnWaves; ++q) {
         const float mq = sm.m[q][j];
         if (mq == -INFINITY) continue;
-        const float wq = exp2f(mq - M);
+        const float wq = __builtin_amdgcn_exp2f((mq - M) * c);
         acc += sm.o[q][j][d] * wq;
         lsum += sm.l[q][j] * wq;
       }
@@ -169,7 +292,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
     const int jh = g * G + j;
     p.o[(size_t(jh) * p.n_splits + s) * D + d] = acc;
     if (d == 0) {
-      p.m[size_t(jh) * p.n_splits + s] = M == -INFINITY ? -INFINITY : M * kLn2;
+      p.m[size_t(jh) * p.n_splits + s] = M == -INFINITY ? -INFINITY : M * c * kLn2;
       p.l[size_t(jh) * p.n_splits + s] = lsum;
     }
   }
@@ -270,11 +393,12 @@ using namespace bc;
 
 extern "C" int bc_attn_default_splits(int n_sel, int n_kv_heads) {
   if (n_sel <= 0 || n_kv_heads <= 0) return 1;
-  // about 1024 work-groups at long context, at least 64 listed tokens each
-  int by_len = ceil_div(n_sel, 64);
-  int by_fill = 1024 / n_kv_heads;
+  // one long-running work-group per compute unit streams best (256 CUs);
+  // at short context at least 64 listed tokens per split
+  int by_fill = 256 / n_kv_heads;
   if (by_fill < 1) by_fill = 1;
-  int s = by_len < by_fill ? by_len : by_fill;
+  const int by_len = ceil_div(n_sel, 64);
+  const int s = by_len < by_fill ? by_len : by_fill;
   return s < 1 ? 1 : s;
 }
 

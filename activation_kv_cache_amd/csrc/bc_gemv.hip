@@ -18,6 +18,7 @@
 // main kernel stores bf16 or fp32 (+ per-tile argmax) directly.
 // Dense mode is the same kernel with idx == NULL.
 #include <math.h>
+#include <stdlib.h>
 
 #include "bc_device.hpp"
 #include "bc_internal.hpp"
@@ -52,31 +53,53 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_main(const GemvParams p) 
   float acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.f;
-  const uint16_t* wcol = p.wt + (col_ok ? col : 0);
+  // plain: row ch of W^T at wt + ch * d_out; tile-major: the tile's rows are
+  // contiguous, each as wide as the tile
+  const int tile_w = min(kGemvTile, p.d_out - tile * kGemvTile);
+  const uint16_t* wcol;
+  size_t row_stride;
+  if (p.tiled) {
+    wcol = p.wt + size_t(tile) * kGemvTile * p.d_in + (col_ok ? l16 * 8 : 0);
+    row_stride = size_t(tile_w);
+  } else {
+    wcol = p.wt + (col_ok ? col : 0);
+    row_stride = size_t(p.d_out);
+  }
+  const bool dense = p.idx == nullptr;
 
   for (int s0 = r0; s0 < r1; s0 += kStageRows) {
     const int s1 = min(r1, s0 + kStageRows);
+    const int n = s1 - s0;
+    // dense rows are known before staging: put the first batch in flight now
+    uint4 wv[kRowsInFlight];
+    if (dense) {
+#pragma unroll
+      for (int u = 0; u < kRowsInFlight; ++u) {
+        const int rr = slot + kSlots * u;
+        wv[u] = (col_ok && rr < n) ? *reinterpret_cast<const uint4*>(wcol + size_t(s0 + rr) * row_stride)
+                                   : make_uint4(0, 0, 0, 0);
+      }
+    }
     for (int r = s0 + tid; r < s1; r += kGemvThreads) {
-      const int ch = p.idx ? p.idx[r] : r;
+      const int ch = dense ? r : p.idx[r];
       sm.ch[r - s0] = ch;
       sm.xv[r - s0] = bf16_to_f32(p.x[ch]);
     }
     __syncthreads();
-    const int n = s1 - s0;
     for (int r = slot; r < n; r += kSlots * kRowsInFlight) {
-      uint4 wv[kRowsInFlight];
       float xv[kRowsInFlight];
+      if (!dense || r != slot) {
+#pragma unroll
+        for (int u = 0; u < kRowsInFlight; ++u) {
+          const int rr = r + kSlots * u;
+          wv[u] = (col_ok && rr < n) ? *reinterpret_cast<const uint4*>(wcol + size_t(sm.ch[rr]) * row_stride)
+                                     : make_uint4(0, 0, 0, 0);
+        }
+      }
 #pragma unroll
       for (int u = 0; u < kRowsInFlight; ++u) {
         const int rr = r + kSlots * u;
-        if (rr < n) {
-          xv[u] = sm.xv[rr];
-          wv[u] = col_ok ? *reinterpret_cast<const uint4*>(wcol + size_t(sm.ch[rr]) * p.d_out)
-                         : make_uint4(0, 0, 0, 0);
-        } else {
-          xv[u] = 0.f;
-          wv[u] = make_uint4(0, 0, 0, 0);
-        }
+        xv[u] = rr < n ? sm.xv[rr] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < kRowsInFlight; ++u) {
@@ -385,10 +408,20 @@ __global__ __launch_bounds__(kOneGroup) void k_norm_select(const uint16_t* h, co
 
 }  // namespace
 
+static int gemv_target_groups() {
+  // tuning override for sweeps; the default is the measured best
+  static const int v = [] {
+    const char* e = getenv("BC_GEMV_GROUPS");
+    const int x = e ? atoi(e) : 0;
+    return x > 0 ? x : 512;
+  }();
+  return v;
+}
+
 GemvPlan plan_gemv(int d_out, int k) {
   GemvPlan pl;
   pl.n_tiles = ceil_div(d_out, kGemvTile);
-  const int target_groups = 512;
+  const int target_groups = gemv_target_groups();
   int splits = ceil_div(target_groups, pl.n_tiles);
   const int max_splits = k > 0 ? ceil_div(k, 64) : 1;   // at least 64 rows per chunk
   if (splits > max_splits) splits = max_splits;
@@ -454,24 +487,25 @@ extern "C" size_t bc_sparse_gemv_workspace_bytes(int d_out, int k) {
   return pl.n_splits > 1 ? pl.partial_bytes : 256;
 }
 
-extern "C" int bc_sparse_gemv(const uint16_t* wt, int d_in, int d_out, const uint16_t* x, const int32_t* idx,
-                              int k, uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
-  if (!wt || !x || !y) return set_error(BC_ERR_INVALID, "bc_sparse_gemv: NULL pointer");
-  if (d_in <= 0 || d_out <= 0) return set_error(BC_ERR_INVALID, "bc_sparse_gemv: d_in=%d d_out=%d", d_in, d_out);
-  if (d_out % 8 != 0) return set_error(BC_ERR_UNSUPPORTED, "bc_sparse_gemv: d_out %% 8 != 0 (%d)", d_out);
+static int sparse_gemv_impl(const uint16_t* wt, int tiled, int d_in, int d_out, const uint16_t* x,
+                            const int32_t* idx, int k, uint16_t* y, void* ws, size_t ws_bytes, void* stream,
+                            const char* name) {
+  if (!wt || !x || !y) return set_error(BC_ERR_INVALID, "%s: NULL pointer", name);
+  if (d_in <= 0 || d_out <= 0) return set_error(BC_ERR_INVALID, "%s: d_in=%d d_out=%d", name, d_in, d_out);
+  if (d_out % 8 != 0) return set_error(BC_ERR_UNSUPPORTED, "%s: d_out %% 8 != 0 (%d)", name, d_out);
   if (idx == nullptr) {
-    if (k != d_in) return set_error(BC_ERR_INVALID, "bc_sparse_gemv: dense call needs k == d_in");
+    if (k != d_in) return set_error(BC_ERR_INVALID, "%s: dense call needs k == d_in", name);
   } else if (k < 1 || k > d_in) {
-    return set_error(BC_ERR_INVALID, "bc_sparse_gemv: k=%d outside [1, %d]", k, d_in);
+    return set_error(BC_ERR_INVALID, "%s: k=%d outside [1, %d]", name, k, d_in);
   }
   if ((reinterpret_cast<uintptr_t>(wt) | reinterpret_cast<uintptr_t>(ws)) & 15)
-    return set_error(BC_ERR_INVALID, "bc_sparse_gemv: wt and ws must be 16-byte aligned");
+    return set_error(BC_ERR_INVALID, "%s: wt and ws must be 16-byte aligned", name);
   GemvPlan pl = plan_gemv(d_out, k);
   const size_t need = bc_sparse_gemv_workspace_bytes(d_out, k);
-  if (!ws || ws_bytes < need) return set_error(BC_ERR_WORKSPACE, "bc_sparse_gemv: workspace %zu < %zu", ws_bytes, need);
+  if (!ws || ws_bytes < need) return set_error(BC_ERR_WORKSPACE, "%s: workspace %zu < %zu", name, ws_bytes, need);
   hipStream_t s = static_cast<hipStream_t>(stream);
   GemvParams p{};
-  p.wt = wt; p.d_in = d_in; p.d_out = d_out; p.x = x; p.idx = idx; p.k = k;
+  p.wt = wt; p.tiled = tiled; p.d_in = d_in; p.d_out = d_out; p.x = x; p.idx = idx; p.k = k;
   p.rows_per_split = pl.rows_per_split; p.n_splits = pl.n_splits; p.n_tiles = pl.n_tiles;
   p.partial = static_cast<float*>(ws);
   p.y = y;
@@ -481,4 +515,15 @@ extern "C" int bc_sparse_gemv(const uint16_t* wt, int d_in, int d_out, const uin
   FinishParams f{};
   f.partial = p.partial; f.n_splits = pl.n_splits; f.d_out = d_out; f.y = y;
   return launch_finish(FIN_BF16, f, s);
+}
+
+extern "C" int bc_sparse_gemv(const uint16_t* wt, int d_in, int d_out, const uint16_t* x, const int32_t* idx,
+                              int k, uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  return sparse_gemv_impl(wt, 0, d_in, d_out, x, idx, k, y, ws, ws_bytes, stream, "bc_sparse_gemv");
+}
+
+extern "C" int bc_sparse_gemv_tiled(const uint16_t* wt_packed, int d_in, int d_out, const uint16_t* x,
+                                    const int32_t* idx, int k, uint16_t* y, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  return sparse_gemv_impl(wt_packed, 1, d_in, d_out, x, idx, k, y, ws, ws_bytes, stream, "bc_sparse_gemv_tiled");
 }

@@ -33,6 +33,7 @@ GemvPlan plan_gemv(int d_out, int k);
 
 struct GemvParams {
   const uint16_t* wt;
+  int tiled;              // 1: tile-major [tile][d_in][tile width]; 0: plain [d_in][d_out]
   int d_in, d_out;
   const uint16_t* x;
   const int32_t* idx;

@@ -53,16 +53,27 @@ __global__ void k_fill_zero(uint4* p, size_t n16, uint8_t* tail, size_t ntail) {
     for (size_t i = threadIdx.x; i < ntail; i += blockDim.x) tail[i] = 0;
 }
 
-__global__ __launch_bounds__(256) void k_pack_gate_up(const uint16_t* gate, const uint16_t* up, int d_ff,
-                                                     uint16_t* out) {
-  const size_t row = blockIdx.x;
-  const uint16_t* gr = gate + row * d_ff;
-  const uint16_t* ur = up + row * d_ff;
-  uint16_t* orow = out + row * size_t(2) * d_ff;
-  for (int c = threadIdx.x; c < 2 * d_ff; c += 256) {
+// Tile-major re-layout of W^T [d_in][d_out]: column tile t (kGemvTile wide,
+// the last one narrower) stores its d_in rows contiguously, each row as wide
+// as the tile.  With gate_up, the source columns are first interleaved per
+// tile: gate columns [64t, 64t + w) then up columns [64t, 64t + w),
+// w = min(64, d_ff - 64t), from two [d_in][d_ff] matrices (d_out = 2 d_ff).
+__global__ __launch_bounds__(256) void k_pack_tiles(const uint16_t* src, const uint16_t* src_up, int d_in,
+                                                   int d_out, uint16_t* out) {
+  const int row = blockIdx.x;
+  const int d_ff = d_out / 2;
+  for (int c = threadIdx.x; c < d_out; c += 256) {
     const int t = c / kGemvTile, off = c % kGemvTile;
-    const int w = min(kGemvTile / 2, d_ff - t * (kGemvTile / 2));
-    orow[c] = off < w ? gr[t * (kGemvTile / 2) + off] : ur[t * (kGemvTile / 2) + off - w];
+    const int tw = min(kGemvTile, d_out - t * kGemvTile);
+    uint16_t v;
+    if (src_up == nullptr) {
+      v = src[size_t(row) * d_out + c];
+    } else {
+      const int half = kGemvTile / 2;
+      const int w = min(half, d_ff - t * half);
+      v = off < w ? src[size_t(row) * d_ff + t * half + off] : src_up[size_t(row) * d_ff + t * half + off - w];
+    }
+    out[size_t(t) * kGemvTile * d_in + size_t(row) * tw + off] = v;
   }
 }
 
@@ -179,8 +190,17 @@ extern "C" int bc_pack_gate_up(const uint16_t* w_gate_t, const uint16_t* w_up_t,
                                void* stream) {
   if (!w_gate_t || !w_up_t || !w_gu) return set_error(BC_ERR_INVALID, "bc_pack_gate_up: NULL pointer");
   if (d <= 0 || d_ff <= 0 || d_ff % 8 != 0) return set_error(BC_ERR_INVALID, "bc_pack_gate_up: d=%d d_ff=%d", d, d_ff);
-  k_pack_gate_up<<<dim3(d), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(w_gate_t, w_up_t, d_ff, w_gu);
-  return check_launch("k_pack_gate_up");
+  k_pack_tiles<<<dim3(d), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(w_gate_t, w_up_t, d, 2 * d_ff, w_gu);
+  return check_launch("k_pack_tiles");
+}
+
+extern "C" int bc_pack_weight_tiles(const uint16_t* wt, int d_in, int d_out, uint16_t* packed, void* stream) {
+  if (!wt || !packed) return set_error(BC_ERR_INVALID, "bc_pack_weight_tiles: NULL pointer");
+  if (d_in <= 0 || d_out <= 0 || d_out % 8 != 0)
+    return set_error(BC_ERR_INVALID, "bc_pack_weight_tiles: d_in=%d d_out=%d", d_in, d_out);
+  if (wt == packed) return set_error(BC_ERR_INVALID, "bc_pack_weight_tiles: in-place packing is not supported");
+  k_pack_tiles<<<dim3(d_in), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(wt, nullptr, d_in, d_out, packed);
+  return check_launch("k_pack_tiles");
 }
 
 extern "C" size_t bc_layer_workspace_bytes(const bc_model_dims* dims, int max_ctx, int max_splits) {
@@ -195,7 +215,7 @@ int run_gemv(const uint16_t* wt, int d_in, int d_out, const uint16_t* x, const i
              int fin_kind, FinishParams f, hipStream_t s) {
   const GemvPlan pl = plan_gemv(d_out, k);
   GemvParams p{};
-  p.wt = wt; p.d_in = d_in; p.d_out = d_out; p.x = x; p.idx = idx; p.k = k;
+  p.wt = wt; p.tiled = 1; p.d_in = d_in; p.d_out = d_out; p.x = x; p.idx = idx; p.k = k;
   p.rows_per_split = pl.rows_per_split; p.n_splits = pl.n_splits; p.n_tiles = pl.n_tiles;
   p.partial = partial;
   int rc = launch_gemv_main(MAIN_PARTIAL, p, s);
@@ -369,7 +389,7 @@ extern "C" int bc_lm_head(const bc_model_dims* dims, const uint16_t* hidden, con
   rc = launch_norm_select(hidden, g_final, dims->d, float(rms_eps), at<uint16_t>(ws, L.x), dims->d, nullptr, s);
   if (rc != BC_OK) return rc;
   GemvParams p{};
-  p.wt = w_head_t; p.d_in = dims->d; p.d_out = dims->vocab; p.x = at<uint16_t>(ws, L.x); p.idx = nullptr;
+  p.wt = w_head_t; p.tiled = 1; p.d_in = dims->d; p.d_out = dims->vocab; p.x = at<uint16_t>(ws, L.x); p.idx = nullptr;
   p.k = dims->d; p.rows_per_split = dims->d; p.n_splits = 1; p.n_tiles = ceil_div(dims->vocab, kGemvTile);
   p.yf = logits; p.tile_max = at<float>(ws, L.logits_tile_max); p.tile_arg = at<int32_t>(ws, L.tile_arg);
   if ((rc = launch_gemv_main(MAIN_F32_ARGMAX, p, s)) != BC_OK) return rc;

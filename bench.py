@@ -104,20 +104,22 @@ class Model:
         self.layers = []
         for li in range(L):
             p = f"layer{li}/"
-            w_qkv = gen.device_normal_bf16(seed, p + "wqkv", (d, H * hd + 2 * Hkv * hd), 0.02)
-            w_o = gen.device_normal_bf16(seed, p + "wo", (H * hd, d), 0.02)
+            w_qkv = bc.packed_tiles(gen.device_normal_bf16(seed, p + "wqkv", (d, H * hd + 2 * Hkv * hd), 0.02))
+            w_o = bc.packed_tiles(gen.device_normal_bf16(seed, p + "wo", (H * hd, d), 0.02))
             gate = gen.device_normal_bf16(seed, p + "wgate", (d, dff), 0.02)
             up = gen.device_normal_bf16(seed, p + "wup", (d, dff), 0.02)
-            w_gu = torch.empty((d, 2 * dff), dtype=torch.int16, device="cuda")
+            w_gu = torch.empty(2 * d * dff, dtype=torch.int16, device="cuda")
             bc.bc_pack_gate_up(gate, up, w_gu)
             del gate, up
-            w_down = gen.device_normal_bf16(seed, p + "wdown", (dff, d), 0.02)
+            w_down = bc.packed_tiles(gen.device_normal_bf16(seed, p + "wdown", (dff, d), 0.02))
             k = gen.device_normal_bf16(seed, p + "kcache", (Hkv, max_ctx, hd), 1.0)
             v = gen.device_normal_bf16(seed, p + "vcache", (Hkv, max_ctx, hd), 1.0)
             summ = torch.empty((Hkv, max_ctx // 16, hd, 2), dtype=torch.int16, device="cuda")
             bc.bc_build_kv_summary(k, max_ctx, summ)
             self.layers.append(dict(w_qkv=w_qkv, w_o=w_o, w_gu=w_gu, w_down=w_down, k=k, v=v, summ=summ))
-        self.w_head = gen.device_normal_bf16(seed, "lm_head", (d, D["vocab"]), 0.02)
+        self.shapes = {"w_qkv": (d, H * hd + 2 * Hkv * hd), "w_o": (H * hd, d), "w_gu": (d, 2 * dff),
+                       "w_down": (dff, d)}
+        self.w_head = bc.packed_tiles(gen.device_normal_bf16(seed, "lm_head", (d, D["vocab"]), 0.02))
         h0 = gen.activation_bf16(seed, "h0", d)
         self.h0 = torch.from_numpy(h0.view(np.int16)).cuda()
         self.h = torch.empty_like(self.h0)
@@ -175,14 +177,14 @@ def time_graph(g, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def time_attention_kernel(model, n, reps=3):
+def time_attention_kernel(model, n, reps=3, S=None):
     """Average duration of bc_splitk_attn_partial over the 32 layers' caches
     (one launch per layer, as in the step), timed with events on the stream
     the kernels are launched on."""
     bc = model.bc
     D = DIMS
     H, Hkv, hd = D["n_heads"], D["n_kv_heads"], D["head_dim"]
-    S = bc.bc_attn_default_splits(n, Hkv)
+    S = S or bc.bc_attn_default_splits(n, Hkv)
     q = torch.randn((H, hd), dtype=torch.bfloat16, device="cuda").view(torch.int16)
     m = torch.empty((H, S), dtype=torch.float32, device="cuda")
     l = torch.empty_like(m)
@@ -203,13 +205,77 @@ def time_attention_kernel(model, n, reps=3):
     return us, attn_bytes(n, S, False), S
 
 
+def time_attention_sparse(model, n, r_kv, reps=3, S=None):
+    """bc_splitk_attn_partial over a scored selection (the list of a random
+    query), one launch per layer."""
+    bc = model.bc
+    D = DIMS
+    H, Hkv, hd = D["n_heads"], D["n_kv_heads"], D["head_dim"]
+    pol = bc.policy(r_kv, SINKS, WINDOW)
+    bud = bc.bc_kv_budget(n, pol)
+    t_sel = bud["t_sel"]
+    S = S or bc.bc_attn_default_splits(t_sel, Hkv)
+    q = torch.randn((H, hd), dtype=torch.bfloat16, device="cuda").view(torch.int16)
+    idx = torch.empty((Hkv, t_sel), dtype=torch.int32, device="cuda")
+    ws = torch.empty(bc.bc_kv_score_select_workspace_bytes(n, Hkv, pol) // 4 + 64, dtype=torch.int32, device="cuda")
+    bc.bc_kv_score_select(q, model.layers[0]["summ"], n, H, Hkv, hd, pol, idx, None, ws)
+    m = torch.empty((H, S), dtype=torch.float32, device="cuda")
+    l = torch.empty_like(m)
+    o = torch.empty((H, S, hd), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(hd)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for ly in model.layers[:4]:
+        bc.bc_splitk_attn_partial(q, ly["k"], ly["v"], idx, t_sel, H, Hkv, S, scale, m, l, o)
+    e0.record(s)
+    for _ in range(reps):
+        for ly in model.layers:
+            bc.bc_splitk_attn_partial(q, ly["k"], ly["v"], idx, t_sel, H, Hkv, S, scale, m, l, o)
+    e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / (reps * len(model.layers))
+    return us, attn_bytes(t_sel, S, True), S
+
+
+def kernel_table(model, contexts, split_sweep=None):
+    """Per-kernel achieved bandwidth of the hot kernels (one launch per layer,
+    rotating over the 32 layers' buffers)."""
+    rows = []
+    for S in split_sweep or []:
+        for n in contexts:
+            for r_kv in (1.0, 0.3):
+                if r_kv >= 1:
+                    us, b, _ = time_attention_kernel(model, n, S=S)
+                else:
+                    us, b, _ = time_attention_sparse(model, n, r_kv, S=S)
+                rows.append({"kernel": f"attn r_kv={r_kv} S={S}", "context": n, "us": round(us, 2), "bytes": b,
+                             "gbs": round(b / us / 1e3, 1), "splits": S})
+    for n in contexts:
+        us, b, S = time_attention_kernel(model, n)
+        rows.append({"kernel": "attn_partial dense", "context": n, "us": round(us, 2), "bytes": b,
+                     "gbs": round(b / us / 1e3, 1), "splits": S})
+        for r_kv in (0.3, 0.5):
+            us, b, S = time_attention_sparse(model, n, r_kv)
+            rows.append({"kernel": f"attn_partial r_kv={r_kv}", "context": n, "us": round(us, 2), "bytes": b,
+                         "gbs": round(b / us / 1e3, 1), "splits": S})
+    for which in ("w_qkv", "w_o", "w_gu", "w_down"):
+        for r_p in (1.0, 0.7, 0.5):
+            us, b, k = time_gemv_kernel(model, which, r_p)
+            rows.append({"kernel": f"gemv {which} r_p={r_p}", "us": round(us, 2), "bytes": b,
+                         "gbs": round(b / us / 1e3, 1), "k": k})
+    for r in rows:
+        log(f"[kernels] {r['kernel']:26s} {r.get('context', ''):>7} {r['us']:9.2f} us {r['gbs']:8.1f} GB/s "
+            f"({100 * r['gbs'] / HBM_PEAK_GBS:.1f}%)")
+    return rows
+
+
 def time_gemv_kernel(model, which="w_gu", r_p=1.0, reps=3):
     """Average duration of one bc_sparse_gemv launch over the 32 layers'
     matrices (dense or top-k channels of a fixed input)."""
     bc = model.bc
     from activation_kv_cache_amd import inputs as gen
-    w0 = model.layers[0][which]
-    d_in, d_out = w0.shape
+    d_in, d_out = model.shapes[which]
     k = channel_keep(r_p, d_in)
     x = torch.from_numpy(gen.activation_bf16(1, "gemvx", d_in).view(np.int16)).cuda()
     idx = None
@@ -220,14 +286,14 @@ def time_gemv_kernel(model, which="w_gu", r_p=1.0, reps=3):
     ws = torch.empty(bc.bc_sparse_gemv_workspace_bytes(d_out, k) // 4 + 64, dtype=torch.int32, device="cuda")
     bc.bc_workspace_init(ws)
     for ly in model.layers[:4]:
-        bc.bc_sparse_gemv(ly[which], x, idx, k, y, ws)
+        bc.bc_sparse_gemv_tiled(ly[which], d_in, d_out, x, idx, k, y, ws)
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
     for _ in range(reps):
         for ly in model.layers:
-            bc.bc_sparse_gemv(ly[which], x, idx, k, y, ws)
+            bc.bc_sparse_gemv_tiled(ly[which], d_in, d_out, x, idx, k, y, ws)
     e1.record(s)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1000.0 / (reps * len(model.layers))
@@ -260,15 +326,26 @@ def cpu_baseline(model, n):
         return t.cpu().numpy().view(np.uint16)
 
     d, dff = D["d"], D["d_ff"]
-    w_gu = h16(ly["w_gu"])
-    # undo the gate|up packing for the oracle's separate matrices
+
+    def untile(flat, d_in, d_out):
+        out = np.empty((d_in, d_out), np.uint16)
+        off = 0
+        for t in range(0, d_out, 128):
+            w = min(128, d_out - t)
+            out[:, t:t + w] = flat[off:off + d_in * w].reshape(d_in, w)
+            off += d_in * w
+        return out
+
+    gu = untile(h16(ly["w_gu"]), d, 2 * dff)
+    # undo the per-tile gate | up interleave for the oracle's separate matrices
     gate = np.empty((d, dff), np.uint16)
     up = np.empty((d, dff), np.uint16)
-    for t in range((dff + 255) // 256):
-        w = min(256, dff - 256 * t)
-        gate[:, 256 * t:256 * t + w] = w_gu[:, 512 * t:512 * t + w]
-        up[:, 256 * t:256 * t + w] = w_gu[:, 512 * t + w:512 * t + 2 * w]
-    W = dict(qkv=h16(ly["w_qkv"]), o=h16(ly["w_o"]), gate=gate, up=up, down=h16(ly["w_down"]),
+    for t in range((dff + 63) // 64):
+        w = min(64, dff - 64 * t)
+        gate[:, 64 * t:64 * t + w] = gu[:, 128 * t:128 * t + w]
+        up[:, 64 * t:64 * t + w] = gu[:, 128 * t + w:128 * t + 2 * w]
+    W = dict(qkv=untile(h16(ly["w_qkv"]), *model.shapes["w_qkv"]), o=untile(h16(ly["w_o"]), *model.shapes["w_o"]),
+             gate=gate, up=up, down=untile(h16(ly["w_down"]), *model.shapes["w_down"]),
              g1=h16(model.g_attn), g2=h16(model.g_mlp))
     K = h16(ly["k"][:, :n])
     V = h16(ly["v"][:, :n])
@@ -299,6 +376,8 @@ def main():
     ap.add_argument("--contexts", default="2048,8192,32768,131072")
     ap.add_argument("--cells", default="default", help="default | dense | none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernels", action="store_true", help="only the per-kernel bandwidth table")
+    ap.add_argument("--split-sweep", default="", help="attention split counts to sweep in --kernels")
     ap.add_argument("--attn-only", type=int, default=0,
                     help="only launch the dense attention kernel this many times per layer (for counters)")
     args = ap.parse_args()
@@ -314,6 +393,11 @@ def main():
     contexts = [int(c) for c in args.contexts.split(",")]
     head_n = max(contexts)
     model = Model(max_ctx=max(contexts))
+
+    if args.kernels:
+        sweep = [int(x) for x in args.split_sweep.split(",") if x]
+        print(json.dumps({"kernels": kernel_table(model, contexts, sweep)}))
+        return
 
     if args.attn_only:
         us, b, S = time_attention_kernel(model, head_n, reps=args.attn_only)

@@ -111,6 +111,11 @@ size_t bc_sparse_gemv_workspace_bytes(int d_out, int k);
 int bc_sparse_gemv(const uint16_t* wt, int d_in, int d_out, const uint16_t* x, const int32_t* idx,
                    int k, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
+/* The same GEMV (same kernel, same result bits) over W^T in the tile-major
+ * layout of bc_pack_weight_tiles, the layout bc_decode_layer reads. */
+int bc_sparse_gemv_tiled(const uint16_t* wt_packed, int d_in, int d_out, const uint16_t* x, const int32_t* idx,
+                         int k, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
 /* a4. Attention-scored KV selection (README "What it does": sinks, part of
  * the history and the recent entries), scored per 16-token block by an upper
  * bound of the query-key product built from per-block key minima and maxima.
@@ -179,11 +184,13 @@ int bc_attn_default_splits(int n_sel, int n_kv_heads);
  *   S3 = top-k(x2); f = SiLU(W_gate x2) * (W_up x2) over S3;
  *   S4 = top-k(f); h = h1 + W_down[:,S4] f[S4].
  * k = bc_channel_keep(r_p, d_in) per GEMV input; r_p >= 1 is dense. */
+/* Weights of a layer are W^T in the tile-major layout of
+ * bc_pack_weight_tiles (gate and up together through bc_pack_gate_up). */
 typedef struct {
-  const uint16_t* w_qkv;   /* bf16 [d][n_heads*hd + 2*n_kv_heads*hd]  (q | k | v) */
-  const uint16_t* w_o;     /* bf16 [n_heads*hd][d] */
-  const uint16_t* w_gu;    /* bf16 [d][2*d_ff] from bc_pack_gate_up */
-  const uint16_t* w_down;  /* bf16 [d_ff][d] */
+  const uint16_t* w_qkv;   /* packed W^T, d_in d, d_out n_heads*hd + 2*n_kv_heads*hd  (q | k | v) */
+  const uint16_t* w_o;     /* packed W^T, d_in n_heads*hd, d_out d */
+  const uint16_t* w_gu;    /* from bc_pack_gate_up, d_in d, d_out 2*d_ff */
+  const uint16_t* w_down;  /* packed W^T, d_in d_ff, d_out d */
   const uint16_t* g_attn;  /* bf16 [d] */
   const uint16_t* g_mlp;   /* bf16 [d] */
   uint16_t* k_cache;       /* bf16 [n_kv_heads][n_cap][hd] */
@@ -223,16 +230,27 @@ size_t bc_layer_workspace_bytes(const bc_model_dims* dims, int max_ctx, int max_
 int bc_decode_layer(const bc_model_dims* dims, const bc_layer* layer, const bc_step* step,
                     uint16_t* hidden, void* ws, size_t ws_bytes, void* stream);
 
-/* Packs W_gate^T and W_up^T (each bf16 [d][d_ff]) into the layout
- * bc_decode_layer reads: per row, groups of up to 64 gate columns followed
- * by the same up columns.  w_gu bf16 [d][2*d_ff].  (setup, not timed) */
+/* Tile-major re-layout of a W^T matrix for bc_decode_layer and bc_lm_head
+ * (setup, not timed): the columns are cut into tiles of 128 (the last one
+ * narrower, w_t columns); tile t stores its d_in rows contiguously, row i at
+ * packed + t*128*d_in + i*w_t.  A GEMV work-group that owns one tile and a
+ * chunk of rows then reads one contiguous block.  wt bf16 [d_in][d_out],
+ * packed bf16 (d_in*d_out elements, not aliasing wt); d_out % 8 == 0. */
+int bc_pack_weight_tiles(const uint16_t* wt, int d_in, int d_out, uint16_t* packed, void* stream);
+
+/* Packs W_gate^T and W_up^T (each bf16 [d][d_ff]) for bc_decode_layer: the
+ * columns are first interleaved per tile -- gate columns [64t, 64t + w) then
+ * up columns [64t, 64t + w), w = min(64, d_ff - 64t) -- and the result is laid
+ * out tile-major as bc_pack_weight_tiles does (d_in d, d_out 2*d_ff).
+ * (setup, not timed) */
 int bc_pack_gate_up(const uint16_t* w_gate_t, const uint16_t* w_up_t, int d, int d_ff, uint16_t* w_gu,
                     void* stream);
 
 /* a8 tail. Final RMSNorm and the dense LM head of the step (the LM head is
  * in the step's bytes: README "Quick start", the 1.60x bound):
  * logits = W_head (RMSNorm(h)*g), token = argmax (lowest index on ties).
- *   w_head_t bf16 [d][vocab]; logits fp32 [vocab]; token int32 [1]. */
+ *   w_head_t: W_head^T (d_in d, d_out vocab) packed by bc_pack_weight_tiles;
+ *   logits fp32 [vocab]; token int32 [1]. */
 size_t bc_lm_head_workspace_bytes(const bc_model_dims* dims);
 int bc_lm_head(const bc_model_dims* dims, const uint16_t* hidden, const uint16_t* g_final,
                const uint16_t* w_head_t, float* logits, int32_t* token, double rms_eps,

@@ -174,7 +174,10 @@ def test_splitk_attention_vs_oracle(name, dims, n_cap, n, r_kv, S, planted):
     assert np.all(gl[empty] == 0) and np.all(go[empty] == 0)
     ne = ~empty
     assert_close(gm[ne], rm[ne], "m", atol=1e-4, rtol=1e-5)
-    assert_close(gl[ne], rl[ne], "l", atol=1e-5, rtol=1e-4)
+    # the kernel rounds each softmax weight to bf16 before adding it into both
+    # l and o (bf16 x bf16 pairs into fp32 on v_dot2), so l carries a relative
+    # error up to 2^-8 against the exact sum
+    assert_close(gl[ne], rl[ne], "l", atol=1e-5, rtol=2.0 ** -8)
     assert_close((go / np.where(gl > 0, gl, 1)[..., None])[ne], (ro / np.where(rl > 0, rl, 1)[..., None])[ne], "o/l")
     rel = assert_close_bf16(host_u16(out), ref64, name)
     assert rel < 1e-2, f"rel-L2 {rel}"

@@ -36,7 +36,7 @@ def _run_layer(dims, n_cap, n, r_p, r_kv, sinks, window, n_splits, seed, k_std=0
         s = oracle.kv_summary(K[g], n - 1)
         summ[g, :s.shape[0]] = s
     w = {k: dev(v) for k, v in W.items()}
-    w_gu = torch.empty((d, 2 * dff), dtype=torch.int16, device="cuda")
+    w_gu = torch.empty(2 * d * dff, dtype=torch.int16, device="cuda")
     bc.bc_pack_gate_up(w["gate"], w["up"], w_gu)
     kc, vc, sm, hh = dev(K), dev(V), dev(summ), dev(h)
     md = bc.dims(dims)
@@ -51,7 +51,8 @@ def _run_layer(dims, n_cap, n, r_p, r_kv, sinks, window, n_splits, seed, k_std=0
              "idx_kv": (Hkv * n_sel, i32), "a": (H * D, i16), "idx_o": (k_d, i32), "h_mid": (d, i16),
              "x2": (d, i16), "idx_gu": (k_d, i32), "hff": (dff, i16), "idx_down": (k_ff, i32)}
     taps = {k: torch.full((n,), -1, dtype=t, device="cuda") for k, (n, t) in sizes.items()}
-    layer = bc.make_layer(w["qkv"], w["o"], w_gu, w["down"], w["g1"], w["g2"], kc, vc, sm)
+    layer = bc.make_layer(bc.packed_tiles(w["qkv"]), bc.packed_tiles(w["o"]), w_gu, bc.packed_tiles(w["down"]),
+                          w["g1"], w["g2"], kc, vc, sm)
     step = bc.make_step(n, r_p, pol, S, taps=bc.make_taps(**taps))
     bc.bc_decode_layer(md, layer, step, hh, ws)
     torch.cuda.synchronize()
@@ -128,7 +129,7 @@ def test_lm_head_tiny():
     ws = workspace(bc.bc_lm_head_workspace_bytes(md))
     logits = torch.empty(V, dtype=torch.float32, device="cuda")
     tok = torch.full((1,), -1, dtype=torch.int32, device="cuda")
-    bc.bc_lm_head(md, dev(h), dev(g), dev(wt), logits, tok, 1e-5, ws)
+    bc.bc_lm_head(md, dev(h), dev(g), bc.packed_tiles(dev(wt)), logits, tok, 1e-5, ws)
     torch.cuda.synchronize()
     _, y64, arg = oracle.lm_head(h, g, wt)
     lg = host(logits)
@@ -149,7 +150,7 @@ def test_lm_head_8b_sampled():
     ws = workspace(bc.bc_lm_head_workspace_bytes(md))
     logits = torch.empty(V, dtype=torch.float32, device="cuda")
     tok = torch.full((1,), -1, dtype=torch.int32, device="cuda")
-    bc.bc_lm_head(md, dev(h), dev(g), wt, logits, tok, 1e-5, ws)
+    bc.bc_lm_head(md, dev(h), dev(g), bc.packed_tiles(wt), logits, tok, 1e-5, ws)
     torch.cuda.synchronize()
     cols = np.sort(gen.rng(13, "lmcols").choice(V, 2048, replace=False))
     sub = host_u16(wt[:, torch.from_numpy(cols).cuda()].contiguous())
@@ -158,3 +159,42 @@ def test_lm_head_8b_sampled():
     lg = host(logits)
     assert_close(lg[cols], y64, "sampled logits")
     assert int(host(tok)[0]) == int(np.argmax(lg))
+
+
+def test_pack_layouts_bit_exact():
+    """bc_pack_weight_tiles and bc_pack_gate_up against a numpy re-layout."""
+    bc = _bc()
+    d_in, d_out = 96, 328            # two full tiles and a 72-wide one
+    wt = gen.normal_bf16(14, "pk", (d_in, d_out))
+    got = host_u16(bc.packed_tiles(dev(wt)))
+    want = []
+    for t in range(0, d_out, 128):
+        want.append(wt[:, t:t + 128].reshape(-1))
+    assert np.array_equal(got, np.concatenate(want))
+    d, dff = 40, 1408 // 8           # d_ff 176: groups of 64, 64, 48
+    gate = gen.normal_bf16(14, "pkg", (d, dff))
+    up = gen.normal_bf16(14, "pku", (d, dff))
+    out = torch.empty(2 * d * dff, dtype=torch.int16, device="cuda")
+    bc.bc_pack_gate_up(dev(gate), dev(up), out)
+    inter = np.concatenate([np.concatenate([gate[:, g:g + 64], up[:, g:g + 64]], axis=1)
+                            for g in range(0, dff, 64)], axis=1)
+    want = [inter[:, t:t + 128].reshape(-1) for t in range(0, 2 * dff, 128)]
+    assert np.array_equal(host_u16(out), np.concatenate(want))
+
+
+def test_tiled_gemv_equals_plain():
+    """The tile-major layout gives the same result bits as the plain one."""
+    bc = _bc()
+    d_in, d_out = 4096, 6144
+    wt = gen.normal_bf16(15, "tg", (d_in, d_out), 0.02)
+    x = gen.activation_bf16(15, "tgx", d_in)
+    for r_p in (1.0, 0.5):
+        k = oracle.channel_keep(r_p, d_in)
+        idx = None if r_p >= 1 else dev(oracle.select_channels(x, k))
+        ws = workspace(bc.bc_sparse_gemv_workspace_bytes(d_out, k))
+        y1 = torch.empty(d_out, dtype=torch.int16, device="cuda")
+        y2 = torch.empty(d_out, dtype=torch.int16, device="cuda")
+        bc.bc_sparse_gemv(dev(wt), dev(x), idx, k, y1, ws)
+        bc.bc_sparse_gemv_tiled(bc.packed_tiles(dev(wt)), d_in, d_out, dev(x), idx, k, y2, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2)
