@@ -86,6 +86,9 @@ _SIG = {
     "bc_pack_gate_up": (c_int, [P, P, c_int, c_int, P, P]),
     "bc_pack_weight_tiles": (c_int, [P, c_int, c_int, P, P]),
     "bc_lm_head_workspace_bytes": (c_size_t, [ctypes.POINTER(bc_model_dims)]),
+    "bc_step_workspace_bytes": (c_size_t, [ctypes.POINTER(bc_model_dims), c_int, c_int]),
+    "bc_decode_step": (c_int, [ctypes.POINTER(bc_model_dims), ctypes.POINTER(bc_layer), c_int, P, P,
+                               ctypes.POINTER(bc_step), P, P, P, P, c_size_t, P]),
     "bc_lm_head": (c_int, [ctypes.POINTER(bc_model_dims), P, P, P, P, P, c_double, P, c_size_t, P]),
 }
 for _name, (_res, _args) in _SIG.items():
@@ -274,3 +277,23 @@ def bc_lm_head(md: bc_model_dims, hidden, g_final, w_head_t, logits, token, rms_
     p, n = _ws(ws)
     return _check(_lib.bc_lm_head(ctypes.byref(md), _ptr(hidden), _ptr(g_final), _ptr(w_head_t), _ptr(logits),
                                   _ptr(token), float(rms_eps), p, n, _stream(stream)), "bc_lm_head")
+
+
+def bc_step_workspace_bytes(md: bc_model_dims, max_ctx: int, max_splits: int) -> int:
+    return _lib.bc_step_workspace_bytes(ctypes.byref(md), int(max_ctx), int(max_splits))
+
+
+def make_layer_array(layers):
+    """A ctypes array of bc_layer structs (kept alive by the caller)."""
+    arr = (bc_layer * len(layers))()
+    for i, ly in enumerate(layers):
+        arr[i] = ly
+    return arr
+
+
+def bc_decode_step(md: bc_model_dims, layer_array, g_final, w_head, step: bc_step, hidden, logits, token, ws,
+                   stream=None):
+    p, n = _ws(ws)
+    return _check(_lib.bc_decode_step(ctypes.byref(md), layer_array, len(layer_array), _ptr(g_final), _ptr(w_head),
+                                      ctypes.byref(step), _ptr(hidden), _ptr(logits), _ptr(token), p, n,
+                                      _stream(stream)), "bc_decode_step")

@@ -53,6 +53,51 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Cross-lane shuffles through LDS (ds_bpermute) cost about as much as a
+// barrier on this chip; the helpers below use DPP (row operations at VALU
+// latency) and v_readlane instead.
+
+// Integer sum over the 64 lanes of a wave; the result is wave-uniform.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += dpp_u<0xB1>(v);     // xor 1
+  v += dpp_u<0x4E>(v);     // xor 2
+  v += dpp_u<0x141>(v);    // half mirror: xor 4 on uniform quads
+  v += dpp_u<0x140>(v);    // mirror: xor 8 on uniform halves
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 0)) + uint32_t(__builtin_amdgcn_readlane(int(v), 16)) +
+         uint32_t(__builtin_amdgcn_readlane(int(v), 32)) + uint32_t(__builtin_amdgcn_readlane(int(v), 48));
+}
+
+// Float sum over the 64 lanes with a fixed order (row butterflies, then the
+// four row sums in row order); the result is wave-uniform.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP: shifts within 16-lane
+// rows, then row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v) {
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x111, 0xF, 0xF, true));   // row_shr:1
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x112, 0xF, 0xF, true));   // row_shr:2
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x114, 0xF, 0xF, true));   // row_shr:4
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x118, 0xF, 0xF, true));   // row_shr:8
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15 -> rows 1, 3
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x143, 0xC, 0xF, false));  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
 __device__ __forceinline__ int wave_lane() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
@@ -101,8 +146,214 @@ struct TopkSmem {
   uint32_t hist[NT / kWave][256];
   uint32_t wave_gt[NT / kWave];
   uint32_t wave_eq[NT / kWave];
+  uint32_t cnt[2][NT / kWave][8];
+  uint32_t scan[NT / kWave + 1];
   uint32_t sel_bin, sel_above;
 };
+
+// Keys per thread of the register path of block_topk.
+constexpr int kTopkRegKeys = 16;
+
+// Exact top-k when n <= NT * kTopkRegKeys and the keys are in sm.keys
+// (synchronised).  Thread t owns positions [t*E, t*E + E), E = ceil(n/NT),
+// held in registers.  Radix passes of 4-bit digits from the top: each thread
+// counts its keys per digit in packed 8-bit fields (no atomics), the wave
+// adds them as 16-bit fields, wave 0 adds the waves and picks the digit.
+// Then one block scan of (ties, greater) counts places every kept position:
+// the ties kept before thread t are min(ties before t, ties needed).
+template <int NT, int BITS, typename KeyT, typename EmitFn>
+__device__ void block_topk_reg(int n, int k, EmitFn emit, TopkSmem<NT, KeyT>& sm) {
+  constexpr int NW = NT / kWave;
+  constexpr int NPASS = (BITS + 3) / 4;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int E = (n + NT - 1) / NT;
+  const int i0 = tid * E;
+  // positions past n hold key 0 and are excluded by the valid count nv
+  const int nv = max(0, min(E, n - i0));
+  uint32_t key[kTopkRegKeys];
+#pragma unroll
+  for (int e = 0; e < kTopkRegKeys; ++e) key[e] = e < nv ? uint32_t(sm.keys[i0 + e]) : 0u;
+  uint32_t prefix = 0, k_rem = uint32_t(k);
+  int decided = 0;
+  const uint32_t keymask = BITS == 32 ? ~0u : ((1u << BITS) - 1u);
+#pragma unroll
+  for (int pass = 0; pass < NPASS; ++pass) {
+    const int width = (BITS - decided) >= 4 ? 4 : (BITS - decided);
+    const int shift = BITS - decided - width;
+    const uint32_t hi_mask = decided == 0 ? 0u : ((~0u << (BITS - decided)) & keymask);
+    uint64_t c_lo = 0, c_hi = 0;
+#pragma unroll
+    for (int e = 0; e < kTopkRegKeys; ++e) {
+      if (e < nv && ((key[e] ^ prefix) & hi_mask) == 0) {
+        const uint32_t d = (key[e] >> shift) & 15u;
+        const uint64_t one = 1ull << (8 * (d & 7u));
+        if (d < 8) c_lo += one; else c_hi += one;
+      }
+    }
+    // 16 digits as 16-bit fields of 8 words: word i holds digits 2i, 2i+1
+    uint32_t* cnt = sm.cnt[pass & 1][w];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = uint32_t((c_lo >> (16 * i)) & 0xFF) | (uint32_t((c_lo >> (16 * i + 8)) & 0xFF) << 16);
+      const uint32_t hi = uint32_t((c_hi >> (16 * i)) & 0xFF) | (uint32_t((c_hi >> (16 * i + 8)) & 0xFF) << 16);
+      const uint32_t slo = wave_sum_u32(lo), shi = wave_sum_u32(hi);
+      if (lane == 0) { cnt[i] = slo; cnt[4 + i] = shi; }
+    }
+    __syncthreads();
+    // every wave picks the digit (no second barrier): lane L < 16 owns digit
+    // 15 - L, so the lane prefix is the count of keys with larger digits
+    const int d = 15 - lane;
+    uint32_t c = 0;
+    if (lane < 16)
+      for (int ww = 0; ww < NW; ++ww) c += (sm.cnt[pass & 1][ww][d >> 1] >> (16 * (d & 1))) & 0xFFFFu;
+    const uint32_t inc = wave_scan_dpp(c);
+    const uint32_t ex = inc - c;
+    const uint64_t hit = __ballot(lane < 16 && ex < k_rem && k_rem <= inc);
+    const int hl = __ffsll((long long)hit) - 1;
+    const uint32_t sel_d = uint32_t(15 - hl);
+    const uint32_t above = uint32_t(__builtin_amdgcn_readlane(int(ex), hl));
+    prefix |= sel_d << shift;
+    k_rem -= above;
+    decided += width;
+  }
+  const uint32_t thr = prefix, need = k_rem;
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int e = 0; e < kTopkRegKeys; ++e) {
+    gt += (e < nv && key[e] > thr) ? 1u : 0u;
+    eq += (e < nv && key[e] == thr) ? 1u : 0u;
+  }
+  // exclusive block scan of (eq << 16 | gt)
+  const uint32_t v = (eq << 16) | gt;
+  const uint32_t inc = wave_scan_dpp(v);
+  if (lane == kWave - 1) sm.scan[w] = inc;
+  __syncthreads();
+  uint32_t before = inc - v;
+  for (int ww = 0; ww < w; ++ww) before += sm.scan[ww];
+  const uint32_t gt_before = before & 0xFFFFu, eq_before = before >> 16;
+  uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
+  uint32_t tie = eq_before;
+#pragma unroll
+  for (int e = 0; e < kTopkRegKeys; ++e) {
+    if (e >= nv) continue;
+    if (key[e] > thr) {
+      emit(int(pos++), i0 + e);
+    } else if (key[e] == thr) {
+      if (tie < need) emit(int(pos++), i0 + e);
+      ++tie;
+    }
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------- 15-bit keys, one histogram pass
+// Exact top-k of n <= 16384 keys below 2^15 (bf16 magnitudes) with 1024
+// threads: thread t owns positions [t*E, t*E + E), E = ceil(n/1024), its keys
+// in registers.  One pass of LDS atomics builds the full 32768-bin histogram
+// (equal keys in one wave instruction are rare, so the atomics hardly
+// collide); a block scan over the bins, taken from the largest key down,
+// finds the threshold key thr and the number `need` of keys equal to thr that
+// are kept; one block scan of (ties, greater) counts then places every kept
+// position (ties kept before thread t: min(ties before t, need)).
+constexpr int kTopk15Threads = 1024;
+constexpr int kTopk15MaxN = kTopk15Threads * 16;
+
+struct Topk15Smem {
+  uint32_t hist[32768];
+  uint32_t wtot[kTopk15Threads / kWave];
+  uint32_t thr, above;
+};
+
+template <typename KeyFn, typename EmitFn>
+__device__ void block_topk15(int n, int k, KeyFn key_of, EmitFn emit, Topk15Smem& sm) {
+  constexpr int NT = kTopk15Threads;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int E = (n + NT - 1) / NT;
+  const int i0 = tid * E;
+  const int nv = max(0, min(E, n - i0));
+  if (k >= n) {
+    for (int e = 0; e < nv; ++e) emit(i0 + e, i0 + e);
+    return;
+  }
+  if (k <= 0) return;
+  uint32_t key[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) key[e] = e < nv ? (uint32_t(key_of(i0 + e)) & 0x7FFFu) : 0u;
+  uint4* h4 = reinterpret_cast<uint4*>(sm.hist);
+  for (int i = tid; i < 32768 / 4; i += NT) h4[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if (e < nv) atomicAdd(&sm.hist[key[e]], 1u);
+  __syncthreads();
+  // thread t owns the 32 bins [b0, b0 + 32), b0 = 32768 - 32 (t + 1): the
+  // largest keys go to thread 0, so the prefix over threads counts larger keys
+  const int b0 = 32768 - 32 * (tid + 1);
+  // neighbouring threads' ranges are 128 B apart (one LDS bank): read the
+  // eight 16-byte pieces in a thread-rotated order to spread the banks
+  uint32_t bins[32];
+  uint32_t local = 0;
+  {
+    const uint4* hb = reinterpret_cast<const uint4*>(sm.hist + b0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int jj = (j + tid) & 7;
+      const uint4 c = hb[jj];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (q == jj) {
+          bins[4 * q] = c.x; bins[4 * q + 1] = c.y; bins[4 * q + 2] = c.z; bins[4 * q + 3] = c.w;
+        }
+      }
+      local += (c.x + c.y) + (c.z + c.w);
+    }
+  }
+  const uint32_t winc = wave_scan_dpp(local);
+  if (lane == kWave - 1) sm.wtot[w] = winc;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int ww = 0; ww < w; ++ww) before += sm.wtot[ww];
+  const uint32_t inc = before + winc, ex = inc - local;
+  const uint32_t ku = uint32_t(k);
+  if (ex < ku && ku <= inc) {
+    uint32_t run = ex;
+#pragma unroll
+    for (int j = 31; j >= 0; --j) {
+      const uint32_t c = bins[j];
+      if (run < ku && ku <= run + c) { sm.thr = uint32_t(b0 + j); sm.above = run; }
+      run += c;
+    }
+  }
+  __syncthreads();
+  const uint32_t thr = sm.thr, need = ku - sm.above;
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    gt += (e < nv && key[e] > thr) ? 1u : 0u;
+    eq += (e < nv && key[e] == thr) ? 1u : 0u;
+  }
+  const uint32_t v = (eq << 16) | gt;
+  const uint32_t vinc = wave_scan_dpp(v);
+  __syncthreads();
+  if (lane == kWave - 1) sm.wtot[w] = vinc;
+  __syncthreads();
+  uint32_t vb = vinc - v;
+  for (int ww = 0; ww < w; ++ww) vb += sm.wtot[ww];
+  const uint32_t gt_before = vb & 0xFFFFu, eq_before = vb >> 16;
+  uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
+  uint32_t tie = eq_before;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    if (e >= nv) continue;
+    if (key[e] > thr) {
+      emit(int(pos++), i0 + e);
+    } else if (key[e] == thr) {
+      if (tie < need) emit(int(pos++), i0 + e);
+      ++tie;
+    }
+  }
+  __syncthreads();
+}
 
 // Exact top-k over n integer keys given by key_fn(i) (the low BITS bits are
 // used; BITS in {15, 32}).  Keeps the k largest keys, equal keys by lower
@@ -116,7 +367,8 @@ struct TopkSmem {
 //      keys > thr and == thr give every wave its tie allowance and output
 //      offset; a ballot pass then emits the kept positions in order.
 template <int NT, int BITS, typename KeyT, typename KeyFn, typename EmitFn>
-__device__ void block_topk(int n, int k, KeyFn key_fn, EmitFn emit, TopkSmem<NT, KeyT>& sm) {
+__device__ void block_topk(int n, int k, KeyFn key_fn, EmitFn emit, TopkSmem<NT, KeyT>& sm,
+                           bool keys_staged = false) {
   constexpr int NW = NT / kWave;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
@@ -125,9 +377,15 @@ __device__ void block_topk(int n, int k, KeyFn key_fn, EmitFn emit, TopkSmem<NT,
     return;
   }
   if (k <= 0) return;
-  const bool staged = n <= TopkSmem<NT, KeyT>::CAP;
-  if (staged) {
+  // keys_staged: the caller already wrote sm.keys[0..n) and synchronised
+  const bool staged = keys_staged || n <= TopkSmem<NT, KeyT>::CAP;
+  if (staged && !keys_staged) {
     for (int i = tid; i < n; i += NT) sm.keys[i] = KeyT(key_fn(i));
+  }
+  if (staged && n <= NT * kTopkRegKeys) {
+    if (!keys_staged) __syncthreads();
+    block_topk_reg<NT, BITS, KeyT>(n, k, emit, sm);
+    return;
   }
   auto key = [&](int i) -> uint32_t { return staged ? uint32_t(sm.keys[i]) : uint32_t(key_fn(i)); };
 

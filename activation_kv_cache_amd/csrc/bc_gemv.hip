@@ -280,7 +280,10 @@ __global__ __launch_bounds__(64) void k_finish_qkv(const FinishParams p) {
 constexpr int kOneGroup = 1024;
 
 struct OneGroupSmem {
-  TopkSmem<kOneGroup, uint16_t> topk;
+  union {
+    TopkSmem<kOneGroup, uint16_t> topk;
+    Topk15Smem topk15;
+  };
   float part[kOneGroup / kWave];
 };
 
@@ -292,8 +295,7 @@ __device__ float one_group_sum_squares(const uint16_t* x, int n, float* part) {
     const float v = bf16_to_f32(x[i]);
     s += v * v;
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, kWave);
+  s = wave_sum_f32(s);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
   __syncthreads();
   float t = 0.f;
@@ -303,11 +305,13 @@ __device__ float one_group_sum_squares(const uint16_t* x, int n, float* part) {
   return t;
 }
 
-__device__ void one_group_select(const uint16_t* x, int n, int k, int32_t* idx_out,
-                                 TopkSmem<kOneGroup, uint16_t>& sm) {
+__device__ void one_group_select(const uint16_t* x, int n, int k, int32_t* idx_out, OneGroupSmem& sm) {
   auto key = [x](int i) -> uint32_t { return uint32_t(x[i]) & 0x7FFFu; };
   auto emit = [idx_out](int r, int i) { idx_out[r] = i; };
-  block_topk<kOneGroup, 15, uint16_t>(n, k, key, emit, sm);
+  if (n <= kTopk15MaxN)
+    block_topk15(n, k, key, emit, sm.topk15);
+  else
+    block_topk<kOneGroup, 15, uint16_t>(n, k, key, emit, sm.topk);
 }
 
 // One work-group: y = bf16(resid + sum of chunks); then optionally
@@ -333,7 +337,7 @@ __global__ __launch_bounds__(kOneGroup) void k_finish_resid(const FinishParams p
   for (int c = threadIdx.x; c < p.d_out; c += kOneGroup)
     p.x_next[c] = f32_to_bf16(bf16_to_f32(p.y[c]) * inv * bf16_to_f32(p.norm_gain[c]));
   __syncthreads();
-  if (p.sel_k > 0 && p.sel_k < p.d_out) one_group_select(p.x_next, p.d_out, p.sel_k, p.idx_next, sm.topk);
+  if (p.sel_k > 0 && p.sel_k < p.d_out) one_group_select(p.x_next, p.d_out, p.sel_k, p.idx_next, sm);
 }
 
 // SwiGLU over the packed gate | up chunks: tile t holds gate columns
@@ -361,7 +365,7 @@ __global__ __launch_bounds__(kOneGroup) void k_finish_swiglu(const FinishParams 
   }
   if (p.sel_k <= 0 || p.sel_k >= p.d_ff) return;
   __syncthreads();
-  one_group_select(p.y, p.d_ff, p.sel_k, p.idx_next, sm.topk);
+  one_group_select(p.y, p.d_ff, p.sel_k, p.idx_next, sm);
 }
 
 __global__ __launch_bounds__(256) void k_argmax_finish(const float* tile_max, const int32_t* tile_arg, int n_tiles,
@@ -391,7 +395,7 @@ __global__ __launch_bounds__(256) void k_argmax_finish(const float* tile_max, co
 }
 
 __global__ __launch_bounds__(kOneGroup) void k_select(const uint16_t* x, int n, int k, int32_t* idx_out) {
-  __shared__ TopkSmem<kOneGroup, uint16_t> sm;
+  __shared__ OneGroupSmem sm;
   one_group_select(x, n, k, idx_out, sm);
 }
 
@@ -403,7 +407,7 @@ __global__ __launch_bounds__(kOneGroup) void k_norm_select(const uint16_t* h, co
   for (int i = threadIdx.x; i < d; i += kOneGroup)
     x_out[i] = f32_to_bf16(bf16_to_f32(h[i]) * inv * bf16_to_f32(g[i]));
   __syncthreads();
-  if (idx_out != nullptr && k > 0 && k < d) one_group_select(x_out, d, k, idx_out, sm.topk);
+  if (idx_out != nullptr && k > 0 && k < d) one_group_select(x_out, d, k, idx_out, sm);
 }
 
 }  // namespace

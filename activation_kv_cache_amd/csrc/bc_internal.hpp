@@ -92,6 +92,8 @@ struct ReduceParams {
   uint16_t* out;
 };
 int launch_attn_reduce(const ReduceParams& p, hipStream_t s);
+// merge and, when 0 < k < n_heads*head_dim, the top-k of the merged output
+int launch_attn_reduce_select(const ReduceParams& p, int k, int32_t* idx_out, hipStream_t s);
 
 struct KvSelectParams {
   const uint16_t* q;

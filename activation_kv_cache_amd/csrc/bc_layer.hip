@@ -228,34 +228,48 @@ int run_gemv(const uint16_t* wt, int d_in, int d_out, const uint16_t* x, const i
 
 }  // namespace
 
-extern "C" int bc_decode_layer(const bc_model_dims* dims, const bc_layer* ly, const bc_step* st, uint16_t* hidden,
-                               void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_dims(dims);
-  if (rc != BC_OK) return rc;
-  if (!ly || !st || !hidden || !ws) return set_error(BC_ERR_INVALID, "bc_decode_layer: NULL argument");
+namespace {
+
+// What the layer does with its output besides writing h: the RMSNorm of h
+// with next_gain into next_x and, when next_sel_k > 0, its top-k into
+// next_idx (the next layer's x1 and S1, or the final norm before the head).
+struct LayerChain {
+  bool x1_ready;               // x1 / idx_qkv already in the workspace
+  const uint16_t* next_gain;
+  uint16_t* next_x;
+  int next_sel_k;
+  int32_t* next_idx;
+};
+
+int check_layer(const bc_layer* ly, const bc_step* st) {
   if (!ly->w_qkv || !ly->w_o || !ly->w_gu || !ly->w_down || !ly->g_attn || !ly->g_mlp || !ly->k_cache ||
       !ly->v_cache)
-    return set_error(BC_ERR_INVALID, "bc_decode_layer: NULL layer pointer");
-  if (ly->n_cap <= 0 || ly->n_cap % 16 != 0) return set_error(BC_ERR_INVALID, "bc_decode_layer: n_cap %% 16 != 0");
+    return set_error(BC_ERR_INVALID, "NULL layer pointer");
+  if (ly->n_cap <= 0 || ly->n_cap % 16 != 0) return set_error(BC_ERR_INVALID, "n_cap %% 16 != 0");
   if (st->n_ctx < 1 || st->n_ctx > ly->n_cap)
-    return set_error(BC_ERR_INVALID, "bc_decode_layer: n_ctx=%d outside [1, n_cap=%d]", st->n_ctx, ly->n_cap);
-  if (!(st->r_p > 0.0)) return set_error(BC_ERR_INVALID, "bc_decode_layer: r_p must be > 0");
-  if (!(st->rms_eps >= 0.0) || !(st->rope_theta > 0.0)) return set_error(BC_ERR_INVALID, "bc_decode_layer: eps/theta");
-  const bool kv_sparse = st->kv.r_kv < 1.0;
-  if (kv_sparse && !ly->kv_summary) return set_error(BC_ERR_INVALID, "bc_decode_layer: r_kv < 1 needs kv_summary");
-  bc_kv_budget_info bud;
-  rc = bc_kv_budget(st->n_ctx, &st->kv, &bud);
-  if (rc != BC_OK) return rc;
-  const bc_model_dims& m = *dims;
-  const int hd = m.head_dim, H = m.n_heads, Hkv = m.n_kv_heads;
-  const int n_sel = kv_sparse ? bud.t_sel : st->n_ctx;
-  const int n_splits = st->n_splits > 0 ? st->n_splits : bc_attn_default_splits(n_sel, Hkv);
-  if (n_splits > 4096) return set_error(BC_ERR_INVALID, "bc_decode_layer: n_splits=%d", n_splits);
-  const LayerLayout L = layer_layout(m, st->n_ctx, n_splits);
-  if (ws_bytes < L.total) return set_error(BC_ERR_WORKSPACE, "bc_decode_layer: workspace %zu < %zu", ws_bytes, L.total);
-  if (reinterpret_cast<uintptr_t>(ws) & 255) return set_error(BC_ERR_INVALID, "bc_decode_layer: ws not 256-byte aligned");
+    return set_error(BC_ERR_INVALID, "n_ctx=%d outside [1, n_cap=%d]", st->n_ctx, ly->n_cap);
+  if (st->kv.r_kv < 1.0 && !ly->kv_summary) return set_error(BC_ERR_INVALID, "r_kv < 1 needs kv_summary");
+  return BC_OK;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
+int check_step(const bc_step* st) {
+  if (!(st->r_p > 0.0)) return set_error(BC_ERR_INVALID, "r_p must be > 0");
+  if (!(st->rms_eps >= 0.0) || !(st->rope_theta > 0.0)) return set_error(BC_ERR_INVALID, "eps/theta out of range");
+  if (st->n_splits < 0 || st->n_splits > 4096) return set_error(BC_ERR_INVALID, "n_splits=%d", st->n_splits);
+  return BC_OK;
+}
+
+int step_splits(const bc_model_dims& m, const bc_step* st, const bc_kv_budget_info& bud) {
+  const int n_sel = st->kv.r_kv < 1.0 ? bud.t_sel : st->n_ctx;
+  return st->n_splits > 0 ? st->n_splits : bc_attn_default_splits(n_sel, m.n_kv_heads);
+}
+
+int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, const bc_kv_budget_info& bud,
+               int n_splits, uint16_t* hidden, void* ws, const LayerLayout& L, hipStream_t s, const LayerChain& ch) {
+  int rc;
+  const int hd = m.head_dim, H = m.n_heads, Hkv = m.n_kv_heads;
+  const bool kv_sparse = st->kv.r_kv < 1.0;
+  const int n_sel = kv_sparse ? bud.t_sel : st->n_ctx;
   const bool sparse = st->r_p < 1.0;
   const int k_d = bc_channel_keep(st->r_p, m.d);
   const int k_ff = bc_channel_keep(st->r_p, m.d_ff);
@@ -269,14 +283,17 @@ extern "C" int bc_decode_layer(const bc_model_dims* dims, const bc_layer* ly, co
   int32_t* idx_down = sparse ? at<int32_t>(ws, L.idx_down) : nullptr;
 
   // x1 = RMSNorm(h), S1
-  rc = launch_norm_select(hidden, ly->g_attn, m.d, eps, at<uint16_t>(ws, L.x1), k_d, idx_qkv, s);
-  if (rc != BC_OK) return rc;
+  if (!ch.x1_ready) {
+    rc = launch_norm_select(hidden, ly->g_attn, m.d, eps, at<uint16_t>(ws, L.x1), k_d, idx_qkv, s);
+    if (rc != BC_OK) return rc;
+  }
 
   // q, k, v; rotary; append; summary
   {
     FinishParams f{};
     f.q_out = at<uint16_t>(ws, L.q); f.k_cache = ly->k_cache; f.v_cache = ly->v_cache; f.summary = ly->kv_summary;
-    f.n_heads = H; f.n_kv_heads = Hkv; f.head_dim = hd; f.n_cap = ly->n_cap; f.pos = pos; f.log2_theta = log2(st->rope_theta);
+    f.n_heads = H; f.n_kv_heads = Hkv; f.head_dim = hd; f.n_cap = ly->n_cap; f.pos = pos;
+    f.log2_theta = log2(st->rope_theta);
     rc = run_gemv(ly->w_qkv, m.d, qkv_out, at<uint16_t>(ws, L.x1), idx_qkv, k_d, partial, FIN_QKV, f, s);
     if (rc != BC_OK) return rc;
   }
@@ -302,9 +319,8 @@ extern "C" int bc_decode_layer(const bc_model_dims* dims, const bc_layer* ly, co
     ReduceParams r{};
     r.m = p.m; r.l = p.l; r.o = p.o; r.n_heads = H; r.n_splits = n_splits; r.head_dim = hd;
     r.out = at<uint16_t>(ws, L.a);
-    if ((rc = launch_attn_reduce(r, s)) != BC_OK) return rc;
-    if (sparse && k_d < H * hd && (rc = launch_select(at<uint16_t>(ws, L.a), H * hd, k_d, idx_o, s)) != BC_OK)
-      return rc;
+    rc = sparse ? launch_attn_reduce_select(r, k_d, idx_o, s) : launch_attn_reduce(r, s);
+    if (rc != BC_OK) return rc;
   }
 
   // h1 = h + W_o a; x2 = RMSNorm(h1); S3
@@ -324,10 +340,11 @@ extern "C" int bc_decode_layer(const bc_model_dims* dims, const bc_layer* ly, co
     if (rc != BC_OK) return rc;
   }
 
-  // h = h1 + W_down f
+  // h = h1 + W_down f; optionally the next input's RMSNorm and top-k
   {
     FinishParams f{};
     f.y = hidden; f.resid = at<uint16_t>(ws, L.h_mid);
+    f.norm_gain = ch.next_gain; f.eps = eps; f.x_next = ch.next_x; f.sel_k = ch.next_sel_k; f.idx_next = ch.next_idx;
     rc = run_gemv(ly->w_down, m.d_ff, m.d, at<uint16_t>(ws, L.hff), idx_down, k_ff, partial, FIN_RESID, f, s);
     if (rc != BC_OK) return rc;
   }
@@ -352,6 +369,85 @@ extern "C" int bc_decode_layer(const bc_model_dims* dims, const bc_layer* ly, co
     if (sparse && (rc = copy_tap(t->idx_down, idx_down, size_t(k_ff) * 4, s)) != BC_OK) return rc;
   }
   return BC_OK;
+}
+
+// Head extras placed after the layer layout in a step workspace.
+struct StepLayout { LayerLayout layer; size_t xh, tile_max, tile_arg, total; };
+StepLayout step_layout(const bc_model_dims& m, int n_ctx, int n_splits) {
+  StepLayout S;
+  S.layer = layer_layout(m, n_ctx, n_splits);
+  size_t off = S.layer.total;
+  auto take = [&off](size_t bytes) { size_t o = off; off += align_up(bytes > 0 ? bytes : 1, 256); return o; };
+  const int n_tiles = ceil_div(m.vocab, kGemvTile);
+  S.xh = take(size_t(m.d) * 2);
+  S.tile_max = take(size_t(n_tiles) * 4);
+  S.tile_arg = take(size_t(n_tiles) * 4);
+  S.total = off;
+  return S;
+}
+
+}  // namespace
+
+extern "C" int bc_decode_layer(const bc_model_dims* dims, const bc_layer* ly, const bc_step* st, uint16_t* hidden,
+                               void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != BC_OK) return rc;
+  if (!ly || !st || !hidden || !ws) return set_error(BC_ERR_INVALID, "bc_decode_layer: NULL argument");
+  if ((rc = check_layer(ly, st)) != BC_OK || (rc = check_step(st)) != BC_OK) return rc;
+  bc_kv_budget_info bud;
+  if ((rc = bc_kv_budget(st->n_ctx, &st->kv, &bud)) != BC_OK) return rc;
+  const int n_splits = step_splits(*dims, st, bud);
+  const LayerLayout L = layer_layout(*dims, st->n_ctx, n_splits);
+  if (ws_bytes < L.total) return set_error(BC_ERR_WORKSPACE, "bc_decode_layer: workspace %zu < %zu", ws_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return set_error(BC_ERR_INVALID, "bc_decode_layer: ws not 256-byte aligned");
+  LayerChain ch{false, nullptr, nullptr, 0, nullptr};
+  return layer_body(*dims, ly, st, bud, n_splits, hidden, ws, L, static_cast<hipStream_t>(stream), ch);
+}
+
+extern "C" size_t bc_step_workspace_bytes(const bc_model_dims* dims, int max_ctx, int max_splits) {
+  if (check_dims(dims) != BC_OK || max_ctx < 1 || max_splits < 1 || dims->vocab <= 0) return 0;
+  return step_layout(*dims, max_ctx, max_splits).total;
+}
+
+extern "C" int bc_decode_step(const bc_model_dims* dims, const bc_layer* layers, int n_layers, const uint16_t* g_final,
+                              const uint16_t* w_head, const bc_step* st, uint16_t* hidden, float* logits,
+                              int32_t* token, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != BC_OK) return rc;
+  if (!layers || n_layers < 1 || !g_final || !w_head || !st || !hidden || !logits || !token || !ws)
+    return set_error(BC_ERR_INVALID, "bc_decode_step: NULL argument or no layers");
+  if (dims->vocab <= 0 || dims->vocab % 8 != 0) return set_error(BC_ERR_UNSUPPORTED, "bc_decode_step: vocab %% 8 != 0");
+  if ((rc = check_step(st)) != BC_OK) return rc;
+  for (int i = 0; i < n_layers; ++i)
+    if ((rc = check_layer(&layers[i], st)) != BC_OK) return rc;
+  bc_kv_budget_info bud;
+  if ((rc = bc_kv_budget(st->n_ctx, &st->kv, &bud)) != BC_OK) return rc;
+  const bc_model_dims& m = *dims;
+  const int n_splits = step_splits(m, st, bud);
+  const StepLayout S = step_layout(m, st->n_ctx, n_splits);
+  if (ws_bytes < S.total) return set_error(BC_ERR_WORKSPACE, "bc_decode_step: workspace %zu < %zu", ws_bytes, S.total);
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return set_error(BC_ERR_INVALID, "bc_decode_step: ws not 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool sparse = st->r_p < 1.0;
+  const int k_d = bc_channel_keep(st->r_p, m.d);
+  bc_step one = *st;
+  one.taps = nullptr;
+  for (int i = 0; i < n_layers; ++i) {
+    const bool last = i + 1 == n_layers;
+    LayerChain ch;
+    ch.x1_ready = i > 0;
+    ch.next_gain = last ? g_final : layers[i + 1].g_attn;
+    ch.next_x = last ? at<uint16_t>(ws, S.xh) : at<uint16_t>(ws, S.layer.x1);
+    ch.next_sel_k = (!last && sparse) ? k_d : 0;
+    ch.next_idx = at<int32_t>(ws, S.layer.idx_qkv);
+    if ((rc = layer_body(m, &layers[i], &one, bud, n_splits, hidden, ws, S.layer, s, ch)) != BC_OK) return rc;
+  }
+  GemvParams p{};
+  p.wt = w_head; p.tiled = 1; p.d_in = m.d; p.d_out = m.vocab; p.x = at<uint16_t>(ws, S.xh); p.idx = nullptr;
+  p.k = m.d; p.rows_per_split = m.d; p.n_splits = 1; p.n_tiles = ceil_div(m.vocab, kGemvTile);
+  p.yf = logits; p.tile_max = at<float>(ws, S.tile_max); p.tile_arg = at<int32_t>(ws, S.tile_arg);
+  if ((rc = launch_gemv_main(MAIN_F32_ARGMAX, p, s)) != BC_OK) return rc;
+  return launch_argmax_finish(p.tile_max, p.tile_arg, p.n_tiles, token, s);
 }
 
 // ------------------------------------------------------------------ LM head

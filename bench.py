@@ -125,7 +125,7 @@ class Model:
         self.h = torch.empty_like(self.h0)
         self.logits = torch.empty(D["vocab"], dtype=torch.float32, device="cuda")
         self.token = torch.empty(1, dtype=torch.int32, device="cuda")
-        self.ws = torch.empty(bc.bc_layer_workspace_bytes(self.md, max_ctx, 1024) // 4 + 64, dtype=torch.int32,
+        self.ws = torch.empty(bc.bc_step_workspace_bytes(self.md, max_ctx, 1024) // 4 + 64, dtype=torch.int32,
                               device="cuda")
         self.ws_head = torch.empty(bc.bc_lm_head_workspace_bytes(self.md) // 4 + 64, dtype=torch.int32,
                                    device="cuda")
@@ -133,6 +133,7 @@ class Model:
         bc.bc_workspace_init(self.ws_head)
         self.c_layers = [bc.make_layer(l["w_qkv"], l["w_o"], l["w_gu"], l["w_down"], self.g_attn, self.g_mlp,
                                        l["k"], l["v"], l["summ"]) for l in self.layers]
+        self.layer_array = bc.make_layer_array(self.c_layers)
         torch.cuda.synchronize()
         log(f"[bench] model ready in {time.time() - t0:.1f}s; "
             f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
@@ -149,9 +150,8 @@ class Model:
         pol, _, S = self.plan(n, r_p, r_kv)
         st = bc.make_step(n, r_p, pol, S)
         self.h.copy_(self.h0)
-        for cl in self.c_layers:
-            bc.bc_decode_layer(self.md, cl, st, self.h, self.ws)
-        bc.bc_lm_head(self.md, self.h, self.g_final, self.w_head, self.logits, self.token, 1e-5, self.ws_head)
+        bc.bc_decode_step(self.md, self.layer_array, self.g_final, self.w_head, st, self.h, self.logits, self.token,
+                          self.ws)
 
     def graph(self, n, r_p, r_kv):
         self.step(n, r_p, r_kv)          # eager once: validates arguments outside capture
@@ -238,6 +238,30 @@ def time_attention_sparse(model, n, r_kv, reps=3, S=None):
     return us, attn_bytes(t_sel, S, True), S
 
 
+def time_select(n, k, reps=50):
+    """bc_select_channels on an activation-distributed input, replayed in a
+    HIP graph (so host launch cost is not timed)."""
+    from activation_kv_cache_amd import binding as bc
+    from activation_kv_cache_amd import inputs as gen
+    x = torch.from_numpy(gen.activation_bf16(3, f"selbench{n}", n).view(np.int16)).cuda()
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    bc.bc_select_channels(x, k, idx)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            bc.bc_select_channels(x, k, idx)
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    g.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / reps
+
+
 def kernel_table(model, contexts, split_sweep=None):
     """Per-kernel achieved bandwidth of the hot kernels (one launch per layer,
     rotating over the 32 layers' buffers)."""
@@ -259,6 +283,10 @@ def kernel_table(model, contexts, split_sweep=None):
             us, b, S = time_attention_sparse(model, n, r_kv)
             rows.append({"kernel": f"attn_partial r_kv={r_kv}", "context": n, "us": round(us, 2), "bytes": b,
                          "gbs": round(b / us / 1e3, 1), "splits": S})
+    for n, k in ((4096, 2048), (4096, 2867), (14336, 7168), (14336, 10035)):
+        us = time_select(n, k)
+        rows.append({"kernel": f"select n={n} k={k}", "us": round(us, 2), "bytes": 2 * n + 4 * k,
+                     "gbs": round((2 * n + 4 * k) / us / 1e3, 1)})
     for which in ("w_qkv", "w_o", "w_gu", "w_down"):
         for r_p in (1.0, 0.7, 0.5):
             us, b, k = time_gemv_kernel(model, which, r_p)

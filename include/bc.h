@@ -230,6 +230,23 @@ size_t bc_layer_workspace_bytes(const bc_model_dims* dims, int max_ctx, int max_
 int bc_decode_layer(const bc_model_dims* dims, const bc_layer* layer, const bc_step* step,
                     uint16_t* hidden, void* ws, size_t ws_bytes, void* stream);
 
+/* a8. One whole decode step (README "Timing and quality on a GPU": a step
+ * is every layer with all seven projections and the cache read, then the
+ * LM head, whose weights are in the step's bytes -- README "Quick start",
+ * the 1.60x bound).  For each of layers[0..n_layers) the work of
+ * bc_decode_layer (same kernels, same results); the last layer's output
+ * goes through RMSNorm(h) * g_final and the dense LM head into logits fp32
+ * [vocab], and token[0] = argmax (lowest index on ties).  Across layer
+ * boundaries the next layer's RMSNorm and channel top-k are produced by the
+ * previous layer's last kernel, so a step launches one kernel fewer per
+ * layer than n_layers separate bc_decode_layer calls.  step->taps is
+ * ignored.  w_head: W_head^T packed by bc_pack_weight_tiles (d_in d, d_out
+ * vocab).  ws from bc_step_workspace_bytes. */
+size_t bc_step_workspace_bytes(const bc_model_dims* dims, int max_ctx, int max_splits);
+int bc_decode_step(const bc_model_dims* dims, const bc_layer* layers, int n_layers, const uint16_t* g_final,
+                   const uint16_t* w_head, const bc_step* step, uint16_t* hidden, float* logits, int32_t* token,
+                   void* ws, size_t ws_bytes, void* stream);
+
 /* Tile-major re-layout of a W^T matrix for bc_decode_layer and bc_lm_head
  * (setup, not timed): the columns are cut into tiles of 128 (the last one
  * narrower, w_t columns); tile t stores its d_in rows contiguously, row i at

@@ -198,3 +198,60 @@ def test_tiled_gemv_equals_plain():
         bc.bc_sparse_gemv_tiled(bc.packed_tiles(dev(wt)), d_in, d_out, dev(x), idx, k, y2, ws)
         torch.cuda.synchronize()
         assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("r_p,r_kv", [(1.0, 1.0), (0.5, 0.3), (0.7, 1.0)])
+def test_decode_step_equals_layer_chain(r_p, r_kv):
+    """bc_decode_step (fused across layers) gives the same bits as
+    bc_decode_layer per layer followed by bc_lm_head."""
+    bc = _bc()
+    dims = dict(gen.TINY, vocab=1000, n_layers=3)
+    d, dff, Hkv, D = dims["d"], dims["d_ff"], dims["n_kv_heads"], dims["head_dim"]
+    n_cap, n, S = 1024, 1000, 4
+    md = bc.dims(dims)
+    pol = bc.policy(r_kv, 4, 64)
+    layers, caches = [], []
+    for li in range(3):
+        W = gen.layer_weights(20, dims, layer=li)
+        w = {k: dev(v) for k, v in W.items()}
+        w_gu = torch.empty(2 * d * dff, dtype=torch.int16, device="cuda")
+        bc.bc_pack_gate_up(w["gate"], w["up"], w_gu)
+        K, V = gen.kv_cache(20, dims, n_cap, 0.5, layer=li)
+        summ = np.zeros((Hkv, n_cap // 16, D, 2), np.uint16)
+        for g in range(Hkv):
+            t = oracle.kv_summary(K[g], n - 1)
+            summ[g, :t.shape[0]] = t
+        layers.append(dict(qkv=bc.packed_tiles(w["qkv"]), o=bc.packed_tiles(w["o"]), gu=w_gu,
+                           down=bc.packed_tiles(w["down"]), g1=w["g1"], g2=w["g2"]))
+        caches.append((K, V, summ))
+    g_final = dev(gen.to_bf16_bits(np.ones(d, np.float32)))
+    w_head = bc.packed_tiles(dev(gen.normal_bf16(20, "head", (d, dims["vocab"]), 0.02)))
+    h0 = gen.activation_bf16(20, "h0", d)
+
+    def fresh():
+        kv = [(dev(K), dev(V), dev(sm)) for K, V, sm in caches]
+        cl = [bc.make_layer(l["qkv"], l["o"], l["gu"], l["down"], l["g1"], l["g2"], *kv[i])
+              for i, l in enumerate(layers)]
+        return kv, cl
+
+    st = bc.make_step(n, r_p, pol, S)
+    kv1, cl1 = fresh()
+    h1 = dev(h0)
+    ws1 = workspace(bc.bc_layer_workspace_bytes(md, n_cap, S))
+    for c in cl1:
+        bc.bc_decode_layer(md, c, st, h1, ws1)
+    lg1 = torch.empty(dims["vocab"], dtype=torch.float32, device="cuda")
+    tk1 = torch.empty(1, dtype=torch.int32, device="cuda")
+    bc.bc_lm_head(md, h1, g_final, w_head, lg1, tk1, 1e-5, workspace(bc.bc_lm_head_workspace_bytes(md)))
+    kv2, cl2 = fresh()
+    h2 = dev(h0)
+    arr = bc.make_layer_array(cl2)
+    lg2 = torch.empty_like(lg1)
+    tk2 = torch.empty_like(tk1)
+    bc.bc_decode_step(md, arr, g_final, w_head, st, h2, lg2, tk2, workspace(bc.bc_step_workspace_bytes(md, n_cap, S)))
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2)
+    assert torch.equal(lg1, lg2) and torch.equal(tk1, tk2)
+    for a, b in zip(kv1, kv2):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
