@@ -405,6 +405,8 @@ def main():
     ap.add_argument("--cells", default="default", help="default | dense | none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true", help="only the per-kernel bandwidth table")
+    ap.add_argument("--calib-copy", type=int, default=0,
+                    help="only copy this many bytes 5 times (calibration of the HBM byte counters)")
     ap.add_argument("--split-sweep", default="", help="attention split counts to sweep in --kernels")
     ap.add_argument("--attn-only", type=int, default=0,
                     help="only launch the dense attention kernel this many times per layer (for counters)")
@@ -417,6 +419,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.calib_copy:
+        src = torch.ones(args.calib_copy // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": src.numel() * 4}))
+        return
 
     contexts = [int(c) for c in args.contexts.split(",")]
     head_n = max(contexts)
