@@ -361,71 +361,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_reduce(const ReduceParams
   }
 }
 
-// One work-group for all heads: the merge of every split into out, then the
-// top-k of out (the channels of the next GEMV input) from keys staged in LDS.
-constexpr int kRsThreads = 1024;
-constexpr int kRsMaxWeights = 8192;   // n_heads * n_splits
-
-struct ReduceSelectSmem {
-  union {
-    float wts[kRsMaxWeights];
-    Topk15Smem topk15;
-  };
-  float den[256];
-};
-
-__global__ __launch_bounds__(kRsThreads) void k_attn_reduce_select(const ReduceParams p, int k, int32_t* idx_out) {
-  __shared__ ReduceSelectSmem sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int H = p.n_heads, S = p.n_splits, D = p.head_dim;
-  for (int j = w; j < H; j += kRsThreads / kWave) {
-    const float* mj = p.m + size_t(j) * S;
-    const float* lj = p.l + size_t(j) * S;
-    float mx = -INFINITY;
-    for (int s = lane; s < S; s += kWave) mx = fmaxf(mx, mj[s]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
-    float den = 0.f;
-    for (int s = lane; s < S; s += kWave) {
-      const float ms = mj[s];
-      const float wt = (ms == -INFINITY || mx == -INFINITY) ? 0.f : expf(ms - mx);
-      sm.wts[j * S + s] = wt;
-      den += wt * lj[s];
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, kWave);
-    if (lane == 0) sm.den[j] = den;
-  }
-  __syncthreads();
-  const int n = H * D;
-  for (int e = tid * 4; e < n; e += kRsThreads * 4) {
-    const int j = e / D, d = e % D;
-    const float* oj = p.o + size_t(j) * S * D + d;
-    const float* wj = sm.wts + j * S;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < S; ++s) {
-      const float4 v = *reinterpret_cast<const float4*>(oj + size_t(s) * D);
-      const float wt = wj[s];
-      acc.x += v.x * wt; acc.y += v.y * wt; acc.z += v.z * wt; acc.w += v.w * wt;
-    }
-    const float den = sm.den[j];
-    const float r[4] = {acc.x, acc.y, acc.z, acc.w};
-    uint16_t b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = f32_to_bf16(den > 0.f ? r[i] / den : 0.f);
-    uint2 ov;
-    ov.x = uint32_t(b[0]) | (uint32_t(b[1]) << 16);
-    ov.y = uint32_t(b[2]) | (uint32_t(b[3]) << 16);
-    *reinterpret_cast<uint2*>(p.out + e) = ov;
-  }
-  __syncthreads();
-  if (k <= 0 || k >= n) return;
-  const uint16_t* x = p.out;
-  auto key = [x](int i) -> uint32_t { return uint32_t(x[i]) & 0x7FFFu; };
-  auto emit = [idx_out](int rk, int i) { idx_out[rk] = i; };
-  block_topk15(n, k, key, emit, sm.topk15);
-}
-
 template <int D>
 int launch_partial_d(const AttnParams& p, hipStream_t s) {
   dim3 grid(p.n_splits, p.n_kv_heads), block(kAttnThreads);
@@ -445,17 +380,6 @@ int launch_attn_partial(const AttnParams& p, hipStream_t s) {
   if (p.head_dim == 128) return launch_partial_d<128>(p, s);
   if (p.head_dim == 64) return launch_partial_d<64>(p, s);
   return set_error(BC_ERR_UNSUPPORTED, "attention: head_dim %d", p.head_dim);
-}
-
-int launch_attn_reduce_select(const ReduceParams& p, int k, int32_t* idx_out, hipStream_t s) {
-  const int n = p.n_heads * p.head_dim;
-  if (p.n_heads * p.n_splits > kRsMaxWeights || p.n_heads > 256 || n > kTopk15MaxN || n % 4 != 0) {
-    int rc = launch_attn_reduce(p, s);
-    if (rc != BC_OK || k <= 0 || k >= n) return rc;
-    return launch_select(p.out, n, k, idx_out, s);
-  }
-  k_attn_reduce_select<<<1, kRsThreads, 0, s>>>(p, k, idx_out);
-  return check_launch("k_attn_reduce_select");
 }
 
 int launch_attn_reduce(const ReduceParams& p, hipStream_t s) {

@@ -473,4 +473,113 @@ __device__ void block_topk(int n, int k, KeyFn key_fn, EmitFn emit, TopkSmem<NT,
   __syncthreads();
 }
 
+// ------------------------------------- 15-bit keys in registers, two passes
+// Exact top-k of n keys below 2^15 held in registers by NT threads: thread t
+// owns positions [t*P, t*P + P) (positions >= n are ignored), so a thread's
+// keys are in position order.  Pass 1 histograms the top 11 key bits (2048
+// bins, LDS atomics; bf16 magnitudes spread over many bins, so the atomics
+// rarely collide) and a block scan taken from the largest bin down finds the
+// bin holding the k-th largest key; pass 2 histograms the low 4 bits of the
+// keys in that bin.  That fixes the threshold key thr and the number `need`
+// of keys equal to thr that are kept (the lowest positions).  One block scan
+// of (ties, greater) counts per thread then gives every kept position its
+// rank: emit(rank, e) for the thread's e-th key, ranks ascending with
+// position.  Requires 1 <= k <= n <= NT * PMAX and n < 65536 (the scan
+// packs two 16-bit counts).  Contains __syncthreads(); the caller
+// synchronises before reading what emit wrote.
+template <int NT>
+struct Topk2Smem {
+  uint32_t hist[2048];
+  uint32_t hist2[16];
+  uint32_t wtot[NT / kWave];
+  uint32_t b1, above1;
+};
+
+template <int NT, int PMAX, typename EmitFn>
+__device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int k, EmitFn emit, Topk2Smem<NT>& sm) {
+  static_assert(2048 % NT == 0 || NT % 2048 == 0, "bins per thread");
+  constexpr int NW = NT / kWave;
+  constexpr int BPT = 2048 / NT;  // bins per thread
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nv = max(0, min(P, n - tid * P));
+  for (int i = tid; i < 2048; i += NT) sm.hist[i] = 0;
+  if (tid < 16) sm.hist2[tid] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < PMAX; ++e)
+    if (e < nv) atomicAdd(&sm.hist[key[e] >> 4], 1u);
+  __syncthreads();
+  // thread t owns bins [b0, b0 + BPT), b0 = 2048 - BPT (t + 1): the largest
+  // bins go to thread 0, so the prefix over threads counts larger keys
+  const int b0 = 2048 - BPT * (tid + 1);
+  uint32_t bins[BPT];
+  uint32_t local = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    bins[j] = sm.hist[b0 + j];
+    local += bins[j];
+  }
+  const uint32_t winc = wave_scan_dpp(local);
+  if (lane == kWave - 1) sm.wtot[w] = winc;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) before += ww < w ? sm.wtot[ww] : 0u;
+  const uint32_t ku = uint32_t(k);
+  {
+    const uint32_t inc = before + winc, ex = inc - local;
+    if (ex < ku && ku <= inc) {
+      uint32_t run = ex;
+#pragma unroll
+      for (int j = BPT - 1; j >= 0; --j) {
+        if (run < ku && ku <= run + bins[j]) { sm.b1 = uint32_t(b0 + j); sm.above1 = run; }
+        run += bins[j];
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t b1 = sm.b1, k2 = ku - sm.above1;
+#pragma unroll
+  for (int e = 0; e < PMAX; ++e)
+    if (e < nv && (key[e] >> 4) == b1) atomicAdd(&sm.hist2[key[e] & 15u], 1u);
+  __syncthreads();
+  uint32_t run = 0, b2 = 0, above2 = 0;
+  bool found = false;
+#pragma unroll
+  for (int j = 15; j >= 0; --j) {
+    const uint32_t c = sm.hist2[j];
+    if (!found && run + c >= k2) { b2 = uint32_t(j); above2 = run; found = true; }
+    run += c;
+  }
+  const uint32_t thr = (b1 << 4) | b2, need = k2 - above2;
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int e = 0; e < PMAX; ++e) {
+    gt += (e < nv && key[e] > thr) ? 1u : 0u;
+    eq += (e < nv && key[e] == thr) ? 1u : 0u;
+  }
+  // exclusive block scan of (eq << 16 | gt); wtot is free again (its last
+  // readers passed two barriers ago)
+  const uint32_t v = (eq << 16) | gt;
+  const uint32_t inc = wave_scan_dpp(v);
+  if (lane == kWave - 1) sm.wtot[w] = inc;
+  __syncthreads();
+  uint32_t bf = inc - v;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) bf += ww < w ? sm.wtot[ww] : 0u;
+  const uint32_t gt_before = bf & 0xFFFFu, eq_before = bf >> 16;
+  uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
+  uint32_t tie = eq_before;
+#pragma unroll
+  for (int e = 0; e < PMAX; ++e) {
+    if (e >= nv) continue;
+    if (key[e] > thr) {
+      emit(int(pos++), e);
+    } else if (key[e] == thr) {
+      if (tie < need) emit(int(pos++), e);
+      ++tie;
+    }
+  }
+}
+
 }  // namespace bc

@@ -3,20 +3,26 @@
 // y[o] = sum_{j<k} W^T[idx_j][o] * x[idx_j]  (README "What it does in one
 // picture": each token's activations select the weight columns read).
 //
-// W^T is [d_in][d_out] bf16: the weights of one input channel are one
-// contiguous row.  The main kernel gives a work-group a 128-column tile of y
-// (256 B of every row) and a fixed chunk of the selected channel list.  Its
-// 256 lanes form 16 row slots of 16 lanes; a slot reads one row's 256 B per
-// load (16 B per lane), 8 rows in flight per slot, so a work-group keeps
-// 128 rows (32 KB) in flight.  The chunk's channel ids and their x values are
-// staged in LDS first.  Each work-group writes its fp32 partial sums for its
-// chunk; no work-group waits for another (cross-XCD fences on this chip cost
-// far more than a kernel boundary).  A finish kernel then adds the chunks in
-// chunk order -- deterministic -- and applies the epilogue: bf16 store,
-// residual add + RMSNorm + top-k of the next input (one work-group), rotary +
-// KV append + block summary, or SwiGLU (+ top-k).  With a single chunk the
-// main kernel stores bf16 or fp32 (+ per-tile argmax) directly.
-// Dense mode is the same kernel with idx == NULL.
+// W^T is [d_in][d_out] bf16: the weights of one input channel are one row,
+// stored tile-major (128-column tiles, each tile's rows contiguous).  A
+// work-group owns one 128-column tile of y and one chunk of list positions.
+// Its 512 lanes form 32 row slots of 16 lanes; a slot reads a row's 256 B
+// with one 16-byte load per lane.  Each slot keeps a ring of 8 rows in flight
+// (64 KB per work-group), issued as non-temporal loads: the weights are read
+// once per step and should not evict the small vectors the kernels share.
+//
+// The prologue forms the input.  IN_NORM computes x = RMSNorm(h) * gain and
+// IN_SEL takes x as given; with k < d_in both then select the exact top-k of
+// |x| (block_topk_2pass) in every work-group, so no separate selection
+// kernel or single-work-group stage sits between two GEMVs.  In dense mode
+// the first ring of weight loads is issued before the prologue.
+//
+// Several chunks write fp32 partials ([chunk][d_out]); a finish kernel adds
+// them in chunk order (deterministic) and applies the epilogue: bf16 store,
+// residual add, rotary + KV append + block summary, SwiGLU, or logits +
+// argmax.  With one chunk the main kernel applies the bf16, SwiGLU or argmax
+// epilogue itself.  No work-group waits for another: cross-XCD fences cost
+// far more on this chip than a kernel boundary.
 #include <math.h>
 #include <stdlib.h>
 
@@ -27,119 +33,229 @@ namespace bc {
 
 namespace {
 
-constexpr int kSlots = kGemvThreads / 16;   // 16 row slots of 16 lanes
-constexpr int kRowsInFlight = 8;            // per slot
-constexpr int kStageRows = 1024;            // channel ids / x values staged per pass
+constexpr int kSlots = kGemvThreads / 16;   // 32 row slots of 16 lanes
+constexpr int kRing = 8;                    // rows in flight per slot
+constexpr int kNW = kGemvThreads / kWave;   // 8 waves
 
-struct MainSmem {
-  int32_t ch[kStageRows];
-  float xv[kStageRows];
-  float red[kSlots][kGemvTile];
-  float amax_v[kGemvThreads / kWave];
-  int32_t amax_i[kGemvThreads / kWave];
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct GemvSmem {
+  union {
+    struct {
+      int32_t ch[kGemvMaxRows];   // channel of each list position of the chunk
+      float xv[kGemvMaxRows];     // its input value
+    } list;
+    float red[kSlots][kGemvTile];  // per-slot sums (after the row loop)
+  };
+  float red2[4][kGemvTile];
+  Topk2Smem<kGemvThreads> tk;
+  float part[kNW];
+  float amax_v[kNW];
+  int32_t amax_i[kNW];
 };
 
-template <int MODE>
-__global__ __launch_bounds__(kGemvThreads) void k_gemv_main(const GemvParams p) {
-  __shared__ MainSmem sm;
+// Input values per thread in the fused prologue: a multiple of 4 (8-byte
+// loads), thread t owning channels [t*P, t*P + P).
+__host__ __device__ inline int fused_per_thread(int d_in) {
+  return ((d_in + kGemvThreads - 1) / kGemvThreads + 3) & ~3;
+}
+
+__device__ __forceinline__ u32x4 load_row_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ float bf16_elt(const uint32_t* packed, int e) {
+  return (e & 1) ? bf16_hi(packed[e >> 1]) : bf16_lo(packed[e >> 1]);
+}
+
+template <int PMAX>
+__device__ __forceinline__ void load_vec(const uint16_t* src, int c0, int P, int d_in, uint32_t (&dst)[PMAX / 2]) {
+#pragma unroll
+  for (int q = 0; q < PMAX / 4; ++q) {
+    uint2 v = make_uint2(0u, 0u);
+    if (4 * q < P && c0 + 4 * q < d_in) v = *reinterpret_cast<const uint2*>(src + c0 + 4 * q);
+    dst[2 * q] = v.x;
+    dst[2 * q + 1] = v.y;
+  }
+}
+
+template <int IN, int OUT, int PMAX>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
+  __shared__ GemvSmem sm;
   const int tile = blockIdx.x, split = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = tid & 15, slot = tid >> 4;
-  const int col = tile * kGemvTile + l16 * 8;
-  const bool col_ok = col < p.d_out;
   const int r0 = split * p.rows_per_split;
   const int r1 = min(p.k, r0 + p.rows_per_split);
+  const int n = r1 - r0;   // >= 1 (plan_gemv)
+  const bool dense = (IN == IN_LIST) ? p.idx == nullptr : p.k == p.d_in;
+  const bool lead = blockIdx.x == 0 && blockIdx.y == 0;
+  const int tile_w = min(kGemvTile, p.d_out - tile * kGemvTile);
+  const bool col_ok = l16 * 8 < tile_w;
+  // lanes past a narrow last tile read the tile's first columns (discarded)
+  const uint16_t* base;
+  size_t stride;
+  if (p.tiled) {
+    base = p.wt + size_t(tile) * kGemvTile * p.d_in + (col_ok ? l16 * 8 : 0);
+    stride = size_t(tile_w);
+  } else {
+    base = p.wt + size_t(tile) * kGemvTile + (col_ok ? l16 * 8 : 0);
+    stride = size_t(p.d_out);
+  }
+  // list position j -> its row; positions past the chunk re-read its last
+  // row (an L2 hit), so every slot issues the same sequence of loads.  Row
+  // ids are clamped to the matrix, so a bad id cannot read outside it.
+  const unsigned last_row = unsigned(p.d_in - 1);
+  auto row_ptr = [&](int j) -> const uint16_t* {
+    const int jj = min(j, n - 1);
+    const unsigned ch = dense ? unsigned(r0 + jj) : min(unsigned(sm.list.ch[jj]), last_row);
+    return base + size_t(ch) * stride;
+  };
+  u32x4 ring[kRing];
+  if (dense) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) ring[u] = load_row_nt(row_ptr(slot + kSlots * u));
+  }
 
+  // ------------------------------------------------------------ prologue
+  if constexpr (IN == IN_LIST) {
+    for (int j = tid; j < n; j += kGemvThreads) {
+      const int ch = dense ? r0 + j : p.idx[r0 + j];
+      if (!dense) sm.list.ch[j] = ch;
+      sm.list.xv[j] = bf16_to_f32(p.x[ch]);
+    }
+  } else {
+    const int P = fused_per_thread(p.d_in);
+    const int c0 = tid * P;
+    uint32_t xb[PMAX / 2];
+    if constexpr (IN == IN_NORM) {
+      uint32_t gb[PMAX / 2];
+      load_vec<PMAX>(p.h, c0, P, p.d_in, xb);
+      load_vec<PMAX>(p.gain, c0, P, p.d_in, gb);
+      // sum of squares in a fixed order: the thread's channels in order, the
+      // wave's fixed tree, then the waves in order (all work-groups agree)
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < PMAX; ++e) {
+        const float v = bf16_elt(xb, e);
+        ss += v * v;   // channels past d_in were loaded as 0
+      }
+      ss = wave_sum_f32(ss);
+      if (lane == 0) sm.part[w] = ss;
+      __syncthreads();
+      float tot = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kNW; ++ww) tot += sm.part[ww];
+      const float inv = 1.0f / sqrtf(tot / float(p.d_in) + p.eps);
+#pragma unroll
+      for (int q = 0; q < PMAX / 2; ++q) {
+        const uint32_t a = f32_to_bf16(bf16_lo(xb[q]) * inv * bf16_lo(gb[q]));
+        const uint32_t b = f32_to_bf16(bf16_hi(xb[q]) * inv * bf16_hi(gb[q]));
+        xb[q] = a | (b << 16);
+      }
+    } else {
+      load_vec<PMAX>(p.x, c0, P, p.d_in, xb);
+    }
+    if (lead && p.x_out) {
+#pragma unroll
+      for (int q = 0; q < PMAX / 4; ++q)
+        if (4 * q < P && c0 + 4 * q < p.d_in)
+          *reinterpret_cast<uint2*>(p.x_out + c0 + 4 * q) = make_uint2(xb[2 * q], xb[2 * q + 1]);
+    }
+    if (dense) {
+#pragma unroll
+      for (int e = 0; e < PMAX; ++e) {
+        const int c = c0 + e;
+        if (e < P && c >= r0 && c < r1) sm.list.xv[c - r0] = bf16_elt(xb, e);
+      }
+    } else {
+      uint32_t key[PMAX];
+#pragma unroll
+      for (int e = 0; e < PMAX; ++e) key[e] = ((xb[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) & 0x7FFFu;
+      int32_t* idx_out = lead ? p.idx_out : nullptr;
+      auto emit = [&](int pos, int e) {
+        const int c = c0 + e;
+        if (pos >= r0 && pos < r1) {
+          sm.list.ch[pos - r0] = c;
+          sm.list.xv[pos - r0] = bf16_elt(xb, e);
+        }
+        if (idx_out && pos < p.k) idx_out[pos] = c;
+      };
+      block_topk_2pass<kGemvThreads, PMAX>(key, P, p.d_in, p.k, emit, sm.tk);
+    }
+  }
+  __syncthreads();
+  if (!dense) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) ring[u] = load_row_nt(row_ptr(slot + kSlots * u));
+  }
+
+  // ------------------------------------------------------------- row loop
   float acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.f;
-  // plain: row ch of W^T at wt + ch * d_out; tile-major: the tile's rows are
-  // contiguous, each as wide as the tile
-  const int tile_w = min(kGemvTile, p.d_out - tile * kGemvTile);
-  const uint16_t* wcol;
-  size_t row_stride;
-  if (p.tiled) {
-    wcol = p.wt + size_t(tile) * kGemvTile * p.d_in + (col_ok ? l16 * 8 : 0);
-    row_stride = size_t(tile_w);
-  } else {
-    wcol = p.wt + (col_ok ? col : 0);
-    row_stride = size_t(p.d_out);
+  const int nsteps = (n + kSlots - 1) / kSlots;
+  for (int st = 0; st < nsteps; st += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int j = slot + kSlots * (st + u);
+      const float x = j < n ? sm.list.xv[j] : 0.f;
+      const u32x4 wv = ring[u];
+      acc[0] += bf16_lo(wv.x) * x;
+      acc[1] += bf16_hi(wv.x) * x;
+      acc[2] += bf16_lo(wv.y) * x;
+      acc[3] += bf16_hi(wv.y) * x;
+      acc[4] += bf16_lo(wv.z) * x;
+      acc[5] += bf16_hi(wv.z) * x;
+      acc[6] += bf16_lo(wv.w) * x;
+      acc[7] += bf16_hi(wv.w) * x;
+      ring[u] = load_row_nt(row_ptr(j + kSlots * kRing));
+    }
   }
-  const bool dense = p.idx == nullptr;
+  // the ring's last loads (past the chunk) are consumed here so that none
+  // is still in flight when the registers are reused
+  uint32_t sink = 0;
+#pragma unroll
+  for (int u = 0; u < kRing; ++u) sink |= ring[u].x & 0u;
+  acc[0] += __uint_as_float(sink);
 
-  for (int s0 = r0; s0 < r1; s0 += kStageRows) {
-    const int s1 = min(r1, s0 + kStageRows);
-    const int n = s1 - s0;
-    // dense rows are known before staging: put the first batch in flight now
-    uint4 wv[kRowsInFlight];
-    if (dense) {
-#pragma unroll
-      for (int u = 0; u < kRowsInFlight; ++u) {
-        const int rr = slot + kSlots * u;
-        wv[u] = (col_ok && rr < n) ? *reinterpret_cast<const uint4*>(wcol + size_t(s0 + rr) * row_stride)
-                                   : make_uint4(0, 0, 0, 0);
-      }
-    }
-    for (int r = s0 + tid; r < s1; r += kGemvThreads) {
-      const int ch = dense ? r : p.idx[r];
-      sm.ch[r - s0] = ch;
-      sm.xv[r - s0] = bf16_to_f32(p.x[ch]);
-    }
-    __syncthreads();
-    for (int r = slot; r < n; r += kSlots * kRowsInFlight) {
-      float xv[kRowsInFlight];
-      if (!dense || r != slot) {
-#pragma unroll
-        for (int u = 0; u < kRowsInFlight; ++u) {
-          const int rr = r + kSlots * u;
-          wv[u] = (col_ok && rr < n) ? *reinterpret_cast<const uint4*>(wcol + size_t(sm.ch[rr]) * row_stride)
-                                     : make_uint4(0, 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kRowsInFlight; ++u) {
-        const int rr = r + kSlots * u;
-        xv[u] = rr < n ? sm.xv[rr] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < kRowsInFlight; ++u) {
-        acc[0] += bf16_lo(wv[u].x) * xv[u];
-        acc[1] += bf16_hi(wv[u].x) * xv[u];
-        acc[2] += bf16_lo(wv[u].y) * xv[u];
-        acc[3] += bf16_hi(wv[u].y) * xv[u];
-        acc[4] += bf16_lo(wv[u].z) * xv[u];
-        acc[5] += bf16_hi(wv[u].z) * xv[u];
-        acc[6] += bf16_lo(wv[u].w) * xv[u];
-        acc[7] += bf16_hi(wv[u].w) * xv[u];
-      }
-    }
-    __syncthreads();
+  // ------------------------------------------------------------- epilogue
+  __syncthreads();   // red aliases the list
+  {
+    float4* rw = reinterpret_cast<float4*>(&sm.red[slot][l16 * 8]);
+    rw[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    rw[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
-
-  // slots 0..15 in order
-  float4* rw = reinterpret_cast<float4*>(&sm.red[slot][l16 * 8]);
-  rw[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  rw[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   __syncthreads();
-  float v = 0.f;
-  int c = -1;
-  if (tid < kGemvTile) {
+  {
+    const int c = tid & (kGemvTile - 1), q = tid >> 7;
+    float s = 0.f;
 #pragma unroll
-    for (int s = 0; s < kSlots; ++s) v += sm.red[s][tid];
-    c = tile * kGemvTile + tid;
-    if (c >= p.d_out) c = -1;
+    for (int i = 0; i < kSlots / 4; ++i) s += sm.red[(kSlots / 4) * q + i][c];
+    sm.red2[q][c] = s;
   }
-  if constexpr (MODE == MAIN_PARTIAL) {
-    if (c >= 0) p.partial[size_t(split) * p.d_out + c] = v;
-  } else if constexpr (MODE == MAIN_BF16) {
-    if (c >= 0) p.y[c] = f32_to_bf16(v);
-  } else if constexpr (MODE == MAIN_F32_ARGMAX) {
+  __syncthreads();
+  auto col_sum = [&](int c) { return ((sm.red2[0][c] + sm.red2[1][c]) + sm.red2[2][c]) + sm.red2[3][c]; };
+  if constexpr (OUT == OUT_PARTIAL) {
+    if (tid < tile_w) p.partial[size_t(split) * p.d_out + tile * kGemvTile + tid] = col_sum(tid);
+  } else if constexpr (OUT == OUT_BF16) {
+    if (tid < tile_w) p.y[tile * kGemvTile + tid] = f32_to_bf16(col_sum(tid));
+  } else if constexpr (OUT == OUT_SWIGLU) {
+    // tile t: gate columns [0, wu) and up columns [wu, 2 wu) of hidden units
+    // [64t, 64t + wu)
+    const int wu = tile_w / 2;
+    if (tid < wu) {
+      const float g = col_sum(tid), u = col_sum(wu + tid);
+      p.y[tile * (kGemvTile / 2) + tid] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+    }
+  } else {
     float best = -INFINITY;
     int besti = 0x7FFFFFFF;
-    if (c >= 0) {
-      p.yf[c] = v;
-      best = v;
+    if (tid < tile_w) {
+      const int c = tile * kGemvTile + tid;
+      best = col_sum(tid);
       besti = c;
+      p.yf[c] = best;
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -147,12 +263,12 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_main(const GemvParams p) 
       const int oi = __shfl_xor(besti, off, kWave);
       if (ov > best || (ov == best && oi < besti)) { best = ov; besti = oi; }
     }
-    if ((tid & 63) == 0) { sm.amax_v[tid >> 6] = best; sm.amax_i[tid >> 6] = besti; }
+    if (lane == 0) { sm.amax_v[w] = best; sm.amax_i[w] = besti; }
     __syncthreads();
     if (tid == 0) {
-      for (int w = 1; w < kGemvThreads / kWave; ++w) {
-        const float ov = sm.amax_v[w];
-        const int oi = sm.amax_i[w];
+      for (int ww = 1; ww < kNW; ++ww) {
+        const float ov = sm.amax_v[ww];
+        const int oi = sm.amax_i[ww];
         if (ov > best || (ov == best && oi < besti)) { best = ov; besti = oi; }
       }
       p.tile_max[tile] = best;
@@ -177,31 +293,60 @@ __device__ __forceinline__ float chunk_sum(const float* partial, int n_splits, i
   return v;
 }
 
-// Same for 4 consecutive columns (c % 4 == 0, d_out % 8 == 0).
-__device__ __forceinline__ float4 chunk_sum4(const float* partial, int n_splits, int d_out, int c) {
-  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* pp = partial + c;
-  int s = 0;
-  for (; s + 4 <= n_splits; s += 4) {
-    const float4 a0 = *reinterpret_cast<const float4*>(pp + size_t(s) * d_out);
-    const float4 a1 = *reinterpret_cast<const float4*>(pp + size_t(s + 1) * d_out);
-    const float4 a2 = *reinterpret_cast<const float4*>(pp + size_t(s + 2) * d_out);
-    const float4 a3 = *reinterpret_cast<const float4*>(pp + size_t(s + 3) * d_out);
-    v.x += a0.x; v.y += a0.y; v.z += a0.z; v.w += a0.w;
-    v.x += a1.x; v.y += a1.y; v.z += a1.z; v.w += a1.w;
-    v.x += a2.x; v.y += a2.y; v.z += a2.z; v.w += a2.w;
-    v.x += a3.x; v.y += a3.y; v.z += a3.z; v.w += a3.w;
-  }
-  for (; s < n_splits; ++s) {
-    const float4 a0 = *reinterpret_cast<const float4*>(pp + size_t(s) * d_out);
-    v.x += a0.x; v.y += a0.y; v.z += a0.z; v.w += a0.w;
-  }
-  return v;
-}
-
 __global__ __launch_bounds__(256) void k_finish_bf16(const FinishParams p) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c < p.d_out) p.y[c] = f32_to_bf16(chunk_sum(p.partial, p.n_splits, p.d_out, c));
+}
+
+// y = bf16(sum of chunks + resid), one column per thread.
+__global__ __launch_bounds__(128) void k_finish_resid(const FinishParams p) {
+  const int c = blockIdx.x * 128 + threadIdx.x;
+  if (c >= p.d_out) return;
+  float v = chunk_sum(p.partial, p.n_splits, p.d_out, c);
+  if (p.resid) v += bf16_to_f32(p.resid[c]);
+  p.y[c] = f32_to_bf16(v);
+}
+
+// SwiGLU over the chunk sums of the packed gate | up tiles: tile t holds gate
+// columns [128t, 128t + w) and up columns [128t + w, 128t + 2w) of hidden
+// units [64t, 64t + w), w = min(64, d_ff - 64t).  One unit per thread.
+__global__ __launch_bounds__(256) void k_finish_swiglu(const FinishParams p) {
+  const int half = kGemvTile / 2;
+  const int u = blockIdx.x * 256 + threadIdx.x;
+  if (u >= p.d_ff) return;
+  const int t = u / half, off = u % half;
+  const int w = min(half, p.d_ff - t * half);
+  const float g = chunk_sum(p.partial, p.n_splits, p.d_out, t * kGemvTile + off);
+  const float v = chunk_sum(p.partial, p.n_splits, p.d_out, t * kGemvTile + w + off);
+  p.y[u] = f32_to_bf16(g / (1.0f + expf(-g)) * v);
+}
+
+// Logits from chunk sums, and the argmax of each block of 256 columns.
+__global__ __launch_bounds__(256) void k_finish_argmax(const FinishParams p) {
+  __shared__ float sv[4];
+  __shared__ int32_t si[4];
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  float best = -INFINITY;
+  int besti = 0x7FFFFFFF;
+  if (c < p.d_out) {
+    best = chunk_sum(p.partial, p.n_splits, p.d_out, c);
+    besti = c;
+    p.yf[c] = best;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(best, off, kWave);
+    const int oi = __shfl_xor(besti, off, kWave);
+    if (ov > best || (ov == best && oi < besti)) { best = ov; besti = oi; }
+  }
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = best; si[threadIdx.x >> 6] = besti; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int ww = 1; ww < 4; ++ww)
+      if (sv[ww] > best || (sv[ww] == best && si[ww] < besti)) { best = sv[ww]; besti = si[ww]; }
+    p.tile_max[blockIdx.x] = best;
+    p.tile_arg[blockIdx.x] = besti;
+  }
 }
 
 // Rotary (rotate-half) cos/sin of pair i at position pos.  The angle
@@ -277,97 +422,6 @@ __global__ __launch_bounds__(64) void k_finish_qkv(const FinishParams p) {
   }
 }
 
-constexpr int kOneGroup = 1024;
-
-struct OneGroupSmem {
-  union {
-    TopkSmem<kOneGroup, uint16_t> topk;
-    Topk15Smem topk15;
-  };
-  float part[kOneGroup / kWave];
-};
-
-// Sum of squares of bf16 x[0..n) with a fixed order (thread-strided partial
-// sums, wave butterfly, waves in order).  All threads get the total.
-__device__ float one_group_sum_squares(const uint16_t* x, int n, float* part) {
-  float s = 0.f;
-  for (int i = threadIdx.x; i < n; i += kOneGroup) {
-    const float v = bf16_to_f32(x[i]);
-    s += v * v;
-  }
-  s = wave_sum_f32(s);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
-  __syncthreads();
-  float t = 0.f;
-#pragma unroll
-  for (int w = 0; w < kOneGroup / kWave; ++w) t += part[w];
-  __syncthreads();
-  return t;
-}
-
-__device__ void one_group_select(const uint16_t* x, int n, int k, int32_t* idx_out, OneGroupSmem& sm) {
-  auto key = [x](int i) -> uint32_t { return uint32_t(x[i]) & 0x7FFFu; };
-  auto emit = [idx_out](int r, int i) { idx_out[r] = i; };
-  if (n <= kTopk15MaxN)
-    block_topk15(n, k, key, emit, sm.topk15);
-  else
-    block_topk<kOneGroup, 15, uint16_t>(n, k, key, emit, sm.topk);
-}
-
-// One work-group: y = bf16(resid + sum of chunks); then optionally
-// x_next = RMSNorm(y) * gain and the top-k of x_next.
-__global__ __launch_bounds__(kOneGroup) void k_finish_resid(const FinishParams p) {
-  __shared__ OneGroupSmem sm;
-  for (int c = threadIdx.x * 4; c < p.d_out; c += kOneGroup * 4) {
-    const float4 v = chunk_sum4(p.partial, p.n_splits, p.d_out, c);
-    float r[4] = {v.x, v.y, v.z, v.w};
-    if (p.resid) {
-      const uint2 rr = *reinterpret_cast<const uint2*>(p.resid + c);
-      r[0] += bf16_lo(rr.x); r[1] += bf16_hi(rr.x); r[2] += bf16_lo(rr.y); r[3] += bf16_hi(rr.y);
-    }
-    uint2 o;
-    o.x = uint32_t(f32_to_bf16(r[0])) | (uint32_t(f32_to_bf16(r[1])) << 16);
-    o.y = uint32_t(f32_to_bf16(r[2])) | (uint32_t(f32_to_bf16(r[3])) << 16);
-    *reinterpret_cast<uint2*>(p.y + c) = o;
-  }
-  __syncthreads();
-  if (p.norm_gain == nullptr) return;
-  const float ss = one_group_sum_squares(p.y, p.d_out, sm.part);
-  const float inv = 1.0f / sqrtf(ss / float(p.d_out) + p.eps);
-  for (int c = threadIdx.x; c < p.d_out; c += kOneGroup)
-    p.x_next[c] = f32_to_bf16(bf16_to_f32(p.y[c]) * inv * bf16_to_f32(p.norm_gain[c]));
-  __syncthreads();
-  if (p.sel_k > 0 && p.sel_k < p.d_out) one_group_select(p.x_next, p.d_out, p.sel_k, p.idx_next, sm);
-}
-
-// SwiGLU over the packed gate | up chunks: tile t holds gate columns
-// [128t, 128t + w) and up columns [128t + w, 128t + 2w) of hidden units
-// [64t, 64t + w), w = min(64, d_ff - 64t).  One work-group when a top-k of
-// the result follows, else one thread per hidden unit.
-__global__ __launch_bounds__(kOneGroup) void k_finish_swiglu(const FinishParams p) {
-  __shared__ OneGroupSmem sm;
-  const int half = kGemvTile / 2;
-  const int stride = gridDim.x * kOneGroup * 4;
-  for (int u = (blockIdx.x * kOneGroup + threadIdx.x) * 4; u < p.d_ff; u += stride) {
-    const int t = u / half, off = u % half;
-    const int w = min(half, p.d_ff - t * half);
-    const float4 gt = chunk_sum4(p.partial, p.n_splits, p.d_out, t * kGemvTile + off);
-    const float4 up = chunk_sum4(p.partial, p.n_splits, p.d_out, t * kGemvTile + w + off);
-    const float g[4] = {gt.x, gt.y, gt.z, gt.w};
-    const float v[4] = {up.x, up.y, up.z, up.w};
-    uint16_t o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(g[e] / (1.0f + expf(-g[e])) * v[e]);
-    uint2 ov;
-    ov.x = uint32_t(o[0]) | (uint32_t(o[1]) << 16);
-    ov.y = uint32_t(o[2]) | (uint32_t(o[3]) << 16);
-    *reinterpret_cast<uint2*>(p.y + u) = ov;
-  }
-  if (p.sel_k <= 0 || p.sel_k >= p.d_ff) return;
-  __syncthreads();
-  one_group_select(p.y, p.d_ff, p.sel_k, p.idx_next, sm);
-}
-
 __global__ __launch_bounds__(256) void k_argmax_finish(const float* tile_max, const int32_t* tile_arg, int n_tiles,
                                                       int32_t* token) {
   __shared__ float sv[4];
@@ -394,72 +448,108 @@ __global__ __launch_bounds__(256) void k_argmax_finish(const float* tile_max, co
   }
 }
 
+
+constexpr int kOneGroup = 1024;
+
+struct OneGroupSmem {
+  union {
+    TopkSmem<kOneGroup, uint16_t> topk;
+    Topk15Smem topk15;
+  };
+};
+
+__device__ void one_group_select(const uint16_t* x, int n, int k, int32_t* idx_out, OneGroupSmem& sm) {
+  auto key = [x](int i) -> uint32_t { return uint32_t(x[i]) & 0x7FFFu; };
+  auto emit = [idx_out](int r, int i) { idx_out[r] = i; };
+  if (n <= kTopk15MaxN)
+    block_topk15(n, k, key, emit, sm.topk15);
+  else
+    block_topk<kOneGroup, 15, uint16_t>(n, k, key, emit, sm.topk);
+}
+
 __global__ __launch_bounds__(kOneGroup) void k_select(const uint16_t* x, int n, int k, int32_t* idx_out) {
   __shared__ OneGroupSmem sm;
   one_group_select(x, n, k, idx_out, sm);
 }
 
-__global__ __launch_bounds__(kOneGroup) void k_norm_select(const uint16_t* h, const uint16_t* g, int d, float eps,
-                                                          uint16_t* x_out, int k, int32_t* idx_out) {
-  __shared__ OneGroupSmem sm;
-  const float ss = one_group_sum_squares(h, d, sm.part);
-  const float inv = 1.0f / sqrtf(ss / float(d) + eps);
-  for (int i = threadIdx.x; i < d; i += kOneGroup)
-    x_out[i] = f32_to_bf16(bf16_to_f32(h[i]) * inv * bf16_to_f32(g[i]));
-  __syncthreads();
-  if (idx_out != nullptr && k > 0 && k < d) one_group_select(x_out, d, k, idx_out, sm);
-}
 
 }  // namespace
 
 static int gemv_target_groups() {
-  // tuning override for sweeps; the default is the measured best
+  // tuning override for sweeps; the default is one work-group per CU
   static const int v = [] {
     const char* e = getenv("BC_GEMV_GROUPS");
     const int x = e ? atoi(e) : 0;
-    return x > 0 ? x : 512;
+    return x > 0 ? x : 256;
   }();
   return v;
 }
 
-GemvPlan plan_gemv(int d_out, int k) {
+GemvPlan plan_gemv(int d_out, int k, bool single) {
   GemvPlan pl;
   pl.n_tiles = ceil_div(d_out, kGemvTile);
-  const int target_groups = gemv_target_groups();
-  int splits = ceil_div(target_groups, pl.n_tiles);
-  const int max_splits = k > 0 ? ceil_div(k, 64) : 1;   // at least 64 rows per chunk
-  if (splits > max_splits) splits = max_splits;
-  if (splits > 32) splits = 32;
-  if (splits < 1) splits = 1;
-  int rps = ceil_div(k > 0 ? k : 1, splits);
+  if (k < 1) k = 1;
+  int splits;
+  if (single && k <= kGemvMaxRows) {
+    splits = 1;
+  } else {
+    const int target = gemv_target_groups();
+    splits = (target + pl.n_tiles / 2) / pl.n_tiles;
+    splits = min(splits, k / 64);   // at least 64 rows per chunk
+    splits = max(splits, 1);
+    splits = max(splits, ceil_div(k, kGemvMaxRows));
+  }
+  int rps = ceil_div(k, splits);
   rps = (rps + 15) / 16 * 16;
-  pl.rows_per_split = rps;
-  pl.n_splits = k > 0 ? ceil_div(k, rps) : 1;
+  pl.rows_per_split = min(rps, kGemvMaxRows);
+  pl.n_splits = ceil_div(k, pl.rows_per_split);
   pl.partial_bytes = align_up(size_t(pl.n_splits) * d_out * 4, 256);
   return pl;
 }
 
-int launch_gemv_main(int mode, const GemvParams& p, hipStream_t s) {
-  dim3 grid(p.n_tiles, p.n_splits), block(kGemvThreads);
-  switch (mode) {
-    case MAIN_PARTIAL: k_gemv_main<MAIN_PARTIAL><<<grid, block, 0, s>>>(p); break;
-    case MAIN_BF16: k_gemv_main<MAIN_BF16><<<grid, block, 0, s>>>(p); break;
-    case MAIN_F32_ARGMAX: k_gemv_main<MAIN_F32_ARGMAX><<<grid, block, 0, s>>>(p); break;
-    default: return set_error(BC_ERR_INVALID, "unknown GEMV mode %d", mode);
+bool gemv_fused_input_ok(int d_in) { return d_in >= 1 && d_in % 4 == 0 && d_in <= kGemvFusedMaxIn; }
+
+namespace {
+template <int IN, int PMAX>
+int launch_gemv_out(int out, const GemvParams& p, dim3 grid, hipStream_t s) {
+  const dim3 block(kGemvThreads);
+  switch (out) {
+    case OUT_PARTIAL: k_gemv<IN, OUT_PARTIAL, PMAX><<<grid, block, 0, s>>>(p); break;
+    case OUT_BF16: k_gemv<IN, OUT_BF16, PMAX><<<grid, block, 0, s>>>(p); break;
+    case OUT_SWIGLU: k_gemv<IN, OUT_SWIGLU, PMAX><<<grid, block, 0, s>>>(p); break;
+    case OUT_ARGMAX: k_gemv<IN, OUT_ARGMAX, PMAX><<<grid, block, 0, s>>>(p); break;
+    default: return set_error(BC_ERR_INVALID, "unknown GEMV output %d", out);
   }
-  return check_launch("k_gemv_main");
+  return check_launch("k_gemv");
 }
+}  // namespace
+
+int launch_gemv(int in, int out, const GemvParams& p, hipStream_t s) {
+  if (p.n_splits < 1 || p.n_tiles < 1 || p.rows_per_split < 1 || p.rows_per_split > kGemvMaxRows ||
+      size_t(p.n_splits - 1) * p.rows_per_split >= size_t(p.k) || size_t(p.n_splits) * p.rows_per_split < size_t(p.k))
+    return set_error(BC_ERR_INVALID, "GEMV plan does not cover k=%d", p.k);
+  if (out != OUT_PARTIAL && p.n_splits != 1) return set_error(BC_ERR_INVALID, "GEMV epilogue needs one chunk");
+  if (out == OUT_SWIGLU && ceil_div(p.d_out, kGemvTile) != p.n_tiles)
+    return set_error(BC_ERR_INVALID, "SwiGLU epilogue: tile count");
+  const dim3 grid(p.n_tiles, p.n_splits);
+  if (in == IN_LIST) return launch_gemv_out<IN_LIST, 4>(out, p, grid, s);
+  if (in != IN_NORM && in != IN_SEL) return set_error(BC_ERR_INVALID, "unknown GEMV input %d", in);
+  if (!gemv_fused_input_ok(p.d_in)) return set_error(BC_ERR_UNSUPPORTED, "fused GEMV input d_in=%d", p.d_in);
+  const bool big = fused_per_thread(p.d_in) > 8;
+  if (in == IN_NORM)
+    return big ? launch_gemv_out<IN_NORM, 32>(out, p, grid, s) : launch_gemv_out<IN_NORM, 8>(out, p, grid, s);
+  return big ? launch_gemv_out<IN_SEL, 32>(out, p, grid, s) : launch_gemv_out<IN_SEL, 8>(out, p, grid, s);
+}
+
+int finish_argmax_groups(int d_out) { return ceil_div(d_out, 256); }
 
 int launch_finish(int kind, const FinishParams& p, hipStream_t s) {
   switch (kind) {
     case FIN_BF16: k_finish_bf16<<<ceil_div(p.d_out, 256), 256, 0, s>>>(p); break;
     case FIN_QKV: k_finish_qkv<<<p.n_heads + 2 * p.n_kv_heads, 64, 0, s>>>(p); break;
-    case FIN_RESID: k_finish_resid<<<1, kOneGroup, 0, s>>>(p); break;
-    case FIN_SWIGLU: {
-      const bool sel = p.sel_k > 0 && p.sel_k < p.d_ff;
-      k_finish_swiglu<<<sel ? 1 : ceil_div(p.d_ff, kOneGroup * 4), kOneGroup, 0, s>>>(p);
-      break;
-    }
+    case FIN_RESID: k_finish_resid<<<ceil_div(p.d_out, 128), 128, 0, s>>>(p); break;
+    case FIN_SWIGLU: k_finish_swiglu<<<ceil_div(p.d_ff, 256), 256, 0, s>>>(p); break;
+    case FIN_ARGMAX: k_finish_argmax<<<finish_argmax_groups(p.d_out), 256, 0, s>>>(p); break;
     default: return set_error(BC_ERR_INVALID, "unknown finish kind %d", kind);
   }
   return check_launch("k_finish");
@@ -468,12 +558,6 @@ int launch_finish(int kind, const FinishParams& p, hipStream_t s) {
 int launch_argmax_finish(const float* tile_max, const int32_t* tile_arg, int n_tiles, int32_t* token, hipStream_t s) {
   k_argmax_finish<<<1, 256, 0, s>>>(tile_max, tile_arg, n_tiles, token);
   return check_launch("k_argmax_finish");
-}
-
-int launch_norm_select(const uint16_t* h, const uint16_t* g, int d, float eps, uint16_t* x_out, int k,
-                       int32_t* idx_out, hipStream_t s) {
-  k_norm_select<<<1, kOneGroup, 0, s>>>(h, g, d, eps, x_out, k, idx_out);
-  return check_launch("k_norm_select");
 }
 
 int launch_select(const uint16_t* x, int n, int k, int32_t* idx_out, hipStream_t s) {
@@ -513,8 +597,8 @@ static int sparse_gemv_impl(const uint16_t* wt, int tiled, int d_in, int d_out, 
   p.rows_per_split = pl.rows_per_split; p.n_splits = pl.n_splits; p.n_tiles = pl.n_tiles;
   p.partial = static_cast<float*>(ws);
   p.y = y;
-  if (pl.n_splits == 1) return launch_gemv_main(MAIN_BF16, p, s);
-  int rc = launch_gemv_main(MAIN_PARTIAL, p, s);
+  if (pl.n_splits == 1) return launch_gemv(IN_LIST, OUT_BF16, p, s);
+  int rc = launch_gemv(IN_LIST, OUT_PARTIAL, p, s);
   if (rc != BC_OK) return rc;
   FinishParams f{};
   f.partial = p.partial; f.n_splits = pl.n_splits; f.d_out = d_out; f.y = y;

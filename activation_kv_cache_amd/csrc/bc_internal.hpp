@@ -17,11 +17,23 @@ int check_launch(const char* what);
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-constexpr int kGemvTile = 128;   // output columns per work-group (16 lanes x 8)
-constexpr int kGemvThreads = 256;
+constexpr int kGemvTile = 128;      // output columns per work-group (16 lanes x 8)
+constexpr int kGemvThreads = 512;   // 32 row slots of 16 lanes
+constexpr int kGemvMaxRows = 4096;  // rows (list positions) per work-group
+constexpr int kGemvFusedMaxIn = 16384;  // inputs a work-group normalises / selects itself
 
-enum GemvMode : int { MAIN_PARTIAL = 0, MAIN_BF16 = 1, MAIN_F32_ARGMAX = 2 };
-enum FinishKind : int { FIN_BF16 = 0, FIN_QKV = 1, FIN_RESID = 2, FIN_SWIGLU = 3 };
+// Where a GEMV work-group gets its input rows and values:
+//   IN_LIST  x and an optional ascending channel list are given;
+//   IN_NORM  x = bf16(RMSNorm(h) * gain) is formed in the prologue, then
+//            (k < d_in) the exact top-k of |x| is selected there too;
+//   IN_SEL   x is given and (k < d_in) its top-k is selected in the prologue.
+// Every work-group of a launch forms the same x and the same selection; the
+// first one also stores them (x_out, idx_out) when asked.
+enum GemvIn : int { IN_LIST = 0, IN_NORM = 1, IN_SEL = 2 };
+// What the main kernel stores: fp32 partials per chunk of rows, or (one
+// chunk) bf16 y, the SwiGLU of a gate|up tile, or fp32 y + per-tile argmax.
+enum GemvOut : int { OUT_PARTIAL = 0, OUT_BF16 = 1, OUT_SWIGLU = 2, OUT_ARGMAX = 3 };
+enum FinishKind : int { FIN_BF16 = 0, FIN_QKV = 1, FIN_RESID = 2, FIN_SWIGLU = 3, FIN_ARGMAX = 4 };
 
 struct GemvPlan {
   int n_tiles;
@@ -29,34 +41,37 @@ struct GemvPlan {
   int rows_per_split;
   size_t partial_bytes;   // n_splits * d_out fp32
 };
-GemvPlan plan_gemv(int d_out, int k);
+// single: one chunk of rows if it fits a work-group (for OUT_BF16 / SWIGLU /
+// ARGMAX epilogues)
+GemvPlan plan_gemv(int d_out, int k, bool single = false);
+bool gemv_fused_input_ok(int d_in);
 
 struct GemvParams {
   const uint16_t* wt;
   int tiled;              // 1: tile-major [tile][d_in][tile width]; 0: plain [d_in][d_out]
   int d_in, d_out;
-  const uint16_t* x;
-  const int32_t* idx;
+  const uint16_t* x;      // IN_LIST, IN_SEL: bf16 [d_in]
+  const int32_t* idx;     // IN_LIST: [k] or NULL
+  const uint16_t* h;      // IN_NORM: bf16 [d_in]
+  const uint16_t* gain;   // IN_NORM: bf16 [d_in]
+  float eps;
+  uint16_t* x_out;        // IN_NORM / IN_SEL: optional copy of x (first work-group)
+  int32_t* idx_out;       // IN_NORM / IN_SEL: optional copy of the selection
   int k;
   int rows_per_split, n_splits, n_tiles;
-  float* partial;         // MAIN_PARTIAL: [n_splits][d_out]
-  uint16_t* y;            // MAIN_BF16
-  float* yf;              // MAIN_F32_ARGMAX
+  float* partial;         // OUT_PARTIAL: [n_splits][d_out]
+  uint16_t* y;            // OUT_BF16: [d_out]; OUT_SWIGLU: [d_out / 2]
+  float* yf;              // OUT_ARGMAX
   float* tile_max;
   int32_t* tile_arg;
 };
-int launch_gemv_main(int mode, const GemvParams& p, hipStream_t s);
+int launch_gemv(int in, int out, const GemvParams& p, hipStream_t s);
 
 struct FinishParams {
   const float* partial;
   int n_splits, d_out;
   uint16_t* y;                  // bf16 output (d_out, or d_ff for SwiGLU)
-  const uint16_t* resid;        // FIN_RESID: optional residual
-  const uint16_t* norm_gain;    // FIN_RESID: RMSNorm gain of the next input (optional)
-  float eps;
-  uint16_t* x_next;             // FIN_RESID: RMSNorm output
-  int sel_k;                    // top-k of the next input when 0 < sel_k < n
-  int32_t* idx_next;
+  const uint16_t* resid;        // FIN_RESID: residual added to the sum
   // FIN_QKV
   uint16_t* q_out;
   uint16_t* k_cache;
@@ -66,8 +81,14 @@ struct FinishParams {
   double log2_theta;
   // FIN_SWIGLU
   int d_ff;
+  // FIN_ARGMAX
+  float* yf;
+  float* tile_max;
+  int32_t* tile_arg;
 };
 int launch_finish(int kind, const FinishParams& p, hipStream_t s);
+// work-groups of a FIN_ARGMAX launch (entries of tile_max / tile_arg)
+int finish_argmax_groups(int d_out);
 int launch_argmax_finish(const float* tile_max, const int32_t* tile_arg, int n_tiles, int32_t* token, hipStream_t s);
 
 struct AttnParams {
@@ -92,8 +113,6 @@ struct ReduceParams {
   uint16_t* out;
 };
 int launch_attn_reduce(const ReduceParams& p, hipStream_t s);
-// merge and, when 0 < k < n_heads*head_dim, the top-k of the merged output
-int launch_attn_reduce_select(const ReduceParams& p, int k, int32_t* idx_out, hipStream_t s);
 
 struct KvSelectParams {
   const uint16_t* q;
@@ -105,8 +124,6 @@ struct KvSelectParams {
 };
 int launch_kv_score_select(const KvSelectParams& p, hipStream_t s);
 
-int launch_norm_select(const uint16_t* h, const uint16_t* g, int d, float eps, uint16_t* x_out, int k,
-                       int32_t* idx_out, hipStream_t s);
 int launch_select(const uint16_t* x, int n, int k, int32_t* idx_out, hipStream_t s);
 int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 

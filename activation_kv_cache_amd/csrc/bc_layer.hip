@@ -3,16 +3,17 @@
 //
 // bc_decode_layer enqueues, on one stream and with no host synchronisation
 // (kernel boundaries are the only cross-work-group synchronisation):
-//   k_norm_select          x1 = RMSNorm(h) * g_attn; S1 = top-k(x1)      (1 work-group)
-//   k_gemv_main, k_finish_qkv   q, k, v over S1; rotary; append k, v at slot
-//                          n-1; refresh that block's (min, max) summary
+//   k_gemv<IN_NORM>, k_finish_qkv   x1 = RMSNorm(h) * g_attn and S1 = top-k(x1)
+//                          in every work-group's prologue; q, k, v over S1;
+//                          rotary; append k, v at slot n-1; refresh that
+//                          block's (min, max) summary
 //   k_kv_score, k_kv_block_select   KV list (r_kv < 1 only)
 //   k_attn_partial, k_attn_reduce   split-K attention -> a
-//   k_select               S2 = top-k(a)                                 (sparse only)
-//   k_gemv_main, k_finish_resid     h1 = h + W_o a over S2; x2 = RMSNorm(h1) * g_mlp;
-//                          S3 = top-k(x2)                                (finish: 1 work-group)
-//   k_gemv_main, k_finish_swiglu    f = SiLU(gate) * up over S3; S4 = top-k(f)
-//   k_gemv_main, k_finish_resid     h = h1 + W_down f over S4
+//   k_gemv<IN_SEL>, k_finish_resid  S2 = top-k(a) in the prologue;
+//                          h1 = h + W_o a over S2
+//   k_gemv<IN_NORM, OUT_SWIGLU>     x2 = RMSNorm(h1) * g_mlp, S3 = top-k(x2);
+//                          f = SiLU(gate) * up over S3 (one chunk per tile)
+//   k_gemv<IN_SEL>, k_finish_resid  S4 = top-k(f); h = h1 + W_down f over S4
 // Every launch size depends only on host-known scalars.
 #include <math.h>
 #include <stdarg.h>
@@ -89,7 +90,7 @@ size_t gemv_partial_max(const bc_model_dims& m) {
   const int outs[4] = {qkv, m.d, 2 * m.d_ff, m.d};
   const int ins[4] = {m.d, m.n_heads * m.head_dim, m.d, m.d_ff};
   for (int i = 0; i < 4; ++i) {
-    GemvPlan pl = plan_gemv(outs[i], ins[i]);
+    GemvPlan pl = plan_gemv(outs[i], ins[i], i == 2);
     if (pl.partial_bytes > mx) mx = pl.partial_bytes;
   }
   return mx;
@@ -130,7 +131,8 @@ int check_dims(const bc_model_dims* m) {
   if (!valid_head_dim(m->head_dim)) return set_error(BC_ERR_UNSUPPORTED, "dims: head_dim %d", m->head_dim);
   if (!valid_group(m->n_heads / m->n_kv_heads)) return set_error(BC_ERR_UNSUPPORTED, "dims: group size");
   if (m->d % 8 != 0 || m->d_ff % 8 != 0) return set_error(BC_ERR_UNSUPPORTED, "dims: d and d_ff must be multiples of 8");
-  if (m->d > 65536 || m->d_ff > 65536) return set_error(BC_ERR_UNSUPPORTED, "dims: d, d_ff <= 65536");
+  if (!gemv_fused_input_ok(m->d) || !gemv_fused_input_ok(m->d_ff))
+    return set_error(BC_ERR_UNSUPPORTED, "dims: d and d_ff must be at most %d", kGemvFusedMaxIn);
   return BC_OK;
 }
 
@@ -210,15 +212,39 @@ extern "C" size_t bc_layer_workspace_bytes(const bc_model_dims* dims, int max_ct
 
 namespace {
 
-// One projection: main kernel (chunk partials) and its finish.
-int run_gemv(const uint16_t* wt, int d_in, int d_out, const uint16_t* x, const int32_t* idx, int k, float* partial,
-             int fin_kind, FinishParams f, hipStream_t s) {
-  const GemvPlan pl = plan_gemv(d_out, k);
+// What a projection GEMV reads: IN_NORM forms x = RMSNorm(v) * gain, IN_SEL
+// takes x = v; with k < d_in the prologue also selects the top-k of |x|.
+struct ProjIn {
+  int mode;
+  const uint16_t* v;
+  const uint16_t* gain;
+  float eps;
+  uint16_t* x_out;      // optional copy of x
+  int32_t* idx_out;     // optional copy of the selection
+};
+
+// One projection: main kernel and, with several chunks, its finish.  The
+// gate|up GEMV (FIN_SWIGLU) runs as one chunk per tile when it fits, with
+// the SwiGLU in the main kernel's epilogue.
+int run_gemv(const uint16_t* wt, int d_in, int d_out, int k, const ProjIn& in, float* partial, int fin_kind,
+             FinishParams f, hipStream_t s) {
+  const bool swiglu = fin_kind == FIN_SWIGLU;
+  const GemvPlan pl = plan_gemv(d_out, k, swiglu);
   GemvParams p{};
-  p.wt = wt; p.tiled = 1; p.d_in = d_in; p.d_out = d_out; p.x = x; p.idx = idx; p.k = k;
+  p.wt = wt; p.tiled = 1; p.d_in = d_in; p.d_out = d_out; p.k = k;
+  if (in.mode == IN_NORM) {
+    p.h = in.v; p.gain = in.gain; p.eps = in.eps;
+  } else {
+    p.x = in.v;
+  }
+  p.x_out = in.x_out; p.idx_out = in.idx_out;
   p.rows_per_split = pl.rows_per_split; p.n_splits = pl.n_splits; p.n_tiles = pl.n_tiles;
   p.partial = partial;
-  int rc = launch_gemv_main(MAIN_PARTIAL, p, s);
+  if (swiglu && pl.n_splits == 1) {
+    p.y = f.y;
+    return launch_gemv(in.mode, OUT_SWIGLU, p, s);
+  }
+  int rc = launch_gemv(in.mode, OUT_PARTIAL, p, s);
   if (rc != BC_OK) return rc;
   f.partial = partial;
   f.n_splits = pl.n_splits;
@@ -226,20 +252,47 @@ int run_gemv(const uint16_t* wt, int d_in, int d_out, const uint16_t* x, const i
   return launch_finish(fin_kind, f, s);
 }
 
+// Final RMSNorm (in the GEMV prologue), dense LM head and argmax.
+int run_head(const bc_model_dims& m, const uint16_t* hidden, const uint16_t* g_final, const uint16_t* w_head,
+             float eps, float* logits, int32_t* token, float* partial, float* tile_max, int32_t* tile_arg,
+             hipStream_t s) {
+  const GemvPlan pl = plan_gemv(m.vocab, m.d, true);
+  GemvParams p{};
+  p.wt = w_head; p.tiled = 1; p.d_in = m.d; p.d_out = m.vocab; p.k = m.d;
+  p.h = hidden; p.gain = g_final; p.eps = eps;
+  p.rows_per_split = pl.rows_per_split; p.n_splits = pl.n_splits; p.n_tiles = pl.n_tiles;
+  p.yf = logits; p.tile_max = tile_max; p.tile_arg = tile_arg; p.partial = partial;
+  int rc;
+  if (pl.n_splits == 1) {
+    if ((rc = launch_gemv(IN_NORM, OUT_ARGMAX, p, s)) != BC_OK) return rc;
+    return launch_argmax_finish(tile_max, tile_arg, pl.n_tiles, token, s);
+  }
+  if ((rc = launch_gemv(IN_NORM, OUT_PARTIAL, p, s)) != BC_OK) return rc;
+  FinishParams f{};
+  f.partial = partial; f.n_splits = pl.n_splits; f.d_out = m.vocab;
+  f.yf = logits; f.tile_max = tile_max; f.tile_arg = tile_arg;
+  if ((rc = launch_finish(FIN_ARGMAX, f, s)) != BC_OK) return rc;
+  return launch_argmax_finish(tile_max, tile_arg, finish_argmax_groups(m.vocab), token, s);
+}
+
+// Workspace of the LM head: chunk partials (only when d exceeds one chunk)
+// and the per-tile argmax candidates.
+struct HeadLayout { size_t partial, tile_max, tile_arg, total; };
+HeadLayout head_layout(const bc_model_dims& m, size_t off = 0) {
+  const GemvPlan pl = plan_gemv(m.vocab, m.d, true);
+  const int n_cand = pl.n_tiles > finish_argmax_groups(m.vocab) ? pl.n_tiles : finish_argmax_groups(m.vocab);
+  HeadLayout L;
+  auto take = [&off](size_t bytes) { size_t o = off; off += align_up(bytes > 0 ? bytes : 1, 256); return o; };
+  L.partial = take(pl.n_splits > 1 ? pl.partial_bytes : 256);
+  L.tile_max = take(size_t(n_cand) * 4);
+  L.tile_arg = take(size_t(n_cand) * 4);
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 namespace {
-
-// What the layer does with its output besides writing h: the RMSNorm of h
-// with next_gain into next_x and, when next_sel_k > 0, its top-k into
-// next_idx (the next layer's x1 and S1, or the final norm before the head).
-struct LayerChain {
-  bool x1_ready;               // x1 / idx_qkv already in the workspace
-  const uint16_t* next_gain;
-  uint16_t* next_x;
-  int next_sel_k;
-  int32_t* next_idx;
-};
 
 int check_layer(const bc_layer* ly, const bc_step* st) {
   if (!ly->w_qkv || !ly->w_o || !ly->w_gu || !ly->w_down || !ly->g_attn || !ly->g_mlp || !ly->k_cache ||
@@ -265,7 +318,7 @@ int step_splits(const bc_model_dims& m, const bc_step* st, const bc_kv_budget_in
 }
 
 int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, const bc_kv_budget_info& bud,
-               int n_splits, uint16_t* hidden, void* ws, const LayerLayout& L, hipStream_t s, const LayerChain& ch) {
+               int n_splits, uint16_t* hidden, void* ws, const LayerLayout& L, hipStream_t s) {
   int rc;
   const int hd = m.head_dim, H = m.n_heads, Hkv = m.n_kv_heads;
   const bool kv_sparse = st->kv.r_kv < 1.0;
@@ -281,21 +334,18 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
   int32_t* idx_o = sparse ? at<int32_t>(ws, L.idx_o) : nullptr;
   int32_t* idx_gu = sparse ? at<int32_t>(ws, L.idx_gu) : nullptr;
   int32_t* idx_down = sparse ? at<int32_t>(ws, L.idx_down) : nullptr;
+  uint16_t* h_mid = at<uint16_t>(ws, L.h_mid);
+  uint16_t* a = at<uint16_t>(ws, L.a);
+  uint16_t* hff = at<uint16_t>(ws, L.hff);
 
-  // x1 = RMSNorm(h), S1
-  if (!ch.x1_ready) {
-    rc = launch_norm_select(hidden, ly->g_attn, m.d, eps, at<uint16_t>(ws, L.x1), k_d, idx_qkv, s);
-    if (rc != BC_OK) return rc;
-  }
-
-  // q, k, v; rotary; append; summary
+  // x1 = RMSNorm(h), S1 (GEMV prologue); q, k, v; rotary; append; summary
   {
+    const ProjIn in{IN_NORM, hidden, ly->g_attn, eps, at<uint16_t>(ws, L.x1), idx_qkv};
     FinishParams f{};
     f.q_out = at<uint16_t>(ws, L.q); f.k_cache = ly->k_cache; f.v_cache = ly->v_cache; f.summary = ly->kv_summary;
     f.n_heads = H; f.n_kv_heads = Hkv; f.head_dim = hd; f.n_cap = ly->n_cap; f.pos = pos;
     f.log2_theta = log2(st->rope_theta);
-    rc = run_gemv(ly->w_qkv, m.d, qkv_out, at<uint16_t>(ws, L.x1), idx_qkv, k_d, partial, FIN_QKV, f, s);
-    if (rc != BC_OK) return rc;
+    if ((rc = run_gemv(ly->w_qkv, m.d, qkv_out, k_d, in, partial, FIN_QKV, f, s)) != BC_OK) return rc;
   }
 
   // KV selection
@@ -307,7 +357,7 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
     if ((rc = launch_kv_score_select(p, s)) != BC_OK) return rc;
   }
 
-  // attention; S2 = top-k(a)
+  // attention
   {
     AttnParams p{};
     p.q = at<uint16_t>(ws, L.q); p.k_cache = ly->k_cache; p.v_cache = ly->v_cache; p.n_cap = ly->n_cap;
@@ -317,36 +367,32 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
     p.m = at<float>(ws, L.m); p.l = at<float>(ws, L.l); p.o = at<float>(ws, L.o);
     if ((rc = launch_attn_partial(p, s)) != BC_OK) return rc;
     ReduceParams r{};
-    r.m = p.m; r.l = p.l; r.o = p.o; r.n_heads = H; r.n_splits = n_splits; r.head_dim = hd;
-    r.out = at<uint16_t>(ws, L.a);
-    rc = sparse ? launch_attn_reduce_select(r, k_d, idx_o, s) : launch_attn_reduce(r, s);
-    if (rc != BC_OK) return rc;
+    r.m = p.m; r.l = p.l; r.o = p.o; r.n_heads = H; r.n_splits = n_splits; r.head_dim = hd; r.out = a;
+    if ((rc = launch_attn_reduce(r, s)) != BC_OK) return rc;
   }
 
-  // h1 = h + W_o a; x2 = RMSNorm(h1); S3
+  // S2 = top-k(a) (GEMV prologue); h1 = h + W_o a
   {
+    const ProjIn in{IN_SEL, a, nullptr, 0.f, nullptr, idx_o};
     FinishParams f{};
-    f.y = at<uint16_t>(ws, L.h_mid); f.resid = hidden; f.norm_gain = ly->g_mlp; f.eps = eps;
-    f.x_next = at<uint16_t>(ws, L.x2); f.sel_k = sparse ? k_d : 0; f.idx_next = idx_gu;
-    rc = run_gemv(ly->w_o, H * hd, m.d, at<uint16_t>(ws, L.a), idx_o, k_d, partial, FIN_RESID, f, s);
-    if (rc != BC_OK) return rc;
+    f.y = h_mid; f.resid = hidden;
+    if ((rc = run_gemv(ly->w_o, H * hd, m.d, k_d, in, partial, FIN_RESID, f, s)) != BC_OK) return rc;
   }
 
-  // f = SiLU(gate) * up; S4
+  // x2 = RMSNorm(h1), S3 (GEMV prologue); f = SiLU(gate) * up
   {
+    const ProjIn in{IN_NORM, h_mid, ly->g_mlp, eps, at<uint16_t>(ws, L.x2), idx_gu};
     FinishParams f{};
-    f.y = at<uint16_t>(ws, L.hff); f.d_ff = m.d_ff; f.sel_k = sparse ? k_ff : 0; f.idx_next = idx_down;
-    rc = run_gemv(ly->w_gu, m.d, 2 * m.d_ff, at<uint16_t>(ws, L.x2), idx_gu, k_d, partial, FIN_SWIGLU, f, s);
-    if (rc != BC_OK) return rc;
+    f.y = hff; f.d_ff = m.d_ff;
+    if ((rc = run_gemv(ly->w_gu, m.d, 2 * m.d_ff, k_d, in, partial, FIN_SWIGLU, f, s)) != BC_OK) return rc;
   }
 
-  // h = h1 + W_down f; optionally the next input's RMSNorm and top-k
+  // S4 = top-k(f) (GEMV prologue); h = h1 + W_down f
   {
+    const ProjIn in{IN_SEL, hff, nullptr, 0.f, nullptr, idx_down};
     FinishParams f{};
-    f.y = hidden; f.resid = at<uint16_t>(ws, L.h_mid);
-    f.norm_gain = ch.next_gain; f.eps = eps; f.x_next = ch.next_x; f.sel_k = ch.next_sel_k; f.idx_next = ch.next_idx;
-    rc = run_gemv(ly->w_down, m.d_ff, m.d, at<uint16_t>(ws, L.hff), idx_down, k_ff, partial, FIN_RESID, f, s);
-    if (rc != BC_OK) return rc;
+    f.y = hidden; f.resid = h_mid;
+    if ((rc = run_gemv(ly->w_down, m.d_ff, m.d, k_ff, in, partial, FIN_RESID, f, s)) != BC_OK) return rc;
   }
 
   if (const bc_layer_taps* t = st->taps) {
@@ -360,29 +406,24 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
       if (t->v && (rc = copy_tap(t->v + size_t(g) * hd, ly->v_cache + src, size_t(hd) * 2, s)) != BC_OK) return rc;
     }
     if (kv_sparse && (rc = copy_tap(t->idx_kv, at<void>(ws, L.idx_kv), size_t(Hkv) * n_sel * 4, s)) != BC_OK) return rc;
-    if ((rc = copy_tap(t->a, at<void>(ws, L.a), qb, s)) != BC_OK) return rc;
+    if ((rc = copy_tap(t->a, a, qb, s)) != BC_OK) return rc;
     if (sparse && (rc = copy_tap(t->idx_o, idx_o, size_t(k_d) * 4, s)) != BC_OK) return rc;
-    if ((rc = copy_tap(t->h_mid, at<void>(ws, L.h_mid), size_t(m.d) * 2, s)) != BC_OK) return rc;
+    if ((rc = copy_tap(t->h_mid, h_mid, size_t(m.d) * 2, s)) != BC_OK) return rc;
     if ((rc = copy_tap(t->x2, at<void>(ws, L.x2), size_t(m.d) * 2, s)) != BC_OK) return rc;
     if (sparse && (rc = copy_tap(t->idx_gu, idx_gu, size_t(k_d) * 4, s)) != BC_OK) return rc;
-    if ((rc = copy_tap(t->hff, at<void>(ws, L.hff), size_t(m.d_ff) * 2, s)) != BC_OK) return rc;
+    if ((rc = copy_tap(t->hff, hff, size_t(m.d_ff) * 2, s)) != BC_OK) return rc;
     if (sparse && (rc = copy_tap(t->idx_down, idx_down, size_t(k_ff) * 4, s)) != BC_OK) return rc;
   }
   return BC_OK;
 }
 
-// Head extras placed after the layer layout in a step workspace.
-struct StepLayout { LayerLayout layer; size_t xh, tile_max, tile_arg, total; };
+// A step workspace: the layer layout, then the LM head's.
+struct StepLayout { LayerLayout layer; HeadLayout head; size_t total; };
 StepLayout step_layout(const bc_model_dims& m, int n_ctx, int n_splits) {
   StepLayout S;
   S.layer = layer_layout(m, n_ctx, n_splits);
-  size_t off = S.layer.total;
-  auto take = [&off](size_t bytes) { size_t o = off; off += align_up(bytes > 0 ? bytes : 1, 256); return o; };
-  const int n_tiles = ceil_div(m.vocab, kGemvTile);
-  S.xh = take(size_t(m.d) * 2);
-  S.tile_max = take(size_t(n_tiles) * 4);
-  S.tile_arg = take(size_t(n_tiles) * 4);
-  S.total = off;
+  S.head = head_layout(m, S.layer.total);
+  S.total = S.head.total;
   return S;
 }
 
@@ -400,8 +441,7 @@ extern "C" int bc_decode_layer(const bc_model_dims* dims, const bc_layer* ly, co
   const LayerLayout L = layer_layout(*dims, st->n_ctx, n_splits);
   if (ws_bytes < L.total) return set_error(BC_ERR_WORKSPACE, "bc_decode_layer: workspace %zu < %zu", ws_bytes, L.total);
   if (reinterpret_cast<uintptr_t>(ws) & 255) return set_error(BC_ERR_INVALID, "bc_decode_layer: ws not 256-byte aligned");
-  LayerChain ch{false, nullptr, nullptr, 0, nullptr};
-  return layer_body(*dims, ly, st, bud, n_splits, hidden, ws, L, static_cast<hipStream_t>(stream), ch);
+  return layer_body(*dims, ly, st, bud, n_splits, hidden, ws, L, static_cast<hipStream_t>(stream));
 }
 
 extern "C" size_t bc_step_workspace_bytes(const bc_model_dims* dims, int max_ctx, int max_splits) {
@@ -428,44 +468,15 @@ extern "C" int bc_decode_step(const bc_model_dims* dims, const bc_layer* layers,
   if (ws_bytes < S.total) return set_error(BC_ERR_WORKSPACE, "bc_decode_step: workspace %zu < %zu", ws_bytes, S.total);
   if (reinterpret_cast<uintptr_t>(ws) & 255) return set_error(BC_ERR_INVALID, "bc_decode_step: ws not 256-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool sparse = st->r_p < 1.0;
-  const int k_d = bc_channel_keep(st->r_p, m.d);
   bc_step one = *st;
   one.taps = nullptr;
-  for (int i = 0; i < n_layers; ++i) {
-    const bool last = i + 1 == n_layers;
-    LayerChain ch;
-    ch.x1_ready = i > 0;
-    ch.next_gain = last ? g_final : layers[i + 1].g_attn;
-    ch.next_x = last ? at<uint16_t>(ws, S.xh) : at<uint16_t>(ws, S.layer.x1);
-    ch.next_sel_k = (!last && sparse) ? k_d : 0;
-    ch.next_idx = at<int32_t>(ws, S.layer.idx_qkv);
-    if ((rc = layer_body(m, &layers[i], &one, bud, n_splits, hidden, ws, S.layer, s, ch)) != BC_OK) return rc;
-  }
-  GemvParams p{};
-  p.wt = w_head; p.tiled = 1; p.d_in = m.d; p.d_out = m.vocab; p.x = at<uint16_t>(ws, S.xh); p.idx = nullptr;
-  p.k = m.d; p.rows_per_split = m.d; p.n_splits = 1; p.n_tiles = ceil_div(m.vocab, kGemvTile);
-  p.yf = logits; p.tile_max = at<float>(ws, S.tile_max); p.tile_arg = at<int32_t>(ws, S.tile_arg);
-  if ((rc = launch_gemv_main(MAIN_F32_ARGMAX, p, s)) != BC_OK) return rc;
-  return launch_argmax_finish(p.tile_max, p.tile_arg, p.n_tiles, token, s);
+  for (int i = 0; i < n_layers; ++i)
+    if ((rc = layer_body(m, &layers[i], &one, bud, n_splits, hidden, ws, S.layer, s)) != BC_OK) return rc;
+  return run_head(m, hidden, g_final, w_head, float(st->rms_eps), logits, token, at<float>(ws, S.head.partial),
+                  at<float>(ws, S.head.tile_max), at<int32_t>(ws, S.head.tile_arg), s);
 }
 
 // ------------------------------------------------------------------ LM head
-namespace {
-struct HeadLayout { size_t x, logits_tile_max, tile_arg, total; };
-HeadLayout head_layout(const bc_model_dims& m) {
-  const int n_tiles = ceil_div(m.vocab, kGemvTile);
-  HeadLayout L;
-  size_t off = 0;
-  auto take = [&off](size_t bytes) { size_t o = off; off += align_up(bytes > 0 ? bytes : 1, 256); return o; };
-  L.x = take(size_t(m.d) * 2);
-  L.logits_tile_max = take(size_t(n_tiles) * 4);
-  L.tile_arg = take(size_t(n_tiles) * 4);
-  L.total = off;
-  return L;
-}
-}  // namespace
-
 extern "C" size_t bc_lm_head_workspace_bytes(const bc_model_dims* dims) {
   if (check_dims(dims) != BC_OK || dims->vocab <= 0 || dims->vocab % 8 != 0) return 0;
   return head_layout(*dims).total;
@@ -481,13 +492,7 @@ extern "C" int bc_lm_head(const bc_model_dims* dims, const uint16_t* hidden, con
   if (dims->vocab <= 0 || dims->vocab % 8 != 0) return set_error(BC_ERR_UNSUPPORTED, "bc_lm_head: vocab %% 8 != 0");
   const HeadLayout L = head_layout(*dims);
   if (ws_bytes < L.total) return set_error(BC_ERR_WORKSPACE, "bc_lm_head: workspace %zu < %zu", ws_bytes, L.total);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  rc = launch_norm_select(hidden, g_final, dims->d, float(rms_eps), at<uint16_t>(ws, L.x), dims->d, nullptr, s);
-  if (rc != BC_OK) return rc;
-  GemvParams p{};
-  p.wt = w_head_t; p.tiled = 1; p.d_in = dims->d; p.d_out = dims->vocab; p.x = at<uint16_t>(ws, L.x); p.idx = nullptr;
-  p.k = dims->d; p.rows_per_split = dims->d; p.n_splits = 1; p.n_tiles = ceil_div(dims->vocab, kGemvTile);
-  p.yf = logits; p.tile_max = at<float>(ws, L.logits_tile_max); p.tile_arg = at<int32_t>(ws, L.tile_arg);
-  if ((rc = launch_gemv_main(MAIN_F32_ARGMAX, p, s)) != BC_OK) return rc;
-  return launch_argmax_finish(p.tile_max, p.tile_arg, p.n_tiles, token, s);
+  if (reinterpret_cast<uintptr_t>(ws) & 15) return set_error(BC_ERR_INVALID, "bc_lm_head: ws not 16-byte aligned");
+  return run_head(*dims, hidden, g_final, w_head_t, float(rms_eps), logits, token, at<float>(ws, L.partial),
+                  at<float>(ws, L.tile_max), at<int32_t>(ws, L.tile_arg), static_cast<hipStream_t>(stream));
 }
