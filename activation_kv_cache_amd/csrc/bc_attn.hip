@@ -49,10 +49,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 template <int D, int G>
 struct AttnSmem {
+  static constexpr int NST = kAttnThreads / (D / 16);   // row-group states per work-group
+  static constexpr int OSTRIDE = G * D + 4;             // padded: row groups write to different banks
   uint16_t q[G][D];
-  float o[kAttnWaves][G][D];
-  float m[kAttnWaves][G];
-  float l[kAttnWaves][G];
+  uint16_t knew[D];   // the current token's k, v (appending work-group)
+  uint16_t vnew[D];
+  alignas(16) float st_o[NST * OSTRIDE];
+  alignas(16) float st_m[G][NST];
+  alignas(16) float st_mx[G][NST];
+  alignas(16) float st_l[G][NST];
+  alignas(16) float wt[G][NST];
+  float M[G];
   int32_t idx[kIdxChunk];
 };
 
@@ -169,26 +176,12 @@ __device__ __forceinline__ void attn_compute(const AttnRows& rw, const uint16_t*
   }
 }
 
-// Merge state b into a (same lane dims).
-template <int G>
-__device__ __forceinline__ void attn_merge(AttnState<G>& a, const AttnState<G>& b, float c) {
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const float M = fmaxf(a.m[j], b.m[j]);
-    const float wa = a.m[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((a.m[j] - M) * c);
-    const float wb = b.m[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((b.m[j] - M) * c);
-    a.l[j] = a.l[j] * wa + b.l[j] * wb;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) a.o[j][e] = a.o[j][e] * wa + b.o[j][e] * wb;
-    a.m[j] = M;
-  }
-}
-
-template <int D, int G>
+template <int D, int G, int QM, int LM>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams p) {
   constexpr int LPT = D / 16;          // lanes per row
   constexpr int TPL = kWave / LPT;     // rows per wave load
   constexpr int TPI = 2 * TPL;         // rows per wave iteration
+  constexpr int STEP = kAttnWaves * TPI;
   constexpr int HALF = D / 2;
   __shared__ AttnSmem<D, G> sm;
 
@@ -200,9 +193,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
   const int hi = min(p.n_sel, lo + cn);
   const float c = p.scale_log2;
   const float tau = 8.0f / c;
+  // the work-group holding the current token attends to it from LDS, not
+  // from the cache slot it writes
+  const bool appends = QM == Q_PARTIAL && lo <= p.pos && p.pos < hi;
+  const int hi_main = appends ? p.pos : hi;
 
-  for (int i = tid; i < G * D / 8; i += kAttnThreads)
-    reinterpret_cast<uint4*>(&sm.q[0][0])[i] = reinterpret_cast<const uint4*>(p.q + size_t(g) * G * D)[i];
   AttnState<G> st;
 #pragma unroll
   for (int j = 0; j < G; ++j) {
@@ -214,87 +209,211 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
   }
   const uint16_t* Kg = p.k_cache + size_t(g) * p.n_cap * D + 8 * r;
   const uint16_t* Vg = p.v_cache + size_t(g) * p.n_cap * D + 8 * r;
-  const int32_t* idxg = p.idx ? p.idx + size_t(g) * p.n_sel : nullptr;
 
+  // the appending work-group refreshes the (min, max) summary of the
+  // current token's block; the block's older rows are loaded now and used
+  // at the end, so their latency hides under the main loop
+  const bool refresh = QM == Q_PARTIAL && appends && p.summary != nullptr && tid < D;
+  const int blk = p.pos / 16;
+  uint32_t srow[8];
+  if (refresh) {
+    const uint16_t* kc = p.k_cache + size_t(g) * p.n_cap * D + tid;
+#pragma unroll
+    for (int t = 0; t < 16; t += 2) {
+      const uint32_t a = blk * 16 + t < p.pos ? kc[size_t(blk * 16 + t) * D] : 0u;
+      const uint32_t b = blk * 16 + t + 1 < p.pos ? kc[size_t(blk * 16 + t + 1) * D] : 0u;
+      srow[t / 2] = a | (b << 16);
+    }
+  }
+
+  // dense list: the first rows are known before q, so they go in flight now
+  AttnRows rw;
+  int base = lo + w * TPI;
+  if constexpr (LM == L_DENSE) {
+    if (base < hi_main) attn_load<D>(Kg, Vg, nullptr, base, lo, hi_main, sub, rw);
+  }
+
+  if constexpr (QM == Q_GLOBAL) {
+    for (int i = tid; i < G * D / 8; i += kAttnThreads)
+      reinterpret_cast<uint4*>(&sm.q[0][0])[i] = reinterpret_cast<const uint4*>(p.q + size_t(g) * G * D)[i];
+  } else {
+    // q: rotary pairs (i, i + D/2) of the group's heads, summed over the qkv
+    // GEMV chunks in chunk order, rounded to bf16
+    for (int e = tid; e < G * HALF; e += kAttnThreads) {
+      const int j = e / HALF, i = e % HALF;
+      const int col = (g * G + j) * D + i;
+      const float a = chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, col);
+      const float b = chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, col + HALF);
+      const float cs = p.rope.c[i], sn = p.rope.s[i];
+      const uint16_t qa = f32_to_bf16(a * cs - b * sn), qb = f32_to_bf16(b * cs + a * sn);
+      sm.q[j][i] = qa;
+      sm.q[j][i + HALF] = qb;
+      if (s == 0 && p.q_out) {
+        p.q_out[size_t(g * G + j) * D + i] = qa;
+        p.q_out[size_t(g * G + j) * D + i + HALF] = qb;
+      }
+    }
+    if (appends) {
+      const int kcol = p.n_heads * D + g * D, vcol = (p.n_heads + p.n_kv_heads) * D + g * D;
+      uint16_t* kr = p.k_cache + (size_t(g) * p.n_cap + p.pos) * D;
+      uint16_t* vr = p.v_cache + (size_t(g) * p.n_cap + p.pos) * D;
+      for (int i = tid; i < HALF; i += kAttnThreads) {
+        const float a = chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + i);
+        const float b = chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + i + HALF);
+        const float cs = p.rope.c[i], sn = p.rope.s[i];
+        const uint16_t ka = f32_to_bf16(a * cs - b * sn), kb = f32_to_bf16(b * cs + a * sn);
+        sm.knew[i] = ka;
+        sm.knew[i + HALF] = kb;
+        kr[i] = ka;
+        kr[i + HALF] = kb;
+      }
+      for (int i = tid; i < D; i += kAttnThreads) {
+        const uint16_t v = f32_to_bf16(chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, vcol + i));
+        sm.vnew[i] = v;
+        vr[i] = v;
+      }
+    }
+  }
   __syncthreads();
-  for (int c0 = lo; c0 < hi; c0 += kIdxChunk) {
-    const int c1 = min(hi, c0 + kIdxChunk);
-    const int32_t* sidx = nullptr;
-    if (idxg) {
+
+  if constexpr (LM == L_DENSE) {
+    const int c1 = hi_main;
+    if (base < c1) {
+      if (base + TPI <= c1)
+        attn_compute<D, G, false>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
+      else
+        attn_compute<D, G, true>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
+      base += STEP;
+      for (; base + TPI <= c1; base += STEP) {
+        attn_load<D>(Kg, Vg, nullptr, base, lo, c1, sub, rw);
+        attn_compute<D, G, false>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
+      }
+      if (base < c1) {
+        attn_load<D>(Kg, Vg, nullptr, base, lo, c1, sub, rw);
+        attn_compute<D, G, true>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
+      }
+    }
+  } else {
+    const int32_t* idxg = p.idx + size_t(g) * p.n_sel;
+    for (int c0 = lo; c0 < hi; c0 += kIdxChunk) {
+      const int c1 = min(hi, c0 + kIdxChunk);
       for (int i = tid; i < c1 - c0; i += kAttnThreads) sm.idx[i] = idxg[c0 + i];
       __syncthreads();
-      sidx = sm.idx;
+      base = c0 + w * TPI;
+      for (; base + TPI <= c1; base += STEP) {
+        attn_load<D>(Kg, Vg, sm.idx, base, c0, c1, sub, rw);
+        attn_compute<D, G, false>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
+      }
+      if (base < c1) {
+        attn_load<D>(Kg, Vg, sm.idx, base, c0, c1, sub, rw);
+        attn_compute<D, G, true>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
+      }
+      __syncthreads();
     }
-    int base = c0 + w * TPI;
-    for (; base + TPI <= c1; base += kAttnWaves * TPI) {
-      AttnRows rw;
-      attn_load<D>(Kg, Vg, sidx, base, c0, c1, sub, rw);
-      attn_compute<D, G, false>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
-    }
-    if (base < c1) {
-      AttnRows rw;
-      attn_load<D>(Kg, Vg, sidx, base, c0, c1, sub, rw);
-      attn_compute<D, G, true>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
-    }
-    if (idxg) __syncthreads();
   }
 
-  // express every lane state at its true max, then merge the row groups of
-  // the wave (lanes with the same r), then the waves
+  // the current token: wave 0, lane group 0 takes it as its row 0; every
+  // other row of that step is masked
+  if (appends && w == 0) {
+    AttnRows nr;
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const float alpha = st.m[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st.m[j] - st.mx[j]) * c);
-    st.l[j] *= alpha;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) st.o[j][e] *= alpha;
-    st.m[j] = st.mx[j];
+    for (int u = 0; u < 2; ++u) {
+      nr.ka[u] = *reinterpret_cast<const uint4*>(sm.knew + 8 * r);
+      nr.kb[u] = *reinterpret_cast<const uint4*>(sm.knew + HALF + 8 * r);
+      nr.va[u] = *reinterpret_cast<const uint4*>(sm.vnew + 8 * r);
+      nr.vb[u] = *reinterpret_cast<const uint4*>(sm.vnew + HALF + 8 * r);
+    }
+    attn_compute<D, G, true>(nr, &sm.q[0][0], 0, 1, sub, r, c, tau, st);
   }
-#pragma unroll
-  for (int off = LPT; off < kWave; off <<= 1) {
-    AttnState<G> o;
+
+  // merge the row groups' states in LDS: every row group writes its lazy
+  // state (m, l, o) and its true max; the weight of state k for head j is
+  // 2^((m_k - M_j) c) with M_j the largest true max, and each output dim is
+  // the weighted sum over the states in state order
+  {
+    using SM = AttnSmem<D, G>;
+    constexpr int NSUB = kWave / LPT;
+    const int k = w * NSUB + sub;
+    float* so = sm.st_o + k * SM::OSTRIDE;
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      o.m[j] = __shfl_xor(st.m[j], off, kWave);
-      o.l[j] = __shfl_xor(st.l[j], off, kWave);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o.o[j][e] = __shfl_xor(st.o[j][e], off, kWave);
-    }
-    attn_merge<G>(st, o, c);
-  }
-  if (sub == 0) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sm.o[w][j][8 * r + e] = st.o[j][e];
-        sm.o[w][j][HALF + 8 * r + e] = st.o[j][8 + e];
-      }
-      if (r == 0) { sm.m[w][j] = st.m[j]; sm.l[w][j] = st.l[j]; }
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < G * D; e += kAttnThreads) {
-    const int j = e / D, d = e % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int q = 0; q < kAttnWaves; ++q) M = fmaxf(M, sm.m[q][j]);
-    float acc = 0.f, lsum = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int q = 0; q < kAttnWaves; ++q) {
-        const float mq = sm.m[q][j];
-        if (mq == -INFINITY) continue;
-        const float wq = __builtin_amdgcn_exp2f((mq - M) * c);
-        acc += sm.o[q][j][d] * wq;
-        lsum += sm.l[q][j] * wq;
+      float4* d0 = reinterpret_cast<float4*>(so + j * D + 8 * r);
+      float4* d1 = reinterpret_cast<float4*>(so + j * D + HALF + 8 * r);
+      d0[0] = make_float4(st.o[j][0], st.o[j][1], st.o[j][2], st.o[j][3]);
+      d0[1] = make_float4(st.o[j][4], st.o[j][5], st.o[j][6], st.o[j][7]);
+      d1[0] = make_float4(st.o[j][8], st.o[j][9], st.o[j][10], st.o[j][11]);
+      d1[1] = make_float4(st.o[j][12], st.o[j][13], st.o[j][14], st.o[j][15]);
+      if (r == 0) {
+        sm.st_m[j][k] = st.m[j];
+        sm.st_mx[j][k] = st.mx[j];
+        sm.st_l[j][k] = st.l[j];
       }
     }
-    const int jh = g * G + j;
-    p.o[(size_t(jh) * p.n_splits + s) * D + d] = acc;
-    if (d == 0) {
-      p.m[size_t(jh) * p.n_splits + s] = M == -INFINITY ? -INFINITY : M * c * kLn2;
-      p.l[size_t(jh) * p.n_splits + s] = lsum;
+    __syncthreads();
+    static_assert(SM::NST % 4 == 0, "states in float4 groups");
+    for (int e = tid; e < G * SM::NST; e += kAttnThreads) {
+      const int j = e / SM::NST, kk = e % SM::NST;
+      float M = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < SM::NST; q += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(&sm.st_mx[j][q]);
+        M = fmaxf(M, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+      }
+      const float mk = sm.st_m[j][kk];
+      sm.wt[j][kk] = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mk - M) * c);
+      if (kk == 0) sm.M[j] = M;
     }
+    __syncthreads();
+    // two adjacent dims per thread (64-bit LDS reads), weights four at a time
+    for (int e = 2 * tid; e < G * D; e += 2 * kAttnThreads) {
+      const int j = e / D, d = e % D;
+      float ax = 0.f, ay = 0.f;
+#pragma unroll
+      for (int q = 0; q < SM::NST; q += 4) {
+        const float4 wv = *reinterpret_cast<const float4*>(&sm.wt[j][q]);
+        const float wq[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float2 ov = *reinterpret_cast<const float2*>(&sm.st_o[(q + u) * SM::OSTRIDE + j * D + d]);
+          ax += ov.x * wq[u];
+          ay += ov.y * wq[u];
+        }
+      }
+      const int jh = g * G + j;
+      *reinterpret_cast<float2*>(&p.o[(size_t(jh) * p.n_splits + s) * D + d]) = make_float2(ax, ay);
+      if (d == 0) {
+        float lsum = 0.f;
+#pragma unroll
+        for (int q = 0; q < SM::NST; q += 4) {
+          const float4 lv = *reinterpret_cast<const float4*>(&sm.st_l[j][q]);
+          const float4 wv = *reinterpret_cast<const float4*>(&sm.wt[j][q]);
+          lsum += lv.x * wv.x;
+          lsum += lv.y * wv.y;
+          lsum += lv.z * wv.z;
+          lsum += lv.w * wv.w;
+        }
+        const float M = sm.M[j];
+        p.m[size_t(jh) * p.n_splits + s] = M == -INFINITY ? -INFINITY : M * c * kLn2;
+        p.l[size_t(jh) * p.n_splits + s] = lsum;
+      }
+    }
+  }
+  if (refresh) {
+    // per dim: the new row first, then rows 16*blk.. in order (rows from
+    // pos on are the new row); an equal value never replaces an earlier one
+    const uint16_t nb = sm.knew[tid];
+    uint16_t bmn = nb, bmx = nb;
+    float mn = bf16_to_f32(nb), mx = mn;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const uint16_t u = blk * 16 + t < p.pos ? uint16_t(srow[t / 2] >> (16 * (t & 1))) : nb;
+      const float f = bf16_to_f32(u);
+      if (f < mn) { mn = f; bmn = u; }
+      if (f > mx) { mx = f; bmx = u; }
+    }
+    uint16_t* sp = p.summary + ((size_t(g) * (p.n_cap / 16) + blk) * D + tid) * 2;
+    sp[0] = bmn;
+    sp[1] = bmx;
   }
 }
 
@@ -361,24 +480,35 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_reduce(const ReduceParams
   }
 }
 
-template <int D>
-int launch_partial_d(const AttnParams& p, hipStream_t s) {
+template <int D, int QM, int LM>
+int launch_partial_dql(const AttnParams& p, hipStream_t s) {
   dim3 grid(p.n_splits, p.n_kv_heads), block(kAttnThreads);
   switch (p.n_heads / p.n_kv_heads) {
-    case 1: k_attn_partial<D, 1><<<grid, block, 0, s>>>(p); break;
-    case 2: k_attn_partial<D, 2><<<grid, block, 0, s>>>(p); break;
-    case 4: k_attn_partial<D, 4><<<grid, block, 0, s>>>(p); break;
-    case 8: k_attn_partial<D, 8><<<grid, block, 0, s>>>(p); break;
+    case 1: k_attn_partial<D, 1, QM, LM><<<grid, block, 0, s>>>(p); break;
+    case 2: k_attn_partial<D, 2, QM, LM><<<grid, block, 0, s>>>(p); break;
+    case 4: k_attn_partial<D, 4, QM, LM><<<grid, block, 0, s>>>(p); break;
+    case 8: k_attn_partial<D, 8, QM, LM><<<grid, block, 0, s>>>(p); break;
     default: return set_error(BC_ERR_UNSUPPORTED, "attention: group size %d", p.n_heads / p.n_kv_heads);
   }
   return check_launch("k_attn_partial");
 }
 
+template <int D>
+int launch_partial_d(int q_mode, int list_mode, const AttnParams& p, hipStream_t s) {
+  if (q_mode == Q_PARTIAL) {
+    if (list_mode != L_DENSE) return set_error(BC_ERR_INVALID, "attention: q from partials needs the dense list");
+    return launch_partial_dql<D, Q_PARTIAL, L_DENSE>(p, s);
+  }
+  if (list_mode == L_IDX) return launch_partial_dql<D, Q_GLOBAL, L_IDX>(p, s);
+  return launch_partial_dql<D, Q_GLOBAL, L_DENSE>(p, s);
+}
+
 }  // namespace
 
-int launch_attn_partial(const AttnParams& p, hipStream_t s) {
-  if (p.head_dim == 128) return launch_partial_d<128>(p, s);
-  if (p.head_dim == 64) return launch_partial_d<64>(p, s);
+int launch_attn_partial(int q_mode, int list_mode, const AttnParams& p, hipStream_t s) {
+  if (list_mode == L_IDX && p.idx == nullptr) return set_error(BC_ERR_INVALID, "attention: NULL index list");
+  if (p.head_dim == 128) return launch_partial_d<128>(q_mode, list_mode, p, s);
+  if (p.head_dim == 64) return launch_partial_d<64>(q_mode, list_mode, p, s);
   return set_error(BC_ERR_UNSUPPORTED, "attention: head_dim %d", p.head_dim);
 }
 
@@ -420,11 +550,12 @@ extern "C" int bc_splitk_attn_partial(const uint16_t* q, const uint16_t* k_cache
        reinterpret_cast<uintptr_t>(v_cache)) & 15)
     return set_error(BC_ERR_INVALID, "bc_splitk_attn_partial: q/K/V must be 16-byte aligned");
   AttnParams p{};
-  p.q = q; p.k_cache = k_cache; p.v_cache = v_cache; p.n_cap = n_cap; p.idx = idx; p.n_sel = n_sel;
+  p.q = q; p.k_cache = const_cast<uint16_t*>(k_cache); p.v_cache = const_cast<uint16_t*>(v_cache);
+  p.n_cap = n_cap; p.idx = idx; p.n_sel = n_sel;
   p.n_heads = n_heads; p.n_kv_heads = n_kv_heads; p.head_dim = head_dim; p.n_splits = n_splits;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.m = m; p.l = l; p.o = o;
-  return launch_attn_partial(p, static_cast<hipStream_t>(stream));
+  return launch_attn_partial(Q_GLOBAL, idx ? L_IDX : L_DENSE, p, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int bc_splitk_reduce(const float* m, const float* l, const float* o, int n_heads, int n_splits,

@@ -62,6 +62,25 @@ __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
 // barrier on this chip; the helpers below use DPP (row operations at VALU
 // latency) and v_readlane instead.
 
+// The value of lane (lane ^ OFF), OFF in {8, 16, 32}, without LDS: DPP
+// row_ror:8 within 16-lane rows; gfx950's v_permlane16_swap / 32_swap, which
+// leave each lane its own value and its partner's in a row-dependent order.
+// Other offsets fall back to a shuffle.
+template <int OFF>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (OFF == 8) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(((threadIdx.x >> 4) & 1) ? r[0] : r[1]);
+  } else if constexpr (OFF == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+  } else {
+    return __shfl_xor(v, OFF, kWave);
+  }
+}
+
 // Integer sum over the 64 lanes of a wave; the result is wave-uniform.
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   v += dpp_u<0xB1>(v);     // xor 1
@@ -133,6 +152,23 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   __syncthreads();
   return ex;
 }
+
+// ------------------------------------------------------- split partials
+// Sum of the n_splits chunk partials of column c, in chunk order.
+__device__ __forceinline__ float chunk_sum(const float* partial, int n_splits, int d_out, int c) {
+  float v = 0.f;
+  int s = 0;
+  for (; s + 4 <= n_splits; s += 4) {
+    const float a0 = partial[size_t(s) * d_out + c];
+    const float a1 = partial[size_t(s + 1) * d_out + c];
+    const float a2 = partial[size_t(s + 2) * d_out + c];
+    const float a3 = partial[size_t(s + 3) * d_out + c];
+    v += a0; v += a1; v += a2; v += a3;
+  }
+  for (; s < n_splits; ++s) v += partial[size_t(s) * d_out + c];
+  return v;
+}
+
 
 // ------------------------------------------------------ block top-k select
 // Keys are staged in LDS when they fit (kTopkLdsBytes); larger inputs read
@@ -476,48 +512,63 @@ __device__ void block_topk(int n, int k, KeyFn key_fn, EmitFn emit, TopkSmem<NT,
 // ------------------------------------- 15-bit keys in registers, two passes
 // Exact top-k of n keys below 2^15 held in registers by NT threads: thread t
 // owns positions [t*P, t*P + P) (positions >= n are ignored), so a thread's
-// keys are in position order.  Pass 1 histograms the top 11 key bits (2048
-// bins, LDS atomics; bf16 magnitudes spread over many bins, so the atomics
-// rarely collide) and a block scan taken from the largest bin down finds the
-// bin holding the k-th largest key; pass 2 histograms the low 4 bits of the
-// keys in that bin.  That fixes the threshold key thr and the number `need`
-// of keys equal to thr that are kept (the lowest positions).  One block scan
-// of (ties, greater) counts per thread then gives every kept position its
-// rank: emit(rank, e) for the thread's e-th key, ranks ascending with
-// position.  Requires 1 <= k <= n <= NT * PMAX and n < 65536 (the scan
-// packs two 16-bit counts).  Contains __syncthreads(); the caller
-// synchronises before reading what emit wrote.
-template <int NT>
+// keys are in position order.  Pass 1 histograms the top 15-SHIFT key bits
+// (LDS atomics) and a block scan taken from the largest bin down finds the
+// bin holding the k-th largest key; pass 2 histograms the low SHIFT bits of
+// the keys in that bin.  That fixes the threshold key thr and the number
+// `need` of keys equal to thr that are kept (the lowest positions).  One
+// block scan of (ties, greater) counts per thread gives each thread the rank
+// of its first kept key; ranks within the thread come from popcounts of the
+// kept-key bit mask, so no thread walks its keys serially.  emit(rank, e) is
+// called for the thread's e-th key when it is kept and its rank is in
+// [r0, r1), or for every kept key when `all`.  Requires 1 <= k <= n <=
+// NT * PMAX, PMAX <= 32, n < 65536 (the scan packs two 16-bit counts).
+// Contains __syncthreads(); the caller synchronises before reading what emit
+// wrote.
+template <int NT, int SHIFT>
 struct Topk2Smem {
-  uint32_t hist[2048];
-  uint32_t hist2[16];
+  static constexpr int NB = 32768 >> SHIFT;
+  uint32_t hist[NB];
+  uint32_t hist2[1 << SHIFT];
   uint32_t wtot[NT / kWave];
   uint32_t b1, above1;
 };
 
-template <int NT, int PMAX, typename EmitFn>
-__device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int k, EmitFn emit, Topk2Smem<NT>& sm) {
-  static_assert(2048 % NT == 0 || NT % 2048 == 0, "bins per thread");
+template <int NT, int SHIFT, int PMAX, typename EmitFn>
+__device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int k, int r0, int r1, bool all,
+                                 EmitFn emit, Topk2Smem<NT, SHIFT>& sm) {
+  static_assert(PMAX <= 32, "bit masks are 32 bits");
+  constexpr int NB = Topk2Smem<NT, SHIFT>::NB;
+  constexpr int NB2 = 1 << SHIFT;
+  static_assert(NB % (4 * NT) == 0, "whole uint4 of bins per thread");
   constexpr int NW = NT / kWave;
-  constexpr int BPT = 2048 / NT;  // bins per thread
+  constexpr int BPT = NB / NT;  // bins per thread
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nv = max(0, min(P, n - tid * P));
-  for (int i = tid; i < 2048; i += NT) sm.hist[i] = 0;
-  if (tid < 16) sm.hist2[tid] = 0;
+  {
+    uint4* h4 = reinterpret_cast<uint4*>(sm.hist);
+#pragma unroll
+    for (int i = 0; i < BPT / 4; ++i) h4[tid + i * NT] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (tid < NB2) sm.hist2[tid] = 0;
   __syncthreads();
 #pragma unroll
   for (int e = 0; e < PMAX; ++e)
-    if (e < nv) atomicAdd(&sm.hist[key[e] >> 4], 1u);
+    if (e < nv) atomicAdd(&sm.hist[key[e] >> SHIFT], 1u);
   __syncthreads();
-  // thread t owns bins [b0, b0 + BPT), b0 = 2048 - BPT (t + 1): the largest
+  // thread t owns bins [b0, b0 + BPT), b0 = NB - BPT (t + 1): the largest
   // bins go to thread 0, so the prefix over threads counts larger keys
-  const int b0 = 2048 - BPT * (tid + 1);
+  const int b0 = NB - BPT * (tid + 1);
   uint32_t bins[BPT];
   uint32_t local = 0;
+  {
+    const uint4* hb = reinterpret_cast<const uint4*>(sm.hist + b0);
 #pragma unroll
-  for (int j = 0; j < BPT; ++j) {
-    bins[j] = sm.hist[b0 + j];
-    local += bins[j];
+    for (int q = 0; q < BPT / 4; ++q) {
+      const uint4 c = hb[q];
+      bins[4 * q] = c.x; bins[4 * q + 1] = c.y; bins[4 * q + 2] = c.z; bins[4 * q + 3] = c.w;
+      local += (c.x + c.y) + (c.z + c.w);
+    }
   }
   const uint32_t winc = wave_scan_dpp(local);
   if (lane == kWave - 1) sm.wtot[w] = winc;
@@ -541,23 +592,29 @@ __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int 
   const uint32_t b1 = sm.b1, k2 = ku - sm.above1;
 #pragma unroll
   for (int e = 0; e < PMAX; ++e)
-    if (e < nv && (key[e] >> 4) == b1) atomicAdd(&sm.hist2[key[e] & 15u], 1u);
+    if (e < nv && (key[e] >> SHIFT) == b1) atomicAdd(&sm.hist2[key[e] & uint32_t(NB2 - 1)], 1u);
   __syncthreads();
-  uint32_t run = 0, b2 = 0, above2 = 0;
-  bool found = false;
+  uint32_t h2[NB2];
 #pragma unroll
-  for (int j = 15; j >= 0; --j) {
-    const uint32_t c = sm.hist2[j];
-    if (!found && run + c >= k2) { b2 = uint32_t(j); above2 = run; found = true; }
-    run += c;
+  for (int j = 0; j < NB2; ++j) h2[j] = sm.hist2[j];
+  uint32_t run = 0, b2 = 0, above2 = 0;
+#pragma unroll
+  for (int j = NB2 - 1; j >= 0; --j) {
+    const bool hit = run < k2 && k2 <= run + h2[j];
+    b2 = hit ? uint32_t(j) : b2;
+    above2 = hit ? run : above2;
+    run += h2[j];
   }
-  const uint32_t thr = (b1 << 4) | b2, need = k2 - above2;
-  uint32_t gt = 0, eq = 0;
+  const uint32_t thr = (b1 << SHIFT) | b2, need = k2 - above2;
+  uint32_t gtm = 0, eqm = 0;
 #pragma unroll
   for (int e = 0; e < PMAX; ++e) {
-    gt += (e < nv && key[e] > thr) ? 1u : 0u;
-    eq += (e < nv && key[e] == thr) ? 1u : 0u;
+    if (e < nv) {
+      gtm |= (key[e] > thr ? 1u : 0u) << e;
+      eqm |= (key[e] == thr ? 1u : 0u) << e;
+    }
   }
+  const uint32_t gt = uint32_t(__popc(gtm)), eq = uint32_t(__popc(eqm));
   // exclusive block scan of (eq << 16 | gt); wtot is free again (its last
   // readers passed two barriers ago)
   const uint32_t v = (eq << 16) | gt;
@@ -568,16 +625,29 @@ __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int 
 #pragma unroll
   for (int ww = 0; ww < NW; ++ww) bf += ww < w ? sm.wtot[ww] : 0u;
   const uint32_t gt_before = bf & 0xFFFFu, eq_before = bf >> 16;
-  uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
-  uint32_t tie = eq_before;
+  const uint32_t ties_before = eq_before < need ? eq_before : need;
+  const uint32_t ties_here = (eq_before + eq < need ? eq_before + eq : need) - ties_before;
+  // keep the lowest ties_here of the thread's ties
+  uint32_t tie_keep = eqm;
+  if (ties_here < eq) {
+    tie_keep = 0;
+    uint32_t m = eqm;
+    for (uint32_t i = 0; i < ties_here; ++i) {
+      const uint32_t low = m & (~m + 1u);
+      tie_keep |= low;
+      m ^= low;
+    }
+  }
+  const uint32_t take = gtm | tie_keep;
+  const uint32_t pos0 = gt_before + ties_before;
+  const uint32_t cnt = gt + ties_here;
+  if (all || (pos0 < uint32_t(r1) && pos0 + cnt > uint32_t(r0))) {
 #pragma unroll
-  for (int e = 0; e < PMAX; ++e) {
-    if (e >= nv) continue;
-    if (key[e] > thr) {
-      emit(int(pos++), e);
-    } else if (key[e] == thr) {
-      if (tie < need) emit(int(pos++), e);
-      ++tie;
+    for (int e = 0; e < PMAX; ++e) {
+      if ((take >> e) & 1u) {
+        const uint32_t pos = pos0 + uint32_t(__popc(take & ((1u << e) - 1u)));
+        if (all || (pos >= uint32_t(r0) && pos < uint32_t(r1))) emit(int(pos), e);
+      }
     }
   }
 }

@@ -36,6 +36,7 @@ namespace {
 constexpr int kSlots = kGemvThreads / 16;   // 32 row slots of 16 lanes
 constexpr int kRing = 8;                    // rows in flight per slot
 constexpr int kNW = kGemvThreads / kWave;   // 8 waves
+constexpr int kTopkShift = 3;               // first selection pass: 4096 bins
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -48,7 +49,7 @@ struct GemvSmem {
     float red[kSlots][kGemvTile];  // per-slot sums (after the row loop)
   };
   float red2[4][kGemvTile];
-  Topk2Smem<kGemvThreads> tk;
+  Topk2Smem<kGemvThreads, kTopkShift> tk;
   float part[kNW];
   float amax_v[kNW];
   int32_t amax_i[kNW];
@@ -181,7 +182,8 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
         }
         if (idx_out && pos < p.k) idx_out[pos] = c;
       };
-      block_topk_2pass<kGemvThreads, PMAX>(key, P, p.d_in, p.k, emit, sm.tk);
+      block_topk_2pass<kGemvThreads, kTopkShift, PMAX>(key, P, p.d_in, p.k, r0, r1, idx_out != nullptr, emit,
+                                                       sm.tk);
     }
   }
   __syncthreads();
@@ -278,21 +280,6 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
 }
 
 // ------------------------------------------------------------------ finish
-// Sum of the n_splits chunk partials of column c, in chunk order.
-__device__ __forceinline__ float chunk_sum(const float* partial, int n_splits, int d_out, int c) {
-  float v = 0.f;
-  int s = 0;
-  for (; s + 4 <= n_splits; s += 4) {
-    const float a0 = partial[size_t(s) * d_out + c];
-    const float a1 = partial[size_t(s + 1) * d_out + c];
-    const float a2 = partial[size_t(s + 2) * d_out + c];
-    const float a3 = partial[size_t(s + 3) * d_out + c];
-    v += a0; v += a1; v += a2; v += a3;
-  }
-  for (; s < n_splits; ++s) v += partial[size_t(s) * d_out + c];
-  return v;
-}
-
 __global__ __launch_bounds__(256) void k_finish_bf16(const FinishParams p) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c < p.d_out) p.y[c] = f32_to_bf16(chunk_sum(p.partial, p.n_splits, p.d_out, c));
@@ -349,19 +336,6 @@ __global__ __launch_bounds__(256) void k_finish_argmax(const FinishParams p) {
   }
 }
 
-// Rotary (rotate-half) cos/sin of pair i at position pos.  The angle
-// pos * theta^(-2i/D) is formed in double and reduced by 2*pi in double
-// (two-part constant), so single-precision sincos of the reduced angle is
-// accurate to float rounding at any position.
-__device__ __forceinline__ void rope_cs(int pos, double log2_theta, int i, int D, float* cs, float* sn) {
-  const double inv_freq = exp2(-2.0 * double(i) / double(D) * log2_theta);
-  const double ang = double(pos) * inv_freq;
-  const double kq = rint(ang * 0.15915494309189533577);
-  double r = fma(-kq, 6.28318530717958623200, ang);
-  r = fma(-kq, 2.44929359829470635445e-16, r);
-  sincosf(float(r), sn, cs);
-}
-
 // One work-group per head of the q | k | v output: thread i owns the pair
 // (i, i + D/2).  q -> q_out; k, v -> cache slot pos; then the (min, max)
 // summary of block pos/16 is recomputed for the key heads.
@@ -374,8 +348,7 @@ __global__ __launch_bounds__(64) void k_finish_qkv(const FinishParams p) {
     float a = chunk_sum(p.partial, p.n_splits, p.d_out, base + i);
     float b = chunk_sum(p.partial, p.n_splits, p.d_out, base + i + half);
     if (head < qh + kvh) {
-      float cs, sn;
-      rope_cs(p.pos, p.log2_theta, i, D, &cs, &sn);
+      const float cs = p.rope.c[i], sn = p.rope.s[i];
       const float ra = a * cs - b * sn;
       const float rb = b * cs + a * sn;
       a = ra;

@@ -17,6 +17,16 @@ int check_launch(const char* what);
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Rotary cos/sin of the current position, pair i = (i, i + head_dim/2),
+// computed on the host in double (angle pos * theta^(-2i/head_dim)) and
+// rounded to float; passed to the kernels by value.
+constexpr int kRopeMaxPairs = 64;   // head_dim <= 128
+struct RopeTable {
+  float c[kRopeMaxPairs];
+  float s[kRopeMaxPairs];
+};
+void rope_table(int pos, double theta, int head_dim, RopeTable* t);
+
 constexpr int kGemvTile = 128;      // output columns per work-group (16 lanes x 8)
 constexpr int kGemvThreads = 512;   // 32 row slots of 16 lanes
 constexpr int kGemvMaxRows = 4096;  // rows (list positions) per work-group
@@ -33,7 +43,7 @@ enum GemvIn : int { IN_LIST = 0, IN_NORM = 1, IN_SEL = 2 };
 // What the main kernel stores: fp32 partials per chunk of rows, or (one
 // chunk) bf16 y, the SwiGLU of a gate|up tile, or fp32 y + per-tile argmax.
 enum GemvOut : int { OUT_PARTIAL = 0, OUT_BF16 = 1, OUT_SWIGLU = 2, OUT_ARGMAX = 3 };
-enum FinishKind : int { FIN_BF16 = 0, FIN_QKV = 1, FIN_RESID = 2, FIN_SWIGLU = 3, FIN_ARGMAX = 4 };
+enum FinishKind : int { FIN_BF16 = 0, FIN_QKV = 1, FIN_RESID = 2, FIN_SWIGLU = 3, FIN_ARGMAX = 4, FIN_NONE = 5 };
 
 struct GemvPlan {
   int n_tiles;
@@ -78,7 +88,7 @@ struct FinishParams {
   uint16_t* v_cache;
   uint16_t* summary;
   int n_heads, n_kv_heads, head_dim, n_cap, pos;
-  double log2_theta;
+  RopeTable rope;
   // FIN_SWIGLU
   int d_ff;
   // FIN_ARGMAX
@@ -91,10 +101,20 @@ int launch_finish(int kind, const FinishParams& p, hipStream_t s);
 int finish_argmax_groups(int d_out);
 int launch_argmax_finish(const float* tile_max, const int32_t* tile_arg, int n_tiles, int32_t* token, hipStream_t s);
 
+// Where the partial pass gets q and its list of tokens.
+//   Q_GLOBAL   q bf16 [n_heads][head_dim] is given;
+//   Q_PARTIAL  q, k, v of the current token come from the qkv GEMV chunk
+//              partials (rotary at pos, bf16 rounding); the work-group whose
+//              range holds list position pos (dense list, pos = n_sel - 1)
+//              appends k, v at cache slot pos and attends to them from LDS.
+//   L_DENSE    tokens 0..n_sel-1;  L_IDX  an index list [n_kv_heads][n_sel].
+enum AttnQ : int { Q_GLOBAL = 0, Q_PARTIAL = 1 };
+enum AttnList : int { L_DENSE = 0, L_IDX = 1 };
+
 struct AttnParams {
   const uint16_t* q;
-  const uint16_t* k_cache;
-  const uint16_t* v_cache;
+  uint16_t* k_cache;      // written only by the appending work-group
+  uint16_t* v_cache;
   int n_cap;
   const int32_t* idx;
   int n_sel, n_heads, n_kv_heads, head_dim, n_splits;
@@ -102,8 +122,15 @@ struct AttnParams {
   float* m;
   float* l;
   float* o;
+  // Q_PARTIAL
+  const float* qkv_partial;   // [qkv_splits][qkv_out]
+  int qkv_splits, qkv_out;
+  int pos;
+  RopeTable rope;
+  uint16_t* q_out;            // optional bf16 copy of q
+  uint16_t* summary;          // optional: (min, max) of block pos/16 refreshed by the appending work-group
 };
-int launch_attn_partial(const AttnParams& p, hipStream_t s);
+int launch_attn_partial(int q_mode, int list_mode, const AttnParams& p, hipStream_t s);
 
 struct ReduceParams {
   const float* m;

@@ -45,6 +45,20 @@ int check_launch(const char* what) {
 bool valid_head_dim(int hd) { return hd == 64 || hd == 128; }
 bool valid_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
+void rope_table(int pos, double theta, int head_dim, RopeTable* t) {
+  const int half = head_dim / 2;
+  for (int i = 0; i < kRopeMaxPairs; ++i) {
+    if (i < half) {
+      const double ang = double(pos) * pow(theta, -2.0 * double(i) / double(head_dim));
+      t->c[i] = float(cos(ang));
+      t->s[i] = float(sin(ang));
+    } else {
+      t->c[i] = 1.0f;
+      t->s[i] = 0.0f;
+    }
+  }
+}
+
 namespace {
 
 __global__ void k_fill_zero(uint4* p, size_t n16, uint8_t* tail, size_t ntail) {
@@ -225,11 +239,13 @@ struct ProjIn {
 
 // One projection: main kernel and, with several chunks, its finish.  The
 // gate|up GEMV (FIN_SWIGLU) runs as one chunk per tile when it fits, with
-// the SwiGLU in the main kernel's epilogue.
+// the SwiGLU in the main kernel's epilogue.  FIN_NONE leaves the chunk
+// partials for the next kernel (their count in *n_splits).
 int run_gemv(const uint16_t* wt, int d_in, int d_out, int k, const ProjIn& in, float* partial, int fin_kind,
-             FinishParams f, hipStream_t s) {
+             FinishParams f, hipStream_t s, int* n_splits = nullptr) {
   const bool swiglu = fin_kind == FIN_SWIGLU;
   const GemvPlan pl = plan_gemv(d_out, k, swiglu);
+  if (n_splits) *n_splits = pl.n_splits;
   GemvParams p{};
   p.wt = wt; p.tiled = 1; p.d_in = d_in; p.d_out = d_out; p.k = k;
   if (in.mode == IN_NORM) {
@@ -245,7 +261,7 @@ int run_gemv(const uint16_t* wt, int d_in, int d_out, int k, const ProjIn& in, f
     return launch_gemv(in.mode, OUT_SWIGLU, p, s);
   }
   int rc = launch_gemv(in.mode, OUT_PARTIAL, p, s);
-  if (rc != BC_OK) return rc;
+  if (rc != BC_OK || fin_kind == FIN_NONE) return rc;
   f.partial = partial;
   f.n_splits = pl.n_splits;
   f.d_out = d_out;
@@ -338,36 +354,50 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
   uint16_t* a = at<uint16_t>(ws, L.a);
   uint16_t* hff = at<uint16_t>(ws, L.hff);
 
-  // x1 = RMSNorm(h), S1 (GEMV prologue); q, k, v; rotary; append; summary
-  {
-    const ProjIn in{IN_NORM, hidden, ly->g_attn, eps, at<uint16_t>(ws, L.x1), idx_qkv};
+  // x1 = RMSNorm(h), S1 (GEMV prologue); q, k, v.  With a scored KV list
+  // the finish kernel applies the rotary, appends k, v and refreshes the
+  // block summary before the scoring; with the dense list the attention
+  // kernel does all of that itself from the chunk partials.
+  const ProjIn qkv_in{IN_NORM, hidden, ly->g_attn, eps, at<uint16_t>(ws, L.x1), idx_qkv};
+  RopeTable rope;
+  rope_table(pos, st->rope_theta, hd, &rope);
+  int qkv_splits = 0;
+  if (kv_sparse) {
     FinishParams f{};
     f.q_out = at<uint16_t>(ws, L.q); f.k_cache = ly->k_cache; f.v_cache = ly->v_cache; f.summary = ly->kv_summary;
     f.n_heads = H; f.n_kv_heads = Hkv; f.head_dim = hd; f.n_cap = ly->n_cap; f.pos = pos;
-    f.log2_theta = log2(st->rope_theta);
-    if ((rc = run_gemv(ly->w_qkv, m.d, qkv_out, k_d, in, partial, FIN_QKV, f, s)) != BC_OK) return rc;
-  }
+    f.rope = rope;
+    if ((rc = run_gemv(ly->w_qkv, m.d, qkv_out, k_d, qkv_in, partial, FIN_QKV, f, s)) != BC_OK) return rc;
 
-  // KV selection
-  if (kv_sparse) {
     KvSelectParams p{};
     p.q = at<uint16_t>(ws, L.q); p.summary = ly->kv_summary; p.nb_cap = ly->n_cap / 16; p.n_ctx = st->n_ctx;
     p.n_heads = H; p.n_kv_heads = Hkv; p.head_dim = hd; p.bud = bud;
     p.scores = at<float>(ws, L.scores); p.idx_out = at<int32_t>(ws, L.idx_kv);
     if ((rc = launch_kv_score_select(p, s)) != BC_OK) return rc;
+  } else {
+    if ((rc = run_gemv(ly->w_qkv, m.d, qkv_out, k_d, qkv_in, partial, FIN_NONE, FinishParams{}, s, &qkv_splits)) !=
+        BC_OK)
+      return rc;
   }
 
   // attention
   {
     AttnParams p{};
-    p.q = at<uint16_t>(ws, L.q); p.k_cache = ly->k_cache; p.v_cache = ly->v_cache; p.n_cap = ly->n_cap;
-    p.idx = kv_sparse ? at<int32_t>(ws, L.idx_kv) : nullptr; p.n_sel = n_sel;
-    p.n_heads = H; p.n_kv_heads = Hkv; p.head_dim = hd; p.n_splits = n_splits;
+    p.k_cache = ly->k_cache; p.v_cache = ly->v_cache; p.n_cap = ly->n_cap;
+    p.n_sel = n_sel; p.n_heads = H; p.n_kv_heads = Hkv; p.head_dim = hd; p.n_splits = n_splits;
     p.scale_log2 = float(1.4426950408889634 / sqrt(double(hd)));
     p.m = at<float>(ws, L.m); p.l = at<float>(ws, L.l); p.o = at<float>(ws, L.o);
-    if ((rc = launch_attn_partial(p, s)) != BC_OK) return rc;
     ReduceParams r{};
     r.m = p.m; r.l = p.l; r.o = p.o; r.n_heads = H; r.n_splits = n_splits; r.head_dim = hd; r.out = a;
+    if (kv_sparse) {
+      p.q = at<uint16_t>(ws, L.q);
+      p.idx = at<int32_t>(ws, L.idx_kv);
+      if ((rc = launch_attn_partial(Q_GLOBAL, L_IDX, p, s)) != BC_OK) return rc;
+    } else {
+      p.qkv_partial = partial; p.qkv_splits = qkv_splits; p.qkv_out = qkv_out; p.pos = pos;
+      p.rope = rope; p.q_out = st->taps ? at<uint16_t>(ws, L.q) : nullptr; p.summary = ly->kv_summary;
+      if ((rc = launch_attn_partial(Q_PARTIAL, L_DENSE, p, s)) != BC_OK) return rc;
+    }
     if ((rc = launch_attn_reduce(r, s)) != BC_OK) return rc;
   }
 

@@ -402,7 +402,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--contexts", default="2048,8192,32768,131072")
-    ap.add_argument("--cells", default="default", help="default | dense | none")
+    ap.add_argument("--cells", default="default", help="default | dense | none | r_p:r_kv:n,...")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", action="store_true", help="only the per-kernel bandwidth table")
     ap.add_argument("--calib-copy", type=int, default=0,
@@ -452,6 +452,10 @@ def main():
         cells += [(rp, rkv, n) for rp, rkv in ((0.7, 0.3), (0.5, 0.3), (0.5, 0.5)) for n in contexts]
     elif args.cells == "none":
         cells = [(1.0, 1.0, head_n)]
+    elif args.cells != "dense":
+        # explicit list "r_p:r_kv:n,..." (the dense cell at the largest context is always kept)
+        cells = [(1.0, 1.0, head_n)] + [(float(a), float(b), int(c)) for a, b, c in
+                                         (t.split(":") for t in args.cells.split(","))]
 
     results = []
     headline = None

@@ -86,6 +86,11 @@ LAYER_CASES = [
     ("tiny-both", gen.TINY, 2048, 2048, 0.5, 0.3, 4, 128, 8),
     ("tiny-ragged-ctx", gen.TINY, 2064, 2051, 0.7, 0.3, 4, 128, 5),
     ("tiny-first-token", gen.TINY, 64, 1, 0.5, 1.0, 4, 128, 1),
+    # dense list, few tokens: the current token (attended from LDS by the
+    # work-group that appends it) carries a large share of the weights; the
+    # last split holds only that token in the second case
+    ("tiny-short-ctx", gen.TINY, 64, 17, 1.0, 1.0, 4, 128, 3),
+    ("tiny-split-of-one", gen.TINY, 64, 13, 1.0, 1.0, 4, 128, 4),
     ("8b-2k-dense", gen.LLAMA8B, 2048, 2048, 1.0, 1.0, 4, 1024, 0),
     ("8b-2k-both-0.5-0.3", gen.LLAMA8B, 2048, 2048, 0.5, 0.3, 4, 1024, 0),
     ("8b-8k-both-0.7-0.3", gen.LLAMA8B, 8192, 8192, 0.7, 0.3, 4, 1024, 0),
@@ -110,12 +115,36 @@ def test_decode_layer_teacher_forced(name, dims, n_cap, n, r_p, r_kv, sinks, win
     assert np.array_equal(got["summ"], so)
 
 
+def _bf16_ulp(x):
+    """One unit in the last place of bf16 values of magnitude |x| (8
+    significant bits: 2^(e-7) for |x| in [2^e, 2^(e+1)))."""
+    a = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 2.0 ** -126)))
+    return 2.0 ** (np.maximum(e, -126) - 7)
+
+
 @pytest.mark.parametrize("dims,n_cap,n", [(gen.TINY, 2048, 2048), (gen.LLAMA8B, 2048, 2048)], ids=["tiny", "8b-2k"])
 def test_dense_layer_end_to_end(dims, n_cap, n):
+    """Without teacher forcing the GPU and the oracle round their stored bf16
+    intermediates independently, so a stored value may differ by one bf16
+    ulp (the stage tests above bound each stage given its inputs).  Two such
+    differences reach h_out: one ulp of the residual h_mid, and one ulp of
+    each SwiGLU output f_i carried through W_down.  The elementwise bound adds
+    ulp(h_mid_o) and 4 standard deviations of that propagated noise,
+    4 * sqrt(sum_i (W_down[i, o] * ulp(f_i))^2), to 2e-3 + 1e-2|ref|; the
+    relative L2 error of the whole vector must stay below 1e-2."""
     W, K, V, h, summ, got, S = _run_layer(dims, n_cap, n, 1.0, 1.0, 4, 1024, 0, seed=10)
     ref = oracle.decode_layer(h, W, K.copy(), V.copy(), summ.copy(), n, dims, 1.0, 1.0, 4, 1024, S)
-    rel = assert_close_bf16(got["h_out"], oracle.bf16_to_f64(ref["h_out"]), "h_out")
-    assert rel < 1e-2
+    g = oracle.bf16_to_f64(got["h_out"]).reshape(-1)
+    r = oracle.bf16_to_f64(ref["h_out"]).reshape(-1)
+    wd = oracle.bf16_to_f64(W["down"]).astype(np.float32)
+    uf = _bf16_ulp(oracle.bf16_to_f64(ref["hff"])).astype(np.float32).reshape(-1)
+    noise = np.sqrt((wd * wd).T.astype(np.float64) @ (uf.astype(np.float64) ** 2))
+    tol = 2e-3 + 1e-2 * np.abs(r) + _bf16_ulp(oracle.bf16_to_f64(ref["h_mid"])).reshape(-1) + 4 * noise
+    err = np.abs(g - r)
+    rel = np.linalg.norm(g - r) / np.linalg.norm(r)
+    assert (err <= tol).all(), f"h_out: {(err > tol).sum()} of {err.size} outside; max err {err.max():.3g}"
+    assert rel < 1e-2, f"h_out: rel-L2 {rel:.3g}"
 
 
 def test_lm_head_tiny():
