@@ -54,7 +54,11 @@ struct AttnSmem {
   uint16_t q[G][D];
   uint16_t knew[D];   // the current token's k, v (appending work-group)
   uint16_t vnew[D];
-  alignas(16) float st_o[NST * OSTRIDE];
+  int32_t blk[kAttnMaxRanks];   // L_SCORES: candidate of each block rank this split reads
+  union {
+    alignas(16) float st_o[NST * OSTRIDE];   // row-group states (after the main loop)
+    Topk32Smem<kAttnThreads> tk;             // block selection (prologue)
+  };
   alignas(16) float st_m[G][NST];
   alignas(16) float st_mx[G][NST];
   alignas(16) float st_l[G][NST];
@@ -233,6 +237,27 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
     if (base < hi_main) attn_load<D>(Kg, Vg, nullptr, base, lo, hi_main, sub, rw);
   }
 
+  // scored list: the block ranks [r_lo, r_hi) this split's slice reads
+  int r_lo = 0, r_hi = 0;
+  if constexpr (LM == L_SCORES) {
+    const int S0 = p.bud.sinks, KB = p.bud.k_blk;
+    if (KB > 0 && hi > S0 && lo < S0 + 16 * KB) {
+      r_lo = lo > S0 ? (lo - S0) / 16 : 0;
+      r_hi = min(KB, (hi - S0 + 15) / 16);
+    }
+    if (r_lo < r_hi) {   // uniform over the work-group
+      const int n = p.bud.n_cand;
+      const int P = (n + kAttnThreads - 1) / kAttnThreads;
+      const float* sc = p.scores + size_t(g) * p.scores_stride + size_t(tid) * P;
+      uint32_t key[32];
+#pragma unroll
+      for (int e = 0; e < 32; ++e) key[e] = (e < P && tid * P + e < n) ? float_order_key(sc[e]) : 0u;
+      const int rl = r_lo;
+      auto emit = [&](int rank, int e) { sm.blk[rank - rl] = tid * P + e; };
+      block_topk32<kAttnThreads, 32>(key, P, n, KB, r_lo, r_hi, false, emit, sm.tk);
+    }
+  }
+
   if constexpr (QM == Q_GLOBAL) {
     for (int i = tid; i < G * D / 8; i += kAttnThreads)
       reinterpret_cast<uint4*>(&sm.q[0][0])[i] = reinterpret_cast<const uint4*>(p.q + size_t(g) * G * D)[i];
@@ -294,10 +319,30 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
       }
     }
   } else {
-    const int32_t* idxg = p.idx + size_t(g) * p.n_sel;
+    const int32_t* idxg = LM == L_IDX ? p.idx + size_t(g) * p.n_sel : nullptr;
+    int32_t* idx_out = LM == L_SCORES && p.idx_out ? p.idx_out + size_t(g) * p.n_sel : nullptr;
     for (int c0 = lo; c0 < hi; c0 += kIdxChunk) {
       const int c1 = min(hi, c0 + kIdxChunk);
-      for (int i = tid; i < c1 - c0; i += kAttnThreads) sm.idx[i] = idxg[c0 + i];
+      for (int i = tid; i < c1 - c0; i += kAttnThreads) {
+        int t;
+        if constexpr (LM == L_IDX) {
+          t = idxg[c0 + i];
+        } else {
+          // list position -> token: sinks, then 16 tokens per kept block
+          // (ascending block order), then the window
+          const int pos = c0 + i, S0 = p.bud.sinks, KB = p.bud.k_blk;
+          if (pos < S0) {
+            t = pos;
+          } else if (pos < S0 + 16 * KB) {
+            const int q = pos - S0;
+            t = 16 * (p.bud.b_lo + sm.blk[(q >> 4) - r_lo]) + (q & 15);
+          } else {
+            t = p.n_ctx - p.bud.window + (pos - S0 - 16 * KB);
+          }
+          if (idx_out) idx_out[pos] = t;
+        }
+        sm.idx[i] = t;
+      }
       __syncthreads();
       base = c0 + w * TPI;
       for (; base + TPI <= c1; base += STEP) {
@@ -500,13 +545,26 @@ int launch_partial_d(int q_mode, int list_mode, const AttnParams& p, hipStream_t
     return launch_partial_dql<D, Q_PARTIAL, L_DENSE>(p, s);
   }
   if (list_mode == L_IDX) return launch_partial_dql<D, Q_GLOBAL, L_IDX>(p, s);
+  if (list_mode == L_SCORES) return launch_partial_dql<D, Q_GLOBAL, L_SCORES>(p, s);
   return launch_partial_dql<D, Q_GLOBAL, L_DENSE>(p, s);
 }
 
 }  // namespace
 
+// Largest number of block ranks a split of a scored list reads.
+static int scored_ranks_per_split(int n_sel, int n_splits) {
+  const int cn = (n_sel + n_splits - 1) / n_splits;
+  return cn / 16 + 2;
+}
+
+bool attn_scored_list_ok(const bc_kv_budget_info& bud, int n_splits) {
+  return bud.n_cand <= kAttnMaxCand && scored_ranks_per_split(bud.t_sel, n_splits) <= kAttnMaxRanks;
+}
+
 int launch_attn_partial(int q_mode, int list_mode, const AttnParams& p, hipStream_t s) {
   if (list_mode == L_IDX && p.idx == nullptr) return set_error(BC_ERR_INVALID, "attention: NULL index list");
+  if (list_mode == L_SCORES && (!p.scores || !attn_scored_list_ok(p.bud, p.n_splits) || p.n_sel != p.bud.t_sel))
+    return set_error(BC_ERR_INVALID, "attention: scored list out of range");
   if (p.head_dim == 128) return launch_partial_d<128>(q_mode, list_mode, p, s);
   if (p.head_dim == 64) return launch_partial_d<64>(q_mode, list_mode, p, s);
   return set_error(BC_ERR_UNSUPPORTED, "attention: head_dim %d", p.head_dim);

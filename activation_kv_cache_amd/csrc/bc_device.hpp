@@ -652,4 +652,241 @@ __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int 
   }
 }
 
+// --------------------------------------- 32-bit keys in registers, adaptive
+// Exact top-k of n 32-bit keys held in registers by NT threads, thread t
+// owning positions [t*P, t*P + P) (positions >= n ignored); ties go to the
+// lower position.  Order-preserving keys of fp32 scores crowd into a few
+// exponents, so the first histogram is taken over the keys' own range:
+// bins (key - min) >> shift, 2048 of them (LDS atomics rarely collide then).
+// Later passes resolve the chosen bin 13 bits at a time (8192 bins) until
+// the threshold key thr is exact; the number `need` of keys equal to thr
+// that are kept follows.  The ranks come from one block scan of (ties,
+// greater) and per-thread popcounts, as in block_topk_2pass; emit(rank, e)
+// for kept keys whose rank is in [r0, r1), or every kept key when `all`.
+// Requires 1 <= k <= n <= NT * PMAX, PMAX <= 32, n < 65536.  Contains
+// __syncthreads(); the caller synchronises before reading what emit wrote.
+template <int NT>
+struct Topk32Smem {
+  static constexpr int kCandCap = 256;   // keys of the chosen bin ranked by brute force
+  uint32_t hist[8192];
+  uint32_t cand[kCandCap];
+  uint32_t wlo[NT / kWave];
+  uint32_t whi[NT / kWave];
+  uint32_t sel_bin, sel_above;
+};
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u<0xB1>(v));
+  v = min(v, dpp_u<0x4E>(v));
+  v = min(v, dpp_u<0x141>(v));
+  v = min(v, dpp_u<0x140>(v));
+  const uint32_t a = uint32_t(__builtin_amdgcn_readlane(int(v), 0)), b = uint32_t(__builtin_amdgcn_readlane(int(v), 16));
+  const uint32_t c = uint32_t(__builtin_amdgcn_readlane(int(v), 32)), d = uint32_t(__builtin_amdgcn_readlane(int(v), 48));
+  return min(min(a, b), min(c, d));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<0xB1>(v));
+  v = max(v, dpp_u<0x4E>(v));
+  v = max(v, dpp_u<0x141>(v));
+  v = max(v, dpp_u<0x140>(v));
+  const uint32_t a = uint32_t(__builtin_amdgcn_readlane(int(v), 0)), b = uint32_t(__builtin_amdgcn_readlane(int(v), 16));
+  const uint32_t c = uint32_t(__builtin_amdgcn_readlane(int(v), 32)), d = uint32_t(__builtin_amdgcn_readlane(int(v), 48));
+  return max(max(a, b), max(c, d));
+}
+
+// One histogram pass: bins hist[0..NB) hold counts of the keys in range;
+// finds the bin holding the k_rem-th largest of them (bins taken from the
+// top) and stores it with the count above it in sm.sel_bin / sm.sel_above.
+template <int NT, int NB>
+__device__ __forceinline__ void topk32_pick_bin(uint32_t k_rem, Topk32Smem<NT>& sm) {
+  constexpr int NW = NT / kWave;
+  constexpr int BPT = NB / NT;
+  static_assert(BPT >= 1 && NB % NT == 0, "bins per thread");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int b0 = NB - BPT * (tid + 1);
+  uint32_t bins[BPT];
+  uint32_t local = 0;
+  if constexpr (BPT % 4 == 0) {
+    // neighbouring threads' ranges are BPT words apart: read the 16-byte
+    // pieces in a thread-rotated order so the lanes spread over the banks
+    constexpr int NQ = BPT / 4;
+    const uint4* hb = reinterpret_cast<const uint4*>(sm.hist + b0);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int jj = (j + tid) % NQ;
+      const uint4 c = hb[jj];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        if (q == jj) { bins[4 * q] = c.x; bins[4 * q + 1] = c.y; bins[4 * q + 2] = c.z; bins[4 * q + 3] = c.w; }
+      }
+      local += (c.x + c.y) + (c.z + c.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      bins[j] = sm.hist[b0 + j];
+      local += bins[j];
+    }
+  }
+  const uint32_t winc = wave_scan_dpp(local);
+  if (lane == kWave - 1) sm.whi[w] = winc;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) before += ww < w ? sm.whi[ww] : 0u;
+  const uint32_t inc = before + winc, ex = inc - local;
+  if (ex < k_rem && k_rem <= inc) {
+    uint32_t run = ex;
+#pragma unroll
+    for (int j = BPT - 1; j >= 0; --j) {
+      if (run < k_rem && k_rem <= run + bins[j]) { sm.sel_bin = uint32_t(b0 + j); sm.sel_above = run; }
+      run += bins[j];
+    }
+  }
+  __syncthreads();
+}
+
+template <int NT, int PMAX, typename EmitFn>
+__device__ void block_topk32(const uint32_t (&key)[PMAX], int P, int n, int k, int r0, int r1, bool all,
+                             EmitFn emit, Topk32Smem<NT>& sm) {
+  static_assert(PMAX <= 32, "bit masks are 32 bits");
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nv = max(0, min(P, n - tid * P));
+  // key range; the first histogram is cleared under the same barrier
+  uint32_t kmin = ~0u, kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < PMAX; ++e)
+    if (e < nv) { kmin = min(kmin, key[e]); kmax = max(kmax, key[e]); }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) { sm.wlo[w] = kmin; sm.whi[w] = kmax; }
+  {
+    uint4* h4 = reinterpret_cast<uint4*>(sm.hist);
+    for (int i = tid; i < 2048 / 4; i += NT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+  kmin = sm.wlo[0];
+  kmax = sm.whi[0];
+#pragma unroll
+  for (int ww = 1; ww < NW; ++ww) { kmin = min(kmin, sm.wlo[ww]); kmax = max(kmax, sm.whi[ww]); }
+  const uint32_t range = kmax - kmin;
+  const int shift = range == 0u ? 0 : max(0, 32 - __clz(int(range)) - 11);   // (range >> shift) < 2048
+  __syncthreads();   // whi is reused by the scans
+#pragma unroll
+  for (int e = 0; e < PMAX; ++e)
+    if (e < nv) atomicAdd(&sm.hist[(key[e] - kmin) >> shift], 1u);
+  __syncthreads();
+  topk32_pick_bin<NT, 2048>(uint32_t(k), sm);
+  const uint32_t b1 = sm.sel_bin;
+  uint32_t base = kmin + (b1 << shift);
+  uint32_t k_rem = uint32_t(k) - sm.sel_above;
+  int rem_bits = shift;
+  if (rem_bits > 0) {
+    // the chosen bin usually holds a few keys: gather them and rank each by
+    // brute force (larger keys, then equal keys); the one whose rank span
+    // holds k_rem is the threshold
+    uint32_t inb = 0;
+#pragma unroll
+    for (int e = 0; e < PMAX; ++e) inb |= (e < nv && ((key[e] - kmin) >> shift) == b1 ? 1u : 0u) << e;
+    // slots by a block scan of the per-thread counts (no returning atomics)
+    const uint32_t cnt = uint32_t(__popc(inb));
+    const uint32_t cinc = wave_scan_dpp(cnt);
+    if (lane == kWave - 1) sm.whi[w] = cinc;
+    __syncthreads();
+    uint32_t off = cinc - cnt, nc = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      off += ww < w ? sm.whi[ww] : 0u;
+      nc += sm.whi[ww];
+    }
+    if (inb != 0u && off < uint32_t(Topk32Smem<NT>::kCandCap)) {
+#pragma unroll
+      for (int e = 0; e < PMAX; ++e) {
+        if ((inb >> e) & 1u) {
+          const uint32_t slot = off + uint32_t(__popc(inb & ((1u << e) - 1u)));
+          if (slot < uint32_t(Topk32Smem<NT>::kCandCap)) sm.cand[slot] = key[e];
+        }
+      }
+    }
+    __syncthreads();
+    if (nc <= uint32_t(Topk32Smem<NT>::kCandCap)) {
+      for (uint32_t t = uint32_t(tid); t < nc; t += NT) {
+        const uint32_t v = sm.cand[t];
+        uint32_t gt = 0, eq = 0;
+        for (uint32_t j = 0; j < nc; ++j) {
+          const uint32_t c = sm.cand[j];
+          gt += c > v ? 1u : 0u;
+          eq += c == v ? 1u : 0u;
+        }
+        if (gt < k_rem && k_rem <= gt + eq) { sm.sel_bin = v; sm.sel_above = gt; }   // equal v write equal values
+      }
+      __syncthreads();
+      base = sm.sel_bin;
+      k_rem -= sm.sel_above;
+      rem_bits = 0;
+    }
+  }
+  while (rem_bits > 0) {   // crowded bin: radix passes (uniform over the work-group)
+    const int wbits = min(13, rem_bits);
+    const int sh = rem_bits - wbits;
+    {
+      uint4* h4 = reinterpret_cast<uint4*>(sm.hist);
+      for (int i = tid; i < 8192 / 4; i += NT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+    const uint32_t span = rem_bits >= 32 ? ~0u : ((1u << rem_bits) - 1u);
+#pragma unroll
+    for (int e = 0; e < PMAX; ++e)
+      if (e < nv && key[e] >= base && key[e] - base <= span) atomicAdd(&sm.hist[(key[e] - base) >> sh], 1u);
+    __syncthreads();
+    topk32_pick_bin<NT, 8192>(k_rem, sm);
+    base += sm.sel_bin << sh;
+    k_rem -= sm.sel_above;
+    rem_bits = sh;
+  }
+  const uint32_t thr = base, need = k_rem;
+  uint32_t gtm = 0, eqm = 0;
+#pragma unroll
+  for (int e = 0; e < PMAX; ++e) {
+    if (e < nv) {
+      gtm |= (key[e] > thr ? 1u : 0u) << e;
+      eqm |= (key[e] == thr ? 1u : 0u) << e;
+    }
+  }
+  const uint32_t gt = uint32_t(__popc(gtm)), eq = uint32_t(__popc(eqm));
+  const uint32_t v = (eq << 16) | gt;
+  const uint32_t inc = wave_scan_dpp(v);
+  if (lane == kWave - 1) sm.whi[w] = inc;
+  __syncthreads();
+  uint32_t bf = inc - v;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) bf += ww < w ? sm.whi[ww] : 0u;
+  const uint32_t gt_before = bf & 0xFFFFu, eq_before = bf >> 16;
+  const uint32_t ties_before = eq_before < need ? eq_before : need;
+  const uint32_t ties_here = (eq_before + eq < need ? eq_before + eq : need) - ties_before;
+  uint32_t tie_keep = eqm;
+  if (ties_here < eq) {
+    tie_keep = 0;
+    uint32_t m = eqm;
+    for (uint32_t i = 0; i < ties_here; ++i) {
+      const uint32_t low = m & (~m + 1u);
+      tie_keep |= low;
+      m ^= low;
+    }
+  }
+  const uint32_t take = gtm | tie_keep;
+  const uint32_t pos0 = gt_before + ties_before;
+  const uint32_t cnt = gt + ties_here;
+  if (all || (pos0 < uint32_t(r1) && pos0 + cnt > uint32_t(r0))) {
+#pragma unroll
+    for (int e = 0; e < PMAX; ++e) {
+      if ((take >> e) & 1u) {
+        const uint32_t pos = pos0 + uint32_t(__popc(take & ((1u << e) - 1u)));
+        if (all || (pos >= uint32_t(r0) && pos < uint32_t(r1))) emit(int(pos), e);
+      }
+    }
+  }
+}
+
 }  // namespace bc

@@ -107,9 +107,14 @@ int launch_argmax_finish(const float* tile_max, const int32_t* tile_arg, int n_t
 //              partials (rotary at pos, bf16 rounding); the work-group whose
 //              range holds list position pos (dense list, pos = n_sel - 1)
 //              appends k, v at cache slot pos and attends to them from LDS.
-//   L_DENSE    tokens 0..n_sel-1;  L_IDX  an index list [n_kv_heads][n_sel].
+//   L_DENSE    tokens 0..n_sel-1;  L_IDX  an index list [n_kv_heads][n_sel];
+//   L_SCORES   the list sinks | top-k_blk scored blocks | window, built in
+//              every work-group's prologue from the block scores (each
+//              split selects the block ranks its slice needs).
 enum AttnQ : int { Q_GLOBAL = 0, Q_PARTIAL = 1 };
-enum AttnList : int { L_DENSE = 0, L_IDX = 1 };
+enum AttnList : int { L_DENSE = 0, L_IDX = 1, L_SCORES = 2 };
+constexpr int kAttnMaxCand = 256 * 32;   // candidate blocks one attention work-group selects from
+constexpr int kAttnMaxRanks = 1024;      // block ranks one split may need
 
 struct AttnParams {
   const uint16_t* q;
@@ -129,8 +134,16 @@ struct AttnParams {
   RopeTable rope;
   uint16_t* q_out;            // optional bf16 copy of q
   uint16_t* summary;          // optional: (min, max) of block pos/16 refreshed by the appending work-group
+  // L_SCORES
+  const float* scores;        // [n_kv_heads][scores_stride]
+  int scores_stride;
+  bc_kv_budget_info bud;
+  int n_ctx;
+  int32_t* idx_out;           // optional: the list [n_kv_heads][n_sel] (each split writes its slice)
 };
 int launch_attn_partial(int q_mode, int list_mode, const AttnParams& p, hipStream_t s);
+// whether a scored list fits the in-prologue selection (candidates, ranks per split)
+bool attn_scored_list_ok(const bc_kv_budget_info& bud, int n_splits);
 
 struct ReduceParams {
   const float* m;
@@ -143,13 +156,28 @@ int launch_attn_reduce(const ReduceParams& p, hipStream_t s);
 
 struct KvSelectParams {
   const uint16_t* q;
-  const uint16_t* summary;
+  uint16_t* summary;
   int nb_cap, n_ctx, n_heads, n_kv_heads, head_dim;
   bc_kv_budget_info bud;
-  float* scores;          // [n_kv_heads][n_cand]
+  float* scores;          // [n_kv_heads][scores_stride]
+  int scores_stride;
   int32_t* idx_out;       // [n_kv_heads][t_sel]
+  // q from the qkv GEMV partials (rotary at pos): the first work-group of
+  // each KV head also stores q, appends k, v at slot pos and refreshes the
+  // summary of block pos/16 (valid when that block is never a candidate)
+  const float* qkv_partial;
+  int qkv_splits, qkv_out, pos, n_cap;
+  RopeTable rope;
+  uint16_t* q_out;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
 };
+// scores, then the list (one work-group per KV head)
 int launch_kv_score_select(const KvSelectParams& p, hipStream_t s);
+// scores only (q given or from the partials, with the append)
+int launch_kv_score(const KvSelectParams& p, hipStream_t s);
+// the list from the scores
+int launch_kv_block_select(const KvSelectParams& p, hipStream_t s);
 
 int launch_select(const uint16_t* x, int n, int k, int32_t* idx_out, hipStream_t s);
 int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);

@@ -14,9 +14,11 @@
 //   a_{j,p} = (t_{j,4p} + t_{j,4p+1}) + (t_{j,4p+2} + t_{j,4p+3}),
 //   c_p = adjacent-pair tree over j, s = adjacent-pair tree over p,
 // the last one being the xor-1,2,4,8,16 butterfly over the lanes.
-// Selection: one 1024-thread work-group per KV head, exact radix top-k on
-// order-preserving keys of the scores (equal scores: lower block), then the
-// list sinks | kept blocks' tokens | window is written in ascending order.
+// Selection (block_topk32, exact; equal scores keep the lower block): in the
+// decode layer every attention work-group selects the block ranks of its own
+// slice of the list in its prologue; bc_kv_score_select writes the whole
+// list sinks | kept blocks' tokens | window with one 1024-thread
+// work-group per KV head.
 #include <math.h>
 
 #include "bc_device.hpp"
@@ -29,23 +31,94 @@ namespace {
 constexpr int kScoreThreads = 256;
 constexpr int kScoreBlocksPerGroup = 64;
 constexpr int kSelThreads = 1024;
+constexpr int kSelMaxCand = kSelThreads * 32;
 
-template <int D, int G>
+// Scores of the candidate blocks of KV head blockIdx.y (64 per work-group).
+// QP: q comes from the qkv GEMV chunk partials (rotary from the host table,
+// bf16 rounding); the first work-group of each KV head also stores q,
+// appends k, v of the current token at slot pos and refreshes the (min, max)
+// summary of block pos/16 (which is then never a candidate).
+template <int D, int G, bool QP>
 __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams p) {
   constexpr int P = D / 4;            // lanes per candidate block
   constexpr int CPW = kWave / P;      // candidate blocks per wave load
+  constexpr int HALF = D / 2;
+  __shared__ uint16_t sq[G][D];
+  __shared__ uint16_t knew[D];
   const int g = blockIdx.y;
-  const int lane = wave_lane(), w = wave_id();
+  const int tid = threadIdx.x, lane = wave_lane(), w = wave_id();
   const int cs = lane / P, pp = lane % P;
   const int n_cand = p.bud.n_cand;
 
   float qf[G][4];
+  if constexpr (QP) {
+    const bool first = blockIdx.x == 0;
+    for (int e = tid; e < G * HALF; e += kScoreThreads) {
+      const int j = e / HALF, i = e % HALF;
+      const int col = (g * G + j) * D + i;
+      const float a = chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, col);
+      const float b = chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, col + HALF);
+      const float c = p.rope.c[i], sn = p.rope.s[i];
+      const uint16_t qa = f32_to_bf16(a * c - b * sn), qb = f32_to_bf16(b * c + a * sn);
+      sq[j][i] = qa;
+      sq[j][i + HALF] = qb;
+      if (first) {
+        p.q_out[size_t(g * G + j) * D + i] = qa;
+        p.q_out[size_t(g * G + j) * D + i + HALF] = qb;
+      }
+    }
+    if (first) {
+      const int kcol = p.n_heads * D + g * D, vcol = (p.n_heads + p.n_kv_heads) * D + g * D;
+      uint16_t* kr = p.k_cache + (size_t(g) * p.n_cap + p.pos) * D;
+      uint16_t* vr = p.v_cache + (size_t(g) * p.n_cap + p.pos) * D;
+      for (int i = tid; i < HALF; i += kScoreThreads) {
+        const float a = chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + i);
+        const float b = chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + i + HALF);
+        const float c = p.rope.c[i], sn = p.rope.s[i];
+        const uint16_t ka = f32_to_bf16(a * c - b * sn), kb = f32_to_bf16(b * c + a * sn);
+        knew[i] = ka;
+        knew[i + HALF] = kb;
+        kr[i] = ka;
+        kr[i + HALF] = kb;
+      }
+      for (int i = tid; i < D; i += kScoreThreads)
+        vr[i] = f32_to_bf16(chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, vcol + i));
+    }
+    __syncthreads();
+    if (first && p.summary && tid < D) {
+      // per dim: the new row first, then rows 16*blk.. in order (rows from
+      // pos on are the new row); an equal value never replaces an earlier one
+      const int blk = p.pos / 16;
+      const uint16_t* kc = p.k_cache + size_t(g) * p.n_cap * D + tid;
+      const uint16_t nb = knew[tid];
+      uint16_t bmn = nb, bmx = nb;
+      float mn = bf16_to_f32(nb), mx = mn;
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    uint2 t = *reinterpret_cast<const uint2*>(p.q + size_t(g * G + j) * D + 4 * pp);
-    qf[j][0] = bf16_lo(t.x); qf[j][1] = bf16_hi(t.x);
-    qf[j][2] = bf16_lo(t.y); qf[j][3] = bf16_hi(t.y);
+      for (int t = 0; t < 16; ++t) {
+        const uint16_t u = blk * 16 + t < p.pos ? kc[size_t(blk * 16 + t) * D] : nb;
+        const float f = bf16_to_f32(u);
+        if (f < mn) { mn = f; bmn = u; }
+        if (f > mx) { mx = f; bmx = u; }
+      }
+      uint16_t* sp = p.summary + ((size_t(g) * p.nb_cap + blk) * D + tid) * 2;
+      sp[0] = bmn;
+      sp[1] = bmx;
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const uint2 t = *reinterpret_cast<const uint2*>(&sq[j][4 * pp]);
+      qf[j][0] = bf16_lo(t.x); qf[j][1] = bf16_hi(t.x);
+      qf[j][2] = bf16_lo(t.y); qf[j][3] = bf16_hi(t.y);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const uint2 t = *reinterpret_cast<const uint2*>(p.q + size_t(g * G + j) * D + 4 * pp);
+      qf[j][0] = bf16_lo(t.x); qf[j][1] = bf16_hi(t.x);
+      qf[j][2] = bf16_lo(t.y); qf[j][3] = bf16_hi(t.y);
+    }
   }
+  if (p.bud.k_blk <= 0) return;
   const int cbeg = blockIdx.x * kScoreBlocksPerGroup;
   const int cend = min(n_cand, cbeg + kScoreBlocksPerGroup);
   const uint16_t* sg = p.summary + size_t(g) * p.nb_cap * D * 2;
@@ -78,28 +151,36 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
     v = v + dpp_f<kDppHalfMirror>(v);
     v = v + dpp_f<kDppMirror>(v);
     if constexpr (P == 32) v = v + __shfl_xor(v, 16, kWave);
-    if (valid && pp == 0) p.scores[size_t(g) * n_cand + c] = v;
+    if (valid && pp == 0) p.scores[size_t(g) * p.scores_stride + c] = v;
   }
 }
 
+// The list of KV head blockIdx.x: sinks, the tokens of the k_blk blocks
+// with the highest scores (block_topk32 on order-preserving keys; equal
+// scores keep the lower block), the window; ascending.
 __global__ __launch_bounds__(kSelThreads) void k_kv_block_select(const KvSelectParams p) {
-  __shared__ TopkSmem<kSelThreads, uint32_t> sm;
+  __shared__ Topk32Smem<kSelThreads> sm;
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   const bc_kv_budget_info bd = p.bud;
   int32_t* out = p.idx_out + size_t(g) * bd.t_sel;
-  const float* sc = p.scores + size_t(g) * bd.n_cand;
   for (int t = tid; t < bd.sinks; t += kSelThreads) out[t] = t;
   for (int t = tid; t < bd.window; t += kSelThreads) out[bd.t_sel - bd.window + t] = p.n_ctx - bd.window + t;
-  auto key = [sc](int i) -> uint32_t { return float_order_key(sc[i]); };
+  if (bd.k_blk <= 0) return;
+  const int n = bd.n_cand;
+  const int P = (n + kSelThreads - 1) / kSelThreads;
+  const float* sc = p.scores + size_t(g) * p.scores_stride + size_t(tid) * P;
+  uint32_t key[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) key[e] = (e < P && tid * P + e < n) ? float_order_key(sc[e]) : 0u;
   const int b_lo = bd.b_lo, sinks = bd.sinks;
-  auto emit = [out, b_lo, sinks](int rk, int i) {
+  auto emit = [&](int rk, int e) {
     int32_t* o = out + sinks + 16 * rk;
-    const int t0 = 16 * (b_lo + i);
+    const int t0 = 16 * (b_lo + tid * P + e);
 #pragma unroll
     for (int u = 0; u < 16; ++u) o[u] = t0 + u;
   };
-  block_topk<kSelThreads, 32, uint32_t>(bd.n_cand, bd.k_blk, key, emit, sm);
+  block_topk32<kSelThreads, 32>(key, P, n, bd.k_blk, 0, bd.k_blk, true, emit, sm);
 }
 
 // One wave per (block, KV head): per dim the min and max over the block's
@@ -128,14 +209,14 @@ __global__ __launch_bounds__(256) void k_build_summary(const uint16_t* k_cache, 
   }
 }
 
-template <int D>
-int launch_score_d(const KvSelectParams& p, hipStream_t s) {
-  dim3 grid(ceil_div(p.bud.n_cand, kScoreBlocksPerGroup), p.n_kv_heads), block(kScoreThreads);
+template <int D, bool QP>
+int launch_score_dq(const KvSelectParams& p, hipStream_t s) {
+  dim3 grid(max(1, ceil_div(p.bud.n_cand, kScoreBlocksPerGroup)), p.n_kv_heads), block(kScoreThreads);
   switch (p.n_heads / p.n_kv_heads) {
-    case 1: k_kv_score<D, 1><<<grid, block, 0, s>>>(p); break;
-    case 2: k_kv_score<D, 2><<<grid, block, 0, s>>>(p); break;
-    case 4: k_kv_score<D, 4><<<grid, block, 0, s>>>(p); break;
-    case 8: k_kv_score<D, 8><<<grid, block, 0, s>>>(p); break;
+    case 1: k_kv_score<D, 1, QP><<<grid, block, 0, s>>>(p); break;
+    case 2: k_kv_score<D, 2, QP><<<grid, block, 0, s>>>(p); break;
+    case 4: k_kv_score<D, 4, QP><<<grid, block, 0, s>>>(p); break;
+    case 8: k_kv_score<D, 8, QP><<<grid, block, 0, s>>>(p); break;
     default: return set_error(BC_ERR_UNSUPPORTED, "kv score: group %d", p.n_heads / p.n_kv_heads);
   }
   return check_launch("k_kv_score");
@@ -143,15 +224,25 @@ int launch_score_d(const KvSelectParams& p, hipStream_t s) {
 
 }  // namespace
 
-int launch_kv_score_select(const KvSelectParams& p, hipStream_t s) {
-  if (p.bud.n_cand > 0 && p.bud.k_blk > 0) {
-    int rc = p.head_dim == 128 ? launch_score_d<128>(p, s)
-             : p.head_dim == 64 ? launch_score_d<64>(p, s)
-                                : set_error(BC_ERR_UNSUPPORTED, "kv score: head_dim %d", p.head_dim);
-    if (rc != BC_OK) return rc;
-  }
+int launch_kv_score(const KvSelectParams& p, hipStream_t s) {
+  const bool qp = p.qkv_partial != nullptr;
+  if (!qp && (p.bud.n_cand <= 0 || p.bud.k_blk <= 0)) return BC_OK;   // nothing to score
+  if (p.head_dim == 128) return qp ? launch_score_dq<128, true>(p, s) : launch_score_dq<128, false>(p, s);
+  if (p.head_dim == 64) return qp ? launch_score_dq<64, true>(p, s) : launch_score_dq<64, false>(p, s);
+  return set_error(BC_ERR_UNSUPPORTED, "kv score: head_dim %d", p.head_dim);
+}
+
+int launch_kv_block_select(const KvSelectParams& p, hipStream_t s) {
+  if (p.bud.n_cand > kSelMaxCand) return set_error(BC_ERR_UNSUPPORTED, "kv select: %d candidate blocks", p.bud.n_cand);
   k_kv_block_select<<<dim3(p.n_kv_heads), dim3(kSelThreads), 0, s>>>(p);
   return check_launch("k_kv_block_select");
+}
+
+int launch_kv_score_select(const KvSelectParams& p, hipStream_t s) {
+  if (p.bud.n_cand > kSelMaxCand) return set_error(BC_ERR_UNSUPPORTED, "kv select: %d candidate blocks", p.bud.n_cand);
+  int rc = launch_kv_score(p, s);
+  if (rc != BC_OK) return rc;
+  return launch_kv_block_select(p, s);
 }
 
 }  // namespace bc
@@ -208,8 +299,9 @@ extern "C" int bc_kv_score_select(const uint16_t* q, const uint16_t* summary, in
     scores = static_cast<float*>(ws);
   }
   KvSelectParams p{};
-  p.q = q; p.summary = summary; p.nb_cap = nb_cap; p.n_ctx = n_ctx; p.n_heads = n_heads;
-  p.n_kv_heads = n_kv_heads; p.head_dim = head_dim; p.bud = b; p.scores = scores; p.idx_out = idx_out;
+  p.q = q; p.summary = const_cast<uint16_t*>(summary); p.nb_cap = nb_cap; p.n_ctx = n_ctx; p.n_heads = n_heads;
+  p.n_kv_heads = n_kv_heads; p.head_dim = head_dim; p.bud = b; p.scores = scores; p.scores_stride = b.n_cand;
+  p.idx_out = idx_out;
   return launch_kv_score_select(p, static_cast<hipStream_t>(stream));
 }
 

@@ -354,31 +354,43 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
   uint16_t* a = at<uint16_t>(ws, L.a);
   uint16_t* hff = at<uint16_t>(ws, L.hff);
 
-  // x1 = RMSNorm(h), S1 (GEMV prologue); q, k, v.  With a scored KV list
-  // the finish kernel applies the rotary, appends k, v and refreshes the
-  // block summary before the scoring; with the dense list the attention
-  // kernel does all of that itself from the chunk partials.
+  // x1 = RMSNorm(h), S1 (GEMV prologue); q, k, v from its chunk partials.
+  // Dense list: the attention kernel applies the rotary, appends k, v and
+  // refreshes the block summary itself.  Scored list: the scoring kernel
+  // does that (unless the window is empty, when the current block may be a
+  // candidate: then a finish kernel does it first), and every attention
+  // work-group selects the blocks of its own slice of the list.
   const ProjIn qkv_in{IN_NORM, hidden, ly->g_attn, eps, at<uint16_t>(ws, L.x1), idx_qkv};
   RopeTable rope;
   rope_table(pos, st->rope_theta, hd, &rope);
   int qkv_splits = 0;
+  const bool fused_score = kv_sparse && (bud.window > 0 || bud.k_blk == 0);
+  const bool scored_attn = kv_sparse && attn_scored_list_ok(bud, n_splits);
+  KvSelectParams kp{};
   if (kv_sparse) {
+    kp.summary = ly->kv_summary; kp.nb_cap = ly->n_cap / 16; kp.n_ctx = st->n_ctx;
+    kp.n_heads = H; kp.n_kv_heads = Hkv; kp.head_dim = hd; kp.bud = bud;
+    kp.scores = at<float>(ws, L.scores); kp.scores_stride = bud.n_cand > 0 ? bud.n_cand : 1;
+    kp.idx_out = at<int32_t>(ws, L.idx_kv);
+  }
+  if (kv_sparse && !fused_score) {
     FinishParams f{};
     f.q_out = at<uint16_t>(ws, L.q); f.k_cache = ly->k_cache; f.v_cache = ly->v_cache; f.summary = ly->kv_summary;
-    f.n_heads = H; f.n_kv_heads = Hkv; f.head_dim = hd; f.n_cap = ly->n_cap; f.pos = pos;
-    f.rope = rope;
+    f.n_heads = H; f.n_kv_heads = Hkv; f.head_dim = hd; f.n_cap = ly->n_cap; f.pos = pos; f.rope = rope;
     if ((rc = run_gemv(ly->w_qkv, m.d, qkv_out, k_d, qkv_in, partial, FIN_QKV, f, s)) != BC_OK) return rc;
-
-    KvSelectParams p{};
-    p.q = at<uint16_t>(ws, L.q); p.summary = ly->kv_summary; p.nb_cap = ly->n_cap / 16; p.n_ctx = st->n_ctx;
-    p.n_heads = H; p.n_kv_heads = Hkv; p.head_dim = hd; p.bud = bud;
-    p.scores = at<float>(ws, L.scores); p.idx_out = at<int32_t>(ws, L.idx_kv);
-    if ((rc = launch_kv_score_select(p, s)) != BC_OK) return rc;
+    kp.q = at<uint16_t>(ws, L.q);
+    if ((rc = launch_kv_score(kp, s)) != BC_OK) return rc;
   } else {
     if ((rc = run_gemv(ly->w_qkv, m.d, qkv_out, k_d, qkv_in, partial, FIN_NONE, FinishParams{}, s, &qkv_splits)) !=
         BC_OK)
       return rc;
+    if (kv_sparse) {
+      kp.qkv_partial = partial; kp.qkv_splits = qkv_splits; kp.qkv_out = qkv_out; kp.pos = pos; kp.n_cap = ly->n_cap;
+      kp.rope = rope; kp.q_out = at<uint16_t>(ws, L.q); kp.k_cache = ly->k_cache; kp.v_cache = ly->v_cache;
+      if ((rc = launch_kv_score(kp, s)) != BC_OK) return rc;
+    }
   }
+  if (kv_sparse && !scored_attn && (rc = launch_kv_block_select(kp, s)) != BC_OK) return rc;
 
   // attention
   {
@@ -391,8 +403,14 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
     r.m = p.m; r.l = p.l; r.o = p.o; r.n_heads = H; r.n_splits = n_splits; r.head_dim = hd; r.out = a;
     if (kv_sparse) {
       p.q = at<uint16_t>(ws, L.q);
-      p.idx = at<int32_t>(ws, L.idx_kv);
-      if ((rc = launch_attn_partial(Q_GLOBAL, L_IDX, p, s)) != BC_OK) return rc;
+      if (scored_attn) {
+        p.scores = kp.scores; p.scores_stride = kp.scores_stride; p.bud = bud; p.n_ctx = st->n_ctx;
+        p.idx_out = st->taps ? at<int32_t>(ws, L.idx_kv) : nullptr;
+        if ((rc = launch_attn_partial(Q_GLOBAL, L_SCORES, p, s)) != BC_OK) return rc;
+      } else {
+        p.idx = at<int32_t>(ws, L.idx_kv);
+        if ((rc = launch_attn_partial(Q_GLOBAL, L_IDX, p, s)) != BC_OK) return rc;
+      }
     } else {
       p.qkv_partial = partial; p.qkv_splits = qkv_splits; p.qkv_out = qkv_out; p.pos = pos;
       p.rope = rope; p.q_out = st->taps ? at<uint16_t>(ws, L.q) : nullptr; p.summary = ly->kv_summary;
