@@ -180,6 +180,18 @@ __device__ __forceinline__ void attn_compute(const AttnRows& rw, const uint16_t*
   }
 }
 
+// Block ranks [r_lo, r_hi) of the exact top-k_blk of n block scores:
+// blk[rank - r_lo] = candidate index.  PM keys per thread (n <= NT * PM).
+template <int NT, int PM>
+__device__ void select_block_ranks(const float* sc, int n, int k_blk, int r_lo, int r_hi, int32_t* blk,
+                                   Topk32Smem<NT>& tk) {
+  uint32_t key[PM];
+  const int P = load_score_keys<NT, PM>(sc, n, key, tk.hist);
+  const int tid = threadIdx.x;
+  auto emit = [&](int rank, int e) { blk[rank - r_lo] = tid * P + e; };
+  block_topk32<NT, PM>(key, P, n, k_blk, r_lo, r_hi, false, emit, tk);
+}
+
 template <int D, int G, int QM, int LM>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams p) {
   constexpr int LPT = D / 16;          // lanes per row
@@ -247,14 +259,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
     }
     if (r_lo < r_hi) {   // uniform over the work-group
       const int n = p.bud.n_cand;
-      const int P = (n + kAttnThreads - 1) / kAttnThreads;
-      const float* sc = p.scores + size_t(g) * p.scores_stride + size_t(tid) * P;
-      uint32_t key[32];
-#pragma unroll
-      for (int e = 0; e < 32; ++e) key[e] = (e < P && tid * P + e < n) ? float_order_key(sc[e]) : 0u;
-      const int rl = r_lo;
-      auto emit = [&](int rank, int e) { sm.blk[rank - rl] = tid * P + e; };
-      block_topk32<kAttnThreads, 32>(key, P, n, KB, r_lo, r_hi, false, emit, sm.tk);
+      const float* sc = p.scores + size_t(g) * p.scores_stride;
+      if (n <= kAttnThreads * 8)
+        select_block_ranks<kAttnThreads, 8>(sc, n, KB, r_lo, r_hi, sm.blk, sm.tk);
+      else
+        select_block_ranks<kAttnThreads, 32>(sc, n, KB, r_lo, r_hi, sm.blk, sm.tk);
     }
   }
 
@@ -323,10 +332,21 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
     int32_t* idx_out = LM == L_SCORES && p.idx_out ? p.idx_out + size_t(g) * p.n_sel : nullptr;
     for (int c0 = lo; c0 < hi; c0 += kIdxChunk) {
       const int c1 = min(hi, c0 + kIdxChunk);
-      for (int i = tid; i < c1 - c0; i += kAttnThreads) {
+      // list positions -> tokens (a chunk is at most 4 positions per thread;
+      // index loads are all issued before the stores)
+      static_assert(kIdxChunk == 4 * kAttnThreads, "chunk of 4 positions per thread");
+      int32_t tk[4];
+      if constexpr (LM == L_IDX) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) tk[u] = tid + u * kAttnThreads < c1 - c0 ? idxg[c0 + tid + u * kAttnThreads] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = tid + u * kAttnThreads;
+        if (i >= c1 - c0) continue;
         int t;
         if constexpr (LM == L_IDX) {
-          t = idxg[c0 + i];
+          t = tk[u];
         } else {
           // list position -> token: sinks, then 16 tokens per kept block
           // (ascending block order), then the window

@@ -154,18 +154,19 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 }
 
 // ------------------------------------------------------- split partials
-// Sum of the n_splits chunk partials of column c, in chunk order.
+// Sum of the n_splits chunk partials of column c, in chunk order.  Up to 8
+// chunks are loaded at once (one memory round trip for the usual plans).
 __device__ __forceinline__ float chunk_sum(const float* partial, int n_splits, int d_out, int c) {
   float v = 0.f;
   int s = 0;
-  for (; s + 4 <= n_splits; s += 4) {
-    const float a0 = partial[size_t(s) * d_out + c];
-    const float a1 = partial[size_t(s + 1) * d_out + c];
-    const float a2 = partial[size_t(s + 2) * d_out + c];
-    const float a3 = partial[size_t(s + 3) * d_out + c];
-    v += a0; v += a1; v += a2; v += a3;
+  for (; s < n_splits; s += 8) {
+    float a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] = s + u < n_splits ? partial[size_t(s + u) * d_out + c] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s + u < n_splits) v += a[u];
   }
-  for (; s < n_splits; ++s) v += partial[size_t(s) * d_out + c];
   return v;
 }
 
@@ -553,8 +554,10 @@ __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int 
   if (tid < NB2) sm.hist2[tid] = 0;
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < PMAX; ++e)
-    if (e < nv) atomicAdd(&sm.hist[key[e] >> SHIFT], 1u);
+  for (int e = 0; e < PMAX; ++e) {
+    const bool ok = e < nv;
+    atomicAdd(&sm.hist[ok ? key[e] >> SHIFT : uint32_t(lane)], ok ? 1u : 0u);
+  }
   __syncthreads();
   // thread t owns bins [b0, b0 + BPT), b0 = NB - BPT (t + 1): the largest
   // bins go to thread 0, so the prefix over threads counts larger keys
@@ -773,9 +776,13 @@ __device__ void block_topk32(const uint32_t (&key)[PMAX], int P, int n, int k, i
   const uint32_t range = kmax - kmin;
   const int shift = range == 0u ? 0 : max(0, 32 - __clz(int(range)) - 11);   // (range >> shift) < 2048
   __syncthreads();   // whi is reused by the scans
+  // every lane adds: positions past n add 0 into a bin of their own lane
+  // (no branches and no colliding dummy adds)
 #pragma unroll
-  for (int e = 0; e < PMAX; ++e)
-    if (e < nv) atomicAdd(&sm.hist[(key[e] - kmin) >> shift], 1u);
+  for (int e = 0; e < PMAX; ++e) {
+    const bool ok = e < nv;
+    atomicAdd(&sm.hist[ok ? (key[e] - kmin) >> shift : uint32_t(lane)], ok ? 1u : 0u);
+  }
   __syncthreads();
   topk32_pick_bin<NT, 2048>(uint32_t(k), sm);
   const uint32_t b1 = sm.sel_bin;
@@ -887,6 +894,43 @@ __device__ void block_topk32(const uint32_t (&key)[PMAX], int P, int n, int k, i
       }
     }
   }
+}
+
+// Keys of n fp32 scores for block_topk32, thread t owning positions
+// [t*PMAX, t*PMAX + PMAX) (P = PMAX, so n <= NT*PMAX; positions >= n carry
+// don't-care keys that block_topk32 ignores): the scores are read with
+// coalesced loads into `stage` (LDS, NT*PMAX words), then each thread takes
+// its PMAX keys as 16-byte pieces in a thread-rotated order (the threads'
+// ranges are PMAX words apart).  Every index is clamped instead of tested,
+// so the code has no branches.  Returns P.  Contains __syncthreads().
+template <int NT, int PMAX>
+__device__ int load_score_keys(const float* src, int n, uint32_t (&key)[PMAX], uint32_t* stage) {
+  static_assert(PMAX % 4 == 0 && ((PMAX / 4) & (PMAX / 4 - 1)) == 0, "power-of-two count of 16-byte pieces");
+  constexpr int NQ = PMAX / 4;
+  const int tid = threadIdx.x;
+  const int last = max(n - 1, 0);
+  float v[PMAX];
+#pragma unroll
+  for (int j = 0; j < PMAX; ++j) v[j] = src[min(tid + j * NT, last)];
+#pragma unroll
+  for (int j = 0; j < PMAX; ++j) stage[tid + j * NT] = float_order_key(v[j]);
+  __syncthreads();
+  const uint4* sp = reinterpret_cast<const uint4*>(stage + tid * PMAX);
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int jj = (j + tid) & (NQ - 1);
+    const uint4 c = sp[jj];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const bool hit = q == jj;
+      key[4 * q] = hit ? c.x : key[4 * q];
+      key[4 * q + 1] = hit ? c.y : key[4 * q + 1];
+      key[4 * q + 2] = hit ? c.z : key[4 * q + 2];
+      key[4 * q + 3] = hit ? c.w : key[4 * q + 3];
+    }
+  }
+  __syncthreads();
+  return PMAX;
 }
 
 }  // namespace bc

@@ -29,7 +29,7 @@ namespace bc {
 namespace {
 
 constexpr int kScoreThreads = 256;
-constexpr int kScoreBlocksPerGroup = 64;
+constexpr int kScoreBlocksPerGroup = 128;
 constexpr int kSelThreads = 1024;
 constexpr int kSelMaxCand = kSelThreads * 32;
 
@@ -50,9 +50,37 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
   const int cs = lane / P, pp = lane % P;
   const int n_cand = p.bud.n_cand;
 
+  // every summary this wave scores is loaded up front (one round trip)
+  constexpr int NIT = kScoreBlocksPerGroup / ((kScoreThreads / kWave) * CPW);
+  const int cbeg = blockIdx.x * kScoreBlocksPerGroup;
+  const int cend = min(n_cand, cbeg + kScoreBlocksPerGroup);
+  const uint16_t* sg = p.summary + size_t(g) * p.nb_cap * D * 2;
+  uint4 mm[NIT];
+  if (p.bud.k_blk > 0) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int c = cbeg + (it * (kScoreThreads / kWave) + w) * CPW + cs;
+      const int b = p.bud.b_lo + (c < cend ? c : cbeg);
+      mm[it] = c < cend || cbeg < cend ? *reinterpret_cast<const uint4*>(sg + (size_t(b) * D + 4 * pp) * 2)
+                                       : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
   float qf[G][4];
   if constexpr (QP) {
     const bool first = blockIdx.x == 0;
+    // the current block's older rows, for its summary (first group only)
+    const int blk = p.pos / 16;
+    uint32_t srow[8];
+    if (first && p.summary && tid < D) {
+      const uint16_t* kc = p.k_cache + size_t(g) * p.n_cap * D + tid;
+#pragma unroll
+      for (int t = 0; t < 16; t += 2) {
+        const uint32_t a = blk * 16 + t < p.pos ? kc[size_t(blk * 16 + t) * D] : 0u;
+        const uint32_t b = blk * 16 + t + 1 < p.pos ? kc[size_t(blk * 16 + t + 1) * D] : 0u;
+        srow[t / 2] = a | (b << 16);
+      }
+    }
     for (int e = tid; e < G * HALF; e += kScoreThreads) {
       const int j = e / HALF, i = e % HALF;
       const int col = (g * G + j) * D + i;
@@ -88,14 +116,12 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
     if (first && p.summary && tid < D) {
       // per dim: the new row first, then rows 16*blk.. in order (rows from
       // pos on are the new row); an equal value never replaces an earlier one
-      const int blk = p.pos / 16;
-      const uint16_t* kc = p.k_cache + size_t(g) * p.n_cap * D + tid;
       const uint16_t nb = knew[tid];
       uint16_t bmn = nb, bmx = nb;
       float mn = bf16_to_f32(nb), mx = mn;
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        const uint16_t u = blk * 16 + t < p.pos ? kc[size_t(blk * 16 + t) * D] : nb;
+        const uint16_t u = blk * 16 + t < p.pos ? uint16_t(srow[t / 2] >> (16 * (t & 1))) : nb;
         const float f = bf16_to_f32(u);
         if (f < mn) { mn = f; bmn = u; }
         if (f > mx) { mx = f; bmx = u; }
@@ -119,16 +145,13 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
     }
   }
   if (p.bud.k_blk <= 0) return;
-  const int cbeg = blockIdx.x * kScoreBlocksPerGroup;
-  const int cend = min(n_cand, cbeg + kScoreBlocksPerGroup);
-  const uint16_t* sg = p.summary + size_t(g) * p.nb_cap * D * 2;
-  for (int cb = cbeg + w * CPW; cb < cend; cb += (kScoreThreads / kWave) * CPW) {
-    const int c = cb + cs;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int c = cbeg + (it * (kScoreThreads / kWave) + w) * CPW + cs;
     const bool valid = c < cend;
-    const int b = p.bud.b_lo + (valid ? c : cbeg);
-    const uint4 mm = *reinterpret_cast<const uint4*>(sg + (size_t(b) * D + 4 * pp) * 2);
-    const float mn[4] = {bf16_lo(mm.x), bf16_lo(mm.y), bf16_lo(mm.z), bf16_lo(mm.w)};
-    const float mx[4] = {bf16_hi(mm.x), bf16_hi(mm.y), bf16_hi(mm.z), bf16_hi(mm.w)};
+    const uint4 m4 = mm[it];
+    const float mn[4] = {bf16_lo(m4.x), bf16_lo(m4.y), bf16_lo(m4.z), bf16_lo(m4.w)};
+    const float mx[4] = {bf16_hi(m4.x), bf16_hi(m4.y), bf16_hi(m4.z), bf16_hi(m4.w)};
     float a[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -168,19 +191,32 @@ __global__ __launch_bounds__(kSelThreads) void k_kv_block_select(const KvSelectP
   for (int t = tid; t < bd.window; t += kSelThreads) out[bd.t_sel - bd.window + t] = p.n_ctx - bd.window + t;
   if (bd.k_blk <= 0) return;
   const int n = bd.n_cand;
-  const int P = (n + kSelThreads - 1) / kSelThreads;
-  const float* sc = p.scores + size_t(g) * p.scores_stride + size_t(tid) * P;
-  uint32_t key[32];
-#pragma unroll
-  for (int e = 0; e < 32; ++e) key[e] = (e < P && tid * P + e < n) ? float_order_key(sc[e]) : 0u;
   const int b_lo = bd.b_lo, sinks = bd.sinks;
-  auto emit = [&](int rk, int e) {
-    int32_t* o = out + sinks + 16 * rk;
-    const int t0 = 16 * (b_lo + tid * P + e);
+  const float* sc = p.scores + size_t(g) * p.scores_stride;
+  if (n <= kSelThreads * 8) {
+    // up to 8 keys per thread, staged through LDS (coalesced loads)
+    uint32_t key[8];
+    const int P = load_score_keys<kSelThreads, 8>(sc, n, key, sm.hist);
+    auto emit = [&](int rk, int e) {
+      int32_t* o = out + sinks + 16 * rk;
+      const int t0 = 16 * (b_lo + tid * P + e);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) o[u] = t0 + u;
-  };
-  block_topk32<kSelThreads, 32>(key, P, n, bd.k_blk, 0, bd.k_blk, true, emit, sm);
+      for (int u = 0; u < 16; ++u) o[u] = t0 + u;
+    };
+    block_topk32<kSelThreads, 8>(key, P, n, bd.k_blk, 0, bd.k_blk, true, emit, sm);
+  } else {
+    const int P = (n + kSelThreads - 1) / kSelThreads;
+    uint32_t key[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) key[e] = (e < P && tid * P + e < n) ? float_order_key(sc[size_t(tid) * P + e]) : 0u;
+    auto emit = [&](int rk, int e) {
+      int32_t* o = out + sinks + 16 * rk;
+      const int t0 = 16 * (b_lo + tid * P + e);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) o[u] = t0 + u;
+    };
+    block_topk32<kSelThreads, 32>(key, P, n, bd.k_blk, 0, bd.k_blk, true, emit, sm);
+  }
 }
 
 // One wave per (block, KV head): per dim the min and max over the block's
