@@ -226,6 +226,28 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
   const uint16_t* Kg = p.k_cache + size_t(g) * p.n_cap * D + 8 * r;
   const uint16_t* Vg = p.v_cache + size_t(g) * p.n_cap * D + 8 * r;
 
+  // q (and for the appending work-group the current token's k, v) from the
+  // qkv GEMV chunk partials: their loads are issued first, since memory
+  // counters retire in order and the other loads below are not needed as soon
+  constexpr int QPT = (G * HALF + kAttnThreads - 1) / kAttnThreads;
+  Chunk8 cqa[QPT], cqb[QPT], cka, ckb, cvv;
+  const int kcol = p.n_heads * D + g * D, vcol = (p.n_heads + p.n_kv_heads) * D + g * D;
+  if constexpr (QM == Q_PARTIAL) {
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int e = min(tid + u * kAttnThreads, G * HALF - 1);
+      const int col = (g * G + e / HALF) * D + e % HALF;
+      chunk_load(cqa[u], p.qkv_partial, p.qkv_splits, p.qkv_out, col);
+      chunk_load(cqb[u], p.qkv_partial, p.qkv_splits, p.qkv_out, col + HALF);
+    }
+    if (appends) {
+      const int ih = min(tid, HALF - 1), id = min(tid, D - 1);
+      chunk_load(cka, p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + ih);
+      chunk_load(ckb, p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + ih + HALF);
+      chunk_load(cvv, p.qkv_partial, p.qkv_splits, p.qkv_out, vcol + id);
+    }
+  }
+
   // the appending work-group refreshes the (min, max) summary of the
   // current token's block; the block's older rows are loaded now and used
   // at the end, so their latency hides under the main loop
@@ -234,10 +256,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
   uint32_t srow[8];
   if (refresh) {
     const uint16_t* kc = p.k_cache + size_t(g) * p.n_cap * D + tid;
+    // rows from pos on are replaced by the new row later; their loads read
+    // an older row (clamped index, no branches)
 #pragma unroll
     for (int t = 0; t < 16; t += 2) {
-      const uint32_t a = blk * 16 + t < p.pos ? kc[size_t(blk * 16 + t) * D] : 0u;
-      const uint32_t b = blk * 16 + t + 1 < p.pos ? kc[size_t(blk * 16 + t + 1) * D] : 0u;
+      const uint32_t a = kc[size_t(max(0, min(blk * 16 + t, p.pos - 1))) * D];
+      const uint32_t b = kc[size_t(max(0, min(blk * 16 + t + 1, p.pos - 1))) * D];
       srow[t / 2] = a | (b << 16);
     }
   }
@@ -271,40 +295,42 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
     for (int i = tid; i < G * D / 8; i += kAttnThreads)
       reinterpret_cast<uint4*>(&sm.q[0][0])[i] = reinterpret_cast<const uint4*>(p.q + size_t(g) * G * D)[i];
   } else {
-    // q: rotary pairs (i, i + D/2) of the group's heads, summed over the qkv
-    // GEMV chunks in chunk order, rounded to bf16
-    for (int e = tid; e < G * HALF; e += kAttnThreads) {
+    // rotary pairs (i, i + D/2) of the group's heads, chunks added in chunk
+    // order, rounded to bf16
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int e = tid + u * kAttnThreads;
+      if (e >= G * HALF) continue;
       const int j = e / HALF, i = e % HALF;
       const int col = (g * G + j) * D + i;
-      const float a = chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, col);
-      const float b = chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, col + HALF);
+      const float qa = chunk_total(cqa[u], p.qkv_partial, p.qkv_splits, p.qkv_out, col);
+      const float qb = chunk_total(cqb[u], p.qkv_partial, p.qkv_splits, p.qkv_out, col + HALF);
       const float cs = p.rope.c[i], sn = p.rope.s[i];
-      const uint16_t qa = f32_to_bf16(a * cs - b * sn), qb = f32_to_bf16(b * cs + a * sn);
-      sm.q[j][i] = qa;
-      sm.q[j][i + HALF] = qb;
+      const uint16_t q0 = f32_to_bf16(qa * cs - qb * sn), q1 = f32_to_bf16(qb * cs + qa * sn);
+      sm.q[j][i] = q0;
+      sm.q[j][i + HALF] = q1;
       if (s == 0 && p.q_out) {
-        p.q_out[size_t(g * G + j) * D + i] = qa;
-        p.q_out[size_t(g * G + j) * D + i + HALF] = qb;
+        p.q_out[size_t(g * G + j) * D + i] = q0;
+        p.q_out[size_t(g * G + j) * D + i + HALF] = q1;
       }
     }
     if (appends) {
-      const int kcol = p.n_heads * D + g * D, vcol = (p.n_heads + p.n_kv_heads) * D + g * D;
       uint16_t* kr = p.k_cache + (size_t(g) * p.n_cap + p.pos) * D;
       uint16_t* vr = p.v_cache + (size_t(g) * p.n_cap + p.pos) * D;
-      for (int i = tid; i < HALF; i += kAttnThreads) {
-        const float a = chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + i);
-        const float b = chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + i + HALF);
-        const float cs = p.rope.c[i], sn = p.rope.s[i];
-        const uint16_t ka = f32_to_bf16(a * cs - b * sn), kb = f32_to_bf16(b * cs + a * sn);
-        sm.knew[i] = ka;
-        sm.knew[i + HALF] = kb;
-        kr[i] = ka;
-        kr[i + HALF] = kb;
+      if (tid < HALF) {
+        const float ka = chunk_total(cka, p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + tid);
+        const float kb = chunk_total(ckb, p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + tid + HALF);
+        const float cs = p.rope.c[tid], sn = p.rope.s[tid];
+        const uint16_t k0 = f32_to_bf16(ka * cs - kb * sn), k1 = f32_to_bf16(kb * cs + ka * sn);
+        sm.knew[tid] = k0;
+        sm.knew[tid + HALF] = k1;
+        kr[tid] = k0;
+        kr[tid + HALF] = k1;
       }
-      for (int i = tid; i < D; i += kAttnThreads) {
-        const uint16_t v = f32_to_bf16(chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, vcol + i));
-        sm.vnew[i] = v;
-        vr[i] = v;
+      if (tid < D) {
+        const uint16_t v0 = f32_to_bf16(chunk_total(cvv, p.qkv_partial, p.qkv_splits, p.qkv_out, vcol + tid));
+        sm.vnew[tid] = v0;
+        vr[tid] = v0;
       }
     }
   }

@@ -156,20 +156,40 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 // ------------------------------------------------------- split partials
 // Sum of the n_splits chunk partials of column c, in chunk order.  Up to 8
 // chunks are loaded at once (one memory round trip for the usual plans).
+// Loads use clamped indices (no branches), so the loads of several
+// chunk_sum calls can all be in flight together.
 __device__ __forceinline__ float chunk_sum(const float* partial, int n_splits, int d_out, int c) {
   float v = 0.f;
-  int s = 0;
-  for (; s < n_splits; s += 8) {
+  for (int s = 0; s < n_splits; s += 8) {
     float a[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) a[u] = s + u < n_splits ? partial[size_t(s + u) * d_out + c] : 0.f;
+    for (int u = 0; u < 8; ++u) a[u] = partial[size_t(min(s + u, n_splits - 1)) * d_out + c];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (s + u < n_splits) v += a[u];
+    for (int u = 0; u < 8; ++u) v = s + u < n_splits ? v + a[u] : v;
   }
   return v;
 }
 
+
+// The same sum split in two, so that other loads can be issued between the
+// loads and the sum (memory counters retire in order): chunk_load issues the
+// first 8 chunk loads, chunk_total adds them (and any later chunks) in chunk
+// order -- the result equals chunk_sum's.
+struct Chunk8 {
+  float a[8];
+};
+__device__ __forceinline__ void chunk_load(Chunk8& c, const float* partial, int n_splits, int d_out, int col) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) c.a[u] = partial[size_t(min(u, n_splits - 1)) * d_out + col];
+}
+__device__ __forceinline__ float chunk_total(const Chunk8& c, const float* partial, int n_splits, int d_out,
+                                             int col) {
+  float v = 0.f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) v = u < n_splits ? v + c.a[u] : v;
+  for (int s = 8; s < n_splits; ++s) v += partial[size_t(s) * d_out + col];
+  return v;
+}
 
 // ------------------------------------------------------ block top-k select
 // Keys are staged in LDS when they fit (kTopkLdsBytes); larger inputs read

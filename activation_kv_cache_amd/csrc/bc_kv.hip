@@ -28,7 +28,7 @@ namespace bc {
 
 namespace {
 
-constexpr int kScoreThreads = 256;
+constexpr int kScoreThreads = 1024;
 constexpr int kScoreBlocksPerGroup = 128;
 constexpr int kSelThreads = 1024;
 constexpr int kSelMaxCand = kSelThreads * 32;
@@ -43,74 +43,97 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
   constexpr int P = D / 4;            // lanes per candidate block
   constexpr int CPW = kWave / P;      // candidate blocks per wave load
   constexpr int HALF = D / 2;
+  constexpr int NIT = kScoreBlocksPerGroup / ((kScoreThreads / kWave) * CPW);
   __shared__ uint16_t sq[G][D];
   __shared__ uint16_t knew[D];
   const int g = blockIdx.y;
   const int tid = threadIdx.x, lane = wave_lane(), w = wave_id();
   const int cs = lane / P, pp = lane % P;
   const int n_cand = p.bud.n_cand;
-
-  // every summary this wave scores is loaded up front (one round trip)
-  constexpr int NIT = kScoreBlocksPerGroup / ((kScoreThreads / kWave) * CPW);
+  const bool first = QP && blockIdx.x == 0;
+  // loads in the order they are needed (memory counters retire in order):
+  // the qkv chunk partials (QP), the current block's older rows (first
+  // group), then every summary this wave scores
+  constexpr int QPT = (G * HALF + kScoreThreads - 1) / kScoreThreads;
+  Chunk8 cqa[QPT], cqb[QPT], cka, ckb, cvv;
+  const int kcol = p.n_heads * D + g * D, vcol = (p.n_heads + p.n_kv_heads) * D + g * D;
+  if constexpr (QP) {
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int e = min(tid + u * kScoreThreads, G * HALF - 1);
+      const int col = (g * G + e / HALF) * D + e % HALF;
+      chunk_load(cqa[u], p.qkv_partial, p.qkv_splits, p.qkv_out, col);
+      chunk_load(cqb[u], p.qkv_partial, p.qkv_splits, p.qkv_out, col + HALF);
+    }
+    if (first) {
+      const int ih = min(tid, HALF - 1), id = min(tid, D - 1);
+      chunk_load(cka, p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + ih);
+      chunk_load(ckb, p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + ih + HALF);
+      chunk_load(cvv, p.qkv_partial, p.qkv_splits, p.qkv_out, vcol + id);
+    }
+  }
+  const int blk = p.pos / 16;
+  uint32_t srow[8];
+  if (first && p.summary && tid < D) {
+    const uint16_t* kc = p.k_cache + size_t(g) * p.n_cap * D + tid;
+    // rows from pos on are replaced by the new row later; their loads read
+    // an older row (clamped index, no branches)
+#pragma unroll
+    for (int t = 0; t < 16; t += 2) {
+      const uint32_t a = kc[size_t(max(0, min(blk * 16 + t, p.pos - 1))) * D];
+      const uint32_t b = kc[size_t(max(0, min(blk * 16 + t + 1, p.pos - 1))) * D];
+      srow[t / 2] = a | (b << 16);
+    }
+  }
   const int cbeg = blockIdx.x * kScoreBlocksPerGroup;
   const int cend = min(n_cand, cbeg + kScoreBlocksPerGroup);
   const uint16_t* sg = p.summary + size_t(g) * p.nb_cap * D * 2;
   uint4 mm[NIT];
   if (p.bud.k_blk > 0) {
+    // candidates past the group's end re-read its first block (discarded)
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int c = cbeg + (it * (kScoreThreads / kWave) + w) * CPW + cs;
       const int b = p.bud.b_lo + (c < cend ? c : cbeg);
-      mm[it] = c < cend || cbeg < cend ? *reinterpret_cast<const uint4*>(sg + (size_t(b) * D + 4 * pp) * 2)
-                                       : make_uint4(0u, 0u, 0u, 0u);
+      mm[it] = *reinterpret_cast<const uint4*>(sg + (size_t(b) * D + 4 * pp) * 2);
     }
   }
 
   float qf[G][4];
   if constexpr (QP) {
-    const bool first = blockIdx.x == 0;
-    // the current block's older rows, for its summary (first group only)
-    const int blk = p.pos / 16;
-    uint32_t srow[8];
-    if (first && p.summary && tid < D) {
-      const uint16_t* kc = p.k_cache + size_t(g) * p.n_cap * D + tid;
+    // q: rotary pairs, chunks added in chunk order, bf16; the first group
+    // also stores q, appends k, v and refreshes the current block's summary
 #pragma unroll
-      for (int t = 0; t < 16; t += 2) {
-        const uint32_t a = blk * 16 + t < p.pos ? kc[size_t(blk * 16 + t) * D] : 0u;
-        const uint32_t b = blk * 16 + t + 1 < p.pos ? kc[size_t(blk * 16 + t + 1) * D] : 0u;
-        srow[t / 2] = a | (b << 16);
-      }
-    }
-    for (int e = tid; e < G * HALF; e += kScoreThreads) {
+    for (int u = 0; u < QPT; ++u) {
+      const int e = tid + u * kScoreThreads;
+      if (e >= G * HALF) continue;
       const int j = e / HALF, i = e % HALF;
       const int col = (g * G + j) * D + i;
-      const float a = chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, col);
-      const float b = chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, col + HALF);
+      const float qa = chunk_total(cqa[u], p.qkv_partial, p.qkv_splits, p.qkv_out, col);
+      const float qb = chunk_total(cqb[u], p.qkv_partial, p.qkv_splits, p.qkv_out, col + HALF);
       const float c = p.rope.c[i], sn = p.rope.s[i];
-      const uint16_t qa = f32_to_bf16(a * c - b * sn), qb = f32_to_bf16(b * c + a * sn);
-      sq[j][i] = qa;
-      sq[j][i + HALF] = qb;
+      const uint16_t q0 = f32_to_bf16(qa * c - qb * sn), q1 = f32_to_bf16(qb * c + qa * sn);
+      sq[j][i] = q0;
+      sq[j][i + HALF] = q1;
       if (first) {
-        p.q_out[size_t(g * G + j) * D + i] = qa;
-        p.q_out[size_t(g * G + j) * D + i + HALF] = qb;
+        p.q_out[size_t(g * G + j) * D + i] = q0;
+        p.q_out[size_t(g * G + j) * D + i + HALF] = q1;
       }
     }
     if (first) {
-      const int kcol = p.n_heads * D + g * D, vcol = (p.n_heads + p.n_kv_heads) * D + g * D;
       uint16_t* kr = p.k_cache + (size_t(g) * p.n_cap + p.pos) * D;
       uint16_t* vr = p.v_cache + (size_t(g) * p.n_cap + p.pos) * D;
-      for (int i = tid; i < HALF; i += kScoreThreads) {
-        const float a = chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + i);
-        const float b = chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + i + HALF);
-        const float c = p.rope.c[i], sn = p.rope.s[i];
-        const uint16_t ka = f32_to_bf16(a * c - b * sn), kb = f32_to_bf16(b * c + a * sn);
-        knew[i] = ka;
-        knew[i + HALF] = kb;
-        kr[i] = ka;
-        kr[i + HALF] = kb;
+      if (tid < HALF) {
+        const float ka = chunk_total(cka, p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + tid);
+        const float kb = chunk_total(ckb, p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + tid + HALF);
+        const float c = p.rope.c[tid], sn = p.rope.s[tid];
+        const uint16_t k0 = f32_to_bf16(ka * c - kb * sn), k1 = f32_to_bf16(kb * c + ka * sn);
+        knew[tid] = k0;
+        knew[tid + HALF] = k1;
+        kr[tid] = k0;
+        kr[tid + HALF] = k1;
       }
-      for (int i = tid; i < D; i += kScoreThreads)
-        vr[i] = f32_to_bf16(chunk_sum(p.qkv_partial, p.qkv_splits, p.qkv_out, vcol + i));
+      if (tid < D) vr[tid] = f32_to_bf16(chunk_total(cvv, p.qkv_partial, p.qkv_splits, p.qkv_out, vcol + tid));
     }
     __syncthreads();
     if (first && p.summary && tid < D) {
@@ -173,7 +196,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
     v = v + dpp_f<kDppXor2>(v);
     v = v + dpp_f<kDppHalfMirror>(v);
     v = v + dpp_f<kDppMirror>(v);
-    if constexpr (P == 32) v = v + __shfl_xor(v, 16, kWave);
+    if constexpr (P == 32) v = v + lane_xor<16>(v);
     if (valid && pp == 0) p.scores[size_t(g) * p.scores_stride + c] = v;
   }
 }
