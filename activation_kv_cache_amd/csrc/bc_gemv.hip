@@ -6,10 +6,12 @@
 // W^T is [d_in][d_out] bf16: the weights of one input channel are one row,
 // stored tile-major (128-column tiles, each tile's rows contiguous).  A
 // work-group owns one 128-column tile of y and one chunk of list positions.
-// Its 512 lanes form 32 row slots of 16 lanes; a slot reads a row's 256 B
-// with one 16-byte load per lane.  Each slot keeps a ring of 8 rows in flight
+// Its 1024 lanes form 64 row slots of 16 lanes; a slot reads a row's 256 B
+// with one 16-byte load per lane.  Each slot keeps a ring of 4 rows in flight
 // (64 KB per work-group), issued as non-temporal loads: the weights are read
 // once per step and should not evict the small vectors the kernels share.
+// Sixteen waves (four per SIMD) also split the prologue's selection work
+// finely and hide its LDS and memory latency.
 //
 // The prologue forms the input.  IN_NORM computes x = RMSNorm(h) * gain and
 // IN_SEL takes x as given; with k < d_in both then select the exact top-k of
@@ -33,9 +35,10 @@ namespace bc {
 
 namespace {
 
-constexpr int kSlots = kGemvThreads / 16;   // 32 row slots of 16 lanes
-constexpr int kRing = 8;                    // rows in flight per slot
-constexpr int kNW = kGemvThreads / kWave;   // 8 waves
+constexpr int kSlots = kGemvThreads / 16;   // 64 row slots of 16 lanes
+constexpr int kRing = 4;                    // rows in flight per slot
+constexpr int kNW = kGemvThreads / kWave;   // 16 waves
+constexpr int kRedQ = kGemvThreads / kGemvTile;   // slot groups in the epilogue sum
 constexpr int kTopkShift = 3;               // first selection pass: 4096 bins
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -48,7 +51,7 @@ struct GemvSmem {
     } list;
     float red[kSlots][kGemvTile];  // per-slot sums (after the row loop)
   };
-  float red2[4][kGemvTile];
+  float red2[kRedQ][kGemvTile];
   Topk2Smem<kGemvThreads, kTopkShift> tk;
   float part[kNW];
   float amax_v[kNW];
@@ -230,14 +233,19 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
   }
   __syncthreads();
   {
-    const int c = tid & (kGemvTile - 1), q = tid >> 7;
+    const int c = tid & (kGemvTile - 1), q = tid / kGemvTile;
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < kSlots / 4; ++i) s += sm.red[(kSlots / 4) * q + i][c];
+    for (int i = 0; i < kSlots / kRedQ; ++i) s += sm.red[(kSlots / kRedQ) * q + i][c];
     sm.red2[q][c] = s;
   }
   __syncthreads();
-  auto col_sum = [&](int c) { return ((sm.red2[0][c] + sm.red2[1][c]) + sm.red2[2][c]) + sm.red2[3][c]; };
+  auto col_sum = [&](int c) {
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < kRedQ; ++q) v += sm.red2[q][c];
+    return v;
+  };
   if constexpr (OUT == OUT_PARTIAL) {
     if (tid < tile_w) p.partial[size_t(split) * p.d_out + tile * kGemvTile + tid] = col_sum(tid);
   } else if constexpr (OUT == OUT_BF16) {
@@ -508,10 +516,11 @@ int launch_gemv(int in, int out, const GemvParams& p, hipStream_t s) {
   if (in == IN_LIST) return launch_gemv_out<IN_LIST, 4>(out, p, grid, s);
   if (in != IN_NORM && in != IN_SEL) return set_error(BC_ERR_INVALID, "unknown GEMV input %d", in);
   if (!gemv_fused_input_ok(p.d_in)) return set_error(BC_ERR_UNSUPPORTED, "fused GEMV input d_in=%d", p.d_in);
-  const bool big = fused_per_thread(p.d_in) > 8;
+  static_assert(kGemvFusedMaxIn <= kGemvThreads * 16, "fused inputs fit 16 per thread");
+  const bool big = fused_per_thread(p.d_in) > 4;
   if (in == IN_NORM)
-    return big ? launch_gemv_out<IN_NORM, 32>(out, p, grid, s) : launch_gemv_out<IN_NORM, 8>(out, p, grid, s);
-  return big ? launch_gemv_out<IN_SEL, 32>(out, p, grid, s) : launch_gemv_out<IN_SEL, 8>(out, p, grid, s);
+    return big ? launch_gemv_out<IN_NORM, 16>(out, p, grid, s) : launch_gemv_out<IN_NORM, 4>(out, p, grid, s);
+  return big ? launch_gemv_out<IN_SEL, 16>(out, p, grid, s) : launch_gemv_out<IN_SEL, 4>(out, p, grid, s);
 }
 
 int finish_argmax_groups(int d_out) { return ceil_div(d_out, 256); }

@@ -28,7 +28,7 @@ struct RopeTable {
 void rope_table(int pos, double theta, int head_dim, RopeTable* t);
 
 constexpr int kGemvTile = 128;      // output columns per work-group (16 lanes x 8)
-constexpr int kGemvThreads = 512;   // 32 row slots of 16 lanes
+constexpr int kGemvThreads = 1024;  // 64 row slots of 16 lanes
 constexpr int kGemvMaxRows = 4096;  // rows (list positions) per work-group
 constexpr int kGemvFusedMaxIn = 16384;  // inputs a work-group normalises / selects itself
 

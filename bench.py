@@ -80,6 +80,30 @@ def step_bytes(n, r_p, r_kv, t_sel, S):
     return D["n_layers"] * layer_bytes(n, r_p, r_kv, t_sel, S) + 2 * D["d"] * D["vocab"] + 4 * D["vocab"]
 
 
+def n_star_k(r_p, r_kv, ext=False):
+    """Context (in units of 1024 tokens) at which skipping (1 - r_p) of the
+    projection weights and (1 - r_kv) of the K and V bytes save the same
+    bytes per step (README "Quick start" / "Usage": the byte crossover).
+    ext also charges the KV branch the block summaries it scores every step
+    (1/16 of the K and V bytes)."""
+    D = DIMS
+    kvd = D["n_kv_heads"] * D["head_dim"]
+    w_proj = 2 * D["n_layers"] * (2 * D["d"] ** 2 + 2 * D["d"] * kvd + 3 * D["d"] * D["d_ff"])
+    kv_per_token = 2 * 2 * D["n_layers"] * kvd
+    return (1 - r_p) * w_proj / ((1 - r_kv - (1.0 / 16 if ext else 0.0)) * kv_per_token) / 1024
+
+
+def crossing_k(contexts, d_vals):
+    """Where d = S_proj - S_kv changes sign from + to -: the last context with
+    d > 0 and the next one, interpolated linearly (in units of 1024 tokens);
+    None when d never turns negative after being positive."""
+    for i in range(len(contexts) - 1):
+        if d_vals[i] > 0 and d_vals[i + 1] <= 0 and all(x > 0 for x in d_vals[:i + 1]):
+            na, nb, da, db = contexts[i], contexts[i + 1], d_vals[i], d_vals[i + 1]
+            return (na + (nb - na) * da / (da - db)) / 1024
+    return None
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -396,6 +420,46 @@ def cpu_baseline(model, n):
                       f"{reps} run(s) in {elapsed:.1f}s; GB/s = that layer's algorithmic bytes / oracle time"}
 
 
+SWEEP_MODES = {"dense": (1.0, 1.0), "proj0.7": (0.7, 1.0), "proj0.5": (0.5, 1.0), "kv0.3": (1.0, 0.3),
+               "kv0.5": (1.0, 0.5), "both0.7/0.3": (0.7, 0.3), "both0.5/0.3": (0.5, 0.3), "both0.5/0.5": (0.5, 0.5)}
+PAIRS = (("proj0.7", "kv0.3", 0.7, 0.3), ("proj0.5", "kv0.3", 0.5, 0.3), ("proj0.5", "kv0.5", 0.5, 0.5))
+
+
+def crossover_sweep(model, contexts, blocks, steps, warmup, seed=0):
+    """Every mode at every context, `blocks` times in a shuffled order; the
+    speedups S = t_dense / t_mode are paired within a block (README
+    "Reproduce": paired blocks), averaged over blocks, and each (r_p, r_kv)
+    pair's crossing of S_proj and S_kv is compared with the byte-account n*."""
+    rng = np.random.default_rng(seed)
+    cells = [(m, n) for m in SWEEP_MODES for n in contexts]
+    t = {m: np.zeros((blocks, len(contexts))) for m in SWEEP_MODES}
+    for b in range(blocks):
+        order = rng.permutation(len(cells))
+        for ci in order:
+            m, n = cells[ci]
+            r_p, r_kv = SWEEP_MODES[m]
+            g = model.graph(n, r_p, r_kv)
+            t[m][b, contexts.index(n)] = time_graph(g, steps, warmup) * 1000.0
+            del g
+        log(f"[bench] crossover block {b + 1}/{blocks} done")
+    sp = {m: (t["dense"] / t[m]).mean(axis=0) for m in SWEEP_MODES}
+    out = {"contexts": contexts, "blocks": blocks, "steps": steps,
+           "step_us": {m: [round(x, 1) for x in t[m].mean(axis=0)] for m in SWEEP_MODES},
+           "speedup": {m: [round(x, 4) for x in sp[m]] for m in SWEEP_MODES if m != "dense"}, "pairs": {}}
+    for mp, mk, r_p, r_kv in PAIRS:
+        d_vals = [float(x) for x in (t["dense"] / t[mp] - t["dense"] / t[mk]).mean(axis=0)]
+        c = crossing_k(contexts, d_vals)
+        ns, nx = n_star_k(r_p, r_kv), n_star_k(r_p, r_kv, ext=True)
+        out["pairs"][f"{r_p}/{r_kv}"] = {
+            "n_star_k": round(ns, 2), "n_star_ext_k": round(nx, 2),
+            "measured_k": None if c is None else round(c, 2),
+            "measured_minus_n_star_k": None if c is None else round(c - ns, 2),
+            "measured_minus_n_star_ext_k": None if c is None else round(c - nx, 2)}
+        log(f"[bench] crossing {r_p}/{r_kv}: measured {c if c is None else round(c, 1)}K, "
+            f"n* {ns:.1f}K, n*_ext {nx:.1f}K")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -408,6 +472,9 @@ def main():
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="only copy this many bytes 5 times (calibration of the HBM byte counters)")
     ap.add_argument("--split-sweep", default="", help="attention split counts to sweep in --kernels")
+    ap.add_argument("--crossover-blocks", type=int, default=1,
+                    help="blocks of the crossover sweep (every mode at 2K, 4K, ..., 128K); 0 skips it")
+    ap.add_argument("--crossover-steps", type=int, default=10, help="timed steps per sweep cell")
     ap.add_argument("--attn-only", type=int, default=0,
                     help="only launch the dense attention kernel this many times per layer (for counters)")
     args = ap.parse_args()
@@ -444,12 +511,11 @@ def main():
         print(json.dumps({"attn_us": us, "attn_bytes": b, "splits": S}))
         return
 
+    # the dense step at each context (the headline is the largest); the
+    # other modes are timed by the crossover sweep
     cells = [(1.0, 1.0, n) for n in contexts]
-    if args.cells == "default":
-        small = [n for n in contexts if n <= 8192]
-        cells += [(1.0, rkv, n) for rkv in (0.3, 0.5) for n in contexts]
-        cells += [(rp, 1.0, n) for rp in (0.7, 0.5) for n in small]
-        cells += [(rp, rkv, n) for rp, rkv in ((0.7, 0.3), (0.5, 0.3), (0.5, 0.5)) for n in contexts]
+    if args.cells in ("default", "dense"):
+        pass
     elif args.cells == "none":
         cells = [(1.0, 1.0, head_n)]
     elif args.cells != "dense":
@@ -514,6 +580,10 @@ def main():
                                       "frac": round(gemv_sp_b / gemv_sp_us / 1e3 / HBM_PEAK_GBS, 4)}},
         "cells": results,
     }
+    if args.cells == "default" and args.crossover_blocks > 0 and head_n >= 131072:
+        sweep_ctx = [2048] + [4096 * i for i in range(1, 33)]
+        out["crossover"] = crossover_sweep(model, sweep_ctx, args.crossover_blocks, args.crossover_steps,
+                                           min(args.warmup, 3))
     if not args.no_cpu_baseline:
         try:
             out["cpu_baseline"] = cpu_baseline(model, head_n)
