@@ -534,18 +534,24 @@ __device__ void block_topk(int n, int k, KeyFn key_fn, EmitFn emit, TopkSmem<NT,
 // Exact top-k of n keys below 2^15 held in registers by NT threads: thread t
 // owns positions [t*P, t*P + P) (positions >= n are ignored), so a thread's
 // keys are in position order.  Pass 1 histograms the top 15-SHIFT key bits
-// (LDS atomics) and a block scan taken from the largest bin down finds the
-// bin holding the k-th largest key; pass 2 histograms the low SHIFT bits of
-// the keys in that bin.  That fixes the threshold key thr and the number
-// `need` of keys equal to thr that are kept (the lowest positions).  One
-// block scan of (ties, greater) counts per thread gives each thread the rank
-// of its first kept key; ranks within the thread come from popcounts of the
-// kept-key bit mask, so no thread walks its keys serially.  emit(rank, e) is
-// called for the thread's e-th key when it is kept and its rank is in
-// [r0, r1), or for every kept key when `all`.  Requires 1 <= k <= n <=
-// NT * PMAX, PMAX <= 32, n < 65536 (the scan packs two 16-bit counts).
-// Contains __syncthreads(); the caller synchronises before reading what emit
-// wrote.
+// (LDS atomics); the bin holding the k-th largest key is found from per-wave
+// totals and a scan inside the one wave whose bins cross k.  Pass 2
+// histograms the low SHIFT bits of the keys in that bin.  That fixes the
+// threshold key thr and the number `need` of keys equal to thr that are kept
+// (the lowest positions).  One block scan of (ties, greater) counts per
+// thread gives each thread the rank of its first kept key; ranks within the
+// thread come from popcounts of the kept-key bit mask, so no thread walks its
+// keys serially.  emit(rank, e) is called for the thread's e-th key when it
+// is kept and its rank is in [r0, r1), or for every kept key when `all`.
+//
+// All NT threads execute every instruction of the block-wide steps, so the
+// searches over wave totals and over the low digit run lane-parallel (one
+// value per lane, a 16-lane DPP scan, a ballot) instead of as per-thread
+// loops.  The caller zeroes the histogram with topk2_clear() and passes a
+// __syncthreads() before the call (so the clear can overlap its own loads).
+// Requires 1 <= k <= n <= NT * PMAX, PMAX <= 32, NT <= 16 waves, n < 65536
+// (the rank scan packs two 16-bit counts).  Contains __syncthreads(); the
+// caller synchronises before reading what emit wrote.
 template <int NT, int SHIFT>
 struct Topk2Smem {
   static constexpr int NB = 32768 >> SHIFT;
@@ -555,24 +561,50 @@ struct Topk2Smem {
   uint32_t b1, above1;
 };
 
+template <int NT, int SHIFT>
+__device__ __forceinline__ void topk2_clear(Topk2Smem<NT, SHIFT>& sm) {
+  constexpr int NQ = Topk2Smem<NT, SHIFT>::NB / 4;
+  static_assert(NQ % NT == 0, "whole uint4 of bins per thread");
+  uint4* h4 = reinterpret_cast<uint4*>(sm.hist);
+#pragma unroll
+  for (int i = 0; i < NQ / NT; ++i) h4[threadIdx.x + i * NT] = make_uint4(0u, 0u, 0u, 0u);
+  if (threadIdx.x < (1 << SHIFT)) sm.hist2[threadIdx.x] = 0u;
+}
+
+// Inclusive prefix sum within each 16-lane row.
+__device__ __forceinline__ uint32_t row16_scan(uint32_t v) {
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x111, 0xF, 0xF, true));   // row_shr:1
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x112, 0xF, 0xF, true));   // row_shr:2
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x114, 0xF, 0xF, true));   // row_shr:4
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x118, 0xF, 0xF, true));   // row_shr:8
+  return v;
+}
+
+// Sum of wave totals tot[0..w) for the calling wave w (w uniform, NW <= 16):
+// lane l holds tot[l], one row scan, one readlane.
+template <int NW>
+__device__ __forceinline__ uint32_t waves_before(const uint32_t* tot, int w) {
+  static_assert(NW <= 16, "one DPP row");
+  const int lane = threadIdx.x & 63;
+  const uint32_t inc = row16_scan(lane < NW ? tot[lane] : 0u);
+  return w == 0 ? 0u : uint32_t(__builtin_amdgcn_readlane(int(inc), w - 1));
+}
+
 template <int NT, int SHIFT, int PMAX, typename EmitFn>
 __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int k, int r0, int r1, bool all,
                                  EmitFn emit, Topk2Smem<NT, SHIFT>& sm) {
   static_assert(PMAX <= 32, "bit masks are 32 bits");
   constexpr int NB = Topk2Smem<NT, SHIFT>::NB;
   constexpr int NB2 = 1 << SHIFT;
-  static_assert(NB % (4 * NT) == 0, "whole uint4 of bins per thread");
+  static_assert(NB2 <= 16, "low digit found in one DPP row");
   constexpr int NW = NT / kWave;
+  static_assert(NW <= 16, "wave totals found in one DPP row");
   constexpr int BPT = NB / NT;  // bins per thread
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  static_assert(BPT % 4 == 0, "whole uint4 of bins per thread");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nv = max(0, min(P, n - tid * P));
-  {
-    uint4* h4 = reinterpret_cast<uint4*>(sm.hist);
-#pragma unroll
-    for (int i = 0; i < BPT / 4; ++i) h4[tid + i * NT] = make_uint4(0u, 0u, 0u, 0u);
-  }
-  if (tid < NB2) sm.hist2[tid] = 0;
-  __syncthreads();
+  const uint32_t ku = uint32_t(k);
 #pragma unroll
   for (int e = 0; e < PMAX; ++e) {
     const bool ok = e < nv;
@@ -580,7 +612,8 @@ __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int 
   }
   __syncthreads();
   // thread t owns bins [b0, b0 + BPT), b0 = NB - BPT (t + 1): the largest
-  // bins go to thread 0, so the prefix over threads counts larger keys
+  // bins go to thread 0, so counts accumulated over threads in order count
+  // larger keys
   const int b0 = NB - BPT * (tid + 1);
   uint32_t bins[BPT];
   uint32_t local = 0;
@@ -596,18 +629,22 @@ __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int 
   const uint32_t winc = wave_scan_dpp(local);
   if (lane == kWave - 1) sm.wtot[w] = winc;
   __syncthreads();
-  uint32_t before = 0;
-#pragma unroll
-  for (int ww = 0; ww < NW; ++ww) before += ww < w ? sm.wtot[ww] : 0u;
-  const uint32_t ku = uint32_t(k);
   {
-    const uint32_t inc = before + winc, ex = inc - local;
-    if (ex < ku && ku <= inc) {
-      uint32_t run = ex;
+    // the wave whose bins hold the k-th largest key (lane-parallel search)
+    const uint32_t c = lane < NW ? sm.wtot[lane] : 0u;
+    const uint32_t inc = row16_scan(c), ex = inc - c;
+    const uint64_t hitw = __ballot(lane < NW && ex < ku && ku <= inc);
+    const int ws = __ffsll((long long)hitw) - 1;
+    if (w == ws) {
+      const uint32_t above_w = uint32_t(__builtin_amdgcn_readlane(int(ex), ws));
+      const uint32_t tinc = above_w + winc, tex = tinc - local;
+      if (tex < ku && ku <= tinc) {
+        uint32_t run = tex;
 #pragma unroll
-      for (int j = BPT - 1; j >= 0; --j) {
-        if (run < ku && ku <= run + bins[j]) { sm.b1 = uint32_t(b0 + j); sm.above1 = run; }
-        run += bins[j];
+        for (int j = BPT - 1; j >= 0; --j) {
+          if (run < ku && ku <= run + bins[j]) { sm.b1 = uint32_t(b0 + j); sm.above1 = run; }
+          run += bins[j];
+        }
       }
     }
   }
@@ -617,18 +654,16 @@ __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int 
   for (int e = 0; e < PMAX; ++e)
     if (e < nv && (key[e] >> SHIFT) == b1) atomicAdd(&sm.hist2[key[e] & uint32_t(NB2 - 1)], 1u);
   __syncthreads();
-  uint32_t h2[NB2];
-#pragma unroll
-  for (int j = 0; j < NB2; ++j) h2[j] = sm.hist2[j];
-  uint32_t run = 0, b2 = 0, above2 = 0;
-#pragma unroll
-  for (int j = NB2 - 1; j >= 0; --j) {
-    const bool hit = run < k2 && k2 <= run + h2[j];
-    b2 = hit ? uint32_t(j) : b2;
-    above2 = hit ? run : above2;
-    run += h2[j];
+  uint32_t thr, need;
+  {
+    // low digit, largest first: lane l holds digit NB2-1-l
+    const uint32_t c = lane < NB2 ? sm.hist2[NB2 - 1 - lane] : 0u;
+    const uint32_t inc = row16_scan(c), ex = inc - c;
+    const uint64_t hit = __ballot(lane < NB2 && ex < k2 && k2 <= inc);
+    const int hl = __ffsll((long long)hit) - 1;
+    thr = (b1 << SHIFT) | uint32_t(NB2 - 1 - hl);
+    need = k2 - uint32_t(__builtin_amdgcn_readlane(int(ex), hl));
   }
-  const uint32_t thr = (b1 << SHIFT) | b2, need = k2 - above2;
   uint32_t gtm = 0, eqm = 0;
 #pragma unroll
   for (int e = 0; e < PMAX; ++e) {
@@ -644,9 +679,7 @@ __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int 
   const uint32_t inc = wave_scan_dpp(v);
   if (lane == kWave - 1) sm.wtot[w] = inc;
   __syncthreads();
-  uint32_t bf = inc - v;
-#pragma unroll
-  for (int ww = 0; ww < NW; ++ww) bf += ww < w ? sm.wtot[ww] : 0u;
+  const uint32_t bf = inc - v + waves_before<NW>(sm.wtot, w);
   const uint32_t gt_before = bf & 0xFFFFu, eq_before = bf >> 16;
   const uint32_t ties_before = eq_before < need ? eq_before : need;
   const uint32_t ties_here = (eq_before + eq < need ? eq_before + eq : need) - ties_before;

@@ -136,6 +136,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
       uint32_t gb[PMAX / 2];
       load_vec<PMAX>(p.h, c0, P, p.d_in, xb);
       load_vec<PMAX>(p.gain, c0, P, p.d_in, gb);
+      if (!dense) topk2_clear(sm.tk);   // while the loads are in flight; the barrier below covers it
       // sum of squares in a fixed order: the thread's channels in order, the
       // wave's fixed tree, then the waves in order (all work-groups agree)
       float ss = 0.f;
@@ -159,6 +160,10 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
       }
     } else {
       load_vec<PMAX>(p.x, c0, P, p.d_in, xb);
+      if (!dense) {
+        topk2_clear(sm.tk);
+        __syncthreads();
+      }
     }
     if (lead && p.x_out) {
 #pragma unroll
