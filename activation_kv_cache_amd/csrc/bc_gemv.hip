@@ -83,6 +83,44 @@ __device__ __forceinline__ void load_vec(const uint16_t* src, int c0, int P, int
   }
 }
 
+// h = bf16(sum of the chunk partials in chunk order + resid) for the thread's
+// channels [c0, c0 + P): the arithmetic of k_finish_resid, with every load
+// issued before the sums.  Channels past d_in give 0.
+template <int PMAX>
+__device__ __forceinline__ void sum_vec(const float* partial, int n_splits, const uint16_t* resid, int c0, int P,
+                                        int d_in, uint32_t (&dst)[PMAX / 2]) {
+  float4 a[PMAX / 4][8];
+  uint2 rv[PMAX / 4];
+#pragma unroll
+  for (int q = 0; q < PMAX / 4; ++q) {
+    const bool ok = 4 * q < P && c0 + 4 * q < d_in;
+    const int c = ok ? c0 + 4 * q : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      a[q][u] = *reinterpret_cast<const float4*>(partial + size_t(min(u, n_splits - 1)) * d_in + c);
+    rv[q] = *reinterpret_cast<const uint2*>(resid + c);
+  }
+#pragma unroll
+  for (int q = 0; q < PMAX / 4; ++q) {
+    const bool ok = 4 * q < P && c0 + 4 * q < d_in;
+    const int c = ok ? c0 + 4 * q : 0;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < n_splits) {
+        v.x += a[q][u].x; v.y += a[q][u].y; v.z += a[q][u].z; v.w += a[q][u].w;
+      }
+    }
+    for (int sp = 8; sp < n_splits; ++sp) {
+      const float4 b = *reinterpret_cast<const float4*>(partial + size_t(sp) * d_in + c);
+      v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+    }
+    v.x += bf16_lo(rv[q].x); v.y += bf16_hi(rv[q].x); v.z += bf16_lo(rv[q].y); v.w += bf16_hi(rv[q].y);
+    dst[2 * q] = ok ? (f32_to_bf16(v.x) | (uint32_t(f32_to_bf16(v.y)) << 16)) : 0u;
+    dst[2 * q + 1] = ok ? (f32_to_bf16(v.z) | (uint32_t(f32_to_bf16(v.w)) << 16)) : 0u;
+  }
+}
+
 template <int IN, int OUT, int PMAX>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
   __shared__ GemvSmem sm;
@@ -132,11 +170,20 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
     const int P = fused_per_thread(p.d_in);
     const int c0 = tid * P;
     uint32_t xb[PMAX / 2];
-    if constexpr (IN == IN_NORM) {
+    if constexpr (IN == IN_NORM || IN == IN_NORM_SUM) {
       uint32_t gb[PMAX / 2];
-      load_vec<PMAX>(p.h, c0, P, p.d_in, xb);
+      if constexpr (IN == IN_NORM) load_vec<PMAX>(p.h, c0, P, p.d_in, xb);
       load_vec<PMAX>(p.gain, c0, P, p.d_in, gb);
       if (!dense) topk2_clear(sm.tk);   // while the loads are in flight; the barrier below covers it
+      if constexpr (IN == IN_NORM_SUM) {
+        sum_vec<PMAX>(p.sum_partial, p.sum_splits, p.h, c0, P, p.d_in, xb);
+        if (lead && p.h_out) {
+#pragma unroll
+          for (int q = 0; q < PMAX / 4; ++q)
+            if (4 * q < P && c0 + 4 * q < p.d_in)
+              *reinterpret_cast<uint2*>(p.h_out + c0 + 4 * q) = make_uint2(xb[2 * q], xb[2 * q + 1]);
+        }
+      }
       // sum of squares in a fixed order: the thread's channels in order, the
       // wave's fixed tree, then the waves in order (all work-groups agree)
       float ss = 0.f;
@@ -494,6 +541,7 @@ GemvPlan plan_gemv(int d_out, int k, bool single) {
 }
 
 bool gemv_fused_input_ok(int d_in) { return d_in >= 1 && d_in % 4 == 0 && d_in <= kGemvFusedMaxIn; }
+bool gemv_sum_input_ok(int d_in) { return gemv_fused_input_ok(d_in) && fused_per_thread(d_in) <= 4; }
 
 namespace {
 template <int IN, int PMAX>
@@ -519,10 +567,15 @@ int launch_gemv(int in, int out, const GemvParams& p, hipStream_t s) {
     return set_error(BC_ERR_INVALID, "SwiGLU epilogue: tile count");
   const dim3 grid(p.n_tiles, p.n_splits);
   if (in == IN_LIST) return launch_gemv_out<IN_LIST, 4>(out, p, grid, s);
-  if (in != IN_NORM && in != IN_SEL) return set_error(BC_ERR_INVALID, "unknown GEMV input %d", in);
+  if (in != IN_NORM && in != IN_SEL && in != IN_NORM_SUM) return set_error(BC_ERR_INVALID, "unknown GEMV input %d", in);
   if (!gemv_fused_input_ok(p.d_in)) return set_error(BC_ERR_UNSUPPORTED, "fused GEMV input d_in=%d", p.d_in);
   static_assert(kGemvFusedMaxIn <= kGemvThreads * 16, "fused inputs fit 16 per thread");
   const bool big = fused_per_thread(p.d_in) > 4;
+  if (in == IN_NORM_SUM) {
+    if (big || !p.sum_partial || !p.h || p.sum_splits < 1)
+      return set_error(BC_ERR_INVALID, "IN_NORM_SUM: d_in=%d, %d chunks", p.d_in, p.sum_splits);
+    return launch_gemv_out<IN_NORM_SUM, 4>(out, p, grid, s);
+  }
   if (in == IN_NORM)
     return big ? launch_gemv_out<IN_NORM, 16>(out, p, grid, s) : launch_gemv_out<IN_NORM, 4>(out, p, grid, s);
   return big ? launch_gemv_out<IN_SEL, 16>(out, p, grid, s) : launch_gemv_out<IN_SEL, 4>(out, p, grid, s);

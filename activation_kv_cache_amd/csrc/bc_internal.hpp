@@ -37,9 +37,14 @@ constexpr int kGemvFusedMaxIn = 16384;  // inputs a work-group normalises / sele
 //   IN_NORM  x = bf16(RMSNorm(h) * gain) is formed in the prologue, then
 //            (k < d_in) the exact top-k of |x| is selected there too;
 //   IN_SEL   x is given and (k < d_in) its top-k is selected in the prologue.
+//   IN_NORM_SUM  as IN_NORM, with h itself formed first from the fp32 chunk
+//            partials of the GEMV before it plus a residual:
+//            h = bf16(sum of chunks in chunk order + resid), the arithmetic
+//            of FIN_RESID; the first work-group stores h (h_out).  This folds
+//            a residual finish kernel into the next GEMV (d_in <= 4096).
 // Every work-group of a launch forms the same x and the same selection; the
 // first one also stores them (x_out, idx_out) when asked.
-enum GemvIn : int { IN_LIST = 0, IN_NORM = 1, IN_SEL = 2 };
+enum GemvIn : int { IN_LIST = 0, IN_NORM = 1, IN_SEL = 2, IN_NORM_SUM = 3 };
 // What the main kernel stores: fp32 partials per chunk of rows, or (one
 // chunk) bf16 y, the SwiGLU of a gate|up tile, or fp32 y + per-tile argmax.
 enum GemvOut : int { OUT_PARTIAL = 0, OUT_BF16 = 1, OUT_SWIGLU = 2, OUT_ARGMAX = 3 };
@@ -55,6 +60,7 @@ struct GemvPlan {
 // ARGMAX epilogues)
 GemvPlan plan_gemv(int d_out, int k, bool single = false);
 bool gemv_fused_input_ok(int d_in);
+bool gemv_sum_input_ok(int d_in);   // IN_NORM_SUM supports this d_in
 
 struct GemvParams {
   const uint16_t* wt;
@@ -62,8 +68,11 @@ struct GemvParams {
   int d_in, d_out;
   const uint16_t* x;      // IN_LIST, IN_SEL: bf16 [d_in]
   const int32_t* idx;     // IN_LIST: [k] or NULL
-  const uint16_t* h;      // IN_NORM: bf16 [d_in]
-  const uint16_t* gain;   // IN_NORM: bf16 [d_in]
+  const uint16_t* h;      // IN_NORM: bf16 [d_in]; IN_NORM_SUM: the residual
+  const uint16_t* gain;   // IN_NORM, IN_NORM_SUM: bf16 [d_in]
+  const float* sum_partial;   // IN_NORM_SUM: [sum_splits][d_in] fp32
+  int sum_splits;
+  uint16_t* h_out;        // IN_NORM_SUM: h (first work-group)
   float eps;
   uint16_t* x_out;        // IN_NORM / IN_SEL: optional copy of x (first work-group)
   int32_t* idx_out;       // IN_NORM / IN_SEL: optional copy of the selection

@@ -94,16 +94,21 @@ __global__ __launch_bounds__(256) void k_pack_tiles(const uint16_t* src, const u
 
 // ------------------------------------------------------------ layer layout
 struct LayerLayout {
-  size_t partial, x1, idx_qkv, q, scores, idx_kv, m, l, o, a, idx_o, h_mid, x2, idx_gu, hff, idx_down;
+  size_t partial, partial2, x1, idx_qkv, q, scores, idx_kv, m, l, o, a, idx_o, h_mid, x2, idx_gu, hff, idx_down;
   size_t total;
 };
 
-size_t gemv_partial_max(const bc_model_dims& m) {
+// Chunk partials: the q/k/v and gate|up GEMVs use one buffer, the o and
+// down GEMVs (whose partials the next GEMV's prologue folds into the
+// residual stream) another, so a prologue never reads a buffer its own
+// launch writes.
+size_t gemv_partial_max(const bc_model_dims& m, bool od) {
   const int qkv = m.n_heads * m.head_dim + 2 * m.n_kv_heads * m.head_dim;
   size_t mx = 0;
   const int outs[4] = {qkv, m.d, 2 * m.d_ff, m.d};
   const int ins[4] = {m.d, m.n_heads * m.head_dim, m.d, m.d_ff};
   for (int i = 0; i < 4; ++i) {
+    if (od != (i == 1 || i == 3)) continue;
     GemvPlan pl = plan_gemv(outs[i], ins[i], i == 2);
     if (pl.partial_bytes > mx) mx = pl.partial_bytes;
   }
@@ -116,7 +121,8 @@ LayerLayout layer_layout(const bc_model_dims& m, int n_ctx, int n_splits) {
   auto take = [&off](size_t bytes) { size_t o = off; off += align_up(bytes > 0 ? bytes : 1, 256); return o; };
   const int hd = m.head_dim, H = m.n_heads, Hkv = m.n_kv_heads;
   const int nb = (n_ctx + 15) / 16;
-  L.partial = take(gemv_partial_max(m));
+  L.partial = take(gemv_partial_max(m, false));
+  L.partial2 = take(gemv_partial_max(m, true));
   L.x1 = take(size_t(m.d) * 2);
   L.idx_qkv = take(size_t(m.d) * 4);
   L.q = take(size_t(H) * hd * 2);
@@ -228,14 +234,40 @@ namespace {
 
 // What a projection GEMV reads: IN_NORM forms x = RMSNorm(v) * gain, IN_SEL
 // takes x = v; with k < d_in the prologue also selects the top-k of |x|.
+// IN_NORM_SUM first forms v = bf16(chunk sums of sum_partial + resid) and
+// stores it at h_out.
 struct ProjIn {
   int mode;
-  const uint16_t* v;
+  const uint16_t* v;    // IN_NORM_SUM: the residual
   const uint16_t* gain;
   float eps;
   uint16_t* x_out;      // optional copy of x
   int32_t* idx_out;     // optional copy of the selection
+  const float* sum_partial = nullptr;
+  int sum_splits = 0;
+  uint16_t* h_out = nullptr;
 };
+
+// A hidden state not yet stored: h = bf16(chunk sums of partial + resid),
+// left by a GEMV for the next GEMV's prologue to form.
+struct Pending {
+  const float* partial;
+  int n_splits;
+  const uint16_t* resid;
+};
+
+ProjIn norm_input(const uint16_t* h, const Pending* pend, uint16_t* h_out, const uint16_t* gain, float eps,
+                  uint16_t* x_out, int32_t* idx_out) {
+  ProjIn in{IN_NORM, h, gain, eps, x_out, idx_out};
+  if (pend) {
+    in.mode = IN_NORM_SUM;
+    in.v = pend->resid;
+    in.sum_partial = pend->partial;
+    in.sum_splits = pend->n_splits;
+    in.h_out = h_out;
+  }
+  return in;
+}
 
 // One projection: main kernel and, with several chunks, its finish.  The
 // gate|up GEMV (FIN_SWIGLU) runs as one chunk per tile when it fits, with
@@ -248,8 +280,9 @@ int run_gemv(const uint16_t* wt, int d_in, int d_out, int k, const ProjIn& in, f
   if (n_splits) *n_splits = pl.n_splits;
   GemvParams p{};
   p.wt = wt; p.tiled = 1; p.d_in = d_in; p.d_out = d_out; p.k = k;
-  if (in.mode == IN_NORM) {
+  if (in.mode == IN_NORM || in.mode == IN_NORM_SUM) {
     p.h = in.v; p.gain = in.gain; p.eps = in.eps;
+    p.sum_partial = in.sum_partial; p.sum_splits = in.sum_splits; p.h_out = in.h_out;
   } else {
     p.x = in.v;
   }
@@ -268,22 +301,28 @@ int run_gemv(const uint16_t* wt, int d_in, int d_out, int k, const ProjIn& in, f
   return launch_finish(fin_kind, f, s);
 }
 
-// Final RMSNorm (in the GEMV prologue), dense LM head and argmax.
-int run_head(const bc_model_dims& m, const uint16_t* hidden, const uint16_t* g_final, const uint16_t* w_head,
-             float eps, float* logits, int32_t* token, float* partial, float* tile_max, int32_t* tile_arg,
-             hipStream_t s) {
+// Final RMSNorm (in the GEMV prologue), dense LM head and argmax.  With a
+// pending hidden state the prologue forms it first and stores it at hidden.
+int run_head(const bc_model_dims& m, uint16_t* hidden, const Pending* pend, const uint16_t* g_final,
+             const uint16_t* w_head, float eps, float* logits, int32_t* token, float* partial, float* tile_max,
+             int32_t* tile_arg, hipStream_t s) {
   const GemvPlan pl = plan_gemv(m.vocab, m.d, true);
   GemvParams p{};
   p.wt = w_head; p.tiled = 1; p.d_in = m.d; p.d_out = m.vocab; p.k = m.d;
   p.h = hidden; p.gain = g_final; p.eps = eps;
+  int in_mode = IN_NORM;
+  if (pend) {
+    in_mode = IN_NORM_SUM;
+    p.h = pend->resid; p.sum_partial = pend->partial; p.sum_splits = pend->n_splits; p.h_out = hidden;
+  }
   p.rows_per_split = pl.rows_per_split; p.n_splits = pl.n_splits; p.n_tiles = pl.n_tiles;
   p.yf = logits; p.tile_max = tile_max; p.tile_arg = tile_arg; p.partial = partial;
   int rc;
   if (pl.n_splits == 1) {
-    if ((rc = launch_gemv(IN_NORM, OUT_ARGMAX, p, s)) != BC_OK) return rc;
+    if ((rc = launch_gemv(in_mode, OUT_ARGMAX, p, s)) != BC_OK) return rc;
     return launch_argmax_finish(tile_max, tile_arg, pl.n_tiles, token, s);
   }
-  if ((rc = launch_gemv(IN_NORM, OUT_PARTIAL, p, s)) != BC_OK) return rc;
+  if ((rc = launch_gemv(in_mode, OUT_PARTIAL, p, s)) != BC_OK) return rc;
   FinishParams f{};
   f.partial = partial; f.n_splits = pl.n_splits; f.d_out = m.vocab;
   f.yf = logits; f.tile_max = tile_max; f.tile_arg = tile_arg;
@@ -333,8 +372,12 @@ int step_splits(const bc_model_dims& m, const bc_step* st, const bc_kv_budget_in
   return st->n_splits > 0 ? st->n_splits : bc_attn_default_splits(n_sel, m.n_kv_heads);
 }
 
+// One decoder layer.  pin: the layer's input is pending (formed by the q/k/v
+// GEMV's prologue, which stores it at hidden); pout: leave the output pending
+// (the down GEMV's chunk partials plus h1) instead of storing it at hidden.
 int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, const bc_kv_budget_info& bud,
-               int n_splits, uint16_t* hidden, void* ws, const LayerLayout& L, hipStream_t s) {
+               int n_splits, uint16_t* hidden, const Pending* pin, Pending* pout, void* ws, const LayerLayout& L,
+               hipStream_t s) {
   int rc;
   const int hd = m.head_dim, H = m.n_heads, Hkv = m.n_kv_heads;
   const bool kv_sparse = st->kv.r_kv < 1.0;
@@ -345,6 +388,7 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
   const int qkv_out = H * hd + 2 * Hkv * hd;
   const int pos = st->n_ctx - 1;
   float* partial = at<float>(ws, L.partial);
+  float* partial2 = at<float>(ws, L.partial2);
   const float eps = float(st->rms_eps);
   int32_t* idx_qkv = sparse ? at<int32_t>(ws, L.idx_qkv) : nullptr;
   int32_t* idx_o = sparse ? at<int32_t>(ws, L.idx_o) : nullptr;
@@ -360,7 +404,7 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
   // does that (unless the window is empty, when the current block may be a
   // candidate: then a finish kernel does it first), and every attention
   // work-group selects the blocks of its own slice of the list.
-  const ProjIn qkv_in{IN_NORM, hidden, ly->g_attn, eps, at<uint16_t>(ws, L.x1), idx_qkv};
+  const ProjIn qkv_in = norm_input(hidden, pin, hidden, ly->g_attn, eps, at<uint16_t>(ws, L.x1), idx_qkv);
   RopeTable rope;
   rope_table(pos, st->rope_theta, hd, &rope);
   int qkv_splits = 0;
@@ -419,28 +463,39 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
     if ((rc = launch_attn_reduce(r, s)) != BC_OK) return rc;
   }
 
-  // S2 = top-k(a) (GEMV prologue); h1 = h + W_o a
+  // S2 = top-k(a) (GEMV prologue); h1 = h + W_o a, left as chunk partials
+  // for the gate|up prologue when it can form h1 itself
+  const bool fold = gemv_sum_input_ok(m.d);
+  int o_splits = 0;
   {
     const ProjIn in{IN_SEL, a, nullptr, 0.f, nullptr, idx_o};
     FinishParams f{};
     f.y = h_mid; f.resid = hidden;
-    if ((rc = run_gemv(ly->w_o, H * hd, m.d, k_d, in, partial, FIN_RESID, f, s)) != BC_OK) return rc;
+    if ((rc = run_gemv(ly->w_o, H * hd, m.d, k_d, in, partial2, fold ? FIN_NONE : FIN_RESID, f, s, &o_splits)) !=
+        BC_OK)
+      return rc;
   }
 
   // x2 = RMSNorm(h1), S3 (GEMV prologue); f = SiLU(gate) * up
   {
-    const ProjIn in{IN_NORM, h_mid, ly->g_mlp, eps, at<uint16_t>(ws, L.x2), idx_gu};
+    const Pending h1{partial2, o_splits, hidden};
+    const ProjIn in = norm_input(h_mid, fold ? &h1 : nullptr, h_mid, ly->g_mlp, eps, at<uint16_t>(ws, L.x2), idx_gu);
     FinishParams f{};
     f.y = hff; f.d_ff = m.d_ff;
     if ((rc = run_gemv(ly->w_gu, m.d, 2 * m.d_ff, k_d, in, partial, FIN_SWIGLU, f, s)) != BC_OK) return rc;
   }
 
-  // S4 = top-k(f) (GEMV prologue); h = h1 + W_down f
+  // S4 = top-k(f) (GEMV prologue); h = h1 + W_down f, stored or left pending
   {
     const ProjIn in{IN_SEL, hff, nullptr, 0.f, nullptr, idx_down};
     FinishParams f{};
     f.y = hidden; f.resid = h_mid;
-    if ((rc = run_gemv(ly->w_down, m.d_ff, m.d, k_ff, in, partial, FIN_RESID, f, s)) != BC_OK) return rc;
+    const bool defer = pout != nullptr && fold;
+    int down_splits = 0;
+    if ((rc = run_gemv(ly->w_down, m.d_ff, m.d, k_ff, in, partial2, defer ? FIN_NONE : FIN_RESID, f, s,
+                       &down_splits)) != BC_OK)
+      return rc;
+    if (pout) *pout = defer ? Pending{partial2, down_splits, h_mid} : Pending{nullptr, 0, nullptr};
   }
 
   if (const bc_layer_taps* t = st->taps) {
@@ -489,7 +544,7 @@ extern "C" int bc_decode_layer(const bc_model_dims* dims, const bc_layer* ly, co
   const LayerLayout L = layer_layout(*dims, st->n_ctx, n_splits);
   if (ws_bytes < L.total) return set_error(BC_ERR_WORKSPACE, "bc_decode_layer: workspace %zu < %zu", ws_bytes, L.total);
   if (reinterpret_cast<uintptr_t>(ws) & 255) return set_error(BC_ERR_INVALID, "bc_decode_layer: ws not 256-byte aligned");
-  return layer_body(*dims, ly, st, bud, n_splits, hidden, ws, L, static_cast<hipStream_t>(stream));
+  return layer_body(*dims, ly, st, bud, n_splits, hidden, nullptr, nullptr, ws, L, static_cast<hipStream_t>(stream));
 }
 
 extern "C" size_t bc_step_workspace_bytes(const bc_model_dims* dims, int max_ctx, int max_splits) {
@@ -518,10 +573,18 @@ extern "C" int bc_decode_step(const bc_model_dims* dims, const bc_layer* layers,
   hipStream_t s = static_cast<hipStream_t>(stream);
   bc_step one = *st;
   one.taps = nullptr;
-  for (int i = 0; i < n_layers; ++i)
-    if ((rc = layer_body(m, &layers[i], &one, bud, n_splits, hidden, ws, S.layer, s)) != BC_OK) return rc;
-  return run_head(m, hidden, g_final, w_head, float(st->rms_eps), logits, token, at<float>(ws, S.head.partial),
-                  at<float>(ws, S.head.tile_max), at<int32_t>(ws, S.head.tile_arg), s);
+  // each layer's output stays pending (down partials + h1) until the next
+  // layer's q/k/v prologue, or the LM head's, forms and stores it
+  Pending pend{nullptr, 0, nullptr};
+  for (int i = 0; i < n_layers; ++i) {
+    Pending next{nullptr, 0, nullptr};
+    if ((rc = layer_body(m, &layers[i], &one, bud, n_splits, hidden, pend.partial ? &pend : nullptr, &next, ws,
+                         S.layer, s)) != BC_OK)
+      return rc;
+    pend = next;
+  }
+  return run_head(m, hidden, pend.partial ? &pend : nullptr, g_final, w_head, float(st->rms_eps), logits, token,
+                  at<float>(ws, S.head.partial), at<float>(ws, S.head.tile_max), at<int32_t>(ws, S.head.tile_arg), s);
 }
 
 // ------------------------------------------------------------------ LM head
@@ -541,6 +604,7 @@ extern "C" int bc_lm_head(const bc_model_dims* dims, const uint16_t* hidden, con
   const HeadLayout L = head_layout(*dims);
   if (ws_bytes < L.total) return set_error(BC_ERR_WORKSPACE, "bc_lm_head: workspace %zu < %zu", ws_bytes, L.total);
   if (reinterpret_cast<uintptr_t>(ws) & 15) return set_error(BC_ERR_INVALID, "bc_lm_head: ws not 16-byte aligned");
-  return run_head(*dims, hidden, g_final, w_head_t, float(rms_eps), logits, token, at<float>(ws, L.partial),
+  return run_head(*dims, const_cast<uint16_t*>(hidden), nullptr, g_final, w_head_t, float(rms_eps), logits, token,
+                  at<float>(ws, L.partial),
                   at<float>(ws, L.tile_max), at<int32_t>(ws, L.tile_arg), static_cast<hipStream_t>(stream));
 }
