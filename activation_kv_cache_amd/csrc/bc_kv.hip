@@ -29,11 +29,11 @@ namespace bc {
 namespace {
 
 constexpr int kScoreThreads = 1024;
-constexpr int kScoreBlocksPerGroup = 128;
+constexpr int kScoreBlocksPerGroup = 256;   // one work-group per CU at 128K
 constexpr int kSelThreads = 1024;
 constexpr int kSelMaxCand = kSelThreads * 32;
 
-// Scores of the candidate blocks of KV head blockIdx.y (64 per work-group).
+// Scores of the candidate blocks of KV head blockIdx.y (256 per work-group).
 // QP: q comes from the qkv GEMV chunk partials (rotary from the host table,
 // bf16 rounding); the first work-group of each KV head also stores q,
 // appends k, v of the current token at slot pos and refreshes the (min, max)
@@ -58,12 +58,16 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
   Chunk8 cqa[QPT], cqb[QPT], cka, ckb, cvv;
   const int kcol = p.n_heads * D + g * D, vcol = (p.n_heads + p.n_kv_heads) * D + g * D;
   if constexpr (QP) {
+    // only the threads that form q load its partials, so the summary loads
+    // of the other waves queue behind none
 #pragma unroll
     for (int u = 0; u < QPT; ++u) {
-      const int e = min(tid + u * kScoreThreads, G * HALF - 1);
-      const int col = (g * G + e / HALF) * D + e % HALF;
-      chunk_load(cqa[u], p.qkv_partial, p.qkv_splits, p.qkv_out, col);
-      chunk_load(cqb[u], p.qkv_partial, p.qkv_splits, p.qkv_out, col + HALF);
+      const int e = tid + u * kScoreThreads;
+      if (e < G * HALF) {
+        const int col = (g * G + e / HALF) * D + e % HALF;
+        chunk_load(cqa[u], p.qkv_partial, p.qkv_splits, p.qkv_out, col);
+        chunk_load(cqb[u], p.qkv_partial, p.qkv_splits, p.qkv_out, col + HALF);
+      }
     }
     if (first) {
       const int ih = min(tid, HALF - 1), id = min(tid, D - 1);
@@ -168,6 +172,15 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
     }
   }
   if (p.bud.k_blk <= 0) return;
+  // t = max(q*kmax, q*kmin) with the larger product taken only when it is
+  // strictly larger; the products are exact in fp32, so for kmax >= kmin
+  // that is q*kmax when q > 0 and kmax > kmin, else q*kmin: one product
+  // per (head, dim) instead of two
+  bool qpos[G][4];
+#pragma unroll
+  for (int j = 0; j < G; ++j)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) qpos[j][u] = qf[j][u] > 0.f;
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int c = cbeg + (it * (kScoreThreads / kWave) + w) * CPW + cs;
@@ -175,16 +188,15 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
     const uint4 m4 = mm[it];
     const float mn[4] = {bf16_lo(m4.x), bf16_lo(m4.y), bf16_lo(m4.z), bf16_lo(m4.w)};
     const float mx[4] = {bf16_hi(m4.x), bf16_hi(m4.y), bf16_hi(m4.z), bf16_hi(m4.w)};
+    bool up[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) up[u] = mx[u] > mn[u];
     float a[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       float t[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float x1 = qf[j][u] * mx[u];
-        const float x2 = qf[j][u] * mn[u];
-        t[u] = x1 > x2 ? x1 : x2;
-      }
+      for (int u = 0; u < 4; ++u) t[u] = qf[j][u] * ((qpos[j][u] && up[u]) ? mx[u] : mn[u]);
       a[j] = (t[0] + t[1]) + (t[2] + t[3]);
     }
 #pragma unroll
