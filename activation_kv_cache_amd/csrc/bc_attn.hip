@@ -80,12 +80,13 @@ struct AttnRows {
   uint4 ka[2], kb[2], va[2], vb[2];
 };
 
-// Rows base + u*TPL + sub (u = 0, 1) of the chunk [c0, c1); positions past
-// c1 read row c1-1 again (their weight is masked to zero).  Lane r of a row
-// group loads dims [8r, 8r+8) and [D/2 + 8r, D/2 + 8r + 8).
-template <int D>
-__device__ __forceinline__ void attn_load(const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
-                                          const int32_t* sidx, int base, int c0, int c1, int sub, AttnRows& rw) {
+// Rows of list positions base + u*TPL + sub (u = 0, 1), below c1; positions
+// past c1 read the row of c1-1 again (their weight is masked to zero).
+// tok maps a list position to its token.  Lane r of a row group loads dims
+// [8r, 8r+8) and [D/2 + 8r, D/2 + 8r + 8).
+template <int D, typename TokFn>
+__device__ __forceinline__ void attn_load(const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg, TokFn tok,
+                                          int base, int c1, int sub, AttnRows& rw) {
   constexpr int LPT = D / 16;
   constexpr int TPL = kWave / LPT;
   constexpr int HALF = D / 2;
@@ -93,7 +94,7 @@ __device__ __forceinline__ void attn_load(const uint16_t* __restrict__ Kg, const
   for (int u = 0; u < 2; ++u) {
     const int pos = base + u * TPL + sub;
     const int pc = pos < c1 ? pos : c1 - 1;
-    const int t = sidx ? sidx[pc - c0] : pc;
+    const int t = tok(pc);
     const size_t off = size_t(t) * D;
     rw.ka[u] = *reinterpret_cast<const uint4*>(Kg + off);
     rw.kb[u] = *reinterpret_cast<const uint4*>(Kg + off + HALF);
@@ -269,8 +270,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
   // dense list: the first rows are known before q, so they go in flight now
   AttnRows rw;
   int base = lo + w * TPI;
+  auto tok_dense = [](int pc) { return pc; };
   if constexpr (LM == L_DENSE) {
-    if (base < hi_main) attn_load<D>(Kg, Vg, nullptr, base, lo, hi_main, sub, rw);
+    if (base < hi_main) attn_load<D>(Kg, Vg, tok_dense, base, hi_main, sub, rw);
   }
 
   // scored list: the block ranks [r_lo, r_hi) this split's slice reads
@@ -336,67 +338,70 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
   }
   __syncthreads();
 
-  if constexpr (LM == L_DENSE) {
-    const int c1 = hi_main;
-    if (base < c1) {
-      if (base + TPI <= c1)
-        attn_compute<D, G, false>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
-      else
-        attn_compute<D, G, true>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
-      base += STEP;
-      for (; base + TPI <= c1; base += STEP) {
-        attn_load<D>(Kg, Vg, nullptr, base, lo, c1, sub, rw);
-        attn_compute<D, G, false>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
-      }
+  if constexpr (LM != L_IDX) {
+    // one pass over the split's list positions [lo, hi_main): the dense list
+    // is tokens themselves; a scored list maps a position to its token from
+    // the budget and the selected block ranks (sinks | blocks | window), so
+    // nothing is staged and the row loads stay pipelined across the split
+    const int S0 = p.bud.sinks, nb0 = p.bud.sinks + 16 * p.bud.k_blk;
+    const int rmax = max(r_hi - r_lo - 1, 0);
+    auto tok_scored = [&](int pc) -> int {
+      const int q = pc - S0;
+      const int ri = min(max((q >> 4) - r_lo, 0), rmax);
+      const int tb = 16 * (p.bud.b_lo + sm.blk[ri]) + (q & 15);
+      const int tw = p.n_ctx - p.bud.window + (pc - nb0);
+      return pc < S0 ? pc : (pc < nb0 ? tb : tw);
+    };
+    auto run = [&](auto tok) {
+      const int c1 = hi_main;
       if (base < c1) {
-        attn_load<D>(Kg, Vg, nullptr, base, lo, c1, sub, rw);
-        attn_compute<D, G, true>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
+        if constexpr (LM == L_SCORES) attn_load<D>(Kg, Vg, tok, base, c1, sub, rw);
+        if (base + TPI <= c1)
+          attn_compute<D, G, false>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
+        else
+          attn_compute<D, G, true>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
+        base += STEP;
+        for (; base + TPI <= c1; base += STEP) {
+          attn_load<D>(Kg, Vg, tok, base, c1, sub, rw);
+          attn_compute<D, G, false>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
+        }
+        if (base < c1) {
+          attn_load<D>(Kg, Vg, tok, base, c1, sub, rw);
+          attn_compute<D, G, true>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
+        }
       }
+    };
+    if constexpr (LM == L_DENSE) {
+      run(tok_dense);
+    } else {
+      if (p.idx_out) {
+        int32_t* io = p.idx_out + size_t(g) * p.n_sel;
+        for (int i = lo + tid; i < hi; i += kAttnThreads) io[i] = tok_scored(i);
+      }
+      run(tok_scored);
     }
   } else {
-    const int32_t* idxg = LM == L_IDX ? p.idx + size_t(g) * p.n_sel : nullptr;
-    int32_t* idx_out = LM == L_SCORES && p.idx_out ? p.idx_out + size_t(g) * p.n_sel : nullptr;
+    const int32_t* idxg = p.idx + size_t(g) * p.n_sel;
     for (int c0 = lo; c0 < hi; c0 += kIdxChunk) {
       const int c1 = min(hi, c0 + kIdxChunk);
-      // list positions -> tokens (a chunk is at most 4 positions per thread;
-      // index loads are all issued before the stores)
+      // the chunk's tokens from the index list (4 positions per thread; the
+      // loads are all issued before the stores)
       static_assert(kIdxChunk == 4 * kAttnThreads, "chunk of 4 positions per thread");
       int32_t tk[4];
-      if constexpr (LM == L_IDX) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) tk[u] = tid + u * kAttnThreads < c1 - c0 ? idxg[c0 + tid + u * kAttnThreads] : 0;
-      }
+      for (int u = 0; u < 4; ++u) tk[u] = tid + u * kAttnThreads < c1 - c0 ? idxg[c0 + tid + u * kAttnThreads] : 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = tid + u * kAttnThreads;
-        if (i >= c1 - c0) continue;
-        int t;
-        if constexpr (LM == L_IDX) {
-          t = tk[u];
-        } else {
-          // list position -> token: sinks, then 16 tokens per kept block
-          // (ascending block order), then the window
-          const int pos = c0 + i, S0 = p.bud.sinks, KB = p.bud.k_blk;
-          if (pos < S0) {
-            t = pos;
-          } else if (pos < S0 + 16 * KB) {
-            const int q = pos - S0;
-            t = 16 * (p.bud.b_lo + sm.blk[(q >> 4) - r_lo]) + (q & 15);
-          } else {
-            t = p.n_ctx - p.bud.window + (pos - S0 - 16 * KB);
-          }
-          if (idx_out) idx_out[pos] = t;
-        }
-        sm.idx[i] = t;
-      }
+      for (int u = 0; u < 4; ++u)
+        if (tid + u * kAttnThreads < c1 - c0) sm.idx[tid + u * kAttnThreads] = tk[u];
       __syncthreads();
+      auto tok = [&](int pc) -> int { return sm.idx[pc - c0]; };
       base = c0 + w * TPI;
       for (; base + TPI <= c1; base += STEP) {
-        attn_load<D>(Kg, Vg, sm.idx, base, c0, c1, sub, rw);
+        attn_load<D>(Kg, Vg, tok, base, c1, sub, rw);
         attn_compute<D, G, false>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
       }
       if (base < c1) {
-        attn_load<D>(Kg, Vg, sm.idx, base, c0, c1, sub, rw);
+        attn_load<D>(Kg, Vg, tok, base, c1, sub, rw);
         attn_compute<D, G, true>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
       }
       __syncthreads();
