@@ -104,6 +104,57 @@ def crossing_k(contexts, d_vals):
     return None
 
 
+def kv_plan(n, r_kv, sinks=SINKS, window=WINDOW, block=16):
+    """(T_sel, attention splits) of the per-step KV policy at context n, as
+    the library's budget and default split rule compute them (host-only
+    replica for the byte account of contexts that were not run)."""
+    D = DIMS
+    if r_kv >= 1:
+        t_sel = n
+    else:
+        T = min(n, int(math.floor(r_kv * n + 0.5)))
+        s = min(sinks, T)
+        w = min(window, T - s)
+        b_lo, b_hi = (s + block - 1) // block, (n - w) // block
+        k_blk = min((T - s - w) // block, max(0, b_hi - b_lo))
+        t_sel = s + w + block * k_blk
+    splits = max(1, min(256 // D["n_kv_heads"], -(-t_sel // 64)))
+    return t_sel, splits
+
+
+def predicted_crossing_k(contexts, t_us, mode_p, mode_k, r_p, r_kv, plan=None):
+    """README "Predicted and measured crossings" (paper Table 2, Pred.): the
+    byte account plus each branch's kernel cost, taken from its own sweep.
+    Reading: a mode's step time is T_m(n) = B_m(n) / BW + C_m, with B_m the
+    step's algorithmic bytes (step_bytes), BW and the dense cost C_dense from
+    a least-squares line through the dense cells, and C_m the mean over the
+    swept contexts of T_m(n) - B_m(n) / BW.  The predicted crossing is the
+    first context on a 256-token grid where the projection branch stops
+    leading (T_kv - T_p turns from positive to non-positive), interpolated
+    linearly; in units of 1024 tokens, None if that does not happen below
+    512K tokens.  Returns (pred_k, bw_gbs, cost_p_us, cost_k_us)."""
+    plan = plan or (lambda n, a, b: kv_plan(n, b))
+    modes = {"dense": (1.0, 1.0), mode_p: (r_p, 1.0), mode_k: (1.0, r_kv)}
+    B = {m: np.array([step_bytes(n, rp, rk, *plan(n, rp, rk)) for n in contexts], float)
+         for m, (rp, rk) in modes.items()}
+    td = np.asarray(t_us["dense"], float)
+    slope, c_dense = np.polyfit(B["dense"], td, 1)    # us per byte, us
+    cost = {m: float(np.mean(np.asarray(t_us[m], float) - B[m] * slope)) for m in (mode_p, mode_k)}
+
+    def t_pred(m, n):
+        rp, rk = modes[m]
+        return step_bytes(n, rp, rk, *plan(n, rp, rk)) * slope + cost[m]
+
+    prev = None
+    for n in range(256, 512 * 1024 + 1, 256):
+        d = t_pred(mode_k, n) - t_pred(mode_p, n)   # > 0 while the projection branch leads
+        if prev is not None and prev[1] > 0 and d <= 0:
+            n0, d0 = prev
+            return (n0 + 256 * d0 / (d0 - d)) / 1024, 1e-3 / slope, cost[mode_p], cost[mode_k]
+        prev = (n, d)
+    return None, 1e-3 / slope, cost[mode_p], cost[mode_k]
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -450,13 +501,19 @@ def crossover_sweep(model, contexts, blocks, steps, warmup, seed=0):
         d_vals = [float(x) for x in (t["dense"] / t[mp] - t["dense"] / t[mk]).mean(axis=0)]
         c = crossing_k(contexts, d_vals)
         ns, nx = n_star_k(r_p, r_kv), n_star_k(r_p, r_kv, ext=True)
+        mean_t = {m: t[m].mean(axis=0) for m in ("dense", mp, mk)}
+        pred, bw, cp, ck = predicted_crossing_k(contexts, mean_t, mp, mk, r_p, r_kv,
+                                                plan=lambda n, a, b: model.plan(n, a, b)[1:])
         out["pairs"][f"{r_p}/{r_kv}"] = {
             "n_star_k": round(ns, 2), "n_star_ext_k": round(nx, 2),
             "measured_k": None if c is None else round(c, 2),
             "measured_minus_n_star_k": None if c is None else round(c - ns, 2),
-            "measured_minus_n_star_ext_k": None if c is None else round(c - nx, 2)}
+            "measured_minus_n_star_ext_k": None if c is None else round(c - nx, 2),
+            "pred_k": None if pred is None else round(pred, 2),
+            "measured_minus_pred_k": None if (c is None or pred is None) else round(c - pred, 2),
+            "pred_fit": {"bw_gbs": round(bw, 1), "cost_proj_us": round(cp, 1), "cost_kv_us": round(ck, 1)}}
         log(f"[bench] crossing {r_p}/{r_kv}: measured {c if c is None else round(c, 1)}K, "
-            f"n* {ns:.1f}K, n*_ext {nx:.1f}K")
+            f"n* {ns:.1f}K, n*_ext {nx:.1f}K, cost-aware prediction {pred if pred is None else round(pred, 1)}K")
     return out
 
 
