@@ -283,7 +283,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
       r_lo = lo > S0 ? (lo - S0) / 16 : 0;
       r_hi = min(KB, (hi - S0 + 15) / 16);
     }
-    if (r_lo < r_hi) {   // uniform over the work-group
+    if (r_lo < r_hi && p.blk) {   // ranks from the selection kernel
+      const int32_t* bg = p.blk + size_t(g) * KB + r_lo;
+      for (int i = tid; i < r_hi - r_lo; i += kAttnThreads) sm.blk[i] = bg[i];
+    } else if (r_lo < r_hi) {   // uniform over the work-group
       const int n = p.bud.n_cand;
       const float* sc = p.scores + size_t(g) * p.scores_stride;
       if (n <= kAttnThreads * 8)
@@ -609,12 +612,16 @@ static int scored_ranks_per_split(int n_sel, int n_splits) {
 }
 
 bool attn_scored_list_ok(const bc_kv_budget_info& bud, int n_splits) {
-  return bud.n_cand <= kAttnMaxCand && scored_ranks_per_split(bud.t_sel, n_splits) <= kAttnMaxRanks;
+  return scored_ranks_per_split(bud.t_sel, n_splits) <= kAttnMaxRanks;
 }
+
+bool attn_prologue_select_ok(const bc_kv_budget_info& bud) { return bud.n_cand <= kAttnThreads * 8; }
 
 int launch_attn_partial(int q_mode, int list_mode, const AttnParams& p, hipStream_t s) {
   if (list_mode == L_IDX && p.idx == nullptr) return set_error(BC_ERR_INVALID, "attention: NULL index list");
-  if (list_mode == L_SCORES && (!p.scores || !attn_scored_list_ok(p.bud, p.n_splits) || p.n_sel != p.bud.t_sel))
+  if (list_mode == L_SCORES &&
+      (!attn_scored_list_ok(p.bud, p.n_splits) || p.n_sel != p.bud.t_sel ||
+       (!p.blk && (!p.scores || p.bud.n_cand > kAttnMaxCand))))
     return set_error(BC_ERR_INVALID, "attention: scored list out of range");
   if (p.head_dim == 128) return launch_partial_d<128>(q_mode, list_mode, p, s);
   if (p.head_dim == 64) return launch_partial_d<64>(q_mode, list_mode, p, s);

@@ -117,9 +117,10 @@ int launch_argmax_finish(const float* tile_max, const int32_t* tile_arg, int n_t
 //              range holds list position pos (dense list, pos = n_sel - 1)
 //              appends k, v at cache slot pos and attends to them from LDS.
 //   L_DENSE    tokens 0..n_sel-1;  L_IDX  an index list [n_kv_heads][n_sel];
-//   L_SCORES   the list sinks | top-k_blk scored blocks | window, built in
-//              every work-group's prologue from the block scores (each
-//              split selects the block ranks its slice needs).
+//   L_SCORES   the list sinks | top-k_blk scored blocks | window: each split
+//              selects the block ranks its slice needs from the block scores
+//              in its prologue, or (blk given) copies them from the kept
+//              blocks' candidate indices in rank order.
 enum AttnQ : int { Q_GLOBAL = 0, Q_PARTIAL = 1 };
 enum AttnList : int { L_DENSE = 0, L_IDX = 1, L_SCORES = 2 };
 constexpr int kAttnMaxCand = 256 * 32;   // candidate blocks one attention work-group selects from
@@ -146,13 +147,17 @@ struct AttnParams {
   // L_SCORES
   const float* scores;        // [n_kv_heads][scores_stride]
   int scores_stride;
+  const int32_t* blk;         // optional: [n_kv_heads][k_blk] kept candidates by rank
   bc_kv_budget_info bud;
   int n_ctx;
   int32_t* idx_out;           // optional: the list [n_kv_heads][n_sel] (each split writes its slice)
 };
 int launch_attn_partial(int q_mode, int list_mode, const AttnParams& p, hipStream_t s);
-// whether a scored list fits the in-prologue selection (candidates, ranks per split)
+// whether a scored list fits the attention kernel (candidates, ranks per split)
 bool attn_scored_list_ok(const bc_kv_budget_info& bud, int n_splits);
+// whether its prologue selection is cheap enough (few candidates per
+// thread); otherwise a selection kernel supplies the ranks (AttnParams::blk)
+bool attn_prologue_select_ok(const bc_kv_budget_info& bud);
 
 struct ReduceParams {
   const float* m;
@@ -170,7 +175,8 @@ struct KvSelectParams {
   bc_kv_budget_info bud;
   float* scores;          // [n_kv_heads][scores_stride]
   int scores_stride;
-  int32_t* idx_out;       // [n_kv_heads][t_sel]
+  int32_t* idx_out;       // [n_kv_heads][t_sel], or NULL
+  int32_t* blk_out;       // optional: [n_kv_heads][k_blk] kept candidates by rank
   // q from the qkv GEMV partials (rotary at pos): the first work-group of
   // each KV head also stores q, appends k, v at slot pos and refreshes the
   // summary of block pos/16 (valid when that block is never a candidate)
@@ -185,7 +191,8 @@ struct KvSelectParams {
 int launch_kv_score_select(const KvSelectParams& p, hipStream_t s);
 // scores only (q given or from the partials, with the append)
 int launch_kv_score(const KvSelectParams& p, hipStream_t s);
-// the list from the scores
+// the list (idx_out) and / or the kept candidates by rank (blk_out) from the
+// scores
 int launch_kv_block_select(const KvSelectParams& p, hipStream_t s);
 
 int launch_select(const uint16_t* x, int n, int k, int32_t* idx_out, hipStream_t s);

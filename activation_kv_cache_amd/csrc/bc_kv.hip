@@ -221,36 +221,39 @@ __global__ __launch_bounds__(kSelThreads) void k_kv_block_select(const KvSelectP
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   const bc_kv_budget_info bd = p.bud;
-  int32_t* out = p.idx_out + size_t(g) * bd.t_sel;
-  for (int t = tid; t < bd.sinks; t += kSelThreads) out[t] = t;
-  for (int t = tid; t < bd.window; t += kSelThreads) out[bd.t_sel - bd.window + t] = p.n_ctx - bd.window + t;
+  int32_t* out = p.idx_out ? p.idx_out + size_t(g) * bd.t_sel : nullptr;
+  int32_t* bout = p.blk_out ? p.blk_out + size_t(g) * bd.k_blk : nullptr;
+  if (out) {
+    for (int t = tid; t < bd.sinks; t += kSelThreads) out[t] = t;
+    for (int t = tid; t < bd.window; t += kSelThreads) out[bd.t_sel - bd.window + t] = p.n_ctx - bd.window + t;
+  }
   if (bd.k_blk <= 0) return;
   const int n = bd.n_cand;
   const int b_lo = bd.b_lo, sinks = bd.sinks;
   const float* sc = p.scores + size_t(g) * p.scores_stride;
+  auto emit_for = [&](int P) {
+    return [=](int rk, int e) {
+      const int cand = tid * P + e;
+      if (bout) bout[rk] = cand;
+      if (out) {
+        int32_t* o = out + sinks + 16 * rk;
+        const int t0 = 16 * (b_lo + cand);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) o[u] = t0 + u;
+      }
+    };
+  };
   if (n <= kSelThreads * 8) {
     // up to 8 keys per thread, staged through LDS (coalesced loads)
     uint32_t key[8];
     const int P = load_score_keys<kSelThreads, 8>(sc, n, key, sm.hist);
-    auto emit = [&](int rk, int e) {
-      int32_t* o = out + sinks + 16 * rk;
-      const int t0 = 16 * (b_lo + tid * P + e);
-#pragma unroll
-      for (int u = 0; u < 16; ++u) o[u] = t0 + u;
-    };
-    block_topk32<kSelThreads, 8>(key, P, n, bd.k_blk, 0, bd.k_blk, true, emit, sm);
+    block_topk32<kSelThreads, 8>(key, P, n, bd.k_blk, 0, bd.k_blk, true, emit_for(P), sm);
   } else {
     const int P = (n + kSelThreads - 1) / kSelThreads;
     uint32_t key[32];
 #pragma unroll
     for (int e = 0; e < 32; ++e) key[e] = (e < P && tid * P + e < n) ? float_order_key(sc[size_t(tid) * P + e]) : 0u;
-    auto emit = [&](int rk, int e) {
-      int32_t* o = out + sinks + 16 * rk;
-      const int t0 = 16 * (b_lo + tid * P + e);
-#pragma unroll
-      for (int u = 0; u < 16; ++u) o[u] = t0 + u;
-    };
-    block_topk32<kSelThreads, 32>(key, P, n, bd.k_blk, 0, bd.k_blk, true, emit, sm);
+    block_topk32<kSelThreads, 32>(key, P, n, bd.k_blk, 0, bd.k_blk, true, emit_for(P), sm);
   }
 }
 

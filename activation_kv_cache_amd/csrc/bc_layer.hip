@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void k_pack_tiles(const uint16_t* src, const u
 
 // ------------------------------------------------------------ layer layout
 struct LayerLayout {
-  size_t partial, partial2, x1, idx_qkv, q, scores, idx_kv, m, l, o, a, idx_o, h_mid, x2, idx_gu, hff, idx_down;
+  size_t partial, partial2, x1, idx_qkv, q, scores, blk, idx_kv, m, l, o, a, idx_o, h_mid, x2, idx_gu, hff, idx_down;
   size_t total;
 };
 
@@ -127,6 +127,7 @@ LayerLayout layer_layout(const bc_model_dims& m, int n_ctx, int n_splits) {
   L.idx_qkv = take(size_t(m.d) * 4);
   L.q = take(size_t(H) * hd * 2);
   L.scores = take(size_t(Hkv) * nb * 4);
+  L.blk = take(size_t(Hkv) * (nb + 1) * 4);
   L.idx_kv = take(size_t(Hkv) * n_ctx * 4);
   L.m = take(size_t(H) * n_splits * 4);
   L.l = take(size_t(H) * n_splits * 4);
@@ -410,6 +411,9 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
   int qkv_splits = 0;
   const bool fused_score = kv_sparse && (bud.window > 0 || bud.k_blk == 0);
   const bool scored_attn = kv_sparse && attn_scored_list_ok(bud, n_splits);
+  // many candidates: one 1024-lane work-group per KV head ranks them once
+  // (a kernel boundary) instead of every attention work-group in its prologue
+  const bool rank_kernel = scored_attn && bud.k_blk > 0 && !attn_prologue_select_ok(bud);
   KvSelectParams kp{};
   if (kv_sparse) {
     kp.summary = ly->kv_summary; kp.nb_cap = ly->n_cap / 16; kp.n_ctx = st->n_ctx;
@@ -435,6 +439,12 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
     }
   }
   if (kv_sparse && !scored_attn && (rc = launch_kv_block_select(kp, s)) != BC_OK) return rc;
+  if (rank_kernel) {
+    KvSelectParams kb = kp;
+    kb.idx_out = nullptr;
+    kb.blk_out = at<int32_t>(ws, L.blk);
+    if ((rc = launch_kv_block_select(kb, s)) != BC_OK) return rc;
+  }
 
   // attention
   {
@@ -449,6 +459,7 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
       p.q = at<uint16_t>(ws, L.q);
       if (scored_attn) {
         p.scores = kp.scores; p.scores_stride = kp.scores_stride; p.bud = bud; p.n_ctx = st->n_ctx;
+        p.blk = rank_kernel ? at<int32_t>(ws, L.blk) : nullptr;
         p.idx_out = st->taps ? at<int32_t>(ws, L.idx_kv) : nullptr;
         if ((rc = launch_attn_partial(Q_GLOBAL, L_SCORES, p, s)) != BC_OK) return rc;
       } else {

@@ -91,6 +91,9 @@ LAYER_CASES = [
     # last split holds only that token in the second case
     ("tiny-short-ctx", gen.TINY, 64, 17, 1.0, 1.0, 4, 128, 3),
     ("tiny-split-of-one", gen.TINY, 64, 13, 1.0, 1.0, 4, 128, 4),
+    # over 2048 candidate blocks: a selection kernel ranks the kept blocks
+    # once per KV head and the attention work-groups copy their ranks
+    ("tiny-long-ctx-ranked", gen.TINY, 40960, 40000, 0.7, 0.3, 4, 128, 0),
     ("8b-2k-dense", gen.LLAMA8B, 2048, 2048, 1.0, 1.0, 4, 1024, 0),
     ("8b-2k-both-0.5-0.3", gen.LLAMA8B, 2048, 2048, 0.5, 0.3, 4, 1024, 0),
     ("8b-8k-both-0.7-0.3", gen.LLAMA8B, 8192, 8192, 0.7, 0.3, 4, 1024, 0),
