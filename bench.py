@@ -532,6 +532,8 @@ def main():
     ap.add_argument("--crossover-blocks", type=int, default=1,
                     help="blocks of the crossover sweep (every mode at 2K, 4K, ..., 128K); 0 skips it")
     ap.add_argument("--crossover-steps", type=int, default=10, help="timed steps per sweep cell")
+    ap.add_argument("--gemv-only", default="",
+                    help="reps:r_p -- only launch the gate|up GEMV reps times per layer (for counters)")
     ap.add_argument("--attn-only", type=int, default=0,
                     help="only launch the dense attention kernel this many times per layer (for counters)")
     args = ap.parse_args()
@@ -560,6 +562,13 @@ def main():
     if args.kernels:
         sweep = [int(x) for x in args.split_sweep.split(",") if x]
         print(json.dumps({"kernels": kernel_table(model, contexts, sweep)}))
+        return
+
+    if args.gemv_only:
+        reps, r_p = args.gemv_only.split(":")
+        us, b, k = time_gemv_kernel(model, "w_gu", float(r_p), reps=int(reps))
+        log(f"[bench] gate|up GEMV at r_p={r_p}: {us:.1f} us, {b / us / 1e3:.0f} GB/s, k={k}")
+        print(json.dumps({"gemv_us": us, "gemv_bytes": b, "k": k}))
         return
 
     if args.attn_only:
