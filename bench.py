@@ -123,7 +123,7 @@ def kv_plan(n, r_kv, sinks=SINKS, window=WINDOW, block=16):
 
 
 def predicted_crossing_k(contexts, t_us, mode_p, mode_k, r_p, r_kv, plan=None):
-    """README "Predicted and measured crossings" (paper Table 2, Pred.): the
+    """README "Results", paper Table 2 (column Pred.): the
     byte account plus each branch's kernel cost, taken from its own sweep.
     Reading: a mode's step time is T_m(n) = B_m(n) / BW + C_m, with B_m the
     step's algorithmic bytes (step_bytes), BW and the dense cost C_dense from
@@ -479,7 +479,7 @@ PAIRS = (("proj0.7", "kv0.3", 0.7, 0.3), ("proj0.5", "kv0.3", 0.5, 0.3), ("proj0
 def crossover_sweep(model, contexts, blocks, steps, warmup, seed=0):
     """Every mode at every context, `blocks` times in a shuffled order; the
     speedups S = t_dense / t_mode are paired within a block (README
-    "Reproduce": paired blocks), averaged over blocks, and each (r_p, r_kv)
+    "Reproduce the paper": paired blocks), averaged over blocks, and each (r_p, r_kv)
     pair's crossing of S_proj and S_kv is compared with the byte-account n*."""
     rng = np.random.default_rng(seed)
     cells = [(m, n) for m in SWEEP_MODES for n in contexts]

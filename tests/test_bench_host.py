@@ -1,6 +1,6 @@
 """Host-side pieces of bench.py: the KV plan replica against the library's
 own budget and split rule, and the cost-aware crossing prediction (README
-"Predicted and measured crossings", paper Table 2) on synthetic timings whose
+"Results", paper Table 2) on synthetic timings whose
 answer is known."""
 import numpy as np
 import pytest
