@@ -77,6 +77,7 @@ _SIG = {
     "bc_kv_score_select": (c_int, [P, P, c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(bc_kv_policy), P, P,
                                    P, c_size_t, P]),
     "bc_build_kv_summary": (c_int, [P, c_int, c_int, c_int, c_int, P, P]),
+    "bc_kv_compact": (c_int, [P, P, c_int, c_int, c_int, P, c_int, P, P, c_int, P]),
     "bc_splitk_attn_partial": (c_int, [P, P, P, c_int, P, c_int, c_int, c_int, c_int, c_int, c_float, P, P, P, P]),
     "bc_splitk_reduce": (c_int, [P, P, P, c_int, c_int, c_int, P, P]),
     "bc_attn_default_splits": (c_int, [c_int, c_int]),
@@ -214,6 +215,12 @@ def bc_build_kv_summary(k_cache, n_ctx: int, summary, stream=None):
     n_kv, n_cap, hd = k_cache.shape
     return _check(_lib.bc_build_kv_summary(_ptr(k_cache), n_kv, n_cap, hd, int(n_ctx), _ptr(summary),
                                            _stream(stream)), "bc_build_kv_summary")
+
+
+def bc_kv_compact(k_cache, v_cache, idx, t_sel: int, k_out, v_out, stream=None):
+    n_kv, n_cap, hd = k_cache.shape
+    return _check(_lib.bc_kv_compact(_ptr(k_cache), _ptr(v_cache), n_cap, n_kv, hd, _ptr(idx), int(t_sel),
+                                     _ptr(k_out), _ptr(v_out), k_out.shape[1], _stream(stream)), "bc_kv_compact")
 
 
 def bc_splitk_attn_partial(q, k_cache, v_cache, idx, n_sel: int, n_heads: int, n_kv_heads: int, n_splits: int,

@@ -259,6 +259,24 @@ __global__ __launch_bounds__(kSelThreads) void k_kv_block_select(const KvSelectP
 
 // One wave per (block, KV head): per dim the min and max over the block's
 // tokens below n_ctx.
+// Gather of the selected rows into a compact cache: one 16-byte piece of a
+// K or V row per thread; row t of head g of the output is row idx[g][t] of
+// the cache (ids clamped to the cache, so a bad id cannot read outside it).
+__global__ __launch_bounds__(256) void k_kv_compact(const uint16_t* k_cache, const uint16_t* v_cache, int n_cap,
+                                                   int head_dim, const int32_t* idx, int t_sel, uint16_t* k_out,
+                                                   uint16_t* v_out, int n_cap_out) {
+  const int g = blockIdx.y;
+  const int per_row = head_dim / 8;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)t_sel * per_row) return;
+  const int t = int(i / per_row), c = int(i % per_row);
+  const int src = min(max(idx[size_t(g) * t_sel + t], 0), n_cap - 1);
+  const size_t si = (size_t(g) * n_cap + src) * head_dim + 8 * c;
+  const size_t di = (size_t(g) * n_cap_out + t) * head_dim + 8 * c;
+  *reinterpret_cast<uint4*>(k_out + di) = *reinterpret_cast<const uint4*>(k_cache + si);
+  *reinterpret_cast<uint4*>(v_out + di) = *reinterpret_cast<const uint4*>(v_cache + si);
+}
+
 __global__ __launch_bounds__(256) void k_build_summary(const uint16_t* k_cache, int n_cap, int head_dim, int n_ctx,
                                                       uint16_t* summary) {
   const int g = blockIdx.y;
@@ -377,6 +395,21 @@ extern "C" int bc_kv_score_select(const uint16_t* q, const uint16_t* summary, in
   p.n_kv_heads = n_kv_heads; p.head_dim = head_dim; p.bud = b; p.scores = scores; p.scores_stride = b.n_cand;
   p.idx_out = idx_out;
   return launch_kv_score_select(p, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int bc_kv_compact(const uint16_t* k_cache, const uint16_t* v_cache, int n_cap, int n_kv_heads,
+                             int head_dim, const int32_t* idx, int t_sel, uint16_t* k_out, uint16_t* v_out,
+                             int n_cap_out, void* stream) {
+  if (!k_cache || !v_cache || !idx || !k_out || !v_out) return set_error(BC_ERR_INVALID, "bc_kv_compact: NULL pointer");
+  if (n_kv_heads <= 0 || n_cap <= 0 || t_sel < 0 || t_sel > n_cap_out)
+    return set_error(BC_ERR_INVALID, "bc_kv_compact: n_kv_heads=%d n_cap=%d t_sel=%d n_cap_out=%d", n_kv_heads, n_cap,
+                     t_sel, n_cap_out);
+  if (!valid_head_dim(head_dim)) return set_error(BC_ERR_UNSUPPORTED, "head_dim %d", head_dim);
+  const long long pieces = (long long)t_sel * (head_dim / 8);
+  if (pieces == 0) return BC_OK;
+  k_kv_compact<<<dim3(unsigned((pieces + 255) / 256), n_kv_heads), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      k_cache, v_cache, n_cap, head_dim, idx, t_sel, k_out, v_out, n_cap_out);
+  return check_launch("k_kv_compact");
 }
 
 extern "C" int bc_build_kv_summary(const uint16_t* k_cache, int n_kv_heads, int n_cap, int head_dim, int n_ctx,

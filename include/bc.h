@@ -147,6 +147,20 @@ int bc_kv_score_select(const uint16_t* q, const uint16_t* summary, int nb_cap, i
 int bc_build_kv_summary(const uint16_t* k_cache, int n_kv_heads, int n_cap, int head_dim, int n_ctx,
                         uint16_t* summary, void* stream);
 
+/* a4 (select once).  The README's timing harness also runs the KV branch as
+ * "sel": the scored selection made once, gathered into one contiguous buffer
+ * and then read by the same dense attention kernel every step (README
+ * "Timing and quality on a GPU"; "API at a glance": select_and_compact).
+ * This is the gather: for every KV head g and t < t_sel,
+ *   k_out[g][t][:] = k_cache[g][idx[g][t]][:],  v_out likewise.
+ *   k_cache, v_cache  bf16 [n_kv_heads][n_cap][head_dim]
+ *   idx     int32 [n_kv_heads][t_sel] token ids (a list from bc_kv_score_select)
+ *   k_out, v_out  bf16 [n_kv_heads][n_cap_out][head_dim]; rows >= t_sel untouched
+ * t_sel <= n_cap_out.  Ids outside [0, n_cap) are clamped (never read out of
+ * the cache).  The output must not overlap the input. */
+int bc_kv_compact(const uint16_t* k_cache, const uint16_t* v_cache, int n_cap, int n_kv_heads, int head_dim,
+                  const int32_t* idx, int t_sel, uint16_t* k_out, uint16_t* v_out, int n_cap_out, void* stream);
+
 /* a5. Split-K decode attention, partial pass (README "Overview": dense and
  * sparse modes read their caches through the same split-K kernel).  For
  * query head j (KV head g = j / (n_heads/n_kv_heads)) and split s covering

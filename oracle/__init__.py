@@ -12,7 +12,9 @@ Decoding" (ByteCross), GitHub README page.  What each function follows:
     "Timing and quality on a GPU" (activations select the projection weights
     read; all seven projections);
   - KV selection: "What it does in one picture" (sinks, part of the history,
-    recent entries), scored per 16-token block by a key min/max bound;
+    recent entries), scored per 16-token block by a key min/max bound; its
+    gather into one contiguous buffer (the sel mode): "Timing and quality on
+    a GPU";
   - split-K attention and its merge: "Overview" (one split-K attention kernel
     for every mode);
   - the layer: the Llama-3.1-8B decoder the README times (RMSNorm, rotary
@@ -206,6 +208,25 @@ def kv_select(q, summ, n: int, n_heads: int, n_kv_heads: int, r_kv: float,
     if want_scores:
         return idx, scores[:, :bud["n_cand"]]
     return idx
+
+
+def kv_compact(K, V, idx, n_cap_out: int):
+    """The scored selection gathered into one contiguous buffer (README
+    "Timing and quality on a GPU": the sel mode; "API at a glance":
+    select_and_compact): row t of head g of the output is row idx[g][t] of the
+    cache.  K, V [Hkv][n_cap][D] bf16; idx [Hkv][T_sel] -> ([Hkv][n_cap_out][D]) x 2,
+    rows past T_sel zero."""
+    K = _c(K, np.uint16)
+    V = _c(V, np.uint16)
+    idx = _c(idx, np.int32)
+    Hkv, t_sel = idx.shape
+    Ko = np.zeros((Hkv, n_cap_out, K.shape[2]), np.uint16)
+    Vo = np.zeros_like(Ko)
+    for g in range(Hkv):
+        for t in range(t_sel):
+            Ko[g, t] = K[g, idx[g, t]]
+            Vo[g, t] = V[g, idx[g, t]]
+    return Ko, Vo
 
 
 # --------------------------------------------------------------- attention

@@ -203,3 +203,45 @@ def test_dense_attention_equals_identity_list():
     torch.cuda.synchronize()
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name,dims,n_cap,n,r_kv", [("tiny", gen.TINY, 2048, 2000, 0.3),
+                                                    ("8b-8k", gen.LLAMA8B, 8192, 8192, 0.5)])
+def test_kv_compact_and_sel_mode_attention(name, dims, n_cap, n, r_kv):
+    """bc_kv_compact (the sel mode's gather) is bit-exact against the oracle's
+    gather, and the dense kernel over the compacted cache gives the same bits
+    as the index-list kernel over the original cache, and the oracle's
+    attention over the list within tolerance."""
+    bc = _bc()
+    H, Hkv, D = dims["n_heads"], dims["n_kv_heads"], dims["head_dim"]
+    window = 128 if dims is gen.TINY else 1024
+    q, K, V = _attn_inputs(f"kc{name}", dims, n_cap)
+    summ = np.zeros((Hkv, n_cap // 16, D, 2), np.uint16)
+    for g in range(Hkv):
+        t = oracle.kv_summary(K[g], n)
+        summ[g, :t.shape[0]] = t
+    lst = oracle.kv_select(q, summ, n, H, Hkv, r_kv, 4, window)
+    t_sel = lst.shape[1]
+    n_out = t_sel + 16
+    Kc = torch.zeros((Hkv, n_out, D), dtype=torch.int16, device="cuda")
+    Vc = torch.zeros_like(Kc)
+    bc.bc_kv_compact(dev(K), dev(V), dev(lst), t_sel, Kc, Vc)
+    Kr, Vr = oracle.kv_compact(K, V, lst, n_out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(Kc), Kr) and np.array_equal(host_u16(Vc), Vr)
+    S = bc.bc_attn_default_splits(t_sel, Hkv)
+    outs = []
+    for kk, vv, idx in ((Kc, Vc, None), (dev(K), dev(V), dev(lst))):
+        m = torch.empty((H, S), dtype=torch.float32, device="cuda")
+        l = torch.empty_like(m)
+        o = torch.empty((H, S, D), dtype=torch.float32, device="cuda")
+        out = torch.empty((H, D), dtype=torch.int16, device="cuda")
+        bc.bc_splitk_attn_partial(dev(q), kk, vv, idx, t_sel, H, Hkv, S, 1 / math.sqrt(D), m, l, o)
+        bc.bc_splitk_reduce(m, l, o, out)
+        outs.append((m, l, o, out))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    ref64, _ = oracle.attn_reduce(*oracle.attn_partial(q, K, V, lst, t_sel, H, Hkv, S))
+    assert_close_bf16(host_u16(outs[0][3]), ref64)

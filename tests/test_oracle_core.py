@@ -375,3 +375,30 @@ def test_attention_brute_force_tiny():
     assert abs(out64[0, 2] - (w @ np.array([1, 2, 3, 4, 5])) / w.sum()) < 1e-14
     w1 = np.exp(np.array([2, 0, 0, 0, 2]) / 2.0)
     assert abs(out64[1, 2] - (w1 @ np.array([1, 2, 3, 4, 5])) / w1.sum()) < 1e-14
+
+
+def test_kv_compact_then_dense_attention_equals_list_attention():
+    """The sel mode (README "Timing and quality on a GPU"): the selection
+    gathered into a contiguous buffer and read densely is the attention over
+    the index list -- the same sums in the same order -- and a planted row
+    lands where its list position says."""
+    H, Hkv, D, n, n_out = 8, 2, 64, 500, 160
+    q = gen.normal_bf16(6, "kc/q", (H, D))
+    K = gen.normal_bf16(6, "kc/k", (Hkv, n, D), 0.5)
+    V = gen.normal_bf16(6, "kc/v", (Hkv, n, D), 1.0)
+    rng = np.random.default_rng(6)
+    t_sel = 150
+    lst = np.stack([np.sort(rng.choice(n, t_sel, replace=False)) for _ in range(Hkv)]).astype(np.int32)
+    Kc, Vc = oracle.kv_compact(K, V, lst, n_out)
+    assert Kc.shape == (Hkv, n_out, D) and not Kc[:, t_sel:].any() and not Vc[:, t_sel:].any()
+    for S in (1, 4, 7):
+        a_list = oracle.attn_partial(q, K, V, lst, t_sel, H, Hkv, S)
+        a_comp = oracle.attn_partial(q, Kc, Vc, None, t_sel, H, Hkv, S)
+        for x, y in zip(a_list, a_comp):
+            assert np.array_equal(x, y)
+    # head 1's 37th kept token is row lst[1][37] of the cache
+    assert np.array_equal(Kc[1, 37], K[1, lst[1, 37]]) and np.array_equal(Vc[1, 37], V[1, lst[1, 37]])
+    # the identity list copies the first rows
+    ident = np.tile(np.arange(t_sel, dtype=np.int32), (Hkv, 1))
+    Ki, Vi = oracle.kv_compact(K, V, ident, t_sel)
+    assert np.array_equal(Ki, K[:, :t_sel]) and np.array_equal(Vi, V[:, :t_sel])
