@@ -122,28 +122,37 @@ def kv_plan(n, r_kv, sinks=SINKS, window=WINDOW, block=16):
     return t_sel, splits
 
 
-def predicted_crossing_k(contexts, t_us, mode_p, mode_k, r_p, r_kv, plan=None):
+def mode_bytes(mode, n, plan=None):
+    """Algorithmic bytes of one step of a sweep mode at context n.  The sel
+    modes (selection made once and gathered, README "Timing and quality on a
+    GPU") step densely over the T_sel kept tokens; the kv modes read the T_sel
+    listed tokens plus the block summaries they rescore every step."""
+    plan = plan or (lambda n_, a, b: kv_plan(n_, b))
+    r_p, r_kv, once = SWEEP_MODES[mode]
+    if once:
+        t_sel, _ = plan(n, 1.0, r_kv)
+        return step_bytes(t_sel, r_p, 1.0, *plan(t_sel, 1.0, 1.0))
+    return step_bytes(n, r_p, r_kv, *plan(n, r_p, r_kv))
+
+
+def predicted_crossing_k(contexts, t_us, mode_p, mode_k, plan=None):
     """README "Results", paper Table 2 (column Pred.): the
     byte account plus each branch's kernel cost, taken from its own sweep.
     Reading: a mode's step time is T_m(n) = B_m(n) / BW + C_m, with B_m the
-    step's algorithmic bytes (step_bytes), BW and the dense cost C_dense from
+    step's algorithmic bytes (mode_bytes), BW and the dense cost C_dense from
     a least-squares line through the dense cells, and C_m the mean over the
     swept contexts of T_m(n) - B_m(n) / BW.  The predicted crossing is the
     first context on a 256-token grid where the projection branch stops
     leading (T_kv - T_p turns from positive to non-positive), interpolated
     linearly; in units of 1024 tokens, None if that does not happen below
     512K tokens.  Returns (pred_k, bw_gbs, cost_p_us, cost_k_us)."""
-    plan = plan or (lambda n, a, b: kv_plan(n, b))
-    modes = {"dense": (1.0, 1.0), mode_p: (r_p, 1.0), mode_k: (1.0, r_kv)}
-    B = {m: np.array([step_bytes(n, rp, rk, *plan(n, rp, rk)) for n in contexts], float)
-         for m, (rp, rk) in modes.items()}
+    B = {m: np.array([mode_bytes(m, n, plan) for n in contexts], float) for m in ("dense", mode_p, mode_k)}
     td = np.asarray(t_us["dense"], float)
     slope, c_dense = np.polyfit(B["dense"], td, 1)    # us per byte, us
     cost = {m: float(np.mean(np.asarray(t_us[m], float) - B[m] * slope)) for m in (mode_p, mode_k)}
 
     def t_pred(m, n):
-        rp, rk = modes[m]
-        return step_bytes(n, rp, rk, *plan(n, rp, rk)) * slope + cost[m]
+        return mode_bytes(m, n, plan) * slope + cost[m]
 
     prev = None
     for n in range(256, 512 * 1024 + 1, 256):
@@ -209,6 +218,21 @@ class Model:
         self.c_layers = [bc.make_layer(l["w_qkv"], l["w_o"], l["w_gu"], l["w_down"], self.g_attn, self.g_mlp,
                                        l["k"], l["v"], l["summ"]) for l in self.layers]
         self.layer_array = bc.make_layer_array(self.c_layers)
+        # sel modes: per layer a compact cache for the gathered selection
+        # (the largest T_sel of the sweep, r_kv 0.5 at max_ctx) and the query
+        # the selection is scored with (seeded; it stands in for the query of
+        # the last pre-filled position)
+        cap = (self.plan(max_ctx, 1.0, 0.5)[1] + 16 + 15) // 16 * 16
+        self.sel_cap = cap
+        self.sel_q = [gen.device_normal_bf16(seed, f"layer{li}/selq", (H, hd), 1.0) for li in range(L)]
+        self.sel_kv = [(torch.empty((Hkv, cap, hd), dtype=torch.int16, device="cuda"),
+                        torch.empty((Hkv, cap, hd), dtype=torch.int16, device="cuda")) for _ in range(L)]
+        self.c_layers_sel = [bc.make_layer(l["w_qkv"], l["w_o"], l["w_gu"], l["w_down"], self.g_attn, self.g_mlp,
+                                           kc, vc, None) for l, (kc, vc) in zip(self.layers, self.sel_kv)]
+        self.layer_array_sel = bc.make_layer_array(self.c_layers_sel)
+        self.sel_idx = torch.empty((Hkv, max_ctx), dtype=torch.int32, device="cuda")
+        self.sel_ws = torch.empty(bc.bc_kv_score_select_workspace_bytes(max_ctx, Hkv, bc.policy(0.3, SINKS, WINDOW))
+                                  // 4 + 64, dtype=torch.int32, device="cuda")
         torch.cuda.synchronize()
         log(f"[bench] model ready in {time.time() - t0:.1f}s; "
             f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
@@ -234,6 +258,43 @@ class Model:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             self.step(n, r_p, r_kv)
+        torch.cuda.synchronize()
+        return g
+
+    def sel_prepare(self, n, r_kv):
+        """Select once and gather (not timed): every layer scores the blocks
+        of its pre-filled cache with its query, and the kept tokens (sinks,
+        blocks, window -- the last one being position n-1) are copied into
+        its compact cache.  Returns T_sel."""
+        bc = self.bc
+        D = DIMS
+        pol = bc.policy(r_kv, SINKS, WINDOW)
+        t_sel = bc.bc_kv_budget(n, pol)["t_sel"]
+        idx = self.sel_idx.view(-1)[:D["n_kv_heads"] * t_sel].view(D["n_kv_heads"], t_sel)
+        for ly, q, (kc, vc) in zip(self.layers, self.sel_q, self.sel_kv):
+            bc.bc_kv_score_select(q, ly["summ"], n, D["n_heads"], D["n_kv_heads"], D["head_dim"], pol, idx, None,
+                                  self.sel_ws)
+            bc.bc_kv_compact(ly["k"], ly["v"], idx, t_sel, kc, vc)
+        torch.cuda.synchronize()
+        return t_sel
+
+    def step_sel(self, t_sel, r_p):
+        """A decode step over the gathered selections: the dense step at
+        context T_sel (the current token rewrites slot T_sel - 1)."""
+        bc = self.bc
+        pol, _, S = self.plan(t_sel, r_p, 1.0)
+        st = bc.make_step(t_sel, r_p, pol, S)
+        self.h.copy_(self.h0)
+        bc.bc_decode_step(self.md, self.layer_array_sel, self.g_final, self.w_head, st, self.h, self.logits,
+                          self.token, self.ws)
+
+    def graph_sel(self, n, r_p, r_kv):
+        t_sel = self.sel_prepare(n, r_kv)
+        self.step_sel(t_sel, r_p)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step_sel(t_sel, r_p)
         torch.cuda.synchronize()
         return g
 
@@ -471,9 +532,15 @@ def cpu_baseline(model, n):
                       f"{reps} run(s) in {elapsed:.1f}s; GB/s = that layer's algorithmic bytes / oracle time"}
 
 
-SWEEP_MODES = {"dense": (1.0, 1.0), "proj0.7": (0.7, 1.0), "proj0.5": (0.5, 1.0), "kv0.3": (1.0, 0.3),
-               "kv0.5": (1.0, 0.5), "both0.7/0.3": (0.7, 0.3), "both0.5/0.3": (0.5, 0.3), "both0.5/0.5": (0.5, 0.5)}
-PAIRS = (("proj0.7", "kv0.3", 0.7, 0.3), ("proj0.5", "kv0.3", 0.5, 0.3), ("proj0.5", "kv0.5", 0.5, 0.5))
+# mode -> (r_p, r_kv, select once): kv modes rescore the history every step;
+# sel modes select once (after the pre-filled context) and step densely over
+# the gathered selection, as the README's timing harness does
+SWEEP_MODES = {"dense": (1.0, 1.0, False), "proj0.7": (0.7, 1.0, False), "proj0.5": (0.5, 1.0, False),
+               "kv0.3": (1.0, 0.3, False), "kv0.5": (1.0, 0.5, False), "sel0.3": (1.0, 0.3, True),
+               "sel0.5": (1.0, 0.5, True), "both0.7/0.3": (0.7, 0.3, False), "both0.5/0.3": (0.5, 0.3, False),
+               "both0.5/0.5": (0.5, 0.5, False)}
+PAIRS = (("proj0.7", "kv0.3", 0.7, 0.3), ("proj0.5", "kv0.3", 0.5, 0.3), ("proj0.5", "kv0.5", 0.5, 0.5),
+         ("proj0.7", "sel0.3", 0.7, 0.3), ("proj0.5", "sel0.3", 0.5, 0.3), ("proj0.5", "sel0.5", 0.5, 0.5))
 
 
 def crossover_sweep(model, contexts, blocks, steps, warmup, seed=0):
@@ -488,8 +555,8 @@ def crossover_sweep(model, contexts, blocks, steps, warmup, seed=0):
         order = rng.permutation(len(cells))
         for ci in order:
             m, n = cells[ci]
-            r_p, r_kv = SWEEP_MODES[m]
-            g = model.graph(n, r_p, r_kv)
+            r_p, r_kv, once = SWEEP_MODES[m]
+            g = model.graph_sel(n, r_p, r_kv) if once else model.graph(n, r_p, r_kv)
             t[m][b, contexts.index(n)] = time_graph(g, steps, warmup) * 1000.0
             del g
         log(f"[bench] crossover block {b + 1}/{blocks} done")
@@ -498,13 +565,18 @@ def crossover_sweep(model, contexts, blocks, steps, warmup, seed=0):
            "step_us": {m: [round(x, 1) for x in t[m].mean(axis=0)] for m in SWEEP_MODES},
            "speedup": {m: [round(x, 4) for x in sp[m]] for m in SWEEP_MODES if m != "dense"}, "pairs": {}}
     for mp, mk, r_p, r_kv in PAIRS:
+        once = SWEEP_MODES[mk][2]
         d_vals = [float(x) for x in (t["dense"] / t[mp] - t["dense"] / t[mk]).mean(axis=0)]
         c = crossing_k(contexts, d_vals)
-        ns, nx = n_star_k(r_p, r_kv), n_star_k(r_p, r_kv, ext=True)
+        # the sel branch moves exactly Eq. 5's bytes; the kv branch also reads
+        # the summaries it rescores every step (n*_ext)
+        ns, nx = n_star_k(r_p, r_kv), n_star_k(r_p, r_kv, ext=not once)
         mean_t = {m: t[m].mean(axis=0) for m in ("dense", mp, mk)}
-        pred, bw, cp, ck = predicted_crossing_k(contexts, mean_t, mp, mk, r_p, r_kv,
+        pred, bw, cp, ck = predicted_crossing_k(contexts, mean_t, mp, mk,
                                                 plan=lambda n, a, b: model.plan(n, a, b)[1:])
-        out["pairs"][f"{r_p}/{r_kv}"] = {
+        key = f"{r_p}/{r_kv}" + (" sel" if once else "")
+        out["pairs"][key] = {
+            "kv_policy": "select once, gathered" if once else "rescored every step",
             "n_star_k": round(ns, 2), "n_star_ext_k": round(nx, 2),
             "measured_k": None if c is None else round(c, 2),
             "measured_minus_n_star_k": None if c is None else round(c - ns, 2),
@@ -512,8 +584,8 @@ def crossover_sweep(model, contexts, blocks, steps, warmup, seed=0):
             "pred_k": None if pred is None else round(pred, 2),
             "measured_minus_pred_k": None if (c is None or pred is None) else round(c - pred, 2),
             "pred_fit": {"bw_gbs": round(bw, 1), "cost_proj_us": round(cp, 1), "cost_kv_us": round(ck, 1)}}
-        log(f"[bench] crossing {r_p}/{r_kv}: measured {c if c is None else round(c, 1)}K, "
-            f"n* {ns:.1f}K, n*_ext {nx:.1f}K, cost-aware prediction {pred if pred is None else round(pred, 1)}K")
+        log(f"[bench] crossing {key}: measured {c if c is None else round(c, 1)}K, n* {ns:.1f}K, "
+            f"n*_ext {nx:.1f}K, cost-aware prediction {pred if pred is None else round(pred, 1)}K")
     return out
 
 
