@@ -611,7 +611,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (no sharding or collectives); "
+        print("bench.py measures one GPU: the library has no multi-GPU path (no sharding or collectives); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
