@@ -80,6 +80,14 @@ struct AttnRows {
   uint4 ka[2], kb[2], va[2], vb[2];
 };
 
+// A 16-byte non-temporal load: K and V rows are read once per step, so they
+// should not displace the small vectors the kernels share in the caches.
+__device__ __forceinline__ uint4 load_nt(const uint16_t* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Rows of list positions base + u*TPL + sub (u = 0, 1), below c1; positions
 // past c1 read the row of c1-1 again (their weight is masked to zero).
 // tok maps a list position to its token.  Lane r of a row group loads dims
@@ -96,10 +104,10 @@ __device__ __forceinline__ void attn_load(const uint16_t* __restrict__ Kg, const
     const int pc = pos < c1 ? pos : c1 - 1;
     const int t = tok(pc);
     const size_t off = size_t(t) * D;
-    rw.ka[u] = *reinterpret_cast<const uint4*>(Kg + off);
-    rw.kb[u] = *reinterpret_cast<const uint4*>(Kg + off + HALF);
-    rw.va[u] = *reinterpret_cast<const uint4*>(Vg + off);
-    rw.vb[u] = *reinterpret_cast<const uint4*>(Vg + off + HALF);
+    rw.ka[u] = load_nt(Kg + off);
+    rw.kb[u] = load_nt(Kg + off + HALF);
+    rw.va[u] = load_nt(Vg + off);
+    rw.vb[u] = load_nt(Vg + off + HALF);
   }
 }
 
