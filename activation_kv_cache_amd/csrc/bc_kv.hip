@@ -33,6 +33,13 @@ constexpr int kScoreBlocksPerGroup = 256;   // one work-group per CU at 128K
 constexpr int kSelThreads = 1024;
 constexpr int kSelMaxCand = kSelThreads * 32;
 
+// A 16-byte non-temporal load: the summaries are read once per step.
+__device__ __forceinline__ uint4 load_nt16(const uint16_t* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Scores of the candidate blocks of KV head blockIdx.y (256 per work-group).
 // QP: q comes from the qkv GEMV chunk partials (rotary from the host table,
 // bf16 rounding); the first work-group of each KV head also stores q,
@@ -99,7 +106,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
     for (int it = 0; it < NIT; ++it) {
       const int c = cbeg + (it * (kScoreThreads / kWave) + w) * CPW + cs;
       const int b = p.bud.b_lo + (c < cend ? c : cbeg);
-      mm[it] = *reinterpret_cast<const uint4*>(sg + (size_t(b) * D + 4 * pp) * 2);
+      mm[it] = load_nt16(sg + (size_t(b) * D + 4 * pp) * 2);
     }
   }
 
