@@ -10,10 +10,14 @@
 // Summary layout: [n_kv_heads][n_cap/16][head_dim][2] bf16, (min, max) per
 // dim, so one 16-byte load gives 4 dims of a block.
 // Scoring: 32 lanes per block at head_dim 128 (16 at 64), lane p holds dims
-// 4p..4p+3 of every query head of the group; the fixed fp32 order is
-//   a_{j,p} = (t_{j,4p} + t_{j,4p+1}) + (t_{j,4p+2} + t_{j,4p+3}),
-//   c_p = adjacent-pair tree over j, s = adjacent-pair tree over p,
-// the last one being the xor-1,2,4,8,16 butterfly over the lanes.
+// 4p..4p+3 of the group's positive and negative query sums P_d, N_d (each
+// an adjacent-pair tree over the heads); the fixed fp32 order is
+//   t_d = fma(kmax_d, P_d, kmin_d * N_d),
+//   a_p = (t_{4p} + t_{4p+1}) + (t_{4p+2} + t_{4p+3}),
+//   s = adjacent-pair tree over p,
+// the last one being the xor-1,2,4,8,16 butterfly over the lanes.  Summed
+// over the heads, max(q kmax, q kmin) is kmax P + kmin N (kmax >= kmin), so
+// each dim costs one product pair, not one per head.
 // Selection (block_topk32, exact; equal scores keep the lower block): in the
 // decode layer every attention work-group selects the block ranks of its own
 // slice of the list in its prologue; bc_kv_score_select writes the whole
@@ -179,15 +183,28 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
     }
   }
   if (p.bud.k_blk <= 0) return;
-  // t = max(q*kmax, q*kmin) with the larger product taken only when it is
-  // strictly larger; the products are exact in fp32, so for kmax >= kmin
-  // that is q*kmax when q > 0 and kmax > kmin, else q*kmin: one product
-  // per (head, dim) instead of two
-  bool qpos[G][4];
+  // per dim the group's positive and negative query parts, each an
+  // adjacent-pair tree over the heads: sum_j max(q kmax, q kmin) is then
+  // kmax * P + kmin * N, one product pair per dim instead of one per head
+  float pq[4], nq[4];
 #pragma unroll
-  for (int j = 0; j < G; ++j)
+  for (int u = 0; u < 4; ++u) {
+    float ps[G], ns[G];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) qpos[j][u] = qf[j][u] > 0.f;
+    for (int j = 0; j < G; ++j) {
+      ps[j] = qf[j][u] > 0.f ? qf[j][u] : 0.f;
+      ns[j] = qf[j][u] > 0.f ? 0.f : qf[j][u];
+    }
+#pragma unroll
+    for (int len = G; len > 1; len >>= 1)
+#pragma unroll
+      for (int i = 0; i < len / 2; ++i) {
+        ps[i] = ps[2 * i] + ps[2 * i + 1];
+        ns[i] = ns[2 * i] + ns[2 * i + 1];
+      }
+    pq[u] = ps[0];
+    nq[u] = ns[0];
+  }
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int c = cbeg + (it * (kScoreThreads / kWave) + w) * CPW + cs;
@@ -195,22 +212,13 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
     const uint4 m4 = mm[it];
     const float mn[4] = {bf16_lo(m4.x), bf16_lo(m4.y), bf16_lo(m4.z), bf16_lo(m4.w)};
     const float mx[4] = {bf16_hi(m4.x), bf16_hi(m4.y), bf16_hi(m4.z), bf16_hi(m4.w)};
-    bool up[4];
+    float t[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) up[u] = mx[u] > mn[u];
-    float a[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      float t[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) t[u] = qf[j][u] * ((qpos[j][u] && up[u]) ? mx[u] : mn[u]);
-      a[j] = (t[0] + t[1]) + (t[2] + t[3]);
+    for (int u = 0; u < 4; ++u) {
+      const float lo = mn[u] * nq[u];
+      t[u] = __builtin_fmaf(mx[u], pq[u], lo);
     }
-#pragma unroll
-    for (int len = G; len > 1; len >>= 1)
-#pragma unroll
-      for (int i = 0; i < len / 2; ++i) a[i] = a[2 * i] + a[2 * i + 1];
-    float v = a[0];
+    float v = (t[0] + t[1]) + (t[2] + t[3]);
     v = v + dpp_f<kDppXor1>(v);
     v = v + dpp_f<kDppXor2>(v);
     v = v + dpp_f<kDppHalfMirror>(v);

@@ -261,6 +261,24 @@ class Model:
         torch.cuda.synchronize()
         return g
 
+    def layer_graph(self, n, r_p, r_kv):
+        """One bc_decode_layer call (layer 0, residual stored at the end), as a
+        graph: the per-layer latency."""
+        bc = self.bc
+        pol, _, S = self.plan(n, r_p, r_kv)
+        st = bc.make_step(n, r_p, pol, S)
+
+        def one():
+            self.h.copy_(self.h0)
+            bc.bc_decode_layer(self.md, self.c_layers[0], st, self.h, self.ws)
+        one()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one()
+        torch.cuda.synchronize()
+        return g
+
     def sel_prepare(self, n, r_kv):
         """Select once and gather (not timed): every layer scores the blocks
         of its pre-filled cache with its query, and the kept tokens (sinks,
@@ -652,7 +670,10 @@ def main():
     # the dense step at each context (the headline is the largest); the
     # other modes are timed by the crossover sweep
     cells = [(1.0, 1.0, n) for n in contexts]
-    if args.cells in ("default", "dense"):
+    if args.cells == "default":
+        for n in sorted({min(contexts), head_n}):
+            cells += [(0.5, 1.0, n), (1.0, 0.3, n), (0.5, 0.3, n)]
+    elif args.cells == "dense":
         pass
     elif args.cells == "none":
         cells = [(1.0, 1.0, head_n)]
@@ -670,12 +691,19 @@ def main():
         ms = time_graph(g, args.steps if is_head else min(args.steps, 20), args.warmup)
         del g
         b = step_bytes(n, r_p, r_kv, t_sel, S)
+        gl = model.layer_graph(n, r_p, r_kv)
+        lms = time_graph(gl, 50, args.warmup)
+        del gl
+        lb = layer_bytes(n, r_p, r_kv, t_sel, S)
         cell = {"r_p": r_p, "r_kv": r_kv, "context": n, "step_us": round(ms * 1000, 1),
                 "gbs": round(b / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "bytes": b, "t_sel": t_sel, "splits": S}
+                "bytes": b, "t_sel": t_sel, "splits": S,
+                "layer_us": round(lms * 1000, 2), "layer_bytes": lb,
+                "layer_frac_hbm": round(lb / (lms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         results.append(cell)
         log(f"[bench] r_p={r_p} r_kv={r_kv} n={n}: {cell['step_us']} us/step, {cell['gbs']} GB/s "
-            f"({100 * cell['frac_hbm']:.1f}% of 8 TB/s)")
+            f"({100 * cell['frac_hbm']:.1f}% of 8 TB/s); one layer {cell['layer_us']} us "
+            f"({100 * cell['layer_frac_hbm']:.1f}%)")
         if is_head:
             headline = (ms, b)
     for c in results:
@@ -718,6 +746,8 @@ def main():
                                       "frac": round(gemv_sp_b / gemv_sp_us / 1e3 / HBM_PEAK_GBS, 4)}},
         "cells": results,
     }
+    if args.cells == "default":
+        out["kernels"] = kernel_table(model, contexts)
     if args.cells == "default" and args.crossover_blocks > 0 and head_n >= 131072:
         sweep_ctx = [2048] + [4096 * i for i in range(1, 33)]
         out["crossover"] = crossover_sweep(model, sweep_ctx, args.crossover_blocks, args.crossover_steps,

@@ -119,13 +119,17 @@ int bc_sparse_gemv_tiled(const uint16_t* wt_packed, int d_in, int d_out, const u
 /* a4. Attention-scored KV selection (README "What it does": sinks, part of
  * the history and the recent entries), scored per 16-token block by an upper
  * bound of the query-key product built from per-block key minima and maxima.
- * For KV head g and candidate block b (see bc_kv_budget_info):
- *   t_{j,d} = max(q_{j,d}*kmax_{b,d}, q_{j,d}*kmin_{b,d})         (fp32, exact)
- *   a_{j,p} = (t_{j,4p} + t_{j,4p+1}) + (t_{j,4p+2} + t_{j,4p+3})
- *   c_p     = adjacent-pair tree over the group's heads j of a_{j,p}
- *   s_{g,b} = adjacent-pair tree over p = 0..head_dim/4-1 of c_p
+ * For KV head g and candidate block b (see bc_kv_budget_info), with the
+ * group's query heads j:
+ *   P_d = adjacent-pair tree over j of (q_{j,d} > 0 ? q_{j,d} : 0)
+ *   N_d = adjacent-pair tree over j of (q_{j,d} > 0 ? 0 : q_{j,d})
+ *   t_d = fma(kmax_{b,d}, P_d, kmin_{b,d} * N_d)   (the product kmin*N rounded first)
+ *   a_p = (t_{4p} + t_{4p+1}) + (t_{4p+2} + t_{4p+3})
+ *   s_{g,b} = adjacent-pair tree over p = 0..head_dim/4-1 of a_p
  * (adjacent-pair tree: v_i <- v_{2i} + v_{2i+1} until one value remains;
- * fp32 in exactly this order).  The k_blk highest scores are kept (equal
+ * fp32 in exactly this order).  In real arithmetic (kmax >= kmin)
+ * t_d = sum_j max(q_{j,d}*kmax_{b,d}, q_{j,d}*kmin_{b,d}), so s bounds
+ * sum_j q_j . k_t from above for every token t of the block.  The k_blk highest scores are kept (equal
  * scores: lower block); idx_out[g] = sinks, kept blocks' tokens and the
  * window, ascending.
  *   q        bf16 [n_heads][head_dim] post-rotary query; query head j reads

@@ -272,35 +272,43 @@ static float orc_pair_tree(float* v, int len)
 }
 
 /* Score of one candidate block for one KV head: an upper bound of q_j . k_t
- * over the block's tokens, summed over the G query heads of the group:
- *   t_{j,d} = max(q_{j,d} * kmax_d, q_{j,d} * kmin_d)   (exact in float)
- *   a_{j,p} = (t_{j,4p} + t_{j,4p+1}) + (t_{j,4p+2} + t_{j,4p+3})
- *   c_p     = adjacent-pair tree over j of a_{j,p}
- *   s       = adjacent-pair tree over p = 0 .. D/4-1 of c_p
- * all in float, in exactly this order.  q is [G][D] bf16, summ is [D][2].   */
+ * over the block's tokens, summed over the G query heads of the group.  Per
+ * dim d the group's positive and negative query parts are summed first,
+ *   P_d = adjacent-pair tree over j of (q_{j,d} > 0 ? q_{j,d} : 0)
+ *   N_d = adjacent-pair tree over j of (q_{j,d} > 0 ? 0 : q_{j,d}),
+ * since sum_j max(q kmax, q kmin) = kmax P + kmin N when kmax >= kmin; then
+ *   t_d = fmaf(kmax_d, P_d, kmin_d * N_d)
+ *   a_p = (t_{4p} + t_{4p+1}) + (t_{4p+2} + t_{4p+3})
+ *   s   = adjacent-pair tree over p = 0 .. D/4-1 of a_p
+ * all in float, in exactly this order.  q is [G][D] bf16, summ is [D][2]. */
 float orc_block_score(const uint16_t* q, const uint16_t* summ, int G, int D)
 {
     int P = D / 4;
-    float* c = (float*)malloc(sizeof(float) * (size_t)P);
-    float* aj = (float*)malloc(sizeof(float) * (size_t)G);
+    float* a = (float*)malloc(sizeof(float) * (size_t)P);
+    float* pos = (float*)malloc(sizeof(float) * (size_t)G);
+    float* neg = (float*)malloc(sizeof(float) * (size_t)G);
     for (int p = 0; p < P; ++p) {
-        for (int j = 0; j < G; ++j) {
-            float t[4];
-            for (int u = 0; u < 4; ++u) {
-                int d = 4 * p + u;
+        float t[4];
+        for (int u = 0; u < 4; ++u) {
+            int d = 4 * p + u;
+            for (int j = 0; j < G; ++j) {
                 float qv = (float)orc_bf16_to_double(q[(size_t)j * D + d]);
-                float mn = (float)orc_bf16_to_double(summ[(size_t)d * 2 + 0]);
-                float mx = (float)orc_bf16_to_double(summ[(size_t)d * 2 + 1]);
-                float a = qv * mx, b = qv * mn;
-                t[u] = a > b ? a : b;
+                pos[j] = qv > 0.0f ? qv : 0.0f;
+                neg[j] = qv > 0.0f ? 0.0f : qv;
             }
-            aj[j] = (t[0] + t[1]) + (t[2] + t[3]);
+            float pd = orc_pair_tree(pos, G);
+            float nd = orc_pair_tree(neg, G);
+            float mn = (float)orc_bf16_to_double(summ[(size_t)d * 2 + 0]);
+            float mx = (float)orc_bf16_to_double(summ[(size_t)d * 2 + 1]);
+            float lo = mn * nd;
+            t[u] = fmaf(mx, pd, lo);
         }
-        c[p] = orc_pair_tree(aj, G);
+        a[p] = (t[0] + t[1]) + (t[2] + t[3]);
     }
-    float s = orc_pair_tree(c, P);
-    free(aj);
-    free(c);
+    float s = orc_pair_tree(a, P);
+    free(neg);
+    free(pos);
+    free(a);
     return s;
 }
 

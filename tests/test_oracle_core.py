@@ -206,25 +206,26 @@ def test_block_score_rounding_and_bound():
 
 
 def test_block_score_exact_order_small():
-    """With values chosen so float rounding matters, the oracle's order
-    (pairs of 4 dims, then heads by adjacent pairs, then dim-groups by adjacent
-    pairs) gives a sum that a different order would not."""
-    G, D = 2, 8
-    q = np.ones((G, D), np.float32)
-    big, tiny = 2.0 ** 24, 1.0
-    mx = np.array([big, tiny, tiny, tiny, -big, tiny, tiny, tiny], np.float32)
-    summ = np.stack([mx, mx], axis=1)
+    """With values chosen so float rounding matters, the oracle's order (per
+    dim the heads' positive parts summed first, then one product pair per dim,
+    pairs of 4 dims, then dim-groups by adjacent pairs) gives a sum that a
+    per-head order would not."""
+    G, D = 2, 4
+    q = np.array([[2.0 ** 24, 0, 0, 0], [1, 1, 0, 0]], np.float32)
+    k = np.array([1, 1, 0, 0], np.float32)
+    summ = np.stack([k, k], axis=1)          # kmin = kmax
     s = oracle.block_score(gen.to_bf16_bits(q), gen.to_bf16_bits(summ))
-    # a_{j,0} = fl(fl(2^24 + 1) + 2) = 2^24 + 2   (2^24 + 1 rounds to even, 2^24)
-    # a_{j,1} = (-2^24 + 1) + 2 = -2^24 + 3       (exact below 2^24)
-    # c_0 = 2^25 + 4, c_1 = -2^25 + 6  ->  s = 10, while the exact sum is 12
-    assert s == 10.0
-    assert abs(_score64(gen.to_bf16_bits(q), gen.to_bf16_bits(summ)) - 12.0) < 1e-9
-    # a plain left-to-right float sum per head would give 3 per head (6 in all)
-    acc = np.float32(0)
-    for v in mx:
-        acc = np.float32(acc + np.float32(v))
-    assert float(acc) == 3.0
+    # P_0 = fl(2^24 + 1) = 2^24 (ties to even), P_1 = 1; t = (2^24, 1, 0, 0);
+    # a = fl(2^24 + 1) + 0 = 2^24
+    assert s == 2.0 ** 24
+    # the exact bound is 2^24 + 2, which a per-head order (head 1 summed to 2
+    # first) would also give
+    assert abs(_score64(gen.to_bf16_bits(q), gen.to_bf16_bits(summ)) - (2.0 ** 24 + 2)) < 1e-9
+    # the negative parts take the minima: q = -1 on a block with kmin = -3,
+    # kmax = 5 contributes (-1) * (-3) = 3, the larger of -5 and 3
+    q2 = np.array([[-1, 0, 0, 0]], np.float32)
+    summ2 = np.array([[-3, 5], [0, 0], [0, 0], [0, 0]], np.float32)
+    assert oracle.block_score(gen.to_bf16_bits(q2), gen.to_bf16_bits(summ2)) == 3.0
 
 
 def _brute_kv_select(q, summ, n, H, Hkv, r_kv, sinks, window):
