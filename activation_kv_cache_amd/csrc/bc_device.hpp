@@ -303,115 +303,6 @@ __device__ void block_topk_reg(int n, int k, EmitFn emit, TopkSmem<NT, KeyT>& sm
   __syncthreads();
 }
 
-// ------------------------------------------- 15-bit keys, one histogram pass
-// Exact top-k of n <= 16384 keys below 2^15 (bf16 magnitudes) with 1024
-// threads: thread t owns positions [t*E, t*E + E), E = ceil(n/1024), its keys
-// in registers.  One pass of LDS atomics builds the full 32768-bin histogram
-// (equal keys in one wave instruction are rare, so the atomics hardly
-// collide); a block scan over the bins, taken from the largest key down,
-// finds the threshold key thr and the number `need` of keys equal to thr that
-// are kept; one block scan of (ties, greater) counts then places every kept
-// position (ties kept before thread t: min(ties before t, need)).
-constexpr int kTopk15Threads = 1024;
-constexpr int kTopk15MaxN = kTopk15Threads * 16;
-
-struct Topk15Smem {
-  uint32_t hist[32768];
-  uint32_t wtot[kTopk15Threads / kWave];
-  uint32_t thr, above;
-};
-
-template <typename KeyFn, typename EmitFn>
-__device__ void block_topk15(int n, int k, KeyFn key_of, EmitFn emit, Topk15Smem& sm) {
-  constexpr int NT = kTopk15Threads;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int E = (n + NT - 1) / NT;
-  const int i0 = tid * E;
-  const int nv = max(0, min(E, n - i0));
-  if (k >= n) {
-    for (int e = 0; e < nv; ++e) emit(i0 + e, i0 + e);
-    return;
-  }
-  if (k <= 0) return;
-  uint32_t key[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) key[e] = e < nv ? (uint32_t(key_of(i0 + e)) & 0x7FFFu) : 0u;
-  uint4* h4 = reinterpret_cast<uint4*>(sm.hist);
-  for (int i = tid; i < 32768 / 4; i += NT) h4[i] = make_uint4(0, 0, 0, 0);
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < 16; ++e)
-    if (e < nv) atomicAdd(&sm.hist[key[e]], 1u);
-  __syncthreads();
-  // thread t owns the 32 bins [b0, b0 + 32), b0 = 32768 - 32 (t + 1): the
-  // largest keys go to thread 0, so the prefix over threads counts larger keys
-  const int b0 = 32768 - 32 * (tid + 1);
-  // neighbouring threads' ranges are 128 B apart (one LDS bank): read the
-  // eight 16-byte pieces in a thread-rotated order to spread the banks
-  uint32_t bins[32];
-  uint32_t local = 0;
-  {
-    const uint4* hb = reinterpret_cast<const uint4*>(sm.hist + b0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int jj = (j + tid) & 7;
-      const uint4 c = hb[jj];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (q == jj) {
-          bins[4 * q] = c.x; bins[4 * q + 1] = c.y; bins[4 * q + 2] = c.z; bins[4 * q + 3] = c.w;
-        }
-      }
-      local += (c.x + c.y) + (c.z + c.w);
-    }
-  }
-  const uint32_t winc = wave_scan_dpp(local);
-  if (lane == kWave - 1) sm.wtot[w] = winc;
-  __syncthreads();
-  uint32_t before = 0;
-  for (int ww = 0; ww < w; ++ww) before += sm.wtot[ww];
-  const uint32_t inc = before + winc, ex = inc - local;
-  const uint32_t ku = uint32_t(k);
-  if (ex < ku && ku <= inc) {
-    uint32_t run = ex;
-#pragma unroll
-    for (int j = 31; j >= 0; --j) {
-      const uint32_t c = bins[j];
-      if (run < ku && ku <= run + c) { sm.thr = uint32_t(b0 + j); sm.above = run; }
-      run += c;
-    }
-  }
-  __syncthreads();
-  const uint32_t thr = sm.thr, need = ku - sm.above;
-  uint32_t gt = 0, eq = 0;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    gt += (e < nv && key[e] > thr) ? 1u : 0u;
-    eq += (e < nv && key[e] == thr) ? 1u : 0u;
-  }
-  const uint32_t v = (eq << 16) | gt;
-  const uint32_t vinc = wave_scan_dpp(v);
-  __syncthreads();
-  if (lane == kWave - 1) sm.wtot[w] = vinc;
-  __syncthreads();
-  uint32_t vb = vinc - v;
-  for (int ww = 0; ww < w; ++ww) vb += sm.wtot[ww];
-  const uint32_t gt_before = vb & 0xFFFFu, eq_before = vb >> 16;
-  uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
-  uint32_t tie = eq_before;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    if (e >= nv) continue;
-    if (key[e] > thr) {
-      emit(int(pos++), i0 + e);
-    } else if (key[e] == thr) {
-      if (tie < need) emit(int(pos++), i0 + e);
-      ++tie;
-    }
-  }
-  __syncthreads();
-}
-
 // Exact top-k over n integer keys given by key_fn(i) (the low BITS bits are
 // used; BITS in {15, 32}).  Keeps the k largest keys, equal keys by lower
 // position, and calls emit(rank, i) for every kept position, rank being its

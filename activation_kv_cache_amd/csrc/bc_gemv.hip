@@ -484,25 +484,32 @@ __global__ __launch_bounds__(256) void k_argmax_finish(const float* tile_max, co
 
 constexpr int kOneGroup = 1024;
 
-struct OneGroupSmem {
-  union {
-    TopkSmem<kOneGroup, uint16_t> topk;
-    Topk15Smem topk15;
-  };
-};
-
-__device__ void one_group_select(const uint16_t* x, int n, int k, int32_t* idx_out, OneGroupSmem& sm) {
-  auto key = [x](int i) -> uint32_t { return uint32_t(x[i]) & 0x7FFFu; };
-  auto emit = [idx_out](int r, int i) { idx_out[r] = i; };
-  if (n <= kTopk15MaxN)
-    block_topk15(n, k, key, emit, sm.topk15);
-  else
-    block_topk<kOneGroup, 15, uint16_t>(n, k, key, emit, sm.topk);
+// bc_select_channels: one 1024-lane work-group.  Up to 16384 channels the
+// keys sit in registers (16 per thread at most) and block_topk_2pass ranks
+// them -- the selection every GEMV work-group runs in its prologue; larger
+// inputs take the 4-bit radix select over keys read from memory.
+template <int PMAX>
+__global__ __launch_bounds__(kOneGroup) void k_select_reg(const uint16_t* x, int n, int k, int32_t* idx_out) {
+  __shared__ Topk2Smem<kOneGroup, kTopkShift> tk;
+  const int P = ((n + kOneGroup - 1) / kOneGroup + 3) & ~3;
+  const int c0 = int(threadIdx.x) * P;
+  topk2_clear<kOneGroup>(tk);
+  uint32_t key[PMAX];
+#pragma unroll
+  for (int e = 0; e < PMAX; ++e) {
+    const int c = c0 + e;
+    key[e] = (e < P && c < n) ? (uint32_t(x[c]) & 0x7FFFu) : 0u;
+  }
+  __syncthreads();
+  auto emit = [&](int pos, int e) { idx_out[pos] = c0 + e; };
+  block_topk_2pass<kOneGroup, kTopkShift, PMAX>(key, P, n, k, 0, k, true, emit, tk);
 }
 
 __global__ __launch_bounds__(kOneGroup) void k_select(const uint16_t* x, int n, int k, int32_t* idx_out) {
-  __shared__ OneGroupSmem sm;
-  one_group_select(x, n, k, idx_out, sm);
+  __shared__ TopkSmem<kOneGroup, uint16_t> sm;
+  auto key = [x](int i) -> uint32_t { return uint32_t(x[i]) & 0x7FFFu; };
+  auto emit = [idx_out](int r, int i) { idx_out[r] = i; };
+  block_topk<kOneGroup, 15, uint16_t>(n, k, key, emit, sm);
 }
 
 
@@ -601,7 +608,12 @@ int launch_argmax_finish(const float* tile_max, const int32_t* tile_arg, int n_t
 }
 
 int launch_select(const uint16_t* x, int n, int k, int32_t* idx_out, hipStream_t s) {
-  k_select<<<1, kOneGroup, 0, s>>>(x, n, k, idx_out);
+  if (n <= kOneGroup * 4)
+    k_select_reg<4><<<1, kOneGroup, 0, s>>>(x, n, k, idx_out);
+  else if (n <= kOneGroup * 16)
+    k_select_reg<16><<<1, kOneGroup, 0, s>>>(x, n, k, idx_out);
+  else
+    k_select<<<1, kOneGroup, 0, s>>>(x, n, k, idx_out);
   return check_launch("k_select");
 }
 

@@ -33,6 +33,11 @@ SELECT_CASES = [
     ("k-n-minus-1", 300, 299, "ladder2"),
     ("ragged-small", 5, 3, "normal"),
     ("max-n", 65536, 40000, "outlier"),
+    # the edges of the register-key paths (4 and 16 keys per thread) and the
+    # radix path above them
+    ("regs4-edge", 4097, 2049, "ladder5"),
+    ("regs16-edge", 16384, 8191, "ladder7"),
+    ("radix-edge", 16385, 8192, "outlier"),
 ]
 
 
