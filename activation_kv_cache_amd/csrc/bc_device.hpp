@@ -131,28 +131,6 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
   return v;
 }
 
-// Block-wide exclusive prefix sum of one value per thread; returns the
-// thread's exclusive prefix and writes the block total to *total.
-// scratch must hold NT/64 + 1 uint32 in LDS.  Contains __syncthreads().
-template <int NT>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
-  constexpr int NW = NT / kWave;
-  const int lane = wave_lane(), w = threadIdx.x >> 6;
-  uint32_t inc = wave_inclusive_scan(v);
-  if (lane == kWave - 1) scratch[w] = inc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int i = 0; i < NW; ++i) { uint32_t t = scratch[i]; scratch[i] = run; run += t; }
-    scratch[NW] = run;
-  }
-  __syncthreads();
-  uint32_t ex = scratch[w] + inc - v;
-  *total = scratch[NW];
-  __syncthreads();
-  return ex;
-}
-
 // ------------------------------------------------------- split partials
 // Sum of the n_splits chunk partials of column c, in chunk order.  Up to 8
 // chunks are loaded at once (one memory round trip for the usual plans).
