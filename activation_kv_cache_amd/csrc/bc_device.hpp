@@ -459,6 +459,16 @@ __device__ __forceinline__ uint32_t waves_before(const uint32_t* tot, int w) {
   return w == 0 ? 0u : uint32_t(__builtin_amdgcn_readlane(int(inc), w - 1));
 }
 
+// Sum of wave totals tot[0..w) and of all NW of them, lane-parallel.
+template <int NW>
+__device__ __forceinline__ void waves_before_total(const uint32_t* tot, int w, uint32_t* before, uint32_t* total) {
+  static_assert(NW <= 16, "one DPP row");
+  const int lane = threadIdx.x & 63;
+  const uint32_t inc = row16_scan(lane < NW ? tot[lane] : 0u);
+  *before = w == 0 ? 0u : uint32_t(__builtin_amdgcn_readlane(int(inc), w - 1));
+  *total = uint32_t(__builtin_amdgcn_readlane(int(inc), NW - 1));
+}
+
 template <int NT, int SHIFT, int PMAX, typename EmitFn>
 __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int k, int r0, int r1, bool all,
                                  EmitFn emit, Topk2Smem<NT, SHIFT>& sm) {
@@ -656,9 +666,7 @@ __device__ __forceinline__ void topk32_pick_bin(uint32_t k_rem, Topk32Smem<NT>& 
   const uint32_t winc = wave_scan_dpp(local);
   if (lane == kWave - 1) sm.whi[w] = winc;
   __syncthreads();
-  uint32_t before = 0;
-#pragma unroll
-  for (int ww = 0; ww < NW; ++ww) before += ww < w ? sm.whi[ww] : 0u;
+  const uint32_t before = waves_before<NW>(sm.whi, __builtin_amdgcn_readfirstlane(w));
   const uint32_t inc = before + winc, ex = inc - local;
   if (ex < k_rem && k_rem <= inc) {
     uint32_t run = ex;
@@ -691,10 +699,9 @@ __device__ void block_topk32(const uint32_t (&key)[PMAX], int P, int n, int k, i
     for (int i = tid; i < 2048 / 4; i += NT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
   }
   __syncthreads();
-  kmin = sm.wlo[0];
-  kmax = sm.whi[0];
-#pragma unroll
-  for (int ww = 1; ww < NW; ++ww) { kmin = min(kmin, sm.wlo[ww]); kmax = max(kmax, sm.whi[ww]); }
+  // every wave reduces the wave minima and maxima itself, one per lane
+  kmin = wave_min_u32(lane < NW ? sm.wlo[lane] : ~0u);
+  kmax = wave_max_u32(lane < NW ? sm.whi[lane] : 0u);
   const uint32_t range = kmax - kmin;
   const int shift = range == 0u ? 0 : max(0, 32 - __clz(int(range)) - 11);   // (range >> shift) < 2048
   __syncthreads();   // whi is reused by the scans
@@ -723,12 +730,9 @@ __device__ void block_topk32(const uint32_t (&key)[PMAX], int P, int n, int k, i
     const uint32_t cinc = wave_scan_dpp(cnt);
     if (lane == kWave - 1) sm.whi[w] = cinc;
     __syncthreads();
-    uint32_t off = cinc - cnt, nc = 0;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      off += ww < w ? sm.whi[ww] : 0u;
-      nc += sm.whi[ww];
-    }
+    uint32_t off, nc;
+    waves_before_total<NW>(sm.whi, __builtin_amdgcn_readfirstlane(w), &off, &nc);
+    off += cinc - cnt;
     if (inb != 0u && off < uint32_t(Topk32Smem<NT>::kCandCap)) {
 #pragma unroll
       for (int e = 0; e < PMAX; ++e) {
@@ -788,9 +792,7 @@ __device__ void block_topk32(const uint32_t (&key)[PMAX], int P, int n, int k, i
   const uint32_t inc = wave_scan_dpp(v);
   if (lane == kWave - 1) sm.whi[w] = inc;
   __syncthreads();
-  uint32_t bf = inc - v;
-#pragma unroll
-  for (int ww = 0; ww < NW; ++ww) bf += ww < w ? sm.whi[ww] : 0u;
+  const uint32_t bf = inc - v + waves_before<NW>(sm.whi, __builtin_amdgcn_readfirstlane(w));
   const uint32_t gt_before = bf & 0xFFFFu, eq_before = bf >> 16;
   const uint32_t ties_before = eq_before < need ? eq_before : need;
   const uint32_t ties_here = (eq_before + eq < need ? eq_before + eq : need) - ties_before;
