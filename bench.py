@@ -619,9 +619,11 @@ def main():
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="only copy this many bytes 5 times (calibration of the HBM byte counters)")
     ap.add_argument("--split-sweep", default="", help="attention split counts to sweep in --kernels")
-    ap.add_argument("--crossover-blocks", type=int, default=1,
+    ap.add_argument("--crossover-blocks", type=int, default=3,
                     help="blocks of the crossover sweep (every mode at 2K, 4K, ..., 128K); 0 skips it")
     ap.add_argument("--crossover-steps", type=int, default=10, help="timed steps per sweep cell")
+    ap.add_argument("--crossover-max-k", type=int, default=160,
+                    help="largest context of the crossover sweep, in units of 1024 tokens (multiple of 4)")
     ap.add_argument("--gemv-only", default="",
                     help="reps:r_p -- only launch the gate|up GEMV reps times per layer (for counters)")
     ap.add_argument("--attn-only", type=int, default=0,
@@ -647,7 +649,12 @@ def main():
 
     contexts = [int(c) for c in args.contexts.split(",")]
     head_n = max(contexts)
-    model = Model(max_ctx=max(contexts))
+    sweep = (args.cells == "default" and args.crossover_blocks > 0 and head_n >= 131072 and not args.kernels
+             and not args.attn_only and not args.gemv_only)
+    # the crossover sweep runs past the headline context (to 160K tokens), so
+    # that the 0.5/0.5 crossing (n*_ext 118.9K) is bracketed by measured cells
+    sweep_ctx = [2048] + [4096 * i for i in range(1, args.crossover_max_k // 4 + 1)] if sweep else []
+    model = Model(max_ctx=max(contexts + sweep_ctx))
 
     if args.kernels:
         sweep = [int(x) for x in args.split_sweep.split(",") if x]
@@ -748,8 +755,7 @@ def main():
     }
     if args.cells == "default":
         out["kernels"] = kernel_table(model, contexts)
-    if args.cells == "default" and args.crossover_blocks > 0 and head_n >= 131072:
-        sweep_ctx = [2048] + [4096 * i for i in range(1, 33)]
+    if sweep:
         out["crossover"] = crossover_sweep(model, sweep_ctx, args.crossover_blocks, args.crossover_steps,
                                            min(args.warmup, 3))
     if not args.no_cpu_baseline:
