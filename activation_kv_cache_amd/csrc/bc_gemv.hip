@@ -486,23 +486,40 @@ constexpr int kOneGroup = 1024;
 
 // bc_select_channels: one 1024-lane work-group.  Up to 16384 channels the
 // keys sit in registers (16 per thread at most) and block_topk_2pass ranks
-// them -- the selection every GEMV work-group runs in its prologue; larger
+// them -- the selection every GEMV work-group runs in its prologue; the
+// ascending list is staged in LDS and stored with coalesced writes.  Larger
 // inputs take the 4-bit radix select over keys read from memory.
 template <int PMAX>
 __global__ __launch_bounds__(kOneGroup) void k_select_reg(const uint16_t* x, int n, int k, int32_t* idx_out) {
   __shared__ Topk2Smem<kOneGroup, kTopkShift> tk;
+  __shared__ int32_t list[kOneGroup * PMAX];
   const int P = ((n + kOneGroup - 1) / kOneGroup + 3) & ~3;
   const int c0 = int(threadIdx.x) * P;
   topk2_clear<kOneGroup>(tk);
   uint32_t key[PMAX];
+  if ((n & 3) == 0 && (reinterpret_cast<uintptr_t>(x) & 7) == 0) {
+    // 8-byte loads of 4 channels (n a multiple of 4: a group is all in or out)
 #pragma unroll
-  for (int e = 0; e < PMAX; ++e) {
-    const int c = c0 + e;
-    key[e] = (e < P && c < n) ? (uint32_t(x[c]) & 0x7FFFu) : 0u;
+    for (int q = 0; q < PMAX / 4; ++q) {
+      uint2 v = make_uint2(0u, 0u);
+      if (4 * q < P && c0 + 4 * q < n) v = *reinterpret_cast<const uint2*>(x + c0 + 4 * q);
+      key[4 * q] = v.x & 0x7FFFu;
+      key[4 * q + 1] = (v.x >> 16) & 0x7FFFu;
+      key[4 * q + 2] = v.y & 0x7FFFu;
+      key[4 * q + 3] = (v.y >> 16) & 0x7FFFu;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < PMAX; ++e) {
+      const int c = c0 + e;
+      key[e] = (e < P && c < n) ? (uint32_t(x[c]) & 0x7FFFu) : 0u;
+    }
   }
   __syncthreads();
-  auto emit = [&](int pos, int e) { idx_out[pos] = c0 + e; };
+  auto emit = [&](int pos, int e) { list[pos] = c0 + e; };
   block_topk_2pass<kOneGroup, kTopkShift, PMAX>(key, P, n, k, 0, k, true, emit, tk);
+  __syncthreads();
+  for (int i = threadIdx.x; i < k; i += kOneGroup) idx_out[i] = list[i];
 }
 
 __global__ __launch_bounds__(kOneGroup) void k_select(const uint16_t* x, int n, int k, int32_t* idx_out) {
