@@ -197,8 +197,8 @@ __device__ void select_block_ranks(const float* sc, int n, int k_blk, int r_lo, 
   uint32_t key[PM];
   const int P = load_score_keys<NT, PM>(sc, n, key, tk.hist);
   const int tid = threadIdx.x;
-  auto emit = [&](int rank, int e) { blk[rank - r_lo] = tid * P + e; };
-  block_topk32<NT, PM>(key, P, n, k_blk, r_lo, r_hi, false, emit, tk);
+  auto emit = [&](int rel, int e) { blk[rel] = tid * P + e; };
+  block_topk32<NT, PM>(key, P, n, k_blk, r_lo, r_hi, emit, tk);
 }
 
 template <int D, int G, int QM, int LM>

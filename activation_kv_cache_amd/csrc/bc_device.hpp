@@ -410,8 +410,9 @@ __device__ void block_topk(int n, int k, KeyFn key_fn, EmitFn emit, TopkSmem<NT,
 // (the lowest positions).  One block scan of (ties, greater) counts per
 // thread gives each thread the rank of its first kept key; ranks within the
 // thread come from popcounts of the kept-key bit mask, so no thread walks its
-// keys serially.  emit(rank, e) is called for the thread's e-th key when it
-// is kept and its rank is in [r0, r1), or for every kept key when `all`.
+// keys serially.  emit(rank - r0, e) is called for the thread's e-th key when
+// it is kept and its rank is in [r0, r1); with `all`, out(rank, e) is also
+// called for every kept key.
 //
 // All NT threads execute every instruction of the block-wide steps, so the
 // searches over wave totals and over the low digit run lane-parallel (one
@@ -469,9 +470,37 @@ __device__ __forceinline__ void waves_before_total(const uint32_t* tot, int w, u
   *total = uint32_t(__builtin_amdgcn_readlane(int(inc), NW - 1));
 }
 
-template <int NT, int SHIFT, int PMAX, typename EmitFn>
-__device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int k, int r0, int r1, bool all,
-                                 EmitFn emit, Topk2Smem<NT, SHIFT>& sm) {
+// Emission of one thread's kept keys: the i-th set bit of `take` (low bits
+// first) holds rank pos0 + i.  emit(rank - r0, e) for ranks in [r0, r1), one
+// popcount, compare and store per key and no branch but the store's own;
+// with `all`, out(rank, e) for every kept key.  Threads whose ranks miss
+// [r0, r1) skip the loop.
+struct TopkNoOut {
+  __device__ void operator()(int, int) const {}
+};
+
+template <int PMAX, typename EmitFn, typename OutFn>
+__device__ __forceinline__ void topk_emit_kept(uint32_t take, uint32_t pos0, uint32_t cnt, int r0, int r1, bool all,
+                                               EmitFn& emit, OutFn& out) {
+  if (all) {
+#pragma unroll
+    for (int e = 0; e < PMAX; ++e)
+      if ((take >> e) & 1u) out(int(pos0 + uint32_t(__popc(take & ((1u << e) - 1u)))), e);
+  }
+  if (pos0 < uint32_t(r1) && pos0 + cnt > uint32_t(r0)) {
+    const uint32_t span = uint32_t(r1 - r0);
+    const uint32_t rel0 = pos0 - uint32_t(r0);   // wraps below r0: those ranks fail rel < span
+#pragma unroll
+    for (int e = 0; e < PMAX; ++e) {
+      const uint32_t rel = rel0 + uint32_t(__popc(take & ((1u << e) - 1u)));
+      if (((take >> e) & 1u) && rel < span) emit(int(rel), e);
+    }
+  }
+}
+
+template <int NT, int SHIFT, int PMAX, typename EmitFn, typename OutFn = TopkNoOut>
+__device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int k, int r0, int r1, EmitFn emit,
+                                 Topk2Smem<NT, SHIFT>& sm, bool all = false, OutFn out = OutFn()) {
   static_assert(PMAX <= 32, "bit masks are 32 bits");
   constexpr int NB = Topk2Smem<NT, SHIFT>::NB;
   constexpr int NB2 = 1 << SHIFT;
@@ -573,18 +602,7 @@ __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int 
       m ^= low;
     }
   }
-  const uint32_t take = gtm | tie_keep;
-  const uint32_t pos0 = gt_before + ties_before;
-  const uint32_t cnt = gt + ties_here;
-  if (all || (pos0 < uint32_t(r1) && pos0 + cnt > uint32_t(r0))) {
-#pragma unroll
-    for (int e = 0; e < PMAX; ++e) {
-      if ((take >> e) & 1u) {
-        const uint32_t pos = pos0 + uint32_t(__popc(take & ((1u << e) - 1u)));
-        if (all || (pos >= uint32_t(r0) && pos < uint32_t(r1))) emit(int(pos), e);
-      }
-    }
-  }
+  topk_emit_kept<PMAX>(gtm | tie_keep, gt_before + ties_before, gt + ties_here, r0, r1, all, emit, out);
 }
 
 // --------------------------------------- 32-bit keys in registers, adaptive
@@ -596,8 +614,8 @@ __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int 
 // Later passes resolve the chosen bin 13 bits at a time (8192 bins) until
 // the threshold key thr is exact; the number `need` of keys equal to thr
 // that are kept follows.  The ranks come from one block scan of (ties,
-// greater) and per-thread popcounts, as in block_topk_2pass; emit(rank, e)
-// for kept keys whose rank is in [r0, r1), or every kept key when `all`.
+// greater) and per-thread popcounts, as in block_topk_2pass; emit(rank - r0,
+// e) for kept keys whose rank is in [r0, r1).
 // Requires 1 <= k <= n <= NT * PMAX, PMAX <= 32, n < 65536.  Contains
 // __syncthreads(); the caller synchronises before reading what emit wrote.
 template <int NT>
@@ -680,8 +698,10 @@ __device__ __forceinline__ void topk32_pick_bin(uint32_t k_rem, Topk32Smem<NT>& 
 }
 
 template <int NT, int PMAX, typename EmitFn>
-__device__ void block_topk32(const uint32_t (&key)[PMAX], int P, int n, int k, int r0, int r1, bool all,
-                             EmitFn emit, Topk32Smem<NT>& sm) {
+__device__ void block_topk32(const uint32_t (&key)[PMAX], int P, int n, int k, int r0, int r1, EmitFn emit,
+                             Topk32Smem<NT>& sm) {
+  const bool all = false;
+  TopkNoOut out;
   static_assert(PMAX <= 32, "bit masks are 32 bits");
   constexpr int NW = NT / kWave;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -806,18 +826,7 @@ __device__ void block_topk32(const uint32_t (&key)[PMAX], int P, int n, int k, i
       m ^= low;
     }
   }
-  const uint32_t take = gtm | tie_keep;
-  const uint32_t pos0 = gt_before + ties_before;
-  const uint32_t cnt = gt + ties_here;
-  if (all || (pos0 < uint32_t(r1) && pos0 + cnt > uint32_t(r0))) {
-#pragma unroll
-    for (int e = 0; e < PMAX; ++e) {
-      if ((take >> e) & 1u) {
-        const uint32_t pos = pos0 + uint32_t(__popc(take & ((1u << e) - 1u)));
-        if (all || (pos >= uint32_t(r0) && pos < uint32_t(r1))) emit(int(pos), e);
-      }
-    }
-  }
+  topk_emit_kept<PMAX>(gtm | tie_keep, gt_before + ties_before, gt + ties_here, r0, r1, all, emit, out);
 }
 
 // Keys of n fp32 scores for block_topk32, thread t owning positions

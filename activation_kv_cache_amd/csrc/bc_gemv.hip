@@ -228,17 +228,14 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
       uint32_t key[PMAX];
 #pragma unroll
       for (int e = 0; e < PMAX; ++e) key[e] = ((xb[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) & 0x7FFFu;
-      int32_t* idx_out = lead ? p.idx_out : nullptr;
-      auto emit = [&](int pos, int e) {
-        const int c = c0 + e;
-        if (pos >= r0 && pos < r1) {
-          sm.list.ch[pos - r0] = c;
-          sm.list.xv[pos - r0] = bf16_elt(xb, e);
-        }
-        if (idx_out && pos < p.k) idx_out[pos] = c;
+      int32_t* idx_out = p.idx_out;
+      auto emit = [&](int rel, int e) {
+        sm.list.ch[rel] = c0 + e;
+        sm.list.xv[rel] = bf16_elt(xb, e);
       };
-      block_topk_2pass<kGemvThreads, kTopkShift, PMAX>(key, P, p.d_in, p.k, r0, r1, idx_out != nullptr, emit,
-                                                       sm.tk);
+      auto out = [&](int pos, int e) { idx_out[pos] = c0 + e; };
+      block_topk_2pass<kGemvThreads, kTopkShift, PMAX>(key, P, p.d_in, p.k, r0, r1, emit, sm.tk,
+                                                       lead && idx_out != nullptr, out);
     }
   }
   __syncthreads();
@@ -517,7 +514,7 @@ __global__ __launch_bounds__(kOneGroup) void k_select_reg(const uint16_t* x, int
   }
   __syncthreads();
   auto emit = [&](int pos, int e) { list[pos] = c0 + e; };
-  block_topk_2pass<kOneGroup, kTopkShift, PMAX>(key, P, n, k, 0, k, true, emit, tk);
+  block_topk_2pass<kOneGroup, kTopkShift, PMAX>(key, P, n, k, 0, k, emit, tk);
   __syncthreads();
   for (int i = threadIdx.x; i < k; i += kOneGroup) idx_out[i] = list[i];
 }

@@ -262,13 +262,13 @@ __global__ __launch_bounds__(kSelThreads) void k_kv_block_select(const KvSelectP
     // up to 8 keys per thread, staged through LDS (coalesced loads)
     uint32_t key[8];
     const int P = load_score_keys<kSelThreads, 8>(sc, n, key, sm.hist);
-    block_topk32<kSelThreads, 8>(key, P, n, bd.k_blk, 0, bd.k_blk, true, emit_for(P), sm);
+    block_topk32<kSelThreads, 8>(key, P, n, bd.k_blk, 0, bd.k_blk, emit_for(P), sm);
   } else {
     const int P = (n + kSelThreads - 1) / kSelThreads;
     uint32_t key[32];
 #pragma unroll
     for (int e = 0; e < 32; ++e) key[e] = (e < P && tid * P + e < n) ? float_order_key(sc[size_t(tid) * P + e]) : 0u;
-    block_topk32<kSelThreads, 32>(key, P, n, bd.k_blk, 0, bd.k_blk, true, emit_for(P), sm);
+    block_topk32<kSelThreads, 32>(key, P, n, bd.k_blk, 0, bd.k_blk, emit_for(P), sm);
   }
 }
 
