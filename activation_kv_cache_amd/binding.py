@@ -54,7 +54,7 @@ class bc_layer(ctypes.Structure):
 
 class bc_layer_taps(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("x1", "idx_qkv", "q", "k", "v", "idx_kv", "a", "idx_o", "h_mid", "x2",
-                                        "idx_gu", "hff", "idx_down")]
+                                        "idx_gu", "hff", "idx_down", "attn_m", "attn_l", "attn_o")]
 
 
 class bc_step(ctypes.Structure):

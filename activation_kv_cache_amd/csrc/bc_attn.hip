@@ -530,6 +530,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
 constexpr int kReduceMaxSplits = 4096;
 
 __global__ __launch_bounds__(kAttnThreads) void k_attn_reduce(const ReduceParams p) {
+  static_assert(kAttnThreads == kCombineThreads, "one thread per den term slot of the combine order");
   __shared__ float wts[kReduceMaxSplits];
   __shared__ float part[kAttnThreads];
   __shared__ float red[kAttnThreads / kWave];
@@ -550,13 +551,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_reduce(const ReduceParams
   __syncthreads();
   float den = 0.f;
   for (int s = tid; s < S; s += kAttnThreads) {
-    const float ms = mj[s];
-    const float wt = (ms == -INFINITY || M == -INFINITY) ? 0.f : expf(ms - M);
+    const float wt = combine_weight(mj[s], M);
     wts[s] = wt;
-    den += wt * lj[s];
+    den = fmaf(wt, lj[s], den);
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, kWave);
+  den = combine_wave_sum(den);
   if (lane == 0) red[w] = den;
   __syncthreads();
   den = 0.f;
@@ -567,18 +566,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_reduce(const ReduceParams
   const int per = (S + groups - 1) / groups;
   const int s0 = min(S, grp * per), s1 = min(S, s0 + per);
   const float* oj = p.o + size_t(j) * S * D + d;
-  float num = 0.f;
-  int s = s0;
-  for (; s + 4 <= s1; s += 4) {
-    const float o0 = oj[size_t(s) * D], o1 = oj[size_t(s + 1) * D];
-    const float o2 = oj[size_t(s + 2) * D], o3 = oj[size_t(s + 3) * D];
-    num += o0 * wts[s];
-    num += o1 * wts[s + 1];
-    num += o2 * wts[s + 2];
-    num += o3 * wts[s + 3];
-  }
-  for (; s < s1; ++s) num += oj[size_t(s) * D] * wts[s];
-  part[tid] = num;
+  part[tid] = combine_group(s0, s1, [&](int s) { return oj[size_t(s) * D]; }, [&](int s) { return wts[s]; });
   __syncthreads();
   if (tid < D) {
     float t = 0.f;

@@ -399,6 +399,41 @@ __device__ void block_topk(int n, int k, KeyFn key_fn, EmitFn emit, TopkSmem<NT,
   __syncthreads();
 }
 
+// ---------------------------------------------------- split-K combine
+// The fp32 order in which one head's split partials (m in natural-log units,
+// l, unnormalised o; S splits) are combined.  k_attn_reduce and the o GEMV
+// prologue that folds the reduce in both follow it, so both give the same
+// bf16 attention output:
+//   M = max_s m_s;  w_s = exp(m_s - M), or 0 when m_s or M is -inf;
+//   den: thread t of kCombineThreads sums w_s l_s over s = t, t + 256, ...
+//        in order (fmaf from 0), a xor butterfly (32, 16, ..., 1) sums each
+//        wave, lane 0's value is taken, and the wave sums are added in order
+//        to 0;
+//   num_d: G = kCombineThreads / D groups of ceil(S / G) consecutive splits,
+//        each summed in split order with fmaf from 0 (combine_group), the
+//        group sums added in order to 0;
+//   out_d = bf16(den > 0 ? num_d / den : 0).
+constexpr int kCombineThreads = 256;
+
+__device__ __forceinline__ float combine_weight(float ms, float M) {
+  return (ms == -INFINITY || M == -INFINITY) ? 0.f : expf(ms - M);
+}
+
+// splits [s0, s1) of one group; o(s) and w(s) give o_s[d] and w_s
+template <typename OF, typename WF>
+__device__ __forceinline__ float combine_group(int s0, int s1, OF o, WF w) {
+  float num = 0.f;
+#pragma unroll 4
+  for (int s = s0; s < s1; ++s) num = fmaf(o(s), w(s), num);
+  return num;
+}
+
+__device__ __forceinline__ float combine_wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
 // ------------------------------------- 15-bit keys in registers, two passes
 // Exact top-k of n keys below 2^15 held in registers by NT threads: thread t
 // owns positions [t*P, t*P + P) (positions >= n are ignored), so a thread's

@@ -17,7 +17,8 @@
 // IN_SEL takes x as given; with k < d_in both then select the exact top-k of
 // |x| (block_topk_2pass) in every work-group, so no separate selection
 // kernel or single-work-group stage sits between two GEMVs.  In dense mode
-// the first ring of weight loads is issued before the prologue.
+// the first ring of weight loads is issued right after the prologue's own
+// loads, before its arithmetic.
 //
 // Several chunks write fp32 partials ([chunk][d_out]); a finish kernel adds
 // them in chunk order (deterministic) and applies the epilogue: bf16 store,
@@ -26,6 +27,7 @@
 // epilogue itself.  No work-group waits for another: cross-XCD fences cost
 // far more on this chip than a kernel boundary.
 #include <math.h>
+#include <type_traits>
 #include <stdlib.h>
 
 #include "bc_device.hpp"
@@ -40,6 +42,9 @@ constexpr int kRing = 4;                    // rows in flight per slot
 constexpr int kNW = kGemvThreads / kWave;   // 16 waves
 constexpr int kRedQ = kGemvThreads / kGemvTile;   // slot groups in the epilogue sum
 constexpr int kTopkShift = 3;               // first selection pass: 4096 bins
+// IN_ATTN: one thread per channel (rows_per_split <= kGemvThreads), so a
+// chunk spans at most kGemvThreads / 64 + 1 heads (head_dim >= 64)
+constexpr int kFoldMaxHeads = kGemvThreads / 64 + 1;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -52,7 +57,13 @@ struct GemvSmem {
     float red[kSlots][kGemvTile];  // per-slot sums (after the row loop)
   };
   float red2[kRedQ][kGemvTile];
-  Topk2Smem<kGemvThreads, kTopkShift> tk;
+  union {
+    Topk2Smem<kGemvThreads, kTopkShift> tk;
+    struct {
+      float w[kFoldMaxHeads][kAttnFoldMaxSplits];   // combine weights w_s per head of the chunk
+      float den[kFoldMaxHeads];
+    } fold;
+  };
   float part[kNW];
   float amax_v[kNW];
   int32_t amax_i[kNW];
@@ -84,22 +95,32 @@ __device__ __forceinline__ void load_vec(const uint16_t* src, int c0, int P, int
 }
 
 // h = bf16(sum of the chunk partials in chunk order + resid) for the thread's
-// channels [c0, c0 + P): the arithmetic of k_finish_resid, with every load
-// issued before the sums.  Channels past d_in give 0.
+// channels [c0, c0 + P): the arithmetic of k_finish_resid.  sum_load issues
+// the loads of the first 8 chunks and of resid, sum_finish adds them (and
+// any further chunks).  Channels past d_in give 0.
 template <int PMAX>
-__device__ __forceinline__ void sum_vec(const float* partial, int n_splits, const uint16_t* resid, int c0, int P,
-                                        int d_in, uint32_t (&dst)[PMAX / 2]) {
+struct SumIn {
   float4 a[PMAX / 4][8];
   uint2 rv[PMAX / 4];
+};
+
+template <int PMAX>
+__device__ __forceinline__ void sum_load(const float* partial, int n_splits, const uint16_t* resid, int c0, int P,
+                                         int d_in, SumIn<PMAX>& in) {
 #pragma unroll
   for (int q = 0; q < PMAX / 4; ++q) {
     const bool ok = 4 * q < P && c0 + 4 * q < d_in;
     const int c = ok ? c0 + 4 * q : 0;
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      a[q][u] = *reinterpret_cast<const float4*>(partial + size_t(min(u, n_splits - 1)) * d_in + c);
-    rv[q] = *reinterpret_cast<const uint2*>(resid + c);
+      in.a[q][u] = *reinterpret_cast<const float4*>(partial + size_t(min(u, n_splits - 1)) * d_in + c);
+    in.rv[q] = *reinterpret_cast<const uint2*>(resid + c);
   }
+}
+
+template <int PMAX>
+__device__ __forceinline__ void sum_finish(const float* partial, int n_splits, int c0, int P, int d_in,
+                                           const SumIn<PMAX>& in, uint32_t (&dst)[PMAX / 2]) {
 #pragma unroll
   for (int q = 0; q < PMAX / 4; ++q) {
     const bool ok = 4 * q < P && c0 + 4 * q < d_in;
@@ -108,14 +129,15 @@ __device__ __forceinline__ void sum_vec(const float* partial, int n_splits, cons
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (u < n_splits) {
-        v.x += a[q][u].x; v.y += a[q][u].y; v.z += a[q][u].z; v.w += a[q][u].w;
+        v.x += in.a[q][u].x; v.y += in.a[q][u].y; v.z += in.a[q][u].z; v.w += in.a[q][u].w;
       }
     }
     for (int sp = 8; sp < n_splits; ++sp) {
       const float4 b = *reinterpret_cast<const float4*>(partial + size_t(sp) * d_in + c);
       v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
     }
-    v.x += bf16_lo(rv[q].x); v.y += bf16_hi(rv[q].x); v.z += bf16_lo(rv[q].y); v.w += bf16_hi(rv[q].y);
+    const uint2 rv = in.rv[q];
+    v.x += bf16_lo(rv.x); v.y += bf16_hi(rv.x); v.z += bf16_lo(rv.y); v.w += bf16_hi(rv.y);
     dst[2 * q] = ok ? (f32_to_bf16(v.x) | (uint32_t(f32_to_bf16(v.y)) << 16)) : 0u;
     dst[2 * q + 1] = ok ? (f32_to_bf16(v.z) | (uint32_t(f32_to_bf16(v.w)) << 16)) : 0u;
   }
@@ -153,96 +175,179 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
     const unsigned ch = dense ? unsigned(r0 + jj) : min(unsigned(sm.list.ch[jj]), last_row);
     return base + size_t(ch) * stride;
   };
+  // A dense chunk's first ring goes out right after the prologue's own
+  // loads: a wave's loads complete in issue order, so the inputs the
+  // prologue waits for are not queued behind its share of the weights, and
+  // the weights stream while the prologue computes.
   u32x4 ring[kRing];
-  if (dense) {
+  auto issue_ring = [&]() {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) ring[u] = load_row_nt(row_ptr(slot + kSlots * u));
-  }
+  };
 
   // ------------------------------------------------------------ prologue
-  if constexpr (IN == IN_LIST) {
-    for (int j = tid; j < n; j += kGemvThreads) {
-      const int ch = dense ? r0 + j : p.idx[r0 + j];
-      if (!dense) sm.list.ch[j] = ch;
-      sm.list.xv[j] = bf16_to_f32(p.x[ch]);
-    }
-  } else {
-    const int P = fused_per_thread(p.d_in);
-    const int c0 = tid * P;
-    uint32_t xb[PMAX / 2];
-    if constexpr (IN == IN_NORM || IN == IN_NORM_SUM) {
-      uint32_t gb[PMAX / 2];
-      if constexpr (IN == IN_NORM) load_vec<PMAX>(p.h, c0, P, p.d_in, xb);
-      load_vec<PMAX>(p.gain, c0, P, p.d_in, gb);
-      if (!dense) topk2_clear(sm.tk);   // while the loads are in flight; the barrier below covers it
-      if constexpr (IN == IN_NORM_SUM) {
-        sum_vec<PMAX>(p.sum_partial, p.sum_splits, p.h, c0, P, p.d_in, xb);
-        if (lead && p.h_out) {
+  // Instantiated for dense and for selected chunks separately, so that the
+  // compiler counts the outstanding loads of each path exactly (a merged
+  // path would wait for the first ring before using the prologue's loads).
+  auto prologue = [&](auto dense_tag) {
+    constexpr bool DENSE = decltype(dense_tag)::value;
+    if constexpr (IN == IN_LIST) {
+      if (DENSE) {
+        constexpr int Q = kGemvMaxRows / kGemvThreads;
+        float xq[Q];
 #pragma unroll
-          for (int q = 0; q < PMAX / 4; ++q)
-            if (4 * q < P && c0 + 4 * q < p.d_in)
-              *reinterpret_cast<uint2*>(p.h_out + c0 + 4 * q) = make_uint2(xb[2 * q], xb[2 * q + 1]);
+        for (int q = 0; q < Q; ++q) {
+          const int j = tid + q * kGemvThreads;
+          xq[q] = j < n ? bf16_to_f32(p.x[r0 + j]) : 0.f;
+        }
+        issue_ring();
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+          if (tid + q * kGemvThreads < n) sm.list.xv[tid + q * kGemvThreads] = xq[q];
+      } else {
+        for (int j = tid; j < n; j += kGemvThreads) {
+          const int ch = p.idx[r0 + j];
+          sm.list.ch[j] = ch;
+          sm.list.xv[j] = bf16_to_f32(p.x[ch]);
         }
       }
-      // sum of squares in a fixed order: the thread's channels in order, the
-      // wave's fixed tree, then the waves in order (all work-groups agree)
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < PMAX; ++e) {
-        const float v = bf16_elt(xb, e);
-        ss += v * v;   // channels past d_in were loaded as 0
+    } else if constexpr (IN == IN_ATTN) {
+      // x of channels [r0, r1) from the attention split partials, in the
+      // combine order of k_attn_reduce: thread j owns channel r0 + j and loads
+      // its S values of o first; one wave per head of the chunk forms w_s and
+      // den (lane s holds split s)
+      const int D = p.a_hd, S = p.a_splits;
+      const int h0 = r0 / D, nh = (r1 - 1) / D - h0 + 1;
+      const int c = r0 + min(tid, n - 1);
+      const int hh = c / D - h0;
+      // wave w's first head: its m and l go out first, then o, then the ring
+      float ms0 = -INFINITY, lv0 = 0.f;
+      if (w < nh && lane < S) {
+        ms0 = p.am[size_t(h0 + w) * S + lane];
+        lv0 = p.al[size_t(h0 + w) * S + lane];
       }
-      ss = wave_sum_f32(ss);
-      if (lane == 0) sm.part[w] = ss;
+      const float* osrc = p.ao + size_t(c / D) * S * D + (c % D);
+      float ov[kAttnFoldMaxSplits];
+#pragma unroll
+      for (int sp = 0; sp < kAttnFoldMaxSplits; ++sp) ov[sp] = osrc[size_t(min(sp, S - 1)) * D];
+      issue_ring();
+      for (int hw = w; hw < nh; hw += kNW) {
+        const size_t hb = size_t(h0 + hw) * S;
+        float ms = ms0, lv = lv0;
+        if (hw != w) {
+          ms = lane < S ? p.am[hb + lane] : -INFINITY;
+          lv = lane < S ? p.al[hb + lane] : 0.f;
+        }
+        float M = ms;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
+        const float wt = combine_weight(ms, M);
+        const float den = combine_wave_sum(lane < S ? fmaf(wt, lv, 0.f) : 0.f);
+        if (lane < S) sm.fold.w[hw][lane] = wt;
+        if (lane == 0) sm.fold.den[hw] = 0.f + den;
+      }
       __syncthreads();
-      float tot = 0.f;
+      if (tid < n) {
+        const int G = kCombineThreads / D, per = (S + G - 1) / G;
+        const float* wv = sm.fold.w[hh];
+        float t = 0.f;
+        for (int g = 0; g < G; ++g) {
+          const int s0 = min(S, g * per), s1 = min(S, s0 + per);
+          // combine_group over registers: splits outside [s0, s1) are skipped
+          float num = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < kNW; ++ww) tot += sm.part[ww];
-      const float inv = 1.0f / sqrtf(tot / float(p.d_in) + p.eps);
-#pragma unroll
-      for (int q = 0; q < PMAX / 2; ++q) {
-        const uint32_t a = f32_to_bf16(bf16_lo(xb[q]) * inv * bf16_lo(gb[q]));
-        const uint32_t b = f32_to_bf16(bf16_hi(xb[q]) * inv * bf16_hi(gb[q]));
-        xb[q] = a | (b << 16);
+          for (int sp = 0; sp < kAttnFoldMaxSplits; ++sp)
+            if (sp >= s0 && sp < s1) num = fmaf(ov[sp], wv[sp], num);
+          t += num;
+        }
+        const float den = sm.fold.den[hh];
+        const uint32_t xb = f32_to_bf16(den > 0.f ? t / den : 0.f);
+        sm.list.xv[tid] = __uint_as_float(xb << 16);
+        if (tile == 0 && p.x_out) p.x_out[c] = uint16_t(xb);
       }
     } else {
-      load_vec<PMAX>(p.x, c0, P, p.d_in, xb);
-      if (!dense) {
-        topk2_clear(sm.tk);
+      const int P = fused_per_thread(p.d_in);
+      const int c0 = tid * P;
+      uint32_t xb[PMAX / 2];
+      if constexpr (IN == IN_NORM || IN == IN_NORM_SUM) {
+        uint32_t gb[PMAX / 2];
+        [[maybe_unused]] SumIn<(IN == IN_NORM_SUM ? PMAX : 4)> sin;
+        if constexpr (IN == IN_NORM_SUM) sum_load<PMAX>(p.sum_partial, p.sum_splits, p.h, c0, P, p.d_in, sin);
+        if constexpr (IN == IN_NORM) load_vec<PMAX>(p.h, c0, P, p.d_in, xb);
+        load_vec<PMAX>(p.gain, c0, P, p.d_in, gb);
+        if (DENSE) issue_ring();
+        if (!DENSE) topk2_clear(sm.tk);   // while the loads are in flight; the barrier below covers it
+        if constexpr (IN == IN_NORM_SUM) {
+          sum_finish<PMAX>(p.sum_partial, p.sum_splits, c0, P, p.d_in, sin, xb);
+          if (lead && p.h_out) {
+#pragma unroll
+            for (int q = 0; q < PMAX / 4; ++q)
+              if (4 * q < P && c0 + 4 * q < p.d_in)
+                *reinterpret_cast<uint2*>(p.h_out + c0 + 4 * q) = make_uint2(xb[2 * q], xb[2 * q + 1]);
+          }
+        }
+        // sum of squares in a fixed order: the thread's channels in order, the
+        // wave's fixed tree, then the waves in order (all work-groups agree)
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < PMAX; ++e) {
+          const float v = bf16_elt(xb, e);
+          ss += v * v;   // channels past d_in were loaded as 0
+        }
+        ss = wave_sum_f32(ss);
+        if (lane == 0) sm.part[w] = ss;
         __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kNW; ++ww) tot += sm.part[ww];
+        const float inv = 1.0f / sqrtf(tot / float(p.d_in) + p.eps);
+#pragma unroll
+        for (int q = 0; q < PMAX / 2; ++q) {
+          const uint32_t a = f32_to_bf16(bf16_lo(xb[q]) * inv * bf16_lo(gb[q]));
+          const uint32_t b = f32_to_bf16(bf16_hi(xb[q]) * inv * bf16_hi(gb[q]));
+          xb[q] = a | (b << 16);
+        }
+      } else {
+        load_vec<PMAX>(p.x, c0, P, p.d_in, xb);
+        if (DENSE) issue_ring();
+        if (!DENSE) {
+          topk2_clear(sm.tk);
+          __syncthreads();
+        }
+      }
+      if (lead && p.x_out) {
+#pragma unroll
+        for (int q = 0; q < PMAX / 4; ++q)
+          if (4 * q < P && c0 + 4 * q < p.d_in)
+            *reinterpret_cast<uint2*>(p.x_out + c0 + 4 * q) = make_uint2(xb[2 * q], xb[2 * q + 1]);
+      }
+      if (DENSE) {
+#pragma unroll
+        for (int e = 0; e < PMAX; ++e) {
+          const int c = c0 + e;
+          if (e < P && c >= r0 && c < r1) sm.list.xv[c - r0] = bf16_elt(xb, e);
+        }
+      } else {
+        uint32_t key[PMAX];
+#pragma unroll
+        for (int e = 0; e < PMAX; ++e) key[e] = ((xb[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) & 0x7FFFu;
+        int32_t* idx_out = p.idx_out;
+        auto emit = [&](int rel, int e) {
+          sm.list.ch[rel] = c0 + e;
+          sm.list.xv[rel] = bf16_elt(xb, e);
+        };
+        auto out = [&](int pos, int e) { idx_out[pos] = c0 + e; };
+        block_topk_2pass<kGemvThreads, kTopkShift, PMAX>(key, P, p.d_in, p.k, r0, r1, emit, sm.tk,
+                                                         lead && idx_out != nullptr, out);
       }
     }
-    if (lead && p.x_out) {
-#pragma unroll
-      for (int q = 0; q < PMAX / 4; ++q)
-        if (4 * q < P && c0 + 4 * q < p.d_in)
-          *reinterpret_cast<uint2*>(p.x_out + c0 + 4 * q) = make_uint2(xb[2 * q], xb[2 * q + 1]);
-    }
-    if (dense) {
-#pragma unroll
-      for (int e = 0; e < PMAX; ++e) {
-        const int c = c0 + e;
-        if (e < P && c >= r0 && c < r1) sm.list.xv[c - r0] = bf16_elt(xb, e);
-      }
-    } else {
-      uint32_t key[PMAX];
-#pragma unroll
-      for (int e = 0; e < PMAX; ++e) key[e] = ((xb[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) & 0x7FFFu;
-      int32_t* idx_out = p.idx_out;
-      auto emit = [&](int rel, int e) {
-        sm.list.ch[rel] = c0 + e;
-        sm.list.xv[rel] = bf16_elt(xb, e);
-      };
-      auto out = [&](int pos, int e) { idx_out[pos] = c0 + e; };
-      block_topk_2pass<kGemvThreads, kTopkShift, PMAX>(key, P, p.d_in, p.k, r0, r1, emit, sm.tk,
-                                                       lead && idx_out != nullptr, out);
-    }
-  }
+  };
+  if (dense)
+    prologue(std::true_type{});
+  else
+    prologue(std::false_type{});
   __syncthreads();
-  if (!dense) {
-#pragma unroll
-    for (int u = 0; u < kRing; ++u) ring[u] = load_row_nt(row_ptr(slot + kSlots * u));
-  }
+  if (!dense) issue_ring();
 
   // ------------------------------------------------------------- row loop
   float acc[8];
@@ -562,6 +667,12 @@ GemvPlan plan_gemv(int d_out, int k, bool single) {
 }
 
 bool gemv_fused_input_ok(int d_in) { return d_in >= 1 && d_in % 4 == 0 && d_in <= kGemvFusedMaxIn; }
+
+bool gemv_attn_fold_ok(int d_in, int d_out, int head_dim, int attn_splits) {
+  if ((head_dim != 64 && head_dim != 128) || d_in < head_dim || d_in % head_dim != 0) return false;
+  if (attn_splits < 1 || attn_splits > kAttnFoldMaxSplits) return false;
+  return plan_gemv(d_out, d_in).rows_per_split <= kGemvThreads;
+}
 bool gemv_sum_input_ok(int d_in) { return gemv_fused_input_ok(d_in) && fused_per_thread(d_in) <= 4; }
 
 namespace {
@@ -588,6 +699,18 @@ int launch_gemv(int in, int out, const GemvParams& p, hipStream_t s) {
     return set_error(BC_ERR_INVALID, "SwiGLU epilogue: tile count");
   const dim3 grid(p.n_tiles, p.n_splits);
   if (in == IN_LIST) return launch_gemv_out<IN_LIST, 4>(out, p, grid, s);
+  if (in == IN_ATTN) {
+    if (p.k != p.d_in || p.idx || !p.am || !p.al || !p.ao || (p.a_hd != 64 && p.a_hd != 128) ||
+        p.d_in % p.a_hd != 0 || p.a_splits < 1 || p.a_splits > kAttnFoldMaxSplits ||
+        p.rows_per_split > kGemvThreads || (out != OUT_PARTIAL && out != OUT_BF16))
+      return set_error(BC_ERR_INVALID, "IN_ATTN: d_in=%d k=%d head_dim=%d splits=%d", p.d_in, p.k, p.a_hd,
+                       p.a_splits);
+    if (out == OUT_PARTIAL)
+      k_gemv<IN_ATTN, OUT_PARTIAL, 4><<<grid, dim3(kGemvThreads), 0, s>>>(p);
+    else
+      k_gemv<IN_ATTN, OUT_BF16, 4><<<grid, dim3(kGemvThreads), 0, s>>>(p);
+    return check_launch("k_gemv");
+  }
   if (in != IN_NORM && in != IN_SEL && in != IN_NORM_SUM) return set_error(BC_ERR_INVALID, "unknown GEMV input %d", in);
   if (!gemv_fused_input_ok(p.d_in)) return set_error(BC_ERR_UNSUPPORTED, "fused GEMV input d_in=%d", p.d_in);
   static_assert(kGemvFusedMaxIn <= kGemvThreads * 16, "fused inputs fit 16 per thread");

@@ -42,9 +42,14 @@ constexpr int kGemvFusedMaxIn = 16384;  // inputs a work-group normalises / sele
 //            h = bf16(sum of chunks in chunk order + resid), the arithmetic
 //            of FIN_RESID; the first work-group stores h (h_out).  This folds
 //            a residual finish kernel into the next GEMV (d_in <= 4096).
+//   IN_ATTN  dense only: x is the attention output, formed for the chunk's
+//            own channels from the split-K partials (m, l, o) in the combine
+//            order of the reduce kernel; this folds the reduce into the o
+//            GEMV.  The first tile's work-groups store their channels of x
+//            (x_out), which together cover it.
 // Every work-group of a launch forms the same x and the same selection; the
 // first one also stores them (x_out, idx_out) when asked.
-enum GemvIn : int { IN_LIST = 0, IN_NORM = 1, IN_SEL = 2, IN_NORM_SUM = 3 };
+enum GemvIn : int { IN_LIST = 0, IN_NORM = 1, IN_SEL = 2, IN_NORM_SUM = 3, IN_ATTN = 4 };
 // What the main kernel stores: fp32 partials per chunk of rows, or (one
 // chunk) bf16 y, the SwiGLU of a gate|up tile, or fp32 y + per-tile argmax.
 enum GemvOut : int { OUT_PARTIAL = 0, OUT_BF16 = 1, OUT_SWIGLU = 2, OUT_ARGMAX = 3 };
@@ -61,6 +66,10 @@ struct GemvPlan {
 GemvPlan plan_gemv(int d_out, int k, bool single = false);
 bool gemv_fused_input_ok(int d_in);
 bool gemv_sum_input_ok(int d_in);   // IN_NORM_SUM supports this d_in
+// IN_ATTN supports a dense GEMV of d_in = heads * head_dim inputs over this
+// many attention splits
+constexpr int kAttnFoldMaxSplits = 32;
+bool gemv_attn_fold_ok(int d_in, int d_out, int head_dim, int attn_splits);
 
 struct GemvParams {
   const uint16_t* wt;
@@ -73,6 +82,10 @@ struct GemvParams {
   const float* sum_partial;   // IN_NORM_SUM: [sum_splits][d_in] fp32
   int sum_splits;
   uint16_t* h_out;        // IN_NORM_SUM: h (first work-group)
+  const float* am;        // IN_ATTN: split partials m, l [heads][a_splits], o [heads][a_splits][a_hd]
+  const float* al;
+  const float* ao;
+  int a_splits, a_hd;
   float eps;
   uint16_t* x_out;        // IN_NORM / IN_SEL: optional copy of x (first work-group)
   int32_t* idx_out;       // IN_NORM / IN_SEL: optional copy of the selection

@@ -10,7 +10,9 @@
 //   k_kv_score, k_kv_block_select   KV list (r_kv < 1 only)
 //   k_attn_partial, k_attn_reduce   split-K attention -> a
 //   k_gemv<IN_SEL>, k_finish_resid  S2 = top-k(a) in the prologue;
-//                          h1 = h + W_o a over S2
+//                          h1 = h + W_o a over S2.  A dense o GEMV
+//                          (k_gemv<IN_ATTN>) forms its chunk of a from the
+//                          split partials itself and the reduce is skipped
 //   k_gemv<IN_NORM, OUT_SWIGLU>     x2 = RMSNorm(h1) * g_mlp, S3 = top-k(x2);
 //                          f = SiLU(gate) * up over S3 (one chunk per tile)
 //   k_gemv<IN_SEL>, k_finish_resid  S4 = top-k(f); h = h1 + W_down f over S4
@@ -247,6 +249,10 @@ struct ProjIn {
   const float* sum_partial = nullptr;
   int sum_splits = 0;
   uint16_t* h_out = nullptr;
+  const float* am = nullptr;   // IN_ATTN: attention split partials
+  const float* al = nullptr;
+  const float* ao = nullptr;
+  int a_splits = 0, a_hd = 0;
 };
 
 // A hidden state not yet stored: h = bf16(chunk sums of partial + resid),
@@ -284,6 +290,8 @@ int run_gemv(const uint16_t* wt, int d_in, int d_out, int k, const ProjIn& in, f
   if (in.mode == IN_NORM || in.mode == IN_NORM_SUM) {
     p.h = in.v; p.gain = in.gain; p.eps = in.eps;
     p.sum_partial = in.sum_partial; p.sum_splits = in.sum_splits; p.h_out = in.h_out;
+  } else if (in.mode == IN_ATTN) {
+    p.am = in.am; p.al = in.al; p.ao = in.ao; p.a_splits = in.a_splits; p.a_hd = in.a_hd;
   } else {
     p.x = in.v;
   }
@@ -446,12 +454,14 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
     if ((rc = launch_kv_block_select(kb, s)) != BC_OK) return rc;
   }
 
-  // attention
+  // attention; a dense o GEMV folds the reduce into its prologue
+  const bool fold_reduce = k_d == H * hd && gemv_attn_fold_ok(H * hd, m.d, hd, n_splits);
   {
     AttnParams p{};
     p.k_cache = ly->k_cache; p.v_cache = ly->v_cache; p.n_cap = ly->n_cap;
     p.n_sel = n_sel; p.n_heads = H; p.n_kv_heads = Hkv; p.head_dim = hd; p.n_splits = n_splits;
-    p.scale_log2 = float(1.4426950408889634 / sqrt(double(hd)));
+    // softmax scale 1/sqrt(head_dim), in the arithmetic of bc_splitk_attn_partial
+    p.scale_log2 = float(1.0 / sqrt(double(hd))) * 1.4426950408889634f;
     p.m = at<float>(ws, L.m); p.l = at<float>(ws, L.l); p.o = at<float>(ws, L.o);
     ReduceParams r{};
     r.m = p.m; r.l = p.l; r.o = p.o; r.n_heads = H; r.n_splits = n_splits; r.head_dim = hd; r.out = a;
@@ -471,7 +481,7 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
       p.rope = rope; p.q_out = st->taps ? at<uint16_t>(ws, L.q) : nullptr; p.summary = ly->kv_summary;
       if ((rc = launch_attn_partial(Q_PARTIAL, L_DENSE, p, s)) != BC_OK) return rc;
     }
-    if ((rc = launch_attn_reduce(r, s)) != BC_OK) return rc;
+    if (!fold_reduce && (rc = launch_attn_reduce(r, s)) != BC_OK) return rc;
   }
 
   // S2 = top-k(a) (GEMV prologue); h1 = h + W_o a, left as chunk partials
@@ -479,7 +489,12 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
   const bool fold = gemv_sum_input_ok(m.d);
   int o_splits = 0;
   {
-    const ProjIn in{IN_SEL, a, nullptr, 0.f, nullptr, idx_o};
+    ProjIn in{IN_SEL, a, nullptr, 0.f, nullptr, idx_o};
+    if (fold_reduce) {
+      in = ProjIn{IN_ATTN, nullptr, nullptr, 0.f, a, nullptr};
+      in.am = at<float>(ws, L.m); in.al = at<float>(ws, L.l); in.ao = at<float>(ws, L.o);
+      in.a_splits = n_splits; in.a_hd = hd;
+    }
     FinishParams f{};
     f.y = h_mid; f.resid = hidden;
     if ((rc = run_gemv(ly->w_o, H * hd, m.d, k_d, in, partial2, fold ? FIN_NONE : FIN_RESID, f, s, &o_splits)) !=
@@ -527,6 +542,10 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
     if (sparse && (rc = copy_tap(t->idx_gu, idx_gu, size_t(k_d) * 4, s)) != BC_OK) return rc;
     if ((rc = copy_tap(t->hff, hff, size_t(m.d_ff) * 2, s)) != BC_OK) return rc;
     if (sparse && (rc = copy_tap(t->idx_down, idx_down, size_t(k_ff) * 4, s)) != BC_OK) return rc;
+    const size_t ml = size_t(H) * n_splits * 4;
+    if ((rc = copy_tap(t->attn_m, at<void>(ws, L.m), ml, s)) != BC_OK) return rc;
+    if ((rc = copy_tap(t->attn_l, at<void>(ws, L.l), ml, s)) != BC_OK) return rc;
+    if ((rc = copy_tap(t->attn_o, at<void>(ws, L.o), ml * hd, s)) != BC_OK) return rc;
   }
   return BC_OK;
 }

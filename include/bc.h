@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define BC_ABI_VERSION 1
+#define BC_ABI_VERSION 2
 
 enum {
   BC_OK = 0,
@@ -232,6 +232,9 @@ typedef struct {
   int32_t* idx_gu;    /* [k_d] */
   uint16_t* hff;      /* [d_ff] */
   int32_t* idx_down;  /* [k_ff] */
+  float* attn_m;      /* [n_heads][n_splits] split-K partials of the attention */
+  float* attn_l;      /* [n_heads][n_splits] */
+  float* attn_o;      /* [n_heads][n_splits][hd] */
 } bc_layer_taps;
 
 typedef struct {

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(bc):
 
 
 def test_abi_version(bc):
-    assert bc.bc_abi_version() == 1
+    assert bc.bc_abi_version() == 2
 
 
 @pytest.mark.parametrize("r_p,d", [(0.5, 4096), (0.7, 4096), (0.7, 14336), (0.5, 1408), (1.0, 77), (0.0001, 77),

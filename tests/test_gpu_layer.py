@@ -49,7 +49,8 @@ def _run_layer(dims, n_cap, n, r_p, r_kv, sinks, window, n_splits, seed, k_std=0
     i16, i32 = torch.int16, torch.int32
     sizes = {"x1": (d, i16), "idx_qkv": (k_d, i32), "q": (H * D, i16), "k": (Hkv * D, i16), "v": (Hkv * D, i16),
              "idx_kv": (Hkv * n_sel, i32), "a": (H * D, i16), "idx_o": (k_d, i32), "h_mid": (d, i16),
-             "x2": (d, i16), "idx_gu": (k_d, i32), "hff": (dff, i16), "idx_down": (k_ff, i32)}
+             "x2": (d, i16), "idx_gu": (k_d, i32), "hff": (dff, i16), "idx_down": (k_ff, i32),
+             "attn_m": (H * S, torch.float32), "attn_l": (H * S, torch.float32), "attn_o": (H * S * D, torch.float32)}
     taps = {k: torch.full((n,), -1, dtype=t, device="cuda") for k, (n, t) in sizes.items()}
     layer = bc.make_layer(bc.packed_tiles(w["qkv"]), bc.packed_tiles(w["o"]), w_gu, bc.packed_tiles(w["down"]),
                           w["g1"], w["g2"], kc, vc, sm)
@@ -58,7 +59,7 @@ def _run_layer(dims, n_cap, n, r_p, r_kv, sinks, window, n_splits, seed, k_std=0
     torch.cuda.synchronize()
     got = {}
     for k, t in taps.items():
-        got[k] = host(t) if t.dtype == torch.int32 else host_u16(t)
+        got[k] = host_u16(t) if t.dtype == torch.int16 else host(t)
     got["h_out"] = host_u16(hh)
     got["K"], got["V"], got["summ"] = host_u16(kc), host_u16(vc), host_u16(sm)
     return W, K, V, h, summ, got, S
@@ -91,6 +92,10 @@ LAYER_CASES = [
     # last split holds only that token in the second case
     ("tiny-short-ctx", gen.TINY, 64, 17, 1.0, 1.0, 4, 128, 3),
     ("tiny-split-of-one", gen.TINY, 64, 13, 1.0, 1.0, 4, 128, 4),
+    # more attention splits than the o GEMV prologue combines: a reduce
+    # kernel forms the attention output
+    ("tiny-dense-40-splits", gen.TINY, 2048, 2048, 1.0, 1.0, 4, 128, 40),
+    ("tiny-first-token-dense", gen.TINY, 64, 1, 1.0, 1.0, 4, 128, 1),
     # over 2048 candidate blocks: a selection kernel ranks the kept blocks
     # once per KV head and the attention work-groups copy their ranks
     ("tiny-long-ctx-ranked", gen.TINY, 40960, 40000, 0.7, 0.3, 4, 128, 0),
@@ -116,6 +121,28 @@ def test_decode_layer_teacher_forced(name, dims, n_cap, n, r_p, r_kv, sinks, win
     # the cache holds the GPU's new row and the refreshed summary matches the oracle's
     assert np.array_equal(got["K"][:, n - 1], forced["k"]) and np.array_equal(got["V"][:, n - 1], forced["v"])
     assert np.array_equal(got["summ"], so)
+
+
+@pytest.mark.parametrize("dims,n_cap,n,S,r_kv", [(gen.TINY, 2048, 2048, 8, 1.0), (gen.TINY, 64, 1, 1, 1.0),
+                                                (gen.TINY, 2048, 2048, 32, 1.0), (gen.TINY, 2048, 2048, 40, 1.0),
+                                                (gen.TINY, 2048, 2048, 8, 0.3), (gen.LLAMA8B, 2048, 2048, 0, 1.0)],
+                         ids=["tiny-8-splits", "tiny-first-token", "tiny-32-splits", "tiny-40-splits-reduce-kernel",
+                              "tiny-kv-0.3", "8b-2k"])
+def test_attention_output_equals_reduce_of_partials(dims, n_cap, n, S, r_kv):
+    """The layer's attention output equals, bit for bit, bc_splitk_reduce
+    over the layer's own split partials: a dense o GEMV forms it in its
+    prologue (up to 32 splits, no reduce launch), otherwise the reduce kernel
+    does; both follow one combine order."""
+    bc = _bc()
+    W, K, V, h, summ, got, S = _run_layer(dims, n_cap, n, 1.0, r_kv, 4, 128, S, seed=5)
+    H, D = dims["n_heads"], dims["head_dim"]
+    m = dev(got["attn_m"].reshape(H, S))
+    l = dev(got["attn_l"].reshape(H, S))
+    o = dev(got["attn_o"].reshape(H, S, D))
+    out = torch.full((H * D,), -1, dtype=torch.int16, device="cuda")
+    bc.bc_splitk_reduce(m, l, o, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(out), got["a"])
 
 
 def _bf16_ulp(x):
