@@ -40,7 +40,6 @@ namespace {
 constexpr int kSlots = kGemvThreads / 16;   // 64 row slots of 16 lanes
 constexpr int kRing = 4;                    // rows in flight per slot
 constexpr int kNW = kGemvThreads / kWave;   // 16 waves
-constexpr int kRedQ = kGemvThreads / kGemvTile;   // slot groups in the epilogue sum
 constexpr int kTopkShift = 3;               // first selection pass: 4096 bins
 // IN_ATTN: one thread per channel (rows_per_split <= kGemvThreads), so a
 // chunk spans at most kGemvThreads / 64 + 1 heads (head_dim >= 64)
@@ -49,14 +48,11 @@ constexpr int kFoldMaxHeads = kGemvThreads / 64 + 1;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct GemvSmem {
-  union {
-    struct {
-      int32_t ch[kGemvMaxRows];   // channel of each list position of the chunk
-      float xv[kGemvMaxRows];     // its input value
-    } list;
-    float red[kSlots][kGemvTile];  // per-slot sums (after the row loop)
-  };
-  float red2[kRedQ][kGemvTile];
+  struct {
+    int32_t ch[kGemvMaxRows];   // channel of each list position of the chunk
+    float xv[kGemvMaxRows];     // its input value
+  } list;
+  float red[kNW][kGemvTile];    // per-wave column sums (after the row loop)
   union {
     Topk2Smem<kGemvThreads, kTopkShift> tk;
     struct {
@@ -379,25 +375,24 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
   acc[0] += __uint_as_float(sink);
 
   // ------------------------------------------------------------- epilogue
-  __syncthreads();   // red aliases the list
-  {
-    float4* rw = reinterpret_cast<float4*>(&sm.red[slot][l16 * 8]);
+  // The four slots of a wave (its 16-lane rows) hold the same 8 columns:
+  // they are summed across rows in registers (lane ^ 32, then lane ^ 16),
+  // the waves' sums through LDS in wave order.
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    acc[c] += lane_xor<32>(acc[c]);
+    acc[c] += lane_xor<16>(acc[c]);
+  }
+  if (lane < 16) {
+    float4* rw = reinterpret_cast<float4*>(&sm.red[w][l16 * 8]);
     rw[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     rw[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-  }
-  __syncthreads();
-  {
-    const int c = tid & (kGemvTile - 1), q = tid / kGemvTile;
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < kSlots / kRedQ; ++i) s += sm.red[(kSlots / kRedQ) * q + i][c];
-    sm.red2[q][c] = s;
   }
   __syncthreads();
   auto col_sum = [&](int c) {
     float v = 0.f;
 #pragma unroll
-    for (int q = 0; q < kRedQ; ++q) v += sm.red2[q][c];
+    for (int ww = 0; ww < kNW; ++ww) v += sm.red[ww][c];
     return v;
   };
   if constexpr (OUT == OUT_PARTIAL) {
