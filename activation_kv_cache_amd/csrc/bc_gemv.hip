@@ -191,20 +191,37 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
       if (DENSE) {
         constexpr int Q = kGemvMaxRows / kGemvThreads;
         float xq[Q];
+        // clamped, unconditional loads: no branch separates a load from its use
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-          const int j = tid + q * kGemvThreads;
-          xq[q] = j < n ? bf16_to_f32(p.x[r0 + j]) : 0.f;
-        }
+        for (int q = 0; q < Q; ++q) xq[q] = bf16_to_f32(p.x[r0 + min(tid + q * kGemvThreads, n - 1)]);
         issue_ring();
 #pragma unroll
         for (int q = 0; q < Q; ++q)
           if (tid + q * kGemvThreads < n) sm.list.xv[tid + q * kGemvThreads] = xq[q];
       } else {
-        for (int j = tid; j < n; j += kGemvThreads) {
-          const int ch = p.idx[r0 + j];
-          sm.list.ch[j] = ch;
-          sm.list.xv[j] = bf16_to_f32(p.x[ch]);
+        // the list entries (the thread's, then its slot's first ring rows),
+        // then x at the thread's entries, then the first ring straight from
+        // the entries in registers: the weights stream while the list is
+        // staged in LDS
+        constexpr int Q = kGemvMaxRows / kGemvThreads;
+        unsigned chq[Q], chr[kRing];
+        float xq[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) chq[q] = unsigned(p.idx[r0 + min(tid + q * kGemvThreads, n - 1)]);
+#pragma unroll
+        for (int u = 0; u < kRing; ++u)
+          chr[u] = min(unsigned(p.idx[r0 + min(slot + kSlots * u, n - 1)]), last_row);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) xq[q] = bf16_to_f32(p.x[min(chq[q], last_row)]);
+#pragma unroll
+        for (int u = 0; u < kRing; ++u) ring[u] = load_row_nt(base + size_t(chr[u]) * stride);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+          const int j = tid + q * kGemvThreads;
+          if (j < n) {
+            sm.list.ch[j] = int(chq[q]);
+            sm.list.xv[j] = xq[q];
+          }
         }
       }
     } else if constexpr (IN == IN_ATTN) {
@@ -343,7 +360,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
   else
     prologue(std::false_type{});
   __syncthreads();
-  if (!dense) issue_ring();
+  if (IN != IN_LIST && !dense) issue_ring();
 
   // ------------------------------------------------------------- row loop
   float acc[8];
