@@ -233,6 +233,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
 // scores keep the lower block), the window; ascending.
 __global__ __launch_bounds__(kSelThreads) void k_kv_block_select(const KvSelectParams p) {
   __shared__ Topk32Smem<kSelThreads> sm;
+  __shared__ uint32_t stage16[kSelThreads * 16];   // coalesced staging of up to 16 keys per thread
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   const bc_kv_budget_info bd = p.bud;
@@ -263,6 +264,12 @@ __global__ __launch_bounds__(kSelThreads) void k_kv_block_select(const KvSelectP
     uint32_t key[8];
     const int P = load_score_keys<kSelThreads, 8>(sc, n, key, sm.hist);
     block_topk32<kSelThreads, 8>(key, P, n, bd.k_blk, 0, bd.k_blk, emit_for(P), sm);
+  } else if (n <= kSelThreads * 16) {
+    // up to 16 keys per thread (a context of up to 256K tokens), staged the
+    // same way
+    uint32_t key[16];
+    const int P = load_score_keys<kSelThreads, 16>(sc, n, key, stage16);
+    block_topk32<kSelThreads, 16>(key, P, n, bd.k_blk, 0, bd.k_blk, emit_for(P), sm);
   } else {
     const int P = (n + kSelThreads - 1) / kSelThreads;
     uint32_t key[32];

@@ -51,6 +51,11 @@ KV_CASES = [
     ("8b-32k-0.3", gen.LLAMA8B, 32768, 32768, 0.3, 4, 1024),
     ("8b-128k-0.3", gen.LLAMA8B, 131072, 131072, 0.3, 4, 1024),
     ("8b-128k-0.5", gen.LLAMA8B, 131072, 131072, 0.5, 4, 1024),
+    # past 8192 candidates: 16 staged keys per selecting thread, then (past
+    # 16384) 32 keys read per thread
+    ("tiny-160k-16-keys", gen.TINY, 160000, 160000, 0.3, 4, 128),
+    ("8b-192k-16-keys", gen.LLAMA8B, 196608, 196608, 0.3, 4, 1024),
+    ("tiny-320k-32-keys", gen.TINY, 320000, 320000, 0.5, 4, 128),
 ]
 
 
