@@ -69,6 +69,7 @@ _SIG = {
     "bc_channel_keep": (c_int, [c_double, c_int]),
     "bc_kv_budget": (c_int, [c_int, ctypes.POINTER(bc_kv_policy), ctypes.POINTER(bc_kv_budget_info)]),
     "bc_workspace_init": (c_int, [P, c_size_t, P]),
+    "bc_stream_read": (c_int, [P, c_size_t, P, P]),
     "bc_select_channels": (c_int, [P, c_int, c_int, P, P]),
     "bc_sparse_gemv_workspace_bytes": (c_size_t, [c_int, c_int]),
     "bc_sparse_gemv": (c_int, [P, c_int, c_int, P, P, c_int, P, P, c_size_t, P]),
@@ -182,6 +183,13 @@ def bc_lm_head_workspace_bytes(md: bc_model_dims) -> int:
 def bc_workspace_init(ws, stream=None):
     p, n = _ws(ws)
     return _check(_lib.bc_workspace_init(p, n, _stream(stream)), "bc_workspace_init")
+
+
+def bc_stream_read(src, sink, stream=None):
+    """Measurement helper: one streaming read of the whole of src (its
+    byte size a multiple of 4 MiB) into 256 checksum words at sink."""
+    nbytes = src.numel() * src.element_size()
+    return _check(_lib.bc_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "bc_stream_read")
 
 
 def bc_select_channels(x, k: int, idx_out, stream=None):

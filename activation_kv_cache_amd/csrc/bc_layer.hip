@@ -63,6 +63,25 @@ void rope_table(int pos, double theta, int head_dim, RopeTable* t) {
 
 namespace {
 
+// Streaming read of a contiguous share per work-group, two 16-byte
+// non-temporal loads in flight per lane (bc_stream_read).
+constexpr int kReadGroups = 256;
+constexpr int kReadThreads = 1024;
+__global__ __launch_bounds__(kReadThreads) void k_stream_read(const uint4* src, size_t n16_per_group, uint32_t* sink) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* base = reinterpret_cast<const u32x4*>(src) + size_t(blockIdx.x) * n16_per_group;
+  uint32_t acc = 0;
+  for (size_t i = threadIdx.x; i < n16_per_group; i += 2 * kReadThreads) {
+    const size_t j = i + kReadThreads;
+    const u32x4 a = __builtin_nontemporal_load(base + i);
+    const u32x4 b = j < n16_per_group ? __builtin_nontemporal_load(base + j) : u32x4{0u, 0u, 0u, 0u};
+    acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w);
+  }
+  // one word per work-group (wave 0's sum); every lane's loads run either way
+  acc = wave_sum_u32(acc);
+  if (threadIdx.x == 0) sink[blockIdx.x] = acc;
+}
+
 __global__ void k_fill_zero(uint4* p, size_t n16, uint8_t* tail, size_t ntail) {
   const size_t stride = size_t(gridDim.x) * blockDim.x;
   for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
@@ -202,6 +221,17 @@ extern "C" int bc_workspace_init(void* ws, size_t bytes, void* stream) {
   if (!ws) return set_error(BC_ERR_INVALID, "bc_workspace_init: NULL workspace");
   if (reinterpret_cast<uintptr_t>(ws) & 15) return set_error(BC_ERR_INVALID, "bc_workspace_init: ws not 16-byte aligned");
   return launch_fill_zero(ws, bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int bc_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  constexpr size_t kUnit = size_t(kReadGroups) * kReadThreads * 16;
+  if (!src || !sink) return set_error(BC_ERR_INVALID, "bc_stream_read: NULL pointer");
+  if (reinterpret_cast<uintptr_t>(src) & 15) return set_error(BC_ERR_INVALID, "bc_stream_read: src not 16-byte aligned");
+  if (bytes == 0 || bytes % kUnit != 0)
+    return set_error(BC_ERR_INVALID, "bc_stream_read: %zu bytes is not a positive multiple of %zu", bytes, kUnit);
+  k_stream_read<<<dim3(kReadGroups), dim3(kReadThreads), 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint4*>(src), bytes / 16 / kReadGroups, sink);
+  return check_launch("k_stream_read");
 }
 
 extern "C" int bc_select_channels(const uint16_t* x, int d_in, int k, int32_t* idx_out, void* stream) {

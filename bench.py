@@ -331,6 +331,30 @@ def time_graph(g, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def time_read_probe(model, nbytes=512 << 20, reps=10):
+    """The practical HBM read ceiling: bc_stream_read (256 work-groups, two
+    16-byte non-temporal loads in flight per lane) over nbytes, alternating
+    two buffers (together beyond the 256 MB MALL), timed with events on the
+    stream it runs on.  Returns (us per launch, bytes)."""
+    bc = model.bc
+    bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(2)]
+    sink = torch.empty(256, dtype=torch.int32, device="cuda")
+    for b in bufs:
+        bc.bc_stream_read(b, sink)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        for b in bufs:
+            bc.bc_stream_read(b, sink)
+    e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / (reps * len(bufs))
+    del bufs
+    return us, nbytes
+
+
 def time_attention_kernel(model, n, reps=3, S=None):
     """Average duration of bc_splitk_attn_partial over the 32 layers' caches
     (one launch per layer, as in the step), timed with events on the stream
@@ -726,6 +750,10 @@ def main():
         f"{gemv_us:.1f} us ({gemv_b / gemv_us / 1e3:.0f} GB/s), r_p 0.5 {gemv_sp_us:.1f} us "
         f"({gemv_sp_b / gemv_sp_us / 1e3:.0f} GB/s)")
     achieved = attn_b / (attn_us * 1e-6) / 1e9
+    probe_us, probe_b = time_read_probe(model)
+    probe_gbs = probe_b / (probe_us * 1e-6) / 1e9
+    log(f"[bench] streaming-read probe {probe_b >> 20} MiB: {probe_us:.1f} us ({probe_gbs:.0f} GB/s); attention at "
+        f"{100 * achieved / probe_gbs:.0f}% of it")
     out = {
         "metric": METRIC,
         "value": round(b / (ms * 1e-3) / 1e9, 1),
@@ -746,6 +774,10 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(head_n),
                      "launch_us": round(attn_us, 2), "bytes_per_launch": attn_b, "splits": attn_S},
+        "read_probe": {"kernel": "bc_stream_read: 256 x 1024 lanes, two 16-byte non-temporal loads in flight per lane",
+                       "bytes": probe_b, "us": round(probe_us, 2), "gbs": round(probe_gbs, 1),
+                       "frac_of_peak": round(probe_gbs / HBM_PEAK_GBS, 4),
+                       "attention_frac_of_probe": round(achieved / probe_gbs, 4)},
         "gemv_roofline": {"kernel": "k_gemv (bc_sparse_gemv), gate|up 4096x28672",
                           "dense": {"us": round(gemv_us, 2), "gbs": round(gemv_b / gemv_us / 1e3, 1),
                                     "frac": round(gemv_b / gemv_us / 1e3 / HBM_PEAK_GBS, 4)},

@@ -294,6 +294,16 @@ int bc_lm_head(const bc_model_dims* dims, const uint16_t* hidden, const uint16_t
                const uint16_t* w_head_t, float* logits, int32_t* token, double rms_eps,
                void* ws, size_t ws_bytes, void* stream);
 
+/* Measurement helper, not a step of the method: reads bytes from src once,
+ * as 256 work-groups of 1024 lanes that each stream one contiguous share
+ * with the hot kernels' 16-byte non-temporal loads, two in flight per lane,
+ * and writes one checksum word per work-group to sink[256] (so the loads
+ * are not dead).  Timed, it gives the practical HBM read ceiling reported
+ * beside the 8 TB/s peak.  bytes: a positive multiple of 4 MiB (256 * 1024
+ * * 16); src 16-byte aligned.  Errors: BC_ERR_INVALID for a NULL pointer,
+ * a misaligned src or a size that is not such a multiple. */
+int bc_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

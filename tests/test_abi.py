@@ -77,6 +77,11 @@ def test_host_side_errors(bc):
     assert lib.bc_splitk_attn_partial(1 << 20, 1 << 20, 1 << 20, 64, P, 65, 8, 2, 64, 1, 0.1, 1 << 20, 1 << 20,
                                       1 << 20, P) == bc.BC_ERR_INVALID
     assert lib.bc_splitk_reduce(1 << 20, 1 << 20, 1 << 20, 8, 0, 64, 1 << 20, P) == bc.BC_ERR_INVALID
+    # the streaming-read probe: NULL, misaligned source, sizes that are not a positive multiple of 4 MiB
+    assert lib.bc_stream_read(P, 4 << 20, 1 << 20, P) == bc.BC_ERR_INVALID
+    assert lib.bc_stream_read((1 << 20) + 8, 4 << 20, 1 << 20, P) == bc.BC_ERR_INVALID
+    assert lib.bc_stream_read(1 << 20, 0, 1 << 20, P) == bc.BC_ERR_INVALID
+    assert lib.bc_stream_read(1 << 20, (4 << 20) + 16, 1 << 20, P) == bc.BC_ERR_INVALID
     pol = bc.policy(0.3, 4, 128, block=32)
     out = bc.bc_kv_budget_info()
     assert lib.bc_kv_budget(100, ctypes.byref(pol), ctypes.byref(out)) == bc.BC_ERR_UNSUPPORTED

@@ -250,3 +250,31 @@ def test_kv_compact_and_sel_mode_attention(name, dims, n_cap, n, r_kv):
         assert torch.equal(a, b)
     ref64, _ = oracle.attn_reduce(*oracle.attn_partial(q, K, V, lst, t_sel, H, Hkv, S))
     assert_close_bf16(host_u16(outs[0][3]), ref64)
+
+
+def test_stream_read_probe_checksum():
+    """The read probe (a measurement helper) reads every 16-byte piece of its
+    source: its per-work-group checksums match a host replay of the lane
+    assignment (work-group g streams share g; lane t of wave 0 takes pieces
+    t, t + 2048, ... and each one's partner 1024 pieces on)."""
+    bc = _bc()
+    nbytes = 8 << 20
+    words = np.arange(nbytes // 4, dtype=np.uint32) * np.uint32(2654435761)
+    src = torch.from_numpy(words.view(np.int32)).cuda()
+    sink = torch.full((256,), -1, dtype=torch.int32, device="cuda")
+    bc.bc_stream_read(src, sink)
+    torch.cuda.synchronize()
+    got = host(sink).view(np.uint32)
+    quads = words.reshape(256, -1, 4)
+    x4 = quads[..., 0] ^ quads[..., 1] ^ quads[..., 2] ^ quads[..., 3]   # [group][piece]
+    n16 = x4.shape[1]
+    ref = np.zeros(256, np.uint64)
+    for t in range(64):
+        acc = np.zeros(256, np.uint32)
+        for i in range(t, n16, 2048):
+            acc ^= x4[:, i]
+            if i + 1024 < n16:
+                acc ^= x4[:, i + 1024]
+        ref += acc
+    assert np.array_equal(got, (ref % (1 << 32)).astype(np.uint32))
+
