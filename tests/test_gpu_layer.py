@@ -19,6 +19,8 @@ from gpu_util import assert_close, assert_close_bf16, dev, host, host_u16, works
 pytestmark = pytest.mark.gpu
 
 FP_STAGES = ("x1", "q", "k", "v", "a", "h_mid", "x2", "hff", "h_out")
+# a mid-size shape whose o GEMV chunks (64 channels) split its 128-wide heads
+MID = dict(d=1024, n_heads=8, n_kv_heads=2, head_dim=128, d_ff=2816, vocab=1000, n_layers=1)
 IDX_STAGES = ("idx_qkv", "idx_kv", "idx_o", "idx_gu", "idx_down")
 
 
@@ -105,6 +107,8 @@ LAYER_CASES = [
     # kernel forms the attention output
     ("tiny-dense-40-splits", gen.TINY, 2048, 2048, 1.0, 1.0, 4, 128, 40),
     ("tiny-first-token-dense", gen.TINY, 64, 1, 1.0, 1.0, 4, 128, 1),
+    # head_dim 128 over 64-channel o-GEMV chunks: a chunk holds half a head
+    ("mid-half-head-chunks", MID, 1024, 1000, 1.0, 1.0, 4, 128, 4),
     # over 2048 candidate blocks: a selection kernel ranks the kept blocks
     # once per KV head and the attention work-groups copy their ranks
     ("tiny-long-ctx-ranked", gen.TINY, 40960, 40000, 0.7, 0.3, 4, 128, 0),
@@ -139,9 +143,10 @@ def test_decode_layer_teacher_forced(name, dims, n_cap, n, r_p, r_kv, sinks, win
 
 @pytest.mark.parametrize("dims,n_cap,n,S,r_kv", [(gen.TINY, 2048, 2048, 8, 1.0), (gen.TINY, 64, 1, 1, 1.0),
                                                 (gen.TINY, 2048, 2048, 32, 1.0), (gen.TINY, 2048, 2048, 40, 1.0),
-                                                (gen.TINY, 2048, 2048, 8, 0.3), (gen.LLAMA8B, 2048, 2048, 0, 1.0)],
+                                                (gen.TINY, 2048, 2048, 8, 0.3), (MID, 1024, 1000, 4, 1.0),
+                                                (gen.LLAMA8B, 2048, 2048, 0, 1.0)],
                          ids=["tiny-8-splits", "tiny-first-token", "tiny-32-splits", "tiny-40-splits-reduce-kernel",
-                              "tiny-kv-0.3", "8b-2k"])
+                              "tiny-kv-0.3", "mid-half-head-chunks", "8b-2k"])
 def test_attention_output_equals_reduce_of_partials(dims, n_cap, n, S, r_kv):
     """The layer's attention output equals, bit for bit, bc_splitk_reduce
     over the layer's own split partials: a dense o GEMV forms it in its
