@@ -14,12 +14,15 @@
 // Sixteen waves (four per SIMD) also split the prologue's selection work
 // finely and hide its LDS and memory latency.
 //
-// The prologue forms the input.  IN_NORM computes x = RMSNorm(h) * gain and
-// IN_SEL takes x as given; with k < d_in both then select the exact top-k of
-// |x| (block_topk_2pass) in every work-group, so no separate selection
-// kernel or single-work-group stage sits between two GEMVs.  In dense mode
-// the first ring of weight loads is issued right after the prologue's own
-// loads, before its arithmetic.
+// The prologue forms the input.  IN_NORM computes x = RMSNorm(h) * gain
+// (IN_NORM_SUM first forms h from the previous GEMV's chunk partials and a
+// residual) and IN_SEL takes x as given; with k < d_in both then select the
+// exact top-k of |x| (block_topk_2pass) in every work-group, so no separate
+// selection kernel or single-work-group stage sits between two GEMVs.
+// IN_ATTN (dense) forms the chunk's channels of x from attention split
+// partials, IN_LIST takes x and an optional channel list as given.  The
+// first ring of weight loads goes out right after the prologue's own loads,
+// before its arithmetic (for a selection, once the list is known).
 //
 // Several chunks write fp32 partials ([chunk][d_out]); a finish kernel adds
 // them in chunk order (deterministic) and applies the epilogue: bf16 store,
@@ -28,8 +31,9 @@
 // epilogue itself.  No work-group waits for another: cross-XCD fences cost
 // far more on this chip than a kernel boundary.
 #include <math.h>
-#include <type_traits>
 #include <stdlib.h>
+
+#include <type_traits>
 
 #include "bc_device.hpp"
 #include "bc_internal.hpp"
