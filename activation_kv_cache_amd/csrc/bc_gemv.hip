@@ -7,10 +7,10 @@
 // stored tile-major (128-column tiles, each tile's rows contiguous).  A
 // work-group owns one 128-column tile of y and one chunk of list positions.
 // Its 1024 lanes form 64 row slots of 16 lanes; a slot reads a row's 256 B
-// with one 16-byte load per lane.  Each slot keeps a ring of 2 or 4 rows in
-// flight (32 or 64 KB per work-group), issued as non-temporal loads: the
-// weights are read once per step and should not evict the small vectors the
-// kernels share.
+// with one 16-byte load per lane.  Each slot keeps a ring of 2 rows in
+// flight (32 KB per work-group), issued as non-temporal loads: the weights
+// are read once per step and should not evict the small vectors the kernels
+// share.
 // Sixteen waves (four per SIMD) also split the prologue's selection work
 // finely and hide its LDS and memory latency.
 //
@@ -43,11 +43,10 @@ namespace bc {
 namespace {
 
 constexpr int kSlots = kGemvThreads / 16;   // 64 row slots of 16 lanes
-// rows in flight per slot: 2 for chunk-partial launches (chunks of at most
-// a few thousand rows, where a shallower ring measured 2-4% faster), 4 for
-// single-chunk launches (up to 4096 rows per work-group)
+// rows in flight per slot (32 KB per work-group): 2 measured 2-4% faster
+// than 4, and 6 or 8 slower still
 template <int OUT>
-constexpr int ring_depth() { return OUT == OUT_PARTIAL ? 2 : 4; }
+constexpr int ring_depth() { return 2; }
 constexpr int kNW = kGemvThreads / kWave;   // 16 waves
 constexpr int kTopkShift = 3;               // first selection pass: 4096 bins
 // IN_ATTN: one thread per channel (rows_per_split <= kGemvThreads), so a
