@@ -4,6 +4,8 @@ host before anything is enqueued.  No device compute here (CPU suite)."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -99,3 +101,41 @@ def test_workspace_queries_monotone(bc):
     assert 0 < a < b < 64 << 20
     assert bc.bc_sparse_gemv_workspace_bytes(28672, 4096) >= bc.bc_sparse_gemv_workspace_bytes(28672, 2048) > 0
     assert bc.bc_lm_head_workspace_bytes(md) > 0
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include "bc.h"
+
+int main(void) {
+  bc_kv_policy pol = {0.3, 4, 1024, 16};
+  bc_kv_budget_info b;
+  bc_model_dims md = {32, 4096, 14336, 128256, 32, 8, 128};
+  if (bc_abi_version() != BC_ABI_VERSION) return 1;
+  if (bc_channel_keep(0.5, 4096) != 2048) return 2;
+  if (bc_kv_budget(131072, &pol, &b) != BC_OK || b.t_sel != 39316) return 3;
+  if (bc_layer_workspace_bytes(&md, 131072, 32) == 0) return 4;
+  if (bc_select_channels(NULL, 16, 4, NULL, NULL) != BC_ERR_INVALID) return 5;
+  printf("%s\n", bc_last_error());
+  return 0;
+}
+"""
+
+
+def test_header_compiles_and_links_as_c(tmp_path):
+    """include/bc.h is plain C: a C11 program includes it, links libbc.so and
+    calls the host-only entry points (no device work)."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    if not os.path.exists(LIB):
+        pytest.fail("libbc.so is not built: run __graft_entry__.build()")
+    src = tmp_path / "abi.c"
+    exe = tmp_path / "abi"
+    src.write_text(C_PROGRAM)
+    subprocess.run([cc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-I", os.path.dirname(HEADER), str(src), LIB,
+                    "-Wl,-rpath," + os.path.dirname(LIB), "-o", str(exe)], check=True)
+    run = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert run.returncode == 0, (run.returncode, run.stdout, run.stderr)
+    assert "bc_select_channels" in run.stdout
+
