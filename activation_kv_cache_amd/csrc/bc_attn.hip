@@ -279,6 +279,24 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
   AttnRows rw;
   int base = lo + w * TPI;
   auto tok_dense = [](int pc) { return pc; };
+  // the rows of list positions [base, c1) in steps of STEP, rw already
+  // holding those of base (< c1); software-pipelined: a wave's next rows are
+  // in flight while it computes the current ones (two row buffers taken in
+  // turn; a load past c1 reads row c1-1 again and is never used)
+  auto stream_rows = [&](auto tok, int c1) {
+    AttnRows nx;
+    attn_load<D>(Kg, Vg, tok, base + STEP, c1, sub, nx);
+    for (;;) {
+      attn_compute<D, G, true>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
+      base += STEP;
+      if (base >= c1) break;
+      attn_load<D>(Kg, Vg, tok, base + STEP, c1, sub, rw);
+      attn_compute<D, G, true>(nx, &sm.q[0][0], base, c1, sub, r, c, tau, st);
+      base += STEP;
+      if (base >= c1) break;
+      attn_load<D>(Kg, Vg, tok, base + STEP, c1, sub, nx);
+    }
+  };
   if constexpr (LM == L_DENSE) {
     if (base < hi_main) attn_load<D>(Kg, Vg, tok_dense, base, hi_main, sub, rw);
   }
@@ -363,25 +381,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
       const int tw = p.n_ctx - p.bud.window + (pc - nb0);
       return pc < S0 ? pc : (pc < nb0 ? tb : tw);
     };
-    // software pipeline: a wave's next rows are in flight while it computes
-    // the current ones (two row buffers, taken in turn; a load past c1 reads
-    // row c1-1 again and is never used)
     auto run = [&](auto tok) {
       const int c1 = hi_main;
       if (base >= c1) return;
       if constexpr (LM == L_SCORES) attn_load<D>(Kg, Vg, tok, base, c1, sub, rw);
-      AttnRows nx;
-      attn_load<D>(Kg, Vg, tok, base + STEP, c1, sub, nx);
-      for (;;) {
-        attn_compute<D, G, true>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
-        base += STEP;
-        if (base >= c1) break;
-        attn_load<D>(Kg, Vg, tok, base + STEP, c1, sub, rw);
-        attn_compute<D, G, true>(nx, &sm.q[0][0], base, c1, sub, r, c, tau, st);
-        base += STEP;
-        if (base >= c1) break;
-        attn_load<D>(Kg, Vg, tok, base + STEP, c1, sub, nx);
-      }
+      stream_rows(tok, c1);
     };
     if constexpr (LM == L_DENSE) {
       run(tok_dense);
@@ -408,13 +412,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
       __syncthreads();
       auto tok = [&](int pc) -> int { return sm.idx[pc - c0]; };
       base = c0 + w * TPI;
-      for (; base + TPI <= c1; base += STEP) {
-        attn_load<D>(Kg, Vg, tok, base, c1, sub, rw);
-        attn_compute<D, G, false>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
-      }
       if (base < c1) {
         attn_load<D>(Kg, Vg, tok, base, c1, sub, rw);
-        attn_compute<D, G, true>(rw, &sm.q[0][0], base, c1, sub, r, c, tau, st);
+        stream_rows(tok, c1);
       }
       __syncthreads();
     }
