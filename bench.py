@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import itertools
 import json
 import math
 import os
@@ -60,7 +61,10 @@ def attn_bytes(n_sel, S, sparse):
     return kv + part + (4 * D["n_kv_heads"] * n_sel if sparse else 0)
 
 
-def layer_bytes(n, r_p, r_kv, t_sel, S):
+def layer_bytes(n, r_p, r_kv, t_sel, S, scored=True):
+    """Algorithmic bytes of one layer.  scored=False is the KV-window
+    baseline: the kept tokens are the sinks and the most recent ones, so no
+    summaries are scored and no index list is written or read."""
     D = DIMS
     d, dff, H, Hkv, hd = D["d"], D["d_ff"], D["n_heads"], D["n_kv_heads"], D["head_dim"]
     sp = r_p < 1
@@ -69,15 +73,28 @@ def layer_bytes(n, r_p, r_kv, t_sel, S):
     b += gemv_bytes(H * hd, d, kd, sp)
     b += gemv_bytes(d, 2 * dff, kd, sp)
     b += gemv_bytes(dff, d, kf, sp)
-    b += attn_bytes(t_sel, S, r_kv < 1)
-    if r_kv < 1:
+    b += attn_bytes(t_sel, S, r_kv < 1 and scored)
+    if r_kv < 1 and scored:
         b += 2 * Hkv * hd * 2 * ((n + 15) // 16) + 4 * Hkv * t_sel
     return b
 
 
-def step_bytes(n, r_p, r_kv, t_sel, S):
+def step_bytes(n, r_p, r_kv, t_sel, S, scored=True):
     D = DIMS
-    return D["n_layers"] * layer_bytes(n, r_p, r_kv, t_sel, S) + 2 * D["d"] * D["vocab"] + 4 * D["vocab"]
+    return D["n_layers"] * layer_bytes(n, r_p, r_kv, t_sel, S, scored) + 2 * D["d"] * D["vocab"] + 4 * D["vocab"]
+
+
+def byte_bound(n, r_p, r_kv):
+    """Ideal speedup of a mode over dense decoding from bytes alone (README
+    "Quick start", bound): B / (B - dB) with B the projection weights, LM
+    head and K and V bytes of the step and dB the bytes the two branches
+    skip; summaries, index lists and activations are left out."""
+    D = DIMS
+    kvd = D["n_kv_heads"] * D["head_dim"]
+    w_proj = 2 * D["n_layers"] * (2 * D["d"] ** 2 + 2 * D["d"] * kvd + 3 * D["d"] * D["d_ff"])
+    B = w_proj + 2 * D["vocab"] * D["d"] + 2 * 2 * D["n_layers"] * kvd * n
+    dB = (1 - r_p) * w_proj + (1 - r_kv) * 2 * 2 * D["n_layers"] * kvd * n
+    return B / (B - dB)
 
 
 def n_star_k(r_p, r_kv, ext=False):
@@ -102,6 +119,44 @@ def crossing_k(contexts, d_vals):
             na, nb, da, db = contexts[i], contexts[i + 1], d_vals[i], d_vals[i + 1]
             return (na + (nb - na) * da / (da - db)) / 1024
     return None
+
+
+def block_resamples(blocks):
+    """Every ordered draw of `blocks` blocks with replacement (blocks**blocks
+    of them: 256 for four blocks, 3,125 for five), as the paper's timing
+    intervals enumerate them (README "Reproduce the paper", conventions)."""
+    return np.array(list(itertools.product(range(blocks), repeat=blocks)), dtype=np.int64)
+
+
+def resample_intervals(t, contexts, pairs, level=0.95):
+    """Block-resampled intervals of the paired speedups and of each pair's
+    crossing.  t[mode] holds step times [blocks][contexts]; every resample
+    averages the per-block paired speedups t_dense / t_mode over its drawn
+    blocks, and its crossing is crossing_k of the averaged S_proj - S_kv.
+    The interval is the central `level` percentile range over all resamples
+    (linear interpolation); resamples whose difference never changes sign
+    are counted, not placed.  Returns (speedup intervals per mode, crossing
+    intervals per pair key)."""
+    B = next(iter(t.values())).shape[0]
+    draws = block_resamples(B)
+    q = (50 * (1 - level), 50 * (1 + level))
+    sp = {m: np.asarray(t["dense"], float) / np.asarray(t[m], float) for m in t if m != "dense"}
+    speed = {}
+    for m, s in sp.items():
+        means = s[draws].mean(axis=1)        # [resamples][contexts]
+        lo, hi = np.percentile(means, q, axis=0)
+        speed[m] = {"lo": [round(float(x), 4) for x in lo], "hi": [round(float(x), 4) for x in hi]}
+    cross = {}
+    for key, mp, mk in pairs:
+        d = (sp[mp] - sp[mk])[draws].mean(axis=1)
+        cs = [crossing_k(contexts, [float(x) for x in row]) for row in d]
+        got = np.array([c for c in cs if c is not None], float)
+        rec = {"resamples": len(cs), "no_crossing": len(cs) - len(got), "level": level}
+        if len(got):
+            lo, hi = np.percentile(got, q)
+            rec.update(lo_k=round(float(lo), 2), hi_k=round(float(hi), 2))
+        cross[key] = rec
+    return speed, cross
 
 
 def kv_plan(n, r_kv, sinks=SINKS, window=WINDOW, block=16):
@@ -237,35 +292,36 @@ class Model:
         log(f"[bench] model ready in {time.time() - t0:.1f}s; "
             f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
 
-    def plan(self, n, r_p, r_kv):
+    def plan(self, n, r_p, r_kv, window=WINDOW):
+        """(policy, T_sel, splits); window=n gives the KV-window baseline."""
         bc = self.bc
-        pol = bc.policy(r_kv, SINKS, WINDOW)
+        pol = bc.policy(r_kv, SINKS, window)
         t_sel = bc.bc_kv_budget(n, pol)["t_sel"]
         S = bc.bc_attn_default_splits(t_sel, DIMS["n_kv_heads"])
         return pol, t_sel, S
 
-    def step(self, n, r_p, r_kv):
+    def step(self, n, r_p, r_kv, window=WINDOW):
         bc = self.bc
-        pol, _, S = self.plan(n, r_p, r_kv)
+        pol, _, S = self.plan(n, r_p, r_kv, window)
         st = bc.make_step(n, r_p, pol, S)
         self.h.copy_(self.h0)
         bc.bc_decode_step(self.md, self.layer_array, self.g_final, self.w_head, st, self.h, self.logits, self.token,
                           self.ws)
 
-    def graph(self, n, r_p, r_kv):
-        self.step(n, r_p, r_kv)          # eager once: validates arguments outside capture
+    def graph(self, n, r_p, r_kv, window=WINDOW):
+        self.step(n, r_p, r_kv, window)          # eager once: validates arguments outside capture
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.step(n, r_p, r_kv)
+            self.step(n, r_p, r_kv, window)
         torch.cuda.synchronize()
         return g
 
-    def layer_graph(self, n, r_p, r_kv):
+    def layer_graph(self, n, r_p, r_kv, window=WINDOW):
         """One bc_decode_layer call (layer 0, residual stored at the end), as a
         graph: the per-layer latency."""
         bc = self.bc
-        pol, _, S = self.plan(n, r_p, r_kv)
+        pol, _, S = self.plan(n, r_p, r_kv, window)
         st = bc.make_step(n, r_p, pol, S)
 
         def one():
@@ -567,8 +623,25 @@ def cpu_baseline(model, n):
         elapsed += time.perf_counter() - t1
         reps += 1
     sample_bytes = layer_bytes(n, 1.0, 1.0, n, S)
-    return {"value": round(sample_bytes * reps / elapsed / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+    # the same layer once more on one thread (thread counts only split
+    # independent outputs, so the result is the same)
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        t1 = time.perf_counter()
+        oracle.decode_layer(h, W, K.copy(), V.copy(), summ.copy(), n, dims, 1.0, 1.0, SINKS, WINDOW, S)
+        one = time.perf_counter() - t1
+    finally:
+        oracle.set_num_threads(threads)
+    log(f"[bench] cpu oracle: one layer {elapsed / reps:.2f}s on {threads} threads, {one:.2f}s on one")
+    cpu_model = ""
+    try:
+        cpu_model = next(ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    return {"value": round(sample_bytes * reps / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "cpu_model": cpu_model, "layer_s": round(elapsed / reps, 3),
+            "single_thread": {"value": round(sample_bytes / one / 1e9, 4), "layer_s": round(one, 3)},
             "sample": f"one of the 32 decoder layers of the dense {n}-token step (weights "
                       f"{layer_bytes(0, 1.0, 1.0, 0, 1) / 1e6:.0f} MB + KV {4096 * n / 1e6:.0f} MB), fp64 oracle, "
                       f"{reps} run(s) in {elapsed:.1f}s; GB/s = that layer's algorithmic bytes / oracle time"}
@@ -594,6 +667,7 @@ def crossover_sweep(model, contexts, blocks, steps, warmup, seed=0):
     cells = [(m, n) for m in SWEEP_MODES for n in contexts]
     t = {m: np.zeros((blocks, len(contexts))) for m in SWEEP_MODES}
     for b in range(blocks):
+        tb = time.time()
         order = rng.permutation(len(cells))
         for ci in order:
             m, n = cells[ci]
@@ -601,11 +675,15 @@ def crossover_sweep(model, contexts, blocks, steps, warmup, seed=0):
             g = model.graph_sel(n, r_p, r_kv) if once else model.graph(n, r_p, r_kv)
             t[m][b, contexts.index(n)] = time_graph(g, steps, warmup) * 1000.0
             del g
-        log(f"[bench] crossover block {b + 1}/{blocks} done")
+        log(f"[bench] crossover block {b + 1}/{blocks} done in {time.time() - tb:.0f}s")
     sp = {m: (t["dense"] / t[m]).mean(axis=0) for m in SWEEP_MODES}
     out = {"contexts": contexts, "blocks": blocks, "steps": steps,
            "step_us": {m: [round(x, 1) for x in t[m].mean(axis=0)] for m in SWEEP_MODES},
            "speedup": {m: [round(x, 4) for x in sp[m]] for m in SWEEP_MODES if m != "dense"}, "pairs": {}}
+    keys = [(f"{r_p}/{r_kv}" + (" sel" if SWEEP_MODES[mk][2] else ""), mp, mk) for mp, mk, r_p, r_kv in PAIRS]
+    sp_iv, cross_iv = resample_intervals(t, contexts, keys)
+    out["speedup_interval"] = sp_iv
+    out["resamples"] = int(blocks ** blocks)
     for mp, mk, r_p, r_kv in PAIRS:
         once = SWEEP_MODES[mk][2]
         d_vals = [float(x) for x in (t["dense"] / t[mp] - t["dense"] / t[mk]).mean(axis=0)]
@@ -625,8 +703,12 @@ def crossover_sweep(model, contexts, blocks, steps, warmup, seed=0):
             "measured_minus_n_star_ext_k": None if c is None else round(c - nx, 2),
             "pred_k": None if pred is None else round(pred, 2),
             "measured_minus_pred_k": None if (c is None or pred is None) else round(c - pred, 2),
-            "pred_fit": {"bw_gbs": round(bw, 1), "cost_proj_us": round(cp, 1), "cost_kv_us": round(ck, 1)}}
-        log(f"[bench] crossing {key}: measured {c if c is None else round(c, 1)}K, n* {ns:.1f}K, "
+            "pred_fit": {"bw_gbs": round(bw, 1), "cost_proj_us": round(cp, 1), "cost_kv_us": round(ck, 1)},
+            "measured_interval": cross_iv[key]}
+        iv = cross_iv[key]
+        iv_s = f"[{iv['lo_k']:.1f}, {iv['hi_k']:.1f}]K" if "lo_k" in iv else "none"
+        log(f"[bench] crossing {key}: measured {c if c is None else round(c, 1)}K "
+            f"(95% over {iv['resamples']} block resamples {iv_s}), n* {ns:.1f}K, "
             f"n*_ext {nx:.1f}K, cost-aware prediction {pred if pred is None else round(pred, 1)}K")
     return out
 
@@ -643,7 +725,7 @@ def main():
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="only copy this many bytes 5 times (calibration of the HBM byte counters)")
     ap.add_argument("--split-sweep", default="", help="attention split counts to sweep in --kernels")
-    ap.add_argument("--crossover-blocks", type=int, default=3,
+    ap.add_argument("--crossover-blocks", type=int, default=4,
                     help="blocks of the crossover sweep (every mode at 2K, 4K, ..., 128K); 0 skips it")
     ap.add_argument("--crossover-steps", type=int, default=10, help="timed steps per sweep cell")
     ap.add_argument("--crossover-max-k", type=int, default=160,
@@ -700,39 +782,48 @@ def main():
 
     # the dense step at each context (the headline is the largest); the
     # other modes are timed by the crossover sweep
-    cells = [(1.0, 1.0, n) for n in contexts]
+    # a cell is (r_p, r_kv, n, kv policy): "scored" keeps sinks, the top
+    # scored blocks and a 1024-token window; "window" is the KV-window
+    # baseline (sinks and the most recent tokens, window = n)
+    cells = [(1.0, 1.0, n, "scored") for n in contexts]
     if args.cells == "default":
         for n in sorted({min(contexts), head_n}):
-            cells += [(0.5, 1.0, n), (1.0, 0.3, n), (0.5, 0.3, n)]
+            cells += [(0.5, 1.0, n, "scored"), (1.0, 0.3, n, "scored"), (0.5, 0.3, n, "scored"),
+                      (1.0, 0.3, n, "window")]
     elif args.cells == "dense":
         pass
     elif args.cells == "none":
-        cells = [(1.0, 1.0, head_n)]
+        cells = [(1.0, 1.0, head_n, "scored")]
     elif args.cells != "dense":
-        # explicit list "r_p:r_kv:n,..." (the dense cell at the largest context is always kept)
-        cells = [(1.0, 1.0, head_n)] + [(float(a), float(b), int(c)) for a, b, c in
-                                         (t.split(":") for t in args.cells.split(","))]
+        # explicit list "r_p:r_kv:n[:window],..." (the dense cell at the largest context is always kept)
+        cells = [(1.0, 1.0, head_n, "scored")] + [
+            (float(f[0]), float(f[1]), int(f[2]), f[3] if len(f) > 3 else "scored")
+            for f in (t.split(":") for t in args.cells.split(","))]
 
     results = []
     headline = None
-    for (r_p, r_kv, n) in cells:
-        _, t_sel, S = model.plan(n, r_p, r_kv)
-        g = model.graph(n, r_p, r_kv)
+    for (r_p, r_kv, n, kv) in cells:
+        win = n if kv == "window" else WINDOW
+        _, t_sel, S = model.plan(n, r_p, r_kv, win)
+        g = model.graph(n, r_p, r_kv, win)
         is_head = (r_p, r_kv, n) == (1.0, 1.0, head_n)
         ms = time_graph(g, args.steps if is_head else min(args.steps, 20), args.warmup)
         del g
-        b = step_bytes(n, r_p, r_kv, t_sel, S)
-        gl = model.layer_graph(n, r_p, r_kv)
+        b = step_bytes(n, r_p, r_kv, t_sel, S, kv != "window")
+        gl = model.layer_graph(n, r_p, r_kv, win)
         lms = time_graph(gl, 50, args.warmup)
         del gl
-        lb = layer_bytes(n, r_p, r_kv, t_sel, S)
-        cell = {"r_p": r_p, "r_kv": r_kv, "context": n, "step_us": round(ms * 1000, 1),
+        lb = layer_bytes(n, r_p, r_kv, t_sel, S, kv != "window")
+        cell = {"r_p": r_p, "r_kv": r_kv, "context": n, "kv_policy": kv if r_kv < 1 else "dense",
+                "step_us": round(ms * 1000, 1),
                 "gbs": round(b / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "bytes": b, "t_sel": t_sel, "splits": S,
                 "layer_us": round(lms * 1000, 2), "layer_bytes": lb,
-                "layer_frac_hbm": round(lb / (lms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                "layer_frac_hbm": round(lb / (lms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "byte_bound": round(byte_bound(n, r_p, r_kv), 4)}
         results.append(cell)
-        log(f"[bench] r_p={r_p} r_kv={r_kv} n={n}: {cell['step_us']} us/step, {cell['gbs']} GB/s "
+        log(f"[bench] r_p={r_p} r_kv={r_kv}{' (KV window)' if kv == 'window' and r_kv < 1 else ''} n={n}: "
+            f"{cell['step_us']} us/step, {cell['gbs']} GB/s "
             f"({100 * cell['frac_hbm']:.1f}% of 8 TB/s); one layer {cell['layer_us']} us "
             f"({100 * cell['layer_frac_hbm']:.1f}%)")
         if is_head:
@@ -741,6 +832,9 @@ def main():
         dense = next((x for x in results if x["context"] == c["context"] and x["r_p"] == 1 and x["r_kv"] == 1), None)
         if dense:
             c["speedup_vs_dense"] = round(dense["step_us"] / c["step_us"], 3)
+            if c is not dense:
+                log(f"[bench] n={c['context']} r_p={c['r_p']} r_kv={c['r_kv']} {c['kv_policy']}: "
+                    f"{c['speedup_vs_dense']}x dense (byte bound {c['byte_bound']:.2f}x)")
 
     ms, b = headline
     attn_us, attn_b, attn_S = time_attention_kernel(model, head_n)

@@ -56,6 +56,10 @@ KV_CASES = [
     ("tiny-160k-16-keys", gen.TINY, 160000, 160000, 0.3, 4, 128),
     ("8b-192k-16-keys", gen.LLAMA8B, 196608, 196608, 0.3, 4, 1024),
     ("tiny-320k-32-keys", gen.TINY, 320000, 320000, 0.5, 4, 128),
+    # the KV-window baseline: a window as long as the context leaves no
+    # scored blocks, so the list is the sinks and the most recent tokens
+    ("tiny-window-0.5", gen.TINY, 2048, 2000, 0.5, 4, 2000),
+    ("8b-128k-window-0.3", gen.LLAMA8B, 131072, 131072, 0.3, 4, 131072),
 ]
 
 

@@ -286,6 +286,24 @@ def test_kv_select_planted_block_and_dense():
     assert np.array_equal(dense, np.tile(np.arange(n, dtype=np.int32), (Hkv, 1)))
 
 
+@pytest.mark.parametrize("n,r_kv", [(2048, 0.3), (2051, 0.5), (40000, 0.3), (17, 0.3), (3, 0.5)])
+def test_kv_window_policy_is_sinks_and_most_recent(n, r_kv):
+    """A window at least as long as the context leaves no room for scored
+    blocks: the kept set is the first min(4, T) tokens and the T - 4 most
+    recent ones, T = floor(r_kv n + 1/2) (the sinks-plus-recent window of
+    StreamingLLM that the paper's KV-window baseline keeps)."""
+    H, Hkv, D = 8, 2, 64
+    q = gen.normal_bf16(4, f"win/q{n}", (H, D))
+    summ = np.zeros((Hkv, (n + 15) // 16, D, 2), np.uint16)
+    bud = oracle.kv_budget(n, r_kv, 4, n)
+    T = min(n, int(math.floor(r_kv * n + 0.5)))
+    s = min(4, T)
+    want = np.array(list(range(s)) + list(range(n - (T - s), n)), np.int32)
+    assert bud["k_blk"] == 0 and bud["T_sel"] == T
+    idx = oracle.kv_select(q, summ, n, H, Hkv, r_kv, 4, n)
+    assert np.array_equal(idx, np.tile(want, (Hkv, 1)))
+
+
 # ------------------------------------------------------------------ attention
 def _softmax_attention(q, K, V, lst, H, Hkv):
     """Textbook softmax(q K^T / sqrt(D)) V over the listed tokens, numpy fp64."""
