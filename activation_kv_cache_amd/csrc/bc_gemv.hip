@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
     stride = size_t(p.d_out);
   }
   // list position j -> its row; positions past the chunk re-read its last
-  // row (an L2 hit), so every slot issues the same sequence of loads.  Row
+  // row, so every slot issues the same sequence of loads.  Row
   // ids are clamped to the matrix, so a bad id cannot read outside it.
   const unsigned last_row = unsigned(p.d_in - 1);
   auto row_ptr = [&](int j) -> const uint16_t* {
@@ -375,30 +375,33 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
   float acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+  auto consume = [&](int j, const u32x4& wv) {
+    const float x = j < n ? sm.list.xv[j] : 0.f;
+    acc[0] += bf16_lo(wv.x) * x;
+    acc[1] += bf16_hi(wv.x) * x;
+    acc[2] += bf16_lo(wv.y) * x;
+    acc[3] += bf16_hi(wv.y) * x;
+    acc[4] += bf16_lo(wv.z) * x;
+    acc[5] += bf16_hi(wv.z) * x;
+    acc[6] += bf16_lo(wv.w) * x;
+    acc[7] += bf16_hi(wv.w) * x;
+  };
+  // Ring groups of kRing steps; every group but the last refills its slot
+  // with the row kRing steps ahead.  The last group only consumes: its
+  // refills would all lie past the chunk, and waiting for them would add a
+  // memory round trip to the end of every work-group.
   const int nsteps = (n + kSlots - 1) / kSlots;
-  for (int st = 0; st < nsteps; st += kRing) {
+  int st = 0;
+  for (; st + kRing < nsteps; st += kRing) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
       const int j = slot + kSlots * (st + u);
-      const float x = j < n ? sm.list.xv[j] : 0.f;
-      const u32x4 wv = ring[u];
-      acc[0] += bf16_lo(wv.x) * x;
-      acc[1] += bf16_hi(wv.x) * x;
-      acc[2] += bf16_lo(wv.y) * x;
-      acc[3] += bf16_hi(wv.y) * x;
-      acc[4] += bf16_lo(wv.z) * x;
-      acc[5] += bf16_hi(wv.z) * x;
-      acc[6] += bf16_lo(wv.w) * x;
-      acc[7] += bf16_hi(wv.w) * x;
+      consume(j, ring[u]);
       ring[u] = load_row_nt(row_ptr(j + kSlots * kRing));
     }
   }
-  // the ring's last loads (past the chunk) are consumed here so that none
-  // is still in flight when the registers are reused
-  uint32_t sink = 0;
 #pragma unroll
-  for (int u = 0; u < kRing; ++u) sink |= ring[u].x & 0u;
-  acc[0] += __uint_as_float(sink);
+  for (int u = 0; u < kRing; ++u) consume(slot + kSlots * (st + u), ring[u]);
 
   // ------------------------------------------------------------- epilogue
   // The four slots of a wave (its 16-lane rows) hold the same 8 columns:

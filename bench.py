@@ -387,27 +387,31 @@ def time_graph(g, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def time_read_probe(model, nbytes=512 << 20, reps=10):
-    """The practical HBM read ceiling: bc_stream_read (256 work-groups, two
-    16-byte non-temporal loads in flight per lane) over nbytes, alternating
-    two buffers (together beyond the 256 MB MALL), timed with events on the
+def time_read_probe(model, nbytes=512 << 20, reps=10, pool=1 << 30):
+    """The practical HBM read ceiling at one launch size: bc_stream_read (256
+    work-groups, two 16-byte non-temporal loads in flight per lane) over
+    nbytes, rotating over the nbytes-sized pieces of a pool of at least two
+    pieces and 1 GiB (beyond the 256 MB MALL), timed with events on the
     stream it runs on.  Returns (us per launch, bytes)."""
     bc = model.bc
-    bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(2)]
+    count = max(2, pool // nbytes)
+    whole = torch.ones(count * nbytes // 4, dtype=torch.int32, device="cuda")
+    bufs = [whole[i * (nbytes // 4):(i + 1) * (nbytes // 4)] for i in range(count)]
     sink = torch.empty(256, dtype=torch.int32, device="cuda")
     for b in bufs:
         bc.bc_stream_read(b, sink)
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rounds = max(1, reps * 2 // count)
     e0.record(s)
-    for _ in range(reps):
+    for _ in range(rounds):
         for b in bufs:
             bc.bc_stream_read(b, sink)
     e1.record(s)
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1000.0 / (reps * len(bufs))
-    del bufs
+    us = e0.elapsed_time(e1) * 1000.0 / (rounds * len(bufs))
+    del bufs, whole
     return us, nbytes
 
 
@@ -848,6 +852,16 @@ def main():
     probe_gbs = probe_b / (probe_us * 1e-6) / 1e9
     log(f"[bench] streaming-read probe {probe_b >> 20} MiB: {probe_us:.1f} us ({probe_gbs:.0f} GB/s); attention at "
         f"{100 * achieved / probe_gbs:.0f}% of it")
+    # the same probe at the gate|up GEMV's own sizes (224 and 112 MiB, within
+    # 0.05% of its dense and r_p 0.5 bytes): a short launch pays its ramp too
+    gemv_probe = {}
+    for mib, (g_us, g_b) in ((224, (gemv_us, gemv_b)), (112, (gemv_sp_us, gemv_sp_b))):
+        p_us, p_b = time_read_probe(model, mib << 20)
+        p_gbs = p_b / p_us / 1e3
+        gemv_probe[f"{mib}MiB"] = {"us": round(p_us, 2), "gbs": round(p_gbs, 1),
+                                   "gemv_frac_of_probe": round(g_b / g_us / 1e3 / p_gbs, 4)}
+        log(f"[bench] streaming-read probe {mib} MiB: {p_us:.1f} us ({p_gbs:.0f} GB/s); gate|up GEMV of that size at "
+            f"{100 * g_b / g_us / 1e3 / p_gbs:.0f}% of it")
     out = {
         "metric": METRIC,
         "value": round(b / (ms * 1e-3) / 1e9, 1),
@@ -876,7 +890,8 @@ def main():
                           "dense": {"us": round(gemv_us, 2), "gbs": round(gemv_b / gemv_us / 1e3, 1),
                                     "frac": round(gemv_b / gemv_us / 1e3 / HBM_PEAK_GBS, 4)},
                           "r_p_0.5": {"us": round(gemv_sp_us, 2), "gbs": round(gemv_sp_b / gemv_sp_us / 1e3, 1),
-                                      "frac": round(gemv_sp_b / gemv_sp_us / 1e3 / HBM_PEAK_GBS, 4)}},
+                                      "frac": round(gemv_sp_b / gemv_sp_us / 1e3 / HBM_PEAK_GBS, 4)},
+                          "read_probe_same_size": gemv_probe},
         "cells": results,
     }
     if args.cells == "default":
