@@ -74,6 +74,8 @@ _SIG = {
     "bc_sparse_gemv_workspace_bytes": (c_size_t, [c_int, c_int]),
     "bc_sparse_gemv": (c_int, [P, c_int, c_int, P, P, c_int, P, P, c_size_t, P]),
     "bc_sparse_gemv_tiled": (c_int, [P, c_int, c_int, P, P, c_int, P, P, c_size_t, P]),
+    "bc_sparse_gemv_batch_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
+    "bc_sparse_gemv_batch": (c_int, [P, c_int, c_int, c_int, P, P, c_int, c_int, P, P, P, c_size_t, P]),
     "bc_kv_score_select_workspace_bytes": (c_size_t, [c_int, c_int, ctypes.POINTER(bc_kv_policy)]),
     "bc_kv_score_select": (c_int, [P, P, c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(bc_kv_policy), P, P,
                                    P, c_size_t, P]),
@@ -167,6 +169,10 @@ def bc_sparse_gemv_workspace_bytes(d_out: int, k: int) -> int:
     return _lib.bc_sparse_gemv_workspace_bytes(int(d_out), int(k))
 
 
+def bc_sparse_gemv_batch_workspace_bytes(d_in: int, d_out: int, k: int, batch: int) -> int:
+    return _lib.bc_sparse_gemv_batch_workspace_bytes(int(d_in), int(d_out), int(k), int(batch))
+
+
 def bc_kv_score_select_workspace_bytes(n_ctx: int, n_kv_heads: int, pol: bc_kv_policy) -> int:
     return _lib.bc_kv_score_select_workspace_bytes(int(n_ctx), int(n_kv_heads), ctypes.byref(pol))
 
@@ -208,6 +214,19 @@ def bc_sparse_gemv_tiled(wt_packed, d_in: int, d_out: int, x, idx, k: int, y, ws
     p, n = _ws(ws)
     return _check(_lib.bc_sparse_gemv_tiled(_ptr(wt_packed), int(d_in), int(d_out), _ptr(x), _ptr(idx), int(k),
                                             _ptr(y), p, n, _stream(stream)), "bc_sparse_gemv_tiled")
+
+
+def bc_sparse_gemv_batch(wt, x, idx, k: int, y, ws, n_union=None, d_in=None, d_out=None, tiled=False,
+                         stream=None):
+    """x [batch][d_in], idx [batch][k] or None, y [batch][d_out]; wt is
+    [d_in][d_out] row-major, or tile-major (tiled=True: pass d_in, d_out)."""
+    batch = x.shape[0]
+    if not tiled:
+        d_in, d_out = wt.shape
+    p, n = _ws(ws)
+    return _check(_lib.bc_sparse_gemv_batch(_ptr(wt), 1 if tiled else 0, int(d_in), int(d_out), _ptr(x), _ptr(idx),
+                                            int(k), int(batch), _ptr(y), _ptr(n_union), p, n, _stream(stream)),
+                  "bc_sparse_gemv_batch")
 
 
 def bc_kv_score_select(q, summary, n_ctx: int, n_heads: int, n_kv_heads: int, head_dim: int,

@@ -110,6 +110,24 @@ def n_star_k(r_p, r_kv, ext=False):
     return (1 - r_p) * w_proj / ((1 - r_kv - (1.0 / 16 if ext else 0.0)) * kv_per_token) / 1024
 
 
+def batch_crossover_k(union_keep, r_kv, batch):
+    """Byte crossover of a batch (README "Quick start", crossover_batch): the
+    projection weights are read once for the union of the batch's channel
+    lists (union_keep of them), the K and V bytes once per sequence; in
+    units of 1024 tokens."""
+    D = DIMS
+    kvd = D["n_kv_heads"] * D["head_dim"]
+    w_proj = 2 * D["n_layers"] * (2 * D["d"] ** 2 + 2 * D["d"] * kvd + 3 * D["d"] * D["d_ff"])
+    kv_per_token = 2 * 2 * D["n_layers"] * kvd
+    return (1 - union_keep) * w_proj / ((1 - r_kv) * batch * kv_per_token) / 1024
+
+
+def batch_gemv_bytes(n_union, d_in, d_out, k, batch):
+    """Algorithmic bytes of one batched GEMV: the union's weight rows once,
+    plus every sequence's input, channel list and output."""
+    return 2 * n_union * d_out + batch * (2 * d_in + 4 * k + 2 * d_out)
+
+
 def crossing_k(contexts, d_vals):
     """Where d = S_proj - S_kv changes sign from + to -: the last context with
     d > 0 and the next one, interpolated linearly (in units of 1024 tokens);
@@ -566,6 +584,67 @@ def time_gemv_kernel(model, which="w_gu", r_p=1.0, reps=3):
     return us, gemv_bytes(d_in, d_out, k, r_p < 1), k
 
 
+def time_batch_gemv(model, batch, r_p=0.5, which="w_gu", reps=3, seed=0):
+    """The gate|up GEMV of `batch` sequences read once for the union of their
+    channel lists (bc_sparse_gemv_batch) against `batch` single-sequence
+    GEMVs, each over the 32 layers' matrices in turn.  Sequence b's input is
+    N(0, 1) with the batch's shared 1% outlier channels x10, and its list is
+    its own top-k (bc_select_channels)."""
+    bc = model.bc
+    from activation_kv_cache_amd import inputs as gen
+    d_in, d_out = model.shapes[which]
+    k = channel_keep(r_p, d_in)
+    pos = gen.outlier_positions(seed, "batchx", d_in)
+    xs = []
+    for b in range(batch):
+        v = gen.rng(seed, f"batchx/{b}").standard_normal(size=d_in, dtype=np.float32)
+        v[pos] *= np.float32(10.0)
+        xs.append(gen.to_bf16_bits(v))
+    x = torch.from_numpy(np.stack(xs).view(np.int16)).cuda()
+    idx = torch.empty((batch, k), dtype=torch.int32, device="cuda")
+    for b in range(batch):
+        bc.bc_select_channels(x[b], k, idx[b])
+    y = torch.empty((batch, d_out), dtype=torch.int16, device="cuda")
+    nu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(bc.bc_sparse_gemv_batch_workspace_bytes(d_in, d_out, k, batch) // 4 + 64, dtype=torch.int32,
+                     device="cuda")
+    ws1 = torch.empty(bc.bc_sparse_gemv_workspace_bytes(d_out, k) // 4 + 64, dtype=torch.int32, device="cuda")
+    bc.bc_workspace_init(ws)
+    bc.bc_workspace_init(ws1)
+
+    # |U| once (its count kernel is not part of the timed GEMV)
+    bc.bc_sparse_gemv_batch(model.layers[0][which], x, idx, k, y, ws, n_union=nu, d_in=d_in, d_out=d_out, tiled=True)
+
+    def batched(ly):
+        bc.bc_sparse_gemv_batch(ly[which], x, idx, k, y, ws, d_in=d_in, d_out=d_out, tiled=True)
+
+    def singles(ly):
+        for b in range(batch):
+            bc.bc_sparse_gemv_tiled(ly[which], d_in, d_out, x[b], idx[b], k, y[b], ws1)
+
+    s = torch.cuda.current_stream()
+    out = {}
+    for label, fn in (("batched", batched), ("singles", singles)):
+        for ly in model.layers[:2]:
+            fn(ly)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            for ly in model.layers:
+                fn(ly)
+        e1.record(s)
+        torch.cuda.synchronize()
+        out[label] = e0.elapsed_time(e1) * 1000.0 / (reps * len(model.layers))
+    n_union = int(nu.item())
+    b = batch_gemv_bytes(n_union, d_in, d_out, k, batch)
+    return {"batch": batch, "k": k, "union": n_union, "union_keep": round(n_union / d_in, 4),
+            "us": round(out["batched"], 2), "bytes": b, "gbs": round(b / out["batched"] / 1e3, 1),
+            "frac": round(b / out["batched"] / 1e3 / HBM_PEAK_GBS, 4), "singles_us": round(out["singles"], 2),
+            "speedup_vs_singles": round(out["singles"] / out["batched"], 3),
+            "crossover_batch_k": {str(r): round(batch_crossover_k(n_union / d_in, r, batch), 2) for r in (0.3, 0.5)}}
+
+
 def load_traffic(n):
     """HBM bytes per launch of the attention kernel from the committed
     rocprofv3 counter summary, or None when the kernel sources changed since
@@ -894,6 +973,14 @@ def main():
                           "read_probe_same_size": gemv_probe},
         "cells": results,
     }
+    # a batch of sequences through one union read of the gate|up weights
+    out["batch_gemv"] = []
+    for nb in (1, 2, 4):
+        r = time_batch_gemv(model, nb)
+        out["batch_gemv"].append(r)
+        log(f"[bench] gate|up GEMV, batch {nb} at r_p 0.5: union keep {r['union_keep']:.3f}, {r['us']:.1f} us "
+            f"({r['gbs']:.0f} GB/s, {100 * r['frac']:.1f}% of 8 TB/s) vs {r['singles_us']:.1f} us as {nb} single "
+            f"GEMVs; batch crossover (r_kv 0.3) {r['crossover_batch_k']['0.3']:.1f}K")
     if args.cells == "default":
         out["kernels"] = kernel_table(model, contexts)
     if sweep:

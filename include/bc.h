@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define BC_ABI_VERSION 2
+#define BC_ABI_VERSION 3
 
 enum {
   BC_OK = 0,
@@ -115,6 +115,32 @@ int bc_sparse_gemv(const uint16_t* wt, int d_in, int d_out, const uint16_t* x, c
  * layout of bc_pack_weight_tiles, the layout bc_decode_layer reads. */
 int bc_sparse_gemv_tiled(const uint16_t* wt_packed, int d_in, int d_out, const uint16_t* x, const int32_t* idx,
                          int k, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/* a2 for a batch (README "Quick start", crossover_batch: a batch reads the
+ * projection weights once for the union of the channels its sequences keep;
+ * the key-value bytes stay per sequence).  Sequence b keeps its own k
+ * channels and gets its own sparse GEMV:
+ *   y[b][o] = sum_{j<k} W^T[idx[b][j]][o] * x[b][idx[b][j]]   (fp32, then bf16)
+ * The matrix rows read are the union U of the batch's channel lists, each
+ * once; |U| / d_in is the union keep of crossover_batch.
+ *   wt     bf16 W^T [d_in][d_out], row-major (tiled = 0) or in the tile-major
+ *          layout of bc_pack_weight_tiles (tiled = 1)
+ *   x      bf16 [batch][d_in]
+ *   idx    int32 [batch][k], each row ascending channel ids, or NULL for the
+ *          dense GEMV of every sequence (k = d_in); ids outside [0, d_in)
+ *          are ignored
+ *   y      bf16 [batch][d_out]
+ *   n_union_out  optional device int32 that receives |U| (NULL: not written)
+ * 1 <= batch <= 4, d_in <= 16384, d_out % 8 == 0.  ws/ws_bytes from
+ * bc_sparse_gemv_batch_workspace_bytes(d_in, d_out, k, batch) (0 for sizes
+ * out of range); it holds per-range row counts and partial sums and is
+ * overwritten.  The order of the sums is fixed (U ascending, in fixed
+ * channel ranges added in range order), so results are deterministic run to
+ * run; they equal bc_sparse_gemv's up to fp32 rounding order. */
+size_t bc_sparse_gemv_batch_workspace_bytes(int d_in, int d_out, int k, int batch);
+int bc_sparse_gemv_batch(const uint16_t* wt, int tiled, int d_in, int d_out, const uint16_t* x, const int32_t* idx,
+                         int k, int batch, uint16_t* y, int32_t* n_union_out, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /* a4. Attention-scored KV selection (README "What it does": sinks, part of
  * the history and the recent entries), scored per 16-token block by an upper

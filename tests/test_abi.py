@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(bc):
 
 
 def test_abi_version(bc):
-    assert bc.bc_abi_version() == 2
+    assert bc.bc_abi_version() == 3
 
 
 @pytest.mark.parametrize("r_p,d", [(0.5, 4096), (0.7, 4096), (0.7, 14336), (0.5, 1408), (1.0, 77), (0.0001, 77),
@@ -79,6 +79,18 @@ def test_host_side_errors(bc):
     assert lib.bc_splitk_attn_partial(1 << 20, 1 << 20, 1 << 20, 64, P, 65, 8, 2, 64, 1, 0.1, 1 << 20, 1 << 20,
                                       1 << 20, P) == bc.BC_ERR_INVALID
     assert lib.bc_splitk_reduce(1 << 20, 1 << 20, 1 << 20, 8, 0, 64, 1 << 20, P) == bc.BC_ERR_INVALID
+    # batched GEMV: NULL, batch outside [1, 4], d_in past the bitmaps, d_out % 8, k, workspace
+    A = 1 << 20
+    assert lib.bc_sparse_gemv_batch(P, 0, 64, 64, A, P, 64, 2, A, P, A, 1 << 30, P) == bc.BC_ERR_INVALID
+    assert lib.bc_sparse_gemv_batch(A, 0, 64, 64, A, P, 64, 0, A, P, A, 1 << 30, P) == bc.BC_ERR_UNSUPPORTED
+    assert lib.bc_sparse_gemv_batch(A, 0, 64, 64, A, P, 64, 5, A, P, A, 1 << 30, P) == bc.BC_ERR_UNSUPPORTED
+    assert lib.bc_sparse_gemv_batch(A, 0, 16385, 64, A, P, 16385, 2, A, P, A, 1 << 30, P) == bc.BC_ERR_UNSUPPORTED
+    assert lib.bc_sparse_gemv_batch(A, 0, 64, 60, A, P, 64, 2, A, P, A, 1 << 30, P) == bc.BC_ERR_UNSUPPORTED
+    assert lib.bc_sparse_gemv_batch(A, 0, 64, 64, A, P, 32, 2, A, P, A, 1 << 30, P) == bc.BC_ERR_INVALID
+    assert lib.bc_sparse_gemv_batch(A, 0, 64, 64, A, A, 65, 2, A, P, A, 1 << 30, P) == bc.BC_ERR_INVALID
+    assert lib.bc_sparse_gemv_batch(A, 0, 64, 64, A, A, 16, 2, A, P, A, 16, P) == bc.BC_ERR_WORKSPACE
+    assert bc.bc_sparse_gemv_batch_workspace_bytes(64, 64, 16, 5) == 0
+    assert bc.bc_sparse_gemv_batch_workspace_bytes(4096, 28672, 2048, 4) > 0
     # the streaming-read probe: NULL, misaligned source, sizes that are not a positive multiple of 4 MiB
     assert lib.bc_stream_read(P, 4 << 20, 1 << 20, P) == bc.BC_ERR_INVALID
     assert lib.bc_stream_read((1 << 20) + 8, 4 << 20, 1 << 20, P) == bc.BC_ERR_INVALID

@@ -146,3 +146,10 @@ def test_window_baseline_bytes_leave_out_scoring():
     D = bench.DIMS
     summaries = 2 * D["n_kv_heads"] * D["head_dim"] * 2 * (n // 16)
     assert scored - window == summaries + 2 * 4 * D["n_kv_heads"] * t
+
+
+@pytest.mark.parametrize("u,r_kv,batch", [(0.92, 0.3, 4), (0.5, 0.3, 1), (0.97, 0.5, 2), (1.0, 0.3, 4)])
+def test_batch_crossover_matches_oracle(u, r_kv, batch):
+    from oracle import byte_account as ba
+    want = ba.crossover_batch(ba.LLAMA_31_8B, union_keep=u, rkv=r_kv, batch=batch) / 1024
+    assert bench.batch_crossover_k(u, r_kv, batch) == pytest.approx(want, rel=1e-12, abs=1e-12)
