@@ -815,6 +815,8 @@ def main():
                     help="largest context of the crossover sweep, in units of 1024 tokens (multiple of 4)")
     ap.add_argument("--gemv-only", default="",
                     help="reps:r_p -- only launch the gate|up GEMV reps times per layer (for counters)")
+    ap.add_argument("--batch-only", type=int, default=0,
+                    help="only the batched gate|up GEMV of this many sequences at r_p 0.5 (for counters)")
     ap.add_argument("--attn-only", type=int, default=0,
                     help="only launch the dense attention kernel this many times per layer (for counters)")
     args = ap.parse_args()
@@ -839,7 +841,7 @@ def main():
     contexts = [int(c) for c in args.contexts.split(",")]
     head_n = max(contexts)
     sweep = (args.cells == "default" and args.crossover_blocks > 0 and head_n >= 131072 and not args.kernels
-             and not args.attn_only and not args.gemv_only)
+             and not args.attn_only and not args.gemv_only and not args.batch_only)
     # the crossover sweep runs past the headline context (to 160K tokens), so
     # that the 0.5/0.5 crossing (n*_ext 118.9K) is bracketed by measured cells
     sweep_ctx = [2048] + [4096 * i for i in range(1, args.crossover_max_k // 4 + 1)] if sweep else []
@@ -855,6 +857,12 @@ def main():
         us, b, k = time_gemv_kernel(model, "w_gu", float(r_p), reps=int(reps))
         log(f"[bench] gate|up GEMV at r_p={r_p}: {us:.1f} us, {b / us / 1e3:.0f} GB/s, k={k}")
         print(json.dumps({"gemv_us": us, "gemv_bytes": b, "k": k}))
+        return
+
+    if args.batch_only:
+        r = time_batch_gemv(model, args.batch_only, reps=1)
+        log(f"[bench] batched gate|up GEMV, batch {args.batch_only}: {r['us']:.1f} us, union keep {r['union_keep']}")
+        print(json.dumps({"batch_gemv": r}))
         return
 
     if args.attn_only:
