@@ -716,7 +716,16 @@ def cpu_baseline(model, n):
         one = time.perf_counter() - t1
     finally:
         oracle.set_num_threads(threads)
-    log(f"[bench] cpu oracle: one layer {elapsed / reps:.2f}s on {threads} threads, {one:.2f}s on one")
+    # the LM head once (final norm + 128256 x 4096 GEMV), for the whole step
+    # extrapolated as 32 x this layer + the LM head
+    w_head = untile(h16(model.w_head), d, D["vocab"])
+    t1 = time.perf_counter()
+    oracle.lm_head(h, h16(model.g_final), w_head)
+    head_s = time.perf_counter() - t1
+    del w_head
+    step_s = D["n_layers"] * elapsed / reps + head_s
+    log(f"[bench] cpu oracle: one layer {elapsed / reps:.2f}s on {threads} threads, {one:.2f}s on one; "
+        f"LM head {head_s:.2f}s; whole step (extrapolated) {step_s:.1f}s")
     cpu_model = ""
     try:
         cpu_model = next(ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name"))
@@ -725,6 +734,9 @@ def cpu_baseline(model, n):
     return {"value": round(sample_bytes * reps / elapsed / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "cpu_model": cpu_model, "layer_s": round(elapsed / reps, 3),
             "single_thread": {"value": round(sample_bytes / one / 1e9, 4), "layer_s": round(one, 3)},
+            "step_extrapolated": {"s": round(step_s, 2), "lm_head_s": round(head_s, 3),
+                                  "gbs": round(step_bytes(n, 1.0, 1.0, n, 32) / step_s / 1e9, 4),
+                                  "how": "32 x the timed layer + the LM head timed once"},
             "sample": f"one of the 32 decoder layers of the dense {n}-token step (weights "
                       f"{layer_bytes(0, 1.0, 1.0, 0, 1) / 1e6:.0f} MB + KV {4096 * n / 1e6:.0f} MB), fp64 oracle, "
                       f"{reps} run(s) in {elapsed:.1f}s; GB/s = that layer's algorithmic bytes / oracle time"}
