@@ -11,8 +11,8 @@
 // channels).  The prologue forms the work-group's share of U itself: it loads
 // the sequences' inputs over its channel range and all list entries, sets a
 // bit per (sequence, kept channel of the range) in LDS, ORs the bits into U,
-// and compacts U's channels (ascending) with their masked inputs
-// xm[j][b] = x_b[U_j] if U_j is in S_b else 0 into LDS.  The row loop then
+// and compacts U's rows (ascending, as element offsets) with their masked
+// inputs x_b[U_j] if U_j is in S_b else 0 (fp32) into LDS.  The row loop then
 // streams U's rows like k_gemv: 64 row slots of 16 lanes, a lane loading 16
 // bytes (8 columns) of a row and updating the B sequences' sums of its 8
 // columns (fp32 multiply-adds).  Chunks are channel ranges, so the launch
@@ -31,6 +31,8 @@ constexpr int kBatchMaxIn = 16384;       // d_in
 constexpr int kBatchRange = 4096;        // input channels per work-group at most
 constexpr int kRangeWords = kBatchRange / 32;
 constexpr int kPerThread = kBatchRange / kGemvThreads;
+constexpr int kRingB = 2;                                  // rows in flight per slot
+constexpr int kBatchPad = kBatchRange + 64 * kRingB;       // U's rows + the ring's overrun
 constexpr int kSlotsB = kGemvThreads / 16;
 constexpr int kNWB = kGemvThreads / kWave;
 
@@ -74,8 +76,8 @@ struct BatchSmem {
   uint32_t umask[kRangeWords];      // U over the range
   uint32_t pre[kRangeWords];        // rows of U before each word
   uint32_t wtot[kNWB];
-  int32_t ch[kBatchRange];          // U's channels, ascending
-  uint2 xm[kBatchRange];            // their masked inputs, four bf16
+  uint32_t off[kBatchPad];          // U's rows (ascending) as element offsets, padding last
+  float4 xf[kBatchPad];             // their masked inputs in fp32 (0 in the padding)
   float red[kNWB][NB][kGemvTile];   // per-wave column sums
 };
 
@@ -152,6 +154,24 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_batch(const BatchParams p
   __syncthreads();
   const int n = int(total);   // rows of U in the range (uniform)
   if (tile == 0 && tid == 0) p.counts[split] = n;
+  const bool col_ok = l16 * 8 < tile_w;
+  const uint16_t* base;
+  uint32_t stride;   // elements; the host keeps every row offset below 2^32
+  if (p.tiled) {
+    base = p.wt + size_t(tile) * kGemvTile * p.d_in + (col_ok ? l16 * 8 : 0);
+    stride = uint32_t(tile_w);
+  } else {
+    base = p.wt + size_t(tile) * kGemvTile + (col_ok ? l16 * 8 : 0);
+    stride = uint32_t(p.d_out);
+  }
+  // the ring reads up to 64 (nsteps + R - 1) positions: the padding past U's
+  // rows re-reads the range's first row with input 0
+  const int nsteps = (n + kSlotsB - 1) / kSlotsB;
+  const int npad = kSlotsB * (nsteps + kRingB - 1);
+  if (tid < npad - n) {
+    sm.off[n + tid] = uint32_t(c0) * stride;
+    sm.xf[n + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const int r = tid + kGemvThreads * i;   // channel c0 + r
@@ -160,11 +180,11 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_batch(const BatchParams p
     const uint32_t u = sm.umask[wd];
     if (!((u >> bit) & 1u)) continue;
     const uint32_t pos = sm.pre[wd] + __popc(u & ((1u << bit) - 1u));
-    uint32_t h[4] = {0u, 0u, 0u, 0u};
+    float h[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int b = 0; b < NB; ++b) h[b] = ((sm.mask[b][wd] >> bit) & 1u) ? xv[b][i] : 0u;
-    sm.ch[pos] = c0 + r;
-    sm.xm[pos] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    for (int b = 0; b < NB; ++b) h[b] = ((sm.mask[b][wd] >> bit) & 1u) ? bf16_to_f32(uint16_t(xv[b][i])) : 0.f;
+    sm.off[pos] = uint32_t(c0 + r) * stride;
+    sm.xf[pos] = make_float4(h[0], h[1], h[2], h[3]);
   }
   __syncthreads();
 
@@ -180,25 +200,15 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_batch(const BatchParams p
     return;
   }
 
-  const bool col_ok = l16 * 8 < tile_w;
-  const uint16_t* base;
-  size_t stride;
-  if (p.tiled) {
-    base = p.wt + size_t(tile) * kGemvTile * p.d_in + (col_ok ? l16 * 8 : 0);
-    stride = size_t(tile_w);
-  } else {
-    base = p.wt + size_t(tile) * kGemvTile + (col_ok ? l16 * 8 : 0);
-    stride = size_t(p.d_out);
-  }
-  // positions past U's rows re-read its last row; their inputs are 0
-  auto row_ptr = [&](int j) -> const uint16_t* { return base + size_t(sm.ch[min(j, n - 1)]) * stride; };
-  auto load = [&](int j) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row_ptr(j))); };
+  auto load = [&](int j) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + sm.off[j]));
+  };
 
   // ------------------------------------------------------------- row loop
   // as k_gemv's: a slot consumes its rows one at a time and refills each
   // right after, R rows ahead (4 rows in flight measured no faster at B = 4;
   // nor did pairing the two rows of a step for v_dot2)
-  constexpr int R = 2;
+  constexpr int R = kRingB;
   u32x4 ring[R];
 #pragma unroll
   for (int u = 0; u < R; ++u) ring[u] = load(slot + kSlotsB * u);
@@ -208,19 +218,16 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_batch(const BatchParams p
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[b][c] = 0.f;
   auto consume = [&](int j, const u32x4& wv) {
-    const uint2 xr = j < n ? sm.xm[j] : make_uint2(0u, 0u);
+    const float4 xr = sm.xf[j];
+    const float xb[4] = {xr.x, xr.y, xr.z, xr.w};
     const float wf[8] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y),
                          bf16_lo(wv.z), bf16_hi(wv.z), bf16_lo(wv.w), bf16_hi(wv.w)};
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const uint32_t pr = b < 2 ? xr.x : xr.y;
-      const float xb = (b & 1) ? bf16_hi(pr) : bf16_lo(pr);
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[b][c] += wf[c] * xb;
-    }
+      for (int c = 0; c < 8; ++c) acc[b][c] += wf[c] * xb[b];
   };
   // every group of R steps but the last refills; the last only consumes
-  const int nsteps = (n + kSlotsB - 1) / kSlotsB;
   int st = 0;
   for (; st + R < nsteps; st += R) {
 #pragma unroll
@@ -315,6 +322,8 @@ extern "C" int bc_sparse_gemv_batch(const uint16_t* wt, int tiled, int d_in, int
   }
   if ((reinterpret_cast<uintptr_t>(wt) | reinterpret_cast<uintptr_t>(ws)) & 15)
     return set_error(BC_ERR_INVALID, "%s: wt and ws must be 16-byte aligned", name);
+  if (!tiled && size_t(d_in) * size_t(d_out) > 0xFFFFFFFFull)
+    return set_error(BC_ERR_UNSUPPORTED, "%s: row-major W^T of %d x %d (use the tiled layout)", name, d_in, d_out);
   const BatchPlan pl = plan_batch(d_in, d_out, batch);
   if (!ws || ws_bytes < pl.bytes)
     return set_error(BC_ERR_WORKSPACE, "%s: workspace %zu < %zu", name, ws_bytes, pl.bytes);
