@@ -584,6 +584,29 @@ def time_gemv_kernel(model, which="w_gu", r_p=1.0, reps=3):
     return us, gemv_bytes(d_in, d_out, k, r_p < 1), k
 
 
+def time_library_gemv(d_in=4096, d_out=28672, count=4, reps=5, seed=0):
+    """The same dense GEMV through torch.matmul in bf16 (the vendor BLAS),
+    over `count` row-major matrices in turn (together beyond the 256 MB
+    MALL): a strength check of the dense baseline.  Returns us per call."""
+    from activation_kv_cache_amd import inputs as gen
+    mats = [gen.device_normal_bf16(seed, f"libgemv{i}", (d_in, d_out), 0.02).view(torch.bfloat16) for i in range(count)]
+    x = gen.device_normal_bf16(seed, "libgemvx", (1, d_in), 1.0).view(torch.bfloat16)
+    for w in mats:
+        torch.matmul(x, w)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        for w in mats:
+            torch.matmul(x, w)
+    e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / (reps * count)
+    del mats
+    return us
+
+
 def time_batch_gemv(model, batch, r_p=0.5, which="w_gu", reps=3, seed=0):
     """The gate|up GEMV of `batch` sequences read once for the union of their
     channel lists (bc_sparse_gemv_batch) against `batch` single-sequence
@@ -951,6 +974,9 @@ def main():
     probe_gbs = probe_b / (probe_us * 1e-6) / 1e9
     log(f"[bench] streaming-read probe {probe_b >> 20} MiB: {probe_us:.1f} us ({probe_gbs:.0f} GB/s); attention at "
         f"{100 * achieved / probe_gbs:.0f}% of it")
+    lib_us = time_library_gemv()
+    log(f"[bench] the dense gate|up GEMV through torch.matmul (vendor BLAS, bf16): {lib_us:.1f} us "
+        f"({gemv_b / lib_us / 1e3:.0f} GB/s); k_gemv {gemv_us:.1f} us")
     # the same probe at the gate|up GEMV's own sizes (224 and 112 MiB, within
     # 0.05% of its dense and r_p 0.5 bytes): a short launch pays its ramp too
     gemv_probe = {}
@@ -990,7 +1016,10 @@ def main():
                                     "frac": round(gemv_b / gemv_us / 1e3 / HBM_PEAK_GBS, 4)},
                           "r_p_0.5": {"us": round(gemv_sp_us, 2), "gbs": round(gemv_sp_b / gemv_sp_us / 1e3, 1),
                                       "frac": round(gemv_sp_b / gemv_sp_us / 1e3 / HBM_PEAK_GBS, 4)},
-                          "read_probe_same_size": gemv_probe},
+                          "read_probe_same_size": gemv_probe,
+                          "vendor_blas_dense": {"us": round(lib_us, 2), "gbs": round(gemv_b / lib_us / 1e3, 1),
+                                                "k_gemv_speedup": round(lib_us / gemv_us, 3),
+                                                "how": "torch.matmul(x[1, 4096], W[4096, 28672]) in bf16"}},
         "cells": results,
     }
     # a batch of sequences through one union read of the gate|up weights
