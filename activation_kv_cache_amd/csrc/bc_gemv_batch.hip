@@ -30,7 +30,9 @@ constexpr int kBatchMax = 4;             // sequences per call (more would spill
 constexpr int kBatchMaxIn = 16384;       // d_in
 constexpr int kBatchRange = 4096;        // input channels per work-group at most
 constexpr int kRangeWords = kBatchRange / 32;
-constexpr int kPerThread = kBatchRange / kGemvThreads;
+constexpr int kPerThread = kBatchRange / kGemvThreads;   // 4: one 8-byte input load per sequence
+static_assert(kPerThread == 4, "the vector input load covers four channels");
+constexpr int kMaskCopies = 4;                             // copies of each bitmap word (atomic collisions)
 constexpr int kRingB = 2;                                  // rows in flight per slot
 constexpr int kBatchPad = kBatchRange + 64 * kRingB;       // U's rows + the ring's overrun
 constexpr int kSlotsB = kGemvThreads / 16;
@@ -72,13 +74,14 @@ BatchPlan plan_batch(int d_in, int d_out, int nb) {
 
 template <int NB>
 struct BatchSmem {
+  alignas(16) uint32_t mask4[NB][kRangeWords * kMaskCopies];   // S_b over the range, four copies per word
   uint32_t mask[NB][kRangeWords];   // S_b over the range
   uint32_t umask[kRangeWords];      // U over the range
   uint32_t pre[kRangeWords];        // rows of U before each word
   uint32_t wtot[kNWB];
   uint32_t off[kBatchPad];          // U's rows (ascending) as element offsets, padding last
   float4 xf[kBatchPad];             // their masked inputs in fp32 (0 in the padding)
-  float red[kNWB][NB][kGemvTile];   // per-wave column sums
+  float red[kNWB][2][NB][kGemvTile];   // per half-wave column sums
 };
 
 template <int NB>
@@ -93,23 +96,33 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_batch(const BatchParams p
   const int tile_w = min(kGemvTile, p.d_out - tile * kGemvTile);
 
   // ------------------------------------------------------------ prologue
-  // the inputs of the range first (channel c0 + tid + 1024 i), then the
-  // list entries; both are in flight while the bitmaps are cleared
+  // the inputs of the range first (thread t owns channels c0 + 4t .. 4t + 3:
+  // one 8-byte load per sequence when the rows allow it), then the list
+  // entries; both are in flight while the bitmaps are cleared
   uint32_t xv[NB][kPerThread];
+  const int cq = c0 + kPerThread * tid;
+  const bool vec = ((p.d_in & 3) == 0) && ((reinterpret_cast<uintptr_t>(p.x) & 7) == 0);
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+  for (int b = 0; b < NB; ++b) {
+    const uint16_t* xr = p.x + size_t(b) * p.d_in;
+    if (vec && cq + kPerThread <= c1) {
+      const uint2 v = *reinterpret_cast<const uint2*>(xr + cq);
+      xv[b][0] = v.x & 0xFFFFu; xv[b][1] = v.x >> 16; xv[b][2] = v.y & 0xFFFFu; xv[b][3] = v.y >> 16;
+    } else {
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int c = c0 + tid + kGemvThreads * i;
-      xv[b][i] = c < c1 ? uint32_t(p.x[size_t(b) * p.d_in + c]) : 0u;
+      for (int i = 0; i < kPerThread; ++i) xv[b][i] = cq + i < c1 ? uint32_t(xr[cq + i]) : 0u;
     }
-  for (int i = tid; i < NB * kRangeWords; i += kGemvThreads) (&sm.mask[0][0])[i] = 0u;
+  }
+  for (int i = tid; i < NB * kRangeWords * kMaskCopies; i += kGemvThreads) (&sm.mask4[0][0])[i] = 0u;
   __syncthreads();
   if (p.idx) {
     // ids outside [0, d_in) are dropped; only the range's ids set bits.
-    // Eight entries per thread are loaded before any is used, so a pass
-    // costs one memory round trip.
+    // Eight entries per thread are loaded before any is used (one memory
+    // round trip per pass).  An ascending list puts about 16 consecutive
+    // entries in one word, so the bits go to four copies of each word (by
+    // lane & 3, adjacent banks) to cut the LDS atomic collisions fourfold.
     const int total_e = NB * p.k;
+    const int cp = tid & (kMaskCopies - 1);
     for (int e0 = 0; e0 < total_e; e0 += 8 * kGemvThreads) {
       int cv[8];
 #pragma unroll
@@ -121,14 +134,15 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_batch(const BatchParams p
       for (int u = 0; u < 8; ++u) {
         const int e = e0 + tid + kGemvThreads * u;
         const int c = cv[u];
-        if (e < total_e && c >= c0 && c < c1) atomicOr(&sm.mask[e / p.k][(c - c0) >> 5], 1u << ((c - c0) & 31));
+        if (e < total_e && c >= c0 && c < c1)
+          atomicOr(&sm.mask4[e / p.k][((c - c0) >> 5) * kMaskCopies + cp], 1u << ((c - c0) & 31));
       }
     }
   } else {
     for (int i = tid; i < NB * nw; i += kGemvThreads) {
       const int b = i / nw, wd = i % nw;
       const int left = c1 - c0 - 32 * wd;
-      sm.mask[b][wd] = left >= 32 ? 0xFFFFFFFFu : ((1u << left) - 1u);
+      sm.mask4[b][wd * kMaskCopies] = left >= 32 ? 0xFFFFFFFFu : ((1u << left) - 1u);
     }
   }
   __syncthreads();
@@ -137,7 +151,12 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_batch(const BatchParams p
   if (tid < nw) {
     uint32_t u = 0;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) u |= sm.mask[b][tid];
+    for (int b = 0; b < NB; ++b) {
+      const uint4 m = *reinterpret_cast<const uint4*>(&sm.mask4[b][tid * kMaskCopies]);
+      const uint32_t mb = (m.x | m.y) | (m.z | m.w);
+      sm.mask[b][tid] = mb;
+      u |= mb;
+    }
     sm.umask[tid] = u;
     cnt = __popc(u);
   }
@@ -174,7 +193,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_batch(const BatchParams p
   }
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
-    const int r = tid + kGemvThreads * i;   // channel c0 + r
+    const int r = kPerThread * tid + i;   // channel c0 + r
     if (c0 + r >= c1) continue;
     const int wd = r >> 5, bit = r & 31;
     const uint32_t u = sm.umask[wd];
@@ -241,19 +260,18 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_batch(const BatchParams p
   for (int u = 0; u < R; ++u) consume(slot + kSlotsB * (st + u), ring[u]);
 
   // ------------------------------------------------------------- epilogue
-  // a wave's four slots summed in registers (lane ^ 32, lane ^ 16), the 16
-  // wave sums through LDS in wave order
+  // slot pairs (lanes l and l ^ 32) summed in registers, then the 32
+  // half-wave sums through LDS in (wave, half) order: a second register step
+  // would cost 8 B more cross-lane swaps per lane than the LDS reads it saves
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      acc[b][c] += lane_xor<32>(acc[b][c]);
-      acc[b][c] += lane_xor<16>(acc[b][c]);
-    }
-  if (lane < 16) {
+    for (int c = 0; c < 8; ++c) acc[b][c] += lane_xor<32>(acc[b][c]);
+  if (lane < 32) {
+    const int half = lane >> 4;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      float4* rw = reinterpret_cast<float4*>(&sm.red[w][b][l16 * 8]);
+      float4* rw = reinterpret_cast<float4*>(&sm.red[w][half][b][l16 * 8]);
       rw[0] = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
       rw[1] = make_float4(acc[b][4], acc[b][5], acc[b][6], acc[b][7]);
     }
@@ -264,7 +282,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_batch(const BatchParams p
     if (c >= tile_w) continue;
     float v = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kNWB; ++ww) v += sm.red[ww][b][c];
+    for (int ww = 0; ww < kNWB; ++ww) v += sm.red[ww][0][b][c] + sm.red[ww][1][b][c];
     store(b, c, v);
   }
 }
