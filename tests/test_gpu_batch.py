@@ -142,3 +142,27 @@ def test_batch_of_one_matches_single_gemv():
     bc.bc_sparse_gemv(dev(wt), dev(x[0]), dev(idx[0]), k, ys, ws)
     torch.cuda.synchronize()
     assert_close_bf16(host_u16(y)[0], oracle.bf16_to_f64(host_u16(ys)), "batch of one vs single GEMV")
+
+
+@pytest.mark.parametrize("d_in,misaligned", [(1001, False), (1024, True)], ids=["d-in-not-multiple-of-4", "x-not-8-byte-aligned"])
+def test_batch_scalar_input_path(d_in, misaligned):
+    """Inputs whose rows are not 8-byte aligned take the element-wise input
+    loads; the result is the same GEMV."""
+    bc = _bc()
+    d_out, batch, k = 256, 3, d_in // 3
+    wt, x, _, _ = _inputs(f"scalar{d_in}", d_in, d_out, batch, 1.0, "random")
+    idx = _lists(10, f"scalar{d_in}", d_in, k, batch, "random")
+    xd = dev(x)
+    if misaligned:   # the same values one bf16 element into a larger buffer
+        buf = torch.zeros(batch * d_in + 1, dtype=torch.int16, device="cuda")
+        buf[1:] = xd.reshape(-1)
+        xd = buf[1:].view(batch, d_in)
+        assert xd.data_ptr() % 8 != 0
+    y = torch.full((batch, d_out), -1, dtype=torch.int16, device="cuda")
+    ws = workspace(bc.bc_sparse_gemv_batch_workspace_bytes(d_in, d_out, k, batch))
+    bc.bc_sparse_gemv_batch(dev(wt), xd, dev(idx), k, y, ws)
+    torch.cuda.synchronize()
+    got = host_u16(y)
+    for b in range(batch):
+        y64, _ = oracle.sparse_gemv(wt, x[b], idx[b])
+        assert_close_bf16(got[b], y64, f"scalar input path, sequence {b}")
