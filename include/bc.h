@@ -131,7 +131,8 @@ int bc_sparse_gemv_tiled(const uint16_t* wt_packed, int d_in, int d_out, const u
  *          are ignored
  *   y      bf16 [batch][d_out]
  *   n_union_out  optional device int32 that receives |U| (NULL: not written)
- * 1 <= batch <= 4, d_in <= 16384, d_out % 8 == 0.  ws/ws_bytes from
+ * 1 <= batch <= 4, d_in <= 16384, d_out % 8 == 0, and for the row-major
+ * layout d_in * d_out < 2^32 (else BC_ERR_UNSUPPORTED).  ws/ws_bytes from
  * bc_sparse_gemv_batch_workspace_bytes(d_in, d_out, k, batch) (0 for sizes
  * out of range); it holds per-range row counts and partial sums and is
  * overwritten.  The order of the sums is fixed (U ascending, in fixed
