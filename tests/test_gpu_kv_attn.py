@@ -56,6 +56,10 @@ KV_CASES = [
     ("tiny-160k-16-keys", gen.TINY, 160000, 160000, 0.3, 4, 128),
     ("8b-192k-16-keys", gen.LLAMA8B, 196608, 196608, 0.3, 4, 1024),
     ("tiny-320k-32-keys", gen.TINY, 320000, 320000, 0.5, 4, 128),
+    # the other GQA group sizes: 1, 2 and 8 query heads per KV head
+    ("g1-d64-0.3", dict(n_heads=2, n_kv_heads=2, head_dim=64), 4096, 4000, 0.3, 4, 128),
+    ("g2-d128-0.3", dict(n_heads=8, n_kv_heads=4, head_dim=128), 4096, 4096, 0.3, 4, 1024),
+    ("g8-d64-0.5", dict(n_heads=16, n_kv_heads=2, head_dim=64), 8192, 8192, 0.5, 4, 128),
     # the KV-window baseline: a window as long as the context leaves no
     # scored blocks, so the list is the sinks and the most recent tokens
     ("tiny-window-0.5", gen.TINY, 2048, 2000, 0.5, 4, 2000),
@@ -150,6 +154,12 @@ ATTN_CASES = [
     ("8b-32k-dense", gen.LLAMA8B, 32768, 32768, 1.0, 0, True),
     ("8b-128k-dense", gen.LLAMA8B, 131072, 131072, 1.0, 0, True),
     ("8b-128k-sel", gen.LLAMA8B, 131072, 131072, 0.3, 0, True),
+    # the other GQA group sizes the kernel is built for (1, 2 and 8 query
+    # heads per KV head), dense and through an index list
+    ("g1-d64-dense", dict(n_heads=4, n_kv_heads=4, head_dim=64), 1024, 1000, 1.0, 8, True),
+    ("g2-d128-sel", dict(n_heads=8, n_kv_heads=4, head_dim=128), 4096, 4096, 0.3, 0, True),
+    ("g8-d128-dense", dict(n_heads=16, n_kv_heads=2, head_dim=128), 2048, 2048, 1.0, 0, True),
+    ("g8-d64-sel", dict(n_heads=16, n_kv_heads=2, head_dim=64), 2048, 2048, 0.3, 8, True),
 ]
 
 
