@@ -124,6 +124,10 @@ LAYER_CASES = [
     # through the same attention kernel
     ("tiny-kv-window", gen.TINY, 2048, 2048, 1.0, 0.3, 4, 2048, 8),
     ("8b-128k-kv-window-0.3", gen.LLAMA8B, 131072, 131072, 1.0, 0.3, 4, 131072, 0),
+    # GQA group sizes 1 and 8 through the whole layer
+    ("tiny-g1-both", dict(gen.TINY, n_kv_heads=8), 2048, 2048, 0.5, 0.3, 4, 128, 8),
+    ("tiny-g8-dense", dict(gen.TINY, n_kv_heads=1), 2048, 2048, 1.0, 1.0, 4, 128, 8),
+    ("tiny-g8-both", dict(gen.TINY, n_kv_heads=1), 2048, 2048, 0.5, 0.3, 4, 128, 8),
 ]
 
 
