@@ -286,7 +286,7 @@ def test_tiled_gemv_equals_plain():
         assert torch.equal(y1, y2)
 
 
-@pytest.mark.parametrize("r_p,r_kv", [(1.0, 1.0), (0.5, 0.3), (0.7, 1.0)])
+@pytest.mark.parametrize("r_p,r_kv", [(1.0, 1.0), (0.5, 0.3), (0.7, 1.0), (1.0, 0.3)])
 def test_decode_step_equals_layer_chain(r_p, r_kv):
     """bc_decode_step (fused across layers) gives the same bits as
     bc_decode_layer per layer followed by bc_lm_head."""
