@@ -237,6 +237,66 @@ def predicted_crossing_k(contexts, t_us, mode_p, mode_k, plan=None):
     return None, 1e-3 / slope, cost[mode_p], cost[mode_k]
 
 
+COMPACT_LIMIT = 4000     # bytes of the last stdout line (the driver keeps only the end of stdout)
+
+
+def _cell_str(c):
+    pol = "" if c["r_kv"] >= 1 else (" win" if c.get("kv_policy") == "window" else " kv")
+    sp = c.get("speedup_vs_dense")
+    return (f"{c['r_p']}/{c['r_kv']}{pol}@{c['context']}: {c['step_us']}us {100 * c['frac_hbm']:.1f}%"
+            + ("" if sp is None else f" {sp}x") + f" L{c['layer_us']}us")
+
+
+def compact_record(out, limit=COMPACT_LIMIT):
+    """The record's headline fields plus one-line summaries of the cells and
+    the crossings, as one JSON object of at most `limit` bytes (the full
+    record is written to a file).  Optional summaries are dropped, largest
+    first, until the line fits."""
+    keep = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+            "vs_baseline", "dtype", "data", "config")
+    c = {k: out[k] for k in keep if k in out}
+    rf = out.get("roofline") or {}
+    c["roofline"] = {k: rf.get(k) for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel",
+                                            "launch_us", "bytes_per_launch")}
+    cb = out.get("cpu_baseline")
+    c["cpu_baseline"] = None if not cb else {k: cb.get(k) for k in ("value", "unit", "cores", "kind", "sample")}
+    opt = {}
+    if out.get("read_probe"):
+        opt["read_probe"] = {k: out["read_probe"].get(k) for k in ("gbs", "frac_of_peak", "attention_frac_of_probe")}
+    if out.get("cells"):
+        opt["cells"] = [_cell_str(x) for x in out["cells"]]
+    if out.get("gemv_roofline"):
+        g = out["gemv_roofline"]
+        opt["gemv_gate_up_frac"] = {k: g[k]["frac"] for k in ("dense", "r_p_0.5") if k in g}
+    for key in ("step_bytes", "masked_baseline", "batch_step", "prediction"):
+        if out.get(key) and isinstance(out[key], dict) and out[key].get("summary") is not None:
+            opt[key] = out[key]["summary"]
+    cr = out.get("crossover")
+    if cr and cr.get("pairs"):
+        # per pair: [measured, interval lo, hi, n*, n*_ext, prediction] in K tokens
+        opt["crossings_k"] = {k: [p.get("measured_k"), p.get("measured_interval", {}).get("lo_k"),
+                                  p.get("measured_interval", {}).get("hi_k"), p.get("n_star_k"),
+                                  p.get("n_star_ext_k"), p.get("pred_k")] for k, p in cr["pairs"].items()}
+        sp = cr.get("speedup", {})
+        ctx = cr.get("contexts", [])
+        if 131072 in ctx:
+            i = ctx.index(131072)
+            opt["speedup_128k"] = {m: v[i] for m, v in sp.items()}
+    if out.get("record_file"):
+        opt["record_file"] = out["record_file"]
+    c.update(opt)
+    drop = ["cells", "speedup_128k", "gemv_gate_up_frac", "read_probe", "batch_step", "masked_baseline",
+            "step_bytes", "prediction", "crossings_k"]
+    line = json.dumps(c, separators=(",", ":"))
+    while len(line.encode()) > limit and drop:
+        c.pop(drop.pop(0), None)
+        line = json.dumps(c, separators=(",", ":"))
+    if len(line.encode()) > limit and c.get("cpu_baseline"):
+        c["cpu_baseline"]["sample"] = c["cpu_baseline"]["sample"][:200]
+        line = json.dumps(c, separators=(",", ":"))
+    return line
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -854,6 +914,9 @@ def main():
                     help="only the batched gate|up GEMV of this many sequences at r_p 0.5 (for counters)")
     ap.add_argument("--attn-only", type=int, default=0,
                     help="only launch the dense attention kernel this many times per layer (for counters)")
+    ap.add_argument("--record", default=os.path.join(ROOT, "gpurun_out", "bench_record.json"),
+                    help="where the full record (cells, kernels, sweep) is written; the last stdout line is a "
+                         "compact summary of it")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -1041,7 +1104,19 @@ def main():
         except Exception as e:  # the GPU figure stands on its own
             log(f"[bench] cpu baseline failed: {e!r}")
             out["cpu_baseline"] = None
-    print(json.dumps(out))
+    emit(out, args.record)
+
+
+def emit(out, path):
+    """Writes the full record to `path` (JSON) and prints the compact record
+    as the last line of stdout."""
+    if path:
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        out["record_file"] = os.path.relpath(os.path.abspath(path), ROOT)
+        with open(path, "w") as fh:
+            json.dump(out, fh)
+        log(f"[bench] full record written to {path}")
+    print(compact_record(out), flush=True)
 
 
 if __name__ == "__main__":

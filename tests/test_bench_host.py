@@ -153,3 +153,72 @@ def test_batch_crossover_matches_oracle(u, r_kv, batch):
     from oracle import byte_account as ba
     want = ba.crossover_batch(ba.LLAMA_31_8B, union_keep=u, rkv=r_kv, batch=batch) / 1024
     assert bench.batch_crossover_k(u, r_kv, batch) == pytest.approx(want, rel=1e-12, abs=1e-12)
+
+
+def synthetic_full_record():
+    """A full record shaped like a default run's: 12 cells, the kernel table,
+    a 41-context sweep of 10 modes with 6 crossing pairs, the cpu baseline."""
+    cells = []
+    for n in (2048, 8192, 32768, 131072):
+        cells.append({"r_p": 1.0, "r_kv": 1.0, "context": n, "kv_policy": "dense", "step_us": 5519.5,
+                      "frac_hbm": 0.7301, "layer_us": 175.12, "speedup_vs_dense": 1.0})
+    for n in (2048, 131072):
+        for r_p, r_kv, pol in ((0.5, 1.0, "dense"), (1.0, 0.3, "scored"), (0.5, 0.3, "scored"),
+                               (1.0, 0.3, "window")):
+            cells.append({"r_p": r_p, "r_kv": r_kv, "context": n, "kv_policy": pol, "step_us": 3973.1,
+                          "frac_hbm": 0.6401, "layer_us": 120.55, "speedup_vs_dense": 1.395})
+    ctx = [2048] + [4096 * i for i in range(1, 41)]
+    pairs = {}
+    for mp, mk, r_p, r_kv in bench.PAIRS:
+        key = f"{r_p}/{r_kv}" + (" sel" if bench.SWEEP_MODES[mk][2] else "")
+        pairs[key] = {"n_star_k": 74.29, "n_star_ext_k": 81.6, "measured_k": 79.01, "pred_k": 81.3,
+                      "measured_interval": {"resamples": 256, "no_crossing": 0, "level": 0.95, "lo_k": 78.71,
+                                            "hi_k": 79.6}}
+    return {
+        "metric": bench.METRIC, "value": 5836.1, "unit": "GB/s", "n_gpus": 1, "steps": 20, "warmup": 5,
+        "ms_per_step": 5.5195, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: random-init N(0,0.02) weights of Llama-3.1-8B shape, N(0,1) pre-filled KV cache",
+        "config": {"workload": "dense decode step of one sequence at Llama-3.1-8B dims: 32 layers + LM head, "
+                               "context 131072, r_p=1, r_kv=1", "context": 131072, "r_p": 1.0, "r_kv": 1.0,
+                   "layers": 32, "batch": 1},
+        "roofline": {"bound": "hbm", "kernel": "k_attn_partial (bc_splitk_attn_partial), dense, one layer",
+                     "achieved": 6301.2, "peak": 8000.0, "unit": "GB/s", "frac": 0.7877,
+                     "traffic": 537803776, "launch_us": 85.29, "bytes_per_launch": 537403392, "splits": 32},
+        "read_probe": {"gbs": 7050.1, "frac_of_peak": 0.8813, "attention_frac_of_probe": 0.9012, "us": 76.1},
+        "gemv_roofline": {"dense": {"frac": 0.8012}, "r_p_0.5": {"frac": 0.7055}},
+        "cells": cells,
+        "kernels": [{"kernel": f"k{i}", "us": 1.0 * i} for i in range(60)],
+        "crossover": {"contexts": ctx, "pairs": pairs,
+                      "speedup": {m: [1.2345] * len(ctx) for m in bench.SWEEP_MODES if m != "dense"},
+                      "step_us": {m: [1234.5] * len(ctx) for m in bench.SWEEP_MODES}},
+        "cpu_baseline": {"value": 1.5612, "unit": "GB/s", "cores": 16, "kind": "oracle", "cpu_model": "x" * 40,
+                         "sample": "one of the 32 decoder layers of the dense 131072-token step (weights 436 MB + "
+                                   "KV 537 MB), fp64 oracle, 16 run(s) in 10.1s; GB/s = that layer's algorithmic "
+                                   "bytes / oracle time"},
+    }
+
+
+def test_compact_record_fits_and_parses():
+    import json
+    full = synthetic_full_record()
+    full_len = len(json.dumps(full))
+    line = bench.compact_record(full)
+    assert len(line.encode()) <= bench.COMPACT_LIMIT < full_len
+    rec = json.loads(line)
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "dtype", "config",
+              "roofline", "cpu_baseline"):
+        assert k in rec, k
+    assert rec["roofline"]["frac"] == 0.7877 and rec["roofline"]["traffic"] == 537803776
+    assert rec["cpu_baseline"]["cores"] == 16 and rec["cpu_baseline"]["kind"] == "oracle"
+    # the default run's summaries fit whole
+    assert len(rec["cells"]) == 12 and len(rec["crossings_k"]) == len(bench.PAIRS)
+    assert "\n" not in line
+
+
+def test_compact_record_drops_summaries_before_the_headline():
+    import json
+    full = synthetic_full_record()
+    full["cells"] = full["cells"] * 20          # far more cells than fit
+    rec = json.loads(bench.compact_record(full))
+    assert "cells" not in rec and rec["roofline"]["frac"] == 0.7877 and "cpu_baseline" in rec
+    assert len(bench.compact_record(full).encode()) <= bench.COMPACT_LIMIT
