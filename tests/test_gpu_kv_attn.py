@@ -292,3 +292,39 @@ def test_stream_read_probe_checksum():
         ref += acc
     assert np.array_equal(got, (ref % (1 << 32)).astype(np.uint32))
 
+
+
+@pytest.mark.parametrize("n,r_kv", [(2048, 0.7), (32768, 0.3), (32768, 0.5), (131072, 0.3), (131072, 0.5)],
+                         ids=["8b-2k-0.7", "8b-32k-0.3", "8b-32k-0.5", "8b-128k-0.3", "8b-128k-0.5"])
+def test_kv_selection_valid_under_plain_scores(n, r_kv):
+    """Order-independent check at Llama-3.1-8B dims: the GPU's kept blocks
+    form a valid top-k of the plain float64 bound sum_j sum_d max(q kmax,
+    q kmin) (numpy, no oracle code), up to swaps within the float32 rounding
+    band of each score; the GPU's float32 scores lie within those bands."""
+    import kv_validity as kvv
+    bc = _bc()
+    H, Hkv, D = 32, 8, 128
+    kc = gen.device_normal_bf16(51, f"validk{n}", (Hkv, n, D), 1.0)
+    summ = torch.zeros((Hkv, n // 16, D, 2), dtype=torch.int16, device="cuda")
+    bc.bc_build_kv_summary(kc, n, summ)
+    q = gen.device_normal_bf16(51, f"validq{n}", (H, D), 1.3)
+    pol = bc.policy(r_kv, 4, 1024)
+    bud = bc.bc_kv_budget(n, pol)
+    assert bud["k_blk"] > 0
+    idx = torch.full((Hkv, bud["t_sel"]), -1, dtype=torch.int32, device="cuda")
+    scores = torch.empty((Hkv, bud["n_cand"]), dtype=torch.float32, device="cuda")
+    ws = workspace(bc.bc_kv_score_select_workspace_bytes(n, Hkv, pol))
+    print(f"[kv-valid] n={n} r_kv={r_kv} k_blk={bud['k_blk']} n_cand={bud['n_cand']}", flush=True)
+    bc.bc_kv_score_select(q, summ, n, H, Hkv, D, pol, idx, scores, ws)
+    torch.cuda.synchronize()
+    s64, band = kvv.plain_scores(host_u16(q), host_u16(summ), bud["n_cand"], bud["b_lo"])
+    s32 = host(scores).astype(np.float64)
+    assert np.all(np.abs(s32 - s64) <= band), "float32 scores outside their rounding bands"
+    ids = host(idx)
+    margins = []
+    for g in range(Hkv):
+        kept = kvv.kept_blocks(ids[g], bud["sinks"], bud["window"], n, bud["b_lo"], bud["n_cand"])
+        ok, margin = kvv.is_valid_topk(s64[g], band[g], kept, bud["k_blk"])
+        margins.append(margin)
+        assert ok, f"head {g}: not a top-{bud['k_blk']} of the plain scores (margin {margin:.3g})"
+    print(f"[kv-valid] margins (>= 0: valid) min {min(margins):.3g}", flush=True)

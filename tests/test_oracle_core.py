@@ -421,3 +421,35 @@ def test_kv_compact_then_dense_attention_equals_list_attention():
     ident = np.tile(np.arange(t_sel, dtype=np.int32), (Hkv, 1))
     Ki, Vi = oracle.kv_compact(K, V, ident, t_sel)
     assert np.array_equal(Ki, K[:, :t_sel]) and np.array_equal(Vi, V[:, :t_sel])
+
+
+@pytest.mark.parametrize("n,r_kv,D,H,Hkv,kstd", [(2048, 0.3, 64, 8, 2, 0.02), (8192, 0.5, 128, 32, 8, 1.0),
+                                                  (40000, 0.3, 64, 8, 2, 1.0), (131072, 0.3, 128, 32, 8, 1.0)])
+def test_kv_select_valid_under_plain_scores(n, r_kv, D, H, Hkv, kstd):
+    """The oracle's selection (scores in the documented float32 order) is a
+    valid top-k of the plain float64 bound sum_j sum_d max(q kmax, q kmin),
+    up to swaps within the float32 rounding band; a selection that swaps
+    one kept block for a clearly lower-scored one fails the same check."""
+    import kv_validity as kvv
+    rng = np.random.default_rng(n)
+    window = 1024 if D == 128 else 128
+    q = gen.to_bf16_bits((rng.standard_normal((H, D)) * 1.3).astype(np.float32))
+    nb = (n + 15) // 16
+    summ = np.zeros((Hkv, nb, D, 2), np.uint16)
+    for g in range(Hkv):
+        keys = gen.to_bf16_bits((rng.standard_normal((n, D)) * kstd).astype(np.float32))
+        summ[g] = oracle.kv_summary(keys, n)
+    bud = oracle.kv_budget(n, r_kv, 4, window)
+    idx, s32 = oracle.kv_select(q, summ, n, H, Hkv, r_kv, 4, window, want_scores=True)
+    s64, band = kvv.plain_scores(q, summ, bud["n_cand"], bud["b_lo"])
+    # the float32 scores lie within their bands of the plain ones
+    assert np.all(np.abs(s32.astype(np.float64) - s64) <= band)
+    for g in range(Hkv):
+        kept = kvv.kept_blocks(idx[g], bud["sinks"], bud["window"], n, bud["b_lo"], bud["n_cand"])
+        ok, margin = kvv.is_valid_topk(s64[g], band[g], kept, bud["k_blk"])
+        assert ok, (g, margin)
+        # negative control: drop the best kept block for the worst dropped one
+        dropped = np.setdiff1d(np.arange(bud["n_cand"]), kept)
+        bad = kept.copy()
+        bad[np.argmax(s64[g][kept])] = dropped[np.argmin(s64[g][dropped])]
+        assert not kvv.is_valid_topk(s64[g], band[g], bad, bud["k_blk"])[0]
