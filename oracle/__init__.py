@@ -15,6 +15,9 @@ Decoding" (ByteCross), GitHub README page.  What each function follows:
     recent entries), scored per 16-token block by a key min/max bound; its
     gather into one contiguous buffer (the sel mode): "Timing and quality on
     a GPU";
+  - the select-once policy in the SnapKV form (FAQ "How is this different
+    from TEAL and SnapKV?"): observation-window attention votes, average
+    pooling, per-head top-k of tokens;
   - split-K attention and its merge: "Overview" (one split-K attention kernel
     for every mode);
   - the layer: the Llama-3.1-8B decoder the README times (RMSNorm, rotary
@@ -74,6 +77,10 @@ def _load():
     lib.orc_kv_select.argtypes = [P, P, I, I, I, I, I, D, I, I, P, P]
     lib.orc_attn_partial.argtypes = [P, P, P, I, P, I, I, I, I, I, D, P, P, P]
     lib.orc_attn_reduce.argtypes = [P, P, P, I, I, I, P, P]
+    lib.orc_snapkv_votes.argtypes = [P, P, I, I, I, I, I, I, D, P]
+    lib.orc_avg_pool.argtypes = [P, I, I, P]
+    lib.orc_token_budget.argtypes = [I, D, I, I, P]
+    lib.orc_token_select.argtypes = [P, I, I, D, I, I, P]
     lib.orc_num_threads.restype = I
     lib.orc_set_num_threads.argtypes = [I]
     _lib = lib
@@ -227,6 +234,62 @@ def kv_compact(K, V, idx, n_cap_out: int):
             Ko[g, t] = K[g, idx[g, t]]
             Vo[g, t] = V[g, idx[g, t]]
     return Ko, Vo
+
+
+# -------------------------------------------- select-once (SnapKV form) policy
+def snapkv_votes(q_obs, K, n: int, n_heads: int, n_kv_heads: int, scale: float | None = None):
+    """Attention votes of the observation queries q_obs [w][H][D] (bf16,
+    positions n-w .. n-1) for every token t < n: [Hkv][n] double."""
+    q_obs = _c(q_obs, np.uint16)
+    K = _c(K, np.uint16)
+    w, H, D = q_obs.shape
+    assert H == n_heads
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = np.empty((n_kv_heads, n), np.float64)
+    _load().orc_snapkv_votes(_p(q_obs), _p(K), int(K.shape[1]), int(n), int(w), int(n_heads), int(n_kv_heads),
+                             int(D), float(scale), _p(out))
+    return out
+
+
+def avg_pool(v, ks: int = 5) -> np.ndarray:
+    """Average pooling of each row over ks neighbouring tokens (zero outside)."""
+    v = _c(v, np.float64)
+    out = np.empty_like(v)
+    rows = v.reshape(-1, v.shape[-1])
+    o = out.reshape(-1, v.shape[-1])
+    for r in range(rows.shape[0]):
+        row = np.ascontiguousarray(rows[r])
+        res = np.empty_like(row)
+        _load().orc_avg_pool(_p(row), row.size, int(ks), _p(res))
+        o[r] = res
+    return out
+
+
+def token_budget(n: int, r_kv: float, sinks: int, window: int) -> dict:
+    out = np.zeros(4, np.int32)
+    _load().orc_token_budget(int(n), float(r_kv), int(sinks), int(window), _p(out))
+    return dict(zip(("T_sel", "k", "sinks", "window"), (int(x) for x in out)))
+
+
+def token_select(scores32, n: int, r_kv: float, sinks: int, window: int) -> np.ndarray:
+    """Per KV head: sinks, the k highest float32 scores among the history
+    candidates (ties: lower token) and the window, ascending [Hkv][T_sel]."""
+    scores32 = _c(scores32, np.float32)
+    Hkv = scores32.shape[0]
+    bud = token_budget(n, r_kv, sinks, window)
+    out = np.empty((Hkv, bud["T_sel"]), np.int32)
+    _load().orc_token_select(_p(scores32), int(n), int(Hkv), float(r_kv), int(sinks), int(window), _p(out))
+    return out
+
+
+def snapkv_select(q_obs, K, n: int, n_heads: int, n_kv_heads: int, r_kv: float, sinks: int, window: int,
+                  ks: int = 5):
+    """The select-once list: votes of the observation window, average-pooled
+    over ks tokens, rounded to float32 (the precision the decision is taken
+    in) and ranked.  Returns (idx [Hkv][T_sel], pooled double [Hkv][n])."""
+    pooled = avg_pool(snapkv_votes(q_obs, K, n, n_heads, n_kv_heads), ks)
+    return token_select(pooled.astype(np.float32), n, r_kv, sinks, window), pooled
 
 
 # --------------------------------------------------------------- attention

@@ -366,6 +366,140 @@ void orc_kv_select(const uint16_t* q, const uint16_t* summ, int nb_cap, int n,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Select-once KV policy in the SnapKV form (README FAQ "How is this different
+ * from TEAL and SnapKV?": the KV branch follows SnapKV, selecting once after
+ * prefill; README "Timing and quality on a GPU" and "API at a glance": the
+ * selection is gathered into one buffer by select_and_compact).  SnapKV
+ * scores every cached token by the attention an observation window of the
+ * last queries pays it, pooled over neighbouring tokens, and keeps the
+ * highest-scored ones.
+ *
+ * Votes.  The observation queries are q_obs[i][j][:], i = 0..w-1 at
+ * position p_i = n - w + i, j = 0..H-1 (post-rotary, bf16).  For KV head g and
+ * its query heads j = g*G .. g*G+G-1:
+ *   z_{i,j,t} = scale * (q_{i,j} . k_t)              for t <= p_i
+ *   A_{i,j,t} = exp(z_{i,j,t} - max_t z) / sum_t exp(z_{i,j,t} - max_t z)
+ *   votes[g][t] = sum_i sum_j A_{i,j,t}   (A = 0 for t > p_i),  t = 0..n-1.
+ * Everything in double; rows are summed i outer, j inner.                   */
+void orc_snapkv_votes(const uint16_t* q_obs, const uint16_t* K, int n_cap, int n, int w, int H, int Hkv,
+                      int D, double scale, double* votes)
+{
+    int G = H / Hkv;
+    int rows = w * G;
+    double* mrow = (double*)malloc(sizeof(double) * (size_t)Hkv * rows);
+    double* lrow = (double*)malloc(sizeof(double) * (size_t)Hkv * rows);
+    /* pass 1: per row, the max and the sum over its causal range */
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int g = 0; g < Hkv; ++g) {
+        for (int r = 0; r < rows; ++r) {
+            int i = r / G, j = g * G + r % G;
+            long p = (long)n - w + i;
+            double qd[512];
+            for (int d = 0; d < D; ++d) qd[d] = orc_bf16_to_double(q_obs[((size_t)i * H + j) * D + d]);
+            double mx = -INFINITY;
+            for (long t = 0; t <= p; ++t) {
+                const uint16_t* kr = K + ((size_t)g * n_cap + t) * D;
+                double acc = 0.0;
+                for (int d = 0; d < D; ++d) acc += qd[d] * orc_bf16_to_double(kr[d]);
+                if (acc * scale > mx) mx = acc * scale;
+            }
+            double sum = 0.0;
+            for (long t = 0; t <= p; ++t) {
+                const uint16_t* kr = K + ((size_t)g * n_cap + t) * D;
+                double acc = 0.0;
+                for (int d = 0; d < D; ++d) acc += qd[d] * orc_bf16_to_double(kr[d]);
+                sum += exp(acc * scale - mx);
+            }
+            mrow[(size_t)g * rows + r] = mx;
+            lrow[(size_t)g * rows + r] = sum;
+        }
+    }
+    /* pass 2: per token, the normalised weights summed over the rows */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int g = 0; g < Hkv; ++g) {
+        for (long t = 0; t < n; ++t) {
+            const uint16_t* kr = K + ((size_t)g * n_cap + t) * D;
+            double v = 0.0;
+            for (int r = 0; r < rows; ++r) {
+                int i = r / G, j = g * G + r % G;
+                if (t > (long)n - w + i) continue;
+                const uint16_t* qr = q_obs + ((size_t)i * H + j) * D;
+                double acc = 0.0;
+                for (int d = 0; d < D; ++d) acc += orc_bf16_to_double(qr[d]) * orc_bf16_to_double(kr[d]);
+                v += exp(acc * scale - mrow[(size_t)g * rows + r]) / lrow[(size_t)g * rows + r];
+            }
+            votes[(size_t)g * n + t] = v;
+        }
+    }
+    free(lrow);
+    free(mrow);
+}
+
+/* Average pooling of one vote vector over neighbouring tokens (SnapKV's
+ * clustering step): out_t = (1/ks) * sum_{u = t-ks/2}^{t+ks/2} v_u, with
+ * v_u = 0 outside [0, n); ks odd.  Summed in u order, in double.           */
+void orc_avg_pool(const double* v, int n, int ks, double* out)
+{
+    int r = ks / 2;
+    for (int t = 0; t < n; ++t) {
+        double acc = 0.0;
+        for (int u = t - r; u <= t + r; ++u)
+            if (u >= 0 && u < n) acc += v[u];
+        out[t] = acc / (double)ks;
+    }
+}
+
+/* Token budget of the select-once policy: T = min(n, floor(r_kv*n + 1/2));
+ * sinks S' = min(sinks, T); window W' = min(window, T - S'); the history
+ * candidates are tokens [S', n - W'), of which k = T - S' - W' are kept, so
+ * T_sel = T.  r_kv >= 1 keeps all n.  out[0]=T_sel out[1]=k out[2]=S'
+ * out[3]=W'.                                                                 */
+void orc_token_budget(int n, double r_kv, int sinks, int window, int* out)
+{
+    if (r_kv >= 1.0) { out[0] = n; out[1] = 0; out[2] = 0; out[3] = 0; return; }
+    long T = (long)floor(r_kv * (double)n + 0.5);
+    if (T > n) T = n;
+    if (T < 0) T = 0;
+    int sp = sinks < T ? sinks : (int)T;
+    int wp = window < (int)T - sp ? window : (int)T - sp;
+    out[0] = (int)T;
+    out[1] = (int)T - sp - wp;
+    out[2] = sp;
+    out[3] = wp;
+}
+
+static uint32_t orc_float_order_key(float f);
+
+/* Token selection from given float scores [Hkv][n] (one list per KV head):
+ * the k highest-scored candidates of [S', n - W') (equal scores: lower token
+ * first), with the sinks and the window, ascending: idx_out [Hkv][T_sel].
+ * The decision is taken on the float values as given.                      */
+void orc_token_select(const float* scores, int n, int Hkv, double r_kv, int sinks, int window, int32_t* idx_out)
+{
+    int bud[4];
+    orc_token_budget(n, r_kv, sinks, window, bud);
+    int T_sel = bud[0], k = bud[1], sp = bud[2], wp = bud[3];
+    int nc = n - wp - sp;
+    for (int g = 0; g < Hkv; ++g) {
+        int32_t* out = idx_out + (size_t)g * T_sel;
+        if (r_kv >= 1.0) {
+            for (int t = 0; t < n; ++t) out[t] = t;
+            continue;
+        }
+        uint32_t* keys = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)(nc > 0 ? nc : 1));
+        int32_t* chosen = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
+        for (int c = 0; c < nc; ++c) keys[c] = orc_float_order_key(scores[(size_t)g * n + sp + c]);
+        orc_topk_positions(keys, nc, k, chosen);
+        int w = 0;
+        for (int t = 0; t < sp; ++t) out[w++] = t;
+        for (int c = 0; c < k; ++c) out[w++] = sp + chosen[c];
+        for (int t = n - wp; t < n; ++t) out[w++] = t;
+        free(chosen);
+        free(keys);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Split-K decode attention, partial pass (README "Overview": one split-K
  * attention kernel reads the cache in every mode).  For query head j (KV
  * head g = j / G) and split s covering list positions [s*c, min(n_sel,

@@ -1,0 +1,168 @@
+"""Pins of the oracle's select-once policy in the SnapKV form (README FAQ
+"How is this different from TEAL and SnapKV?": the KV branch follows SnapKV
+with one selection after prefill): attention votes of an observation window
+of queries, average pooling over neighbouring tokens, per-KV-head top-k.
+
+The pins check the oracle against what the definition fixes without
+retyping it: every softmax row sums to one, a single query's votes are the
+weights of the attention oracle (itself pinned against numpy softmax),
+causality inside the observation window, the closed form for zero queries,
+pooling of a spike and of a constant, budget and list invariants, a brute
+force ranking of given scores, a planted cluster, and the group sum."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from activation_kv_cache_amd import inputs as gen
+
+
+def _inputs(seed, w, H, Hkv, D, n, qstd=1.0, kstd=1.0):
+    q = gen.normal_bf16(seed, "snap/q", (w, H, D), qstd)
+    K = gen.normal_bf16(seed, "snap/k", (Hkv, n, D), kstd)
+    return q, K
+
+
+@pytest.mark.parametrize("w,H,Hkv,D,n", [(8, 8, 2, 64, 300), (32, 4, 1, 128, 200), (1, 2, 2, 64, 50)])
+def test_votes_sum_to_the_number_of_rows(w, H, Hkv, D, n):
+    q, K = _inputs(1, w, H, Hkv, D, n)
+    v = oracle.snapkv_votes(q, K, n, H, Hkv)
+    assert v.shape == (Hkv, n) and np.all(v >= 0)
+    assert np.allclose(v.sum(axis=1), w * (H // Hkv), rtol=1e-12, atol=1e-12)
+
+
+def test_single_query_votes_are_the_attention_weights():
+    """One observation query per head at position n-1 (it sees every token):
+    sum_t votes_t v_t equals the attention oracle's output for that query."""
+    H = Hkv = 2
+    D, n = 64, 257
+    q, K = _inputs(2, 1, H, Hkv, D, n, qstd=2.0)
+    V = gen.normal_bf16(2, "snap/v", (Hkv, n, D))
+    votes = oracle.snapkv_votes(q, K, n, H, Hkv)
+    m, l, o = oracle.attn_partial(q[0], K, V, None, n, H, Hkv, 1)
+    out64, _ = oracle.attn_reduce(m, l, o)
+    Vf = oracle.bf16_to_f64(V)
+    for g in range(Hkv):
+        assert np.allclose(votes[g] @ Vf[g], out64[g], rtol=1e-10, atol=1e-12)
+
+
+def test_causality_inside_the_observation_window():
+    """A key that every observation query favours (all queries share one
+    direction), planted at the last position, is seen only by the last
+    observation query; planted at the first observation position it is seen
+    by all of them."""
+    w, H, Hkv, D, n = 8, 4, 1, 64, 100
+    rng = np.random.default_rng(3)
+    base = rng.standard_normal(D)
+    q = gen.to_bf16_bits((base[None, None, :] + 0.1 * rng.standard_normal((w, H, D))).astype(np.float32))
+    K = gen.normal_bf16(3, "snap/kc", (Hkv, n, D), 0.3)
+    big = oracle.f64_to_bf16(50.0 * base / np.linalg.norm(base))
+    for t, seen_by in ((n - 1, 1), (n - w, w)):
+        K2 = K.copy()
+        K2[0, t] = big
+        v = oracle.snapkv_votes(q, K2, n, H, Hkv)
+        assert abs(v[0, t] - H * seen_by) < 1e-3, (t, v[0, t])
+
+
+@pytest.mark.parametrize("w,n", [(4, 20), (32, 100)])
+def test_zero_queries_closed_form(w, n):
+    """q = 0: every token in a query's causal range gets weight 1/(p+1), so
+    votes_t = G * sum over the observation positions p >= t of 1/(p+1)."""
+    H, Hkv, D = 4, 2, 64
+    q = np.zeros((w, H, D), np.uint16)
+    K = gen.normal_bf16(4, "snap/k0", (Hkv, n, D))
+    v = oracle.snapkv_votes(q, K, n, H, Hkv)
+    ps = np.arange(n - w, n)
+    want = np.array([sum(1.0 / (p + 1) for p in ps if p >= t) for t in range(n)]) * (H // Hkv)
+    assert np.allclose(v, want[None, :], rtol=1e-13, atol=1e-15)
+
+
+def test_avg_pool_spike_and_constant():
+    n, ks = 40, 5
+    spike = np.zeros(n)
+    spike[17] = 5.0
+    out = oracle.avg_pool(spike, ks)
+    assert np.allclose(out[15:20], 1.0) and np.allclose(np.delete(out, range(15, 20)), 0.0)
+    ones = oracle.avg_pool(np.ones(n), ks)
+    assert np.allclose(ones[2:-2], 1.0) and np.allclose(ones[[0, 1, -2, -1]], [0.6, 0.8, 0.8, 0.6])
+    # an edge spike: the pads are zeros, the window still divides by ks
+    e = np.zeros(n)
+    e[0] = 1.0
+    assert np.allclose(oracle.avg_pool(e, ks)[:4], [0.2, 0.2, 0.2, 0.0])
+
+
+@pytest.mark.parametrize("n,r_kv,sinks,window", [(2048, 0.3, 4, 128), (131072, 0.3, 4, 1024),
+                                                 (2048, 0.3, 4, 1024), (10, 0.5, 4, 16), (1, 0.3, 4, 16),
+                                                 (1000, 1.0, 4, 64)])
+def test_token_budget(n, r_kv, sinks, window):
+    b = oracle.token_budget(n, r_kv, sinks, window)
+    if r_kv >= 1:
+        assert b["T_sel"] == n
+        return
+    T = min(n, int(math.floor(r_kv * n + 0.5)))
+    s = min(sinks, T)
+    wn = min(window, T - s)
+    assert (b["T_sel"], b["sinks"], b["window"], b["k"]) == (T, s, wn, T - s - wn)
+    assert b["k"] <= n - wn - s
+
+
+def _brute_token_select(scores32, n, r_kv, sinks, window):
+    b = oracle.token_budget(n, r_kv, sinks, window)
+    lo, hi = b["sinks"], n - b["window"]
+    out = []
+    for g in range(scores32.shape[0]):
+        cand = list(range(lo, hi))
+        cand.sort(key=lambda t: (-float(scores32[g, t]), t))
+        keep = sorted(cand[:b["k"]])
+        out.append(list(range(b["sinks"])) + keep + list(range(n - b["window"], n)))
+    return np.array(out, np.int32)
+
+
+@pytest.mark.parametrize("n,r_kv,window,levels", [(300, 0.3, 16, 0), (300, 0.5, 64, 7), (64, 0.4, 8, 3),
+                                                  (20, 0.3, 16, 0)])
+def test_token_select_brute_force(n, r_kv, window, levels):
+    """Ranking of given float scores against a plain sort (largest first,
+    lower token on ties); with few distinct levels most ranks are ties."""
+    rng = np.random.default_rng(n + levels)
+    s = rng.standard_normal((3, n)).astype(np.float32)
+    if levels:
+        s = np.round(s * levels).astype(np.float32)
+    idx = oracle.token_select(s, n, r_kv, 4, window)
+    assert np.array_equal(idx, _brute_token_select(s, n, r_kv, 4, window))
+    for row in idx:
+        assert np.all(np.diff(row) > 0)
+    assert np.array_equal(oracle.token_select(s, n, 1.0, 4, window), np.tile(np.arange(n, dtype=np.int32), (3, 1)))
+
+
+def test_planted_cluster_is_selected():
+    """Four history tokens whose keys every observation query favours are
+    kept, together with the neighbours whose pooling window reaches them
+    (two on each side), at a budget of 12 history tokens."""
+    w, H, Hkv, D, n = 8, 8, 2, 64, 400
+    q, K = _inputs(5, w, H, Hkv, D, n, qstd=0.5, kstd=0.5)
+    qf = oracle.bf16_to_f64(q)
+    for g in range(Hkv):
+        direction = qf[:, g * 4:(g + 1) * 4].reshape(-1, D).sum(0)
+        K[g, 200:204] = oracle.f64_to_bf16(np.tile(8.0 * direction / np.linalg.norm(direction), (4, 1)))
+    r_kv = (4 + 16 + 12) / n
+    idx, pooled = oracle.snapkv_select(q, K, n, H, Hkv, r_kv, 4, 16)
+    assert oracle.token_budget(n, r_kv, 4, 16)["k"] == 12
+    for g in range(Hkv):
+        hist = set(idx[g, 4:16].tolist())
+        assert set(range(198, 206)) <= hist, sorted(hist)
+        # the pooled scores of those eight are the largest of all candidates
+        cand = pooled[g, 4:n - 16]
+        assert cand[198 - 4:206 - 4].min() > np.delete(cand, range(198 - 4, 206 - 4)).max()
+
+
+def test_group_sum_of_identical_heads():
+    """With the same queries in every head of a group, the group's votes are
+    G times those of one head."""
+    w, D, n = 4, 64, 120
+    q1 = gen.normal_bf16(6, "snap/q1", (w, 1, D))
+    K = gen.normal_bf16(6, "snap/k1", (1, n, D))
+    v1 = oracle.snapkv_votes(q1, K, n, 1, 1)
+    q4 = np.repeat(q1, 4, axis=1)
+    v4 = oracle.snapkv_votes(q4, K, n, 4, 1)
+    assert np.allclose(v4, 4 * v1, rtol=1e-13)
