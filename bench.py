@@ -836,32 +836,69 @@ PAIRS = (("proj0.7", "kv0.3", 0.7, 0.3), ("proj0.5", "kv0.3", 0.5, 0.3), ("proj0
          ("proj0.7", "sel0.3", 0.7, 0.3), ("proj0.5", "sel0.3", 0.5, 0.3), ("proj0.5", "sel0.5", 0.5, 0.5))
 
 
-def crossover_sweep(model, contexts, blocks, steps, warmup, seed=0):
+CALIB_CONTEXTS = [2048, 16384, 32768, 65536, 98304, 131072, 163840]
+CALIB_MODES = ("dense", "proj0.7", "proj0.5", "kv0.3", "kv0.5", "sel0.3", "sel0.5")
+
+
+def time_cells(model, cells, steps, warmup, rng):
+    """Step time (us) of every (mode, context) cell, in a shuffled order."""
+    out = {}
+    for ci in rng.permutation(len(cells)):
+        m, n = cells[ci]
+        r_p, r_kv, once = SWEEP_MODES[m]
+        g = model.graph_sel(n, r_p, r_kv) if once else model.graph(n, r_p, r_kv)
+        out[(m, n)] = time_graph(g, steps, warmup) * 1000.0
+        del g
+    return out
+
+
+def calibration_sweep(model, blocks, steps, warmup, seed=1, contexts=None):
+    """The branches' own sweeps for the cost-aware prediction (README
+    "Results", paper Table 2: the kernel cost of each branch taken from
+    separate sweeps): dense and every single-branch mode at a few contexts,
+    in blocks of their own, timed before and apart from the crossover
+    blocks whose crossings the prediction is compared with.  Returns the
+    mean step time per mode over the blocks, [contexts]."""
+    contexts = contexts or [n for n in CALIB_CONTEXTS if n <= model.max_ctx]
+    rng = np.random.default_rng(seed)
+    cells = [(m, n) for m in CALIB_MODES for n in contexts]
+    t = {m: np.zeros((blocks, len(contexts))) for m in CALIB_MODES}
+    for b in range(blocks):
+        got = time_cells(model, cells, steps, warmup, rng)
+        for (m, n), us in got.items():
+            t[m][b, contexts.index(n)] = us
+    log(f"[bench] calibration sweep: {len(cells)} cells x {blocks} blocks")
+    return contexts, {m: t[m].mean(axis=0) for m in CALIB_MODES}
+
+
+def crossover_sweep(model, contexts, blocks, steps, warmup, seed=0, calib=None):
     """Every mode at every context, `blocks` times in a shuffled order; the
     speedups S = t_dense / t_mode are paired within a block (README
     "Reproduce the paper": paired blocks), averaged over blocks, and each (r_p, r_kv)
-    pair's crossing of S_proj and S_kv is compared with the byte-account n*."""
+    pair's crossing of S_proj and S_kv is compared with the byte-account n*
+    and with the cost-aware prediction fitted on the separate calibration
+    sweep `calib` = (contexts, mean step times per mode)."""
     rng = np.random.default_rng(seed)
     cells = [(m, n) for m in SWEEP_MODES for n in contexts]
     t = {m: np.zeros((blocks, len(contexts))) for m in SWEEP_MODES}
     for b in range(blocks):
         tb = time.time()
-        order = rng.permutation(len(cells))
-        for ci in order:
-            m, n = cells[ci]
-            r_p, r_kv, once = SWEEP_MODES[m]
-            g = model.graph_sel(n, r_p, r_kv) if once else model.graph(n, r_p, r_kv)
-            t[m][b, contexts.index(n)] = time_graph(g, steps, warmup) * 1000.0
-            del g
+        got = time_cells(model, cells, steps, warmup, rng)
+        for (m, n), us in got.items():
+            t[m][b, contexts.index(n)] = us
         log(f"[bench] crossover block {b + 1}/{blocks} done in {time.time() - tb:.0f}s")
     sp = {m: (t["dense"] / t[m]).mean(axis=0) for m in SWEEP_MODES}
     out = {"contexts": contexts, "blocks": blocks, "steps": steps,
            "step_us": {m: [round(x, 1) for x in t[m].mean(axis=0)] for m in SWEEP_MODES},
            "speedup": {m: [round(x, 4) for x in sp[m]] for m in SWEEP_MODES if m != "dense"}, "pairs": {}}
+    if calib:
+        out["calibration"] = {"contexts": calib[0], "step_us": {m: [round(x, 1) for x in v]
+                                                                  for m, v in calib[1].items()}}
     keys = [(f"{r_p}/{r_kv}" + (" sel" if SWEEP_MODES[mk][2] else ""), mp, mk) for mp, mk, r_p, r_kv in PAIRS]
     sp_iv, cross_iv = resample_intervals(t, contexts, keys)
     out["speedup_interval"] = sp_iv
     out["resamples"] = int(blocks ** blocks)
+    plan = lambda n, a, b: model.plan(n, a, b)[1:]   # noqa: E731
     for mp, mk, r_p, r_kv in PAIRS:
         once = SWEEP_MODES[mk][2]
         d_vals = [float(x) for x in (t["dense"] / t[mp] - t["dense"] / t[mk]).mean(axis=0)]
@@ -869,26 +906,107 @@ def crossover_sweep(model, contexts, blocks, steps, warmup, seed=0):
         # the sel branch moves exactly Eq. 5's bytes; the kv branch also reads
         # the summaries it rescores every step (n*_ext)
         ns, nx = n_star_k(r_p, r_kv), n_star_k(r_p, r_kv, ext=not once)
-        mean_t = {m: t[m].mean(axis=0) for m in ("dense", mp, mk)}
-        pred, bw, cp, ck = predicted_crossing_k(contexts, mean_t, mp, mk,
-                                                plan=lambda n, a, b: model.plan(n, a, b)[1:])
         key = f"{r_p}/{r_kv}" + (" sel" if once else "")
-        out["pairs"][key] = {
-            "kv_policy": "select once, gathered" if once else "rescored every step",
-            "n_star_k": round(ns, 2), "n_star_ext_k": round(nx, 2),
-            "measured_k": None if c is None else round(c, 2),
-            "measured_minus_n_star_k": None if c is None else round(c - ns, 2),
-            "measured_minus_n_star_ext_k": None if c is None else round(c - nx, 2),
-            "pred_k": None if pred is None else round(pred, 2),
-            "measured_minus_pred_k": None if (c is None or pred is None) else round(c - pred, 2),
-            "pred_fit": {"bw_gbs": round(bw, 1), "cost_proj_us": round(cp, 1), "cost_kv_us": round(ck, 1)},
-            "measured_interval": cross_iv[key]}
+        rec = {"kv_policy": "select once, gathered" if once else "rescored every step",
+               "n_star_k": round(ns, 2), "n_star_ext_k": round(nx, 2),
+               "measured_k": None if c is None else round(c, 2),
+               "measured_minus_n_star_k": None if c is None else round(c - ns, 2),
+               "measured_minus_n_star_ext_k": None if c is None else round(c - nx, 2),
+               "measured_interval": cross_iv[key]}
+        # in-sample: costs fitted on the very sweep whose crossing is measured
+        mean_t = {m: t[m].mean(axis=0) for m in ("dense", mp, mk)}
+        pin, bw, cp, ck = predicted_crossing_k(contexts, mean_t, mp, mk, plan=plan)
+        rec["pred_in_sample_k"] = None if pin is None else round(pin, 2)
+        rec["pred_in_sample_fit"] = {"bw_gbs": round(bw, 1), "cost_proj_us": round(cp, 1), "cost_kv_us": round(ck, 1)}
+        pred = None
+        if calib:
+            cctx, ct = calib
+            pred, bw, cp, ck = predicted_crossing_k(cctx, ct, mp, mk, plan=plan)
+            rec["pred_fit"] = {"bw_gbs": round(bw, 1), "cost_proj_us": round(cp, 1), "cost_kv_us": round(ck, 1),
+                               "from": "separate calibration sweep"}
+        rec["pred_k"] = None if pred is None else round(pred, 2)
+        rec["measured_minus_pred_k"] = None if (c is None or pred is None) else round(c - pred, 2)
+        out["pairs"][key] = rec
         iv = cross_iv[key]
         iv_s = f"[{iv['lo_k']:.1f}, {iv['hi_k']:.1f}]K" if "lo_k" in iv else "none"
         log(f"[bench] crossing {key}: measured {c if c is None else round(c, 1)}K "
             f"(95% over {iv['resamples']} block resamples {iv_s}), n* {ns:.1f}K, "
-            f"n*_ext {nx:.1f}K, cost-aware prediction {pred if pred is None else round(pred, 1)}K")
+            f"n*_ext {nx:.1f}K, cost-aware prediction (separate sweep) "
+            f"{pred if pred is None else round(pred, 1)}K, in-sample {pin if pin is None else round(pin, 1)}K")
     return out
+
+
+def _read_counters(path):
+    """(dispatch id, kernel name, counter value) rows of a rocprofv3
+    counter-collection CSV."""
+    import csv
+    rows = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            did = r.get("Dispatch_Id") or r.get("Dispatch_ID") or r.get("dispatch_id")
+            name = r.get("Kernel_Name") or r.get("Kernel-Name") or r.get("kernel_name") or ""
+            val = r.get("Counter_Value") or r.get("counter_value")
+            if did is None or val is None:
+                continue
+            rows.append((int(did), name, float(val)))
+    return rows
+
+
+def step_pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, specs, copy_bytes):
+    """HBM bytes of one decode step per mode, from two counter runs of
+    --step-pmc (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled
+    by what the same counter reads for a plain copy of copy_bytes bytes.
+    The dispatches between a mode's marker launch (k_stream_read) and the
+    next marker are that mode's REPS steps.  Each step is compared with its
+    algorithmic bytes (step_bytes) and with the README's byte account
+    r_p W_proj + W_head + (kept tokens) x KV bytes per token (README
+    "Overview"; "Usage", the byte account).  Returns one record per mode."""
+    specs = [(m, int(n), int(r)) for m, n, r in (x.split(":") for x in specs.split("+"))]
+    copy_bytes = int(copy_bytes)
+    cf = sum(v for _, _, v in _read_counters(cfetch_csv)) * 1024 / copy_bytes
+    cw = sum(v for _, _, v in _read_counters(cwrite_csv)) * 1024 / copy_bytes
+
+    def segments(path, factor):
+        rows = sorted(_read_counters(path))
+        marks = [d for d, k, _ in rows if "k_stream_read" in k]
+        assert len(marks) == len(specs), f"{path}: {len(marks)} markers for {len(specs)} modes"
+        out = []
+        for i, (mode, n, reps) in enumerate(specs):
+            lo, hi = marks[i], marks[i + 1] if i + 1 < len(marks) else float("inf")
+            tot, by = 0.0, {}
+            for d, k, v in rows:
+                if lo < d < hi:
+                    b = v * 1024 / factor / reps
+                    tot += b
+                    key = k.split("(")[0][:48]
+                    by[key] = by.get(key, 0.0) + b
+            out.append((tot, by))
+        return out
+
+    fseg = segments(fetch_csv, cf)
+    wseg = segments(write_csv, cw)
+    D = DIMS
+    kvd = D["n_kv_heads"] * D["head_dim"]
+    w_proj = 2 * D["n_layers"] * (2 * D["d"] ** 2 + 2 * D["d"] * kvd + 3 * D["d"] * D["d_ff"])
+    w_head = 2 * D["vocab"] * D["d"]
+    kv_tok = 2 * 2 * D["n_layers"] * kvd
+    recs = []
+    for (mode, n, reps), (fetch, fby), (write, wby) in zip(specs, fseg, wseg):
+        r_p, r_kv, once = SWEEP_MODES[mode]
+        t_sel, S = kv_plan(n, r_kv)
+        algo = step_bytes(t_sel, r_p, 1.0, *kv_plan(t_sel, 1.0)) if once else step_bytes(n, r_p, r_kv, t_sel, S)
+        kept = t_sel if r_kv < 1 else n
+        account = r_p * w_proj + w_head + kept * kv_tok
+        meas = fetch + write
+        recs.append({"mode": mode, "context": n, "reps": reps, "t_sel": kept,
+                     "fetch_bytes": round(fetch), "write_bytes": round(write), "measured_bytes": round(meas),
+                     "algorithmic_bytes": algo, "page_account_bytes": round(account),
+                     "measured_over_algorithmic": round(meas / algo, 4),
+                     "measured_over_page_account": round(meas / account, 4),
+                     "copy_factors": {"fetch": round(cf, 6), "write": round(cw, 6)},
+                     "fetch_by_kernel": {k: round(v) for k, v in sorted(fby.items(), key=lambda x: -x[1])},
+                     "write_by_kernel": {k: round(v) for k, v in sorted(wby.items(), key=lambda x: -x[1])}})
+    return recs
 
 
 def main():
@@ -906,6 +1024,8 @@ def main():
     ap.add_argument("--crossover-blocks", type=int, default=4,
                     help="blocks of the crossover sweep (every mode at 2K, 4K, ..., 128K); 0 skips it")
     ap.add_argument("--crossover-steps", type=int, default=10, help="timed steps per sweep cell")
+    ap.add_argument("--calib-blocks", type=int, default=2,
+                    help="blocks of the separate calibration sweep the cost-aware prediction is fitted on")
     ap.add_argument("--crossover-max-k", type=int, default=160,
                     help="largest context of the crossover sweep, in units of 1024 tokens (multiple of 4)")
     ap.add_argument("--gemv-only", default="",
@@ -914,10 +1034,23 @@ def main():
                     help="only the batched gate|up GEMV of this many sequences at r_p 0.5 (for counters)")
     ap.add_argument("--attn-only", type=int, default=0,
                     help="only launch the dense attention kernel this many times per layer (for counters)")
+    ap.add_argument("--step-pmc", default="",
+                    help="MODE:N:REPS[+MODE:N:REPS...] -- only REPS steps of each sweep mode at context N, each "
+                         "mode's steps after one marker launch (bc_stream_read of 4 MiB), for whole-step counters "
+                         "and kernel traces")
+    ap.add_argument("--eager", action="store_true", help="with --step-pmc: eager steps instead of graph replays")
+    ap.add_argument("--pmc-summary", default="",
+                    help="FETCH_CSV,WRITE_CSV,CFETCH_CSV,CWRITE_CSV,SPECS,COPY_BYTES -- SPECS as for --step-pmc: "
+                         "sum the counters of each mode's steps (between its marker and the next) and print each "
+                         "step's HBM bytes against its byte account")
     ap.add_argument("--record", default=os.path.join(ROOT, "gpurun_out", "bench_record.json"),
                     help="where the full record (cells, kernels, sweep) is written; the last stdout line is a "
                          "compact summary of it")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        print(json.dumps(step_pmc_summary(*args.pmc_summary.split(","))))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (no sharding or collectives); "
@@ -934,6 +1067,29 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes": src.numel() * 4}))
+        return
+
+    if args.step_pmc:
+        specs = [(m, int(n), int(r)) for m, n, r in (x.split(":") for x in args.step_pmc.split("+"))]
+        model = Model(max_ctx=max(n for _, n, _ in specs))
+        sink = torch.empty(256, dtype=torch.int32, device="cuda")
+        marker = torch.ones(1 << 20, dtype=torch.int32, device="cuda")
+        for mode, n, reps in specs:
+            r_p, r_kv, once = SWEEP_MODES[mode]
+            t_sel = model.sel_prepare(n, r_kv) if once else None
+            if args.eager:
+                run = (lambda: model.step_sel(t_sel, r_p)) if once else (lambda: model.step(n, r_p, r_kv))
+                run()
+            else:
+                g = model.graph_sel(n, r_p, r_kv) if once else model.graph(n, r_p, r_kv)
+                run = g.replay
+            torch.cuda.synchronize()
+            model.bc.bc_stream_read(marker, sink)       # marks where this mode's steps begin
+            for _ in range(reps):
+                run()
+            torch.cuda.synchronize()
+            log(f"[bench] steps only: {mode} at {n}: {reps} steps ({'eager' if args.eager else 'graph'})")
+        print(json.dumps({"step_pmc": args.step_pmc}))
         return
 
     contexts = [int(c) for c in args.contexts.split(",")]
@@ -1096,8 +1252,9 @@ def main():
     if args.cells == "default":
         out["kernels"] = kernel_table(model, contexts)
     if sweep:
+        calib = calibration_sweep(model, args.calib_blocks, args.crossover_steps, min(args.warmup, 3))
         out["crossover"] = crossover_sweep(model, sweep_ctx, args.crossover_blocks, args.crossover_steps,
-                                           min(args.warmup, 3))
+                                           min(args.warmup, 3), calib=calib)
     if not args.no_cpu_baseline:
         try:
             out["cpu_baseline"] = cpu_baseline(model, head_n)

@@ -222,3 +222,49 @@ def test_compact_record_drops_summaries_before_the_headline():
     rec = json.loads(bench.compact_record(full))
     assert "cells" not in rec and rec["roofline"]["frac"] == 0.7877 and "cpu_baseline" in rec
     assert len(bench.compact_record(full).encode()) <= bench.COMPACT_LIMIT
+
+
+@pytest.mark.parametrize("mp,mk,r_p,r_kv", bench.PAIRS)
+def test_prediction_from_a_separate_calibration_grid(mp, mk, r_p, r_kv):
+    """The prediction fitted on the coarse calibration contexts (a separate
+    sweep) agrees with the one fitted on the crossover grid when the step
+    times follow bytes / BW + per-mode constants exactly."""
+    costs = {"dense": 250.0, mp: 700.0, mk: 520.0}
+    fine = synthetic_times(6500.0, costs)
+    ctx = bench.CALIB_CONTEXTS
+    coarse = {m: np.array([bench.mode_bytes(m, n) / 6500e3 + costs.get(m, 0.0) for n in ctx])
+              for m in ("dense", mp, mk)}
+    p_fine = bench.predicted_crossing_k(CTX, fine, mp, mk)
+    p_coarse = bench.predicted_crossing_k(ctx, coarse, mp, mk)
+    assert p_coarse[0] == pytest.approx(p_fine[0], abs=1e-6)
+    assert p_coarse[2] == pytest.approx(700.0, abs=1e-3) and p_coarse[3] == pytest.approx(520.0, abs=1e-3)
+
+
+def test_step_pmc_summary_on_synthetic_counters(tmp_path):
+    """The whole-step byte sum keeps only the dispatches after the marker,
+    divides by the number of steps and scales by the copy calibration."""
+    def write(path, rows):
+        with open(path, "w") as fh:
+            fh.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+            for d, k, v in rows:
+                fh.write(f'{d},"{k}",X,{v}\n')
+    # setup dispatches, the marker, then 2 steps of two kernels each; a
+    # second mode's setup, its marker and one step of one kernel
+    fetch = [(1, "k_pack_tiles", 9e9), (2, "k_stream_read(uint4 const*)", 2048.0),
+             (3, "k_gemv<1, 0, 4>(...)", 1000.0), (4, "k_attn_partial<128, 4, 1, 0>(...)", 500.0),
+             (5, "k_gemv<1, 0, 4>(...)", 1000.0), (6, "k_attn_partial<128, 4, 1, 0>(...)", 500.0),
+             (7, "k_stream_read(uint4 const*)", 2048.0), (8, "k_gemv<3, 0, 4>(...)", 300.0)]
+    write_ = [(d, k, v / 10) for d, k, v in fetch]
+    write(tmp_path / "f.csv", fetch)
+    write(tmp_path / "w.csv", write_)
+    write(tmp_path / "cf.csv", [(1, "copyBuffer", 512.0)])      # 1 MiB copy: fetch factor 0.5
+    write(tmp_path / "cw.csv", [(1, "copyBuffer", 1024.0)])     # write factor 1.0
+    r, r2 = bench.step_pmc_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
+                                   str(tmp_path / "cw.csv"), "dense:2048:2+proj0.5:2048:1", str(1 << 20))
+    assert r2["fetch_bytes"] == round(300 * 1024 / 0.5) and list(r2["fetch_by_kernel"]) == ["k_gemv<3, 0, 4>"]
+    assert r["copy_factors"] == {"fetch": 0.5, "write": 1.0}
+    assert r["fetch_bytes"] == round(1500 * 1024 / 0.5)
+    assert r["write_bytes"] == round(150 * 1024)
+    assert r["measured_bytes"] == r["fetch_bytes"] + r["write_bytes"]
+    assert set(r["fetch_by_kernel"]) == {"k_gemv<1, 0, 4>", "k_attn_partial<128, 4, 1, 0>"}
+    assert r["algorithmic_bytes"] == bench.step_bytes(2048, 1.0, 1.0, *bench.kv_plan(2048, 1.0))
