@@ -93,6 +93,8 @@ _SIG = {
     "bc_step_workspace_bytes": (c_size_t, [ctypes.POINTER(bc_model_dims), c_int, c_int]),
     "bc_decode_step": (c_int, [ctypes.POINTER(bc_model_dims), ctypes.POINTER(bc_layer), c_int, P, P,
                                ctypes.POINTER(bc_step), P, P, P, P, c_size_t, P]),
+    "bc_decode_step_noalloc": (c_int, [ctypes.POINTER(bc_model_dims), ctypes.POINTER(bc_layer), c_int, P, P,
+                                       ctypes.POINTER(bc_step), P, P, P, P]),
     "bc_lm_head": (c_int, [ctypes.POINTER(bc_model_dims), P, P, P, P, P, c_double, P, c_size_t, P]),
 }
 for _name, (_res, _args) in _SIG.items():
@@ -331,3 +333,14 @@ def bc_decode_step(md: bc_model_dims, layer_array, g_final, w_head, step: bc_ste
     return _check(_lib.bc_decode_step(ctypes.byref(md), layer_array, len(layer_array), _ptr(g_final), _ptr(w_head),
                                       ctypes.byref(step), _ptr(hidden), _ptr(logits), _ptr(token), p, n,
                                       _stream(stream)), "bc_decode_step")
+
+
+BC_STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def bc_decode_step_noalloc(md: bc_model_dims, layer_array, g_final, w_head, step: bc_step, hidden, logits, token,
+                           stream=None):
+    """bc_decode_step with the library's static workspace (no ws argument)."""
+    return _check(_lib.bc_decode_step_noalloc(ctypes.byref(md), layer_array, len(layer_array), _ptr(g_final),
+                                              _ptr(w_head), ctypes.byref(step), _ptr(hidden), _ptr(logits),
+                                              _ptr(token), _stream(stream)), "bc_decode_step_noalloc")

@@ -21,6 +21,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "bc_device.hpp"
 #include "bc_internal.hpp"
 
@@ -612,25 +614,31 @@ extern "C" size_t bc_step_workspace_bytes(const bc_model_dims* dims, int max_ctx
   return step_layout(*dims, max_ctx, max_splits).total;
 }
 
-extern "C" int bc_decode_step(const bc_model_dims* dims, const bc_layer* layers, int n_layers, const uint16_t* g_final,
-                              const uint16_t* w_head, const bc_step* st, uint16_t* hidden, float* logits,
-                              int32_t* token, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+// Arguments of a whole step, checked on the host; fills *S with the step's
+// workspace layout.
+int check_step_call(const bc_model_dims* dims, const bc_layer* layers, int n_layers, const uint16_t* g_final,
+                    const uint16_t* w_head, const bc_step* st, uint16_t* hidden, float* logits, int32_t* token,
+                    const char* who, bc_kv_budget_info* bud, int* n_splits, StepLayout* S) {
   int rc = check_dims(dims);
   if (rc != BC_OK) return rc;
-  if (!layers || n_layers < 1 || !g_final || !w_head || !st || !hidden || !logits || !token || !ws)
-    return set_error(BC_ERR_INVALID, "bc_decode_step: NULL argument or no layers");
-  if (dims->vocab <= 0 || dims->vocab % 8 != 0) return set_error(BC_ERR_UNSUPPORTED, "bc_decode_step: vocab %% 8 != 0");
+  if (!layers || n_layers < 1 || !g_final || !w_head || !st || !hidden || !logits || !token)
+    return set_error(BC_ERR_INVALID, "%s: NULL argument or no layers", who);
+  if (dims->vocab <= 0 || dims->vocab % 8 != 0) return set_error(BC_ERR_UNSUPPORTED, "%s: vocab %% 8 != 0", who);
   if ((rc = check_step(st)) != BC_OK) return rc;
   for (int i = 0; i < n_layers; ++i)
     if ((rc = check_layer(&layers[i], st)) != BC_OK) return rc;
-  bc_kv_budget_info bud;
-  if ((rc = bc_kv_budget(st->n_ctx, &st->kv, &bud)) != BC_OK) return rc;
-  const bc_model_dims& m = *dims;
-  const int n_splits = step_splits(m, st, bud);
-  const StepLayout S = step_layout(m, st->n_ctx, n_splits);
-  if (ws_bytes < S.total) return set_error(BC_ERR_WORKSPACE, "bc_decode_step: workspace %zu < %zu", ws_bytes, S.total);
-  if (reinterpret_cast<uintptr_t>(ws) & 255) return set_error(BC_ERR_INVALID, "bc_decode_step: ws not 256-byte aligned");
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((rc = bc_kv_budget(st->n_ctx, &st->kv, bud)) != BC_OK) return rc;
+  *n_splits = step_splits(*dims, st, *bud);
+  *S = step_layout(*dims, st->n_ctx, *n_splits);
+  return BC_OK;
+}
+
+int step_body(const bc_model_dims& m, const bc_layer* layers, int n_layers, const uint16_t* g_final,
+              const uint16_t* w_head, const bc_step* st, const bc_kv_budget_info& bud, int n_splits,
+              const StepLayout& S, uint16_t* hidden, float* logits, int32_t* token, void* ws, hipStream_t s) {
+  int rc;
   bc_step one = *st;
   one.taps = nullptr;
   // each layer's output stays pending (down partials + h1) until the next
@@ -645,6 +653,79 @@ extern "C" int bc_decode_step(const bc_model_dims* dims, const bc_layer* layers,
   }
   return run_head(m, hidden, pend.partial ? &pend : nullptr, g_final, w_head, float(st->rms_eps), logits, token,
                   at<float>(ws, S.head.partial), at<float>(ws, S.head.tile_max), at<int32_t>(ws, S.head.tile_arg), s);
+}
+
+}  // namespace
+
+extern "C" int bc_decode_step(const bc_model_dims* dims, const bc_layer* layers, int n_layers, const uint16_t* g_final,
+                              const uint16_t* w_head, const bc_step* st, uint16_t* hidden, float* logits,
+                              int32_t* token, void* ws, size_t ws_bytes, void* stream) {
+  bc_kv_budget_info bud;
+  int n_splits = 0;
+  StepLayout S;
+  int rc = check_step_call(dims, layers, n_layers, g_final, w_head, st, hidden, logits, token, "bc_decode_step",
+                           &bud, &n_splits, &S);
+  if (rc != BC_OK) return rc;
+  if (!ws) return set_error(BC_ERR_INVALID, "bc_decode_step: NULL workspace");
+  if (ws_bytes < S.total) return set_error(BC_ERR_WORKSPACE, "bc_decode_step: workspace %zu < %zu", ws_bytes, S.total);
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return set_error(BC_ERR_INVALID, "bc_decode_step: ws not 256-byte aligned");
+  return step_body(*dims, layers, n_layers, g_final, w_head, st, bud, n_splits, S, hidden, logits, token, ws,
+                   static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------- allocation-free step
+// The workspace of bc_decode_step_noalloc: one static device array, which
+// every GPU the library runs on holds (at its own address) until the process
+// ends.  Host code never uses the array's name as an address: the address is
+// looked up once per device with hipGetSymbolAddress and kept in
+// g_scratch_ptr, and only that pointer reaches kernels.
+static __device__ __align__(256) unsigned char scratch[BC_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of `scratch`.  The first call on a device (that
+// device current) looks it up and enqueues one fill kernel on `s` that
+// clears it.
+int scratch_on_device(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(BC_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return set_error(BC_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(BC_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    const int rc = launch_fill_zero(p, BC_STATIC_SCRATCH_BYTES, s);
+    if (rc != BC_OK) return rc;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BC_OK;
+}
+}  // namespace
+
+extern "C" int bc_decode_step_noalloc(const bc_model_dims* dims, const bc_layer* layers, int n_layers,
+                                      const uint16_t* g_final, const uint16_t* w_head, const bc_step* st,
+                                      uint16_t* hidden, float* logits, int32_t* token, void* stream) {
+  bc_kv_budget_info bud;
+  int n_splits = 0;
+  StepLayout S;
+  int rc = check_step_call(dims, layers, n_layers, g_final, w_head, st, hidden, logits, token,
+                           "bc_decode_step_noalloc", &bud, &n_splits, &S);
+  if (rc != BC_OK) return rc;
+  if (S.total > size_t(BC_STATIC_SCRATCH_BYTES))
+    return set_error(BC_ERR_WORKSPACE,
+                     "bc_decode_step_noalloc: this step needs %zu bytes of workspace, above the static %u "
+                     "(use bc_decode_step with a workspace)", S.total, unsigned(BC_STATIC_SCRATCH_BYTES));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if ((rc = scratch_on_device(s, &ws)) != BC_OK) return rc;
+  return step_body(*dims, layers, n_layers, g_final, w_head, st, bud, n_splits, S, hidden, logits, token, ws, s);
 }
 
 // ------------------------------------------------------------------ LM head

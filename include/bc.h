@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define BC_ABI_VERSION 3
+#define BC_ABI_VERSION 4
 
 enum {
   BC_OK = 0,
@@ -299,6 +299,26 @@ size_t bc_step_workspace_bytes(const bc_model_dims* dims, int max_ctx, int max_s
 int bc_decode_step(const bc_model_dims* dims, const bc_layer* layers, int n_layers, const uint16_t* g_final,
                    const uint16_t* w_head, const bc_step* step, uint16_t* hidden, float* logits, int32_t* token,
                    void* ws, size_t ws_bytes, void* stream);
+
+/* The step of bc_decode_step without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments (minus ws and
+ * ws_bytes), same kernels, same result bits.  The workspace is a static
+ * device array of BC_STATIC_SCRATCH_BYTES (16 MiB) inside the library, which
+ * each GPU the library runs on holds until the process ends; this call
+ * allocates and frees nothing.  A step whose workspace
+ * (bc_step_workspace_bytes) is larger fails with BC_ERR_WORKSPACE before
+ * anything is enqueued (at Llama-3.1-8B dims with the default splits that is
+ * a context above about 440K tokens).  The first call on a device, with that
+ * device current, looks up the array's address and enqueues one fill kernel
+ * on `stream` that clears it.  Every call on a GPU shares that GPU's array
+ * and leaves in it what the last call wrote: calls that overlap in time on
+ * one GPU (other streams, other threads) race and must be ordered by the
+ * caller. */
+#define BC_STATIC_SCRATCH_BYTES (16u << 20)
+int bc_decode_step_noalloc(const bc_model_dims* dims, const bc_layer* layers, int n_layers, const uint16_t* g_final,
+                           const uint16_t* w_head, const bc_step* st, uint16_t* hidden, float* logits,
+                           int32_t* token, void* stream);
 
 /* Tile-major re-layout of a W^T matrix for bc_decode_layer and bc_lm_head
  * (setup, not timed): the columns are cut into tiles of 128 (the last one

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(bc):
 
 
 def test_abi_version(bc):
-    assert bc.bc_abi_version() == 3
+    assert bc.bc_abi_version() == 4
 
 
 @pytest.mark.parametrize("r_p,d", [(0.5, 4096), (0.7, 4096), (0.7, 14336), (0.5, 1408), (1.0, 77), (0.0001, 77),
@@ -104,6 +104,25 @@ def test_host_side_errors(bc):
     assert bc.bc_layer_workspace_bytes(md, 2048, 8) > 0
     bad = bc.dims(dict(d=500, d_ff=1408, n_heads=8, n_kv_heads=2, head_dim=64))
     assert bc.bc_layer_workspace_bytes(bad, 2048, 8) == 0
+
+
+def test_noalloc_step_rejects_oversized_steps_on_the_host(bc):
+    """bc_decode_step_noalloc checks the step's workspace against its static
+    array before anything is enqueued (and before the array is looked up)."""
+    lib = bc.library()
+    md = bc.dims(dict(d=4096, d_ff=14336, n_heads=32, n_kv_heads=8, head_dim=128, vocab=128256, n_layers=1))
+    A = 1 << 20
+    n_cap = 600000
+    ly = bc.bc_layer(A, A, A, A, A, A, A, A, A, n_cap)
+    arr = bc.make_layer_array([ly])
+    assert bc.bc_step_workspace_bytes(md, n_cap, bc.bc_attn_default_splits(n_cap, 8)) > bc.BC_STATIC_SCRATCH_BYTES
+    st = bc.make_step(n_cap, 1.0, bc.policy(1.0))
+    rc = lib.bc_decode_step_noalloc(ctypes.byref(md), arr, 1, A, A, ctypes.byref(st), A, A, A, None)
+    assert rc == bc.BC_ERR_WORKSPACE
+    assert "static" in lib.bc_last_error().decode()
+    # NULL arguments are rejected the same way as by bc_decode_step
+    rc = lib.bc_decode_step_noalloc(ctypes.byref(md), arr, 1, None, A, ctypes.byref(st), A, A, A, None)
+    assert rc == bc.BC_ERR_INVALID
 
 
 def test_workspace_queries_monotone(bc):
