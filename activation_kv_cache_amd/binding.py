@@ -59,7 +59,8 @@ class bc_layer_taps(ctypes.Structure):
 
 class bc_step(ctypes.Structure):
     _fields_ = [("n_ctx", c_int), ("r_p", c_double), ("kv", bc_kv_policy), ("n_splits", c_int),
-                ("rope_theta", c_double), ("rms_eps", c_double), ("taps", ctypes.POINTER(bc_layer_taps))]
+                ("rope_theta", c_double), ("rms_eps", c_double), ("taps", ctypes.POINTER(bc_layer_taps)),
+                ("masked_ws", c_void_p), ("masked_ws_bytes", c_size_t)]
 
 
 P = c_void_p
@@ -81,9 +82,15 @@ _SIG = {
                                    P, c_size_t, P]),
     "bc_build_kv_summary": (c_int, [P, c_int, c_int, c_int, c_int, P, P]),
     "bc_kv_compact": (c_int, [P, P, c_int, c_int, c_int, P, c_int, P, P, c_int, P]),
+    "bc_kv_snap_t_sel": (c_int, [c_int, ctypes.POINTER(bc_kv_policy)]),
+    "bc_kv_snap_select_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
+    "bc_kv_snap_select": (c_int, [P, c_int, P, c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(bc_kv_policy), c_int,
+                                  P, P, P, c_size_t, P]),
     "bc_splitk_attn_partial": (c_int, [P, P, P, c_int, P, c_int, c_int, c_int, c_int, c_int, c_float, P, P, P, P]),
     "bc_splitk_reduce": (c_int, [P, P, P, c_int, c_int, c_int, P, P]),
     "bc_attn_default_splits": (c_int, [c_int, c_int]),
+    "bc_masked_attn_workspace_bytes": (c_size_t, [c_int, c_int, c_int]),
+    "bc_masked_attn": (c_int, [P, P, P, c_int, c_int, c_int, c_int, c_int, c_float, P, P, c_size_t, P]),
     "bc_layer_workspace_bytes": (c_size_t, [ctypes.POINTER(bc_model_dims), c_int, c_int]),
     "bc_decode_layer": (c_int, [ctypes.POINTER(bc_model_dims), ctypes.POINTER(bc_layer), ctypes.POINTER(bc_step),
                                 P, P, c_size_t, P]),
@@ -240,6 +247,28 @@ def bc_kv_score_select(q, summary, n_ctx: int, n_heads: int, n_kv_heads: int, he
                                           _stream(stream)), "bc_kv_score_select")
 
 
+def bc_kv_snap_t_sel(n_ctx: int, pol: bc_kv_policy) -> int:
+    t = _lib.bc_kv_snap_t_sel(int(n_ctx), ctypes.byref(pol))
+    if t < 0:
+        raise BcError(t, "bc_kv_snap_t_sel")
+    return t
+
+
+def bc_kv_snap_select_workspace_bytes(n_ctx: int, n_heads: int, n_kv_heads: int, w_obs: int) -> int:
+    return _lib.bc_kv_snap_select_workspace_bytes(int(n_ctx), int(n_heads), int(n_kv_heads), int(w_obs))
+
+
+def bc_kv_snap_select(q_obs, k_cache, n_ctx: int, n_heads: int, n_kv_heads: int, pol: bc_kv_policy, idx_out,
+                      scores_out=None, ws=None, pool_kernel: int = 5, stream=None):
+    """q_obs [w_obs][n_heads][head_dim], k_cache [n_kv_heads][n_cap][head_dim]."""
+    w_obs, _, hd = q_obs.shape
+    n_cap = k_cache.shape[1]
+    p, n = _ws(ws)
+    return _check(_lib.bc_kv_snap_select(_ptr(q_obs), int(w_obs), _ptr(k_cache), int(n_cap), int(n_ctx), int(n_heads),
+                                         int(n_kv_heads), int(hd), ctypes.byref(pol), int(pool_kernel), _ptr(idx_out),
+                                         _ptr(scores_out), p, n, _stream(stream)), "bc_kv_snap_select")
+
+
 def bc_build_kv_summary(k_cache, n_ctx: int, summary, stream=None):
     n_kv, n_cap, hd = k_cache.shape
     return _check(_lib.bc_build_kv_summary(_ptr(k_cache), n_kv, n_cap, hd, int(n_ctx), _ptr(summary),
@@ -264,6 +293,19 @@ def bc_splitk_reduce(m, l, o, out, stream=None):
     n_heads, n_splits, hd = o.shape
     return _check(_lib.bc_splitk_reduce(_ptr(m), _ptr(l), _ptr(o), n_heads, n_splits, hd, _ptr(out),
                                         _stream(stream)), "bc_splitk_reduce")
+
+
+def bc_masked_attn_workspace_bytes(n_cap: int, n_heads: int, head_dim: int) -> int:
+    return _lib.bc_masked_attn_workspace_bytes(int(n_cap), int(n_heads), int(head_dim))
+
+
+def bc_masked_attn(q, k_cache, v_cache, n_ctx: int, n_heads: int, n_kv_heads: int, scale: float, out, ws,
+                   stream=None):
+    _, n_cap, hd = k_cache.shape
+    p, n = _ws(ws)
+    return _check(_lib.bc_masked_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(n_cap), int(n_ctx), int(n_heads),
+                                      int(n_kv_heads), int(hd), float(scale), _ptr(out), p, n, _stream(stream)),
+                  "bc_masked_attn")
 
 
 def bc_pack_gate_up(w_gate_t, w_up_t, w_gu, stream=None):
@@ -296,8 +338,11 @@ def make_taps(**bufs) -> bc_layer_taps:
 
 
 def make_step(n_ctx: int, r_p: float, pol: bc_kv_policy, n_splits: int = 0, rope_theta: float = 500000.0,
-              rms_eps: float = 1e-5, taps: bc_layer_taps | None = None) -> bc_step:
-    st = bc_step(int(n_ctx), float(r_p), pol, int(n_splits), float(rope_theta), float(rms_eps), None)
+              rms_eps: float = 1e-5, taps: bc_layer_taps | None = None, masked_ws=None) -> bc_step:
+    """masked_ws: a device workspace for the masked-attention dense baseline
+    (None: split-K attention)."""
+    mp, mn = _ws(masked_ws)
+    st = bc_step(int(n_ctx), float(r_p), pol, int(n_splits), float(rope_theta), float(rms_eps), None, mp, mn)
     if taps is not None:
         st.taps = ctypes.pointer(taps)
     return st

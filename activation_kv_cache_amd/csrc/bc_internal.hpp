@@ -208,6 +208,12 @@ int launch_kv_score(const KvSelectParams& p, hipStream_t s);
 // scores
 int launch_kv_block_select(const KvSelectParams& p, hipStream_t s);
 
+// The masked-attention dense baseline (bc_masked.hip): out bf16 [H][D].
+size_t masked_attn_workspace(int n_cap, int n_heads, int head_dim);
+int launch_masked_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, int n_cap, int n_ctx,
+                       int n_heads, int n_kv_heads, int head_dim, float scale, uint16_t* out, void* ws,
+                       hipStream_t s);
+
 int launch_select(const uint16_t* x, int n, int k, int32_t* idx_out, hipStream_t s);
 int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 

@@ -401,10 +401,22 @@ int check_layer(const bc_layer* ly, const bc_step* st) {
   return BC_OK;
 }
 
+// The masked-attention baseline's workspace against the layer's cache.
+int check_masked(const bc_model_dims& m, const bc_layer* ly, const bc_step* st) {
+  if (!st->masked_ws) return BC_OK;
+  const size_t need = masked_attn_workspace(ly->n_cap, m.n_heads, m.head_dim);
+  if (st->masked_ws_bytes < need)
+    return set_error(BC_ERR_WORKSPACE, "masked attention workspace %zu < %zu", st->masked_ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(st->masked_ws) & 255) return set_error(BC_ERR_INVALID, "masked_ws not 256-byte aligned");
+  return BC_OK;
+}
+
 int check_step(const bc_step* st) {
   if (!(st->r_p > 0.0)) return set_error(BC_ERR_INVALID, "r_p must be > 0");
   if (!(st->rms_eps >= 0.0) || !(st->rope_theta > 0.0)) return set_error(BC_ERR_INVALID, "eps/theta out of range");
   if (st->n_splits < 0 || st->n_splits > 4096) return set_error(BC_ERR_INVALID, "n_splits=%d", st->n_splits);
+  if (st->masked_ws && st->kv.r_kv < 1.0)
+    return set_error(BC_ERR_UNSUPPORTED, "masked attention is the dense baseline: it needs r_kv >= 1");
   return BC_OK;
 }
 
@@ -449,6 +461,7 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
   RopeTable rope;
   rope_table(pos, st->rope_theta, hd, &rope);
   int qkv_splits = 0;
+  const bool masked = st->masked_ws != nullptr;   // the masked-attention dense baseline
   const bool fused_score = kv_sparse && (bud.window > 0 || bud.k_blk == 0);
   const bool scored_attn = kv_sparse && attn_scored_list_ok(bud, n_splits);
   // many candidates: one 1024-lane work-group per KV head ranks them once
@@ -461,13 +474,13 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
     kp.scores = at<float>(ws, L.scores); kp.scores_stride = bud.n_cand > 0 ? bud.n_cand : 1;
     kp.idx_out = at<int32_t>(ws, L.idx_kv);
   }
-  if (kv_sparse && !fused_score) {
+  if ((kv_sparse && !fused_score) || masked) {
     FinishParams f{};
     f.q_out = at<uint16_t>(ws, L.q); f.k_cache = ly->k_cache; f.v_cache = ly->v_cache; f.summary = ly->kv_summary;
     f.n_heads = H; f.n_kv_heads = Hkv; f.head_dim = hd; f.n_cap = ly->n_cap; f.pos = pos; f.rope = rope;
     if ((rc = run_gemv(ly->w_qkv, m.d, qkv_out, k_d, qkv_in, partial, FIN_QKV, f, s)) != BC_OK) return rc;
     kp.q = at<uint16_t>(ws, L.q);
-    if ((rc = launch_kv_score(kp, s)) != BC_OK) return rc;
+    if (kv_sparse && (rc = launch_kv_score(kp, s)) != BC_OK) return rc;
   } else {
     if ((rc = run_gemv(ly->w_qkv, m.d, qkv_out, k_d, qkv_in, partial, FIN_NONE, FinishParams{}, s, &qkv_splits)) !=
         BC_OK)
@@ -487,8 +500,13 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
   }
 
   // attention; a dense o GEMV folds the reduce into its prologue
-  const bool fold_reduce = k_d == H * hd && gemv_attn_fold_ok(H * hd, m.d, hd, n_splits);
-  {
+  const bool fold_reduce = !masked && k_d == H * hd && gemv_attn_fold_ok(H * hd, m.d, hd, n_splits);
+  if (masked) {
+    const float scale = float(1.0 / sqrt(double(hd)));
+    if ((rc = launch_masked_attn(at<uint16_t>(ws, L.q), ly->k_cache, ly->v_cache, ly->n_cap, st->n_ctx, H, Hkv, hd,
+                                 scale, a, st->masked_ws, s)) != BC_OK)
+      return rc;
+  } else {
     AttnParams p{};
     p.k_cache = ly->k_cache; p.v_cache = ly->v_cache; p.n_cap = ly->n_cap;
     p.n_sel = n_sel; p.n_heads = H; p.n_kv_heads = Hkv; p.head_dim = hd; p.n_splits = n_splits;
@@ -574,7 +592,7 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
     if (sparse && (rc = copy_tap(t->idx_gu, idx_gu, size_t(k_d) * 4, s)) != BC_OK) return rc;
     if ((rc = copy_tap(t->hff, hff, size_t(m.d_ff) * 2, s)) != BC_OK) return rc;
     if (sparse && (rc = copy_tap(t->idx_down, idx_down, size_t(k_ff) * 4, s)) != BC_OK) return rc;
-    const size_t ml = size_t(H) * n_splits * 4;
+    const size_t ml = masked ? 0 : size_t(H) * n_splits * 4;   // the masked baseline has no split partials
     if ((rc = copy_tap(t->attn_m, at<void>(ws, L.m), ml, s)) != BC_OK) return rc;
     if ((rc = copy_tap(t->attn_l, at<void>(ws, L.l), ml, s)) != BC_OK) return rc;
     if ((rc = copy_tap(t->attn_o, at<void>(ws, L.o), ml * hd, s)) != BC_OK) return rc;
@@ -599,7 +617,9 @@ extern "C" int bc_decode_layer(const bc_model_dims* dims, const bc_layer* ly, co
   int rc = check_dims(dims);
   if (rc != BC_OK) return rc;
   if (!ly || !st || !hidden || !ws) return set_error(BC_ERR_INVALID, "bc_decode_layer: NULL argument");
-  if ((rc = check_layer(ly, st)) != BC_OK || (rc = check_step(st)) != BC_OK) return rc;
+  if ((rc = check_layer(ly, st)) != BC_OK || (rc = check_step(st)) != BC_OK ||
+      (rc = check_masked(*dims, ly, st)) != BC_OK)
+    return rc;
   bc_kv_budget_info bud;
   if ((rc = bc_kv_budget(st->n_ctx, &st->kv, &bud)) != BC_OK) return rc;
   const int n_splits = step_splits(*dims, st, bud);
@@ -628,7 +648,7 @@ int check_step_call(const bc_model_dims* dims, const bc_layer* layers, int n_lay
   if (dims->vocab <= 0 || dims->vocab % 8 != 0) return set_error(BC_ERR_UNSUPPORTED, "%s: vocab %% 8 != 0", who);
   if ((rc = check_step(st)) != BC_OK) return rc;
   for (int i = 0; i < n_layers; ++i)
-    if ((rc = check_layer(&layers[i], st)) != BC_OK) return rc;
+    if ((rc = check_layer(&layers[i], st)) != BC_OK || (rc = check_masked(*dims, &layers[i], st)) != BC_OK) return rc;
   if ((rc = bc_kv_budget(st->n_ctx, &st->kv, bud)) != BC_OK) return rc;
   *n_splits = step_splits(*dims, st, *bud);
   *S = step_layout(*dims, st->n_ctx, *n_splits);

@@ -37,6 +37,7 @@ METRIC = "decode-step µs and achieved HBM GB/s vs context 2K–128K, Llama-3.1-
 HBM_PEAK_GBS = 8000.0
 DIMS = dict(n_layers=32, d=4096, d_ff=14336, vocab=128256, n_heads=32, n_kv_heads=8, head_dim=128)
 SINKS, WINDOW = 4, 1024
+W_OBS, POOL = 32, 5       # select-once (SnapKV form): observation window, pooling kernel
 KERNEL_SOURCES = ["activation_kv_cache_amd/csrc/bc_attn.hip", "activation_kv_cache_amd/csrc/bc_device.hpp"]
 
 
@@ -195,6 +196,12 @@ def kv_plan(n, r_kv, sinks=SINKS, window=WINDOW, block=16):
     return t_sel, splits
 
 
+def snap_t_sel(n, r_kv):
+    """Tokens kept by the select-once policy: T = min(n, floor(r_kv n + 1/2))
+    (host replica of bc_kv_snap_t_sel)."""
+    return n if r_kv >= 1 else min(n, int(math.floor(r_kv * n + 0.5)))
+
+
 def mode_bytes(mode, n, plan=None):
     """Algorithmic bytes of one step of a sweep mode at context n.  The sel
     modes (selection made once and gathered, README "Timing and quality on a
@@ -203,7 +210,7 @@ def mode_bytes(mode, n, plan=None):
     plan = plan or (lambda n_, a, b: kv_plan(n_, b))
     r_p, r_kv, once = SWEEP_MODES[mode]
     if once:
-        t_sel, _ = plan(n, 1.0, r_kv)
+        t_sel = snap_t_sel(n, r_kv)
         return step_bytes(t_sel, r_p, 1.0, *plan(t_sel, 1.0, 1.0))
     return step_bytes(n, r_p, r_kv, *plan(n, r_p, r_kv))
 
@@ -352,20 +359,21 @@ class Model:
                                        l["k"], l["v"], l["summ"]) for l in self.layers]
         self.layer_array = bc.make_layer_array(self.c_layers)
         # sel modes: per layer a compact cache for the gathered selection
-        # (the largest T_sel of the sweep, r_kv 0.5 at max_ctx) and the query
-        # the selection is scored with (seeded; it stands in for the query of
-        # the last pre-filled position)
-        cap = (self.plan(max_ctx, 1.0, 0.5)[1] + 16 + 15) // 16 * 16
+        # (the largest T_sel of the sweep, r_kv 0.5 at max_ctx) and the
+        # observation window the selection is scored with: the post-rotary
+        # queries of the last W_OBS pre-filled positions (seeded; they stand
+        # in for the queries of a prefill of real text)
+        cap = (snap_t_sel(max_ctx, 0.5) + 16 + 15) // 16 * 16
         self.sel_cap = cap
-        self.sel_q = [gen.device_normal_bf16(seed, f"layer{li}/selq", (H, hd), 1.0) for li in range(L)]
+        self.sel_q = [gen.device_normal_bf16(seed, f"layer{li}/selq", (W_OBS, H, hd), 1.0) for li in range(L)]
         self.sel_kv = [(torch.empty((Hkv, cap, hd), dtype=torch.int16, device="cuda"),
                         torch.empty((Hkv, cap, hd), dtype=torch.int16, device="cuda")) for _ in range(L)]
         self.c_layers_sel = [bc.make_layer(l["w_qkv"], l["w_o"], l["w_gu"], l["w_down"], self.g_attn, self.g_mlp,
                                            kc, vc, None) for l, (kc, vc) in zip(self.layers, self.sel_kv)]
         self.layer_array_sel = bc.make_layer_array(self.c_layers_sel)
         self.sel_idx = torch.empty((Hkv, max_ctx), dtype=torch.int32, device="cuda")
-        self.sel_ws = torch.empty(bc.bc_kv_score_select_workspace_bytes(max_ctx, Hkv, bc.policy(0.3, SINKS, WINDOW))
-                                  // 4 + 64, dtype=torch.int32, device="cuda")
+        self.sel_ws = torch.empty(bc.bc_kv_snap_select_workspace_bytes(max_ctx, H, Hkv, W_OBS) // 4 + 64,
+                                  dtype=torch.int32, device="cuda")
         torch.cuda.synchronize()
         log(f"[bench] model ready in {time.time() - t0:.1f}s; "
             f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
@@ -414,18 +422,20 @@ class Model:
         return g
 
     def sel_prepare(self, n, r_kv):
-        """Select once and gather (not timed): every layer scores the blocks
-        of its pre-filled cache with its query, and the kept tokens (sinks,
-        blocks, window -- the last one being position n-1) are copied into
-        its compact cache.  Returns T_sel."""
+        """Select once and gather (not timed; README FAQ: the KV branch
+        follows SnapKV with one selection after prefill): every layer scores
+        the tokens of its pre-filled cache by the pooled attention of its
+        observation window (bc_kv_snap_select) and copies the kept tokens
+        (sinks, history, window -- the last one being position n-1) into its
+        compact cache (bc_kv_compact).  Returns T_sel."""
         bc = self.bc
         D = DIMS
         pol = bc.policy(r_kv, SINKS, WINDOW)
-        t_sel = bc.bc_kv_budget(n, pol)["t_sel"]
+        t_sel = bc.bc_kv_snap_t_sel(n, pol)
         idx = self.sel_idx.view(-1)[:D["n_kv_heads"] * t_sel].view(D["n_kv_heads"], t_sel)
         for ly, q, (kc, vc) in zip(self.layers, self.sel_q, self.sel_kv):
-            bc.bc_kv_score_select(q, ly["summ"], n, D["n_heads"], D["n_kv_heads"], D["head_dim"], pol, idx, None,
-                                  self.sel_ws)
+            bc.bc_kv_snap_select(q, ly["k"], n, D["n_heads"], D["n_kv_heads"], pol, idx, None, self.sel_ws,
+                                 pool_kernel=POOL)
             bc.bc_kv_compact(ly["k"], ly["v"], idx, t_sel, kc, vc)
         torch.cuda.synchronize()
         return t_sel
@@ -741,6 +751,29 @@ def load_traffic(n):
     return rec.get("traffic_bytes_per_launch")
 
 
+def all_sources_hash():
+    import glob
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "activation_kv_cache_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_step_bytes():
+    """Whole-step HBM bytes per mode against the byte account, from the
+    committed counter summary (profiles/decode_step_bytes_pmc.json), with a
+    flag telling whether the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "decode_step_bytes_pmc.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    cur = rec.get("kernel_sources_hash") == all_sources_hash()
+    modes = rec.get("modes", [])
+    return {"source": "profiles/decode_step_bytes_pmc.json", "kernel_sources_unchanged": cur, "modes": modes,
+            "summary": {f"{m['mode']}@{m['context']}": [m["measured_over_algorithmic"], m["measured_over_page_account"]]
+                        for m in modes} if cur else None}
+
+
 def cpu_baseline(model, n):
     """The CPU oracle, as it stands, on one decoder layer of the dense step at
     context n (layer 0's weights and cache copied to the host)."""
@@ -952,33 +985,46 @@ def _read_counters(path):
     return rows
 
 
+def kernel_key(name):
+    """A kernel's name without its namespace and argument list, with its
+    template arguments (k_gemv<3, 0, 4>)."""
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "").replace("bc::", "")
+    return name.split("(")[0].strip()[:48]
+
+
 def step_pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, specs, copy_bytes):
     """HBM bytes of one decode step per mode, from two counter runs of
     --step-pmc (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled
     by what the same counter reads for a plain copy of copy_bytes bytes.
-    The dispatches between a mode's marker launch (k_stream_read) and the
-    next marker are that mode's REPS steps.  Each step is compared with its
+    The dispatches between a mode's two marker launches (k_stream_read,
+    before and after its steps) are that mode's REPS steps.  Each step is compared with its
     algorithmic bytes (step_bytes) and with the README's byte account
     r_p W_proj + W_head + (kept tokens) x KV bytes per token (README
     "Overview"; "Usage", the byte account).  Returns one record per mode."""
     specs = [(m, int(n), int(r)) for m, n, r in (x.split(":") for x in specs.split("+"))]
     copy_bytes = int(copy_bytes)
-    cf = sum(v for _, _, v in _read_counters(cfetch_csv)) * 1024 / copy_bytes
-    cw = sum(v for _, _, v in _read_counters(cwrite_csv)) * 1024 / copy_bytes
+
+    def copy_factor(path):
+        # the copy dispatches only (the run also fills its source)
+        vals = [v for _, k, v in _read_counters(path) if "copyBuffer" in k]
+        assert vals, f"no copy dispatch in {path}"
+        return float(np.mean(vals)) * 1024 / copy_bytes
+
+    cf, cw = copy_factor(cfetch_csv), copy_factor(cwrite_csv)
 
     def segments(path, factor):
         rows = sorted(_read_counters(path))
         marks = [d for d, k, _ in rows if "k_stream_read" in k]
-        assert len(marks) == len(specs), f"{path}: {len(marks)} markers for {len(specs)} modes"
+        assert len(marks) == 2 * len(specs), f"{path}: {len(marks)} markers for {len(specs)} modes"
         out = []
         for i, (mode, n, reps) in enumerate(specs):
-            lo, hi = marks[i], marks[i + 1] if i + 1 < len(marks) else float("inf")
+            lo, hi = marks[2 * i], marks[2 * i + 1]
             tot, by = 0.0, {}
             for d, k, v in rows:
                 if lo < d < hi:
                     b = v * 1024 / factor / reps
                     tot += b
-                    key = k.split("(")[0][:48]
+                    key = kernel_key(k)
                     by[key] = by.get(key, 0.0) + b
             out.append((tot, by))
         return out
@@ -993,7 +1039,7 @@ def step_pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, specs, copy_b
     recs = []
     for (mode, n, reps), (fetch, fby), (write, wby) in zip(specs, fseg, wseg):
         r_p, r_kv, once = SWEEP_MODES[mode]
-        t_sel, S = kv_plan(n, r_kv)
+        t_sel, S = (snap_t_sel(n, r_kv), 0) if once else kv_plan(n, r_kv)
         algo = step_bytes(t_sel, r_p, 1.0, *kv_plan(t_sel, 1.0)) if once else step_bytes(n, r_p, r_kv, t_sel, S)
         kept = t_sel if r_kv < 1 else n
         account = r_p * w_proj + w_head + kept * kv_tok
@@ -1007,6 +1053,49 @@ def step_pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, specs, copy_b
                      "fetch_by_kernel": {k: round(v) for k, v in sorted(fby.items(), key=lambda x: -x[1])},
                      "write_by_kernel": {k: round(v) for k, v in sorted(wby.items(), key=lambda x: -x[1])}})
     return recs
+
+
+def step_trace_summary(trace_csv, specs):
+    """Per-mode kernel times of a rocprofv3 kernel trace of --step-pmc runs:
+    after each mode's first marker launch, its REPS steps (each ending with
+    the LM head's k_argmax_finish); the first two are left out as warm-up.
+    Returns per mode the mean step time (first kernel start to last kernel
+    end) and per kernel its launches per step and mean duration (us)."""
+    import csv
+    rows = []
+    with open(trace_csv) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((int(r["Dispatch_Id"]), kernel_key(r["Kernel_Name"]), int(r["Start_Timestamp"]),
+                         int(r["End_Timestamp"])))
+    rows.sort()
+    specs = [(m, int(n), int(k)) for m, n, k in (x.split(":") for x in specs.split("+"))]
+    marks = [i for i, r in enumerate(rows) if r[1].startswith("k_stream_read")]
+    per = len(marks) // len(specs)
+    out = []
+    for si, (mode, n, reps) in enumerate(specs):
+        steps, cur = [], []
+        for r in rows[marks[si * per] + 1:]:
+            cur.append(r)
+            if r[1].startswith("k_argmax_finish"):
+                steps.append(cur)
+                cur = []
+                if len(steps) == reps:
+                    break
+        use = steps[2:]
+        wall = float(np.mean([st[-1][3] - st[0][2] for st in use])) / 1e3
+        kern = {}
+        for st in use:
+            for _, k, a, b in st:
+                e = kern.setdefault(k, [0, 0.0])
+                e[0] += 1
+                e[1] += (b - a) / 1e3
+        ks = sorted(kern.items(), key=lambda kv: -kv[1][1])
+        out.append({"mode": mode, "context": n, "steps": len(use), "step_us": round(wall, 1),
+                    "launches_per_step": round(sum(v[0] for _, v in ks) / len(use), 1),
+                    "kernels": [{"kernel": k, "per_step": round(v[0] / len(use), 1),
+                                 "mean_us": round(v[1] / v[0], 2), "us_per_step": round(v[1] / len(use), 1)}
+                                for k, v in ks]})
+    return out
 
 
 def main():
@@ -1036,13 +1125,15 @@ def main():
                     help="only launch the dense attention kernel this many times per layer (for counters)")
     ap.add_argument("--step-pmc", default="",
                     help="MODE:N:REPS[+MODE:N:REPS...] -- only REPS steps of each sweep mode at context N, each "
-                         "mode's steps after one marker launch (bc_stream_read of 4 MiB), for whole-step counters "
-                         "and kernel traces")
+                         "mode's steps between two marker launches (bc_stream_read of 4 MiB), for whole-step "
+                         "counters and kernel traces")
     ap.add_argument("--eager", action="store_true", help="with --step-pmc: eager steps instead of graph replays")
     ap.add_argument("--pmc-summary", default="",
                     help="FETCH_CSV,WRITE_CSV,CFETCH_CSV,CWRITE_CSV,SPECS,COPY_BYTES -- SPECS as for --step-pmc: "
-                         "sum the counters of each mode's steps (between its marker and the next) and print each "
-                         "step's HBM bytes against its byte account")
+                         "sum the counters of each mode's steps (between its two markers) and print each step's "
+                         "HBM bytes against its byte account")
+    ap.add_argument("--trace-summary", default="",
+                    help="TRACE_CSV,SPECS -- per-mode kernel times of a kernel trace of --step-pmc runs")
     ap.add_argument("--record", default=os.path.join(ROOT, "gpurun_out", "bench_record.json"),
                     help="where the full record (cells, kernels, sweep) is written; the last stdout line is a "
                          "compact summary of it")
@@ -1050,6 +1141,9 @@ def main():
 
     if args.pmc_summary:
         print(json.dumps(step_pmc_summary(*args.pmc_summary.split(","))))
+        return
+    if args.trace_summary:
+        print(json.dumps(step_trace_summary(*args.trace_summary.split(","))))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -1087,6 +1181,7 @@ def main():
             model.bc.bc_stream_read(marker, sink)       # marks where this mode's steps begin
             for _ in range(reps):
                 run()
+            model.bc.bc_stream_read(marker, sink)       # and where they end
             torch.cuda.synchronize()
             log(f"[bench] steps only: {mode} at {n}: {reps} steps ({'eager' if args.eager else 'graph'})")
         print(json.dumps({"step_pmc": args.step_pmc}))
@@ -1241,6 +1336,7 @@ def main():
                                                 "how": "torch.matmul(x[1, 4096], W[4096, 28672]) in bf16"}},
         "cells": results,
     }
+    out["step_bytes"] = load_step_bytes()
     # a batch of sequences through one union read of the gate|up weights
     out["batch_gemv"] = []
     for nb in (1, 2, 4):

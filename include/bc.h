@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define BC_ABI_VERSION 4
+#define BC_ABI_VERSION 5
 
 enum {
   BC_OK = 0,
@@ -192,6 +192,42 @@ int bc_build_kv_summary(const uint16_t* k_cache, int n_kv_heads, int n_cap, int 
 int bc_kv_compact(const uint16_t* k_cache, const uint16_t* v_cache, int n_cap, int n_kv_heads, int head_dim,
                   const int32_t* idx, int t_sel, uint16_t* k_out, uint16_t* v_out, int n_cap_out, void* stream);
 
+/* a4 (select once, SnapKV form).  The README's KV branch follows SnapKV with
+ * one selection after prefill (README FAQ "How is this different from TEAL
+ * and SnapKV?"); the selection is then gathered (bc_kv_compact) and read by
+ * the same dense split-K attention every step ("Timing and quality on a
+ * GPU"; "API at a glance": select_and_compact).  For KV head g, the
+ * observation rows are the w_obs queries of the last positions
+ * p_i = n_ctx - w_obs + i in each of the group's query heads j:
+ *   A_{i,j,t} = softmax over t <= p_i of scale * (q_obs[i][j] . k_t),
+ *               scale = 1/sqrt(head_dim);
+ *   vote_t   = sum_i sum_j A_{i,j,t}                      (t < n_ctx)
+ *   score_t  = (1/pool_kernel) * sum of vote_u over |u - t| <= pool_kernel/2
+ *              (votes outside [0, n_ctx) are 0)
+ * Budget (tokens, host-computable by bc_kv_snap_t_sel):
+ *   T = min(n, floor(r_kv*n + 1/2)); sinks' = min(sinks, T);
+ *   window' = min(window, T - sinks'); the k = T - sinks' - window' highest
+ *   float32 scores among tokens [sinks', n - window') are kept (equal scores:
+ *   lower token); T_sel = T.
+ * idx_out[g] = sinks', kept tokens, window', ascending.  policy->block is
+ * not used (token granularity).  The logits are computed with bf16 matrix
+ * instructions and float32 accumulation; softmax, votes and pooling in
+ * float32.
+ *   q_obs     bf16 [w_obs][n_heads][head_dim]  post-rotary observation queries
+ *   k_cache   bf16 [n_kv_heads][n_cap][head_dim]
+ *   idx_out   int32 [n_kv_heads][T_sel]
+ *   scores_out  optional fp32 [n_kv_heads][n_ctx]: score_t of every token
+ * Requires r_kv < 1, 1 <= w_obs <= n_ctx <= n_cap, w_obs * (n_heads /
+ * n_kv_heads) a multiple of 32 and at most 256 (BC_ERR_UNSUPPORTED
+ * otherwise), pool_kernel odd in [1, 63], q_obs and k_cache 16-byte aligned,
+ * ws 256-byte aligned, ws_bytes from bc_kv_snap_select_workspace_bytes.  Run
+ * once per layer after prefill; not part of the decode step. */
+int bc_kv_snap_t_sel(int n_ctx, const bc_kv_policy* pol);
+size_t bc_kv_snap_select_workspace_bytes(int n_ctx, int n_heads, int n_kv_heads, int w_obs);
+int bc_kv_snap_select(const uint16_t* q_obs, int w_obs, const uint16_t* k_cache, int n_cap, int n_ctx, int n_heads,
+                      int n_kv_heads, int head_dim, const bc_kv_policy* pol, int pool_kernel, int32_t* idx_out,
+                      float* scores_out, void* ws, size_t ws_bytes, void* stream);
+
 /* a5. Split-K decode attention, partial pass (README "Overview": dense and
  * sparse modes read their caches through the same split-K kernel).  For
  * query head j (KV head g = j / (n_heads/n_kv_heads)) and split s covering
@@ -217,6 +253,28 @@ int bc_splitk_attn_partial(const uint16_t* q, const uint16_t* k_cache, const uin
  * attention output equals this call's on the same partials, bit for bit. */
 int bc_splitk_reduce(const float* m, const float* l, const float* o, int n_heads, int n_splits,
                      int head_dim, uint16_t* out, void* stream);
+
+/* The masked-attention dense baseline (README FAQ "A KV method reports a
+ * speedup above its byte bound": timing the dense baseline with masked rather
+ * than split-K attention inflates a KV policy's apparent speedup; the
+ * abstract: about fivefold).  Decode attention as a plain masked attention
+ * over a preallocated cache computes it, for every query head j (KV head
+ * g = j / (n_heads/n_kv_heads)):
+ *   z_t = scale * (q_j . k_t) for every cache slot t < n_cap, -inf for
+ *         t >= n_ctx (the mask);  p = softmax(z) over all n_cap slots;
+ *   out_j = sum over all n_cap slots of p_t v_t, rounded to bf16.
+ * The scores and weights ([n_heads][n_cap] fp32) go through the workspace
+ * between the kernels, and each query head reads its KV head's rows itself.
+ * In real arithmetic it equals softmax attention over tokens 0..n_ctx-1.
+ * Slots n_ctx..n_cap-1 are read and must hold finite values.
+ *   q  bf16 [n_heads][head_dim]; k_cache, v_cache bf16 [n_kv_heads][n_cap][head_dim]
+ *   out bf16 [n_heads][head_dim]
+ * n_cap % 16 == 0, 1 <= n_ctx <= n_cap; ws 256-byte aligned, ws_bytes from
+ * bc_masked_attn_workspace_bytes. */
+size_t bc_masked_attn_workspace_bytes(int n_cap, int n_heads, int head_dim);
+int bc_masked_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, int n_cap, int n_ctx,
+                   int n_heads, int n_kv_heads, int head_dim, float scale, uint16_t* out, void* ws, size_t ws_bytes,
+                   void* stream);
 
 /* Split count the library picks for n_sel listed tokens (used when a step
  * passes n_splits = 0). */
@@ -277,6 +335,12 @@ typedef struct {
   double rope_theta;   /* e.g. 500000 */
   double rms_eps;      /* e.g. 1e-5 */
   const bc_layer_taps* taps;  /* optional */
+  /* Optional: the dense baseline with masked attention (bc_masked_attn) in
+   * place of split-K attention, its workspace of bc_masked_attn_workspace_bytes
+   * (n_cap, n_heads, head_dim) bytes given here; NULL = split-K attention.
+   * Requires r_kv >= 1. */
+  void* masked_ws;
+  size_t masked_ws_bytes;
 } bc_step;
 
 size_t bc_layer_workspace_bytes(const bc_model_dims* dims, int max_ctx, int max_splits);

@@ -386,6 +386,15 @@ void orc_snapkv_votes(const uint16_t* q_obs, const uint16_t* K, int n_cap, int n
 {
     int G = H / Hkv;
     int rows = w * G;
+    /* the keys and queries in double, once */
+    double* kd = (double*)malloc(sizeof(double) * (size_t)Hkv * n * D);
+    double* qd = (double*)malloc(sizeof(double) * (size_t)w * H * D);
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < (long)Hkv * n; ++r) {
+        long g = r / n, t = r % n;
+        for (int d = 0; d < D; ++d) kd[(size_t)r * D + d] = orc_bf16_to_double(K[((size_t)g * n_cap + t) * D + d]);
+    }
+    for (long e = 0; e < (long)w * H * D; ++e) qd[e] = orc_bf16_to_double(q_obs[e]);
     double* mrow = (double*)malloc(sizeof(double) * (size_t)Hkv * rows);
     double* lrow = (double*)malloc(sizeof(double) * (size_t)Hkv * rows);
     /* pass 1: per row, the max and the sum over its causal range */
@@ -394,38 +403,35 @@ void orc_snapkv_votes(const uint16_t* q_obs, const uint16_t* K, int n_cap, int n
         for (int r = 0; r < rows; ++r) {
             int i = r / G, j = g * G + r % G;
             long p = (long)n - w + i;
-            double qd[512];
-            for (int d = 0; d < D; ++d) qd[d] = orc_bf16_to_double(q_obs[((size_t)i * H + j) * D + d]);
+            const double* q = qd + ((size_t)i * H + j) * D;
+            double* z = (double*)malloc(sizeof(double) * (size_t)(p + 1));
             double mx = -INFINITY;
             for (long t = 0; t <= p; ++t) {
-                const uint16_t* kr = K + ((size_t)g * n_cap + t) * D;
+                const double* k = kd + ((size_t)g * n + t) * D;
                 double acc = 0.0;
-                for (int d = 0; d < D; ++d) acc += qd[d] * orc_bf16_to_double(kr[d]);
-                if (acc * scale > mx) mx = acc * scale;
+                for (int d = 0; d < D; ++d) acc += q[d] * k[d];
+                z[t] = acc * scale;
+                if (z[t] > mx) mx = z[t];
             }
             double sum = 0.0;
-            for (long t = 0; t <= p; ++t) {
-                const uint16_t* kr = K + ((size_t)g * n_cap + t) * D;
-                double acc = 0.0;
-                for (int d = 0; d < D; ++d) acc += qd[d] * orc_bf16_to_double(kr[d]);
-                sum += exp(acc * scale - mx);
-            }
+            for (long t = 0; t <= p; ++t) sum += exp(z[t] - mx);
             mrow[(size_t)g * rows + r] = mx;
             lrow[(size_t)g * rows + r] = sum;
+            free(z);
         }
     }
     /* pass 2: per token, the normalised weights summed over the rows */
 #pragma omp parallel for collapse(2) schedule(static)
     for (int g = 0; g < Hkv; ++g) {
         for (long t = 0; t < n; ++t) {
-            const uint16_t* kr = K + ((size_t)g * n_cap + t) * D;
+            const double* k = kd + ((size_t)g * n + t) * D;
             double v = 0.0;
             for (int r = 0; r < rows; ++r) {
                 int i = r / G, j = g * G + r % G;
                 if (t > (long)n - w + i) continue;
-                const uint16_t* qr = q_obs + ((size_t)i * H + j) * D;
+                const double* q = qd + ((size_t)i * H + j) * D;
                 double acc = 0.0;
-                for (int d = 0; d < D; ++d) acc += orc_bf16_to_double(qr[d]) * orc_bf16_to_double(kr[d]);
+                for (int d = 0; d < D; ++d) acc += q[d] * k[d];
                 v += exp(acc * scale - mrow[(size_t)g * rows + r]) / lrow[(size_t)g * rows + r];
             }
             votes[(size_t)g * n + t] = v;
@@ -433,6 +439,8 @@ void orc_snapkv_votes(const uint16_t* q_obs, const uint16_t* K, int n_cap, int n
     }
     free(lrow);
     free(mrow);
+    free(qd);
+    free(kd);
 }
 
 /* Average pooling of one vote vector over neighbouring tokens (SnapKV's

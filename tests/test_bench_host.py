@@ -23,6 +23,13 @@ def test_kv_plan_matches_library(bc, r_kv):
         assert bench.kv_plan(n, r_kv) == (t_sel, S), n
 
 
+def test_snap_t_sel_matches_library(bc):
+    for r_kv in (0.3, 0.5, 1.0):
+        pol = bc.policy(r_kv, bench.SINKS, bench.WINDOW)
+        for n in [1, 5, 1000, 1040, 2048, 4096, 6144, 32768, 65536 + 7, 131072]:
+            assert bench.snap_t_sel(n, r_kv) == bc.bc_kv_snap_t_sel(n, pol), (n, r_kv)
+
+
 CTX = [2048] + [4096 * i for i in range(1, 33)]
 
 
@@ -248,17 +255,24 @@ def test_step_pmc_summary_on_synthetic_counters(tmp_path):
             fh.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
             for d, k, v in rows:
                 fh.write(f'{d},"{k}",X,{v}\n')
-    # setup dispatches, the marker, then 2 steps of two kernels each; a
-    # second mode's setup, its marker and one step of one kernel
-    fetch = [(1, "k_pack_tiles", 9e9), (2, "k_stream_read(uint4 const*)", 2048.0),
-             (3, "k_gemv<1, 0, 4>(...)", 1000.0), (4, "k_attn_partial<128, 4, 1, 0>(...)", 500.0),
-             (5, "k_gemv<1, 0, 4>(...)", 1000.0), (6, "k_attn_partial<128, 4, 1, 0>(...)", 500.0),
-             (7, "k_stream_read(uint4 const*)", 2048.0), (8, "k_gemv<3, 0, 4>(...)", 300.0)]
+    # setup dispatches, the begin marker, 2 steps of two kernels each, the
+    # end marker; a second mode's setup, its markers around one step of one
+    # kernel
+    fetch = [(1, "k_pack_tiles", 9e9), (2, "void bc::(anonymous namespace)::k_stream_read(uint4 const*)", 2048.0),
+             (3, "void bc::(anonymous namespace)::k_gemv<1, 0, 4>(bc::GemvParams)", 1000.0),
+             (4, "k_attn_partial<128, 4, 1, 0>(...)", 500.0),
+             (5, "void bc::(anonymous namespace)::k_gemv<1, 0, 4>(bc::GemvParams)", 1000.0),
+             (6, "k_attn_partial<128, 4, 1, 0>(...)", 500.0),
+             (7, "k_stream_read(uint4 const*)", 2048.0), (8, "k_kv_compact", 5e9),
+             (9, "k_stream_read(uint4 const*)", 2048.0), (10, "k_gemv<3, 0, 4>(...)", 300.0),
+             (11, "k_stream_read(uint4 const*)", 2048.0)]
     write_ = [(d, k, v / 10) for d, k, v in fetch]
     write(tmp_path / "f.csv", fetch)
     write(tmp_path / "w.csv", write_)
-    write(tmp_path / "cf.csv", [(1, "copyBuffer", 512.0)])      # 1 MiB copy: fetch factor 0.5
-    write(tmp_path / "cw.csv", [(1, "copyBuffer", 1024.0)])     # write factor 1.0
+    # the copy run fills its source first; only the copy dispatches count
+    write(tmp_path / "cf.csv", [(1, "fill", 7.0), (2, "__amd_rocclr_copyBuffer", 512.0),
+                                (3, "__amd_rocclr_copyBuffer", 512.0)])      # 1 MiB copy: fetch factor 0.5
+    write(tmp_path / "cw.csv", [(1, "fill", 7.0), (2, "__amd_rocclr_copyBuffer", 1024.0)])     # write factor 1.0
     r, r2 = bench.step_pmc_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
                                    str(tmp_path / "cw.csv"), "dense:2048:2+proj0.5:2048:1", str(1 << 20))
     assert r2["fetch_bytes"] == round(300 * 1024 / 0.5) and list(r2["fetch_by_kernel"]) == ["k_gemv<3, 0, 4>"]

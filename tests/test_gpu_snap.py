@@ -1,0 +1,119 @@
+"""GPU parity of the select-once KV policy in the SnapKV form
+(bc_kv_snap_select) against the CPU oracle.
+
+The GPU computes the observation-window logits with bf16 matrix instructions
+and float32 accumulation, the softmax, votes and pooling in float32.  Checks:
+  - its pooled scores (scores_out) against the oracle's float64 ones,
+    |gpu - ref| <= 2e-4 |ref| (float32 accumulation over up to n terms of a
+    row's softmax sum; the reading is in the design doc);
+  - its token lists bit for bit against the oracle's ranking of the GPU's own
+    float32 scores (the decision taken in the kernel's precision);
+  - the kept tokens are a valid top-k of the oracle's float64 scores up to
+    swaps within that tolerance, and the lists hold the sinks, the window,
+    ascending and unique."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from activation_kv_cache_amd import inputs as gen
+
+from gpu_util import dev, host, workspace
+
+pytestmark = pytest.mark.gpu
+RTOL = 2e-4
+
+CASES = [
+    # (name, H, Hkv, D, w_obs, n_cap, n, r_kv, sinks, window, qstd, kstd)
+    ("tiny-g4", 8, 2, 64, 32, 2048, 2048, 0.3, 4, 128, 1.0, 1.0),
+    ("tiny-g4-ragged", 8, 2, 64, 32, 2048, 2000, 0.4, 4, 100, 1.0, 1.0),
+    ("g1-d64", 2, 2, 64, 32, 1024, 1000, 0.3, 4, 64, 1.0, 1.0),
+    ("g2-d128-w16", 8, 4, 128, 16, 4096, 3000, 0.5, 4, 256, 1.0, 1.0),
+    ("g8-d64-256-rows", 16, 2, 64, 32, 4096, 4096, 0.3, 4, 128, 1.0, 1.0),
+    ("short-ctx", 8, 2, 64, 32, 64, 40, 0.5, 4, 4, 1.0, 1.0),
+    ("peaky", 8, 2, 64, 32, 2048, 2048, 0.3, 4, 128, 3.0, 1.0),
+    ("8b-8k-0.3", 32, 8, 128, 32, 8192, 8192, 0.3, 4, 1024, 1.0, 1.0),
+    ("8b-32k-0.5", 32, 8, 128, 32, 32768, 32768, 0.5, 4, 1024, 1.0, 1.0),
+]
+
+
+def _valid(s64, kept_idx, lo, hi, k):
+    kept = np.zeros(s64.size, bool)
+    kept[kept_idx] = True
+    cand = np.zeros(s64.size, bool)
+    cand[lo:hi] = True
+    band = RTOL * np.abs(s64)
+    if k == 0 or kept[cand].all():
+        return True, np.inf
+    margin = (s64[kept] + band[kept]).min() - (s64[cand & ~kept] - band[cand & ~kept]).max()
+    return margin >= 0, margin
+
+
+@pytest.mark.parametrize("name,H,Hkv,D,w_obs,n_cap,n,r_kv,sinks,window,qstd,kstd", CASES, ids=[c[0] for c in CASES])
+def test_snap_select_vs_oracle(name, H, Hkv, D, w_obs, n_cap, n, r_kv, sinks, window, qstd, kstd):
+    from activation_kv_cache_amd import binding as bc
+    q = gen.normal_bf16(61, f"snapq/{name}", (w_obs, H, D), qstd)
+    K = gen.normal_bf16(61, f"snapk/{name}", (Hkv, n_cap, D), kstd)
+    pol = bc.policy(r_kv, sinks, window)
+    t_sel = bc.bc_kv_snap_t_sel(n, pol)
+    bud = oracle.token_budget(n, r_kv, sinks, window)
+    assert t_sel == bud["T_sel"]
+    idx = torch.full((Hkv, t_sel), -1, dtype=torch.int32, device="cuda")
+    scores = torch.full((Hkv, n), float("nan"), dtype=torch.float32, device="cuda")
+    ws = workspace(bc.bc_kv_snap_select_workspace_bytes(n, H, Hkv, w_obs))
+    print(f"[snap] {name}: n={n} T_sel={t_sel} k={bud['k']} rows={w_obs * H // Hkv}", flush=True)
+    bc.bc_kv_snap_select(dev(q), dev(K), n, H, Hkv, pol, idx, scores, ws)
+    torch.cuda.synchronize()
+    s32 = host(scores)
+    ids = host(idx)
+    ref64 = oracle.avg_pool(oracle.snapkv_votes(q, K[:, :n].copy() if n < n_cap else K, n, H, Hkv), 5)
+    err = np.abs(s32.astype(np.float64) - ref64)
+    worst = (err / np.maximum(np.abs(ref64), 1e-300)).max()
+    print(f"[snap] {name}: max relative score error {worst:.3g}", flush=True)
+    assert np.all(err <= RTOL * np.abs(ref64) + 1e-30), f"scores: {(err > RTOL * np.abs(ref64)).sum()} outside"
+    # the ranking of the GPU's own scores, bit for bit
+    assert np.array_equal(ids, oracle.token_select(s32, n, r_kv, sinks, window)), "token lists differ"
+    own = oracle.token_select(ref64.astype(np.float32), n, r_kv, sinks, window)
+    lo, hi = bud["sinks"], n - bud["window"]
+    for g in range(Hkv):
+        row = ids[g]
+        assert np.all(np.diff(row) > 0)
+        assert np.array_equal(row[:bud["sinks"]], np.arange(bud["sinks"]))
+        assert np.array_equal(row[t_sel - bud["window"]:], np.arange(n - bud["window"], n))
+        ok, margin = _valid(ref64[g], row[bud["sinks"]:t_sel - bud["window"]], lo, hi, bud["k"])
+        assert ok, f"head {g}: not a valid top-k of the float64 scores (margin {margin:.3g})"
+    print(f"[snap] {name}: tokens the oracle's own float32 ranking keeps differently: "
+          f"{int((own != ids).sum())} (reported)", flush=True)
+
+
+def test_snap_then_compact_then_dense_attention():
+    """The select-once path end to end: the gathered selection read by the
+    dense attention kernel equals attention over the index list."""
+    from activation_kv_cache_amd import binding as bc
+    H, Hkv, D, w_obs, n = 8, 2, 64, 32, 2048
+    q_obs = gen.normal_bf16(62, "snapq/e2e", (w_obs, H, D))
+    K = gen.normal_bf16(62, "snapk/e2e", (Hkv, n, D))
+    V = gen.normal_bf16(62, "snapv/e2e", (Hkv, n, D))
+    pol = bc.policy(0.3, 4, 128)
+    t_sel = bc.bc_kv_snap_t_sel(n, pol)
+    idx = torch.empty((Hkv, t_sel), dtype=torch.int32, device="cuda")
+    kd, vd = dev(K), dev(V)
+    bc.bc_kv_snap_select(dev(q_obs), kd, n, H, Hkv, pol, idx, None,
+                         workspace(bc.bc_kv_snap_select_workspace_bytes(n, H, Hkv, w_obs)))
+    cap = (t_sel + 15) // 16 * 16
+    kc = torch.zeros((Hkv, cap, D), dtype=torch.int16, device="cuda")
+    vc = torch.zeros_like(kc)
+    bc.bc_kv_compact(kd, vd, idx, t_sel, kc, vc)
+    q = dev(gen.normal_bf16(62, "snapq/step", (H, D)))
+    S = 4
+    outs = []
+    for kk, vv, lst in ((kc, vc, None), (kd, vd, idx)):
+        m = torch.empty((H, S), dtype=torch.float32, device="cuda")
+        l = torch.empty_like(m)
+        o = torch.empty((H, S, D), dtype=torch.float32, device="cuda")
+        bc.bc_splitk_attn_partial(q, kk, vv, lst, t_sel, H, Hkv, S, 1.0 / np.sqrt(D), m, l, o)
+        out = torch.empty((H, D), dtype=torch.int16, device="cuda")
+        bc.bc_splitk_reduce(m, l, o, out)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
