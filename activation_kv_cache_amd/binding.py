@@ -102,6 +102,11 @@ _SIG = {
                                ctypes.POINTER(bc_step), P, P, P, P, c_size_t, P]),
     "bc_decode_step_noalloc": (c_int, [ctypes.POINTER(bc_model_dims), ctypes.POINTER(bc_layer), c_int, P, P,
                                        ctypes.POINTER(bc_step), P, P, P, P]),
+    "bc_layer_batch_workspace_bytes": (c_size_t, [ctypes.POINTER(bc_model_dims), c_int, c_int, c_int]),
+    "bc_decode_layer_batch": (c_int, [ctypes.POINTER(bc_model_dims), ctypes.POINTER(bc_layer), c_int,
+                                      ctypes.POINTER(bc_step), P, P, P, c_size_t, P]),
+    "bc_decode_step_batch": (c_int, [ctypes.POINTER(bc_model_dims), ctypes.POINTER(bc_layer), c_int, c_int, P, P,
+                                     ctypes.POINTER(bc_step), P, P, P, P, c_size_t, P]),
     "bc_lm_head": (c_int, [ctypes.POINTER(bc_model_dims), P, P, P, P, P, c_double, P, c_size_t, P]),
 }
 for _name, (_res, _args) in _SIG.items():
@@ -389,3 +394,32 @@ def bc_decode_step_noalloc(md: bc_model_dims, layer_array, g_final, w_head, step
     return _check(_lib.bc_decode_step_noalloc(ctypes.byref(md), layer_array, len(layer_array), _ptr(g_final),
                                               _ptr(w_head), ctypes.byref(step), _ptr(hidden), _ptr(logits),
                                               _ptr(token), _stream(stream)), "bc_decode_step_noalloc")
+
+
+def bc_layer_batch_workspace_bytes(md: bc_model_dims, batch: int, max_ctx: int, max_splits: int) -> int:
+    return _lib.bc_layer_batch_workspace_bytes(ctypes.byref(md), int(batch), int(max_ctx), int(max_splits))
+
+
+def make_taps_array(taps):
+    arr = (bc_layer_taps * len(taps))()
+    for i, t in enumerate(taps):
+        arr[i] = t
+    return arr
+
+
+def bc_decode_layer_batch(md: bc_model_dims, layer_array, step: bc_step, hidden, ws, taps_array=None, stream=None):
+    """layer_array: bc_layer per sequence (shared weights, own caches);
+    hidden [batch][d]."""
+    p, n = _ws(ws)
+    tp = ctypes.cast(taps_array, c_void_p) if taps_array is not None else None
+    return _check(_lib.bc_decode_layer_batch(ctypes.byref(md), layer_array, len(layer_array), ctypes.byref(step),
+                                             _ptr(hidden), tp, p, n, _stream(stream)), "bc_decode_layer_batch")
+
+
+def bc_decode_step_batch(md: bc_model_dims, layer_array, n_layers: int, batch: int, g_final, w_head, step: bc_step,
+                         hidden, logits, tokens, ws, stream=None):
+    """layer_array: [n_layers * batch] bc_layer, layer-major."""
+    p, n = _ws(ws)
+    return _check(_lib.bc_decode_step_batch(ctypes.byref(md), layer_array, int(n_layers), int(batch), _ptr(g_final),
+                                            _ptr(w_head), ctypes.byref(step), _ptr(hidden), _ptr(logits),
+                                            _ptr(tokens), p, n, _stream(stream)), "bc_decode_step_batch")

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbc.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["bc_gemv.hip", "bc_gemv_batch.hip", "bc_attn.hip", "bc_kv.hip", "bc_snap.hip", "bc_masked.hip", "bc_layer.hip"]
+SOURCES = ["bc_gemv.hip", "bc_gemv_batch.hip", "bc_attn.hip", "bc_kv.hip", "bc_snap.hip", "bc_masked.hip", "bc_batch.hip", "bc_layer.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-ffp-contract=fast", "-munsafe-fp-atomics"]

@@ -616,8 +616,11 @@ constexpr int kOneGroup = 1024;
 // ascending list is staged in LDS and stored with coalesced writes.  Larger
 // inputs take the 4-bit radix select over keys read from memory.
 template <int PMAX>
-__global__ __launch_bounds__(kOneGroup) void k_select_reg(const uint16_t* x, int n, int k, int32_t* idx_out) {
+__global__ __launch_bounds__(kOneGroup) void k_select_reg(const uint16_t* x, int n, int k, int32_t* idx_out,
+                                                          int x_stride) {
   __shared__ Topk2Smem<kOneGroup, kTopkShift> tk;
+  x += size_t(blockIdx.x) * x_stride;       // one work-group per sequence of a batch
+  idx_out += size_t(blockIdx.x) * k;
   __shared__ int32_t list[kOneGroup * PMAX];
   const int P = ((n + kOneGroup - 1) / kOneGroup + 3) & ~3;
   const int c0 = int(threadIdx.x) * P;
@@ -648,8 +651,11 @@ __global__ __launch_bounds__(kOneGroup) void k_select_reg(const uint16_t* x, int
   for (int i = threadIdx.x; i < k; i += kOneGroup) idx_out[i] = list[i];
 }
 
-__global__ __launch_bounds__(kOneGroup) void k_select(const uint16_t* x, int n, int k, int32_t* idx_out) {
+__global__ __launch_bounds__(kOneGroup) void k_select(const uint16_t* x, int n, int k, int32_t* idx_out,
+                                                      int x_stride) {
   __shared__ TopkSmem<kOneGroup, uint16_t> sm;
+  x += size_t(blockIdx.x) * x_stride;
+  idx_out += size_t(blockIdx.x) * k;
   auto key = [x](int i) -> uint32_t { return uint32_t(x[i]) & 0x7FFFu; };
   auto emit = [idx_out](int r, int i) { idx_out[r] = i; };
   block_topk<kOneGroup, 15, uint16_t>(n, k, key, emit, sm);
@@ -768,14 +774,19 @@ int launch_argmax_finish(const float* tile_max, const int32_t* tile_arg, int n_t
   return check_launch("k_argmax_finish");
 }
 
-int launch_select(const uint16_t* x, int n, int k, int32_t* idx_out, hipStream_t s) {
+int launch_select_batch(const uint16_t* x, int n, int k, int32_t* idx_out, int batch, int x_stride, hipStream_t s) {
+  const dim3 grid{unsigned(batch)};
   if (n <= kOneGroup * 4)
-    k_select_reg<4><<<1, kOneGroup, 0, s>>>(x, n, k, idx_out);
+    k_select_reg<4><<<grid, kOneGroup, 0, s>>>(x, n, k, idx_out, x_stride);
   else if (n <= kOneGroup * 16)
-    k_select_reg<16><<<1, kOneGroup, 0, s>>>(x, n, k, idx_out);
+    k_select_reg<16><<<grid, kOneGroup, 0, s>>>(x, n, k, idx_out, x_stride);
   else
-    k_select<<<1, kOneGroup, 0, s>>>(x, n, k, idx_out);
+    k_select<<<grid, kOneGroup, 0, s>>>(x, n, k, idx_out, x_stride);
   return check_launch("k_select");
+}
+
+int launch_select(const uint16_t* x, int n, int k, int32_t* idx_out, hipStream_t s) {
+  return launch_select_batch(x, n, k, idx_out, 1, n, s);
 }
 
 }  // namespace bc

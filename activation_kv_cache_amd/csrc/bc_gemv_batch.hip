@@ -48,7 +48,8 @@ struct BatchParams {
   int32_t* counts;        // [n_splits] rows of U per range (workspace)
   int32_t* count_out;     // optional |U|
   float* partial;         // [n_splits][nb][d_out] when n_splits > 1
-  uint16_t* y;            // [nb][d_out]
+  uint16_t* y;            // [nb][d_out] bf16, or
+  float* yf;              // [nb][d_out] fp32 (when y is NULL)
 };
 
 struct BatchPlan {
@@ -208,8 +209,10 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_batch(const BatchParams p
   __syncthreads();
 
   auto store = [&](int b, int c, float v) {
-    if (p.n_splits == 1)
+    if (p.n_splits == 1 && p.y)
       p.y[size_t(b) * p.d_out + tile * kGemvTile + c] = f32_to_bf16(v);
+    else if (p.n_splits == 1)
+      p.yf[size_t(b) * p.d_out + tile * kGemvTile + c] = v;
     else
       p.partial[(size_t(split) * NB + b) * p.d_out + tile * kGemvTile + c] = v;
   };
@@ -293,7 +296,10 @@ __global__ __launch_bounds__(256) void k_batch_finish(const BatchParams p) {
   for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += size_t(gridDim.x) * 256) {
     float v = 0.f;
     for (int s = 0; s < p.n_splits; ++s) v += p.partial[size_t(s) * n + i];
-    p.y[i] = f32_to_bf16(v);
+    if (p.y)
+      p.y[i] = f32_to_bf16(v);
+    else
+      p.yf[i] = v;
   }
 }
 
@@ -342,10 +348,17 @@ extern "C" int bc_sparse_gemv_batch(const uint16_t* wt, int tiled, int d_in, int
     return set_error(BC_ERR_INVALID, "%s: wt and ws must be 16-byte aligned", name);
   if (!tiled && size_t(d_in) * size_t(d_out) > 0xFFFFFFFFull)
     return set_error(BC_ERR_UNSUPPORTED, "%s: row-major W^T of %d x %d (use the tiled layout)", name, d_in, d_out);
+  return run_gemv_batch(wt, tiled, d_in, d_out, x, idx, k, batch, y, nullptr, n_union_out, ws, ws_bytes,
+                        static_cast<hipStream_t>(stream));
+}
+
+int bc::run_gemv_batch(const uint16_t* wt, int tiled, int d_in, int d_out, const uint16_t* x, const int32_t* idx,
+                       int k, int batch, uint16_t* y, float* yf, int32_t* n_union_out, void* ws, size_t ws_bytes,
+                       hipStream_t s) {
+  const char* name = "batched GEMV";
   const BatchPlan pl = plan_batch(d_in, d_out, batch);
   if (!ws || ws_bytes < pl.bytes)
     return set_error(BC_ERR_WORKSPACE, "%s: workspace %zu < %zu", name, ws_bytes, pl.bytes);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   BatchParams p{};
   p.wt = wt; p.tiled = tiled ? 1 : 0; p.d_in = d_in; p.d_out = d_out; p.k = k; p.nb = batch;
@@ -354,6 +367,7 @@ extern "C" int bc_sparse_gemv_batch(const uint16_t* wt, int tiled, int d_in, int
   p.count_out = n_union_out;
   p.partial = pl.n_splits > 1 ? reinterpret_cast<float*>(w + pl.off_part) : nullptr;
   p.y = y;
+  p.yf = yf;
   const dim3 grid(pl.n_tiles, pl.n_splits);
   switch (batch) {
     case 1: launch_batch_nb<1>(p, grid, s); break;

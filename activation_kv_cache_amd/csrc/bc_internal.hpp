@@ -215,6 +215,12 @@ int launch_masked_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_
                        hipStream_t s);
 
 int launch_select(const uint16_t* x, int n, int k, int32_t* idx_out, hipStream_t s);
+// one selection per sequence of a batch: x [batch][x_stride], idx_out [batch][k]
+int launch_select_batch(const uint16_t* x, int n, int k, int32_t* idx_out, int batch, int x_stride, hipStream_t s);
+// the batched union GEMV (bc_gemv_batch.hip) without the ABI checks: bf16 y
+// or (y == NULL) fp32 yf [batch][d_out]
+int run_gemv_batch(const uint16_t* wt, int tiled, int d_in, int d_out, const uint16_t* x, const int32_t* idx, int k,
+                   int batch, uint16_t* y, float* yf, int32_t* n_union_out, void* ws, size_t ws_bytes, hipStream_t s);
 int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 
 bool valid_head_dim(int hd);

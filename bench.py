@@ -321,6 +321,7 @@ class Model:
         D = DIMS
         d, dff, H, Hkv, hd, L = D["d"], D["d_ff"], D["n_heads"], D["n_kv_heads"], D["head_dim"], D["n_layers"]
         self.max_ctx = max_ctx
+        self.masked_ws = None
         self.md = bc.dims(D)
         t0 = time.time()
         one = torch.full((d,), 1.0, dtype=torch.bfloat16, device="cuda").view(torch.int16)
@@ -386,20 +387,24 @@ class Model:
         S = bc.bc_attn_default_splits(t_sel, DIMS["n_kv_heads"])
         return pol, t_sel, S
 
-    def step(self, n, r_p, r_kv, window=WINDOW):
+    def step(self, n, r_p, r_kv, window=WINDOW, masked=False):
         bc = self.bc
         pol, _, S = self.plan(n, r_p, r_kv, window)
-        st = bc.make_step(n, r_p, pol, S)
+        if masked and self.masked_ws is None:
+            D = DIMS
+            self.masked_ws = torch.empty(bc.bc_masked_attn_workspace_bytes(self.max_ctx, D["n_heads"], D["head_dim"])
+                                         // 4 + 64, dtype=torch.int32, device="cuda")
+        st = bc.make_step(n, r_p, pol, S, masked_ws=self.masked_ws if masked else None)
         self.h.copy_(self.h0)
         bc.bc_decode_step(self.md, self.layer_array, self.g_final, self.w_head, st, self.h, self.logits, self.token,
                           self.ws)
 
-    def graph(self, n, r_p, r_kv, window=WINDOW):
-        self.step(n, r_p, r_kv, window)          # eager once: validates arguments outside capture
+    def graph(self, n, r_p, r_kv, window=WINDOW, masked=False):
+        self.step(n, r_p, r_kv, window, masked)          # eager once: validates arguments outside capture
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.step(n, r_p, r_kv, window)
+            self.step(n, r_p, r_kv, window, masked)
         torch.cuda.synchronize()
         return g
 
@@ -738,6 +743,111 @@ def time_batch_gemv(model, batch, r_p=0.5, which="w_gu", reps=3, seed=0):
             "crossover_batch_k": {str(r): round(batch_crossover_k(n_union / d_in, r, batch), 2) for r in (0.3, 0.5)}}
 
 
+BATCH_SWEEPS = {2: [4096 * i for i in range(1, 11)], 4: [1024, 2048, 3072, 4096, 6144, 8192, 10240]}
+
+
+def batch_crossover(model, B, contexts, steps, warmup, blocks=2, r_p=0.5, r_kv=0.3, seed=3):
+    """A batch of B sequences sharing the weights (README "Quick start" /
+    "Usage": crossover_batch): whole batched decode steps (bc_decode_step_batch:
+    32 layers, the projections read once for the union of the sequences'
+    channel lists, each sequence's own cache) in three modes -- dense, the
+    projection branch (r_p) and the rescored KV branch (r_kv) -- at every
+    context, in `blocks` shuffled blocks.  The crossing of the two branches'
+    speedups over the batched dense step is compared with crossover_batch at
+    the union keep measured on layer 0's channel lists (its GEMVs weighted by
+    their weight bytes)."""
+    bc = model.bc
+    from activation_kv_cache_amd import inputs as gen
+    D = DIMS
+    d, dff, H, Hkv, hd, L = D["d"], D["d_ff"], D["n_heads"], D["n_kv_heads"], D["head_dim"], D["n_layers"]
+    n_cap = max(contexts)
+    caches = []
+    for li in range(L):
+        row = []
+        for b in range(B):
+            k = gen.device_normal_bf16(seed, f"batch{b}/layer{li}/kcache", (Hkv, n_cap, hd), 1.0)
+            v = gen.device_normal_bf16(seed, f"batch{b}/layer{li}/vcache", (Hkv, n_cap, hd), 1.0)
+            summ = torch.empty((Hkv, n_cap // 16, hd, 2), dtype=torch.int16, device="cuda")
+            bc.bc_build_kv_summary(k, n_cap, summ)
+            row.append((k, v, summ))
+        caches.append(row)
+    lys = [bc.make_layer(model.layers[li]["w_qkv"], model.layers[li]["w_o"], model.layers[li]["w_gu"],
+                         model.layers[li]["w_down"], model.g_attn, model.g_mlp, *caches[li][b])
+           for li in range(L) for b in range(B)]
+    arr = bc.make_layer_array(lys)
+    h0 = torch.from_numpy(np.stack([gen.activation_bf16(seed, f"batchh/{b}", d) for b in range(B)])
+                          .view(np.int16)).cuda()
+    hid = torch.empty_like(h0)
+    logits = torch.empty((B, D["vocab"]), dtype=torch.float32, device="cuda")
+    tok = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws = torch.empty(bc.bc_layer_batch_workspace_bytes(model.md, B, n_cap, 64) // 4 + 64, dtype=torch.int32,
+                     device="cuda")
+    bc.bc_workspace_init(ws)
+
+    # union keep of each GEMV input on layer 0 (channel lists from the taps)
+    n0 = contexts[0]
+    k_d, k_ff = channel_keep(r_p, d), channel_keep(r_p, dff)
+    taps = [{k: torch.empty(m, dtype=torch.int32, device="cuda") for k, m in
+             (("idx_qkv", k_d), ("idx_o", k_d), ("idx_gu", k_d), ("idx_down", k_ff))} for _ in range(B)]
+    tarr = bc.make_taps_array([bc.make_taps(**t) for t in taps])
+    hid.copy_(h0)
+    bc.bc_decode_layer_batch(model.md, bc.make_layer_array(lys[:B]), bc.make_step(n0, r_p, bc.policy(1.0)), hid, ws,
+                             taps_array=tarr)
+    torch.cuda.synchronize()
+    kvd = Hkv * hd
+    wbytes = {"idx_qkv": (d, d * (H * hd + 2 * kvd)), "idx_o": (H * hd, H * hd * d), "idx_gu": (d, d * 2 * dff),
+              "idx_down": (dff, dff * d)}
+    union = {}
+    for key, (d_in, w) in wbytes.items():
+        u = np.unique(np.concatenate([t[key].cpu().numpy() for t in taps]))
+        union[key] = u.size / d_in
+    u_eff = sum(union[k] * wbytes[k][1] for k in wbytes) / sum(w for _, w in wbytes.values())
+
+    modes = {"dense": (1.0, 1.0), "proj": (r_p, 1.0), "kv": (1.0, r_kv)}
+
+    def graph(n, rp, rk):
+        st = bc.make_step(n, rp, bc.policy(rk, SINKS, WINDOW), 0)
+
+        def run():
+            hid.copy_(h0)
+            bc.bc_decode_step_batch(model.md, arr, L, B, model.g_final, model.w_head, st, hid, logits, tok, ws)
+        run()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        torch.cuda.synchronize()
+        return g
+
+    rng = np.random.default_rng(seed)
+    cells = [(m, n) for m in modes for n in contexts]
+    t = {m: np.zeros((blocks, len(contexts))) for m in modes}
+    for blk in range(blocks):
+        for ci in rng.permutation(len(cells)):
+            m, n = cells[ci]
+            g = graph(n, *modes[m])
+            t[m][blk, contexts.index(n)] = time_graph(g, steps, warmup) * 1000.0
+            del g
+    sp = {m: (t["dense"] / t[m]).mean(axis=0) for m in ("proj", "kv")}
+    c = crossing_k(contexts, [float(x) for x in sp["proj"] - sp["kv"]])
+    pred = batch_crossover_k(u_eff, r_kv, B)
+    kv_per_token = 2 * 2 * L * kvd
+    w_proj = 2 * L * (2 * d * d + 2 * d * kvd + 3 * d * dff)
+    pred_ext = (1 - u_eff) * w_proj / ((1 - r_kv - 1.0 / 16) * B * kv_per_token) / 1024
+    rec = {"batch": B, "r_p": r_p, "r_kv": r_kv, "contexts": contexts, "blocks": blocks,
+           "union_keep": {k: round(v, 4) for k, v in union.items()}, "union_keep_weighted": round(u_eff, 4),
+           "step_us": {m: [round(x, 1) for x in t[m].mean(axis=0)] for m in modes},
+           "speedup": {m: [round(x, 4) for x in sp[m]] for m in sp},
+           "measured_k": None if c is None else round(c, 2), "crossover_batch_k": round(pred, 2),
+           "crossover_batch_ext_k": round(pred_ext, 2)}
+    log(f"[bench] batch {B}: union keep {u_eff:.3f}; crossing of the projection (r_p {r_p}) and KV (r_kv {r_kv}) "
+        f"branches {rec['measured_k']}K, crossover_batch {pred:.1f}K (with the scored summaries {pred_ext:.1f}K); "
+        f"dense step {rec['step_us']['dense'][0]} us at {contexts[0]}")
+    del caches, lys, arr, ws
+    torch.cuda.empty_cache()
+    return rec
+
+
 def load_traffic(n):
     """HBM bytes per launch of the attention kernel from the committed
     rocprofv3 counter summary, or None when the kernel sources changed since
@@ -772,6 +882,36 @@ def load_step_bytes():
     return {"source": "profiles/decode_step_bytes_pmc.json", "kernel_sources_unchanged": cur, "modes": modes,
             "summary": {f"{m['mode']}@{m['context']}": [m["measured_over_algorithmic"], m["measured_over_page_account"]]
                         for m in modes} if cur else None}
+
+
+def masked_comparison(n, steps, warmup):
+    """The KV-window cell against two dense baselines (README FAQ "A KV method
+    reports a speedup above its byte bound", paper Section 4.4; the
+    abstract's "about fivefold"): the dense step with split-K attention and
+    the dense step with masked attention (bc_masked_attn), all three on one
+    model whose cache holds exactly n tokens (the masked baseline scans the
+    whole cache).  Returns the record and frees the model."""
+    model = Model(max_ctx=n, seed=2)
+    t = {}
+    for key, (r_p, r_kv, win, masked) in {"dense_splitk": (1.0, 1.0, WINDOW, False),
+                                          "dense_masked": (1.0, 1.0, WINDOW, True),
+                                          "kv_window_0.3": (1.0, 0.3, n, False)}.items():
+        g = model.graph(n, r_p, r_kv, win, masked)
+        t[key] = time_graph(g, steps, warmup) * 1000.0
+        del g
+    del model
+    torch.cuda.empty_cache()
+    bound = byte_bound(n, 1.0, 0.3)
+    rec = {"context": n, "cache_slots": n, "step_us": {k: round(v, 1) for k, v in t.items()},
+           "window_speedup_vs_splitk": round(t["dense_splitk"] / t["kv_window_0.3"], 3),
+           "window_speedup_vs_masked": round(t["dense_masked"] / t["kv_window_0.3"], 3),
+           "inflation": round(t["dense_masked"] / t["dense_splitk"], 3), "byte_bound": round(bound, 4)}
+    rec["summary"] = {k: rec[k] for k in ("window_speedup_vs_splitk", "window_speedup_vs_masked", "inflation",
+                                          "byte_bound")}
+    log(f"[bench] KV window (r_kv 0.3) at {n}: {rec['window_speedup_vs_splitk']}x the split-K dense step, "
+        f"{rec['window_speedup_vs_masked']}x the masked-attention dense step (inflation {rec['inflation']}x; "
+        f"byte bound {bound:.2f}x); steps {rec['step_us']}")
+    return rec
 
 
 def cpu_baseline(model, n):
@@ -1113,6 +1253,8 @@ def main():
     ap.add_argument("--crossover-blocks", type=int, default=4,
                     help="blocks of the crossover sweep (every mode at 2K, 4K, ..., 128K); 0 skips it")
     ap.add_argument("--crossover-steps", type=int, default=10, help="timed steps per sweep cell")
+    ap.add_argument("--batch-sweep", type=int, default=1,
+                    help="1: also time batched steps (2 and 4 sequences) and locate their crossing (0 skips it)")
     ap.add_argument("--calib-blocks", type=int, default=2,
                     help="blocks of the separate calibration sweep the cost-aware prediction is fitted on")
     ap.add_argument("--crossover-max-k", type=int, default=160,
@@ -1351,6 +1493,16 @@ def main():
         calib = calibration_sweep(model, args.calib_blocks, args.crossover_steps, min(args.warmup, 3))
         out["crossover"] = crossover_sweep(model, sweep_ctx, args.crossover_blocks, args.crossover_steps,
                                            min(args.warmup, 3), calib=calib)
+    if sweep and args.batch_sweep:
+        out["batch_step"] = {"runs": [batch_crossover(model, B, BATCH_SWEEPS[B], args.crossover_steps,
+                                                      min(args.warmup, 3)) for B in (2, 4)]}
+        out["batch_step"]["summary"] = {f"b{r['batch']}": [r["measured_k"], r["crossover_batch_k"],
+                                                          r["crossover_batch_ext_k"], r["union_keep_weighted"]]
+                                        for r in out["batch_step"]["runs"]}
+    if args.cells == "default" and head_n >= 131072:
+        # on a model of its own (cache of exactly head_n slots), after the
+        # headline cells
+        out["masked_baseline"] = masked_comparison(head_n, min(args.steps, 10), args.warmup)
     if not args.no_cpu_baseline:
         try:
             out["cpu_baseline"] = cpu_baseline(model, head_n)

@@ -384,6 +384,34 @@ int bc_decode_step_noalloc(const bc_model_dims* dims, const bc_layer* layers, in
                            const uint16_t* w_head, const bc_step* st, uint16_t* hidden, float* logits,
                            int32_t* token, void* stream);
 
+/* A batch of up to four sequences that share the weights (README "Quick
+ * start" and "Usage": crossover_batch -- a batch reads the projection
+ * weights once for the union of the channels its sequences keep, and the
+ * key-value bytes once per sequence).  layers[b] (b < batch) holds the
+ * shared weights (every entry the same pointers) and sequence b's own cache
+ * and summaries; every sequence attends to step->n_ctx tokens.  Per
+ * sequence the layer computes what bc_decode_layer does (its own channel
+ * selections, rotary, append, KV selection and attention), with the
+ * projections of the whole batch read through one union GEMV each
+ * (bc_sparse_gemv_batch): hidden [batch][d] in and out.  Every value is
+ * rounded to bf16 where bc_decode_layer rounds it (the projections hand fp32
+ * sums on), so results equal bc_decode_layer's up to the fp32 order of the
+ * sums over the kept channels.  taps: NULL or [batch] (attn_m/l/o are not
+ * written).
+ * step->masked_ws must be NULL.  ws from bc_layer_batch_workspace_bytes. */
+size_t bc_layer_batch_workspace_bytes(const bc_model_dims* dims, int batch, int max_ctx, int max_splits);
+int bc_decode_layer_batch(const bc_model_dims* dims, const bc_layer* layers, int batch, const bc_step* step,
+                          uint16_t* hidden, const bc_layer_taps* taps, void* ws, size_t ws_bytes, void* stream);
+
+/* A whole decode step for a batch: layers [n_layers][batch] (layer-major),
+ * then per sequence the final RMSNorm and the dense LM head (its weights
+ * read once for the batch), logits fp32 [batch][vocab], tokens [batch]
+ * (argmax, lowest index on ties).  ws from bc_layer_batch_workspace_bytes
+ * with the same dims (vocab included). */
+int bc_decode_step_batch(const bc_model_dims* dims, const bc_layer* layers, int n_layers, int batch,
+                         const uint16_t* g_final, const uint16_t* w_head, const bc_step* step, uint16_t* hidden,
+                         float* logits, int32_t* tokens, void* ws, size_t ws_bytes, void* stream);
+
 /* Tile-major re-layout of a W^T matrix for bc_decode_layer and bc_lm_head
  * (setup, not timed): the columns are cut into tiles of 128 (the last one
  * narrower, w_t columns); tile t stores its d_in rows contiguously, row i at
