@@ -1,8 +1,8 @@
 // bc_attn.hip -- split-K grouped-query decode attention for gfx950.
 //
-// README "Overview": dense and sparse modes read their caches through the
-// same split-K attention kernel, so the dense baseline stays fixed.  Here the
-// dense mode is the same kernel with idx == NULL.
+// README "Overview": one split-K attention kernel serves the dense mode and
+// every sparse mode, which keeps the dense reference from moving with the
+// mode.  Here the dense mode is the same kernel with idx == NULL.
 //
 // Partial pass: one work-group per (split, KV head).  A key (value) row is
 // head_dim bf16 = 256 B at head_dim 128; a group of 8 lanes holds one row,

@@ -1,7 +1,7 @@
 // bc_kv.hip -- attention-scored KV selection for gfx950.
 //
-// README "What it does in one picture": an attention-scored selection keeps
-// sinks, part of the history and the recent KV entries.  History is scored
+// README "What it does in one picture": the selection, scored by attention,
+// keeps the first tokens, a share of the older history and the newest tokens.  History is scored
 // per 16-token block with an upper bound of the query-key product built from
 // the block's per-dimension key minima and maxima (the query-aware block
 // bound of Quest, one of the paper's listed ancestors), summed over the

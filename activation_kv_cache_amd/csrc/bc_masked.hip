@@ -1,9 +1,9 @@
 // bc_masked.hip -- the masked-attention dense baseline, for gfx950.
 //
-// README FAQ "A KV method reports a speedup above its byte bound": timing the
-// dense baseline with masked attention instead of split-K attention inflates
-// the apparent speedup of a KV policy (the abstract puts it at about five
-// times).  This is that baseline: decode attention computed the way a plain
+// README FAQ "A KV method reports a speedup above its byte bound": measured
+// against a dense step whose attention is masked rather than split-K, a KV
+// policy looks several times faster than it is (the abstract: near five).
+// This is that baseline: decode attention computed the way a plain
 // masked attention does it over a preallocated cache -- scores of every query
 // head against every slot of the cache, a mask of -inf on the slots past the
 // context, a softmax over the whole row, then the weighted sum of every value

@@ -428,7 +428,7 @@ class Model:
 
     def sel_prepare(self, n, r_kv):
         """Select once and gather (not timed; README FAQ: the KV branch
-        follows SnapKV with one selection after prefill): every layer scores
+        selects once after prefill, in SnapKV's way): every layer scores
         the tokens of its pre-filled cache by the pooled attention of its
         observation window (bc_kv_snap_select) and copies the kept tokens
         (sinks, history, window -- the last one being position n-1) into its
@@ -1027,8 +1027,9 @@ def time_cells(model, cells, steps, warmup, rng):
 
 def calibration_sweep(model, blocks, steps, warmup, seed=1, contexts=None):
     """The branches' own sweeps for the cost-aware prediction (README
-    "Results", paper Table 2: the kernel cost of each branch taken from
-    separate sweeps): dense and every single-branch mode at a few contexts,
+    "Results", paper Table 2: each branch's kernel cost comes from sweeps
+    other than the one whose crossing is predicted): dense and every
+    single-branch mode at a few contexts,
     in blocks of their own, timed before and apart from the crossover
     blocks whose crossings the prediction is compared with.  Returns the
     mean step time per mode over the blocks, [contexts]."""

@@ -54,8 +54,8 @@ typedef struct {
   int n_layers, d, d_ff, vocab, n_heads, n_kv_heads, head_dim;
 } bc_model_dims;
 
-/* KV policy (README "What it does in one picture": the selection keeps
- * sinks, part of the history and the recent entries).  r_kv >= 1 reads the
+/* KV policy (README "What it does in one picture": the kept entries are the
+ * first tokens, a share of the older history and the newest tokens).  r_kv >= 1 reads the
  * whole cache.  block must be 16 (the summary granularity). */
 typedef struct {
   double r_kv;
@@ -143,8 +143,9 @@ int bc_sparse_gemv_batch(const uint16_t* wt, int tiled, int d_in, int d_out, con
                          int k, int batch, uint16_t* y, int32_t* n_union_out, void* ws, size_t ws_bytes,
                          void* stream);
 
-/* a4. Attention-scored KV selection (README "What it does": sinks, part of
- * the history and the recent entries), scored per 16-token block by an upper
+/* a4. Attention-scored KV selection (README "What it does in one picture":
+ * the first tokens, a share of the older history and the newest tokens are
+ * kept), the history scored per 16-token block by an upper
  * bound of the query-key product built from per-block key minima and maxima.
  * For KV head g and candidate block b (see bc_kv_budget_info), with the
  * group's query heads j:
@@ -179,7 +180,7 @@ int bc_build_kv_summary(const uint16_t* k_cache, int n_kv_heads, int n_cap, int 
                         uint16_t* summary, void* stream);
 
 /* a4 (select once).  The README's timing harness also runs the KV branch as
- * "sel": the scored selection made once, gathered into one contiguous buffer
+ * "sel": the scored selection made once and copied into a buffer of its own
  * and then read by the same dense attention kernel every step (README
  * "Timing and quality on a GPU"; "API at a glance": select_and_compact).
  * This is the gather: for every KV head g and t < t_sel,
@@ -228,8 +229,8 @@ int bc_kv_snap_select(const uint16_t* q_obs, int w_obs, const uint16_t* k_cache,
                       int n_kv_heads, int head_dim, const bc_kv_policy* pol, int pool_kernel, int32_t* idx_out,
                       float* scores_out, void* ws, size_t ws_bytes, void* stream);
 
-/* a5. Split-K decode attention, partial pass (README "Overview": dense and
- * sparse modes read their caches through the same split-K kernel).  For
+/* a5. Split-K decode attention, partial pass (README "Overview": one split-K
+ * kernel serves the dense and every sparse mode).  For
  * query head j (KV head g = j / (n_heads/n_kv_heads)) and split s covering
  * list positions [s*c, min(n_sel, (s+1)*c)), c = ceil(n_sel/n_splits):
  *   z_t = scale * (q_j . k_t); m = max z; l = sum e^(z-m); o = sum e^(z-m) v_t
@@ -255,9 +256,9 @@ int bc_splitk_reduce(const float* m, const float* l, const float* o, int n_heads
                      int head_dim, uint16_t* out, void* stream);
 
 /* The masked-attention dense baseline (README FAQ "A KV method reports a
- * speedup above its byte bound": timing the dense baseline with masked rather
- * than split-K attention inflates a KV policy's apparent speedup; the
- * abstract: about fivefold).  Decode attention as a plain masked attention
+ * speedup above its byte bound": a dense baseline built on masked attention
+ * makes a KV policy look faster than one built on split-K attention does; the
+ * abstract puts the factor near five).  Decode attention as a plain masked attention
  * over a preallocated cache computes it, for every query head j (KV head
  * g = j / (n_heads/n_kv_heads)):
  *   z_t = scale * (q_j . k_t) for every cache slot t < n_cap, -inf for

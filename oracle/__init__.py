@@ -218,7 +218,7 @@ def kv_select(q, summ, n: int, n_heads: int, n_kv_heads: int, r_kv: float,
 
 
 def kv_compact(K, V, idx, n_cap_out: int):
-    """The scored selection gathered into one contiguous buffer (README
+    """The scored selection copied into a buffer of its own, in list order (README
     "Timing and quality on a GPU": the sel mode; "API at a glance":
     select_and_compact): row t of head g of the output is row idx[g][t] of the
     cache.  K, V [Hkv][n_cap][D] bf16; idx [Hkv][T_sel] -> ([Hkv][n_cap_out][D]) x 2,

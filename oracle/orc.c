@@ -81,8 +81,8 @@ void orc_bf16_from_double_array(const double* in, uint16_t* out, long n)
 
 /* ------------------------------------------------------------------------ */
 /* Channel selection (README "What it does in one picture" and "Timing and
- * quality on a GPU": the activations of each token select the projection
- * weights that are read; TEAL on all seven projections).  Read here as the
+ * quality on a GPU": a token's own activations decide which projection
+ * weights are read; TEAL on all seven projections).  Read here as the
  * exact per-step top-k of |x|: the key of channel i is its bf16 magnitude
  * bits, larger key first, equal keys by lower index; k channels are kept and
  * reported in ascending channel order.                                       */
@@ -229,8 +229,9 @@ void orc_kv_summary(const uint16_t* k, int n, int D, uint16_t* out)
 }
 
 /* ------------------------------------------------------------------------ */
-/* KV budget (README "What it does": sinks, part of the history and the recent
- * entries; block size 16).  T = min(n, floor(r_kv*n + 1/2)); sinks
+/* KV budget (README "What it does in one picture": the kept entries are the
+ * first tokens, a share of the older history and the newest tokens; block
+ * size 16).  T = min(n, floor(r_kv*n + 1/2)); sinks
  * S' = min(sinks, T); window W' = min(window, T - S'); whole 16-token blocks
  * fill the rest: k_blk = floor((T - S' - W') / 16), capped by the number of
  * candidate blocks, which are the aligned blocks lying wholly in [S', n - W').

@@ -1,6 +1,6 @@
 """Pins of the oracle's select-once policy in the SnapKV form (README FAQ
-"How is this different from TEAL and SnapKV?": the KV branch follows SnapKV
-with one selection after prefill): attention votes of an observation window
+"How is this different from TEAL and SnapKV?": the KV branch selects once,
+after prefill, the way SnapKV does): attention votes of an observation window
 of queries, average pooling over neighbouring tokens, per-KV-head top-k.
 
 The pins check the oracle against what the definition fixes without
