@@ -508,10 +508,53 @@ def time_read_probe(model, nbytes=512 << 20, reps=10, pool=1 << 30):
     return us, nbytes
 
 
+def replay_us(one_pass, launches, reps):
+    """Per-launch time of `one_pass` (a pass of `launches` library calls on
+    the current stream), replayed `reps` times from one HIP graph: what the
+    GPU spends per launch back to back, with no host launch cost in it.  The
+    pass runs once eagerly first (argument checks outside capture)."""
+    one_pass()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        one_pass()
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        g.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / (reps * launches)
+    del g
+    return us
+
+
+def stream_us(one_pass, launches, reps):
+    """Per-launch time of `one_pass` (a pass of `launches` library calls)
+    launched `reps` times from the host onto the current stream, after one
+    untimed pass, timed with events on that stream."""
+    one_pass()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        one_pass()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / (reps * launches)
+
+
 def time_attention_kernel(model, n, reps=3, S=None):
     """Average duration of bc_splitk_attn_partial over the 32 layers' caches
     (one launch per layer, as in the step), timed with events on the stream
-    the kernels are launched on."""
+    the kernels are launched on.  Launched from the host: each launch outlasts
+    the host's launch cost, and stream launches sit closer together than the
+    nodes of a graph replay, so the time per launch stays close to the
+    kernel's own duration in a kernel trace."""
     bc = model.bc
     D = DIMS
     H, Hkv, hd = D["n_heads"], D["n_kv_heads"], D["head_dim"]
@@ -521,18 +564,11 @@ def time_attention_kernel(model, n, reps=3, S=None):
     l = torch.empty_like(m)
     o = torch.empty((H, S, hd), dtype=torch.float32, device="cuda")
     scale = 1.0 / math.sqrt(hd)
-    for ly in model.layers[:4]:
-        bc.bc_splitk_attn_partial(q, ly["k"], ly["v"], None, n, H, Hkv, S, scale, m, l, o)
-    torch.cuda.synchronize()
-    s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(reps):
+
+    def one_pass():
         for ly in model.layers:
             bc.bc_splitk_attn_partial(q, ly["k"], ly["v"], None, n, H, Hkv, S, scale, m, l, o)
-    e1.record(s)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1000.0 / (reps * len(model.layers))
+    us = stream_us(one_pass, len(model.layers), reps)
     return us, attn_bytes(n, S, False), S
 
 
@@ -554,18 +590,11 @@ def time_attention_sparse(model, n, r_kv, reps=3, S=None):
     l = torch.empty_like(m)
     o = torch.empty((H, S, hd), dtype=torch.float32, device="cuda")
     scale = 1.0 / math.sqrt(hd)
-    torch.cuda.synchronize()
-    s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for ly in model.layers[:4]:
-        bc.bc_splitk_attn_partial(q, ly["k"], ly["v"], idx, t_sel, H, Hkv, S, scale, m, l, o)
-    e0.record(s)
-    for _ in range(reps):
+
+    def one_pass():
         for ly in model.layers:
             bc.bc_splitk_attn_partial(q, ly["k"], ly["v"], idx, t_sel, H, Hkv, S, scale, m, l, o)
-    e1.record(s)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1000.0 / (reps * len(model.layers))
+    us = stream_us(one_pass, len(model.layers), reps)
     return us, attn_bytes(t_sel, S, True), S
 
 
@@ -595,7 +624,10 @@ def time_select(n, k, reps=50):
 
 def kernel_table(model, contexts, split_sweep=None):
     """Per-kernel achieved bandwidth of the hot kernels (one launch per layer,
-    rotating over the 32 layers' buffers)."""
+    rotating over the 32 layers' buffers): attention launched from the host,
+    each row beside the streaming-read probe at about its byte count; the
+    selections and GEMVs (launches as short as the host's own launch cost)
+    replayed from HIP graphs."""
     rows = []
     for S in split_sweep or []:
         for n in contexts:
@@ -606,14 +638,23 @@ def kernel_table(model, contexts, split_sweep=None):
                     us, b, _ = time_attention_sparse(model, n, r_kv, S=S)
                 rows.append({"kernel": f"attn r_kv={r_kv} S={S}", "context": n, "us": round(us, 2), "bytes": b,
                              "gbs": round(b / us / 1e3, 1), "splits": S})
+    def with_probe(row):
+        # the streaming-read probe over about the same bytes (the nearest
+        # multiple of 4 MiB): what one launch of that size reaches at best, so
+        # launch ramp and kernel loss separate
+        pb = max(1, round(row["bytes"] / (4 << 20))) << 22
+        p_us, _ = time_read_probe(model, pb)
+        row["probe_gbs"] = round(pb / p_us / 1e3, 1)
+        row["frac_of_probe"] = round(row["gbs"] / row["probe_gbs"], 4)
+        return row
     for n in contexts:
         us, b, S = time_attention_kernel(model, n)
-        rows.append({"kernel": "attn_partial dense", "context": n, "us": round(us, 2), "bytes": b,
-                     "gbs": round(b / us / 1e3, 1), "splits": S})
+        rows.append(with_probe({"kernel": "attn_partial dense", "context": n, "us": round(us, 2), "bytes": b,
+                                "gbs": round(b / us / 1e3, 1), "splits": S}))
         for r_kv in (0.3, 0.5):
             us, b, S = time_attention_sparse(model, n, r_kv)
-            rows.append({"kernel": f"attn_partial r_kv={r_kv}", "context": n, "us": round(us, 2), "bytes": b,
-                         "gbs": round(b / us / 1e3, 1), "splits": S})
+            rows.append(with_probe({"kernel": f"attn_partial r_kv={r_kv}", "context": n, "us": round(us, 2),
+                                    "bytes": b, "gbs": round(b / us / 1e3, 1), "splits": S}))
     for n, k in ((4096, 2048), (4096, 2867), (14336, 7168), (14336, 10035)):
         us = time_select(n, k)
         rows.append({"kernel": f"select n={n} k={k}", "us": round(us, 2), "bytes": 2 * n + 4 * k,
@@ -624,14 +665,17 @@ def kernel_table(model, contexts, split_sweep=None):
             rows.append({"kernel": f"gemv {which} r_p={r_p}", "us": round(us, 2), "bytes": b,
                          "gbs": round(b / us / 1e3, 1), "k": k})
     for r in rows:
+        pr = (f"; probe {r['probe_gbs']:.0f} GB/s ({100 * r['probe_gbs'] / HBM_PEAK_GBS:.1f}%), kernel at "
+              f"{100 * r['frac_of_probe']:.1f}% of it") if "probe_gbs" in r else ""
         log(f"[kernels] {r['kernel']:26s} {r.get('context', ''):>7} {r['us']:9.2f} us {r['gbs']:8.1f} GB/s "
-            f"({100 * r['gbs'] / HBM_PEAK_GBS:.1f}%)")
+            f"({100 * r['gbs'] / HBM_PEAK_GBS:.1f}%){pr}")
     return rows
 
 
 def time_gemv_kernel(model, which="w_gu", r_p=1.0, reps=3):
-    """Average duration of one bc_sparse_gemv launch over the 32 layers'
-    matrices (dense or top-k channels of a fixed input)."""
+    """Average duration of one bc_sparse_gemv_tiled call (its GEMV and, with
+    several chunks, its finish kernel) over the 32 layers' matrices (dense or
+    top-k channels of a fixed input), replayed from a HIP graph."""
     bc = model.bc
     from activation_kv_cache_amd import inputs as gen
     d_in, d_out = model.shapes[which]
@@ -644,18 +688,11 @@ def time_gemv_kernel(model, which="w_gu", r_p=1.0, reps=3):
     y = torch.empty(d_out, dtype=torch.int16, device="cuda")
     ws = torch.empty(bc.bc_sparse_gemv_workspace_bytes(d_out, k) // 4 + 64, dtype=torch.int32, device="cuda")
     bc.bc_workspace_init(ws)
-    for ly in model.layers[:4]:
-        bc.bc_sparse_gemv_tiled(ly[which], d_in, d_out, x, idx, k, y, ws)
-    torch.cuda.synchronize()
-    s = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(reps):
+
+    def one_pass():
         for ly in model.layers:
             bc.bc_sparse_gemv_tiled(ly[which], d_in, d_out, x, idx, k, y, ws)
-    e1.record(s)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1000.0 / (reps * len(model.layers))
+    us = replay_us(one_pass, len(model.layers), reps)
     return us, gemv_bytes(d_in, d_out, k, r_p < 1), k
 
 
