@@ -254,6 +254,28 @@ def _cell_str(c):
             + ("" if sp is None else f" {sp}x") + f" L{c['layer_us']}us")
 
 
+def kernel_fractions(rows):
+    """Each hot kernel's fraction of the 8 TB/s peak from the kernel table,
+    next to the 70% target: the GEMVs (q/k/v, o, gate|up, down) dense and at
+    r_p 0.5, attention dense and at r_kv 0.3 per context (with the fraction
+    of the streaming-read probe at its size)."""
+    res = {"target": 0.7}
+    names = {"w_qkv": "qkv", "w_o": "o", "w_gu": "gu", "w_down": "down"}
+    for r in rows:
+        k = r.get("kernel", "")
+        if r.get("gbs") is None:
+            continue
+        frac = round(r["gbs"] / HBM_PEAK_GBS, 3)
+        if k.startswith("gemv "):
+            which, rp = k.split()[1], k.split("r_p=")[1]
+            if rp in ("1.0", "0.5"):
+                res.setdefault(f"gemv_r_p_{rp}", {})[names.get(which, which)] = frac
+        elif k == "attn_partial dense" or k == "attn_partial r_kv=0.3":
+            tag = "dense" if "dense" in k else "kv0.3"
+            res.setdefault("attn", {})[f"{tag}@{r['context']}"] = [frac, r.get("frac_of_probe")]
+    return res
+
+
 def compact_record(out, limit=COMPACT_LIMIT):
     """The record's headline fields plus one-line summaries of the cells and
     the crossings, as one JSON object of at most `limit` bytes (the full
@@ -275,6 +297,8 @@ def compact_record(out, limit=COMPACT_LIMIT):
     if out.get("gemv_roofline"):
         g = out["gemv_roofline"]
         opt["gemv_gate_up_frac"] = {k: g[k]["frac"] for k in ("dense", "r_p_0.5") if k in g}
+    if out.get("kernels"):
+        opt["kernel_frac"] = kernel_fractions(out["kernels"])
     for key in ("step_bytes", "masked_baseline", "batch_step", "prediction"):
         if out.get(key) and isinstance(out[key], dict) and out[key].get("summary") is not None:
             opt[key] = out[key]["summary"]
@@ -293,7 +317,7 @@ def compact_record(out, limit=COMPACT_LIMIT):
         opt["record_file"] = out["record_file"]
     c.update(opt)
     drop = ["cells", "speedup_128k", "gemv_gate_up_frac", "read_probe", "batch_step", "masked_baseline",
-            "step_bytes", "prediction", "crossings_k"]
+            "kernel_frac", "step_bytes", "prediction", "crossings_k"]
     line = json.dumps(c, separators=(",", ":"))
     while len(line.encode()) > limit and drop:
         c.pop(drop.pop(0), None)
@@ -304,10 +328,38 @@ def compact_record(out, limit=COMPACT_LIMIT):
     return line
 
 
+def code_text(path):
+    """A source file's code without its comments and white space: counters
+    taken on a kernel stay valid across edits of its comments only."""
+    src = open(path, encoding="utf-8").read()
+    out, i, n = [], 0, len(src)
+    while i < n:
+        ch = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif ch in "\"'":
+            j = i + 1
+            while j < n and src[j] != ch:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            if not ch.isspace():
+                out.append(ch)
+            i += 1
+    return "".join(out)
+
+
 def kernel_source_hash():
+    """Hash of the attention kernel's code (bc_attn.hip, bc_device.hpp),
+    comments and white space left out."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        h.update(code_text(os.path.join(ROOT, f)).encode())
     return h.hexdigest()[:16]
 
 
@@ -899,10 +951,12 @@ def load_traffic(n):
 
 
 def all_sources_hash():
+    """Hash of the code of every library source (csrc/*), comments and white
+    space left out."""
     import glob
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "activation_kv_cache_amd", "csrc", "*"))):
-        h.update(open(f, "rb").read())
+        h.update(code_text(f).encode())
     return h.hexdigest()[:16]
 
 

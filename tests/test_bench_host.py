@@ -194,7 +194,13 @@ def synthetic_full_record():
         "read_probe": {"gbs": 7050.1, "frac_of_peak": 0.8813, "attention_frac_of_probe": 0.9012, "us": 76.1},
         "gemv_roofline": {"dense": {"frac": 0.8012}, "r_p_0.5": {"frac": 0.7055}},
         "cells": cells,
-        "kernels": [{"kernel": f"k{i}", "us": 1.0 * i} for i in range(60)],
+        "kernels": ([{"kernel": f"k{i}", "us": 1.0 * i} for i in range(40)]
+                    + [{"kernel": f"gemv {w} r_p={rp}", "us": 10.0, "gbs": 4321.0}
+                       for w in ("w_qkv", "w_o", "w_gu", "w_down") for rp in ("1.0", "0.7", "0.5")]
+                    + [{"kernel": k, "context": n, "us": 30.0, "gbs": 5555.0, "probe_gbs": 6666.0,
+                        "frac_of_probe": 0.8333}
+                       for k in ("attn_partial dense", "attn_partial r_kv=0.3", "attn_partial r_kv=0.5")
+                       for n in (2048, 8192, 32768, 131072)]),
         "crossover": {"contexts": ctx, "pairs": pairs,
                       "speedup": {m: [1.2345] * len(ctx) for m in bench.SWEEP_MODES if m != "dense"},
                       "step_us": {m: [1234.5] * len(ctx) for m in bench.SWEEP_MODES}},
@@ -212,6 +218,14 @@ def test_compact_record_fits_and_parses():
     line = bench.compact_record(full)
     assert len(line.encode()) <= bench.COMPACT_LIMIT < full_len
     rec = json.loads(line)
+    # each GEMV's and the attention's fraction of peak sits beside the 70% target
+    kf = rec["kernel_frac"]
+    assert kf["target"] == 0.7
+    for rp in ("1.0", "0.5"):
+        assert set(kf[f"gemv_r_p_{rp}"]) == {"qkv", "o", "gu", "down"}
+        assert kf[f"gemv_r_p_{rp}"]["o"] == round(4321.0 / bench.HBM_PEAK_GBS, 3)
+    assert kf["attn"]["kv0.3@131072"] == [round(5555.0 / bench.HBM_PEAK_GBS, 3), 0.8333]
+    assert "gemv_r_p_0.7" not in kf and not any("0.5@" in k for k in kf["attn"])
     for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "dtype", "config",
               "roofline", "cpu_baseline"):
         assert k in rec, k
@@ -282,3 +296,17 @@ def test_step_pmc_summary_on_synthetic_counters(tmp_path):
     assert r["measured_bytes"] == r["fetch_bytes"] + r["write_bytes"]
     assert set(r["fetch_by_kernel"]) == {"k_gemv<1, 0, 4>", "k_attn_partial<128, 4, 1, 0>"}
     assert r["algorithmic_bytes"] == bench.step_bytes(2048, 1.0, 1.0, *bench.kv_plan(2048, 1.0))
+
+
+def test_code_text_ignores_comments_and_white_space(tmp_path):
+    """The counter summaries are keyed to the kernels' code: an edit of a
+    comment keeps them valid, an edit of code (or of a string) does not."""
+    a = tmp_path / "a.hip"
+    b = tmp_path / "b.hip"
+    c = tmp_path / "c.hip"
+    a.write_text('int f(int x) {  // add one\n  return x + 1; /* done */\n}\nconst char* s = "a // b";\n')
+    b.write_text('// another comment\nint f(int x) {\n    return x + 1;\n}\n/* x */ const char* s = "a // b";\n')
+    c.write_text('int f(int x) {  // add one\n  return x + 2;\n}\nconst char* s = "a // b";\n')
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(c)
+    assert '"a // b"' in bench.code_text(a)
