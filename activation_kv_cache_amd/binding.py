@@ -13,10 +13,16 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libbc.so")
+# BC_LIBRARY=libbc_clk.so selects the instrumented build (per-phase clocks;
+# same kernels) from this directory; the default is the library itself
+LIB_NAME = os.environ.get("BC_LIBRARY", "libbc.so")
+if os.path.basename(LIB_NAME) != LIB_NAME or LIB_NAME not in ("libbc.so", "libbc_clk.so"):
+    raise ImportError(f"BC_LIBRARY={LIB_NAME!r}: expected libbc.so or libbc_clk.so")
+LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"libbc.so is not built ({LIB_PATH}); run __graft_entry__.build() first")
+    raise ImportError(f"{LIB_NAME} is not built ({LIB_PATH}); run __graft_entry__.build() first"
+                      + (" and activation_kv_cache_amd/build.py --phase-clocks" if LIB_NAME != "libbc.so" else ""))
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -108,6 +114,9 @@ _SIG = {
     "bc_decode_step_batch": (c_int, [ctypes.POINTER(bc_model_dims), ctypes.POINTER(bc_layer), c_int, c_int, P, P,
                                      ctypes.POINTER(bc_step), P, P, P, P, c_size_t, P]),
     "bc_lm_head": (c_int, [ctypes.POINTER(bc_model_dims), P, P, P, P, P, c_double, P, c_size_t, P]),
+    "bc_phase_clocks_begin": (c_int, [P, c_size_t]),
+    "bc_phase_clocks_count": (c_int, []),
+    "bc_phase_clocks_info": (c_int, [c_int, ctypes.POINTER(ctypes.c_longlong)]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(_lib, _name)
@@ -203,6 +212,29 @@ def bc_lm_head_workspace_bytes(md: bc_model_dims) -> int:
 def bc_workspace_init(ws, stream=None):
     p, n = _ws(ws)
     return _check(_lib.bc_workspace_init(p, n, _stream(stream)), "bc_workspace_init")
+
+
+def bc_phase_clocks_begin(buf=None):
+    """Registers buf (an int64 device tensor) for the per-phase clocks of the
+    launches that follow, or stops recording (None).  Raises BcError with
+    BC_ERR_UNSUPPORTED unless the instrumented build is loaded."""
+    if buf is None:
+        return _check(_lib.bc_phase_clocks_begin(None, 0), "bc_phase_clocks_begin")
+    return _check(_lib.bc_phase_clocks_begin(_ptr(buf), buf.numel() * buf.element_size()), "bc_phase_clocks_begin")
+
+
+def bc_phase_clocks_launches():
+    """The launches recorded since the last begin: a list of (kind, a, b, c,
+    d, work-groups, first entry) tuples (include/bc.h)."""
+    n = _lib.bc_phase_clocks_count()
+    if n < 0:
+        raise BcError(n, "bc_phase_clocks_count")
+    out = []
+    for i in range(n):
+        rec = (ctypes.c_longlong * 7)()
+        _check(_lib.bc_phase_clocks_info(i, rec), "bc_phase_clocks_info")
+        out.append(tuple(int(v) for v in rec))
+    return out
 
 
 def bc_stream_read(src, sink, stream=None):

@@ -13,20 +13,29 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbc.so")
 BUILD = os.path.join(HERE, "_build")
+# the instrumented variant: the same kernels plus per-phase clock reads
+LIB_CLK = os.path.join(HERE, "libbc_clk.so")
+BUILD_CLK = os.path.join(HERE, "_build_clk")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["bc_gemv.hip", "bc_gemv_batch.hip", "bc_attn.hip", "bc_kv.hip", "bc_snap.hip", "bc_masked.hip", "bc_batch.hip", "bc_layer.hip"]
+SOURCES = ["bc_gemv.hip", "bc_gemv_batch.hip", "bc_attn.hip", "bc_kv.hip", "bc_snap.hip", "bc_masked.hip", "bc_batch.hip",
+           "bc_layer.hip", "bc_clock.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-ffp-contract=fast", "-munsafe-fp-atomics"]
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
+def build(verbose: bool = False, jobs: int = 4, phase_clocks: bool = False) -> str:
+    """Builds libbc.so, or with phase_clocks the instrumented libbc_clk.so
+    (-DBC_PHASE_CLOCKS: the kernels also read the shader clock at phase
+    ends; a measurement build, loaded with BC_LIBRARY=libbc_clk.so)."""
+    lib, bdir = (LIB_CLK, BUILD_CLK) if phase_clocks else (LIB, BUILD)
+    flags = FLAGS + (["-DBC_PHASE_CLOCKS"] if phase_clocks else [])
     objs = []
     procs = []
     for src in SOURCES:
-        os.makedirs(BUILD, exist_ok=True)
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        os.makedirs(bdir, exist_ok=True)
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
+        cmd = [HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True)))
@@ -35,12 +44,12 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             _wait(procs.pop(0))
     while procs:
         _wait(procs.pop(0))
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib + ".tmp", *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 def _wait(item):
@@ -54,4 +63,4 @@ def _wait(item):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, phase_clocks="--phase-clocks" in sys.argv))

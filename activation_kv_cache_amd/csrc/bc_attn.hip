@@ -23,6 +23,7 @@
 // one work-group per query head.
 #include <math.h>
 
+#include "bc_clock.hpp"
 #include "bc_device.hpp"
 #include "bc_internal.hpp"
 
@@ -209,6 +210,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
   constexpr int STEP = kAttnWaves * TPI;
   constexpr int HALF = D / 2;
   __shared__ AttnSmem<D, G> sm;
+  // phase ends (a build with phase clocks only): [3] q (and the list's
+  // block ranks) ready after the prologue's barrier, [12] the first wave's
+  // rows done, [5] every wave's rows done (the merge's first barrier), [6]
+  // merge weights ready
+  PhaseClock clk;
+  clk.begin();
 
   const int s = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, lane = wave_lane(), w = wave_id();
@@ -366,6 +373,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
     }
   }
   __syncthreads();
+  clk.stamp(3);
 
   if constexpr (LM != L_IDX) {
     // one pass over the split's list positions [lo, hi_main): the dense list
@@ -434,6 +442,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
     attn_compute<D, G, true>(nr, &sm.q[0][0], 0, 1, sub, r, c, tau, st);
   }
 
+  clk.stamp_after(12, st.l[0] + st.o[0][15]);
   // merge the row groups' states in LDS: every row group writes its lazy
   // state (m, l, o) and its true max; the weight of state k for head j is
   // 2^((m_k - M_j) c) with M_j the largest true max, and each output dim is
@@ -458,6 +467,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
       }
     }
     __syncthreads();
+    clk.stamp(5);
     static_assert(SM::NST % 4 == 0, "states in float4 groups");
     for (int e = tid; e < G * SM::NST; e += kAttnThreads) {
       const int j = e / SM::NST, kk = e % SM::NST;
@@ -472,6 +482,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
       if (kk == 0) sm.M[j] = M;
     }
     __syncthreads();
+    clk.stamp(6);
     // two adjacent dims per thread (64-bit LDS reads), weights four at a time
     for (int e = 2 * tid; e < G * D; e += 2 * kAttnThreads) {
       const int j = e / D, d = e % D;
@@ -523,6 +534,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
     sp[0] = bmn;
     sp[1] = bmx;
   }
+  clk.end(p.clk, size_t(g) * gridDim.x + s);
 }
 
 // One work-group per query head.  M and the weights w_s = e^(m_s - M) are
@@ -614,7 +626,10 @@ bool attn_scored_list_ok(const bc_kv_budget_info& bud, int n_splits) {
 
 bool attn_prologue_select_ok(const bc_kv_budget_info& bud) { return bud.n_cand <= kAttnThreads * 8; }
 
-int launch_attn_partial(int q_mode, int list_mode, const AttnParams& p, hipStream_t s) {
+int launch_attn_partial(int q_mode, int list_mode, const AttnParams& p_in, hipStream_t s) {
+  AttnParams p = p_in;
+  p.clk = clock_take(size_t(p.n_splits) * p.n_kv_heads, CLOCK_ATTN, q_mode | (list_mode << 8), p.n_sel, p.n_splits,
+                     p.n_kv_heads);
   if (list_mode == L_IDX && p.idx == nullptr) return set_error(BC_ERR_INVALID, "attention: NULL index list");
   if (list_mode == L_SCORES &&
       (!attn_scored_list_ok(p.bud, p.n_splits) || p.n_sel != p.bud.t_sel ||

@@ -513,6 +513,10 @@ __device__ __forceinline__ void waves_before_total(const uint32_t* tot, int w, u
 struct TopkNoOut {
   __device__ void operator()(int, int) const {}
 };
+// stamp(i) after the selection's i-th barrier (i = 0..4) and at its end (5)
+struct TopkNoStamp {
+  __device__ void operator()(int) const {}
+};
 
 template <int PMAX, typename EmitFn, typename OutFn>
 __device__ __forceinline__ void topk_emit_kept(uint32_t take, uint32_t pos0, uint32_t cnt, int r0, int r1, bool all,
@@ -533,9 +537,10 @@ __device__ __forceinline__ void topk_emit_kept(uint32_t take, uint32_t pos0, uin
   }
 }
 
-template <int NT, int SHIFT, int PMAX, typename EmitFn, typename OutFn = TopkNoOut>
+template <int NT, int SHIFT, int PMAX, typename EmitFn, typename OutFn = TopkNoOut, typename StampFn = TopkNoStamp>
 __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int k, int r0, int r1, EmitFn emit,
-                                 Topk2Smem<NT, SHIFT>& sm, bool all = false, OutFn out = OutFn()) {
+                                 Topk2Smem<NT, SHIFT>& sm, bool all = false, OutFn out = OutFn(),
+                                 StampFn stamp = StampFn()) {
   static_assert(PMAX <= 32, "bit masks are 32 bits");
   constexpr int NB = Topk2Smem<NT, SHIFT>::NB;
   constexpr int NB2 = 1 << SHIFT;
@@ -554,6 +559,7 @@ __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int 
     atomicAdd(&sm.hist[ok ? key[e] >> SHIFT : uint32_t(lane)], ok ? 1u : 0u);
   }
   __syncthreads();
+  stamp(0);
   // thread t owns bins [b0, b0 + BPT), b0 = NB - BPT (t + 1): the largest
   // bins go to thread 0, so counts accumulated over threads in order count
   // larger keys
@@ -572,6 +578,7 @@ __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int 
   const uint32_t winc = wave_scan_dpp(local);
   if (lane == kWave - 1) sm.wtot[w] = winc;
   __syncthreads();
+  stamp(1);
   {
     // the wave whose bins hold the k-th largest key (lane-parallel search)
     const uint32_t c = lane < NW ? sm.wtot[lane] : 0u;
@@ -592,11 +599,13 @@ __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int 
     }
   }
   __syncthreads();
+  stamp(2);
   const uint32_t b1 = sm.b1, k2 = ku - sm.above1;
 #pragma unroll
   for (int e = 0; e < PMAX; ++e)
     if (e < nv && (key[e] >> SHIFT) == b1) atomicAdd(&sm.hist2[key[e] & uint32_t(NB2 - 1)], 1u);
   __syncthreads();
+  stamp(3);
   uint32_t thr, need;
   {
     // low digit, largest first: lane l holds digit NB2-1-l
@@ -622,6 +631,7 @@ __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int 
   const uint32_t inc = wave_scan_dpp(v);
   if (lane == kWave - 1) sm.wtot[w] = inc;
   __syncthreads();
+  stamp(4);
   const uint32_t bf = inc - v + waves_before<NW>(sm.wtot, w);
   const uint32_t gt_before = bf & 0xFFFFu, eq_before = bf >> 16;
   const uint32_t ties_before = eq_before < need ? eq_before : need;
@@ -638,6 +648,7 @@ __device__ void block_topk_2pass(const uint32_t (&key)[PMAX], int P, int n, int 
     }
   }
   topk_emit_kept<PMAX>(gtm | tie_keep, gt_before + ties_before, gt + ties_here, r0, r1, all, emit, out);
+  stamp(5);
 }
 
 // --------------------------------------- 32-bit keys in registers, adaptive

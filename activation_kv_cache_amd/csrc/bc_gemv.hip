@@ -35,6 +35,7 @@
 
 #include <type_traits>
 
+#include "bc_clock.hpp"
 #include "bc_device.hpp"
 #include "bc_internal.hpp"
 
@@ -151,6 +152,11 @@ template <int IN, int OUT, int PMAX>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
   constexpr int kRing = ring_depth<OUT>();
   __shared__ GemvSmem sm;
+  // phase ends (a build with phase clocks only): [3] inputs arrived, [4]
+  // input formed (after its barrier), [5..9] the selection's barriers, [10]
+  // selection emitted, [11] prologue done, [12] row loop done
+  PhaseClock clk;
+  clk.begin();
   const int tile = blockIdx.x, split = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = tid & 15, slot = tid >> 4;
@@ -204,6 +210,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
 #pragma unroll
         for (int q = 0; q < Q; ++q) xq[q] = bf16_to_f32(p.x[r0 + min(tid + q * kGemvThreads, n - 1)]);
         issue_ring();
+        clk.stamp_after(3, xq[Q - 1]);
 #pragma unroll
         for (int q = 0; q < Q; ++q)
           if (tid + q * kGemvThreads < n) sm.list.xv[tid + q * kGemvThreads] = xq[q];
@@ -224,6 +231,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
         for (int q = 0; q < Q; ++q) xq[q] = bf16_to_f32(p.x[min(chq[q], last_row)]);
 #pragma unroll
         for (int u = 0; u < kRing; ++u) ring[u] = load_row_nt(base + size_t(chr[u]) * stride);
+        clk.stamp_after(3, xq[Q - 1]);
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
           const int j = tid + q * kGemvThreads;
@@ -253,6 +261,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
 #pragma unroll
       for (int sp = 0; sp < kAttnFoldMaxSplits; ++sp) ov[sp] = osrc[size_t(min(sp, S - 1)) * D];
       issue_ring();
+      clk.stamp_after(3, ov[kAttnFoldMaxSplits - 1]);
       for (int hw = w; hw < nh; hw += kNW) {
         const size_t hb = size_t(h0 + hw) * S;
         float ms = ms0, lv = lv0;
@@ -269,6 +278,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
         if (lane == 0) sm.fold.den[hw] = 0.f + den;
       }
       __syncthreads();
+      clk.stamp(4);
       if (tid < n) {
         const int G = kCombineThreads / D, per = (S + G - 1) / G;
         const float* wv = sm.fold.w[hh];
@@ -299,6 +309,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
         load_vec<PMAX>(p.gain, c0, P, p.d_in, gb);
         if (DENSE) issue_ring();
         if (!DENSE) topk2_clear(sm.tk);   // while the loads are in flight; the barrier below covers it
+        clk.stamp_after(3, __uint_as_float(gb[PMAX / 2 - 1]));
         if constexpr (IN == IN_NORM_SUM) {
           sum_finish<PMAX>(p.sum_partial, p.sum_splits, c0, P, p.d_in, sin, xb);
           if (lead && p.h_out) {
@@ -319,6 +330,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
         ss = wave_sum_f32(ss);
         if (lane == 0) sm.part[w] = ss;
         __syncthreads();
+        clk.stamp(4);
         float tot = 0.f;
 #pragma unroll
         for (int ww = 0; ww < kNW; ++ww) tot += sm.part[ww];
@@ -332,9 +344,11 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
       } else {
         load_vec<PMAX>(p.x, c0, P, p.d_in, xb);
         if (DENSE) issue_ring();
+        clk.stamp_after(3, __uint_as_float(xb[PMAX / 2 - 1]));
         if (!DENSE) {
           topk2_clear(sm.tk);
           __syncthreads();
+          clk.stamp(4);
         }
       }
       if (lead && p.x_out) {
@@ -359,8 +373,9 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
           sm.list.xv[rel] = bf16_elt(xb, e);
         };
         auto out = [&](int pos, int e) { idx_out[pos] = c0 + e; };
+        auto stamp = [&](int phase) { clk.stamp(5 + phase); };
         block_topk_2pass<kGemvThreads, kTopkShift, PMAX>(key, P, p.d_in, p.k, r0, r1, emit, sm.tk,
-                                                         lead && idx_out != nullptr, out);
+                                                         lead && idx_out != nullptr, out, stamp);
       }
     }
   };
@@ -370,6 +385,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
     prologue(std::false_type{});
   __syncthreads();
   if (IN != IN_LIST && !dense) issue_ring();
+  clk.stamp(11);
 
   // ------------------------------------------------------------- row loop
   float acc[8];
@@ -402,6 +418,8 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
   }
 #pragma unroll
   for (int u = 0; u < kRing; ++u) consume(slot + kSlots * (st + u), ring[u]);
+
+  clk.stamp_after(12, acc[7]);
 
   // ------------------------------------------------------------- epilogue
   // The four slots of a wave (its 16-lane rows) hold the same 8 columns:
@@ -463,6 +481,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
       p.tile_arg[tile] = besti;
     }
   }
+  clk.end(p.clk, size_t(split) * gridDim.x + tile);
 }
 
 // ------------------------------------------------------------------ finish
@@ -720,7 +739,9 @@ int launch_gemv_out(int out, const GemvParams& p, dim3 grid, hipStream_t s) {
 }
 }  // namespace
 
-int launch_gemv(int in, int out, const GemvParams& p, hipStream_t s) {
+int launch_gemv(int in, int out, const GemvParams& p_in, hipStream_t s) {
+  GemvParams p = p_in;
+  p.clk = clock_take(size_t(p.n_tiles) * p.n_splits, CLOCK_GEMV, in | (out << 8), p.d_in, p.d_out, p.k);
   if (p.n_splits < 1 || p.n_tiles < 1 || p.rows_per_split < 1 || p.rows_per_split > kGemvMaxRows ||
       size_t(p.n_splits - 1) * p.rows_per_split >= size_t(p.k) || size_t(p.n_splits) * p.rows_per_split < size_t(p.k))
     return set_error(BC_ERR_INVALID, "GEMV plan does not cover k=%d", p.k);

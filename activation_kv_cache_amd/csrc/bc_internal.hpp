@@ -96,6 +96,7 @@ struct GemvParams {
   float* yf;              // OUT_ARGMAX
   float* tile_max;
   int32_t* tile_arg;
+  unsigned long long* clk;   // phase clocks of the launch (set by launch_gemv; NULL in the library itself)
 };
 int launch_gemv(int in, int out, const GemvParams& p, hipStream_t s);
 
@@ -164,6 +165,7 @@ struct AttnParams {
   bc_kv_budget_info bud;
   int n_ctx;
   int32_t* idx_out;           // optional: the list [n_kv_heads][n_sel] (each split writes its slice)
+  unsigned long long* clk;    // phase clocks of the launch (set by launch_attn_partial; NULL in the library itself)
 };
 int launch_attn_partial(int q_mode, int list_mode, const AttnParams& p, hipStream_t s);
 // whether a scored list fits the attention kernel (candidates, ranks per split)

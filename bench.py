@@ -1100,6 +1100,114 @@ PAIRS = (("proj0.7", "kv0.3", 0.7, 0.3), ("proj0.5", "kv0.3", 0.5, 0.3), ("proj0
          ("proj0.7", "sel0.3", 0.7, 0.3), ("proj0.5", "sel0.3", 0.5, 0.3), ("proj0.5", "sel0.5", 0.5, 0.5))
 
 
+GEMV_IN = {0: "list", 1: "norm", 2: "sel", 3: "norm_sum", 4: "attn"}
+GEMV_OUT = {0: "partial", 1: "bf16", 2: "swiglu", 3: "argmax"}
+ATTN_LIST = {0: "dense", 1: "idx", 2: "scores"}
+
+
+def phase_clock_launch(launch, clk):
+    """Summary of one recorded launch (bc_phase_clocks_launches entry) from
+    its clock slice (int64 numpy, 16 entries per work-group; include/bc.h):
+    span and start skew from the real-time counter (10 ns), per-phase times
+    of the median work-group from the shader clock (converted with its rate
+    against the real-time counter), the last work-group's end after the
+    median one, and per-XCC mean work-group times."""
+    kind, a, b, c, d, groups, off = launch
+    t = clk[off: off + 16 * groups].reshape(groups, 16).astype(np.float64)
+    r0, r1, c0, c13 = t[:, 0], t[:, 1], t[:, 2], t[:, 13]
+    ok = (r1 > r0) & (c13 > c0)
+    mhz = 100.0 * float(np.median((c13 - c0)[ok] / (r1 - r0)[ok]))
+
+    def ph(i, j):
+        sel = (t[:, i] > 0) & (t[:, j] > 0)
+        return round(float(np.median(t[sel, j] - t[sel, i])) / mhz, 3) if sel.any() else None
+    rec = {"span_us": round((r1.max() - r0.min()) * 0.01, 3), "skew_us": round((r0.max() - r0.min()) * 0.01, 3),
+           "last_after_median_us": round((r1.max() - np.median(r1)) * 0.01, 3), "mhz": round(mhz),
+           "start_r": float(r0.min()), "end_r": float(r1.max())}
+    xcc = t[:, 14].astype(np.int64) & 0xF
+    rec["xcc_wg_us"] = {int(x): round(float(((r1 - r0)[xcc == x]).mean()) * 0.01, 3) for x in np.unique(xcc)}
+    if kind == 1:
+        rec["kernel"] = (f"k_gemv {GEMV_IN.get(a & 255)}/{GEMV_OUT.get(a >> 8)} {b}x{c}"
+                         + ("" if d == b else f" k={d}") + f" ({groups} work-groups)")
+        rec["phases_us"] = {"inputs_arrived": ph(2, 3), "input_formed": ph(2, 4), "selected": ph(2, 10),
+                            "prologue": ph(2, 11), "row_loop": ph(11, 12), "epilogue": ph(12, 13),
+                            "total": ph(2, 13)}
+        if rec["phases_us"]["selected"] is not None:
+            rec["selection_us"] = {"clear_and_barrier": ph(3, 4), "histogram": ph(4, 5), "wave_totals": ph(5, 6),
+                                   "bin": ph(6, 7), "low_digit": ph(7, 8), "rank_scan": ph(8, 9), "emit": ph(9, 10)}
+    else:
+        rec["kernel"] = (f"k_attn_partial q={'partial' if (a & 255) else 'global'} list={ATTN_LIST.get(a >> 8)} "
+                         f"{b} tokens, {c} splits ({groups} work-groups)")
+        rec["phases_us"] = {"prologue": ph(2, 3), "rows_first_wave": ph(3, 12), "rows_all_waves": ph(3, 5),
+                            "merge": ph(5, 13), "total": ph(2, 13)}
+    return rec
+
+
+def phase_clock_summary(model, specs, reps=5):
+    """Per-phase clocks of every GEMV and attention launch of one decode step
+    per (mode, context) spec, from the instrumented build: the step is
+    captured in a HIP graph while recording (each launch takes its clock
+    slice), replayed `reps` times, and the last replay's clocks are read.
+    Launches of the same kernel and shape are averaged over the layers."""
+    bc = model.bc
+    buf = torch.zeros(16 << 20, dtype=torch.int64, device="cuda")
+    out = {}
+    for mode, n in specs:
+        r_p, r_kv, once = SWEEP_MODES[mode]
+        if once:
+            t_sel = model.sel_prepare(n, r_kv)
+            run = lambda: model.step_sel(t_sel, r_p)
+        else:
+            run = lambda: model.step(n, r_p, r_kv)
+        run()
+        torch.cuda.synchronize()
+        buf.zero_()
+        torch.cuda.synchronize()
+        bc.bc_phase_clocks_begin(buf)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        launches = bc.bc_phase_clocks_launches()
+        bc.bc_phase_clocks_begin(None)
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        clk = buf.cpu().numpy()
+        recs = [phase_clock_launch(l, clk) for l in launches]
+        for i in range(1, len(recs)):
+            recs[i]["since_previous_us"] = round((recs[i]["start_r"] - recs[i - 1]["end_r"]) * 0.01, 3)
+        groups = {}
+        for r in recs:
+            groups.setdefault(r["kernel"], []).append(r)
+        rows = []
+        for name, rs in groups.items():
+            row = {"kernel": name, "launches": len(rs), "mhz": round(float(np.mean([r["mhz"] for r in rs])))}
+            for key in ("span_us", "skew_us", "last_after_median_us"):
+                row[key] = round(float(np.mean([r[key] for r in rs])), 3)
+            gaps = [r["since_previous_us"] for r in rs if "since_previous_us" in r]
+            # from the previous clocked launch's end (kernels without clocks
+            # in between, such as the split-K reduce, count into it)
+            row["since_previous_us"] = round(float(np.mean(gaps)), 3) if gaps else None
+            for key in ("phases_us", "selection_us"):
+                if key in rs[0]:
+                    row[key] = {k: (None if rs[0][key][k] is None else
+                                    round(float(np.mean([r[key][k] for r in rs if r[key][k] is not None])), 3))
+                                for k in rs[0][key]}
+            xs = sorted({x for r in rs for x in r["xcc_wg_us"]})
+            row["xcc_wg_us"] = {x: round(float(np.mean([r["xcc_wg_us"][x] for r in rs if x in r["xcc_wg_us"]])), 3)
+                                for x in xs}
+            rows.append(row)
+            ph_ = row["phases_us"]
+            log(f"[clocks] {mode}@{n} {name} x{len(rs)}: span {row['span_us']:.2f} us, " +
+                ", ".join(f"{k} {v:.2f}" for k, v in ph_.items() if v is not None) +
+                (f"; selection " + ", ".join(f"{k} {v:.2f}" for k, v in row["selection_us"].items() if v is not None)
+                 if "selection_us" in row else "") +
+                f"; last work-group {row['last_after_median_us']:.2f} us after the median")
+        out[f"{mode}@{n}"] = rows
+        del g
+    return out
+
+
 CALIB_CONTEXTS = [2048, 16384, 32768, 65536, 98304, 131072, 163840]
 CALIB_MODES = ("dense", "proj0.7", "proj0.5", "kv0.3", "kv0.5", "sel0.3", "sel0.5")
 
@@ -1362,6 +1470,9 @@ def main():
                          "mode's steps between two marker launches (bc_stream_read of 4 MiB), for whole-step "
                          "counters and kernel traces")
     ap.add_argument("--eager", action="store_true", help="with --step-pmc: eager steps instead of graph replays")
+    ap.add_argument("--phase-clocks", default="",
+                    help="MODE:N+...: per-phase clocks of the GEMV and attention launches of one step per spec "
+                         "(needs BC_LIBRARY=libbc_clk.so, the instrumented build)")
     ap.add_argument("--pmc-summary", default="",
                     help="FETCH_CSV,WRITE_CSV,CFETCH_CSV,CWRITE_CSV,SPECS,COPY_BYTES -- SPECS as for --step-pmc: "
                          "sum the counters of each mode's steps (between its two markers) and print each step's "
@@ -1395,6 +1506,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes": src.numel() * 4}))
+        return
+
+    if args.phase_clocks:
+        specs = [(m, int(n)) for m, n in (x.split(":") for x in args.phase_clocks.split("+"))]
+        model = Model(max_ctx=max(n for _, n in specs))
+        res = phase_clock_summary(model, specs)
+        print(json.dumps({"phase_clocks": res, "library": model.bc.LIB_NAME}, separators=(",", ":")))
         return
 
     if args.step_pmc:

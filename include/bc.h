@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define BC_ABI_VERSION 5
+#define BC_ABI_VERSION 6
 
 enum {
   BC_OK = 0,
@@ -448,6 +448,32 @@ int bc_lm_head(const bc_model_dims* dims, const uint16_t* hidden, const uint16_t
  * * 16); src 16-byte aligned.  Errors: BC_ERR_INVALID for a NULL pointer,
  * a misaligned src or a size that is not such a multiple. */
 int bc_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
+/* Measurement helpers, not steps of the method: per-phase clocks of the GEMV
+ * and attention kernels.  Only the instrumented build of this library
+ * (libbc_clk.so, compiled with -DBC_PHASE_CLOCKS; same kernels plus clock
+ * reads) records them; the library itself returns BC_ERR_UNSUPPORTED from
+ * all three and its kernels take no clock reads.
+ * bc_phase_clocks_begin registers buf (device memory, 8-byte aligned, bytes
+ * long; NULL stops recording) and forgets earlier launches; each later GEMV
+ * or attention-partial launch then takes the next 16 64-bit entries per
+ * work-group of it, while they fit, and its work-group g stores at
+ * entries [16 g, 16 g + 16) of its slice: the 100 MHz real-time counter at
+ * its start and end, the shader clock at its start, at phase ends and at
+ * its end, its XCC id and hardware id (which phase each entry holds is
+ * listed in the kernel's source).  A launch recorded during graph capture
+ * writes its slice at every replay.  The caller owns buf and reads it after
+ * the kernels end.
+ * bc_phase_clocks_count: the number of launches recorded since the last
+ * begin (or a negative error code).
+ * bc_phase_clocks_info(i, out7): launch i as out7 = {kind (1 GEMV, 2
+ * attention), a, b, c, d, work-groups, first entry}; a..d are, for a GEMV,
+ * (input mode | output mode << 8, d_in, d_out, k) and, for attention, (q
+ * mode | list mode << 8, listed tokens, splits, KV heads).  Errors:
+ * BC_ERR_INVALID for i out of range or a NULL out7. */
+int bc_phase_clocks_begin(void* buf, size_t bytes);
+int bc_phase_clocks_count(void);
+int bc_phase_clocks_info(int i, long long* out7);
 
 #ifdef __cplusplus
 }

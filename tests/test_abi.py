@@ -45,7 +45,21 @@ def test_library_exports_every_declared_symbol(bc):
 
 
 def test_abi_version(bc):
-    assert bc.bc_abi_version() == 5
+    assert bc.bc_abi_version() == 6
+
+
+def test_phase_clocks_unsupported_in_the_library(bc):
+    """The library itself records no phase clocks: its three clock entry
+    points report BC_ERR_UNSUPPORTED (only libbc_clk.so, the instrumented
+    build, records them)."""
+    lib = bc.library()
+    assert bc.LIB_NAME == "libbc.so"
+    assert lib.bc_phase_clocks_begin(None, 0) == bc.BC_ERR_UNSUPPORTED
+    assert lib.bc_phase_clocks_count() == bc.BC_ERR_UNSUPPORTED
+    rec = (ctypes.c_longlong * 7)()
+    assert lib.bc_phase_clocks_info(0, rec) == bc.BC_ERR_UNSUPPORTED
+    with pytest.raises(bc.BcError):
+        bc.bc_phase_clocks_begin(None)
 
 
 @pytest.mark.parametrize("r_p,d", [(0.5, 4096), (0.7, 4096), (0.7, 14336), (0.5, 1408), (1.0, 77), (0.0001, 77),

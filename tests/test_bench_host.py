@@ -310,3 +310,30 @@ def test_code_text_ignores_comments_and_white_space(tmp_path):
     assert bench.code_text(a) == bench.code_text(b)
     assert bench.code_text(a) != bench.code_text(c)
     assert '"a // b"' in bench.code_text(a)
+
+
+def test_phase_clock_launch_reads_the_stamps():
+    """One GEMV launch of two work-groups with known stamps: spans from the
+    real-time counter (10 ns), phases from the shader clock at its measured
+    rate (here 2000 MHz: 20 shader ticks per real-time tick)."""
+    import numpy as np
+    clk = np.zeros(64, dtype=np.int64)
+    for g, (start, xcc) in enumerate(((1000, 0), (1010, 1))):
+        e = clk[16 + 16 * g: 32 + 16 * g]        # slice at entry 16
+        e[0], e[1] = start, start + 500          # 5 us of real time
+        e[2] = 20 * start                        # shader clock, 2000 MHz
+        e[3] = e[2] + 2000                       # inputs after 1 us
+        e[4] = e[2] + 3000
+        e[11] = e[2] + 6000                      # prologue 3 us
+        e[12] = e[11] + 2000 * 1 + 4000 * g      # row loop 1 or 3 us
+        e[13] = e[2] + 10000                     # 5 us in all
+        e[14] = xcc
+    launch = (1, 2 | (0 << 8), 14336, 4096, 7168, 2, 16)
+    rec = bench.phase_clock_launch(launch, clk)
+    assert rec["mhz"] == 2000
+    assert rec["span_us"] == 5.1 and rec["skew_us"] == 0.1
+    assert rec["kernel"].startswith("k_gemv sel/partial 14336x4096 k=7168")
+    ph = rec["phases_us"]
+    assert ph["inputs_arrived"] == 1.0 and ph["input_formed"] == 1.5 and ph["prologue"] == 3.0
+    assert ph["row_loop"] == 2.0 and ph["total"] == 5.0 and ph["selected"] is None
+    assert rec["xcc_wg_us"] == {0: 5.0, 1: 5.0}
