@@ -1450,7 +1450,7 @@ def main():
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="only copy this many bytes 5 times (calibration of the HBM byte counters)")
     ap.add_argument("--split-sweep", default="", help="attention split counts to sweep in --kernels")
-    ap.add_argument("--crossover-blocks", type=int, default=4,
+    ap.add_argument("--crossover-blocks", type=int, default=5,
                     help="blocks of the crossover sweep (every mode at 2K, 4K, ..., 128K); 0 skips it")
     ap.add_argument("--crossover-steps", type=int, default=10, help="timed steps per sweep cell")
     ap.add_argument("--batch-sweep", type=int, default=1,
