@@ -65,7 +65,7 @@ struct GemvSmem {
   union {
     Topk2Smem<kGemvThreads, kTopkShift> tk;
     struct {
-      float w[kFoldMaxHeads][kAttnFoldMaxSplits];   // combine weights w_s per head of the chunk
+      alignas(16) float w[kFoldMaxHeads][kAttnFoldMaxSplits];   // combine weights w_s per head of the chunk
       float den[kFoldMaxHeads];
     } fold;
   };
@@ -262,13 +262,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
       for (int sp = 0; sp < kAttnFoldMaxSplits; ++sp) ov[sp] = osrc[size_t(min(sp, S - 1)) * D];
       issue_ring();
       clk.stamp_after(3, ov[kAttnFoldMaxSplits - 1]);
-      for (int hw = w; hw < nh; hw += kNW) {
-        const size_t hb = size_t(h0 + hw) * S;
-        float ms = ms0, lv = lv0;
-        if (hw != w) {
-          ms = lane < S ? p.am[hb + lane] : -INFINITY;
-          lv = lane < S ? p.al[hb + lane] : 0.f;
-        }
+      auto head_weights = [&](int hw, float ms, float lv) {
         float M = ms;
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
@@ -276,20 +270,43 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
         const float den = combine_wave_sum(lane < S ? fmaf(wt, lv, 0.f) : 0.f);
         if (lane < S) sm.fold.w[hw][lane] = wt;
         if (lane == 0) sm.fold.den[hw] = 0.f + den;
+      };
+      // the first head from the values loaded above: no load of the same
+      // address sits in a loop behind the weight rows, where waiting for it
+      // would mean waiting for them too
+      if (w < nh) head_weights(w, ms0, lv0);
+      // more heads than waves (head_dim 64, 17 heads): loaded here
+      for (int hw = w + kNW; hw < nh; hw += kNW) {
+        const size_t hb = size_t(h0 + hw) * S;
+        head_weights(hw, lane < S ? p.am[hb + lane] : -INFINITY, lane < S ? p.al[hb + lane] : 0.f);
       }
       __syncthreads();
       clk.stamp(4);
       if (tid < n) {
         const int G = kCombineThreads / D, per = (S + G - 1) / G;
-        const float* wv = sm.fold.w[hh];
+        // the head's weights in registers first (16-byte LDS reads, one
+        // wait), so the sums below do not wait on LDS split by split
+        float wr[kAttnFoldMaxSplits];
+        const float4* wv4 = reinterpret_cast<const float4*>(sm.fold.w[hh]);
+#pragma unroll
+        for (int q = 0; q < kAttnFoldMaxSplits / 4; ++q) {
+          const float4 v4 = wv4[q];
+          wr[4 * q] = v4.x;
+          wr[4 * q + 1] = v4.y;
+          wr[4 * q + 2] = v4.z;
+          wr[4 * q + 3] = v4.w;
+        }
         float t = 0.f;
         for (int g = 0; g < G; ++g) {
           const int s0 = min(S, g * per), s1 = min(S, s0 + per);
-          // combine_group over registers: splits outside [s0, s1) are skipped
+          // combine_group over registers: splits outside [s0, s1) leave the
+          // sum as it is (their weights are not set; the select drops them)
           float num = 0.f;
 #pragma unroll
-          for (int sp = 0; sp < kAttnFoldMaxSplits; ++sp)
-            if (sp >= s0 && sp < s1) num = fmaf(ov[sp], wv[sp], num);
+          for (int sp = 0; sp < kAttnFoldMaxSplits; ++sp) {
+            const float nx = fmaf(ov[sp], wr[sp], num);
+            num = (sp >= s0 && sp < s1) ? nx : num;
+          }
           t += num;
         }
         const float den = sm.fold.den[hh];
