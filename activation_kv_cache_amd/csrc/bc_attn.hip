@@ -269,17 +269,15 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
   // at the end, so their latency hides under the main loop
   const bool refresh = QM == Q_PARTIAL && appends && p.summary != nullptr && tid < D;
   const int blk = p.pos / 16;
-  uint32_t srow[8];
+  // one register per row (not packed in pairs): nothing waits for these
+  // loads before their use at the end
+  uint16_t srow[16];
   if (refresh) {
     const uint16_t* kc = p.k_cache + size_t(g) * p.n_cap * D + tid;
     // rows from pos on are replaced by the new row later; their loads read
     // an older row (clamped index, no branches)
 #pragma unroll
-    for (int t = 0; t < 16; t += 2) {
-      const uint32_t a = kc[size_t(max(0, min(blk * 16 + t, p.pos - 1))) * D];
-      const uint32_t b = kc[size_t(max(0, min(blk * 16 + t + 1, p.pos - 1))) * D];
-      srow[t / 2] = a | (b << 16);
-    }
+    for (int t = 0; t < 16; ++t) srow[t] = kc[size_t(max(0, min(blk * 16 + t, p.pos - 1))) * D];
   }
 
   // dense list: the first rows are known before q, so they go in flight now
@@ -525,7 +523,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
     float mn = bf16_to_f32(nb), mx = mn;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const uint16_t u = blk * 16 + t < p.pos ? uint16_t(srow[t / 2] >> (16 * (t & 1))) : nb;
+      const uint16_t u = blk * 16 + t < p.pos ? srow[t] : nb;
       const float f = bf16_to_f32(u);
       if (f < mn) { mn = f; bmn = u; }
       if (f > mx) { mx = f; bmx = u; }
