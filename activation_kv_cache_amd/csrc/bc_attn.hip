@@ -263,21 +263,34 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
       chunk_load(cvv, p.qkv_partial, p.qkv_splits, p.qkv_out, vcol + id);
     }
   }
+  // the rotary cos/sin of the thread's pairs: the table is a kernel argument
+  // indexed per lane, so these are memory loads, issued before the K/V rows
+  // (loads retire in order: issued later, forming q would wait for the rows)
+  float rc[QPT], rsn[QPT];
+  if constexpr (QM == Q_PARTIAL) {
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int i = min(tid + u * kAttnThreads, G * HALF - 1) % HALF;
+      rc[u] = p.rope.c[i];
+      rsn[u] = p.rope.s[i];
+    }
+  }
 
   // the appending work-group refreshes the (min, max) summary of the
   // current token's block; the block's older rows are loaded now and used
   // at the end, so their latency hides under the main loop
-  const bool refresh = QM == Q_PARTIAL && appends && p.summary != nullptr && tid < D;
+  const bool refresh = QM == Q_PARTIAL && appends && p.summary != nullptr && tid < HALF;
   const int blk = p.pos / 16;
-  // one register per row (not packed in pairs): nothing waits for these
-  // loads before their use at the end
-  uint16_t srow[16];
+  // two dims per lane, one 32-bit word per row: a full register each, which
+  // the compiler keeps as loaded (16-bit values it repacks in pairs right
+  // after the loads, and then waits for them before the K/V row loads)
+  uint32_t srow[16];
   if (refresh) {
-    const uint16_t* kc = p.k_cache + size_t(g) * p.n_cap * D + tid;
+    const uint32_t* kc = reinterpret_cast<const uint32_t*>(p.k_cache + size_t(g) * p.n_cap * D) + tid;
     // rows from pos on are replaced by the new row later; their loads read
     // an older row (clamped index, no branches)
 #pragma unroll
-    for (int t = 0; t < 16; ++t) srow[t] = kc[size_t(max(0, min(blk * 16 + t, p.pos - 1))) * D];
+    for (int t = 0; t < 16; ++t) srow[t] = kc[size_t(max(0, min(blk * 16 + t, p.pos - 1))) * HALF];
   }
 
   // dense list: the first rows are known before q, so they go in flight now
@@ -338,10 +351,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
       const int e = tid + u * kAttnThreads;
       if (e >= G * HALF) continue;
       const int j = e / HALF, i = e % HALF;
-      const int col = (g * G + j) * D + i;
-      const float qa = chunk_total(cqa[u], p.qkv_partial, p.qkv_splits, p.qkv_out, col);
-      const float qb = chunk_total(cqb[u], p.qkv_partial, p.qkv_splits, p.qkv_out, col + HALF);
-      const float cs = p.rope.c[i], sn = p.rope.s[i];
+      const float qa = chunk_total(cqa[u], p.qkv_splits);
+      const float qb = chunk_total(cqb[u], p.qkv_splits);
+      const float cs = rc[u], sn = rsn[u];
       const uint16_t q0 = f32_to_bf16(qa * cs - qb * sn), q1 = f32_to_bf16(qb * cs + qa * sn);
       sm.q[j][i] = q0;
       sm.q[j][i + HALF] = q1;
@@ -354,9 +366,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
       uint16_t* kr = p.k_cache + (size_t(g) * p.n_cap + p.pos) * D;
       uint16_t* vr = p.v_cache + (size_t(g) * p.n_cap + p.pos) * D;
       if (tid < HALF) {
-        const float ka = chunk_total(cka, p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + tid);
-        const float kb = chunk_total(ckb, p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + tid + HALF);
-        const float cs = p.rope.c[tid], sn = p.rope.s[tid];
+        const float ka = chunk_total(cka, p.qkv_splits);
+        const float kb = chunk_total(ckb, p.qkv_splits);
+        // pair tid: the pair of q element tid as well (tid < D/2 <= G*D/2)
+        const float cs = rc[0], sn = rsn[0];
         const uint16_t k0 = f32_to_bf16(ka * cs - kb * sn), k1 = f32_to_bf16(kb * cs + ka * sn);
         sm.knew[tid] = k0;
         sm.knew[tid + HALF] = k1;
@@ -364,7 +377,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
         kr[tid + HALF] = k1;
       }
       if (tid < D) {
-        const uint16_t v0 = f32_to_bf16(chunk_total(cvv, p.qkv_partial, p.qkv_splits, p.qkv_out, vcol + tid));
+        const uint16_t v0 = f32_to_bf16(chunk_total(cvv, p.qkv_splits));
         sm.vnew[tid] = v0;
         vr[tid] = v0;
       }
@@ -516,21 +529,26 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
     }
   }
   if (refresh) {
-    // per dim: the new row first, then rows 16*blk.. in order (rows from
-    // pos on are the new row); an equal value never replaces an earlier one
-    const uint16_t nb = sm.knew[tid];
-    uint16_t bmn = nb, bmx = nb;
-    float mn = bf16_to_f32(nb), mx = mn;
+    // dims 2*tid and 2*tid + 1, (min, max) each: the new row first, then
+    // rows 16*blk.. in order (rows from pos on are the new row); an equal
+    // value never replaces an earlier one
+    uint32_t mm[2];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const uint16_t u = blk * 16 + t < p.pos ? srow[t] : nb;
-      const float f = bf16_to_f32(u);
-      if (f < mn) { mn = f; bmn = u; }
-      if (f > mx) { mx = f; bmx = u; }
+    for (int h = 0; h < 2; ++h) {
+      const uint16_t nb = sm.knew[2 * tid + h];
+      uint16_t bmn = nb, bmx = nb;
+      float mn = bf16_to_f32(nb), mx = mn;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const uint16_t u = blk * 16 + t < p.pos ? uint16_t(srow[t] >> (16 * h)) : nb;
+        const float f = bf16_to_f32(u);
+        if (f < mn) { mn = f; bmn = u; }
+        if (f > mx) { mx = f; bmx = u; }
+      }
+      mm[h] = uint32_t(bmn) | (uint32_t(bmx) << 16);
     }
-    uint16_t* sp = p.summary + ((size_t(g) * (p.n_cap / 16) + blk) * D + tid) * 2;
-    sp[0] = bmn;
-    sp[1] = bmx;
+    uint16_t* sp = p.summary + ((size_t(g) * (p.n_cap / 16) + blk) * D + 2 * tid) * 2;
+    *reinterpret_cast<uint2*>(sp) = make_uint2(mm[0], mm[1]);
   }
   clk.end(p.clk, size_t(g) * gridDim.x + s);
 }
@@ -629,6 +647,8 @@ int launch_attn_partial(int q_mode, int list_mode, const AttnParams& p_in, hipSt
   p.clk = clock_take(size_t(p.n_splits) * p.n_kv_heads, CLOCK_ATTN, q_mode | (list_mode << 8), p.n_sel, p.n_splits,
                      p.n_kv_heads);
   if (list_mode == L_IDX && p.idx == nullptr) return set_error(BC_ERR_INVALID, "attention: NULL index list");
+  if (q_mode == Q_PARTIAL && (p.qkv_splits < 1 || p.qkv_splits > kQkvMaxChunks))
+    return set_error(BC_ERR_INVALID, "attention: %d q/k/v chunks (1..%d)", p.qkv_splits, kQkvMaxChunks);
   if (list_mode == L_SCORES &&
       (!attn_scored_list_ok(p.bud, p.n_splits) || p.n_sel != p.bud.t_sel ||
        (!p.blk && (!p.scores || p.bud.n_cand > kAttnMaxCand))))

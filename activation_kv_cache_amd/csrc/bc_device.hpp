@@ -149,23 +149,29 @@ __device__ __forceinline__ float chunk_sum(const float* partial, int n_splits, i
 }
 
 
-// The same sum split in two, so that other loads can be issued between the
-// loads and the sum (memory counters retire in order): chunk_load issues the
-// first 8 chunk loads, chunk_total adds them (and any later chunks) in chunk
-// order -- the result equals chunk_sum's.
+// Chunks of q/k/v partials the attention and scoring prologues add (all
+// their loads unrolled): the layer's q/k/v GEMV is planned with at most this
+// many.
+constexpr int kQkvMaxChunks = 8;
+
+// The same sum split in two for at most kQkvMaxChunks chunks, so that
+// other loads can be issued between the loads and the sum (memory counters
+// retire in order): chunk_load issues the chunk loads, chunk_total adds them
+// in chunk order -- the result equals chunk_sum's.  No loop: a loop of loads
+// ahead of the sum makes the compiler wait for every load issued so far (the
+// first K/V rows or block summaries included) before the sum; the launchers
+// reject more chunks.
 struct Chunk8 {
-  float a[8];
+  float a[kQkvMaxChunks];
 };
 __device__ __forceinline__ void chunk_load(Chunk8& c, const float* partial, int n_splits, int d_out, int col) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) c.a[u] = partial[size_t(min(u, n_splits - 1)) * d_out + col];
+  for (int u = 0; u < kQkvMaxChunks; ++u) c.a[u] = partial[size_t(min(u, n_splits - 1)) * d_out + col];
 }
-__device__ __forceinline__ float chunk_total(const Chunk8& c, const float* partial, int n_splits, int d_out,
-                                             int col) {
+__device__ __forceinline__ float chunk_total(const Chunk8& c, int n_splits) {
   float v = 0.f;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) v = u < n_splits ? v + c.a[u] : v;
-  for (int s = 8; s < n_splits; ++s) v += partial[size_t(s) * d_out + col];
+  for (int u = 0; u < kQkvMaxChunks; ++u) v = u < n_splits ? v + c.a[u] : v;
   return v;
 }
 

@@ -710,7 +710,7 @@ static int gemv_target_groups() {
   return v;
 }
 
-GemvPlan plan_gemv(int d_out, int k, bool single) {
+GemvPlan plan_gemv(int d_out, int k, bool single, int max_splits) {
   GemvPlan pl;
   pl.n_tiles = ceil_div(d_out, kGemvTile);
   if (k < 1) k = 1;
@@ -721,6 +721,7 @@ GemvPlan plan_gemv(int d_out, int k, bool single) {
     const int target = gemv_target_groups();
     splits = (target + pl.n_tiles / 2) / pl.n_tiles;
     splits = min(splits, k / 64);   // at least 64 rows per chunk
+    if (max_splits > 0) splits = min(splits, max_splits);
     splits = max(splits, 1);
     splits = max(splits, ceil_div(k, kGemvMaxRows));
   }

@@ -62,8 +62,9 @@ struct GemvPlan {
   size_t partial_bytes;   // n_splits * d_out fp32
 };
 // single: one chunk of rows if it fits a work-group (for OUT_BF16 / SWIGLU /
-// ARGMAX epilogues)
-GemvPlan plan_gemv(int d_out, int k, bool single = false);
+// ARGMAX epilogues); max_splits > 0 caps the chunk count where the rows
+// allow it (a work-group takes at most kGemvMaxRows)
+GemvPlan plan_gemv(int d_out, int k, bool single = false, int max_splits = 0);
 bool gemv_fused_input_ok(int d_in);
 bool gemv_sum_input_ok(int d_in);   // IN_NORM_SUM supports this d_in
 // IN_ATTN supports a dense GEMV of d_in = heads * head_dim inputs over this

@@ -87,16 +87,30 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
       chunk_load(cvv, p.qkv_partial, p.qkv_splits, p.qkv_out, vcol + id);
     }
   }
+  // the rotary cos/sin of the thread's pairs: the table is a kernel argument
+  // indexed per lane, so these are memory loads, issued before the summaries
+  // (loads retire in order: issued later, forming q would wait for them all)
+  float rc[QPT], rsn[QPT];
+  if constexpr (QP) {
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int i = min(tid + u * kScoreThreads, G * HALF - 1) % HALF;
+      rc[u] = p.rope.c[i];
+      rsn[u] = p.rope.s[i];
+    }
+  }
   const int blk = p.pos / 16;
-  // one register per row (not packed in pairs): nothing waits for these
-  // loads before their use at the end
-  uint16_t srow[16];
-  if (first && p.summary && tid < D) {
-    const uint16_t* kc = p.k_cache + size_t(g) * p.n_cap * D + tid;
+  // two dims per lane, one 32-bit word per row: a full register each, which
+  // the compiler keeps as loaded (nothing waits for these loads before their
+  // use at the end)
+  const bool refresh = first && p.summary && tid < HALF;
+  uint32_t srow[16];
+  if (refresh) {
+    const uint32_t* kc = reinterpret_cast<const uint32_t*>(p.k_cache + size_t(g) * p.n_cap * D) + tid;
     // rows from pos on are replaced by the new row later; their loads read
     // an older row (clamped index, no branches)
 #pragma unroll
-    for (int t = 0; t < 16; ++t) srow[t] = kc[size_t(max(0, min(blk * 16 + t, p.pos - 1))) * D];
+    for (int t = 0; t < 16; ++t) srow[t] = kc[size_t(max(0, min(blk * 16 + t, p.pos - 1))) * HALF];
   }
   const int cbeg = blockIdx.x * kScoreBlocksPerGroup;
   const int cend = min(n_cand, cbeg + kScoreBlocksPerGroup);
@@ -121,10 +135,9 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
       const int e = tid + u * kScoreThreads;
       if (e >= G * HALF) continue;
       const int j = e / HALF, i = e % HALF;
-      const int col = (g * G + j) * D + i;
-      const float qa = chunk_total(cqa[u], p.qkv_partial, p.qkv_splits, p.qkv_out, col);
-      const float qb = chunk_total(cqb[u], p.qkv_partial, p.qkv_splits, p.qkv_out, col + HALF);
-      const float c = p.rope.c[i], sn = p.rope.s[i];
+      const float qa = chunk_total(cqa[u], p.qkv_splits);
+      const float qb = chunk_total(cqb[u], p.qkv_splits);
+      const float c = rc[u], sn = rsn[u];
       const uint16_t q0 = f32_to_bf16(qa * c - qb * sn), q1 = f32_to_bf16(qb * c + qa * sn);
       sq[j][i] = q0;
       sq[j][i + HALF] = q1;
@@ -137,34 +150,40 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
       uint16_t* kr = p.k_cache + (size_t(g) * p.n_cap + p.pos) * D;
       uint16_t* vr = p.v_cache + (size_t(g) * p.n_cap + p.pos) * D;
       if (tid < HALF) {
-        const float ka = chunk_total(cka, p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + tid);
-        const float kb = chunk_total(ckb, p.qkv_partial, p.qkv_splits, p.qkv_out, kcol + tid + HALF);
-        const float c = p.rope.c[tid], sn = p.rope.s[tid];
+        const float ka = chunk_total(cka, p.qkv_splits);
+        const float kb = chunk_total(ckb, p.qkv_splits);
+        // pair tid: the pair of q element tid as well (tid < D/2 <= G*D/2)
+        const float c = rc[0], sn = rsn[0];
         const uint16_t k0 = f32_to_bf16(ka * c - kb * sn), k1 = f32_to_bf16(kb * c + ka * sn);
         knew[tid] = k0;
         knew[tid + HALF] = k1;
         kr[tid] = k0;
         kr[tid + HALF] = k1;
       }
-      if (tid < D) vr[tid] = f32_to_bf16(chunk_total(cvv, p.qkv_partial, p.qkv_splits, p.qkv_out, vcol + tid));
+      if (tid < D) vr[tid] = f32_to_bf16(chunk_total(cvv, p.qkv_splits));
     }
     __syncthreads();
-    if (first && p.summary && tid < D) {
-      // per dim: the new row first, then rows 16*blk.. in order (rows from
-      // pos on are the new row); an equal value never replaces an earlier one
-      const uint16_t nb = knew[tid];
-      uint16_t bmn = nb, bmx = nb;
-      float mn = bf16_to_f32(nb), mx = mn;
+    if (refresh) {
+      // dims 2*tid and 2*tid + 1, (min, max) each: the new row first, then
+      // rows 16*blk.. in order (rows from pos on are the new row); an equal
+      // value never replaces an earlier one
+      uint32_t mm2[2];
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const uint16_t u = blk * 16 + t < p.pos ? srow[t] : nb;
-        const float f = bf16_to_f32(u);
-        if (f < mn) { mn = f; bmn = u; }
-        if (f > mx) { mx = f; bmx = u; }
+      for (int h = 0; h < 2; ++h) {
+        const uint16_t nb = knew[2 * tid + h];
+        uint16_t bmn = nb, bmx = nb;
+        float mn = bf16_to_f32(nb), mx = mn;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const uint16_t u = blk * 16 + t < p.pos ? uint16_t(srow[t] >> (16 * h)) : nb;
+          const float f = bf16_to_f32(u);
+          if (f < mn) { mn = f; bmn = u; }
+          if (f > mx) { mx = f; bmx = u; }
+        }
+        mm2[h] = uint32_t(bmn) | (uint32_t(bmx) << 16);
       }
-      uint16_t* sp = p.summary + ((size_t(g) * p.nb_cap + blk) * D + tid) * 2;
-      sp[0] = bmn;
-      sp[1] = bmx;
+      uint16_t* sp = p.summary + ((size_t(g) * p.nb_cap + blk) * D + 2 * tid) * 2;
+      *reinterpret_cast<uint2*>(sp) = make_uint2(mm2[0], mm2[1]);
     }
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -338,6 +357,8 @@ int launch_score_dq(const KvSelectParams& p, hipStream_t s) {
 
 int launch_kv_score(const KvSelectParams& p, hipStream_t s) {
   const bool qp = p.qkv_partial != nullptr;
+  if (qp && (p.qkv_splits < 1 || p.qkv_splits > kQkvMaxChunks))
+    return set_error(BC_ERR_INVALID, "kv score: %d q/k/v chunks (1..%d)", p.qkv_splits, kQkvMaxChunks);
   if (!qp && (p.bud.n_cand <= 0 || p.bud.k_blk <= 0)) return BC_OK;   // nothing to score
   if (p.head_dim == 128) return qp ? launch_score_dq<128, true>(p, s) : launch_score_dq<128, false>(p, s);
   if (p.head_dim == 64) return qp ? launch_score_dq<64, true>(p, s) : launch_score_dq<64, false>(p, s);

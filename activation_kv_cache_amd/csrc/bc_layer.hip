@@ -313,9 +313,9 @@ ProjIn norm_input(const uint16_t* h, const Pending* pend, uint16_t* h_out, const
 // the SwiGLU in the main kernel's epilogue.  FIN_NONE leaves the chunk
 // partials for the next kernel (their count in *n_splits).
 int run_gemv(const uint16_t* wt, int d_in, int d_out, int k, const ProjIn& in, float* partial, int fin_kind,
-             FinishParams f, hipStream_t s, int* n_splits = nullptr) {
+             FinishParams f, hipStream_t s, int* n_splits = nullptr, int max_splits = 0) {
   const bool swiglu = fin_kind == FIN_SWIGLU;
-  const GemvPlan pl = plan_gemv(d_out, k, swiglu);
+  const GemvPlan pl = plan_gemv(d_out, k, swiglu, max_splits);
   if (n_splits) *n_splits = pl.n_splits;
   GemvParams p{};
   p.wt = wt; p.tiled = 1; p.d_in = d_in; p.d_out = d_out; p.k = k;
@@ -482,8 +482,8 @@ int layer_body(const bc_model_dims& m, const bc_layer* ly, const bc_step* st, co
     kp.q = at<uint16_t>(ws, L.q);
     if (kv_sparse && (rc = launch_kv_score(kp, s)) != BC_OK) return rc;
   } else {
-    if ((rc = run_gemv(ly->w_qkv, m.d, qkv_out, k_d, qkv_in, partial, FIN_NONE, FinishParams{}, s, &qkv_splits)) !=
-        BC_OK)
+    if ((rc = run_gemv(ly->w_qkv, m.d, qkv_out, k_d, qkv_in, partial, FIN_NONE, FinishParams{}, s, &qkv_splits,
+                       kQkvMaxChunks)) != BC_OK)
       return rc;
     if (kv_sparse) {
       kp.qkv_partial = partial; kp.qkv_splits = qkv_splits; kp.qkv_out = qkv_out; kp.pos = pos; kp.n_cap = ly->n_cap;
