@@ -299,7 +299,7 @@ def compact_record(out, limit=COMPACT_LIMIT):
         opt["gemv_gate_up_frac"] = {k: g[k]["frac"] for k in ("dense", "r_p_0.5") if k in g}
     if out.get("kernels"):
         opt["kernel_frac"] = kernel_fractions(out["kernels"])
-    for key in ("step_bytes", "masked_baseline", "batch_step", "prediction"):
+    for key in ("step_bytes", "masked_baseline", "batch_step", "prediction", "composed"):
         if out.get(key) and isinstance(out[key], dict) and out[key].get("summary") is not None:
             opt[key] = out[key]["summary"]
     cr = out.get("crossover")
@@ -316,7 +316,7 @@ def compact_record(out, limit=COMPACT_LIMIT):
     if out.get("record_file"):
         opt["record_file"] = out["record_file"]
     c.update(opt)
-    drop = ["cells", "speedup_128k", "gemv_gate_up_frac", "read_probe", "batch_step", "masked_baseline",
+    drop = ["cells", "speedup_128k", "gemv_gate_up_frac", "read_probe", "batch_step", "composed", "masked_baseline",
             "kernel_frac", "step_bytes", "prediction", "crossings_k"]
     line = json.dumps(c, separators=(",", ":"))
     while len(line.encode()) > limit and drop:
@@ -1005,6 +1005,56 @@ def masked_comparison(n, steps, warmup):
     return rec
 
 
+# Composition of the projection branch with the select-once KV branch (the
+# pages' sel modes), as the README's headline speedups at 128K (A100) and its
+# 32K composition table (RTX A6000) quote them: (r_p, r_kv) per context
+COMPOSED_GRID = {131072: ((0.7, 1.0), (0.5, 1.0), (1.0, 0.3), (1.0, 0.5), (0.7, 0.3), (0.5, 0.3), (0.5, 0.5)),
+                 32768: ((1.0, 0.2), (0.7, 0.2), (0.6, 0.2), (0.5, 0.2))}
+PAGE_COMPOSED = {"131072": "A100: 1.91x composed, 1.54x KV selection, 1.15x activation sparsity (keep ratios not "
+                           "stated)",
+                 "32768": "RTX A6000: 1.20x / 1.53x / 1.69x / 1.86x at 1.0/0.2, 0.7/0.2, 0.6/0.2, 0.5/0.2"}
+
+
+def composed_once(model, steps, warmup, rounds=3):
+    """Speedups over the dense step of the projection branch, the select-once
+    KV branch (selection made once after the pre-filled cache, gathered,
+    then read densely by the unchanged split-K kernel) and their composition,
+    at the contexts and keep ratios of COMPOSED_GRID (README "What it does in
+    one picture" and "Timing and quality on a GPU"; paper Table 4 for 32K).
+    Each round times the dense step and every cell of the context once,
+    paired: a speedup is the mean over rounds of dense / cell."""
+    rec = {"rounds": rounds, "steps": steps, "pages": PAGE_COMPOSED, "contexts": {}}
+    for n, grid in COMPOSED_GRID.items():
+        if n > model.max_ctx:
+            continue
+        t = {"dense": []}
+        for _ in range(rounds):
+            g = model.graph(n, 1.0, 1.0)
+            t["dense"].append(time_graph(g, steps, warmup) * 1000.0)
+            del g
+            for r_p, r_kv in grid:
+                key = f"{r_p}/{r_kv}"
+                g = model.graph_sel(n, r_p, r_kv) if r_kv < 1 else model.graph(n, r_p, 1.0)
+                t.setdefault(key, []).append(time_graph(g, steps, warmup) * 1000.0)
+                del g
+        dense = np.array(t["dense"])
+        cells = {}
+        for r_p, r_kv in grid:
+            key = f"{r_p}/{r_kv}"
+            tk = snap_t_sel(n, r_kv)
+            b = step_bytes(tk, r_p, 1.0, *kv_plan(tk, 1.0))
+            sp = float(np.mean(dense / np.array(t[key])))
+            cells[key] = {"r_p": r_p, "r_kv": r_kv, "t_sel": tk, "step_us": round(float(np.mean(t[key])), 1),
+                          "speedup": round(sp, 4), "byte_bound": round(byte_bound(n, r_p, r_kv), 4),
+                          "bytes": b}
+            log(f"[bench] select-once composition at {n}: r_p {r_p}, r_kv {r_kv}: {sp:.3f}x dense "
+                f"(byte bound {byte_bound(n, r_p, r_kv):.2f}x), {np.mean(t[key]):.1f} us/step")
+        rec["contexts"][str(n)] = {"dense_us": round(float(dense.mean()), 1), "cells": cells}
+    rec["summary"] = {n: {k: [c["speedup"], c["byte_bound"]] for k, c in v["cells"].items()}
+                      for n, v in rec["contexts"].items()}
+    return rec
+
+
 def cpu_baseline(model, n):
     """The CPU oracle, as it stands, on one decoder layer of the dense step at
     context n (layer 0's weights and cache copied to the host)."""
@@ -1470,6 +1520,8 @@ def main():
                          "mode's steps between two marker launches (bc_stream_read of 4 MiB), for whole-step "
                          "counters and kernel traces")
     ap.add_argument("--eager", action="store_true", help="with --step-pmc: eager steps instead of graph replays")
+    ap.add_argument("--composed", action="store_true",
+                    help="also time the select-once composition grid (part of the default run)")
     ap.add_argument("--phase-clocks", default="",
                     help="MODE:N+...: per-phase clocks of the GEMV and attention launches of one step per spec "
                          "(needs BC_LIBRARY=libbc_clk.so, the instrumented build)")
@@ -1703,6 +1755,8 @@ def main():
         calib = calibration_sweep(model, args.calib_blocks, args.crossover_steps, min(args.warmup, 3))
         out["crossover"] = crossover_sweep(model, sweep_ctx, args.crossover_blocks, args.crossover_steps,
                                            min(args.warmup, 3), calib=calib)
+    if sweep or args.composed:
+        out["composed"] = composed_once(model, min(args.steps, 20), min(args.warmup, 3))
     if sweep and args.batch_sweep:
         out["batch_step"] = {"runs": [batch_crossover(model, B, BATCH_SWEEPS[B], args.crossover_steps,
                                                       min(args.warmup, 3)) for B in (2, 4)]}

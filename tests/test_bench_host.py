@@ -204,6 +204,8 @@ def synthetic_full_record():
         "crossover": {"contexts": ctx, "pairs": pairs,
                       "speedup": {m: [1.2345] * len(ctx) for m in bench.SWEEP_MODES if m != "dense"},
                       "step_us": {m: [1234.5] * len(ctx) for m in bench.SWEEP_MODES}},
+        "composed": {"summary": {str(n): {f"{a}/{b}": [1.2345, 1.8765] for a, b in grid}
+                                 for n, grid in bench.COMPOSED_GRID.items()}},
         "cpu_baseline": {"value": 1.5612, "unit": "GB/s", "cores": 16, "kind": "oracle", "cpu_model": "x" * 40,
                          "sample": "one of the 32 decoder layers of the dense 131072-token step (weights 436 MB + "
                                    "KV 537 MB), fp64 oracle, 16 run(s) in 10.1s; GB/s = that layer's algorithmic "
@@ -233,6 +235,7 @@ def test_compact_record_fits_and_parses():
     assert rec["cpu_baseline"]["cores"] == 16 and rec["cpu_baseline"]["kind"] == "oracle"
     # the default run's summaries fit whole
     assert len(rec["cells"]) == 12 and len(rec["crossings_k"]) == len(bench.PAIRS)
+    assert rec["composed"]["131072"]["0.5/0.3"] == [1.2345, 1.8765] and len(rec["composed"]["32768"]) == 4
     assert "\n" not in line
 
 
