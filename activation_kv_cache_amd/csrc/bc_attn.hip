@@ -558,8 +558,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
 // thread groups (fixed halves) and combined in a fixed order.
 constexpr int kReduceMaxSplits = 4096;
 
+// Up to kAttnFoldMaxSplits splits every load goes out before any arithmetic
+// (m and l of split tid, the thread's o values): one memory round trip
+// instead of one per phase.  The arithmetic is the same in either case.
+constexpr int kReducePre = kAttnFoldMaxSplits / 2;   // o values per thread (head_dim >= 64: >= 2 groups)
+
 __global__ __launch_bounds__(kAttnThreads) void k_attn_reduce(const ReduceParams p) {
   static_assert(kAttnThreads == kCombineThreads, "one thread per den term slot of the combine order");
+  static_assert(kAttnFoldMaxSplits <= kWave, "preloaded m and l sit in wave 0");
   __shared__ float wts[kReduceMaxSplits];
   __shared__ float part[kAttnThreads];
   __shared__ float red[kAttnThreads / kWave];
@@ -568,8 +574,28 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_reduce(const ReduceParams
   const int D = p.head_dim, S = p.n_splits;
   const float* mj = p.m + size_t(j) * S;
   const float* lj = p.l + size_t(j) * S;
+  const int groups = kAttnThreads / D;          // 2 at head_dim 128, 4 at 64
+  const int grp = tid / D, d = tid % D;
+  const int per = (S + groups - 1) / groups;
+  const int s0 = min(S, grp * per), s1 = min(S, s0 + per);
+  const float* oj = p.o + size_t(j) * S * D + d;
+  const bool pre = S <= kAttnFoldMaxSplits && per <= kReducePre;   // uniform
+  float mp = -INFINITY, lp = 0.f;
+  float ov[kReducePre];
+  if (pre) {
+    if (tid < S) {
+      mp = mj[tid];
+      lp = lj[tid];
+    }
+    // clamped, unconditional loads (splits past the group's end are dropped below)
+#pragma unroll
+    for (int i = 0; i < kReducePre; ++i) ov[i] = oj[size_t(min(s0 + i, S - 1)) * D];
+  }
   float mx = -INFINITY;
-  for (int s = tid; s < S; s += kAttnThreads) mx = fmaxf(mx, mj[s]);
+  if (pre)
+    mx = mp;
+  else
+    for (int s = tid; s < S; s += kAttnThreads) mx = fmaxf(mx, mj[s]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
   if (lane == 0) red[w] = mx;
@@ -579,10 +605,18 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_reduce(const ReduceParams
   for (int i = 1; i < kAttnThreads / kWave; ++i) M = fmaxf(M, red[i]);
   __syncthreads();
   float den = 0.f;
-  for (int s = tid; s < S; s += kAttnThreads) {
-    const float wt = combine_weight(mj[s], M);
-    wts[s] = wt;
-    den = fmaf(wt, lj[s], den);
+  if (pre) {
+    if (tid < S) {
+      const float wt = combine_weight(mp, M);
+      wts[tid] = wt;
+      den = fmaf(wt, lp, den);
+    }
+  } else {
+    for (int s = tid; s < S; s += kAttnThreads) {
+      const float wt = combine_weight(mj[s], M);
+      wts[s] = wt;
+      den = fmaf(wt, lj[s], den);
+    }
   }
   den = combine_wave_sum(den);
   if (lane == 0) red[w] = den;
@@ -590,12 +624,19 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_reduce(const ReduceParams
   den = 0.f;
 #pragma unroll
   for (int i = 0; i < kAttnThreads / kWave; ++i) den += red[i];
-  const int groups = kAttnThreads / D;          // 2 at head_dim 128, 4 at 64
-  const int grp = tid / D, d = tid % D;
-  const int per = (S + groups - 1) / groups;
-  const int s0 = min(S, grp * per), s1 = min(S, s0 + per);
-  const float* oj = p.o + size_t(j) * S * D + d;
-  part[tid] = combine_group(s0, s1, [&](int s) { return oj[size_t(s) * D]; }, [&](int s) { return wts[s]; });
+  float num;
+  if (pre) {
+    // combine_group over registers, in split order
+    num = 0.f;
+#pragma unroll
+    for (int i = 0; i < kReducePre; ++i) {
+      const float nx = fmaf(ov[i], wts[min(s0 + i, S - 1)], num);
+      num = s0 + i < s1 ? nx : num;
+    }
+  } else {
+    num = combine_group(s0, s1, [&](int s) { return oj[size_t(s) * D]; }, [&](int s) { return wts[s]; });
+  }
+  part[tid] = num;
   __syncthreads();
   if (tid < D) {
     float t = 0.f;
