@@ -160,6 +160,9 @@ ATTN_CASES = [
     ("g2-d128-sel", dict(n_heads=8, n_kv_heads=4, head_dim=128), 4096, 4096, 0.3, 0, True),
     ("g8-d128-dense", dict(n_heads=16, n_kv_heads=2, head_dim=128), 2048, 2048, 1.0, 0, True),
     ("g8-d64-sel", dict(n_heads=16, n_kv_heads=2, head_dim=64), 2048, 2048, 0.3, 8, True),
+    # more splits than the reduce kernel preloads (32): its looping path
+    ("tiny-33-splits", gen.TINY, 2048, 2048, 1.0, 33, False),
+    ("8b-2k-64-splits", gen.LLAMA8B, 2048, 2048, 1.0, 64, True),
 ]
 
 
@@ -200,6 +203,31 @@ def test_splitk_attention_vs_oracle(name, dims, n_cap, n, r_kv, S, planted):
     assert_close((go / np.where(gl > 0, gl, 1)[..., None])[ne], (ro / np.where(rl > 0, rl, 1)[..., None])[ne], "o/l")
     rel = assert_close_bf16(host_u16(out), ref64, name)
     assert rel < 1e-2, f"rel-L2 {rel}"
+
+
+@pytest.mark.parametrize("H,S,D", [(8, 1, 64), (8, 2, 128), (32, 16, 128), (32, 31, 64), (32, 32, 128),
+                                   (32, 33, 128), (8, 64, 64), (4, 257, 128)])
+def test_splitk_reduce_vs_oracle(H, S, D):
+    """bc_splitk_reduce alone on seeded partials (some splits empty: m = -inf,
+    l = o = 0; one head with every split empty) against the oracle's merge,
+    on both sides of the 32 splits the kernel preloads."""
+    bc = _bc()
+    rng = gen.rng(0, f"reduce/{H}/{S}/{D}")
+    m = rng.normal(0.0, 2.0, size=(H, S)).astype(np.float32)
+    l = rng.uniform(0.5, 5.0, size=(H, S)).astype(np.float32)
+    o = (rng.standard_normal(size=(H, S, D)) * l[..., None]).astype(np.float32)
+    empty = rng.random(size=(H, S)) < 0.2
+    empty[H - 1, :] = True
+    m[empty] = -np.inf
+    l[empty] = 0.0
+    o[empty] = 0.0
+    out = torch.empty((H, D), dtype=torch.int16, device="cuda")
+    bc.bc_splitk_reduce(torch.from_numpy(m).cuda(), torch.from_numpy(l).cuda(), torch.from_numpy(o).cuda(), out)
+    torch.cuda.synchronize()
+    ref64, _ = oracle.attn_reduce(m, l, o)
+    got = host_u16(out)
+    assert np.all(got[H - 1] == 0)
+    assert_close_bf16(got, ref64, f"reduce H={H} S={S} D={D}")
 
 
 def test_dense_attention_equals_identity_list():
