@@ -1382,6 +1382,47 @@ def kernel_key(name):
     return name.split("(")[0].strip()[:48]
 
 
+def _copy_factor(path, copy_bytes):
+    """KiB a counter reads per byte of a plain copy, from the copy dispatches
+    (rocclr copyBuffer) of a --calib-copy run (which also fills its source)."""
+    vals = [v for _, k, v in _read_counters(path) if "copyBuffer" in k]
+    assert vals, f"no copy dispatch in {path}"
+    return float(np.mean(vals)) * 1024 / copy_bytes
+
+
+def attn_pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, n="131072", copy_bytes="1073741824"):
+    """HBM bytes per launch of the attention kernel from two counter runs of
+    --attn-only (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled
+    by what the same counter reads for a plain copy; set against the
+    kernel's algorithmic bytes (K and V of n tokens plus the partials).  The
+    record carries the hash of the kernel's code, so that the bench reports
+    this traffic only while the kernel is the one counted."""
+    n, copy_bytes = int(n), int(copy_bytes)
+    cf, cw = _copy_factor(cfetch_csv, copy_bytes), _copy_factor(cwrite_csv, copy_bytes)
+
+    def per_dispatch(path):
+        vals = [v for _, k, v in _read_counters(path) if kernel_key(k).startswith("k_attn_partial")]
+        assert vals, f"no attention dispatch in {path}"
+        return float(np.mean(vals)), len(vals)
+
+    (fk, nd), (wk, _) = per_dispatch(fetch_csv), per_dispatch(write_csv)
+    _, S = kv_plan(n, 1.0)
+    algo = attn_bytes(n, S, False)
+    traffic = fk * 1024 / cf + wk * 1024 / cw
+    D = DIMS
+    return {"kernel": f"k_attn_partial<{D['head_dim']}, {D['n_heads'] // D['n_kv_heads']}> "
+                      f"(bc_splitk_attn_partial), dense, head_dim {D['head_dim']}, {D['n_kv_heads']} KV heads, "
+                      f"{S} splits",
+            "context": n, "kernel_source_hash": kernel_source_hash(),
+            "kernel_source_hash_of": "code of bc_attn.hip + bc_device.hpp without comments and white space "
+                                     "(bench.code_text)",
+            "fetch_size_kib_per_dispatch": round(fk, 3), "write_size_kib_per_dispatch": round(wk, 3),
+            "dispatches_averaged": nd,
+            "copy_calibration": {"bytes": copy_bytes, "fetch_factor": round(cf, 6), "write_factor": round(cw, 6)},
+            "traffic_bytes_per_launch": int(round(traffic)), "algorithmic_bytes_per_launch": algo,
+            "traffic_over_algorithmic": round(traffic / algo, 4)}
+
+
 def step_pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, specs, copy_bytes):
     """HBM bytes of one decode step per mode, from two counter runs of
     --step-pmc (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled
@@ -1393,14 +1434,7 @@ def step_pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, specs, copy_b
     "Overview"; "Usage", the byte account).  Returns one record per mode."""
     specs = [(m, int(n), int(r)) for m, n, r in (x.split(":") for x in specs.split("+"))]
     copy_bytes = int(copy_bytes)
-
-    def copy_factor(path):
-        # the copy dispatches only (the run also fills its source)
-        vals = [v for _, k, v in _read_counters(path) if "copyBuffer" in k]
-        assert vals, f"no copy dispatch in {path}"
-        return float(np.mean(vals)) * 1024 / copy_bytes
-
-    cf, cw = copy_factor(cfetch_csv), copy_factor(cwrite_csv)
+    cf, cw = _copy_factor(cfetch_csv, copy_bytes), _copy_factor(cwrite_csv, copy_bytes)
 
     def segments(path, factor):
         rows = sorted(_read_counters(path))
@@ -1529,6 +1563,9 @@ def main():
                     help="FETCH_CSV,WRITE_CSV,CFETCH_CSV,CWRITE_CSV,SPECS,COPY_BYTES -- SPECS as for --step-pmc: "
                          "sum the counters of each mode's steps (between its two markers) and print each step's "
                          "HBM bytes against its byte account")
+    ap.add_argument("--attn-pmc-summary", default="",
+                    help="FETCH_CSV,WRITE_CSV,COPY_FETCH_CSV,COPY_WRITE_CSV[,N[,COPY_BYTES]] -- HBM bytes per "
+                         "launch of the attention kernel from counter runs of --attn-only (the committed profile)")
     ap.add_argument("--trace-summary", default="",
                     help="TRACE_CSV,SPECS -- per-mode kernel times of a kernel trace of --step-pmc runs")
     ap.add_argument("--record", default=os.path.join(ROOT, "gpurun_out", "bench_record.json"),
@@ -1537,7 +1574,18 @@ def main():
     args = ap.parse_args()
 
     if args.pmc_summary:
-        print(json.dumps(step_pmc_summary(*args.pmc_summary.split(","))))
+        recs = step_pmc_summary(*args.pmc_summary.split(","))
+        # the committed profile: the records, the copy factors and the hash
+        # of the library's code they were taken on
+        print(json.dumps({"what": "HBM bytes of one whole decode step per mode (Llama-3.1-8B dims, 32 layers + "
+                                  "LM head), eager steps, from two rocprofv3 counter passes scaled by a 1 GiB copy",
+                          "copy_factors": recs[0]["copy_factors"] if recs else None,
+                          "modes": recs, "kernel_sources_hash": all_sources_hash(),
+                          "kernel_sources": "activation_kv_cache_amd/csrc/* (code without comments and white space)"},
+                         indent=1))
+        return
+    if args.attn_pmc_summary:
+        print(json.dumps(attn_pmc_summary(*args.attn_pmc_summary.split(",")), indent=1))
         return
     if args.trace_summary:
         print(json.dumps(step_trace_summary(*args.trace_summary.split(","))))

@@ -301,6 +301,28 @@ def test_step_pmc_summary_on_synthetic_counters(tmp_path):
     assert r["algorithmic_bytes"] == bench.step_bytes(2048, 1.0, 1.0, *bench.kv_plan(2048, 1.0))
 
 
+def test_attn_pmc_summary_on_synthetic_counters(tmp_path):
+    """The attention kernel's bytes per launch: the mean over its dispatches
+    of each counter, scaled by the copy calibration, against its algorithmic
+    bytes, keyed to the kernel's code."""
+    def write(path, rows):
+        with open(path, "w") as fh:
+            fh.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+            for d, k, v in rows:
+                fh.write(f'{d},"{k}",X,{v}\n')
+    att = "void bc::(anonymous namespace)::k_attn_partial<128, 4, 0, 0>(bc::AttnParams)"
+    write(tmp_path / "f.csv", [(1, "k_fill", 9e9), (2, att, 262000.0), (3, att, 262400.0)])
+    write(tmp_path / "w.csv", [(1, "k_fill", 9e9), (2, att, 570.0), (3, att, 580.0)])
+    write(tmp_path / "cf.csv", [(1, "fill", 7.0), (2, "__amd_rocclr_copyBuffer", 512.0)])      # 1 MiB: 0.5
+    write(tmp_path / "cw.csv", [(1, "fill", 7.0), (2, "__amd_rocclr_copyBuffer", 1024.0)])     # 1.0
+    r = bench.attn_pmc_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
+                               str(tmp_path / "cw.csv"), "131072", str(1 << 20))
+    assert r["dispatches_averaged"] == 2 and r["fetch_size_kib_per_dispatch"] == 262200.0
+    assert r["traffic_bytes_per_launch"] == round(262200.0 * 1024 / 0.5 + 575.0 * 1024)
+    assert r["algorithmic_bytes_per_launch"] == 537403392
+    assert r["kernel_source_hash"] == bench.kernel_source_hash() and r["context"] == 131072
+
+
 def test_code_text_ignores_comments_and_white_space(tmp_path):
     """The counter summaries are keyed to the kernels' code: an edit of a
     comment keeps them valid, an edit of code (or of a string) does not."""
