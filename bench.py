@@ -244,7 +244,7 @@ def predicted_crossing_k(contexts, t_us, mode_p, mode_k, plan=None):
     return None, 1e-3 / slope, cost[mode_p], cost[mode_k]
 
 
-COMPACT_LIMIT = 4000     # bytes of the last stdout line (the driver keeps only the end of stdout)
+COMPACT_LIMIT = 4000     # bytes of the last stdout line (a reader that keeps only the end of stdout gets it whole)
 
 
 def _cell_str(c):
