@@ -202,6 +202,7 @@ struct KvSelectParams {
   uint16_t* q_out;
   uint16_t* k_cache;
   uint16_t* v_cache;
+  int score_bpg;          // candidate blocks per scoring work-group (set by launch_kv_score)
 };
 // scores, then the list (one work-group per KV head)
 int launch_kv_score_select(const KvSelectParams& p, hipStream_t s);

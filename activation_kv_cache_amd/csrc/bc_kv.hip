@@ -33,7 +33,12 @@ namespace bc {
 namespace {
 
 constexpr int kScoreThreads = 1024;
-constexpr int kScoreBlocksPerGroup = 256;   // one work-group per CU at 128K
+// Candidate blocks per scoring work-group: 256, one work-group per CU at
+// 128K tokens (8 KV heads); with more candidates than one round of such
+// work-groups covers, up to 384 per group (the loads all in registers), so
+// that one round still covers them
+constexpr int kScoreBlocksPerGroup = 256;
+constexpr int kScoreTargetGroups = 256;     // work-groups (over all KV heads) one round holds
 constexpr int kSelThreads = 1024;
 constexpr int kSelMaxCand = kSelThreads * 32;
 
@@ -49,12 +54,13 @@ __device__ __forceinline__ uint4 load_nt16(const uint16_t* p) {
 // bf16 rounding); the first work-group of each KV head also stores q,
 // appends k, v of the current token at slot pos and refreshes the (min, max)
 // summary of block pos/16 (which is then never a candidate).
-template <int D, int G, bool QP>
+// NIT wave loads of summaries per lane (a group of at most NIT * 16 waves *
+// CPW blocks), all issued before q is formed.
+template <int D, int G, bool QP, int NIT>
 __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams p) {
   constexpr int P = D / 4;            // lanes per candidate block
   constexpr int CPW = kWave / P;      // candidate blocks per wave load
   constexpr int HALF = D / 2;
-  constexpr int NIT = kScoreBlocksPerGroup / ((kScoreThreads / kWave) * CPW);
   __shared__ uint16_t sq[G][D];
   __shared__ uint16_t knew[D];
   const int g = blockIdx.y;
@@ -112,8 +118,8 @@ __global__ __launch_bounds__(kScoreThreads) void k_kv_score(const KvSelectParams
 #pragma unroll
     for (int t = 0; t < 16; ++t) srow[t] = kc[size_t(max(0, min(blk * 16 + t, p.pos - 1))) * HALF];
   }
-  const int cbeg = blockIdx.x * kScoreBlocksPerGroup;
-  const int cend = min(n_cand, cbeg + kScoreBlocksPerGroup);
+  const int cbeg = blockIdx.x * p.score_bpg;
+  const int cend = min(n_cand, cbeg + p.score_bpg);
   const uint16_t* sg = p.summary + size_t(g) * p.nb_cap * D * 2;
   uint4 mm[NIT];
   if (p.bud.k_blk > 0) {
@@ -340,17 +346,42 @@ __global__ __launch_bounds__(256) void k_build_summary(const uint16_t* k_cache, 
   }
 }
 
-template <int D, bool QP>
-int launch_score_dq(const KvSelectParams& p, hipStream_t s) {
-  dim3 grid(max(1, ceil_div(p.bud.n_cand, kScoreBlocksPerGroup)), p.n_kv_heads), block(kScoreThreads);
+template <int D, bool QP, int NIT>
+int launch_score_dqn(const KvSelectParams& p, hipStream_t s) {
+  dim3 grid(max(1, ceil_div(p.bud.n_cand, p.score_bpg)), p.n_kv_heads), block(kScoreThreads);
   switch (p.n_heads / p.n_kv_heads) {
-    case 1: k_kv_score<D, 1, QP><<<grid, block, 0, s>>>(p); break;
-    case 2: k_kv_score<D, 2, QP><<<grid, block, 0, s>>>(p); break;
-    case 4: k_kv_score<D, 4, QP><<<grid, block, 0, s>>>(p); break;
-    case 8: k_kv_score<D, 8, QP><<<grid, block, 0, s>>>(p); break;
+    case 1: k_kv_score<D, 1, QP, NIT><<<grid, block, 0, s>>>(p); break;
+    case 2: k_kv_score<D, 2, QP, NIT><<<grid, block, 0, s>>>(p); break;
+    case 4: k_kv_score<D, 4, QP, NIT><<<grid, block, 0, s>>>(p); break;
+    case 8: k_kv_score<D, 8, QP, NIT><<<grid, block, 0, s>>>(p); break;
     default: return set_error(BC_ERR_UNSUPPORTED, "kv score: group %d", p.n_heads / p.n_kv_heads);
   }
   return check_launch("k_kv_score");
+}
+
+// 256 blocks per work-group while one round of work-groups covers the
+// candidates; beyond that as many as spread them over that round (a
+// multiple of one wave load of all 16 waves, at most 1.5 x 256); past that,
+// 256 per work-group again in more rounds
+template <int D, bool QP>
+int launch_score_dq(const KvSelectParams& p_in, hipStream_t s) {
+  constexpr int UNIT = (kScoreThreads / kWave) * (kWave / (D / 4));   // blocks per wave load of every wave
+  constexpr int NIT1 = kScoreBlocksPerGroup / UNIT;
+  KvSelectParams p = p_in;
+  const int groups = max(1, kScoreTargetGroups / max(1, p.n_kv_heads));   // per KV head
+  const int n = max(1, p.bud.n_cand);
+  if (ceil_div(n, kScoreBlocksPerGroup) <= groups) {
+    p.score_bpg = kScoreBlocksPerGroup;
+    return launch_score_dqn<D, QP, NIT1>(p, s);
+  }
+  constexpr int NIT2 = NIT1 + NIT1 / 2;   // all issued before q is formed: its registers still fit
+  const int bpg = ceil_div(ceil_div(n, groups), UNIT) * UNIT;
+  if (bpg <= NIT2 * UNIT) {
+    p.score_bpg = bpg;
+    return launch_score_dqn<D, QP, NIT2>(p, s);
+  }
+  p.score_bpg = kScoreBlocksPerGroup;   // more rounds of work-groups
+  return launch_score_dqn<D, QP, NIT1>(p, s);
 }
 
 }  // namespace

@@ -120,6 +120,10 @@ LAYER_CASES = [
     # ranked by their own kernel when sparse)
     ("8b-128k-dense", gen.LLAMA8B, 131072, 131072, 1.0, 1.0, 4, 1024, 0),
     ("8b-128k-both-0.5-0.3", gen.LLAMA8B, 131072, 131072, 0.5, 0.3, 4, 1024, 0),
+    # over 8192 candidate blocks at 8 KV heads: the scoring work-groups take
+    # more than 256 blocks each (their last loads issued after q is formed)
+    # and the ranking kernel holds 16 keys per thread
+    ("8b-160k-kv-0.3", gen.LLAMA8B, 163840, 163840, 1.0, 0.3, 4, 1024, 0),
     # the KV-window baseline (sinks and the most recent tokens, no scoring)
     # through the same attention kernel
     ("tiny-kv-window", gen.TINY, 2048, 2048, 1.0, 0.3, 4, 2048, 8),
