@@ -192,3 +192,120 @@ def test_step_vs_oracle_8b_2k(r_p, r_kv):
     head, in the launch configuration of the bench (default splits, window
     1024), KV ~ N(0, 1)."""
     _case(gen.LLAMA8B, 2, 2048, 2048, r_p, r_kv, 4, 1024, 0, seed=42, kv_std=1.0)
+
+
+@pytest.mark.parametrize("r_p,r_kv", [(1.0, 1.0), (0.5, 0.3)], ids=["dense", "both-0.5-0.3"])
+def test_consecutive_steps_cross_a_block(r_p, r_kv):
+    """Eight consecutive decode steps on one cache (tiny dims, two layers, LM
+    head of 1000 words) at contexts 1020..1027: the appends (slots 1019..1026)
+    cross the block boundary at 1024, each step refreshing the summary of the
+    block it writes into and the next step reading both.  Per step: the step
+    equals, bit for bit, the chain of bc_decode_layer calls run on a second
+    copy of the caches (hidden state, logits, token), and the oracle's chain
+    of layers -- on host copies of the caches, with the GPU's index sets and
+    appended k, v rows -- gives the same hidden state within the single-step
+    bound.  After the last step both caches, and every block summary, equal
+    the oracle's; each summary also equals its definition (per dim the min
+    and max over the block's rows below the context) recomputed from the
+    GPU's own cache."""
+    from activation_kv_cache_amd import binding as bc
+    dims = dict(gen.TINY, vocab=1000, n_layers=2)
+    d, dff, H, Hkv, D, vocab = (dims["d"], dims["d_ff"], dims["n_heads"], dims["n_kv_heads"], dims["head_dim"],
+                                dims["vocab"])
+    n_cap, n0, steps, sinks, window, S, seed = 2048, 1020, 8, 4, 128, 4, 43
+    md = bc.dims(dims)
+    pol = bc.policy(r_kv, sinks, window)
+    Ws, host_caches = [], []
+    for li in range(2):
+        Ws.append(_weights(seed, dims, li, False))
+        K = gen.normal_bf16(seed, f"layer{li}/kcache", (Hkv, n_cap, D), 0.5)
+        V = gen.normal_bf16(seed, f"layer{li}/vcache", (Hkv, n_cap, D), 0.5)
+        summ = np.zeros((Hkv, n_cap // 16, D, 2), np.uint16)
+        for g in range(Hkv):
+            s = oracle.kv_summary(K[g], n0 - 1)
+            summ[g, :s.shape[0]] = s
+        host_caches.append([K, V, summ])
+    g_final = gen.to_bf16_bits(np.ones(d, np.float32))
+    w_head = gen.normal_bf16(seed, "head", (d, vocab), 0.02)
+    gf_d, wh_d = dev(g_final), bc.packed_tiles(dev(w_head))
+    packed = []
+    for W in Ws:
+        w = {k: dev(v) for k, v in W.items()}
+        w_gu = torch.empty(2 * d * dff, dtype=torch.int16, device="cuda")
+        bc.bc_pack_gate_up(w["gate"], w["up"], w_gu)
+        packed.append(dict(qkv=bc.packed_tiles(w["qkv"]), o=bc.packed_tiles(w["o"]), gu=w_gu,
+                           down=bc.packed_tiles(w["down"]), g1=w["g1"], g2=w["g2"]))
+
+    def device_copy():
+        kv = [(dev(K), dev(V), dev(sm)) for K, V, sm in host_caches]
+        return kv, [bc.make_layer(p["qkv"], p["o"], p["gu"], p["down"], p["g1"], p["g2"], *kv[i])
+                    for i, p in enumerate(packed)]
+
+    kv_a, cl_a = device_copy()     # the step's caches
+    kv_b, cl_b = device_copy()     # the layer chain's caches
+    arr = bc.make_layer_array(cl_a)
+    ws_step = workspace(bc.bc_step_workspace_bytes(md, n_cap, S))
+    ws_layer = workspace(bc.bc_layer_workspace_bytes(md, n_cap, S))
+    ws_head = workspace(bc.bc_lm_head_workspace_bytes(md))
+    k_d, k_ff = oracle.channel_keep(r_p, d), oracle.channel_keep(r_p, dff)
+    for t in range(steps):
+        n = n0 + t
+        t_sel = bc.bc_kv_budget(n, pol)["t_sel"]
+        h0 = gen.activation_bf16(seed, f"h{t}", d)
+        h_a = dev(h0)
+        lg_a = torch.full((vocab,), float("nan"), dtype=torch.float32, device="cuda")
+        tk_a = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        bc.bc_decode_step(md, arr, gf_d, wh_d, bc.make_step(n, r_p, pol, S), h_a, lg_a, tk_a, ws_step)
+        h_b = dev(h0)
+        forced = []
+        for c in cl_b:
+            sizes = {"k": Hkv * D, "v": Hkv * D}
+            if r_p < 1:
+                sizes.update(idx_qkv=k_d, idx_o=k_d, idx_gu=k_d, idx_down=k_ff)
+            if r_kv < 1:
+                sizes["idx_kv"] = Hkv * t_sel
+            taps = {k: torch.full((v,), -1, dtype=torch.int16 if k in ("k", "v") else torch.int32, device="cuda")
+                    for k, v in sizes.items()}
+            bc.bc_decode_layer(md, c, bc.make_step(n, r_p, pol, S, taps=bc.make_taps(**taps)), h_b, ws_layer)
+            torch.cuda.synchronize()
+            f = {}
+            for k, tv in taps.items():
+                if k in ("k", "v"):
+                    f[k] = host_u16(tv).reshape(Hkv, D)
+                else:
+                    f[k] = host(tv).reshape(Hkv, -1) if k == "idx_kv" else host(tv)
+            forced.append(f)
+        lg_b = torch.empty_like(lg_a)
+        tk_b = torch.empty_like(tk_a)
+        bc.bc_lm_head(md, h_b, gf_d, wh_d, lg_b, tk_b, 1e-5, ws_head)
+        torch.cuda.synchronize()
+        assert torch.equal(h_a, h_b) and torch.equal(lg_a, lg_b) and torch.equal(tk_a, tk_b), \
+            f"step {t}: bc_decode_step differs from its chain of bc_decode_layer calls"
+        # the oracle's chain on its own caches (updated in place)
+        h_ref = h0
+        slack = np.zeros(d)
+        for li in range(2):
+            K, V, summ = host_caches[li]
+            ref = oracle.decode_layer(h_ref, Ws[li], K, V, summ, n, dims, r_p, r_kv, sinks, window, S,
+                                      forced=forced[li])
+            wd = oracle.bf16_to_f64(Ws[li]["down"])
+            uf = _ulp(oracle.bf16_to_f64(ref["hff"])).reshape(-1)
+            slack += _ulp(oracle.bf16_to_f64(ref["h_mid"])).reshape(-1) + 4 * np.sqrt((wd * wd).T @ (uf * uf))
+            h_ref = ref["h_out"]
+        g = oracle.bf16_to_f64(host_u16(h_a)).reshape(-1)
+        r = oracle.bf16_to_f64(h_ref).reshape(-1)
+        err = np.abs(g - r)
+        assert (err <= 2e-3 + 1e-2 * np.abs(r) + slack).all(), f"step {t} (context {n}): hidden outside the bound"
+        assert np.linalg.norm(g - r) / np.linalg.norm(r) < 1e-2
+    n_last = n0 + steps - 1
+    nb = (n_last + 15) // 16
+    for li in range(2):
+        K, V, summ = host_caches[li]
+        Ka, Va, Sa = (host_u16(x) for x in kv_a[li])
+        Kb, Vb, Sb = (host_u16(x) for x in kv_b[li])
+        assert np.array_equal(Ka, Kb) and np.array_equal(Va, Vb) and np.array_equal(Sa, Sb), f"layer {li}: caches"
+        assert np.array_equal(Ka, K) and np.array_equal(Va, V), f"layer {li}: cache rows differ from the oracle's"
+        assert np.array_equal(Sa[:, :nb], summ[:, :nb]), f"layer {li}: summaries differ from the oracle's"
+        for g in range(Hkv):   # as values (a refresh meets the new row first: -0 and +0 may swap)
+            assert np.array_equal(oracle.bf16_to_f64(Sa[g, :nb]), oracle.bf16_to_f64(oracle.kv_summary(Ka[g], n_last))), \
+                f"layer {li} head {g}: summary"
