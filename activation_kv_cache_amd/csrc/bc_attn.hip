@@ -39,6 +39,7 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 constexpr int kAttnThreads = 256;
+static_assert(kAttnMaxCand == 8 * kAttnThreads, "prologue block ranking: 8 candidate keys per thread");
 constexpr int kAttnWaves = kAttnThreads / kWave;
 constexpr int kIdxChunk = 1024;
 constexpr float kLn2 = 0.693147180559945309f;
@@ -333,10 +334,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(const AttnParams 
     } else if (r_lo < r_hi) {   // uniform over the work-group
       const int n = p.bud.n_cand;
       const float* sc = p.scores + size_t(g) * p.scores_stride;
-      if (n <= kAttnThreads * 8)
-        select_block_ranks<kAttnThreads, 8>(sc, n, KB, r_lo, r_hi, sm.blk, sm.tk);
-      else
-        select_block_ranks<kAttnThreads, 32>(sc, n, KB, r_lo, r_hi, sm.blk, sm.tk);
+      // n <= kAttnMaxCand: 8 keys per thread (more candidates are ranked by
+      // their own kernel, which measured faster)
+      select_block_ranks<kAttnThreads, kAttnMaxCand / kAttnThreads>(sc, n, KB, r_lo, r_hi, sm.blk, sm.tk);
     }
   }
 
@@ -681,7 +681,7 @@ bool attn_scored_list_ok(const bc_kv_budget_info& bud, int n_splits) {
   return scored_ranks_per_split(bud.t_sel, n_splits) <= kAttnMaxRanks;
 }
 
-bool attn_prologue_select_ok(const bc_kv_budget_info& bud) { return bud.n_cand <= kAttnThreads * 8; }
+bool attn_prologue_select_ok(const bc_kv_budget_info& bud) { return bud.n_cand <= kAttnMaxCand; }
 
 int launch_attn_partial(int q_mode, int list_mode, const AttnParams& p_in, hipStream_t s) {
   AttnParams p = p_in;
@@ -692,7 +692,7 @@ int launch_attn_partial(int q_mode, int list_mode, const AttnParams& p_in, hipSt
     return set_error(BC_ERR_INVALID, "attention: %d q/k/v chunks (1..%d)", p.qkv_splits, kQkvMaxChunks);
   if (list_mode == L_SCORES &&
       (!attn_scored_list_ok(p.bud, p.n_splits) || p.n_sel != p.bud.t_sel ||
-       (!p.blk && (!p.scores || p.bud.n_cand > kAttnMaxCand))))
+       (!p.blk && p.bud.k_blk > 0 && (!p.scores || p.bud.n_cand > kAttnMaxCand))))
     return set_error(BC_ERR_INVALID, "attention: scored list out of range");
   if (p.head_dim == 128) return launch_partial_d<128>(q_mode, list_mode, p, s);
   if (p.head_dim == 64) return launch_partial_d<64>(q_mode, list_mode, p, s);

@@ -138,7 +138,7 @@ int launch_argmax_finish(const float* tile_max, const int32_t* tile_arg, int n_t
 //              blocks' candidate indices in rank order.
 enum AttnQ : int { Q_GLOBAL = 0, Q_PARTIAL = 1 };
 enum AttnList : int { L_DENSE = 0, L_IDX = 1, L_SCORES = 2 };
-constexpr int kAttnMaxCand = 256 * 32;   // candidate blocks one attention work-group selects from
+constexpr int kAttnMaxCand = 256 * 8;    // candidate blocks one attention work-group selects from
 constexpr int kAttnMaxRanks = 1024;      // block ranks one split may need
 
 struct AttnParams {
