@@ -297,17 +297,42 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
           wr[4 * q + 3] = v4.w;
         }
         float t = 0.f;
-        for (int g = 0; g < G; ++g) {
-          const int s0 = min(S, g * per), s1 = min(S, s0 + per);
-          // combine_group over registers: splits outside [s0, s1) leave the
-          // sum as it is (their weights are not set; the select drops them)
-          float num = 0.f;
+        if (S == kAttnFoldMaxSplits && (G == 2 || G == 4)) {
+          // every split present (the usual case): each group's splits are
+          // known, so the sums take no selects; the same fmaf chains and the
+          // same group order as below
+          static_assert(kAttnFoldMaxSplits % 4 == 0, "groups of whole splits");
+          float nm[4] = {0.f, 0.f, 0.f, 0.f};
+          if (G == 2) {
 #pragma unroll
-          for (int sp = 0; sp < kAttnFoldMaxSplits; ++sp) {
-            const float nx = fmaf(ov[sp], wr[sp], num);
-            num = (sp >= s0 && sp < s1) ? nx : num;
+            for (int i = 0; i < kAttnFoldMaxSplits / 2; ++i) {
+              nm[0] = fmaf(ov[i], wr[i], nm[0]);
+              nm[1] = fmaf(ov[kAttnFoldMaxSplits / 2 + i], wr[kAttnFoldMaxSplits / 2 + i], nm[1]);
+            }
+            t += nm[0];
+            t += nm[1];
+          } else {
+#pragma unroll
+            for (int i = 0; i < kAttnFoldMaxSplits / 4; ++i)
+#pragma unroll
+              for (int g = 0; g < 4; ++g)
+                nm[g] = fmaf(ov[g * (kAttnFoldMaxSplits / 4) + i], wr[g * (kAttnFoldMaxSplits / 4) + i], nm[g]);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) t += nm[g];
           }
-          t += num;
+        } else {
+          for (int g = 0; g < G; ++g) {
+            const int s0 = min(S, g * per), s1 = min(S, s0 + per);
+            // combine_group over registers: splits outside [s0, s1) leave the
+            // sum as it is (their weights are not set; the select drops them)
+            float num = 0.f;
+#pragma unroll
+            for (int sp = 0; sp < kAttnFoldMaxSplits; ++sp) {
+              const float nx = fmaf(ov[sp], wr[sp], num);
+              num = (sp >= s0 && sp < s1) ? nx : num;
+            }
+            t += num;
+          }
         }
         const float den = sm.fold.den[hh];
         const uint32_t xb = f32_to_bf16(den > 0.f ? t / den : 0.f);
