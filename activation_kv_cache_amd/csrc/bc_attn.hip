@@ -596,8 +596,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_reduce(const ReduceParams
     mx = mp;
   else
     for (int s = tid; s < S; s += kAttnThreads) mx = fmaxf(mx, mj[s]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+  mx = wave_max_f32(mx);
   if (lane == 0) red[w] = mx;
   __syncthreads();
   float M = red[0];

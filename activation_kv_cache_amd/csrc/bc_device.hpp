@@ -412,9 +412,10 @@ __device__ void block_topk(int n, int k, KeyFn key_fn, EmitFn emit, TopkSmem<NT,
 // bf16 attention output:
 //   M = max_s m_s;  w_s = exp(m_s - M), or 0 when m_s or M is -inf;
 //   den: thread t of kCombineThreads sums w_s l_s over s = t, t + 256, ...
-//        in order (fmaf from 0), a xor butterfly (32, 16, ..., 1) sums each
-//        wave, lane 0's value is taken, and the wave sums are added in order
-//        to 0;
+//        in order (fmaf from 0), each wave's sum is wave_sum_f32's (DPP
+//        pairs, quads, eights and sixteens within each row of 16 lanes, then
+//        the four rows as (r0 + r1) + (r2 + r3)), and the wave sums are added
+//        in order to 0;
 //   num_d: G = kCombineThreads / D groups of ceil(S / G) consecutive splits,
 //        each summed in split order with fmaf from 0 (combine_group), the
 //        group sums added in order to 0;
@@ -434,10 +435,20 @@ __device__ __forceinline__ float combine_group(int s0, int s1, OF o, WF w) {
   return num;
 }
 
-__device__ __forceinline__ float combine_wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+__device__ __forceinline__ float combine_wave_sum(float v) { return wave_sum_f32(v); }
+
+// Largest value over the 64 lanes (exact in any order): DPP within rows of
+// 16, then the four rows.
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // ------------------------------------- 15-bit keys in registers, two passes

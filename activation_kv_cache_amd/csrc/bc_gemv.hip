@@ -264,8 +264,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const GemvParams p) {
       clk.stamp_after(3, ov[kAttnFoldMaxSplits - 1]);
       auto head_weights = [&](int hw, float ms, float lv) {
         float M = ms;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
+        M = wave_max_f32(M);
         const float wt = combine_weight(ms, M);
         const float den = combine_wave_sum(lane < S ? fmaf(wt, lv, 0.f) : 0.f);
         if (lane < S) sm.fold.w[hw][lane] = wt;

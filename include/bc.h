@@ -247,8 +247,8 @@ int bc_splitk_attn_partial(const uint16_t* q, const uint16_t* k_cache, const uin
 /* a6. Merge of the split partials (README "Overview", split-K attention):
  * M = max_s m_s; out = sum_s o_s e^(m_s-M) / sum_s l_s e^(m_s-M), rounded to
  * bf16; all splits empty gives 0.  out bf16 [n_heads][head_dim].  The fp32
- * order is fixed (the denominator over 256 thread slots and a wave
- * butterfly, the numerator in 256/head_dim groups of consecutive splits
+ * order is fixed (the denominator over 256 thread slots and a fixed
+ * cross-lane sum per wave, the numerator in 256/head_dim groups of consecutive splits
  * with fma in split order), and bc_decode_layer's dense o projection, which
  * merges the splits in its own prologue, follows the same order: its
  * attention output equals this call's on the same partials, bit for bit. */
