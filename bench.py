@@ -518,7 +518,29 @@ class Model:
         return g
 
 
+SETTLE_S = 1.0         # untimed replays before a process's first timed graph
+_settled = False
+
+
+def settle(g, seconds=SETTLE_S):
+    """Replays g, untimed, for about `seconds`: a GPU that was idle takes a
+    few hundred ms of sustained load to reach its steady clocks (without
+    this, a process's first 30-step timing of the dense 128K step read 4-5%
+    slower than the same graph timed after it, and the cells right after it
+    were slow too), so the first timed measurement of a process waits for
+    that; later ones follow back-to-back work."""
+    global _settled
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        for _ in range(8):
+            g.replay()
+        torch.cuda.synchronize()
+    _settled = True
+
+
 def time_graph(g, steps, warmup):
+    if not _settled:
+        settle(g)
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
