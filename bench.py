@@ -1590,7 +1590,7 @@ def main():
                          "launch of the attention kernel from counter runs of --attn-only (the committed profile)")
     ap.add_argument("--trace-summary", default="",
                     help="TRACE_CSV,SPECS -- per-mode kernel times of a kernel trace of --step-pmc runs")
-    ap.add_argument("--record", default=os.path.join(ROOT, "gpurun_out", "bench_record.json"),
+    ap.add_argument("--record", default=os.path.join(ROOT, "results", "bench_record.json"),
                     help="where the full record (cells, kernels, sweep) is written; the last stdout line is a "
                          "compact summary of it")
     args = ap.parse_args()

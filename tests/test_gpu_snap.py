@@ -5,7 +5,8 @@ The GPU computes the observation-window logits with bf16 matrix instructions
 and float32 accumulation, the softmax, votes and pooling in float32.  Checks:
   - its pooled scores (scores_out) against the oracle's float64 ones,
     |gpu - ref| <= 2e-4 |ref| (float32 accumulation over up to n terms of a
-    row's softmax sum; the reading is in DESIGN.md);
+    row's softmax sum, far above the errors measured, at most 7e-7, and far
+    below the gaps between distinct votes that the tests rely on);
   - its token lists bit for bit against the oracle's ranking of the GPU's own
     float32 scores (the decision taken in the kernel's precision);
   - the kept tokens are a valid top-k of the oracle's float64 scores up to
